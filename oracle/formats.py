@@ -1,0 +1,82 @@
+"""Number formats: fp16 rounding and the FP6 e3m2 code.
+
+Test infrastructure only (see the package docstring for who may import it).
+
+FP6 is named, with no bit layout, on the FP6-LLM news page (m.zhengruan.com),
+sections "用FP6跑Llama，单卡比双卡还快" and "重新设计内核方案". The reading used here
+is e3m2: 1 sign bit, 3 exponent bits with bias 3, 2 mantissa bits, subnormals when the
+exponent field is 0, no infinities or NaNs, largest magnitude 28.
+"""
+
+import numpy as np
+
+E3M2_BIAS = 3
+E3M2_MAX = 28.0
+
+
+def fp16_bits(values):
+    """Round float64 values to fp16 (round to nearest, ties to even) and return the bit patterns.
+
+    numpy converts float64 to float16 in one correctly rounded step. Values at or
+    above 65520 in magnitude become +-inf, as IEEE rounding dictates.
+    """
+    a = np.asarray(values, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return a.astype(np.float16).view(np.uint16)
+
+
+def fp16_from_bits(bits):
+    """fp16 bit patterns (uint16) -> exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return b.view(np.float16).astype(np.float64)
+
+
+def e3m2_value(code):
+    """Value of one 6-bit e3m2 code ``s e2 e1 e0 m1 m0`` (closed form, exact in float64)."""
+    code = int(code)
+    if not 0 <= code < 64:
+        raise ValueError("e3m2 code out of range: %r" % code)
+    sign = -1.0 if (code >> 5) & 1 else 1.0
+    e = (code >> 2) & 7
+    m = code & 3
+    if e == 0:
+        mag = m * 2.0 ** (1 - E3M2_BIAS) / 4.0          # subnormal: 0.m x 2^(1-bias)
+    else:
+        mag = (1.0 + m / 4.0) * 2.0 ** (e - E3M2_BIAS)  # normal: 1.m x 2^(e-bias)
+    return sign * mag
+
+
+def e3m2_table():
+    """All 64 code values as float64 (code 32 is -0.0)."""
+    return np.array([e3m2_value(c) for c in range(64)], dtype=np.float64)
+
+
+def e3m2_encode(t):
+    """Encode float64 values as e3m2 codes: nearest magnitude, ties to the even code, saturating.
+
+    The sign bit is the sign bit of ``t`` (so a negative value that rounds to zero gives
+    code 32, i.e. -0). The magnitude code is the one among the 32 non-negative values
+    nearest to ``|t|``; when two are equally near, the one with an even code wins.
+    Magnitudes above 28 are nearest to 28 and so saturate there. This is written as a
+    brute-force search over all 32 magnitudes, not as bit manipulation.
+    """
+    t = np.asarray(t, dtype=np.float64)
+    if not np.all(np.isfinite(t)):
+        raise ValueError("e3m2_encode: non-finite input")
+    mags = e3m2_table()[:32].reshape(1, -1)       # increasing: 0, 1/16, ..., 28
+    even = (np.arange(32) % 2 == 0).reshape(1, -1)
+    flat = t.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 1 << 16
+    for i in range(0, flat.size, step):
+        # above 28 every magnitude is nearest to 28; clamping first keeps the float64
+        # distances below exact (Sterbenz) so that a tie is found only where one exists
+        a = np.minimum(np.abs(flat[i:i + step]), E3M2_MAX).reshape(-1, 1)
+        dist = np.abs(a - mags)
+        is_min = dist == dist.min(axis=1, keepdims=True)
+        # at most two codes tie and they are adjacent, so exactly one of them is even
+        n_min = is_min.sum(axis=1)
+        mag_code = np.where(n_min > 1, np.argmax(is_min & even, axis=1), np.argmax(is_min, axis=1))
+        sign = np.signbit(flat[i:i + step]).astype(np.uint8)
+        out[i:i + step] = mag_code.astype(np.uint8) | (sign << 5)
+    return out.reshape(t.shape)

@@ -1,0 +1,201 @@
+"""The packed byte layout of the quantized weights, written twice: bit by bit and vectorised.
+
+Test infrastructure only (see the package docstring for who may import it).
+
+The FP6-LLM news page (m.zhengruan.com), section "重新设计内核方案", says that 6-bit
+weights fit a memory system built on 32/64-bit accesses badly, and that they are
+therefore re-packed before inference into aligned blocks, in the order in which the
+kernel consumes them. It gives no concrete layout. The layout used here is:
+
+* Rows are stored one after another (output row n first). Row n holds K codes, cut
+  into units of 32 consecutive K (unit u covers k = 32u .. 32u+31). Units follow one
+  another with no padding, so a row is exactly K*bits/8 bytes and the whole array is
+  exactly N*K*bits/8 bytes.
+* Inside a unit, for code j (k = 32u + j):
+    - W8 (32 bytes): byte j holds q_j + 128 (offset binary; q in -127..127).
+    - W4 (16 bytes): four little-endian 32-bit words. Word d holds codes 8d .. 8d+7.
+      Code 8d+2t sits in nibble t and code 8d+2t+1 in nibble t+4 (t = 0..3), nibble p
+      being bits 4p .. 4p+3 of the word.
+    - W6 (24 bytes): one 192-bit little-endian number; code j sits in bits 6j .. 6j+5.
+    - F16 (64 bytes, the unquantized baseline): bytes 2j, 2j+1 hold the fp16 bits of
+      weight j, little-endian.
+* Metadata stays in logical order: W8/W6 scales [N]; W4 scales and zeros [N][K/32],
+  row-major (group g of row n covers the same 32 K as unit g).
+
+Codes given to and returned by these functions are the logical codes: int8 q for W8,
+0..15 for W4, 0..63 for W6, uint16 fp16 bits for F16.
+"""
+
+import numpy as np
+
+FMT_F16 = 0
+FMT_W8 = 1
+FMT_W4G32 = 2
+FMT_W6E3M2 = 3
+
+_BITS = {FMT_F16: 16, FMT_W8: 8, FMT_W4G32: 4, FMT_W6E3M2: 6}
+UNIT = 32
+
+
+def _bits(fmt):
+    if fmt not in _BITS:
+        raise ValueError("unknown format %r" % fmt)
+    return _BITS[fmt]
+
+
+def unit_bytes(fmt):
+    return UNIT * _bits(fmt) // 8
+
+
+def packed_bytes(fmt, n, k):
+    return n * k * _bits(fmt) // 8
+
+
+def scales_count(fmt, n, k):
+    """Number of fp16 scales."""
+    _bits(fmt)
+    if fmt == FMT_F16:
+        return 0
+    return n * (k // 32) if fmt == FMT_W4G32 else n
+
+
+def zeros_count(fmt, n, k):
+    """Number of fp16 zero points."""
+    _bits(fmt)
+    return n * (k // 32) if fmt == FMT_W4G32 else 0
+
+
+def code_field(fmt, j):
+    """(first bit, width) of code j inside its unit, counting bits little-endian from the unit's first byte."""
+    if fmt == FMT_W8:
+        return 8 * j, 8
+    if fmt == FMT_W4G32:
+        d, i = divmod(j, 8)
+        t, odd = divmod(i, 2)
+        nibble = t + 4 * odd
+        return 32 * d + 4 * nibble, 4
+    if fmt == FMT_W6E3M2:
+        return 6 * j, 6
+    if fmt == FMT_F16:
+        return 16 * j, 16
+    raise ValueError("unknown format %r" % fmt)
+
+
+def _stored(fmt, code):
+    """The unsigned field value stored for one logical code."""
+    code = int(code)
+    if fmt == FMT_W8:
+        if not -127 <= code <= 127:
+            raise ValueError("int8 code out of range")
+        return code + 128
+    limit = {FMT_W4G32: 16, FMT_W6E3M2: 64, FMT_F16: 65536}[fmt]
+    if not 0 <= code < limit:
+        raise ValueError("code out of range")
+    return code
+
+
+def _logical(fmt, field):
+    return field - 128 if fmt == FMT_W8 else field
+
+
+def _check_shape(codes, k):
+    if k % UNIT:
+        raise ValueError("K must be a multiple of 32")
+    return codes
+
+
+def pack_scalar(fmt, codes):
+    """Bit-writer: pack logical codes [N,K] one code at a time. Slow; for small arrays."""
+    codes = np.asarray(codes)
+    n, k = codes.shape
+    _check_shape(codes, k)
+    ub = unit_bytes(fmt)
+    out = bytearray(packed_bytes(fmt, n, k))
+    for r in range(n):
+        for u in range(k // UNIT):
+            acc = 0
+            for j in range(UNIT):
+                first, width = code_field(fmt, j)
+                v = _stored(fmt, codes[r, UNIT * u + j])
+                for b in range(width):
+                    if (v >> b) & 1:
+                        acc |= 1 << (first + b)
+            off = (r * (k // UNIT) + u) * ub
+            out[off:off + ub] = acc.to_bytes(ub, "little")
+    return np.frombuffer(bytes(out), dtype=np.uint8).copy()
+
+
+def unpack_scalar(fmt, packed, n, k):
+    """Bit-reader: the inverse of pack_scalar."""
+    packed = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    if packed.size != packed_bytes(fmt, n, k):
+        raise ValueError("packed size mismatch")
+    ub = unit_bytes(fmt)
+    dtype = {FMT_W8: np.int8, FMT_W4G32: np.uint8, FMT_W6E3M2: np.uint8, FMT_F16: np.uint16}[fmt]
+    codes = np.zeros((n, k), dtype=dtype)
+    for r in range(n):
+        for u in range(k // UNIT):
+            off = (r * (k // UNIT) + u) * ub
+            acc = int.from_bytes(bytes(packed[off:off + ub]), "little")
+            for j in range(UNIT):
+                first, width = code_field(fmt, j)
+                codes[r, UNIT * u + j] = _logical(fmt, (acc >> first) & ((1 << width) - 1))
+    return codes
+
+
+# ---- vectorised packer / unpacker: the same layout, computed with whole-array ops ----
+# W4: slot p of a 32-bit word holds code order[p]; W6: every 4 codes fill 3 whole bytes.
+_W4_ORDER = np.array([0, 2, 4, 6, 1, 3, 5, 7])
+
+
+def pack_vectorized(fmt, codes):
+    codes = np.asarray(codes)
+    n, k = codes.shape
+    _check_shape(codes, k)
+    if fmt == FMT_W8:
+        c = codes.astype(np.int16)
+        if c.min(initial=0) < -127 or c.max(initial=0) > 127:
+            raise ValueError("int8 code out of range")
+        return (c + 128).astype(np.uint8).reshape(-1)
+    if fmt == FMT_W4G32:
+        c = codes.astype(np.uint32)
+        if c.max(initial=0) > 15:
+            raise ValueError("int4 code out of range")
+        c = c.reshape(n, k // 8, 8)[:, :, _W4_ORDER]          # slot p <- code order[p]
+        words = np.zeros((n, k // 8), dtype=np.uint32)
+        for p in range(8):
+            words |= c[:, :, p] << np.uint32(4 * p)
+        return words.astype("<u4").view(np.uint8).reshape(-1)
+    if fmt == FMT_W6E3M2:
+        c = codes.astype(np.uint32)
+        if c.max(initial=0) > 63:
+            raise ValueError("fp6 code out of range")
+        c = c.reshape(n, k // 4, 4)
+        v = c[:, :, 0] | (c[:, :, 1] << 6) | (c[:, :, 2] << 12) | (c[:, :, 3] << 18)
+        b = np.stack([v & 0xFF, (v >> 8) & 0xFF, (v >> 16) & 0xFF], axis=-1).astype(np.uint8)
+        return b.reshape(-1)
+    if fmt == FMT_F16:
+        return codes.astype(np.uint16).astype("<u2").view(np.uint8).reshape(-1)
+    raise ValueError("unknown format %r" % fmt)
+
+
+def unpack_vectorized(fmt, packed, n, k):
+    packed = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    if packed.size != packed_bytes(fmt, n, k):
+        raise ValueError("packed size mismatch")
+    if fmt == FMT_W8:
+        return (packed.astype(np.int16) - 128).astype(np.int8).reshape(n, k)
+    if fmt == FMT_W4G32:
+        words = packed.view("<u4").reshape(n, k // 8)
+        out = np.zeros((n, k // 8, 8), dtype=np.uint8)
+        for p in range(8):
+            out[:, :, _W4_ORDER[p]] = (words >> np.uint32(4 * p)) & 0xF
+        return out.reshape(n, k)
+    if fmt == FMT_W6E3M2:
+        b = packed.reshape(n, k // 4, 3).astype(np.uint32)
+        v = b[:, :, 0] | (b[:, :, 1] << 8) | (b[:, :, 2] << 16)
+        out = np.stack([(v >> s) & 0x3F for s in (0, 6, 12, 18)], axis=-1).astype(np.uint8)
+        return out.reshape(n, k)
+    if fmt == FMT_F16:
+        return packed.view("<u2").reshape(n, k).astype(np.uint16)
+    raise ValueError("unknown format %r" % fmt)

@@ -1,0 +1,90 @@
+"""Dequantisation to fp16 and the reference linear layer.
+
+Test infrastructure only (see the package docstring for who may import it).
+
+The FP6-LLM news page (m.zhengruan.com), section "重新设计内核方案", describes the
+computation: the low-bit weights are turned back into fp16 values and the layer is then
+an fp16 matrix product, ``y = x . W^T``. The pages do not state a precision for the
+product. The reading used here is fp32 accumulation with fp16 inputs and outputs. The
+reference below is therefore the exact sum, computed in float64, of the fp16 inputs
+times the fp16 dequantised weights. A device result is accepted when it lies within the
+bound given by ``error_bound``.
+"""
+
+import numpy as np
+
+from .formats import fp16_bits, fp16_from_bits, e3m2_table
+from .layout import FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, pack_vectorized
+from .quantize import quantize_int8, quantize_int4_g32, quantize_fp6
+
+
+def dequant_fp16(fmt, codes, scales=None, zeros=None):
+    """Logical codes + fp16 metadata bits -> dequantised weights as fp16 bits [N,K].
+
+    W8: fp16(q * s). W4: fp16((q - z) * s) with s, z of the weight's group.
+    W6: fp16(e3m2(c) * s). F16: the weights themselves.
+    Each product is formed exactly in float64 (the factors have at most 11 and 8
+    significant bits) and then rounded once to fp16.
+    """
+    codes = np.asarray(codes)
+    n, k = codes.shape
+    if fmt == FMT_F16:
+        return codes.astype(np.uint16)
+    s = fp16_from_bits(scales)
+    if fmt == FMT_W8:
+        v = codes.astype(np.float64) * s.reshape(n, 1)
+    elif fmt == FMT_W4G32:
+        z = fp16_from_bits(zeros).reshape(n, k // 32, 1)
+        q = codes.astype(np.float64).reshape(n, k // 32, 32)
+        v = ((q - z) * s.reshape(n, k // 32, 1)).reshape(n, k)
+    elif fmt == FMT_W6E3M2:
+        v = e3m2_table()[codes.astype(np.int64)] * s.reshape(n, 1)
+    else:
+        raise ValueError("unknown format %r" % fmt)
+    return fp16_bits(v)
+
+
+def linear_ref(x_bits, w_bits):
+    """y[m,n] = sum_k x[m,k] * w[n,k] in float64, for fp16 bit inputs x [M,K] and w [N,K]."""
+    x = fp16_from_bits(x_bits)
+    w = fp16_from_bits(w_bits)
+    return x @ w.T
+
+
+def error_bound(x_bits, w_bits, y_ref):
+    """Largest error allowed for a device output, element by element.
+
+    With fp16 inputs, fp32 accumulation over K terms and one final rounding to fp16,
+    a result is accepted when
+        |y - y_ref| <= 2^-11 |y_ref| + (2^-11 + K 2^-23) S + 2^-25 A + 2^-24
+    where S = sum_k |x w| and A = sum_k |x|. The terms cover: the output rounding; a
+    per-row or per-group scale applied after the sum instead of to every weight; the
+    fp32 summation in any order; fp16 subnormal weights; a subnormal output.
+    """
+    x = np.abs(fp16_from_bits(x_bits))
+    w = np.abs(fp16_from_bits(w_bits))
+    k = x.shape[1]
+    s = x @ w.T
+    a = x.sum(axis=1, keepdims=True)
+    return 2.0 ** -11 * np.abs(y_ref) + (2.0 ** -11 + k * 2.0 ** -23) * s + 2.0 ** -25 * a + 2.0 ** -24
+
+
+def quantize_and_pack(fmt, w):
+    """fp32 W [N,K] -> (packed bytes, scale bits, zero bits, logical codes), all as numpy arrays."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    if fmt == FMT_W8:
+        codes, s = quantize_int8(w)
+        z = np.zeros(0, dtype=np.uint16)
+    elif fmt == FMT_W4G32:
+        codes, s, z = quantize_int4_g32(w)
+    elif fmt == FMT_W6E3M2:
+        codes, s = quantize_fp6(w)
+        z = np.zeros(0, dtype=np.uint16)
+    elif fmt == FMT_F16:
+        codes = fp16_bits(w.astype(np.float64))
+        s = np.zeros(0, dtype=np.uint16)
+        z = np.zeros(0, dtype=np.uint16)
+    else:
+        raise ValueError("unknown format %r" % fmt)
+    return pack_vectorized(fmt, codes), s, z, codes

@@ -1,0 +1,273 @@
+"""Independent checks that pin the CPU oracle to something other than itself.
+
+Nothing here calls the oracle's own arithmetic. These are exact-rational (Fraction)
+statements of the definitions, brute-force searches over every code, and fixtures
+typed by hand under tests/golden/. Each ``check_*`` takes the function under test as
+an argument, so the same predicate both accepts the oracle and rejects planted
+mistakes (see test_oracle_mutations.py).
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------- exact rounding
+def rint_even(fr):
+    """Nearest integer to a Fraction, ties to even."""
+    fl = math.floor(fr)
+    rem = fr - fl
+    if rem > Fraction(1, 2):
+        return fl + 1
+    if rem < Fraction(1, 2):
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+def fp16_round(fr):
+    """Round a Fraction to the nearest fp16 value (ties to even). Returns a Fraction, or +-inf as float."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    # fix e so that 2^e <= a < 2^(e+1) exactly
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -14)                                  # below 2^-14 the spacing stays 2^-24
+    quantum = Fraction(2) ** (e - 10)
+    n = rint_even(a / quantum)
+    v = n * quantum
+    if v >= 65536 or (v == 65536):
+        return sign * math.inf
+    if v > 65504:                                    # rounds past the largest finite value
+        return sign * math.inf
+    return sign * v
+
+
+def f16_bits_to_fraction(b):
+    b = int(b)
+    s = -1 if b >> 15 else 1
+    e = (b >> 10) & 31
+    m = b & 1023
+    if e == 0:
+        return s * Fraction(m, 1 << 24)
+    assert e != 31
+    return s * Fraction(1024 + m, 1 << 10) * Fraction(2) ** (e - 15)
+
+
+def fraction_to_f16_bits(v):
+    """Exact fp16 value (Fraction, or inf) -> bit pattern; v must be representable."""
+    if isinstance(v, float) and math.isinf(v):
+        return 0x7C00 if v > 0 else 0xFC00
+    return int(np.float16(float(v)).view(np.uint16))  # float(v) is exact for fp16 values
+
+
+# ---------------------------------------------------------------- e3m2 from the golden table
+def golden_e3m2():
+    """64 magnitudes as Fractions with the sign of each code: (value, negative?)."""
+    rows = []
+    with open(os.path.join(GOLDEN, "e3m2_table.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([Fraction(t) for t in line.split()])
+    assert len(rows) == 8 and all(len(r) == 4 for r in rows)
+    mags = [rows[c >> 2][c & 3] for c in range(32)]
+    return [(mags[c & 31], bool(c & 32)) for c in range(64)]
+
+
+def check_e3m2_table(value_fn):
+    """value_fn(code) must equal the hand-typed table, with -0 for code 32."""
+    for c, (mag, neg) in enumerate(golden_e3m2()):
+        v = value_fn(c)
+        if Fraction(v) != (-mag if neg else mag):
+            return False
+        if math.copysign(1.0, v) != (-1.0 if neg else 1.0):
+            return False
+    return True
+
+
+# ---------------------------------------------------------------- brute-force quantizers
+def brute_fp6_code(t):
+    """Nearest e3m2 code to a float t: sign from t's sign bit, nearest magnitude, ties to even code."""
+    tab = golden_e3m2()
+    neg = math.copysign(1.0, t) < 0
+    ft = abs(Fraction(t))
+    best = None
+    for c in range(32):
+        d = abs(ft - tab[c][0])
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1] | (32 if neg else 0)
+
+
+def brute_int8_row(w_row):
+    """(codes, scale bits) for one fp32 row, by exact arithmetic and search over -127..127."""
+    amax = max(abs(Fraction(float(v))) for v in w_row)
+    s = fp16_round(amax / 127)
+    if s == 0:
+        return [0] * len(w_row), 0
+    codes = []
+    for v in w_row:
+        fv = Fraction(float(v))
+        best = None
+        for q in range(-127, 128):
+            d = abs(fv - q * s)
+            if best is None or d < best[0] or (d == best[0] and q % 2 == 0):
+                best = (d, q)
+        codes.append(best[1])
+    return codes, fraction_to_f16_bits(s)
+
+
+def brute_int4_group(w_grp):
+    """(codes, scale bits, zero bits) for one group of 32 fp32 weights."""
+    fw = [Fraction(float(v)) for v in w_grp]
+    lo = min(min(fw), Fraction(0))
+    hi = max(max(fw), Fraction(0))
+    s = fp16_round((hi - lo) / 15)
+    if s == 0:
+        return [0] * len(w_grp), 0, 0
+    # zero point: the integer 0..15 nearest to -lo/s, ties to even
+    best = None
+    for z in range(16):
+        d = abs(-lo / s - z)
+        if best is None or d < best[0] or (d == best[0] and z % 2 == 0):
+            best = (d, z)
+    z = best[1]
+    codes = []
+    for fv in fw:
+        best = None
+        for q in range(16):
+            d = abs(fv / s - (q - z))
+            if best is None or d < best[0] or (d == best[0] and (q - z) % 2 == 0):
+                best = (d, q)
+        codes.append(best[1])
+    return codes, fraction_to_f16_bits(s), fraction_to_f16_bits(Fraction(z))
+
+
+def brute_fp6_row(w_row):
+    """(codes, scale bits) for one fp32 row: exact quotient w/s, nearest e3m2 magnitude, ties to even code."""
+    amax = max(abs(Fraction(float(v))) for v in w_row)
+    s = fp16_round(amax / 28)
+    if s == 0:
+        return [0] * len(w_row), 0
+    tab = golden_e3m2()
+    codes = []
+    for v in w_row:
+        a = abs(Fraction(float(v))) / s
+        best = None
+        for c in range(32):
+            d = abs(a - tab[c][0])
+            if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+                best = (d, c)
+        codes.append(best[1] | (32 if math.copysign(1.0, float(v)) < 0 else 0))
+    return codes, fraction_to_f16_bits(s)
+
+
+def check_quantizer(fmt_name, quant_fn, w):
+    """Compare quant_fn(w) with the brute-force exact quantizer on every row (and group)."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    out = quant_fn(w)
+    if fmt_name == "w8":
+        q, s = out
+        for r in range(n):
+            bq, bs = brute_int8_row(w[r])
+            if int(s[r]) != bs or [int(v) for v in q[r]] != bq:
+                return False
+        return True
+    if fmt_name == "w4":
+        q, s, z = out
+        s = np.asarray(s).reshape(n, k // 32)
+        z = np.asarray(z).reshape(n, k // 32)
+        for r in range(n):
+            for g in range(k // 32):
+                bq, bs, bz = brute_int4_group(w[r, 32 * g:32 * g + 32])
+                if int(s[r, g]) != bs or int(z[r, g]) != bz:
+                    return False
+                if [int(v) for v in q[r, 32 * g:32 * g + 32]] != bq:
+                    return False
+        return True
+    if fmt_name == "w6":
+        q, s = out
+        for r in range(n):
+            bq, bs = brute_fp6_row(w[r])
+            if int(s[r]) != bs or [int(v) for v in q[r]] != bq:
+                return False
+        return True
+    raise ValueError(fmt_name)
+
+
+# ---------------------------------------------------------------- packing fixtures
+def golden_pack_examples():
+    """[(fmt name, codes list, expected bytes)] from tests/golden/pack_examples.txt."""
+    out = []
+    with open(os.path.join(GOLDEN, "pack_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, codes, hexbytes = [p.strip() for p in line.split("|")]
+            if name == "F16":
+                cl = [int(t, 16) for t in codes.split()]
+            else:
+                cl = [int(t) for t in codes.split()]
+            out.append((name, cl, bytes(int(t, 16) for t in hexbytes.split())))
+    return out
+
+
+# ---------------------------------------------------------------- exact linear and dequant
+def exact_dequant(fmt_name, code, scale_bits, zero_bits=0):
+    """Exact dequantized value (Fraction) rounded once to fp16, returned as bits."""
+    s = f16_bits_to_fraction(scale_bits)
+    if fmt_name == "w8":
+        v = code * s
+    elif fmt_name == "w4":
+        v = (code - f16_bits_to_fraction(zero_bits)) * s
+    elif fmt_name == "w6":
+        mag, neg = golden_e3m2()[code]
+        v = (-mag if neg else mag) * s
+        if v == 0:
+            return 0x8000 if (neg and s > 0) or (not neg and s < 0) else 0
+    else:
+        raise ValueError(fmt_name)
+    r = fp16_round(v)
+    if r == 0:
+        return 0x8000 if v < 0 else 0
+    return fraction_to_f16_bits(r)
+
+
+def exact_linear(x_bits, w_bits):
+    """y[m][n] = sum_k x*w as exact Fractions, by a plain triple loop."""
+    m, k = x_bits.shape
+    n = w_bits.shape[0]
+    y = [[Fraction(0)] * n for _ in range(m)]
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for t in range(k):
+                acc += f16_bits_to_fraction(x_bits[i, t]) * f16_bits_to_fraction(w_bits[j, t])
+            y[i][j] = acc
+    return y
+
+
+def check_linear(linear_fn, x_bits, w_bits):
+    """linear_fn(x, w) (float64) must equal the exact sum to within float64 rounding."""
+    y = np.asarray(linear_fn(x_bits, w_bits), dtype=np.float64)
+    ye = exact_linear(x_bits, w_bits)
+    if y.shape != (x_bits.shape[0], w_bits.shape[0]):
+        return False
+    k = x_bits.shape[1]
+    for i in range(y.shape[0]):
+        for j in range(y.shape[1]):
+            mag = sum(abs(f16_bits_to_fraction(x_bits[i, t]) * f16_bits_to_fraction(w_bits[j, t])) for t in range(k))
+            if abs(Fraction(float(y[i, j])) - ye[i][j]) > mag * Fraction(k + 1, 2 ** 52):
+                return False
+    return True

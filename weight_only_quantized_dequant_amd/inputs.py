@@ -1,0 +1,57 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle checks.
+
+This module holds random-number generation and shapes only. It does no
+quantization, packing, rounding rule or product of the method. Both sides (the device
+path and the CPU oracle) receive the same arrays from here.
+
+Weights are ``0.02 * N(0,1)`` in fp32 and activations are ``N(0,1)`` rounded to fp16.
+This is the random-init stand-in for trained Llama weights: the device path has no
+data-dependent branches, so time depends only on shapes and bytes.
+"""
+
+import numpy as np
+
+SEED = 0
+
+# Linear shapes (N, K) of the decode layers, by model.
+LLAMA2_7B_LINEARS = [
+    ("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
+    ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008),
+]
+LLAMA_70B_LINEARS = [
+    ("q", 8192, 8192), ("k", 1024, 8192), ("v", 1024, 8192), ("o", 8192, 8192),
+    ("gate", 28672, 8192), ("up", 28672, 8192), ("down", 8192, 28672),
+]
+
+# Named workloads: format name, list of (N, K), list of M.
+WORKLOADS = {
+    "w8_single_1024x1024": ("w8", [(1024, 1024)], [1]),
+    "llama7b_w4g32_linears": ("w4g32", [(4096, 4096), (11008, 4096), (4096, 11008)], [1]),
+    "llama70b_w6e3m2_linears": ("w6e3m2", [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)], [1, 4, 8, 16]),
+}
+# stream index of each workload, so that every workload draws from its own stream
+WORKLOAD_STREAM = {"w8_single_1024x1024": 0, "llama7b_w4g32_linears": 1, "llama70b_w6e3m2_linears": 2}
+
+
+def rng_for(stream, linear):
+    """The generator for one linear of one workload."""
+    return np.random.default_rng([SEED, stream, linear])
+
+
+def weights_and_x(rng, n, k, m):
+    """Draw W (fp32 [n,k]) first, then x (fp16 bits [m,k]), from one generator."""
+    w = 0.02 * rng.standard_normal((n, k), dtype=np.float32)
+    x = rng.standard_normal((m, k), dtype=np.float32).astype(np.float16).view(np.uint16)
+    return w.astype(np.float32), x
+
+
+def x_only(rng, m, k):
+    return rng.standard_normal((m, k), dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def small_case(seed, n, k, m, scale=0.02):
+    """A small seeded case for parity tests."""
+    rng = np.random.default_rng([SEED, 100, seed])
+    w = (scale * rng.standard_normal((n, k), dtype=np.float32)).astype(np.float32)
+    x = rng.standard_normal((m, k), dtype=np.float32).astype(np.float16).view(np.uint16)
+    return w, x
