@@ -1,0 +1,124 @@
+/*
+ * wq.h -- C ABI of libwq: weight-only-quantized linear layers on AMD MI355X (gfx950).
+ *
+ * The operation is the linear layer of LLM decode with low-bit weights and fp16
+ * activations:  y[M,N] = x[M,K] . dequant(Wq)[N,K]^T  (fp16 in and out, fp32 sums).
+ *   - gpt-fast write-up (m.greenbasetech.com): decode is bound by memory bandwidth; the
+ *     lever is fewer bytes per parameter, first int8, then groupwise int4 weights.
+ *   - gpt-fast guide (www.jsqmd.com), section "量化技术深度解析": int4, group size 32.
+ *   - FP6-LLM news (m.zhengruan.com), section "重新设计内核方案": FP6 weights with fp16
+ *     activations; dequantization fused with the matrix product in one kernel, and the
+ *     weights re-packed offline into aligned 32/64-bit blocks.
+ *
+ * Formats (the pages give names, not bit formats; these are this library's readings):
+ *   WQ_FMT_W8      int8, symmetric, one fp16 scale per output row: s = fp16(max|w|/127),
+ *                  q = clamp(rint(w/s), -127, 127), w^ = q*s.
+ *   WQ_FMT_W4G32   int4, asymmetric, groups of 32 consecutive K: s = fp16((hi-lo)/15) with
+ *                  lo = min(min w, 0), hi = max(max w, 0); integer zero point
+ *                  z = clamp(rint(-lo/s), 0, 15) stored as fp16; q = clamp(rint(w/s)+z, 0, 15);
+ *                  w^ = (q-z)*s.
+ *   WQ_FMT_W6E3M2  FP6 e3m2 (sign, 3 exponent bits with bias 3, 2 mantissa bits, subnormals,
+ *                  no inf/NaN, max 28), one fp16 scale per row: s = fp16(max|w|/28), code =
+ *                  nearest e3m2 to w/s (ties to even code, saturating); w^ = e3m2(code)*s.
+ *   WQ_FMT_F16     plain fp16 weights W[N,K] (the unquantized baseline); no metadata.
+ *   Quotients are IEEE float64 operations; rint and fp16 conversion round to nearest even.
+ *   A scale that rounds to 0 makes the codes of its row or group 0 (and z = 0).
+ *
+ * Packed layout (identical for host and device): rows one after another; row n holds
+ * K codes cut into units of 32 consecutive K, each unit stored whole, no padding:
+ *   W8  32 B: byte j = q_j + 128.
+ *   W4  16 B: four little-endian u32; word d holds codes 8d..8d+7, code 8d+2t in nibble t,
+ *             code 8d+2t+1 in nibble t+4.
+ *   W6  24 B: code j in bits 6j..6j+5 of the unit read as a 192-bit little-endian number.
+ *   F16 64 B: fp16 weight j at bytes 2j..2j+1.
+ * So packed_w is exactly N*K*bits/8 bytes. scales: W8/W6 [N]; W4 [N][K/32] row-major.
+ * zeros: W4 [N][K/32] row-major; otherwise unused (may be NULL). fp16 values are passed
+ * as uint16_t bit patterns.
+ *
+ * Conventions for every call:
+ *   - K must be a positive multiple of 32; N >= 1; M >= 1. Otherwise WQ_ERR_SHAPE.
+ *   - Every error is returned synchronously, before anything is launched. The device
+ *     calls never synchronize; a fault in a kernel shows up at the caller's next sync.
+ *   - Memory is owned by the caller. The library allocates no device memory, keeps no
+ *     state between calls and may be called from several host threads at once.
+ *   - stream is a hipStream_t (NULL = the legacy default stream).
+ */
+#ifndef WQ_H_
+#define WQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { WQ_FMT_F16 = 0, WQ_FMT_W8 = 1, WQ_FMT_W4G32 = 2, WQ_FMT_W6E3M2 = 3 } wq_fmt;
+
+typedef enum {
+  WQ_OK = 0,
+  WQ_ERR_ARG = -1,        /* NULL pointer or a negative size                        */
+  WQ_ERR_SHAPE = -2,      /* K not a positive multiple of 32, N < 1 or M < 1         */
+  WQ_ERR_FMT = -3,        /* unknown format code                                     */
+  WQ_ERR_NONFINITE = -4,  /* a weight given to a packer is NaN or infinite           */
+  WQ_ERR_ALIGN = -5,      /* a device pointer is not 16-byte aligned                 */
+  WQ_ERR_DEVICE = -6,     /* the HIP runtime refused the launch                      */
+  WQ_ERR_RANGE = -7       /* a scale would overflow fp16 (max|w| too large)          */
+} wq_status;
+
+/* Library version, (major << 16) | minor. */
+int wq_version(void);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* wq_status_string(int status);
+
+/* Sizes in bytes of packed_w, scales and zeros for (fmt, N, K); 0 for an invalid
+ * combination (unknown fmt, N < 1, K not a positive multiple of 32) or, for zeros, a
+ * format without zero points. Host only. */
+size_t wq_packed_bytes(int fmt, int64_t N, int64_t K);
+size_t wq_scales_bytes(int fmt, int64_t N, int64_t K);
+size_t wq_zeros_bytes(int fmt, int64_t N, int64_t K);
+
+/* Offline quantize + pack, on the host (the FP6-LLM page re-packs weights before
+ * inference). w: host fp32 W[N,K], row-major. packed, scales, zeros: host buffers of
+ * the sizes above, written completely. Rows are processed in parallel on host threads.
+ * Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_NONFINITE, WQ_ERR_RANGE; on error the output
+ * buffers hold unspecified bytes. */
+int wq_pack_int8(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
+int wq_pack_int4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales, uint16_t* zeros);
+int wq_pack_fp6(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
+
+/* Inverse of the packers' layout step, on the host: packed -> logical codes [N,K]
+ * (int8 for W8; 0..15 for W4; 0..63 for W6, one byte each; uint16 fp16 bits for F16) and
+ * a copy of the metadata in logical order (scales_out/zeros_out may be NULL to skip).
+ * A test hook. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT. */
+int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,
+              void* codes, uint16_t* scales_out, uint16_t* zeros_out);
+
+/* On the device: dequantize packed weights to fp16 W^[N,K] row-major, w_out[n*K+k] =
+ * fp16(w^[n,k]) rounded once to nearest even (bit-exact by construction: each product
+ * is exact in fp32). All pointers are device pointers, 16-byte aligned; zeros only for
+ * W4. Asynchronous on stream. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT,
+ * WQ_ERR_ALIGN, WQ_ERR_DEVICE. */
+int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, uint16_t* w_out,
+               int64_t N, int64_t K, void* stream);
+
+/* On the device: y[M,N] = x[M,K] . dequant(packed_w)[N,K]^T with fp16 x and y (row-major,
+ * row strides K and N) and fp32 accumulation; the one fused kernel reads every packed
+ * byte once and never writes dequantized weights to memory. All pointers are device
+ * pointers, 16-byte aligned; zeros only for W4 (else may be NULL). M of any size; M up to
+ * 16 is one launch, larger M runs in slabs of 16 rows. y must not overlap the inputs.
+ * Asynchronous on stream. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT, WQ_ERR_ALIGN,
+ * WQ_ERR_DEVICE. */
+int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros, uint16_t* y,
+              int64_t M, int64_t N, int64_t K, int fmt, void* stream);
+
+/* Name of the kernel wq_linear launches for (fmt, M, N, K) (for profiles), or "" if the
+ * arguments are invalid. Host only; static storage. */
+const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H_ */

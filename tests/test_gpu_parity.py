@@ -1,0 +1,159 @@
+"""GPU parity: libwq's device path (through the C ABI) against the CPU oracle.
+
+* wq_dequant: bit-exact fp16 patterns (+-0 included) for every format.
+* wq_linear: within the oracle's closed-form error bound and rtol = atol = 1e-2, for
+  every M in 1..16 (and slabs above 16), ragged N and K, one-hot x bit-exact, x = 0
+  exact, and repeat calls bit-identical.
+* The workloads at full size, in the launch configuration the benchmark times, on
+  sampled output rows that the oracle computes row by row.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_quantized_dequant_amd import inputs, wq
+from tests.gpu_util import DeviceWeights, check_linear, dev, host_bits, oracle_rows, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_F16]
+FMT_ID = {wq.FMT_W8: "w8", wq.FMT_W4G32: "w4", wq.FMT_W6E3M2: "w6", wq.FMT_F16: "f16"}
+
+
+def _weights(n, k, seed, adversarial=True):
+    w, _ = inputs.small_case(seed, n, k, 1)
+    if adversarial and n >= 8:
+        w[0, :] = 0.0                       # zero row: scale 0
+        w[1, 3] = 0.7                       # one outlier
+        w[2, :] = np.abs(w[2, :])           # one-signed rows / groups
+        w[3, :] = -np.abs(w[3, :])
+        w[4, :32] = 1e-9                    # subnormal scale
+        w[5, :] *= 1e-4                     # subnormal dequantized values
+        w[6, 1] = -0.0
+    return w
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("n,k", [(1, 32), (15, 64), (17, 96), (64, 4096), (1000, 2080)])
+def test_dequant_bit_exact(fmt, n, k):
+    torch_cuda()
+    w = _weights(n, k, n + k)
+    dw = DeviceWeights(fmt, w)
+    got = dw.dequant()
+    if fmt == wq.FMT_F16:
+        want = w.astype(np.float16).view(np.uint16)
+    else:
+        want, _, _, _ = oracle_rows(fmt, w)
+    assert np.array_equal(got, want), "%d of %d differ" % (int((got != want).sum()), got.size)
+
+
+def test_dequant_w6_all_codes():
+    # every one of the 64 codes, at scale 1 and at a non-power-of-two scale
+    torch = torch_cuda()
+    codes = np.tile(np.arange(64, dtype=np.uint8), 2).reshape(2, 64)
+    packed = oracle.pack_vectorized(wq.FMT_W6E3M2, codes)
+    for s in (0x3C00, 0x2E66):
+        sc = np.array([s, s], dtype=np.uint16)
+        out = torch.empty((2, 64), dtype=torch.int16, device="cuda:0")
+        wq.wq_dequant(wq.FMT_W6E3M2, dev(packed), dev(sc), None, out, 2, 64)
+        torch.cuda.synchronize()
+        want = oracle.dequant_fp16(wq.FMT_W6E3M2, codes, sc)
+        assert np.array_equal(host_bits(out), want)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("m", list(range(1, 17)))
+def test_linear_every_m(fmt, m):
+    # 37 rows (ragged against 4-row and 16-row blocks); K = 4256 = 133 units: 3 chunks of
+    # 64 units, the last ragged, and 34 K tiles of 4 units, the last ragged
+    n, k = 37, 4256
+    w = _weights(n, k, 7)
+    _, x = inputs.small_case(1000 + m, 1, k, m)
+    dw = DeviceWeights(fmt, w)
+    wd = w.astype(np.float16).view(np.uint16) if fmt == wq.FMT_F16 else oracle_rows(fmt, w)[0]
+    y = dw.linear(x)
+    check_linear(y, x, wd, "fmt %d m %d" % (fmt, m))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("n,k,m", [(1, 32, 1), (1, 32, 16), (3, 64, 2), (16, 128, 5), (33, 2048, 1), (33, 2048, 9),
+                                   (130, 8192, 1), (130, 8192, 16), (5, 96, 37), (64, 1024, 20)])
+def test_linear_shapes(fmt, n, k, m):
+    w = _weights(n, k, 3 * n + k)
+    _, x = inputs.small_case(2000 + n + m, 1, k, m)
+    dw = DeviceWeights(fmt, w)
+    wd = w.astype(np.float16).view(np.uint16) if fmt == wq.FMT_F16 else oracle_rows(fmt, w)[0]
+    check_linear(dw.linear(x), x, wd, "fmt %d n %d k %d m %d" % (fmt, n, k, m))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("m", [1, 3, 16])
+def test_linear_one_hot_is_bit_exact(fmt, m):
+    # x = e_k in every row: y[:, n] must equal the dequantized weight w^[n, k] exactly
+    n, k = 40, 2080
+    w = _weights(n, k, 11)
+    dw = DeviceWeights(fmt, w)
+    wd = w.astype(np.float16).view(np.uint16) if fmt == wq.FMT_F16 else oracle_rows(fmt, w)[0]
+    for kk in (0, 31, 32, 1000, k - 1):
+        x = np.zeros((m, k), dtype=np.float16)
+        x[:, kk] = 1.0
+        y = dw.linear(x.view(np.uint16))
+        want = np.tile(wd[:, kk], (m, 1))
+        same = (y == want) | ((y & 0x7FFF) == 0) & ((want & 0x7FFF) == 0)   # +-0 both mean zero in a sum
+        assert same.all(), (kk, np.argwhere(~same)[:3].tolist())
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+def test_linear_zero_x_and_repeatability(fmt):
+    n, k = 70, 4096
+    w = _weights(n, k, 13)
+    dw = DeviceWeights(fmt, w)
+    for m in (1, 16):
+        y0 = dw.linear(np.zeros((m, k), dtype=np.uint16))
+        assert np.all((y0 & 0x7FFF) == 0)
+        _, x = inputs.small_case(77, 1, k, m)
+        ys = [dw.linear(x) for _ in range(3)]
+        assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+
+
+def test_linear_rows_of_a_batch_match_single_rows():
+    n, k = 48, 4096
+    w = _weights(n, k, 21)
+    for fmt in (wq.FMT_W4G32, wq.FMT_W6E3M2):
+        dw = DeviceWeights(fmt, w)
+        _, x = inputs.small_case(5, 1, k, 16)
+        wd = oracle_rows(fmt, w)[0]
+        yb = dw.linear(x)
+        for i in (0, 7, 15):
+            yi = dw.linear(x[i:i + 1])
+            check_linear(yi, x[i:i + 1], wd)
+            check_linear(yb[i:i + 1], x[i:i + 1], wd)
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled rows)
+FULL = [
+    ("w8_single_1024x1024", wq.FMT_W8),
+    ("llama7b_w4g32_linears", wq.FMT_W4G32),
+    ("llama70b_w6e3m2_linears", wq.FMT_W6E3M2),
+]
+
+
+@pytest.mark.parametrize("name,fmt", FULL, ids=[f[0] for f in FULL])
+def test_workload_full_size_sampled(name, fmt):
+    _, shapes, ms = inputs.WORKLOADS[name]
+    stream = inputs.WORKLOAD_STREAM[name]
+    mmax = max(ms)
+    for li, (n, k) in enumerate(shapes):
+        w, x = inputs.weights_and_x(inputs.rng_for(stream, li), n, k, mmax)
+        dw = DeviceWeights(fmt, w)
+        rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(li).choice(n, 62, replace=False)]))
+        wd, codes, s, z = oracle_rows(fmt, w[rows])
+        # the library's packing of these rows equals the oracle's codes
+        lib_codes, _, _ = wq.wq_unpack(fmt, dw.packed_host, dw.scales_host, dw.zeros_host, n, k)
+        assert np.array_equal(lib_codes[rows], codes)
+        for m in ms:
+            y = dw.linear(x[:m])
+            check_linear(y[:, rows], x[:m], wd, "%s linear %d (%dx%d) m %d" % (name, li, n, k, m))
+        del dw
+        torch_cuda().cuda.empty_cache()

@@ -1,0 +1,210 @@
+"""CPU tests of libwq's host half: exported symbols, sizes, quantize+pack bit-identical to the oracle,
+unpack round trips and every synchronous error path. No GPU calls."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_quantized_dequant_amd import wq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(wq.LIB_PATH), reason="libwq.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "wq_linear" in names and "wq_pack_fp6" in names and len(names) >= 12
+    L = wq.lib()
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert wq.wq_version() >> 16 == 1
+    for s in range(-7, 1):
+        assert wq.wq_status_string(s) and wq.wq_status_string(s) != "unknown status"
+
+
+@pytest.mark.parametrize("fmt", [wq.FMT_F16, wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2])
+@pytest.mark.parametrize("n,k", [(1, 32), (7, 64), (33, 96), (4096, 11008)])
+def test_sizes_match_oracle(fmt, n, k):
+    assert wq.wq_packed_bytes(fmt, n, k) == oracle.packed_bytes(fmt, n, k)
+    assert wq.wq_scales_bytes(fmt, n, k) == 2 * oracle.scales_count(fmt, n, k)
+    assert wq.wq_zeros_bytes(fmt, n, k) == 2 * oracle.zeros_count(fmt, n, k)
+
+
+def test_sizes_reject_bad_shapes():
+    for fmt in range(4):
+        assert wq.wq_packed_bytes(fmt, 4, 48) == 0
+        assert wq.wq_packed_bytes(fmt, 0, 64) == 0
+        assert wq.wq_packed_bytes(fmt, 4, 0) == 0
+    assert wq.wq_packed_bytes(9, 4, 64) == 0
+
+
+def _adversarial(n, k, seed):
+    rng = np.random.default_rng(seed)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    if n >= 8:
+        w[0, :] = 0.0
+        w[1, 3] = 3.0
+        w[2, :] = np.abs(w[2, :])
+        w[3, :] = -np.abs(w[3, :])
+        w[4, :32] = 1e-9
+        w[5, 7] = -0.0
+        w[6, :] *= 1e-5
+        w[7, :32] = np.linspace(-1, 1, 32, dtype=np.float32)
+    return w
+
+
+def _exact_ties(fmt):
+    """Rows whose quotients w/s land exactly on rounding midpoints (scale 1 or 2^k)."""
+    rows = []
+    if fmt == wq.FMT_W8:
+        r = np.zeros(64, dtype=np.float32); r[0] = 127.0; r[1:9] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, -126.5]
+        rows.append(r)
+    if fmt == wq.FMT_W6E3M2:
+        r = np.zeros(64, dtype=np.float32); r[0] = 28.0
+        r[1:12] = [1.875, 0.03125, 0.09375, 26.0, -26.0, 5.5, -0.0, -0.01, 3.25, 0.40625, 14.999]
+        rows.append(r)
+    if fmt == wq.FMT_W4G32:
+        r = np.zeros(64, dtype=np.float32); r[0] = -7.5; r[1] = 7.5; r[2:6] = [0.5, 1.5, -0.5, 2.5]   # s = 1, z = 8 (7.5 -> even)
+        rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2])
+@pytest.mark.parametrize("n,k,seed", [(8, 64, 0), (9, 96, 1), (33, 128, 2), (300, 4096, 3)])
+def test_pack_bit_identical_to_oracle(fmt, n, k, seed):
+    w = _adversarial(n, k, seed)
+    packed_o, s_o, z_o, codes_o = oracle.quantize_and_pack(fmt, w)
+    if fmt == wq.FMT_W8:
+        packed, s = wq.wq_pack_int8(w)
+        z = None
+    elif fmt == wq.FMT_W4G32:
+        packed, s, z = wq.wq_pack_int4(w)
+    else:
+        packed, s = wq.wq_pack_fp6(w)
+        z = None
+    assert np.array_equal(packed, packed_o)
+    assert np.array_equal(s, s_o.reshape(-1))
+    if fmt == wq.FMT_W4G32:
+        assert np.array_equal(z, z_o.reshape(-1))
+    codes, s2, z2 = wq.wq_unpack(fmt, packed, s, z, n, k)
+    assert np.array_equal(codes, codes_o)
+    assert np.array_equal(s2, s)
+
+
+@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2])
+def test_pack_exact_ties_identical_to_oracle(fmt):
+    w = _exact_ties(fmt)
+    packed_o, s_o, z_o, _ = oracle.quantize_and_pack(fmt, w)
+    fn = {wq.FMT_W8: wq.wq_pack_int8, wq.FMT_W4G32: wq.wq_pack_int4, wq.FMT_W6E3M2: wq.wq_pack_fp6}[fmt]
+    out = fn(w)
+    assert np.array_equal(out[0], packed_o)
+    assert np.array_equal(out[1], s_o.reshape(-1))
+
+
+def test_pack_multithreaded_large_matches_oracle():
+    rng = np.random.default_rng(12)
+    w = (0.02 * rng.standard_normal((1024, 8192))).astype(np.float32)
+    for fmt, fn in ((wq.FMT_W8, wq.wq_pack_int8), (wq.FMT_W4G32, wq.wq_pack_int4)):
+        packed_o, s_o, z_o, _ = oracle.quantize_and_pack(fmt, w)
+        out = fn(w)
+        assert np.array_equal(out[0], packed_o)
+        assert np.array_equal(out[1], s_o.reshape(-1))
+    # fp6: the oracle's brute-force encoder is slow, so compare a row sample
+    packed, s = wq.wq_pack_fp6(w)
+    rows = rng.choice(1024, 24, replace=False)
+    packed_o, s_o, _, _ = oracle.quantize_and_pack(wq.FMT_W6E3M2, w[rows])
+    rb = 8192 * 3 // 4
+    got = np.concatenate([packed[r * rb:(r + 1) * rb] for r in rows])
+    assert np.array_equal(got, packed_o)
+    assert np.array_equal(s[rows], s_o)
+
+
+def test_unpack_f16_and_round_trip_of_oracle_packing():
+    rng = np.random.default_rng(5)
+    for fmt, codes in ((wq.FMT_W8, rng.integers(-127, 128, (3, 96)).astype(np.int8)),
+                       (wq.FMT_W4G32, rng.integers(0, 16, (3, 96)).astype(np.uint8)),
+                       (wq.FMT_W6E3M2, rng.integers(0, 64, (3, 96)).astype(np.uint8)),
+                       (wq.FMT_F16, rng.integers(0, 65536, (3, 96)).astype(np.uint16))):
+        packed = oracle.pack_scalar(fmt, codes)
+        got, _, _ = wq.wq_unpack(fmt, packed, np.zeros(9, np.uint16), np.zeros(9, np.uint16), 3, 96)
+        assert np.array_equal(got, codes)
+
+
+def test_scale_rounding_matches_oracle_over_magnitudes():
+    # scales span fp16 subnormals, normals and the edge of the range
+    mags = np.geomspace(1e-9, 1e6, 400).astype(np.float32)
+    w = np.zeros((400, 32), dtype=np.float32)
+    w[:, 0] = mags
+    w[:, 1] = -mags / 3
+    _, s = wq.wq_pack_int8(w)
+    _, s_o = oracle.quantize_int8(w)
+    assert np.array_equal(s, s_o)
+    ok = mags < 1.8e6
+    _, s6 = wq.wq_pack_fp6(w[ok & (mags < 1e5)])
+    _, s6_o = oracle.quantize_fp6(w[ok & (mags < 1e5)])
+    assert np.array_equal(s6, s6_o)
+
+
+def test_pack_errors():
+    w = np.zeros((2, 64), dtype=np.float32)
+    L = wq.lib()
+    buf = np.zeros(4096, dtype=np.uint8)
+    sc = np.zeros(64, dtype=np.uint16)
+    p = wq._host_ptr
+    assert L.wq_pack_int8(None, 2, 64, p(buf), p(sc)) == -1
+    assert L.wq_pack_int8(p(w), 2, 64, None, p(sc)) == -1
+    assert L.wq_pack_int4(p(w), 2, 64, p(buf), p(sc), None) == -1
+    assert L.wq_pack_int8(p(w), -1, 64, p(buf), p(sc)) == -1
+    assert L.wq_pack_int8(p(w), 2, 48, p(buf), p(sc)) == -2
+    assert L.wq_pack_fp6(p(w), 0, 64, p(buf), p(sc)) == -2
+    assert L.wq_pack_int4(p(w), 2, 0, p(buf), p(sc), p(sc)) == -2
+    bad = w.copy()
+    bad[1, 5] = np.nan
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_pack_fp6(bad)
+    assert e.value.status == -4
+    bad[1, 5] = np.inf
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_pack_int4(bad)
+    assert e.value.status == -4
+    big = np.full((1, 32), 1e7, dtype=np.float32)
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_pack_int8(big)      # 1e7/127 > 65504
+    assert e.value.status == -7
+    assert L.wq_unpack(7, p(buf), p(sc), p(sc), 2, 64, p(buf), None, None) == -3
+
+
+def test_device_entry_points_reject_bad_arguments_before_launch():
+    # these return before any HIP call, so they run without a GPU
+    L = wq.lib()
+    a = 1 << 20                                # a 16-byte-aligned fake address, never dereferenced
+    assert L.wq_linear(a, a, a, a, a, 1, 64, 64, 9, None) == -3
+    assert L.wq_linear(None, a, a, a, a, 1, 64, 64, 1, None) == -1
+    assert L.wq_linear(a, a, None, None, a, 1, 64, 64, 1, None) == -1
+    assert L.wq_linear(a, a, a, None, a, 1, 64, 64, 2, None) == -1
+    assert L.wq_linear(a, a, a, a, a, 0, 64, 64, 1, None) == -2
+    assert L.wq_linear(a, a, a, a, a, 1, 64, 48, 1, None) == -2
+    assert L.wq_linear(a, a, a, a, a, 1, 0, 64, 1, None) == -2
+    assert L.wq_linear(a + 8, a, a, a, a, 1, 64, 64, 1, None) == -5
+    assert L.wq_linear(a, a, a, a, a + 2, 1, 64, 64, 1, None) == -5
+    assert L.wq_dequant(1, a, a, a, a, 64, 40, None) == -2
+    assert L.wq_dequant(5, a, a, a, a, 64, 64, None) == -3
+    assert L.wq_dequant(2, a, a, None, a, 64, 64, None) == -1
+    assert L.wq_dequant(1, a + 4, a, a, a, 64, 64, None) == -5
+    assert wq.wq_linear_kernel_name(2, 1, 4096, 4096).startswith("gemv_kernel")
+    assert wq.wq_linear_kernel_name(3, 16, 4096, 4096).startswith("mfma_kernel")
+    assert wq.wq_linear_kernel_name(3, 16, 4096, 40) == ""

@@ -1,0 +1,315 @@
+// Host half of libwq: argument checks, sizes, and the offline quantize + pack step.
+//
+// The FP6-LLM news page (m.zhengruan.com), section "重新设计内核方案", re-packs the
+// low-bit weights before inference so that the kernel reads aligned 32/64-bit blocks.
+// Here that step runs on the host in float64, row-parallel over std::thread workers,
+// and writes the layout declared in include/wq.h.
+//
+// Scale and code rules (readings; the pages give names, not formulas):
+//   int8  per row:       s = fp16(max|w| / 127),      q = clamp(rint(w/s), -127, 127)
+//   int4  per 32 along K: s = fp16((hi - lo) / 15), z = clamp(rint(-lo/s), 0, 15),
+//                        q = clamp(rint(w/s) + z, 0, 15), lo/hi widened to include 0
+//   fp6   per row:       s = fp16(max|w| / 28),       code = e3m2 nearest to w/s
+// Every quotient is one IEEE float64 operation; every rounding is to nearest even.
+
+#include "wq_internal.h"
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace wq {
+
+// float64 -> fp16 bits, round to nearest even, written from the fp16 definition:
+// normal values (1 + n/1024) 2^E for E in [-14, 15], subnormals n 2^-24.
+uint16_t f64_to_f16_bits(double v) {
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  const double a = std::fabs(v);
+  if (std::isnan(v)) return 0x7E00;
+  if (a >= 65520.0) return sign | 0x7C00;  // rounds past 65504 (or is infinite)
+  if (a < 0x1p-14) {
+    // subnormal range: spacing 2^-24; a * 2^24 is exact, rint rounds half to even
+    const double n = std::nearbyint(a * 0x1p24);
+    return sign | static_cast<uint16_t>(n);  // n == 1024 encodes 2^-14, the smallest normal
+  }
+  int e2 = 0;
+  (void)std::frexp(a, &e2);  // a = f 2^e2, f in [0.5, 1)
+  int E = e2 - 1;            // 2^E <= a < 2^(E+1)
+  const double frac = std::ldexp(a, -E) - 1.0;  // exact, in [0, 1)
+  double n = std::nearbyint(frac * 1024.0);     // exact product, rounded half to even
+  if (n == 1024.0) { n = 0.0; ++E; }
+  if (E > 15) return sign | 0x7C00;
+  return sign | static_cast<uint16_t>(((E + 15) << 10) | static_cast<int>(n));
+}
+
+double f16_bits_to_f64(uint16_t h) {
+  const int e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0) v = std::ldexp(static_cast<double>(m), -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = std::ldexp(static_cast<double>(1024 + m), e - 25);
+  return (h & 0x8000) ? -v : v;
+}
+
+// e3m2 code of a finite float64 t: sign from t's sign bit, magnitude rounded to the
+// nearest e3m2 value with ties to the even code, saturating at 28. Written from the
+// format's structure: below 0.25 the values are multiples of 1/16 (codes 0..4, code 4
+// being 0.25); from 0.25 up, exponent E in [-2, 4] and two mantissa bits.
+uint8_t e3m2_encode(double t) {
+  const uint8_t sign = std::signbit(t) ? 0x20 : 0;
+  const double a = std::fabs(t);
+  if (a >= 28.0) return sign | 31;
+  if (a < 0.25) {
+    const double n = std::nearbyint(a * 16.0);  // exact product; 0..4
+    return sign | static_cast<uint8_t>(n);
+  }
+  int e2 = 0;
+  (void)std::frexp(a, &e2);
+  const int E = e2 - 1;                               // -2 .. 4
+  const double m = std::nearbyint((std::ldexp(a, -E) - 1.0) * 4.0);  // 0..4, ties to even
+  int code = 4 * (E + 3) + static_cast<int>(m);       // m == 4 carries into the next binade
+  if (code > 31) code = 31;
+  return sign | static_cast<uint8_t>(code);
+}
+
+namespace {
+
+bool shape_ok(int64_t N, int64_t K) { return N >= 1 && K >= 32 && K % 32 == 0; }
+
+int fmt_bits(int fmt) {
+  switch (fmt) {
+    case WQ_FMT_F16: return 16;
+    case WQ_FMT_W8: return 8;
+    case WQ_FMT_W4G32: return 4;
+    case WQ_FMT_W6E3M2: return 6;
+    default: return 0;
+  }
+}
+
+// Run f(row_begin, row_end) over [0, N) on up to hardware_concurrency threads and return the
+// first non-OK status.
+template <class F>
+int parallel_rows(int64_t N, int64_t work_per_row, F f) {
+  unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+  int64_t total = N * work_per_row;
+  unsigned nt = static_cast<unsigned>(std::min<int64_t>(hw, std::max<int64_t>(1, total / (1 << 20))));
+  nt = std::max(1u, std::min<unsigned>(nt, static_cast<unsigned>(N)));
+  if (nt == 1) return f(0, N);
+  std::vector<std::thread> ts;
+  std::vector<int> st(nt, WQ_OK);
+  int64_t per = (N + nt - 1) / nt;
+  for (unsigned i = 0; i < nt; ++i) {
+    int64_t b = i * per, e = std::min<int64_t>(N, b + per);
+    if (b >= e) break;
+    ts.emplace_back([&, i, b, e] { st[i] = f(b, e); });
+  }
+  for (auto& t : ts) t.join();
+  for (int s : st)
+    if (s != WQ_OK) return s;
+  return WQ_OK;
+}
+
+// ---- layout writers (one 32-code unit at a time) ----
+void put_unit_w8(uint8_t* dst, const int8_t* q) {
+  for (int j = 0; j < 32; ++j) dst[j] = static_cast<uint8_t>(q[j] + 128);
+}
+void put_unit_w4(uint8_t* dst, const uint8_t* q) {
+  for (int d = 0; d < 4; ++d) {
+    uint32_t word = 0;
+    for (int t = 0; t < 4; ++t) {
+      word |= static_cast<uint32_t>(q[8 * d + 2 * t] & 15) << (4 * t);
+      word |= static_cast<uint32_t>(q[8 * d + 2 * t + 1] & 15) << (4 * (t + 4));
+    }
+    for (int b = 0; b < 4; ++b) dst[4 * d + b] = static_cast<uint8_t>(word >> (8 * b));
+  }
+}
+void put_unit_w6(uint8_t* dst, const uint8_t* c) {
+  // 32 codes x 6 bits = 192 bits, low code first; assembled in three 64-bit words
+  uint64_t w[3] = {0, 0, 0};
+  for (int j = 0; j < 32; ++j) {
+    const int bit = 6 * j, word = bit >> 6, off = bit & 63;
+    w[word] |= static_cast<uint64_t>(c[j] & 63) << off;
+    if (off > 58) w[word + 1] |= static_cast<uint64_t>(c[j] & 63) >> (64 - off);
+  }
+  for (int i = 0; i < 24; ++i) dst[i] = static_cast<uint8_t>(w[i >> 3] >> (8 * (i & 7)));
+}
+
+int check_weights(const float* w, int64_t K, int64_t r) {
+  for (int64_t k = 0; k < K; ++k)
+    if (!std::isfinite(w[r * K + k])) return WQ_ERR_NONFINITE;
+  return WQ_OK;
+}
+
+}  // namespace
+}  // namespace wq
+
+using namespace wq;
+
+extern "C" {
+
+int wq_version(void) { return (1 << 16) | 0; }
+
+const char* wq_status_string(int s) {
+  switch (s) {
+    case WQ_OK: return "ok";
+    case WQ_ERR_ARG: return "invalid argument (NULL pointer or negative size)";
+    case WQ_ERR_SHAPE: return "invalid shape (K must be a positive multiple of 32, N >= 1, M >= 1)";
+    case WQ_ERR_FMT: return "unknown weight format";
+    case WQ_ERR_NONFINITE: return "non-finite weight";
+    case WQ_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case WQ_ERR_DEVICE: return "HIP runtime error at launch";
+    case WQ_ERR_RANGE: return "scale overflows fp16";
+    default: return "unknown status";
+  }
+}
+
+size_t wq_packed_bytes(int fmt, int64_t N, int64_t K) {
+  int b = fmt_bits(fmt);
+  if (!b || !shape_ok(N, K)) return 0;
+  return static_cast<size_t>(N) * static_cast<size_t>(K) * b / 8;
+}
+
+size_t wq_scales_bytes(int fmt, int64_t N, int64_t K) {
+  if (!fmt_bits(fmt) || !shape_ok(N, K) || fmt == WQ_FMT_F16) return 0;
+  return fmt == WQ_FMT_W4G32 ? static_cast<size_t>(N) * (K / 32) * 2 : static_cast<size_t>(N) * 2;
+}
+
+size_t wq_zeros_bytes(int fmt, int64_t N, int64_t K) {
+  if (fmt != WQ_FMT_W4G32 || !shape_ok(N, K)) return 0;
+  return static_cast<size_t>(N) * (K / 32) * 2;
+}
+
+int wq_pack_int8(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales) {
+  if (!w || !packed || !scales || N < 0 || K < 0) return WQ_ERR_ARG;
+  if (!shape_ok(N, K)) return WQ_ERR_SHAPE;
+  uint8_t* out = static_cast<uint8_t*>(packed);
+  return parallel_rows(N, K, [&](int64_t r0, int64_t r1) {
+    std::vector<int8_t> q(K);
+    for (int64_t r = r0; r < r1; ++r) {
+      if (check_weights(w, K, r)) return static_cast<int>(WQ_ERR_NONFINITE);
+      const float* row = w + r * K;
+      float amax = 0.0f;
+      for (int64_t k = 0; k < K; ++k) amax = std::max(amax, std::fabs(row[k]));
+      const uint16_t sb = f64_to_f16_bits(static_cast<double>(amax) / 127.0);
+      if ((sb & 0x7FFF) == 0x7C00) return static_cast<int>(WQ_ERR_RANGE);
+      const double s = f16_bits_to_f64(sb);
+      scales[r] = sb;
+      for (int64_t k = 0; k < K; ++k) {
+        double v = s > 0 ? std::nearbyint(static_cast<double>(row[k]) / s) : 0.0;
+        q[k] = static_cast<int8_t>(std::min(127.0, std::max(-127.0, v)));
+      }
+      for (int64_t u = 0; u < K / 32; ++u) put_unit_w8(out + (r * K + 32 * u), q.data() + 32 * u);
+    }
+    return static_cast<int>(WQ_OK);
+  });
+}
+
+int wq_pack_int4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales, uint16_t* zeros) {
+  if (!w || !packed || !scales || !zeros || N < 0 || K < 0) return WQ_ERR_ARG;
+  if (!shape_ok(N, K)) return WQ_ERR_SHAPE;
+  uint8_t* out = static_cast<uint8_t*>(packed);
+  const int64_t G = K / 32;
+  return parallel_rows(N, K, [&](int64_t r0, int64_t r1) {
+    uint8_t q[32];
+    for (int64_t r = r0; r < r1; ++r) {
+      if (check_weights(w, K, r)) return static_cast<int>(WQ_ERR_NONFINITE);
+      for (int64_t g = 0; g < G; ++g) {
+        const float* grp = w + r * K + 32 * g;
+        double lo = 0.0, hi = 0.0;
+        for (int j = 0; j < 32; ++j) {
+          lo = std::min(lo, static_cast<double>(grp[j]));
+          hi = std::max(hi, static_cast<double>(grp[j]));
+        }
+        const uint16_t sb = f64_to_f16_bits((hi - lo) / 15.0);
+        if ((sb & 0x7FFF) == 0x7C00) return static_cast<int>(WQ_ERR_RANGE);
+        const double s = f16_bits_to_f64(sb);
+        double z = 0.0;
+        if (s > 0) {
+          z = std::min(15.0, std::max(0.0, std::nearbyint(-lo / s)));
+          for (int j = 0; j < 32; ++j) {
+            double v = std::nearbyint(static_cast<double>(grp[j]) / s) + z;
+            q[j] = static_cast<uint8_t>(std::min(15.0, std::max(0.0, v)));
+          }
+        } else {
+          std::memset(q, 0, sizeof(q));
+        }
+        scales[r * G + g] = sb;
+        zeros[r * G + g] = static_cast<uint16_t>(f64_to_f16_bits(z) & 0x7FFF);  // integer zero point: +0 never -0
+        put_unit_w4(out + (r * G + g) * 16, q);
+      }
+    }
+    return static_cast<int>(WQ_OK);
+  });
+}
+
+int wq_pack_fp6(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales) {
+  if (!w || !packed || !scales || N < 0 || K < 0) return WQ_ERR_ARG;
+  if (!shape_ok(N, K)) return WQ_ERR_SHAPE;
+  uint8_t* out = static_cast<uint8_t*>(packed);
+  const int64_t U = K / 32;
+  return parallel_rows(N, K, [&](int64_t r0, int64_t r1) {
+    std::vector<uint8_t> c(K);
+    for (int64_t r = r0; r < r1; ++r) {
+      if (check_weights(w, K, r)) return static_cast<int>(WQ_ERR_NONFINITE);
+      const float* row = w + r * K;
+      float amax = 0.0f;
+      for (int64_t k = 0; k < K; ++k) amax = std::max(amax, std::fabs(row[k]));
+      const uint16_t sb = f64_to_f16_bits(static_cast<double>(amax) / 28.0);
+      if ((sb & 0x7FFF) == 0x7C00) return static_cast<int>(WQ_ERR_RANGE);
+      const double s = f16_bits_to_f64(sb);
+      scales[r] = sb;
+      for (int64_t k = 0; k < K; ++k) c[k] = s > 0 ? e3m2_encode(static_cast<double>(row[k]) / s) : 0;
+      for (int64_t u = 0; u < U; ++u) put_unit_w6(out + (r * U + u) * 24, c.data() + 32 * u);
+    }
+    return static_cast<int>(WQ_OK);
+  });
+}
+
+int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,
+              void* codes, uint16_t* scales_out, uint16_t* zeros_out) {
+  if (!fmt_bits(fmt)) return WQ_ERR_FMT;
+  if (!packed || !codes || N < 0 || K < 0) return WQ_ERR_ARG;
+  if (!shape_ok(N, K)) return WQ_ERR_SHAPE;
+  const uint8_t* in = static_cast<const uint8_t*>(packed);
+  const int64_t U = K / 32;
+  if (fmt == WQ_FMT_W8) {
+    int8_t* o = static_cast<int8_t*>(codes);
+    for (int64_t i = 0; i < N * K; ++i) o[i] = static_cast<int8_t>(static_cast<int>(in[i]) - 128);
+  } else if (fmt == WQ_FMT_W4G32) {
+    uint8_t* o = static_cast<uint8_t*>(codes);
+    for (int64_t r = 0; r < N; ++r)
+      for (int64_t u = 0; u < U; ++u)
+        for (int d = 0; d < 4; ++d) {
+          const uint8_t* p = in + (r * U + u) * 16 + 4 * d;
+          const uint32_t word = p[0] | (p[1] << 8) | (p[2] << 16) | (static_cast<uint32_t>(p[3]) << 24);
+          for (int t = 0; t < 4; ++t) {
+            o[r * K + 32 * u + 8 * d + 2 * t] = (word >> (4 * t)) & 15;
+            o[r * K + 32 * u + 8 * d + 2 * t + 1] = (word >> (4 * (t + 4))) & 15;
+          }
+        }
+  } else if (fmt == WQ_FMT_W6E3M2) {
+    uint8_t* o = static_cast<uint8_t*>(codes);
+    for (int64_t r = 0; r < N; ++r)
+      for (int64_t u = 0; u < U; ++u) {
+        const uint8_t* p = in + (r * U + u) * 24;
+        for (int j = 0; j < 32; ++j) {
+          int v = 0;
+          for (int b = 0; b < 6; ++b) {
+            const int bit = 6 * j + b;
+            v |= ((p[bit >> 3] >> (bit & 7)) & 1) << b;
+          }
+          o[r * K + 32 * u + j] = static_cast<uint8_t>(v);
+        }
+      }
+  } else {
+    std::memcpy(codes, packed, static_cast<size_t>(N) * K * 2);
+  }
+  if (scales_out && scales) std::memcpy(scales_out, scales, wq_scales_bytes(fmt, N, K));
+  if (zeros_out && zeros) std::memcpy(zeros_out, zeros, wq_zeros_bytes(fmt, N, K));
+  return WQ_OK;
+}
+
+}  // extern "C"

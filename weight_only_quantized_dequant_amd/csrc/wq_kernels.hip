@@ -1,0 +1,463 @@
+// Device half of libwq: fused dequant + linear kernels for gfx950 (CDNA4), and wq_dequant.
+//
+// The FP6-LLM news page (m.zhengruan.com), section "重新设计内核方案", describes the
+// computation these kernels perform. Low-bit weights are re-packed offline into aligned
+// blocks, loaded, turned into fp16 values in registers, and fed to the matrix units,
+// with dequantization and the product in ONE kernel, so that no fp16 weight tensor is
+// ever written to memory. The gpt-fast write-up (m.greenbasetech.com) explains why this
+// is the decode lever: the layer is bound by memory bandwidth, and the bytes per
+// parameter set the speed.
+//
+// gfx950 design:
+//  * Layout: row-major, 32-code units (32/16/24/64 bytes for W8/W4/W6/F16). Lane l of a
+//    wave reads unit l of a 64-unit "chunk" of one row, so one wave-load covers 1-4 KB
+//    contiguously.
+//  * Decode in VGPRs, exact:
+//      W8  offset-binary byte u = q+128 -> fp16 (1024+u) by v_perm_b32 against 0x64,
+//          then -1152 (v_pk_add_f16).
+//      W4  nibble pairs -> fp16 (1024+q) / (1024+16q) by one v_and_or_b32, then one
+//          v_pk_fma_f16 gives q-z.
+//      W6  the 192-bit unit goes through gfx950's v_cvt_scalef32_pk32_f16_bf6 at scale 1.0,
+//          which yields the 32 e3m2 values as exact fp16.
+//  * M <= GEMV_MAX_M: VALU GEMV. v_dot2_f32_f16 accumulates in fp32, lanes run along K,
+//    and each row's sum finishes with a DPP + cross-row shuffle wave reduction; waves of a
+//    workgroup split K and add their partials through LDS in a fixed order.
+//  * Larger M: v_mfma_f32_16x16x32_f16. Lane (n = l%16, q = l/16) decodes its own unit
+//    straight into the B fragment; the A fragment is x at the same K positions, since any
+//    permutation of K applied to both operands leaves the product unchanged.
+//  * No atomics anywhere, so every result is deterministic.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+
+#include "wq_internal.h"
+
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h32 __attribute__((ext_vector_type(32)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x6 __attribute__((ext_vector_type(6)));
+
+constexpr int GEMV_MAX_M = 4;   // largest M served by the VALU GEMV; above it the MFMA kernel runs
+constexpr int MFMA_M = 16;      // rows of x per MFMA launch
+constexpr int MAX_WAVES = 4;    // waves per workgroup (split of K inside a workgroup)
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// ---------------------------------------------------------------- raw units and loads
+template <int FMT> struct Raw;
+template <> struct Raw<WQ_FMT_W8> { uint4 a, b; };
+template <> struct Raw<WQ_FMT_W4G32> { uint4 a; };
+template <> struct Raw<WQ_FMT_W6E3M2> { uint3 a, b; };
+template <> struct Raw<WQ_FMT_F16> { uint4 a, b, c, d; };
+
+template <int FMT> constexpr int unit_bytes() {
+  return FMT == WQ_FMT_W8 ? 32 : FMT == WQ_FMT_W4G32 ? 16 : FMT == WQ_FMT_W6E3M2 ? 24 : 64;
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_raw(const uint8_t* __restrict__ p, Raw<FMT>& r) {
+  if constexpr (FMT == WQ_FMT_W8) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    r.a = q[0]; r.b = q[1];
+  } else if constexpr (FMT == WQ_FMT_W4G32) {
+    r.a = *reinterpret_cast<const uint4*>(p);
+  } else if constexpr (FMT == WQ_FMT_W6E3M2) {
+    const uint3* q = reinterpret_cast<const uint3*>(p);
+    r.a = q[0]; r.b = q[1];
+  } else {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    r.a = q[0]; r.b = q[1]; r.c = q[2]; r.d = q[3];
+  }
+}
+
+// ---------------------------------------------------------------- exact decode to fp16 pairs
+// out[p] holds the values of codes 2p and 2p+1 of the unit:
+//   W8: q      W4: q - z      W6: e3m2(code)      F16: the weights
+// zc1 = -(1024 + z), zc2 = -(64 + z) as fp16 pairs (W4 only; exact small integers).
+__device__ __forceinline__ void decode_w8_word(uint32_t d, h2& lo, h2& hi) {
+  const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  lo = as_h2(__builtin_amdgcn_perm(0x64646464u, d, 0x04010400u)) + bias;
+  hi = as_h2(__builtin_amdgcn_perm(0x64646464u, d, 0x04030402u)) + bias;
+}
+
+__device__ __forceinline__ void decode_w4_word(uint32_t d, h2 zc1, h2 zc2, h2& o0, h2& o1, h2& o2, h2& o3) {
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t d8 = d >> 8;
+  o0 = as_h2((d & 0x000F000Fu) | 0x64006400u) + zc1;                       // codes 0,1: 1024+q
+  o1 = __builtin_elementwise_fma(as_h2((d & 0x00F000F0u) | 0x64006400u), sixteenth, zc2);   // 1024+16q
+  o2 = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + zc1;
+  o3 = __builtin_elementwise_fma(as_h2((d8 & 0x00F000F0u) | 0x64006400u), sixteenth, zc2);
+}
+
+template <int FMT>
+__device__ __forceinline__ void decode(const Raw<FMT>& r, h2 zc1, h2 zc2, h2 (&out)[16]) {
+  if constexpr (FMT == WQ_FMT_W8) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) decode_w8_word(w[i], out[2 * i], out[2 * i + 1]);
+  } else if constexpr (FMT == WQ_FMT_W4G32) {
+    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) decode_w4_word(w[i], zc1, zc2, out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+  } else if constexpr (FMT == WQ_FMT_W6E3M2) {
+    u32x6 v;
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.b.x; v[4] = r.b.y; v[5] = r.b.z;
+    const h32 h = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(v, 1.0f);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) { out[p][0] = h[2 * p]; out[p][1] = h[2 * p + 1]; }
+  } else {
+    const uint32_t w[16] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w,
+                            r.c.x, r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w};
+#pragma unroll
+    for (int p = 0; p < 16; ++p) out[p] = as_h2(w[p]);
+  }
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// zero-point constants of one W4 group
+__device__ __forceinline__ void w4_consts(uint16_t zbits, h2& zc1, h2& zc2) {
+  const _Float16 z = __builtin_bit_cast(_Float16, zbits);
+  const _Float16 c1 = (_Float16)-1024.0f - z, c2 = (_Float16)-64.0f - z;   // exact integers
+  zc1 = h2{c1, c1};
+  zc2 = h2{c2, c2};
+}
+
+// x[32u .. 32u+32) of one row as 16 fp16 pairs
+__device__ __forceinline__ void load_x(const uint16_t* __restrict__ xrow, int u, h2 (&xv)[16]) {
+  const uint4* p = reinterpret_cast<const uint4*>(xrow + 32 * u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = p[i];
+    xv[4 * i] = as_h2(v.x); xv[4 * i + 1] = as_h2(v.y); xv[4 * i + 2] = as_h2(v.z); xv[4 * i + 3] = as_h2(v.w);
+  }
+}
+
+// ---------------------------------------------------------------- wave reduction
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the 64 lanes; every lane receives the total
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp<0x141>(v);   // row_half_mirror: pairs the two quads of each 8 lanes
+  v += dpp<0x140>(v);   // row_mirror: pairs the two halves of each 16-lane row
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------- GEMV (M <= GEMV_MAX_M)
+// Workgroup: B output rows x all of K; its WK waves take the 64-unit chunks of K in turn.
+template <int FMT, int M, int B>
+__global__ __launch_bounds__(64 * MAX_WAVES) void gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                                              const uint16_t* __restrict__ scales,
+                                                              const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
+                                                              int N, int K) {
+  constexpr int UB = unit_bytes<FMT>();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, WK = blockDim.x >> 6;
+  const int U = K >> 5, C = (U + 63) >> 6;
+  const int row0 = blockIdx.x * B;
+  float acc[B][M];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[b][m] = 0.0f;
+
+  for (int c = wave; c < C; c += WK) {
+    const int u = c * 64 + lane;
+    if (u < U) {
+      Raw<FMT> raw[B];
+      uint16_t zb[B], sb[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int n = min(row0 + b, N - 1);
+        load_raw<FMT>(w + ((size_t)n * U + u) * UB, raw[b]);
+        if constexpr (FMT == WQ_FMT_W4G32) { sb[b] = scales[(size_t)n * U + u]; zb[b] = zeros[(size_t)n * U + u]; }
+      }
+      h2 xv[M][16];
+#pragma unroll
+      for (int m = 0; m < M; ++m) load_x(x + (size_t)m * K, u, xv[m]);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        h2 zc1 = {}, zc2 = {};
+        if constexpr (FMT == WQ_FMT_W4G32) w4_consts(zb[b], zc1, zc2);
+        h2 wv[16];
+        decode<FMT>(raw[b], zc1, zc2, wv);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          float part = 0.0f;
+#pragma unroll
+          for (int p = 0; p < 16; ++p) part = __builtin_amdgcn_fdot2(wv[p], xv[m][p], part, false);
+          if constexpr (FMT == WQ_FMT_W4G32) acc[b][m] = __builtin_fmaf(part, f16_to_f32(sb[b]), acc[b][m]);
+          else acc[b][m] += part;
+        }
+      }
+    }
+  }
+
+  __shared__ float red[MAX_WAVES][B * M];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float t = wave_sum(acc[b][m]);
+      if (lane == 0) red[wave][b * M + m] = t;
+    }
+  __syncthreads();
+  if (wave == 0 && lane < B * M) {
+    const int b = lane / M, m = lane % M, n = row0 + b;
+    float t = 0.0f;
+    for (int i = 0; i < WK; ++i) t += red[i][lane];
+    if (n < N) {
+      if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) t *= f16_to_f32(scales[n]);
+      y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)t);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- MFMA (M up to 16)
+// Workgroup: 16 output rows x all of K; its WK waves take the 128-wide K tiles in turn.
+template <int FMT>
+__global__ __launch_bounds__(64 * MAX_WAVES) void mfma_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                                              const uint16_t* __restrict__ scales,
+                                                              const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
+                                                              int M, int N, int K) {
+  constexpr int UB = unit_bytes<FMT>();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, WK = blockDim.x >> 6;
+  const int nl = lane & 15, q = lane >> 4;
+  const int n = blockIdx.x * 16 + nl, nc = min(n, N - 1);
+  const int U = K >> 5, T = (U + 3) >> 2;
+  f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int t = wave; t < T; t += WK) {
+    const int u = 4 * t + q;
+    h2 wv[16];
+    h8 xa[4];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) wv[p] = h2{};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xa[i] = h8{};
+    if (u < U) {
+      Raw<FMT> raw;
+      load_raw<FMT>(w + ((size_t)nc * U + u) * UB, raw);
+      h2 zc1 = {}, zc2 = {};
+      uint16_t sbits = 0;
+      if constexpr (FMT == WQ_FMT_W4G32) {
+        sbits = scales[(size_t)nc * U + u];
+        w4_consts(zeros[(size_t)nc * U + u], zc1, zc2);
+      }
+      decode<FMT>(raw, zc1, zc2, wv);
+      if constexpr (FMT == WQ_FMT_W4G32) {
+        const _Float16 s = __builtin_bit_cast(_Float16, sbits);
+        const h2 s2 = {s, s};
+#pragma unroll
+        for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
+      }
+      if (nl < M) {
+        const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)nl * K + 32 * u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xa[i] = __builtin_bit_cast(h8, xp[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h8 bfrag;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { bfrag[2 * j] = wv[4 * i + j][0]; bfrag[2 * j + 1] = wv[4 * i + j][1]; }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[i], bfrag, acc, 0, 0, 0);
+    }
+  }
+
+  __shared__ f4 red[MAX_WAVES][64];
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f4 t = red[0][lane];
+    for (int i = 1; i < WK; ++i) t += red[i][lane];
+    if (n < N) {
+      float s = 1.0f;
+      if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) s = f16_to_f32(scales[n]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * q + i;   // D[m][n] sits in lane (n + 16*(m/4)), register m%4
+        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(t[i] * s));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dequant
+// One thread per unit: decode exactly, multiply by the scale in fp32 (exact), round once.
+template <int FMT>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ scales,
+                                                      const uint16_t* __restrict__ zeros, uint16_t* __restrict__ out,
+                                                      int N, int K) {
+  constexpr int UB = unit_bytes<FMT>();
+  const int U = K >> 5;
+  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (size_t)N * U) return;
+  const int n = (int)(gid / U), u = (int)(gid % U);
+  Raw<FMT> raw;
+  load_raw<FMT>(w + gid * UB, raw);
+  h2 zc1 = {}, zc2 = {};
+  float s = 1.0f;
+  if constexpr (FMT == WQ_FMT_W4G32) {
+    w4_consts(zeros[gid], zc1, zc2);
+    s = f16_to_f32(scales[gid]);
+  } else if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) {
+    s = f16_to_f32(scales[n]);
+  }
+  h2 wv[16];
+  decode<FMT>(raw, zc1, zc2, wv);
+  uint32_t o[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    if constexpr (FMT == WQ_FMT_F16) {
+      o[p] = as_u32(wv[p]);
+    } else {
+      const _Float16 a = (_Float16)((float)wv[p][0] * s), b = (_Float16)((float)wv[p][1] * s);
+      o[p] = as_u32(h2{a, b});
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(out + (size_t)n * K + 32 * u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+}
+
+// ---------------------------------------------------------------- host-side planning
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool valid_fmt(int fmt) { return fmt >= WQ_FMT_F16 && fmt <= WQ_FMT_W6E3M2; }
+
+struct GemvPlan {
+  int B;      // rows per workgroup
+  int WK;     // waves per workgroup
+  int grid;   // workgroups
+};
+
+// Enough waves to keep 8 per CU busy (256 CUs), with as many rows per wave as that allows
+// (x is loaded once per chunk and reused for every row of the wave).
+GemvPlan plan_gemv(int64_t N, int64_t K) {
+  const int64_t U = K / 32, C = (U + 63) / 64;
+  const int WK = static_cast<int>(C < MAX_WAVES ? C : MAX_WAVES);
+  int B = 4;
+  while (B > 1 && ((N + B - 1) / B) * WK < 2048) B >>= 1;
+  return {B, WK, static_cast<int>((N + B - 1) / B)};
+}
+
+int mfma_waves(int64_t K) {
+  const int64_t T = (K / 32 + 3) / 4;
+  return static_cast<int>(T < MAX_WAVES ? T : MAX_WAVES);
+}
+
+template <int FMT, int M>
+hipError_t launch_gemv_m(const GemvPlan& p, hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
+                         const uint16_t* z, uint16_t* y, int N, int K) {
+  switch (p.B) {
+    case 4: hipLaunchKernelGGL((gemv_kernel<FMT, M, 4>), dim3(p.grid), dim3(64 * p.WK), 0, s, x, w, sc, z, y, N, K); break;
+    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, M, 2>), dim3(p.grid), dim3(64 * p.WK), 0, s, x, w, sc, z, y, N, K); break;
+    default: hipLaunchKernelGGL((gemv_kernel<FMT, M, 1>), dim3(p.grid), dim3(64 * p.WK), 0, s, x, w, sc, z, y, N, K); break;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
+                             uint16_t* y, int M, int N, int K) {
+  if (M <= GEMV_MAX_M) {
+    const GemvPlan p = plan_gemv(N, K);
+    switch (M) {
+      case 1: return launch_gemv_m<FMT, 1>(p, s, x, w, sc, z, y, N, K);
+      case 2: return launch_gemv_m<FMT, 2>(p, s, x, w, sc, z, y, N, K);
+      case 3: return launch_gemv_m<FMT, 3>(p, s, x, w, sc, z, y, N, K);
+      default: return launch_gemv_m<FMT, 4>(p, s, x, w, sc, z, y, N, K);
+    }
+  }
+  const int WK = mfma_waves(K);
+  hipLaunchKernelGGL((mfma_kernel<FMT>), dim3((N + 15) / 16), dim3(64 * WK), 0, s, x, w, sc, z, y, M, N, K);
+  return hipGetLastError();
+}
+
+int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, const uint16_t* z, const uint16_t* y,
+                      int64_t M, int64_t N, int64_t K, int fmt) {
+  if (!valid_fmt(fmt)) return WQ_ERR_FMT;
+  if (!x || !w || !y || M < 0 || N < 0 || K < 0) return WQ_ERR_ARG;
+  if (fmt != WQ_FMT_F16 && !sc) return WQ_ERR_ARG;
+  if (fmt == WQ_FMT_W4G32 && !z) return WQ_ERR_ARG;
+  if (M < 1 || N < 1 || K < 32 || K % 32) return WQ_ERR_SHAPE;
+  if (N > INT32_MAX / 2 || K > INT32_MAX / 2 || (N * (K / 32)) > INT32_MAX) return WQ_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (sc && !aligned16(sc)) || (z && !aligned16(z))) return WQ_ERR_ALIGN;
+  return WQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros, uint16_t* y,
+              int64_t M, int64_t N, int64_t K, int fmt, void* stream) {
+  const int st = check_linear_args(x, packed_w, scales, zeros, y, M, N, K, fmt);
+  if (st != WQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* w = static_cast<const uint8_t*>(packed_w);
+  for (int64_t m0 = 0; m0 < M; m0 += MFMA_M) {
+    const int mm = static_cast<int>(M - m0 < MFMA_M ? M - m0 : MFMA_M);
+    const uint16_t* xs = x + m0 * K;
+    uint16_t* ys = y + m0 * N;
+    hipError_t e = hipSuccess;
+    switch (fmt) {
+      case WQ_FMT_W8: e = launch_linear_fmt<WQ_FMT_W8>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
+      case WQ_FMT_W4G32: e = launch_linear_fmt<WQ_FMT_W4G32>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
+      case WQ_FMT_W6E3M2: e = launch_linear_fmt<WQ_FMT_W6E3M2>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
+      default: e = launch_linear_fmt<WQ_FMT_F16>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
+    }
+    if (e != hipSuccess) return WQ_ERR_DEVICE;
+  }
+  return WQ_OK;
+}
+
+int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, uint16_t* w_out, int64_t N,
+               int64_t K, void* stream) {
+  if (!valid_fmt(fmt)) return WQ_ERR_FMT;
+  if (!packed || !w_out || N < 0 || K < 0) return WQ_ERR_ARG;
+  if (fmt != WQ_FMT_F16 && !scales) return WQ_ERR_ARG;
+  if (fmt == WQ_FMT_W4G32 && !zeros) return WQ_ERR_ARG;
+  if (N < 1 || K < 32 || K % 32) return WQ_ERR_SHAPE;
+  if (N * (K / 32) > INT32_MAX) return WQ_ERR_SHAPE;
+  if (!aligned16(packed) || !aligned16(w_out) || (scales && !aligned16(scales)) || (zeros && !aligned16(zeros)))
+    return WQ_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* w = static_cast<const uint8_t*>(packed);
+  const int64_t units = N * (K / 32);
+  const dim3 grid(static_cast<unsigned>((units + 255) / 256)), block(256);
+  switch (fmt) {
+    case WQ_FMT_W8: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_W8>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
+    case WQ_FMT_W4G32: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_W4G32>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
+    case WQ_FMT_W6E3M2: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_W6E3M2>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
+    default: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_F16>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
+  }
+  return hipGetLastError() == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
+}
+
+const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
+  static thread_local char buf[96];
+  if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 32 || K % 32) return "";
+  const int64_t mm = M < MFMA_M ? M : MFMA_M;
+  if (mm <= GEMV_MAX_M) {
+    const GemvPlan p = plan_gemv(N, K);
+    snprintf(buf, sizeof(buf), "gemv_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), p.B);
+  } else {
+    snprintf(buf, sizeof(buf), "mfma_kernel<%d>", fmt);
+  }
+  return buf;
+}
+
+}  // extern "C"

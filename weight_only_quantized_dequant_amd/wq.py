@@ -1,0 +1,170 @@
+"""Python binding of libwq: the C ABI of include/wq.h under the same names.
+
+Argument marshalling only. Every step of the path, including quantize and pack, runs
+inside libwq.so (host C++ or HIP kernels). Host arrays are numpy arrays. Device
+buffers are torch tensors, which serve only as device memory and streams. A missing
+library raises an error; there is no fallback.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2 = 0, 1, 2, 3
+FMT_NAMES = {"f16": FMT_F16, "w8": FMT_W8, "w4g32": FMT_W4G32, "w6e3m2": FMT_W6E3M2}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwq.so")
+_lib = None
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+class WqError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, lib().wq_status_string(status).decode(), status))
+
+
+def lib():
+    """Load libwq.so (built in place by weight_only_quantized_dequant_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libwq.so is not built (%s); run `python -m weight_only_quantized_dequant_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        L.wq_version.restype = ctypes.c_int
+        L.wq_status_string.restype = ctypes.c_char_p
+        L.wq_status_string.argtypes = [ctypes.c_int]
+        for name in ("wq_packed_bytes", "wq_scales_bytes", "wq_zeros_bytes"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_size_t
+            f.argtypes = [ctypes.c_int, _i64, _i64]
+        L.wq_pack_int8.argtypes = [_p, _i64, _i64, _p, _p]
+        L.wq_pack_int4.argtypes = [_p, _i64, _i64, _p, _p, _p]
+        L.wq_pack_fp6.argtypes = [_p, _i64, _i64, _p, _p]
+        L.wq_unpack.argtypes = [ctypes.c_int, _p, _p, _p, _i64, _i64, _p, _p, _p]
+        L.wq_dequant.argtypes = [ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _p]
+        L.wq_linear.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, ctypes.c_int, _p]
+        L.wq_linear_kernel_name.restype = ctypes.c_char_p
+        L.wq_linear_kernel_name.argtypes = [ctypes.c_int, _i64, _i64, _i64]
+        for name in ("wq_pack_int8", "wq_pack_int4", "wq_pack_fp6", "wq_unpack", "wq_dequant", "wq_linear"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status, where):
+    if status != 0:
+        raise WqError(status, where)
+
+
+def _host_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None and a.size else None
+
+
+def _dev_ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# ------------------------------------------------------------------ sizes
+def wq_version():
+    return lib().wq_version()
+
+
+def wq_status_string(status):
+    return lib().wq_status_string(status).decode()
+
+
+def wq_packed_bytes(fmt, n, k):
+    return lib().wq_packed_bytes(fmt, n, k)
+
+
+def wq_scales_bytes(fmt, n, k):
+    return lib().wq_scales_bytes(fmt, n, k)
+
+
+def wq_zeros_bytes(fmt, n, k):
+    return lib().wq_zeros_bytes(fmt, n, k)
+
+
+def wq_linear_kernel_name(fmt, m, n, k):
+    return lib().wq_linear_kernel_name(fmt, m, n, k).decode()
+
+
+# ------------------------------------------------------------------ host: pack / unpack
+def _w_host(w):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    return w
+
+
+def _alloc(fmt, n, k):
+    packed = np.empty(max(wq_packed_bytes(fmt, n, k), 1), dtype=np.uint8)
+    scales = np.empty(max(wq_scales_bytes(fmt, n, k) // 2, 1), dtype=np.uint16)
+    zeros = np.empty(max(wq_zeros_bytes(fmt, n, k) // 2, 1), dtype=np.uint16)
+    return packed, scales, zeros
+
+
+def wq_pack_int8(w):
+    """fp32 W [N,K] -> (packed uint8, scales uint16 [N])."""
+    w = _w_host(w)
+    n, k = w.shape
+    packed, scales, _ = _alloc(FMT_W8, n, k)
+    _check(lib().wq_pack_int8(_host_ptr(w), n, k, _host_ptr(packed), _host_ptr(scales)), "wq_pack_int8")
+    return packed, scales
+
+
+def wq_pack_int4(w):
+    """fp32 W [N,K] -> (packed uint8, scales uint16 [N*K/32], zeros uint16 [N*K/32])."""
+    w = _w_host(w)
+    n, k = w.shape
+    packed, scales, zeros = _alloc(FMT_W4G32, n, k)
+    _check(lib().wq_pack_int4(_host_ptr(w), n, k, _host_ptr(packed), _host_ptr(scales), _host_ptr(zeros)), "wq_pack_int4")
+    return packed, scales, zeros
+
+
+def wq_pack_fp6(w):
+    """fp32 W [N,K] -> (packed uint8, scales uint16 [N])."""
+    w = _w_host(w)
+    n, k = w.shape
+    packed, scales, _ = _alloc(FMT_W6E3M2, n, k)
+    _check(lib().wq_pack_fp6(_host_ptr(w), n, k, _host_ptr(packed), _host_ptr(scales)), "wq_pack_fp6")
+    return packed, scales
+
+
+def wq_unpack(fmt, packed, scales, zeros, n, k):
+    """packed (host) -> (logical codes [N,K], scales copy, zeros copy)."""
+    dtype = {FMT_W8: np.int8, FMT_W4G32: np.uint8, FMT_W6E3M2: np.uint8, FMT_F16: np.uint16}.get(fmt, np.uint8)
+    codes = np.empty((n, k), dtype=dtype)
+    s_out = np.empty(max(wq_scales_bytes(fmt, n, k) // 2, 1), dtype=np.uint16)
+    z_out = np.empty(max(wq_zeros_bytes(fmt, n, k) // 2, 1), dtype=np.uint16)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    sc = np.ascontiguousarray(scales, dtype=np.uint16) if scales is not None else None
+    zc = np.ascontiguousarray(zeros, dtype=np.uint16) if zeros is not None else None
+    _check(lib().wq_unpack(fmt, _host_ptr(packed), _host_ptr(sc), _host_ptr(zc), n, k, _host_ptr(codes),
+                           _host_ptr(s_out), _host_ptr(z_out)), "wq_unpack")
+    return codes, s_out, z_out
+
+
+# ------------------------------------------------------------------ device
+def wq_dequant(fmt, packed, scales, zeros, w_out, n, k, stream=None):
+    """Device: packed (torch uint8 on the GPU) -> w_out (torch int16/uint16-sized [N,K] on the GPU), async."""
+    _check(lib().wq_dequant(fmt, _dev_ptr(packed), _dev_ptr(scales), _dev_ptr(zeros), _dev_ptr(w_out), n, k,
+                            _stream_ptr(stream)), "wq_dequant")
+
+
+def wq_linear(x, packed_w, scales, zeros, y, m, n, k, fmt, stream=None):
+    """Device: y[M,N] = x[M,K] . dequant(W)[N,K]^T on torch device buffers, async on stream."""
+    _check(lib().wq_linear(_dev_ptr(x), _dev_ptr(packed_w), _dev_ptr(scales), _dev_ptr(zeros), _dev_ptr(y), m, n, k,
+                           fmt, _stream_ptr(stream)), "wq_linear")
