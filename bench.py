@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-only-quantized linear (libwq) on one MI355X.
+
+Metric: weight-stream HBM GB/s (and % of the 8 TB/s peak) of the fused dequant + linear.
+A step is one pass of the device hot path over one batch. By default the batch is the
+three Llama-7B-shaped W4 (int4, group 32) linears at M = 1 ([4096x4096], [11008x4096],
+[4096x11008]), one wq_linear call each. Quantize + pack happen once, offline, before
+timing (the pages re-pack weights before inference).
+
+Method:
+* Weights are packed on the host by libwq and copied to HBM R times, with R * (bytes per
+  step) >= 1 GiB. Step s reads copy s % R, so the 256 MB Infinity Cache cannot serve the
+  weights from an earlier step: every step streams from HBM, as a real decode does.
+* The K timed steps run as replays of a HIP graph that holds R steps (no host gaps),
+  bracketed by synchronize + events on the launch stream.
+* Roofline: the same launches, one at a time, each bracketed by events on the launch
+  stream, give the average duration of the dominant kernel.
+* fp16 baselines: libwq's own fp16 kernel and torch's F.linear (hipBLASLt) on the same
+  shapes, timed the same way.
+* cpu_baseline: the CPU oracle (unpack + dequant + float64 product) on a bounded sample
+  of rows of the same linears, on this host's cores.
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from weight_only_quantized_dequant_amd import inputs, wq  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "weight-stream HBM GB/s (% of peak) for W8/W6/W4-A16 linear, M=1..16"
+FMT_OF = {"w8": wq.FMT_W8, "w4g32": wq.FMT_W4G32, "w6e3m2": wq.FMT_W6E3M2, "f16": wq.FMT_F16}
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="llama7b_w4g32_linears", choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--m", type=int, default=None, help="rows of x (default: the workload's first M)")
+    ap.add_argument("--no-baselines", action="store_true", help="skip the fp16 baselines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def metadata_bytes(fmt, n, k):
+    return wq.wq_scales_bytes(fmt, n, k) + wq.wq_zeros_bytes(fmt, n, k)
+
+
+class Linear:
+    """One linear: packed weights (R rotation copies on the device) and its x, y buffers."""
+
+    def __init__(self, torch, fmt, w, x_bits, copies):
+        self.fmt = fmt
+        self.n, self.k = w.shape
+        self.m = x_bits.shape[0]
+        if fmt == wq.FMT_W8:
+            p, s = wq.wq_pack_int8(w); z = None
+        elif fmt == wq.FMT_W4G32:
+            p, s, z = wq.wq_pack_int4(w)
+        elif fmt == wq.FMT_W6E3M2:
+            p, s = wq.wq_pack_fp6(w); z = None
+        else:
+            p, s, z = w.astype(np.float16).view(np.uint8).reshape(-1), None, None
+        dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).to("cuda")
+        p0, s0, z0 = dev(p), dev(s), dev(z)
+        self.copies = [(p0, s0, z0)] + [(p0.clone(), None if s0 is None else s0.clone(), None if z0 is None else z0.clone())
+                                        for _ in range(copies - 1)]
+        self.x = torch.from_numpy(x_bits.view(np.int16).copy()).to("cuda")
+        self.y = torch.empty((self.m, self.n), dtype=torch.int16, device="cuda")
+        self.weight_bytes = wq.wq_packed_bytes(fmt, self.n, self.k) + metadata_bytes(fmt, self.n, self.k)
+        self.io_bytes = 2 * self.m * self.k + 2 * self.m * self.n
+        self.kernel = wq.wq_linear_kernel_name(fmt, self.m, self.n, self.k)
+
+    def launch(self, copy, stream=None):
+        p, s, z = self.copies[copy]
+        wq.wq_linear(self.x, p, s, z, self.y, self.m, self.n, self.k, self.fmt, stream)
+
+
+def graph_of_steps(torch, run_step, first, count):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run_step(first)                     # warm the launch path before capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(count):
+                run_step(first + i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_steps(torch, run_step, steps, warmup, rot):
+    """Run `steps` steps as replays of graphs of `rot` steps; returns elapsed ms for exactly `steps` steps."""
+    full = graph_of_steps(torch, run_step, 0, rot)
+    rem = steps % rot
+    tail = graph_of_steps(torch, run_step, 0, rem) if rem else None
+    for _ in range(max(1, math.ceil(warmup / rot))):
+        full.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps // rot):
+        full.replay()
+    if tail is not None:
+        tail.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def per_launch_ms(torch, launches, reps):
+    """Average duration (ms) of each launch, each bracketed by events on the launch stream."""
+    out = []
+    for fn in launches:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (a, b) in enumerate(evs):
+            a.record(); fn(i); b.record()
+        torch.cuda.synchronize()
+        out.append(float(np.mean([a.elapsed_time(b) for a, b in evs])))
+    return out
+
+
+def cpu_baseline(fmt, linears_host, seconds):
+    """The oracle (test infrastructure) timed on a bounded sample: per linear, a block of rows is
+    unpacked, dequantized and multiplied in float64, repeated until `seconds` have passed."""
+    import oracle  # the oracle is imported here only, for this reported baseline
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    rows = 256
+    work = []
+    for (p, s, z, n, k, x) in linears_host:
+        rb = wq.wq_packed_bytes(fmt, n, k) // n
+        g = k // 32
+        sl_s = None if s is None else (s[:rows] if fmt != wq.FMT_W4G32 else s[:rows * g])
+        sl_z = None if z is None else z[:rows * g]
+        work.append((p[:rows * rb], sl_s, sl_z, rows, k, x, rows * rb + 2 * (0 if s is None else sl_s.size)
+                     + 2 * (0 if z is None else sl_z.size)))
+    done_bytes, t0, reps = 0, time.perf_counter(), 0
+    while True:
+        for (pp, ss, zz, r, k, x, b) in work:
+            codes = oracle.unpack_vectorized(fmt, pp, r, k)
+            wd = oracle.dequant_fp16(fmt, codes, ss, zz)
+            oracle.linear_ref(x, wd)
+            done_bytes += b
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": "%d rows of each linear (unpack + dequant + float64 product), %d passes in %.1f s; "
+                      "elementwise steps single-threaded, the product on %d BLAS threads" % (rows, reps, dt, blas_threads)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs the path on a single MI355X "
+              "(no collectives); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    wq.lib()
+    fmt_name, shapes, ms = inputs.WORKLOADS[args.workload]
+    fmt = FMT_OF[fmt_name]
+    m = args.m if args.m is not None else ms[0]
+    stream_id = inputs.WORKLOAD_STREAM[args.workload]
+
+    host = []
+    for li, (n, k) in enumerate(shapes):
+        w, x = inputs.weights_and_x(inputs.rng_for(stream_id, li), n, k, max(ms + [m]))
+        host.append((w, x[:m]))
+    step_weight_bytes = sum(wq.wq_packed_bytes(fmt, n, k) + metadata_bytes(fmt, n, k) for n, k in shapes)
+    rot = max(1, math.ceil(ROTATE_BYTES / step_weight_bytes))
+    lins = [Linear(torch, fmt, w, x, rot) for (w, x) in host]
+    step_io = sum(l.io_bytes for l in lins)
+
+    def run_step(i):
+        for l in lins:
+            l.launch(i % rot)
+
+    steps = args.steps
+    ms_total = time_steps(torch, run_step, steps, args.warmup, rot)
+    value = step_weight_bytes * steps / (ms_total * 1e-3) / 1e9
+
+    # roofline of the dominant kernel: average duration over the launches of one step, eager + events
+    reps = max(20, min(200, steps))
+    durs = per_launch_ms(torch, [lambda i, l=l: l.launch(i % rot) for l in lins], reps)
+    by_kernel = {}
+    for l, d in zip(lins, durs):
+        e = by_kernel.setdefault(l.kernel, [0.0, 0, 0])
+        e[0] += d; e[1] += l.weight_bytes + l.io_bytes; e[2] += 1
+    dom = max(by_kernel.items(), key=lambda kv: kv[1][0])
+    dom_name, (dom_ms, dom_bytes, dom_launches) = dom
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": dom_name, "launches_per_step": dom_launches,
+                "avg_launch_us": round(1e3 * dom_ms / dom_launches, 3),
+                "algorithmic_bytes_per_launch": int(dom_bytes / dom_launches),
+                "per_shape_us": {"%dx%d" % (l.n, l.k): round(1e3 * d, 3) for l, d in zip(lins, durs)}}
+
+    extras = {}
+    if not args.no_baselines:
+        f16_bytes = sum(2 * n * k for n, k in shapes)
+        rot16 = max(1, math.ceil(ROTATE_BYTES / f16_bytes))
+        f16 = [Linear(torch, wq.FMT_F16, w, x, rot16) for (w, x) in host]
+        ms16 = time_steps(torch, lambda i: [l.launch(i % rot16) for l in f16], steps, args.warmup, rot16)
+        gbs16 = f16_bytes * steps / (ms16 * 1e-3) / 1e9
+        # torch F.linear (hipBLASLt) on fp16 weights, same rotation
+        import torch.nn.functional as F
+        tw = [[c[0].view(torch.float16).view(l.n, l.k) for c in l.copies] for l in f16]
+        tx = [l.x.view(torch.float16) for l in f16]
+        def vendor_step(i):
+            for j in range(len(f16)):
+                F.linear(tx[j], tw[j][i % rot16])
+        msv = time_steps(torch, vendor_step, steps, args.warmup, rot16)
+        gbsv = f16_bytes * steps / (msv * 1e-3) / 1e9
+        best16_ms = min(ms16, msv)
+        bytes_ratio = f16_bytes / step_weight_bytes
+        speedup = best16_ms / ms_total
+        extras["fp16_baseline"] = {
+            "libwq_f16": {"GB/s": round(gbs16, 1), "ms_per_step": round(ms16 / steps, 5)},
+            "torch_F_linear": {"GB/s": round(gbsv, 1), "ms_per_step": round(msv / steps, 5)},
+            "speedup_vs_faster_fp16": round(speedup, 3), "bytes_ratio": round(bytes_ratio, 3),
+            "speedup_over_0.8x_bytes_ratio": round(speedup / (0.8 * bytes_ratio), 3)}
+        del f16, tw, tx
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        lh = []
+        for (w, x), l in zip(host, lins):
+            p0, s0, z0 = l.copies[0]
+            to_np = lambda t, dt: None if t is None else t.cpu().numpy().view(dt)
+            lh.append((to_np(p0, np.uint8), to_np(s0, np.uint16), to_np(z0, np.uint16), l.n, l.k, x))
+        cpu = cpu_baseline(fmt, lh, args.cpu_seconds)
+
+    flops = sum(2 * m * n * k for n, k in shapes)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_total / steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "config": {"workload": args.workload, "weights": fmt_name, "M": m,
+                   "shapes_NxK": ["%dx%d" % s for s in shapes], "weight_bytes_per_step": step_weight_bytes,
+                   "io_bytes_per_step": step_io, "rotation_copies": rot,
+                   "tflops": round(flops * steps / (ms_total * 1e-3) / 1e12, 3),
+                   "timing": "HIP graph replays of %d steps, events on the launch stream" % rot},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    out.update(extras)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

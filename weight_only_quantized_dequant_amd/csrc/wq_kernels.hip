@@ -139,84 +139,258 @@ __device__ __forceinline__ void load_x(const uint16_t* __restrict__ xrow, int u,
 }
 
 // ---------------------------------------------------------------- wave reduction
-template <int CTRL>
+template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
 }
 
-// sum over the 64 lanes; every lane receives the total
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
-  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
-  v += dpp<0x141>(v);   // row_half_mirror: pairs the two quads of each 8 lanes
-  v += dpp<0x140>(v);   // row_mirror: pairs the two halves of each 16-lane row
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
+// Sum over the 64 lanes with DPP only (no LDS): the total lands in lane 63.
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v += dpp<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp<0x141, 0xF>(v);   // row_half_mirror: adds the other quad of each 8 lanes
+  v += dpp<0x140, 0xF>(v);   // row_mirror: adds the other half of each 16-lane row
+  v += dpp<0x142, 0xA>(v);   // row_bcast15: rows 1 and 3 add the last lane of rows 0 and 2
+  v += dpp<0x143, 0xC>(v);   // row_bcast31: rows 2 and 3 add lane 31
   return v;
 }
 
+// A constant kept in a VGPR. gfx950 VALU ops take at most one SGPR or literal and VOP3
+// ops take no literal, so masks used by v_and_or_b32 / v_perm_b32 must sit in VGPRs.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
+  asm volatile("" : "+v"(c));
+  return c;
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming (nontemporal) loads of packed weights: each byte is used once per call.
+template <int FMT>
+__device__ __forceinline__ void load_raw_nt(const uint8_t* __restrict__ p, Raw<FMT>& r) {
+  auto ld4 = [](const uint8_t* q) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+  };
+  if constexpr (FMT == WQ_FMT_W8) {
+    r.a = ld4(p); r.b = ld4(p + 16);
+  } else if constexpr (FMT == WQ_FMT_W4G32) {
+    r.a = ld4(p);
+  } else if constexpr (FMT == WQ_FMT_W6E3M2) {
+    const u32x2* q = reinterpret_cast<const u32x2*>(p);       // 24-byte units are 8-byte aligned
+    const u32x2 t0 = __builtin_nontemporal_load(q), t1 = __builtin_nontemporal_load(q + 1), t2 = __builtin_nontemporal_load(q + 2);
+    r.a = make_uint3(t0[0], t0[1], t1[0]);
+    r.b = make_uint3(t1[1], t2[0], t2[1]);
+  } else {
+    r.a = ld4(p); r.b = ld4(p + 16); r.c = ld4(p + 32); r.d = ld4(p + 48);
+  }
+}
+
 // ---------------------------------------------------------------- GEMV (M <= GEMV_MAX_M)
-// Workgroup: B output rows x all of K; its WK waves take the 64-unit chunks of K in turn.
+// One lane per 32-code unit, lanes along K: a wave covers a 64-unit chunk (2048 K) of B
+// rows. Workgroup = B rows x all of K; its WK waves take the chunks c = wave, wave + WK, ...
+// Each wave double-buffers its chunk stream: while chunk i is decoded, the loads of chunk
+// i+1 (x first, then the B rows) are in flight.
+//
+// The decode skips the per-weight bias and zero-point subtraction. A lane dots x with
+// the biased fp16 values it forms in one v_and_or_b32 / v_perm_b32:
+//   W8: (1152 + q)                      -> sum - 1152 X
+//   W4: (1024 + q) for nibbles 0 and 2, (1024 + 16 q) for nibbles 1 and 3
+//                                       -> lo + hi/16 - (1024 X_lo + 64 X_hi) - z (X_lo + X_hi)
+// where X, X_lo, X_hi are sums of x over the unit's positions, shared by all rows of the
+// wave. Every product is exact in fp32; one-hot inputs give exact results.
+template <int FMT, int M, int B>
+struct GemvStage {
+  h2 x[M][16];
+  Raw<FMT> w[B];
+  uint16_t s[B], z[B];
+};
+
+template <int FMT, int M, int B>
+__device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16_t* __restrict__ x,
+                                          const uint8_t* __restrict__ w, const uint16_t* __restrict__ scales,
+                                          const uint16_t* __restrict__ zeros, int row0, int N, int K, int U, int c,
+                                          int lane) {
+  constexpr int UB = unit_bytes<FMT>();
+  const int u = min(c * 64 + lane, U - 1);   // lanes past the row end read a valid unit and are masked later
+#pragma unroll
+  for (int m = 0; m < M; ++m) load_x(x + (size_t)m * K, u, st.x[m]);
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const int n = min(row0 + b, N - 1);
+    load_raw_nt<FMT>(w + ((size_t)n * U + u) * UB, st.w[b]);
+    if constexpr (FMT == WQ_FMT_W4G32) {
+      st.s[b] = scales[(size_t)n * U + u];
+      st.z[b] = zeros[(size_t)n * U + u];
+    }
+  }
+}
+
+template <int FMT, int M, int B>
+__device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, float (&acc)[B][M], bool active) {
+  if (!active) return;
+  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  if constexpr (FMT == WQ_FMT_W4G32) {
+    const uint32_t m0 = in_vgpr(0x000F000Fu), m1 = in_vgpr(0x00F000F0u), mag = in_vgpr(0x64006400u);
+    float cx[M], sx[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float xl = 0.f, xh = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xl = __builtin_amdgcn_fdot2(st.x[m][4 * i], ones, xl, false);
+        xh = __builtin_amdgcn_fdot2(st.x[m][4 * i + 1], ones, xh, false);
+        xl = __builtin_amdgcn_fdot2(st.x[m][4 * i + 2], ones, xl, false);
+        xh = __builtin_amdgcn_fdot2(st.x[m][4 * i + 3], ones, xh, false);
+      }
+      cx[m] = __builtin_fmaf(1024.0f, xl, 64.0f * xh);
+      sx[m] = xl + xh;
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const uint32_t wd[4] = {st.w[b].a.x, st.w[b].a.y, st.w[b].a.z, st.w[b].a.w};
+      h2 v[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t d = wd[i], e = d >> 8;
+        v[4 * i] = as_h2((d & m0) | mag);
+        v[4 * i + 1] = as_h2((d & m1) | mag);
+        v[4 * i + 2] = as_h2((e & m0) | mag);
+        v[4 * i + 3] = as_h2((e & m1) | mag);
+      }
+      const float s = f16_to_f32(st.s[b]), z = f16_to_f32(st.z[b]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float lo = 0.f, hi = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo = __builtin_amdgcn_fdot2(v[4 * i], st.x[m][4 * i], lo, false);
+          hi = __builtin_amdgcn_fdot2(v[4 * i + 1], st.x[m][4 * i + 1], hi, false);
+          lo = __builtin_amdgcn_fdot2(v[4 * i + 2], st.x[m][4 * i + 2], lo, false);
+          hi = __builtin_amdgcn_fdot2(v[4 * i + 3], st.x[m][4 * i + 3], hi, false);
+        }
+        const float part = __builtin_fmaf(hi, 0.0625f, lo) - __builtin_fmaf(z, sx[m], cx[m]);
+        acc[b][m] = __builtin_fmaf(s, part, acc[b][m]);
+      }
+    }
+  } else if constexpr (FMT == WQ_FMT_W8) {
+    const uint32_t mag = in_vgpr(0x64646464u);
+    float sx[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float a = 0.f, c = 0.f;
+#pragma unroll
+      for (int p = 0; p < 16; p += 2) {
+        a = __builtin_amdgcn_fdot2(st.x[m][p], ones, a, false);
+        c = __builtin_amdgcn_fdot2(st.x[m][p + 1], ones, c, false);
+      }
+      sx[m] = 1152.0f * (a + c);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const uint32_t wd[8] = {st.w[b].a.x, st.w[b].a.y, st.w[b].a.z, st.w[b].a.w,
+                              st.w[b].b.x, st.w[b].b.y, st.w[b].b.z, st.w[b].b.w};
+      h2 v[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = as_h2(__builtin_amdgcn_perm(mag, wd[i], 0x04010400u));       // (1024+u0, 1024+u1)
+        v[2 * i + 1] = as_h2(__builtin_amdgcn_perm(mag, wd[i], 0x04030402u));   // (1024+u2, 1024+u3)
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float a = 0.f, c = 0.f;
+#pragma unroll
+        for (int p = 0; p < 16; p += 2) {
+          a = __builtin_amdgcn_fdot2(v[p], st.x[m][p], a, false);
+          c = __builtin_amdgcn_fdot2(v[p + 1], st.x[m][p + 1], c, false);
+        }
+        acc[b][m] += (a + c) - sx[m];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      h2 v[16];
+      decode<FMT>(st.w[b], h2{}, h2{}, v);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float a = 0.f, c = 0.f;
+#pragma unroll
+        for (int p = 0; p < 16; p += 2) {
+          a = __builtin_amdgcn_fdot2(v[p], st.x[m][p], a, false);
+          c = __builtin_amdgcn_fdot2(v[p + 1], st.x[m][p + 1], c, false);
+        }
+        acc[b][m] += a + c;
+      }
+    }
+  }
+}
+
 template <int FMT, int M, int B>
 __global__ __launch_bounds__(64 * MAX_WAVES) void gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                                               const uint16_t* __restrict__ scales,
                                                               const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
                                                               int N, int K) {
-  constexpr int UB = unit_bytes<FMT>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, WK = blockDim.x >> 6;
   const int U = K >> 5, C = (U + 63) >> 6;
   const int row0 = blockIdx.x * B;
+  const int NI = wave < C ? (C - wave + WK - 1) / WK : 0;   // chunks of this wave (wave-uniform)
   float acc[B][M];
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[b][m] = 0.0f;
 
-  for (int c = wave; c < C; c += WK) {
-    const int u = c * 64 + lane;
-    if (u < U) {
-      Raw<FMT> raw[B];
-      uint16_t zb[B], sb[B];
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const int n = min(row0 + b, N - 1);
-        load_raw<FMT>(w + ((size_t)n * U + u) * UB, raw[b]);
-        if constexpr (FMT == WQ_FMT_W4G32) { sb[b] = scales[(size_t)n * U + u]; zb[b] = zeros[(size_t)n * U + u]; }
-      }
-      h2 xv[M][16];
-#pragma unroll
-      for (int m = 0; m < M; ++m) load_x(x + (size_t)m * K, u, xv[m]);
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        h2 zc1 = {}, zc2 = {};
-        if constexpr (FMT == WQ_FMT_W4G32) w4_consts(zb[b], zc1, zc2);
-        h2 wv[16];
-        decode<FMT>(raw[b], zc1, zc2, wv);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          float part = 0.0f;
-#pragma unroll
-          for (int p = 0; p < 16; ++p) part = __builtin_amdgcn_fdot2(wv[p], xv[m][p], part, false);
-          if constexpr (FMT == WQ_FMT_W4G32) acc[b][m] = __builtin_fmaf(part, f16_to_f32(sb[b]), acc[b][m]);
-          else acc[b][m] += part;
-        }
-      }
+  // Double-buffered chunk stream. Loads are never under a branch that the compute of the
+  // other buffer waits behind, so the wait before each compute covers only its own loads.
+  GemvStage<FMT, M, B> A, Bf;
+  auto chunk = [&](int i) { return wave + i * WK; };
+  auto act = [&](int i) { return chunk(i) * 64 + lane < U; };
+  if (NI > 0) {
+    gemv_load<FMT, M, B>(A, x, w, scales, zeros, row0, N, K, U, chunk(0), lane);
+    int i = 0;
+    for (; i + 2 < NI; i += 2) {
+      gemv_load<FMT, M, B>(Bf, x, w, scales, zeros, row0, N, K, U, chunk(i + 1), lane);
+      gemv_compute<FMT, M, B>(A, acc, act(i));
+      gemv_load<FMT, M, B>(A, x, w, scales, zeros, row0, N, K, U, chunk(i + 2), lane);
+      gemv_compute<FMT, M, B>(Bf, acc, act(i + 1));
+    }
+    if (i + 1 < NI) {
+      gemv_load<FMT, M, B>(Bf, x, w, scales, zeros, row0, N, K, U, chunk(i + 1), lane);
+      gemv_compute<FMT, M, B>(A, acc, act(i));
+      gemv_compute<FMT, M, B>(Bf, acc, act(i + 1));
+    } else {
+      gemv_compute<FMT, M, B>(A, acc, act(i));
     }
   }
 
+  if (WK == 1) {
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float t = wave_sum_to_lane63(acc[b][m]);
+        const int n = row0 + b;
+        if (lane == 63 && n < N) {
+          if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) t *= f16_to_f32(scales[n]);
+          y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)t);
+        }
+      }
+    return;
+  }
   __shared__ float red[MAX_WAVES][B * M];
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float t = wave_sum(acc[b][m]);
-      if (lane == 0) red[wave][b * M + m] = t;
+      const float t = wave_sum_to_lane63(acc[b][m]);
+      if (lane == 63) red[wave][b * M + m] = t;
     }
   __syncthreads();
   if (wave == 0 && lane < B * M) {
     const int b = lane / M, m = lane % M, n = row0 + b;
     float t = 0.0f;
-    for (int i = 0; i < WK; ++i) t += red[i][lane];
+    for (int i = 0; i < WK; ++i) t += red[i][lane];   // fixed order: deterministic
     if (n < N) {
       if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) t *= f16_to_f32(scales[n]);
       y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)t);
