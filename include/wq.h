@@ -25,12 +25,15 @@
  *   A scale that rounds to 0 makes the codes of its row or group 0 (and z = 0).
  *
  * Packed layout (identical for host and device): rows one after another; row n holds
- * K codes cut into units of 32 consecutive K, each unit stored whole, no padding:
+ * K codes cut into units of 32 consecutive K, stored in order with no padding:
  *   W8  32 B: byte j = q_j + 128.
  *   W4  16 B: four little-endian u32; word d holds codes 8d..8d+7, code 8d+2t in nibble t,
  *             code 8d+2t+1 in nibble t+4.
- *   W6  24 B: code j in bits 6j..6j+5 of the unit read as a 192-bit little-endian number.
- *   F16 64 B: fp16 weight j at bytes 2j..2j+1.
+ *   W6  24 B: code j in bits 6j..6j+5 of the unit read as a 192-bit little-endian number,
+ *       stored split by planes: a row's units are taken 64 at a time (a chunk; the last
+ *       chunk of a row may hold fewer, Uc), and in a chunk bytes 0..15 of its Uc units
+ *       come first, unit after unit, then bytes 16..23 of the same units.
+ *   F16 64 B: fp16 weight j at bytes 2j..2j+1 (so F16 is the plain row-major matrix).
  * So packed_w is exactly N*K*bits/8 bytes. scales: W8/W6 [N]; W4 [N][K/32] row-major.
  * zeros: W4 [N][K/32] row-major; otherwise unused (may be NULL). fp16 values are passed
  * as uint16_t bit patterns.

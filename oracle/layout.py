@@ -17,8 +17,14 @@ kernel consumes them. It gives no concrete layout. The layout used here is:
       Code 8d+2t sits in nibble t and code 8d+2t+1 in nibble t+4 (t = 0..3), nibble p
       being bits 4p .. 4p+3 of the word.
     - W6 (24 bytes): one 192-bit little-endian number; code j sits in bits 6j .. 6j+5.
+      These 24 bytes are not stored in one piece (see below).
     - F16 (64 bytes, the unquantized baseline): bytes 2j, 2j+1 hold the fp16 bits of
       weight j, little-endian.
+* W6 only, split by planes: the units of a row are taken 64 at a time ("chunks"; the
+  last chunk of a row may hold fewer, Uc units). In a chunk, bytes 0..15 of its units
+  come first, unit after unit (16*Uc bytes), then bytes 16..23 of its units (8*Uc
+  bytes). A chunk with one unit is therefore stored exactly as that unit. (A device
+  lane reads one unit, so each of the two loads of a wave reads one contiguous block.)
 * Metadata stays in logical order: W8/W6 scales [N]; W4 scales and zeros [N][K/32],
   row-major (group g of row n covers the same 32 K as unit g).
 
@@ -35,6 +41,7 @@ FMT_W6E3M2 = 3
 
 _BITS = {FMT_F16: 16, FMT_W8: 8, FMT_W4G32: 4, FMT_W6E3M2: 6}
 UNIT = 32
+CHUNK = 64          # units per W6 plane chunk
 
 
 def _bits(fmt):
@@ -120,9 +127,22 @@ def pack_scalar(fmt, codes):
                 for b in range(width):
                     if (v >> b) & 1:
                         acc |= 1 << (first + b)
-            off = (r * (k // UNIT) + u) * ub
-            out[off:off + ub] = acc.to_bytes(ub, "little")
+            unit = acc.to_bytes(ub, "little")
+            for i in range(ub):
+                out[_byte_home(fmt, r, u, i, k)] = unit[i]
     return np.frombuffer(bytes(out), dtype=np.uint8).copy()
+
+
+def _byte_home(fmt, r, u, i, k):
+    """Offset in the packed array of byte i of unit u of row r."""
+    ub = unit_bytes(fmt)
+    units = k // UNIT
+    if fmt != FMT_W6E3M2:
+        return (r * units + u) * ub + i
+    c, j = divmod(u, CHUNK)
+    uc = min(CHUNK, units - c * CHUNK)
+    base = (r * units + c * CHUNK) * ub
+    return base + 16 * j + i if i < 16 else base + 16 * uc + 8 * j + (i - 16)
 
 
 def unpack_scalar(fmt, packed, n, k):
@@ -135,8 +155,8 @@ def unpack_scalar(fmt, packed, n, k):
     codes = np.zeros((n, k), dtype=dtype)
     for r in range(n):
         for u in range(k // UNIT):
-            off = (r * (k // UNIT) + u) * ub
-            acc = int.from_bytes(bytes(packed[off:off + ub]), "little")
+            unit = bytes(int(packed[_byte_home(fmt, r, u, i, k)]) for i in range(ub))
+            acc = int.from_bytes(unit, "little")
             for j in range(UNIT):
                 first, width = code_field(fmt, j)
                 codes[r, UNIT * u + j] = _logical(fmt, (acc >> first) & ((1 << width) - 1))
@@ -173,7 +193,7 @@ def pack_vectorized(fmt, codes):
         c = c.reshape(n, k // 4, 4)
         v = c[:, :, 0] | (c[:, :, 1] << 6) | (c[:, :, 2] << 12) | (c[:, :, 3] << 18)
         b = np.stack([v & 0xFF, (v >> 8) & 0xFF, (v >> 16) & 0xFF], axis=-1).astype(np.uint8)
-        return b.reshape(-1)
+        return _w6_to_planes(b.reshape(n, k // UNIT, 24)).reshape(-1)
     if fmt == FMT_F16:
         return codes.astype(np.uint16).astype("<u2").view(np.uint8).reshape(-1)
     raise ValueError("unknown format %r" % fmt)
@@ -192,10 +212,35 @@ def unpack_vectorized(fmt, packed, n, k):
             out[:, :, _W4_ORDER[p]] = (words >> np.uint32(4 * p)) & 0xF
         return out.reshape(n, k)
     if fmt == FMT_W6E3M2:
-        b = packed.reshape(n, k // 4, 3).astype(np.uint32)
+        b = _w6_from_planes(packed.reshape(n, -1), k // UNIT).reshape(n, k // 4, 3).astype(np.uint32)
         v = b[:, :, 0] | (b[:, :, 1] << 8) | (b[:, :, 2] << 16)
         out = np.stack([(v >> s) & 0x3F for s in (0, 6, 12, 18)], axis=-1).astype(np.uint8)
         return out.reshape(n, k)
     if fmt == FMT_F16:
         return packed.view("<u2").reshape(n, k).astype(np.uint16)
     raise ValueError("unknown format %r" % fmt)
+
+
+def _w6_to_planes(units):
+    """[N, U, 24] unit-contiguous bytes -> [N, U*24] with every chunk of 64 units split into planes."""
+    n, u, _ = units.shape
+    parts = []
+    for c0 in range(0, u, CHUNK):
+        blk = units[:, c0:c0 + CHUNK, :]
+        parts.append(blk[:, :, :16].reshape(n, -1))
+        parts.append(blk[:, :, 16:].reshape(n, -1))
+    return np.concatenate(parts, axis=1)
+
+
+def _w6_from_planes(rows, u):
+    """Inverse of _w6_to_planes: [N, U*24] -> [N, U, 24]."""
+    n = rows.shape[0]
+    out = np.empty((n, u, 24), dtype=np.uint8)
+    pos = 0
+    for c0 in range(0, u, CHUNK):
+        uc = min(CHUNK, u - c0)
+        out[:, c0:c0 + uc, :16] = rows[:, pos:pos + 16 * uc].reshape(n, uc, 16)
+        pos += 16 * uc
+        out[:, c0:c0 + uc, 16:] = rows[:, pos:pos + 8 * uc].reshape(n, uc, 8)
+        pos += 8 * uc
+    return out

@@ -137,3 +137,12 @@ def test_dequant_w6_sign_dropped_is_caught():
     bad = oracle.fp16_bits(np.abs(oracle.e3m2_table()[codes]))
     mismatches = [c for c in range(64) if int(bad[0, c]) != pins.exact_dequant("w6", c, 0x3C00)]
     assert mismatches and all(int(good[0, c]) == pins.exact_dequant("w6", c, 0x3C00) for c in range(64))
+
+
+def test_w6_units_stored_whole_is_caught():
+    # two units stored one after the other (no planes) must not match the two-unit fixture
+    for name, codes, expected in pins.golden_pack_examples():
+        if name != "W6x2":
+            continue
+        whole = b"".join(oracle.pack_scalar(FMT_W6E3M2, np.array([codes[32 * i:32 * i + 32]])).tobytes() for i in range(2))
+        assert whole != expected and len(whole) == len(expected)

@@ -143,17 +143,17 @@ def test_quantizer_errors():
 # ------------------------------------------------------------------ layout
 def test_pack_matches_hand_derived_bytes():
     for name, codes, expected in pins.golden_pack_examples():
-        fmt = FMTS[name.lower()]
+        fmt = FMTS[name.lower().split("x")[0]]
         c = np.array([codes])
         assert bytes(oracle.pack_scalar(fmt, c)) == expected, name
         assert bytes(oracle.pack_vectorized(fmt, c)) == expected, name
 
 
 @pytest.mark.parametrize("name", ["w8", "w4", "w6", "f16"])
-def test_pack_scalar_equals_vectorized_and_round_trips(name):
+@pytest.mark.parametrize("n,k", [(3, 96), (2, 32 * 130)])       # 130 units: two full chunks of 64 and one of 2
+def test_pack_scalar_equals_vectorized_and_round_trips(name, n, k):
     fmt = FMTS[name]
     rng = np.random.default_rng(5)
-    n, k = 3, 96
     if name == "w8":
         codes = rng.integers(-127, 128, (n, k)).astype(np.int8)
     elif name == "w4":

@@ -137,6 +137,17 @@ void put_unit_w6(uint8_t* dst, const uint8_t* c) {
   for (int i = 0; i < 24; ++i) dst[i] = static_cast<uint8_t>(w[i >> 3] >> (8 * (i & 7)));
 }
 
+// W6 units are stored split by planes, 64 units ("chunk") at a time: bytes 0..15 of the
+// chunk's Uc units first, then bytes 16..23 of the same units. Returns where the two
+// slices of unit u of row r live.
+template <class P>
+void w6_unit_homes(P base, int64_t r, int64_t u, int64_t U, P& lo, P& hi) {
+  const int64_t c = u / 64, j = u % 64, uc = std::min<int64_t>(64, U - 64 * c);
+  P chunk = base + (r * U + 64 * c) * 24;
+  lo = chunk + 16 * j;
+  hi = chunk + 16 * uc + 8 * j;
+}
+
 int check_weights(const float* w, int64_t K, int64_t r) {
   for (int64_t k = 0; k < K; ++k)
     if (!std::isfinite(w[r * K + k])) return WQ_ERR_NONFINITE;
@@ -262,7 +273,15 @@ int wq_pack_fp6(const float* w, int64_t N, int64_t K, void* packed, uint16_t* sc
       const double s = f16_bits_to_f64(sb);
       scales[r] = sb;
       for (int64_t k = 0; k < K; ++k) c[k] = s > 0 ? e3m2_encode(static_cast<double>(row[k]) / s) : 0;
-      for (int64_t u = 0; u < U; ++u) put_unit_w6(out + (r * U + u) * 24, c.data() + 32 * u);
+      for (int64_t u = 0; u < U; ++u) {
+        uint8_t unit[24];
+        put_unit_w6(unit, c.data() + 32 * u);
+        uint8_t* lo;
+        uint8_t* hi;
+        w6_unit_homes(out, r, u, U, lo, hi);
+        std::memcpy(lo, unit, 16);
+        std::memcpy(hi, unit + 16, 8);
+      }
     }
     return static_cast<int>(WQ_OK);
   });
@@ -294,7 +313,12 @@ int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_
     uint8_t* o = static_cast<uint8_t*>(codes);
     for (int64_t r = 0; r < N; ++r)
       for (int64_t u = 0; u < U; ++u) {
-        const uint8_t* p = in + (r * U + u) * 24;
+        const uint8_t* lo;
+        const uint8_t* hi;
+        w6_unit_homes(in, r, u, U, lo, hi);
+        uint8_t p[24];
+        std::memcpy(p, lo, 16);
+        std::memcpy(p + 16, hi, 8);
         for (int j = 0; j < 32; ++j) {
           int v = 0;
           for (int b = 0; b < 6; ++b) {

@@ -49,28 +49,42 @@ __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, 
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
 // ---------------------------------------------------------------- raw units and loads
+// A 32-code unit in registers. W6 keeps its two plane slices (16 + 8 bytes), which read in
+// order are the unit's 192-bit little-endian stream.
 template <int FMT> struct Raw;
 template <> struct Raw<WQ_FMT_W8> { uint4 a, b; };
 template <> struct Raw<WQ_FMT_W4G32> { uint4 a; };
-template <> struct Raw<WQ_FMT_W6E3M2> { uint3 a, b; };
+template <> struct Raw<WQ_FMT_W6E3M2> { uint4 a; uint2 b; };
 template <> struct Raw<WQ_FMT_F16> { uint4 a, b, c, d; };
 
 template <int FMT> constexpr int unit_bytes() {
   return FMT == WQ_FMT_W8 ? 32 : FMT == WQ_FMT_W4G32 ? 16 : FMT == WQ_FMT_W6E3M2 ? 24 : 64;
 }
 
+// Byte offsets, from the start of row n, of the two plane slices of W6 unit u (U units per row).
+__device__ __forceinline__ void w6_homes(int u, int U, uint32_t& lo, uint32_t& hi) {
+  const int c = u >> 6, j = u & 63, uc = min(64, U - 64 * c);
+  lo = (uint32_t)(64 * c * 24 + 16 * j);
+  hi = (uint32_t)(64 * c * 24 + 16 * uc + 8 * j);
+}
+
+// Unit u of row n (used by the MFMA and dequant kernels, where a lane owns a whole unit).
 template <int FMT>
-__device__ __forceinline__ void load_raw(const uint8_t* __restrict__ p, Raw<FMT>& r) {
+__device__ __forceinline__ void load_unit(const uint8_t* __restrict__ w, int n, int u, int U, Raw<FMT>& r) {
+  constexpr int UB = unit_bytes<FMT>();
+  const uint8_t* row = w + (size_t)n * U * UB;
   if constexpr (FMT == WQ_FMT_W8) {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
+    const uint4* q = reinterpret_cast<const uint4*>(row + (size_t)u * UB);
     r.a = q[0]; r.b = q[1];
   } else if constexpr (FMT == WQ_FMT_W4G32) {
-    r.a = *reinterpret_cast<const uint4*>(p);
+    r.a = *reinterpret_cast<const uint4*>(row + (size_t)u * UB);
   } else if constexpr (FMT == WQ_FMT_W6E3M2) {
-    const uint3* q = reinterpret_cast<const uint3*>(p);
-    r.a = q[0]; r.b = q[1];
+    uint32_t lo, hi;
+    w6_homes(u, U, lo, hi);
+    r.a = *reinterpret_cast<const uint4*>(row + lo);
+    r.b = *reinterpret_cast<const uint2*>(row + hi);
   } else {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
+    const uint4* q = reinterpret_cast<const uint4*>(row + (size_t)u * UB);
     r.a = q[0]; r.b = q[1]; r.c = q[2]; r.d = q[3];
   }
 }
@@ -106,7 +120,7 @@ __device__ __forceinline__ void decode(const Raw<FMT>& r, h2 zc1, h2 zc2, h2 (&o
     for (int i = 0; i < 4; ++i) decode_w4_word(w[i], zc1, zc2, out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
   } else if constexpr (FMT == WQ_FMT_W6E3M2) {
     u32x6 v;
-    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.b.x; v[4] = r.b.y; v[5] = r.b.z;
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w; v[4] = r.b.x; v[5] = r.b.y;
     const h32 h = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(v, 1.0f);
 #pragma unroll
     for (int p = 0; p < 16; ++p) { out[p][0] = h[2 * p]; out[p][1] = h[2 * p + 1]; }
@@ -126,16 +140,6 @@ __device__ __forceinline__ void w4_consts(uint16_t zbits, h2& zc1, h2& zc2) {
   const _Float16 c1 = (_Float16)-1024.0f - z, c2 = (_Float16)-64.0f - z;   // exact integers
   zc1 = h2{c1, c1};
   zc2 = h2{c2, c2};
-}
-
-// x[32u .. 32u+32) of one row as 16 fp16 pairs
-__device__ __forceinline__ void load_x(const uint16_t* __restrict__ xrow, int u, h2 (&xv)[16]) {
-  const uint4* p = reinterpret_cast<const uint4*>(xrow + 32 * u);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 v = p[i];
-    xv[4 * i] = as_h2(v.x); xv[4 * i + 1] = as_h2(v.y); xv[4 * i + 2] = as_h2(v.z); xv[4 * i + 3] = as_h2(v.w);
-  }
 }
 
 // ---------------------------------------------------------------- wave reduction
@@ -165,63 +169,77 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// Streaming (nontemporal) loads of packed weights: each byte is used once per call.
-template <int FMT>
-__device__ __forceinline__ void load_raw_nt(const uint8_t* __restrict__ p, Raw<FMT>& r) {
-  auto ld4 = [](const uint8_t* q) {
-    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
-    return make_uint4(t[0], t[1], t[2], t[3]);
-  };
-  if constexpr (FMT == WQ_FMT_W8) {
-    r.a = ld4(p); r.b = ld4(p + 16);
-  } else if constexpr (FMT == WQ_FMT_W4G32) {
-    r.a = ld4(p);
-  } else if constexpr (FMT == WQ_FMT_W6E3M2) {
-    const u32x2* q = reinterpret_cast<const u32x2*>(p);       // 24-byte units are 8-byte aligned
-    const u32x2 t0 = __builtin_nontemporal_load(q), t1 = __builtin_nontemporal_load(q + 1), t2 = __builtin_nontemporal_load(q + 2);
-    r.a = make_uint3(t0[0], t0[1], t1[0]);
-    r.b = make_uint3(t1[1], t2[0], t2[1]);
-  } else {
-    r.a = ld4(p); r.b = ld4(p + 16); r.c = ld4(p + 32); r.d = ld4(p + 48);
-  }
+__device__ __forceinline__ uint4 ld_nt16(const uint8_t* p) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ uint2 ld_nt8(const uint8_t* p) {
+  const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(t[0], t[1]);
 }
 
 // ---------------------------------------------------------------- GEMV (M <= GEMV_MAX_M)
-// One lane per 32-code unit, lanes along K: a wave covers a 64-unit chunk (2048 K) of B
-// rows. Workgroup = B rows x all of K; its WK waves take the chunks c = wave, wave + WK, ...
-// Each wave double-buffers its chunk stream: while chunk i is decoded, the loads of chunk
-// i+1 (x first, then the B rows) are in flight.
+// Lanes run along K. Lane l of a wave owns one "segment" of SEG consecutive K of a row
+// and reads its weight bytes with one 16-byte load (W6: a 16-byte and an 8-byte load),
+// so every load instruction of a wave reads one contiguous block:
+//   W4: SEG = 32 (one unit = one zero-point group)   W6: SEG = 32 (one unit, two planes)
+//   W8: SEG = 16 (half a unit)                       F16: SEG = 8
+// A wave covers a chunk of 64 segments of B rows. The workgroup is B rows x all of K; its
+// WK waves take the chunks c = wave, wave + WK, ... and double-buffer them: while chunk i
+// is decoded, the loads of chunk i+1 (x first, then the B rows) are in flight.
 //
 // The decode skips the per-weight bias and zero-point subtraction. A lane dots x with
 // the biased fp16 values it forms in one v_and_or_b32 / v_perm_b32:
 //   W8: (1152 + q)                      -> sum - 1152 X
 //   W4: (1024 + q) for nibbles 0 and 2, (1024 + 16 q) for nibbles 1 and 3
 //                                       -> lo + hi/16 - (1024 X_lo + 64 X_hi) - z (X_lo + X_hi)
-// where X, X_lo, X_hi are sums of x over the unit's positions, shared by all rows of the
-// wave. Every product is exact in fp32; one-hot inputs give exact results.
+// where X, X_lo, X_hi are sums of x over the segment, shared by all rows of the wave.
+// Every product is exact in fp32; one-hot inputs give exact results.
+template <int FMT> constexpr int seg_codes() { return FMT == WQ_FMT_W8 ? 16 : FMT == WQ_FMT_F16 ? 8 : 32; }
+
+template <int FMT> struct Seg { uint4 a; };
+template <> struct Seg<WQ_FMT_W6E3M2> { uint4 a; uint2 b; };
+
 template <int FMT, int M, int B>
 struct GemvStage {
-  h2 x[M][16];
-  Raw<FMT> w[B];
+  h2 x[M][seg_codes<FMT>() / 2];
+  Seg<FMT> w[B];
   uint16_t s[B], z[B];
 };
 
 template <int FMT, int M, int B>
 __device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16_t* __restrict__ x,
                                           const uint8_t* __restrict__ w, const uint16_t* __restrict__ scales,
-                                          const uint16_t* __restrict__ zeros, int row0, int N, int K, int U, int c,
-                                          int lane) {
-  constexpr int UB = unit_bytes<FMT>();
-  const int u = min(c * 64 + lane, U - 1);   // lanes past the row end read a valid unit and are masked later
+                                          const uint16_t* __restrict__ zeros, int row0, int N, int K, int c, int lane) {
+  constexpr int L = seg_codes<FMT>();
+  const int S = K / L;                         // segments per row
+  const int sg = min(c * 64 + lane, S - 1);    // lanes past the row end read a valid segment, masked later
 #pragma unroll
-  for (int m = 0; m < M; ++m) load_x(x + (size_t)m * K, u, st.x[m]);
+  for (int m = 0; m < M; ++m) {
+    const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)L * sg);
+#pragma unroll
+    for (int i = 0; i < L / 8; ++i) {
+      const uint4 v = xp[i];
+      st.x[m][4 * i] = as_h2(v.x); st.x[m][4 * i + 1] = as_h2(v.y);
+      st.x[m][4 * i + 2] = as_h2(v.z); st.x[m][4 * i + 3] = as_h2(v.w);
+    }
+  }
+  const size_t row_bytes = (size_t)K * unit_bytes<FMT>() / 32;
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     const int n = min(row0 + b, N - 1);
-    load_raw_nt<FMT>(w + ((size_t)n * U + u) * UB, st.w[b]);
+    const uint8_t* row = w + (size_t)n * row_bytes;          // wave-uniform
+    if constexpr (FMT == WQ_FMT_W6E3M2) {
+      uint32_t lo, hi;
+      w6_homes(sg, S, lo, hi);
+      st.w[b].a = ld_nt16(row + lo);
+      st.w[b].b = ld_nt8(row + hi);
+    } else {
+      st.w[b].a = ld_nt16(row + 16u * (uint32_t)sg);
+    }
     if constexpr (FMT == WQ_FMT_W4G32) {
-      st.s[b] = scales[(size_t)n * U + u];
-      st.z[b] = zeros[(size_t)n * U + u];
+      st.s[b] = scales[(size_t)n * S + sg];
+      st.z[b] = zeros[(size_t)n * S + sg];
     }
   }
 }
@@ -229,6 +247,7 @@ __device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16
 template <int FMT, int M, int B>
 __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, float (&acc)[B][M], bool active) {
   if (!active) return;
+  constexpr int P = seg_codes<FMT>() / 2;   // fp16 pairs per segment
   const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
   if constexpr (FMT == WQ_FMT_W4G32) {
     const uint32_t m0 = in_vgpr(0x000F000Fu), m1 = in_vgpr(0x00F000F0u), mag = in_vgpr(0x64006400u);
@@ -280,7 +299,7 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
     for (int m = 0; m < M; ++m) {
       float a = 0.f, c = 0.f;
 #pragma unroll
-      for (int p = 0; p < 16; p += 2) {
+      for (int p = 0; p < P; p += 2) {
         a = __builtin_amdgcn_fdot2(st.x[m][p], ones, a, false);
         c = __builtin_amdgcn_fdot2(st.x[m][p + 1], ones, c, false);
       }
@@ -288,11 +307,10 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const uint32_t wd[8] = {st.w[b].a.x, st.w[b].a.y, st.w[b].a.z, st.w[b].a.w,
-                              st.w[b].b.x, st.w[b].b.y, st.w[b].b.z, st.w[b].b.w};
-      h2 v[16];
+      const uint32_t wd[4] = {st.w[b].a.x, st.w[b].a.y, st.w[b].a.z, st.w[b].a.w};
+      h2 v[P];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         v[2 * i] = as_h2(__builtin_amdgcn_perm(mag, wd[i], 0x04010400u));       // (1024+u0, 1024+u1)
         v[2 * i + 1] = as_h2(__builtin_amdgcn_perm(mag, wd[i], 0x04030402u));   // (1024+u2, 1024+u3)
       }
@@ -300,7 +318,7 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
       for (int m = 0; m < M; ++m) {
         float a = 0.f, c = 0.f;
 #pragma unroll
-        for (int p = 0; p < 16; p += 2) {
+        for (int p = 0; p < P; p += 2) {
           a = __builtin_amdgcn_fdot2(v[p], st.x[m][p], a, false);
           c = __builtin_amdgcn_fdot2(v[p + 1], st.x[m][p + 1], c, false);
         }
@@ -310,13 +328,22 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
   } else {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      h2 v[16];
-      decode<FMT>(st.w[b], h2{}, h2{}, v);
+      h2 v[P];
+      if constexpr (FMT == WQ_FMT_W6E3M2) {
+        u32x6 u;
+        u[0] = st.w[b].a.x; u[1] = st.w[b].a.y; u[2] = st.w[b].a.z; u[3] = st.w[b].a.w;
+        u[4] = st.w[b].b.x; u[5] = st.w[b].b.y;
+        const h32 h = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(u, 1.0f);
+#pragma unroll
+        for (int p = 0; p < 16; ++p) { v[p][0] = h[2 * p]; v[p][1] = h[2 * p + 1]; }
+      } else {
+        v[0] = as_h2(st.w[b].a.x); v[1] = as_h2(st.w[b].a.y); v[2] = as_h2(st.w[b].a.z); v[3] = as_h2(st.w[b].a.w);
+      }
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float a = 0.f, c = 0.f;
 #pragma unroll
-        for (int p = 0; p < 16; p += 2) {
+        for (int p = 0; p < P; p += 2) {
           a = __builtin_amdgcn_fdot2(v[p], st.x[m][p], a, false);
           c = __builtin_amdgcn_fdot2(v[p + 1], st.x[m][p + 1], c, false);
         }
@@ -332,7 +359,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemv_kernel(const uint16_t* __
                                                               const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
                                                               int N, int K) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, WK = blockDim.x >> 6;
-  const int U = K >> 5, C = (U + 63) >> 6;
+  const int S = K / seg_codes<FMT>(), C = (S + 63) >> 6;
   const int row0 = blockIdx.x * B;
   const int NI = wave < C ? (C - wave + WK - 1) / WK : 0;   // chunks of this wave (wave-uniform)
   float acc[B][M];
@@ -341,22 +368,22 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemv_kernel(const uint16_t* __
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[b][m] = 0.0f;
 
-  // Double-buffered chunk stream. Loads are never under a branch that the compute of the
+  // Double-buffered chunk stream. No load sits under a branch that the compute of the
   // other buffer waits behind, so the wait before each compute covers only its own loads.
   GemvStage<FMT, M, B> A, Bf;
   auto chunk = [&](int i) { return wave + i * WK; };
-  auto act = [&](int i) { return chunk(i) * 64 + lane < U; };
+  auto act = [&](int i) { return chunk(i) * 64 + lane < S; };
   if (NI > 0) {
-    gemv_load<FMT, M, B>(A, x, w, scales, zeros, row0, N, K, U, chunk(0), lane);
+    gemv_load<FMT, M, B>(A, x, w, scales, zeros, row0, N, K, chunk(0), lane);
     int i = 0;
     for (; i + 2 < NI; i += 2) {
-      gemv_load<FMT, M, B>(Bf, x, w, scales, zeros, row0, N, K, U, chunk(i + 1), lane);
+      gemv_load<FMT, M, B>(Bf, x, w, scales, zeros, row0, N, K, chunk(i + 1), lane);
       gemv_compute<FMT, M, B>(A, acc, act(i));
-      gemv_load<FMT, M, B>(A, x, w, scales, zeros, row0, N, K, U, chunk(i + 2), lane);
+      gemv_load<FMT, M, B>(A, x, w, scales, zeros, row0, N, K, chunk(i + 2), lane);
       gemv_compute<FMT, M, B>(Bf, acc, act(i + 1));
     }
     if (i + 1 < NI) {
-      gemv_load<FMT, M, B>(Bf, x, w, scales, zeros, row0, N, K, U, chunk(i + 1), lane);
+      gemv_load<FMT, M, B>(Bf, x, w, scales, zeros, row0, N, K, chunk(i + 1), lane);
       gemv_compute<FMT, M, B>(A, acc, act(i));
       gemv_compute<FMT, M, B>(Bf, acc, act(i + 1));
     } else {
@@ -405,7 +432,6 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void mfma_kernel(const uint16_t* __
                                                               const uint16_t* __restrict__ scales,
                                                               const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
                                                               int M, int N, int K) {
-  constexpr int UB = unit_bytes<FMT>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, WK = blockDim.x >> 6;
   const int nl = lane & 15, q = lane >> 4;
   const int n = blockIdx.x * 16 + nl, nc = min(n, N - 1);
@@ -422,7 +448,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void mfma_kernel(const uint16_t* __
     for (int i = 0; i < 4; ++i) xa[i] = h8{};
     if (u < U) {
       Raw<FMT> raw;
-      load_raw<FMT>(w + ((size_t)nc * U + u) * UB, raw);
+      load_unit<FMT>(w, nc, u, U, raw);
       h2 zc1 = {}, zc2 = {};
       uint16_t sbits = 0;
       if constexpr (FMT == WQ_FMT_W4G32) {
@@ -475,13 +501,12 @@ template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ scales,
                                                       const uint16_t* __restrict__ zeros, uint16_t* __restrict__ out,
                                                       int N, int K) {
-  constexpr int UB = unit_bytes<FMT>();
   const int U = K >> 5;
   const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (size_t)N * U) return;
   const int n = (int)(gid / U), u = (int)(gid % U);
   Raw<FMT> raw;
-  load_raw<FMT>(w + gid * UB, raw);
+  load_unit<FMT>(w, n, u, U, raw);
   h2 zc1 = {}, zc2 = {};
   float s = 1.0f;
   if constexpr (FMT == WQ_FMT_W4G32) {
@@ -517,12 +542,15 @@ struct GemvPlan {
   int grid;   // workgroups
 };
 
-// Enough waves to keep 8 per CU busy (256 CUs), with as many rows per wave as that allows
-// (x is loaded once per chunk and reused for every row of the wave).
-GemvPlan plan_gemv(int64_t N, int64_t K) {
-  const int64_t U = K / 32, C = (U + 63) / 64;
-  const int WK = static_cast<int>(C < MAX_WAVES ? C : MAX_WAVES);
-  int B = 4;
+// Rows per wave B and waves per workgroup WK: four rows per wave (x is loaded once per
+// chunk and reused for every row of the wave), and enough waves to fill the chip: WK grows
+// (up to the number of chunks) until there are ~16 waves per CU, and B shrinks when N is
+// too small to give 8 per CU.
+GemvPlan plan_gemv(int fmt, int64_t N, int64_t K) {
+  const int64_t L = fmt == WQ_FMT_W8 ? 16 : fmt == WQ_FMT_F16 ? 8 : 32;
+  const int64_t C = (K / L + 63) / 64;
+  int B = 4, WK = 1;
+  while (WK < MAX_WAVES && WK < C && ((N + B - 1) / B) * WK < 4096) ++WK;
   while (B > 1 && ((N + B - 1) / B) * WK < 2048) B >>= 1;
   return {B, WK, static_cast<int>((N + B - 1) / B)};
 }
@@ -547,7 +575,7 @@ template <int FMT>
 hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
                              uint16_t* y, int M, int N, int K) {
   if (M <= GEMV_MAX_M) {
-    const GemvPlan p = plan_gemv(N, K);
+    const GemvPlan p = plan_gemv(FMT, N, K);
     switch (M) {
       case 1: return launch_gemv_m<FMT, 1>(p, s, x, w, sc, z, y, N, K);
       case 2: return launch_gemv_m<FMT, 2>(p, s, x, w, sc, z, y, N, K);
@@ -626,7 +654,7 @@ const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 32 || K % 32) return "";
   const int64_t mm = M < MFMA_M ? M : MFMA_M;
   if (mm <= GEMV_MAX_M) {
-    const GemvPlan p = plan_gemv(N, K);
+    const GemvPlan p = plan_gemv(fmt, N, K);
     snprintf(buf, sizeof(buf), "gemv_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), p.B);
   } else {
     snprintf(buf, sizeof(buf), "mfma_kernel<%d>", fmt);
