@@ -4,19 +4,22 @@
 Metric: weight-stream HBM GB/s (and % of the 8 TB/s peak) of the fused dequant + linear.
 A step is one pass of the device hot path over one batch. By default the batch is the
 three Llama-7B-shaped W4 (int4, group 32) linears at M = 1 ([4096x4096], [11008x4096],
-[4096x11008]), one wq_linear call each. Quantize + pack happen once, offline, before
+[4096x11008]). Quantize + pack happen once, offline, before
 timing (the pages re-pack weights before inference).
 
 Method:
 * Weights are packed on the host by libwq and copied to HBM R times, with R * (bytes per
   step) >= 1 GiB. Step s reads copy s % R, so the 256 MB Infinity Cache cannot serve the
   weights from an earlier step: every step streams from HBM, as a real decode does.
-* The K timed steps run as replays of a HIP graph that holds R steps (no host gaps),
-  bracketed by synchronize + events on the launch stream.
-* Roofline: the same launches, one at a time, each bracketed by events on the launch
-  stream, give the average duration of the dominant kernel.
-* fp16 baselines: libwq's own fp16 kernel and torch's F.linear (hipBLASLt) on the same
-  shapes, timed the same way.
+* A step launches all linears of the workload in one wq_linear_grouped call (or, with
+  --separate, one wq_linear call each). The K timed steps run as replays of a HIP graph
+  that holds R steps (no host gaps), bracketed by synchronize + events on the launch
+  stream. The other launch style and each linear alone are timed the same way and
+  reported beside it.
+* Roofline: the step holds only the dominant kernel's launches, back to back, so its
+  average launch duration is the timed-region time per step over its launches.
+* fp16 baselines: libwq's own fp16 kernel (grouped and separate) and torch's F.linear
+  (hipBLASLt) on the same shapes, timed the same way.
 * cpu_baseline: the CPU oracle (unpack + dequant + float64 product) on a bounded sample
   of rows of the same linears, on this host's cores.
 Prints one JSON line.
@@ -49,10 +52,39 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="llama7b_w4g32_linears", choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--m", type=int, default=None, help="rows of x (default: the workload's first M)")
+    ap.add_argument("--separate", action="store_true",
+                    help="time one wq_linear call per linear instead of one grouped call per step")
     ap.add_argument("--no-baselines", action="store_true", help="skip the fp16 baselines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of 512 MiB (a known-size kernel for counter calibration)")
     return ap.parse_args()
+
+
+KERNEL_SRC = os.path.join(ROOT, "weight_only_quantized_dequant_amd", "csrc", "wq_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE + WRITE_SIZE,
+    scaled by the same counters on a plain copy of known size), or None when there is no summary
+    for this kernel and workload or the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = rec.get("entries", {}).get("%s|%s" % (workload, kernel))
+    if not e or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
 
 
 def metadata_bytes(fmt, n, k):
@@ -123,18 +155,6 @@ def time_steps(torch, run_step, steps, warmup, rot):
     return e0.elapsed_time(e1)
 
 
-def per_launch_ms(torch, launches, reps):
-    """Average duration (ms) of each launch, each bracketed by events on the launch stream."""
-    out = []
-    for fn in launches:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for i, (a, b) in enumerate(evs):
-            a.record(); fn(i); b.record()
-        torch.cuda.synchronize()
-        out.append(float(np.mean([a.elapsed_time(b) for a, b in evs])))
-    return out
-
-
 def cpu_baseline(fmt, linears_host, seconds):
     """The oracle (test infrastructure) timed on a bounded sample: per linear, a block of rows is
     unpacked, dequantized and multiplied in float64, repeated until `seconds` have passed."""
@@ -180,6 +200,12 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 1
     wq.lib()
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     fmt_name, shapes, ms = inputs.WORKLOADS[args.workload]
     fmt = FMT_OF[fmt_name]
     m = args.m if args.m is not None else ms[0]
@@ -194,39 +220,67 @@ def main():
     lins = [Linear(torch, fmt, w, x, rot) for (w, x) in host]
     step_io = sum(l.io_bytes for l in lins)
 
-    def run_step(i):
-        for l in lins:
-            l.launch(i % rot)
+    def grouped_step(group, rotation):
+        """One step: every linear of the workload in one wq_linear_grouped launch."""
+        def run(i):
+            items = []
+            for l in group:
+                p, sc, z = l.copies[i % rotation]
+                items.append((l.x, p, sc, z, l.y, l.n, l.k))
+            wq.wq_linear_grouped(items, m, group[0].fmt)
+        return run
+
+    def separate_step(group, rotation):
+        """One step: one wq_linear launch per linear."""
+        def run(i):
+            for l in group:
+                l.launch(i % rotation)
+        return run
 
     steps = args.steps
-    ms_total = time_steps(torch, run_step, steps, args.warmup, rot)
+    grouped = not args.separate
+    step_fn = grouped_step(lins, rot) if grouped else separate_step(lins, rot)
+    ms_total = time_steps(torch, step_fn, steps, args.warmup, rot)
     value = step_weight_bytes * steps / (ms_total * 1e-3) / 1e9
 
-    # roofline of the dominant kernel: average duration over the launches of one step, eager + events
-    reps = max(20, min(200, steps))
-    durs = per_launch_ms(torch, [lambda i, l=l: l.launch(i % rot) for l in lins], reps)
-    by_kernel = {}
-    for l, d in zip(lins, durs):
-        e = by_kernel.setdefault(l.kernel, [0.0, 0, 0])
-        e[0] += d; e[1] += l.weight_bytes + l.io_bytes; e[2] += 1
-    dom = max(by_kernel.items(), key=lambda kv: kv[1][0])
-    dom_name, (dom_ms, dom_bytes, dom_launches) = dom
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    # roofline of the dominant kernel, from the same timed region: the step holds only this
+    # kernel's launches, back to back in the graph, so its average duration is the step time
+    # divided by its launches per step
+    launches = 1 if grouped else len(lins)
+    if grouped:
+        dom_name = wq.wq_linear_grouped_kernel_name(fmt, m, shapes)
+    else:
+        dom_name = lins[0].kernel if len({l.kernel for l in lins}) == 1 else "mixed"
+    step_bytes = step_weight_bytes + step_io
+    avg_launch_ms = ms_total / steps / launches
+    achieved = step_bytes / launches / (avg_launch_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": dom_name, "launches_per_step": dom_launches,
-                "avg_launch_us": round(1e3 * dom_ms / dom_launches, 3),
-                "algorithmic_bytes_per_launch": int(dom_bytes / dom_launches),
-                "per_shape_us": {"%dx%d" % (l.n, l.k): round(1e3 * d, 3) for l, d in zip(lins, durs)}}
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(dom_name, args.workload),
+                "kernel": dom_name, "launches_per_step": launches,
+                "avg_launch_us": round(1e3 * avg_launch_ms, 3),
+                "algorithmic_bytes_per_launch": int(step_bytes / launches)}
 
     extras = {}
+    # each linear alone (one launch per step, its own graph): per-shape durations and rates
+    per_shape = {}
+    for l in lins:
+        ms_l = time_steps(torch, separate_step([l], rot), steps, args.warmup, rot)
+        per_shape["%dx%d" % (l.n, l.k)] = {"us": round(1e3 * ms_l / steps, 3),
+                                           "GB/s": round(l.weight_bytes * steps / (ms_l * 1e-3) / 1e9, 1)}
+    extras["per_linear"] = per_shape
+    other = separate_step(lins, rot) if grouped else grouped_step(lins, rot)
+    ms_other = time_steps(torch, other, steps, args.warmup, rot)
+    extras["separate_calls" if grouped else "grouped_call"] = {
+        "GB/s": round(step_weight_bytes * steps / (ms_other * 1e-3) / 1e9, 1), "ms_per_step": round(ms_other / steps, 5)}
+
     if not args.no_baselines:
         f16_bytes = sum(2 * n * k for n, k in shapes)
         rot16 = max(1, math.ceil(ROTATE_BYTES / f16_bytes))
         f16 = [Linear(torch, wq.FMT_F16, w, x, rot16) for (w, x) in host]
-        ms16 = time_steps(torch, lambda i: [l.launch(i % rot16) for l in f16], steps, args.warmup, rot16)
-        gbs16 = f16_bytes * steps / (ms16 * 1e-3) / 1e9
-        # torch F.linear (hipBLASLt) on fp16 weights, same rotation
+        ms16g = time_steps(torch, grouped_step(f16, rot16), steps, args.warmup, rot16)
+        ms16s = time_steps(torch, separate_step(f16, rot16), steps, args.warmup, rot16)
+        # torch F.linear (hipBLASLt) on the same fp16 weights, same rotation
         import torch.nn.functional as F
         tw = [[c[0].view(torch.float16).view(l.n, l.k) for c in l.copies] for l in f16]
         tx = [l.x.view(torch.float16) for l in f16]
@@ -234,14 +288,15 @@ def main():
             for j in range(len(f16)):
                 F.linear(tx[j], tw[j][i % rot16])
         msv = time_steps(torch, vendor_step, steps, args.warmup, rot16)
-        gbsv = f16_bytes * steps / (msv * 1e-3) / 1e9
-        best16_ms = min(ms16, msv)
+        gbs = lambda ms_: round(f16_bytes * steps / (ms_ * 1e-3) / 1e9, 1)
+        best16_ms = min(ms16g, ms16s, msv)
         bytes_ratio = f16_bytes / step_weight_bytes
         speedup = best16_ms / ms_total
         extras["fp16_baseline"] = {
-            "libwq_f16": {"GB/s": round(gbs16, 1), "ms_per_step": round(ms16 / steps, 5)},
-            "torch_F_linear": {"GB/s": round(gbsv, 1), "ms_per_step": round(msv / steps, 5)},
-            "speedup_vs_faster_fp16": round(speedup, 3), "bytes_ratio": round(bytes_ratio, 3),
+            "libwq_f16_grouped": {"GB/s": gbs(ms16g), "ms_per_step": round(ms16g / steps, 5)},
+            "libwq_f16_separate": {"GB/s": gbs(ms16s), "ms_per_step": round(ms16s / steps, 5)},
+            "torch_F_linear": {"GB/s": gbs(msv), "ms_per_step": round(msv / steps, 5)},
+            "speedup_vs_fastest_fp16": round(speedup, 3), "bytes_ratio": round(bytes_ratio, 3),
             "speedup_over_0.8x_bytes_ratio": round(speedup / (0.8 * bytes_ratio), 3)}
         del f16, tw, tx
         torch.cuda.empty_cache()
@@ -265,6 +320,7 @@ def main():
                    "shapes_NxK": ["%dx%d" % s for s in shapes], "weight_bytes_per_step": step_weight_bytes,
                    "io_bytes_per_step": step_io, "rotation_copies": rot,
                    "tflops": round(flops * steps / (ms_total * 1e-3) / 1e12, 3),
+                   "launch": "one wq_linear_grouped call per step" if grouped else "one wq_linear call per linear",
                    "timing": "HIP graph replays of %d steps, events on the launch stream" % rot},
         "roofline": roofline,
         "cpu_baseline": cpu,

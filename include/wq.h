@@ -116,9 +116,32 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
 int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros, uint16_t* y,
               int64_t M, int64_t N, int64_t K, int fmt, void* stream);
 
+/* One independent linear of a grouped call: device pointers as for wq_linear. */
+typedef struct {
+  const uint16_t* x;       /* [M,K] fp16 */
+  const void* packed_w;    /* packed weights of fmt */
+  const uint16_t* scales;  /* as for wq_linear */
+  const uint16_t* zeros;   /* W4 only, else NULL */
+  uint16_t* y;             /* [M,N] fp16 output */
+  int64_t N, K;
+} wq_linear_item;
+
+/* On the device: count (0..16) independent linears of one format and one M in a single
+ * launch, each computing exactly what wq_linear computes for it (same decode; the fp32
+ * sum may run in another order when the items' sizes differ a lot). One launch
+ * instead of count means the GPU ramps up and drains once; in a decode step this fits
+ * q/k/v or gate/up, and any set of linears whose inputs are ready. Items must not write
+ * into one another's inputs. For M > 4 the items run as separate launches. Errors: as
+ * wq_linear, per item, all checked before any launch; WQ_ERR_ARG also for count
+ * outside 0..16 or items == NULL. */
+int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt, void* stream);
+
 /* Name of the kernel wq_linear launches for (fmt, M, N, K) (for profiles), or "" if the
  * arguments are invalid. Host only; static storage. */
 const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
+
+/* Name of the kernel wq_linear_grouped launches for count items of sizes N[i] x K[i], or "". */
+const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, const int64_t* K, int count);
 
 #ifdef __cplusplus
 }

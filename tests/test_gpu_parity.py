@@ -157,3 +157,55 @@ def test_workload_full_size_sampled(name, fmt):
             check_linear(y[:, rows], x[:m], wd, "%s linear %d (%dx%d) m %d" % (name, li, n, k, m))
         del dw
         torch_cuda().cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ grouped launches
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("m", [1, 3, 7])
+def test_grouped_matches_separate_calls(fmt, m):
+    torch = torch_cuda()
+    shapes = [(40, 2080), (300, 4096), (64, 6144), (17, 96)]
+    dws, xs = [], []
+    for i, (n, k) in enumerate(shapes):
+        w = _weights(n, k, 50 + i)
+        dws.append(DeviceWeights(fmt, w))
+        xs.append(inputs.small_case(60 + i, 1, k, m)[1])
+    sep = [dw.linear(x) for dw, x in zip(dws, xs)]
+    ys = [torch.zeros((m, dw.n), dtype=torch.int16, device="cuda:0") for dw in dws]
+    xd = [dev(x) for x in xs]
+    items = [(xd[i], dw.packed, dw.scales, dw.zeros, ys[i], dw.n, dw.k) for i, dw in enumerate(dws)]
+    wq.wq_linear_grouped(items, m, fmt)
+    torch.cuda.synchronize()
+    for i, dw in enumerate(dws):
+        got = host_bits(ys[i])
+        wd = dw.packed_host.view(np.uint16).reshape(dw.n, dw.k) if fmt == wq.FMT_F16 else oracle_rows(fmt, _weights(dw.n, dw.k, 50 + i))[0]
+        check_linear(got, xs[i], wd, "grouped item %d" % i)
+        # every item here gets the rows-per-wave of its own plan, so the grouped launch runs the
+        # same kernel body with the same K split as a separate call: identical bits
+        assert np.array_equal(got, sep[i]), "item %d differs from its separate call" % i
+
+
+def test_grouped_llama7b_w4_linears_bit_identical_to_separate_calls():
+    torch = torch_cuda()
+    _, shapes, _ = inputs.WORKLOADS["llama7b_w4g32_linears"]
+    dws, xs, ys = [], [], []
+    for li, (n, k) in enumerate(shapes):
+        w, x = inputs.weights_and_x(inputs.rng_for(inputs.WORKLOAD_STREAM["llama7b_w4g32_linears"], li), n, k, 1)
+        dws.append(DeviceWeights(wq.FMT_W4G32, w))
+        xs.append(x)
+        ys.append(torch.zeros((1, n), dtype=torch.int16, device="cuda:0"))
+    items = [(dev(x), dw.packed, dw.scales, dw.zeros, y, dw.n, dw.k) for x, dw, y in zip(xs, dws, ys)]
+    wq.wq_linear_grouped(items, 1, wq.FMT_W4G32)
+    torch.cuda.synchronize()
+    for x, dw, y in zip(xs, dws, ys):
+        assert np.array_equal(host_bits(y), dw.linear(x))
+
+
+def test_grouped_argument_errors():
+    torch_cuda()
+    L = wq.lib()
+    assert L.wq_linear_grouped(None, 1, 1, 1, None) == -1
+    arr = (wq.LinearItem * 17)()
+    assert L.wq_linear_grouped(arr, 17, 1, 1, None) == -1
+    assert L.wq_linear_grouped(arr, 0, 1, 1, None) == 0
+    assert L.wq_linear_grouped(arr, 1, 1, 9, None) == -3

@@ -28,6 +28,8 @@
 //  * No atomics anywhere, so every result is deterministic.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <numeric>
 #include <cstdint>
 #include <cstdio>
 
@@ -40,10 +42,15 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h32 __attribute__((ext_vector_type(32)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x6 __attribute__((ext_vector_type(6)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int GEMV_MAX_M = 4;   // largest M served by the VALU GEMV; above it the MFMA kernel runs
 constexpr int MFMA_M = 16;      // rows of x per MFMA launch
-constexpr int MAX_WAVES = 4;    // waves per workgroup (split of K inside a workgroup)
+constexpr int GEMV_MAX_WAVES = 12;  // waves per workgroup of the GEMV (row blocks x split of K)
+// M = 3, 4 keep more x in registers: 8 waves per workgroup, so 256 VGPRs per lane.
+constexpr int gemv_max_waves(int M) { return M <= 2 ? GEMV_MAX_WAVES : 8; }
+constexpr int MFMA_MAX_WAVES = 8;   // waves per workgroup of the MFMA kernel
 
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -166,8 +173,14 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
   return c;
 }
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+// A wave-uniform byte offset held in SGPRs. Adding it to a kernel-argument pointer keeps
+// the global address space and lets loads take the SGPR-base + 32-bit VGPR offset form
+// instead of a per-lane 64-bit address computed on the VALU.
+__device__ __forceinline__ size_t uniform(size_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return (static_cast<size_t>(hi) << 32) | lo;
+}
 
 __device__ __forceinline__ uint4 ld_nt16(const uint8_t* p) {
   const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -190,9 +203,11 @@ __device__ __forceinline__ uint2 ld_nt8(const uint8_t* p) {
 //
 // The decode skips the per-weight bias and zero-point subtraction. A lane dots x with
 // the biased fp16 values it forms in one v_and_or_b32 / v_perm_b32:
-//   W8: (1152 + q)                      -> sum - 1152 X
-//   W4: (1024 + q) for nibbles 0 and 2, (1024 + 16 q) for nibbles 1 and 3
-//                                       -> lo + hi/16 - (1024 X_lo + 64 X_hi) - z (X_lo + X_hi)
+//   W8: (1152 + q)                         -> sum - 1152 X
+//   W4: (1024 + q) from nibbles 0 and 2 (fp16 exponent of 1024: mantissa step 1),
+//       (64 + q)   from nibbles 1 and 3 (exponent of 64, so the nibble's 16 q is q)
+//                                          -> one dot2 chain that starts at
+//                                             -(1024 X_lo + 64 X_hi + z (X_lo + X_hi))
 // where X, X_lo, X_hi are sums of x over the segment, shared by all rows of the wave.
 // Every product is exact in fp32; one-hot inputs give exact results.
 template <int FMT> constexpr int seg_codes() { return FMT == WQ_FMT_W8 ? 16 : FMT == WQ_FMT_F16 ? 8 : 32; }
@@ -204,19 +219,22 @@ template <int FMT, int M, int B>
 struct GemvStage {
   h2 x[M][seg_codes<FMT>() / 2];
   Seg<FMT> w[B];
-  uint16_t s[B], z[B];
+  uint16_t s[FMT == WQ_FMT_W4G32 ? B : 1], z[FMT == WQ_FMT_W4G32 ? B : 1];   // W4 group scale / zero
 };
 
+// Base pointers are a kernel argument plus a wave-uniform offset (uniform() keeps it in
+// SGPRs), so the loads take the SGPR-base + 32-bit lane offset form.
 template <int FMT, int M, int B>
 __device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16_t* __restrict__ x,
                                           const uint8_t* __restrict__ w, const uint16_t* __restrict__ scales,
                                           const uint16_t* __restrict__ zeros, int row0, int N, int K, int c, int lane) {
   constexpr int L = seg_codes<FMT>();
   const int S = K / L;                         // segments per row
-  const int sg = min(c * 64 + lane, S - 1);    // lanes past the row end read a valid segment, masked later
+  const uint32_t sg = (uint32_t)min(c * 64 + lane, S - 1);   // lanes past the row end read a valid segment, masked later
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)L * sg);
+    const uint8_t* xr = reinterpret_cast<const uint8_t*>(x) + uniform((size_t)m * K * 2);
+    const uint4* xp = reinterpret_cast<const uint4*>(xr + 2u * L * sg);
 #pragma unroll
     for (int i = 0; i < L / 8; ++i) {
       const uint4 v = xp[i];
@@ -228,18 +246,18 @@ __device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     const int n = min(row0 + b, N - 1);
-    const uint8_t* row = w + (size_t)n * row_bytes;          // wave-uniform
+    const uint8_t* row = w + uniform((size_t)n * row_bytes);
     if constexpr (FMT == WQ_FMT_W6E3M2) {
       uint32_t lo, hi;
       w6_homes(sg, S, lo, hi);
       st.w[b].a = ld_nt16(row + lo);
       st.w[b].b = ld_nt8(row + hi);
     } else {
-      st.w[b].a = ld_nt16(row + 16u * (uint32_t)sg);
+      st.w[b].a = ld_nt16(row + 16u * sg);
     }
     if constexpr (FMT == WQ_FMT_W4G32) {
-      st.s[b] = scales[(size_t)n * S + sg];
-      st.z[b] = zeros[(size_t)n * S + sg];
+      st.s[b] = (scales + uniform((size_t)n * S))[sg];
+      st.z[b] = (zeros + uniform((size_t)n * S))[sg];
     }
   }
 }
@@ -249,18 +267,20 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
   if (!active) return;
   constexpr int P = seg_codes<FMT>() / 2;   // fp16 pairs per segment
   const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  const auto& xp = st.x;
   if constexpr (FMT == WQ_FMT_W4G32) {
-    const uint32_t m0 = in_vgpr(0x000F000Fu), m1 = in_vgpr(0x00F000F0u), mag = in_vgpr(0x64006400u);
+    const uint32_t m0 = in_vgpr(0x000F000Fu), m1 = in_vgpr(0x00F000F0u);
+    const uint32_t mag_lo = in_vgpr(0x64006400u), mag_hi = in_vgpr(0x54005400u);
     float cx[M], sx[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       float xl = 0.f, xh = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        xl = __builtin_amdgcn_fdot2(st.x[m][4 * i], ones, xl, false);
-        xh = __builtin_amdgcn_fdot2(st.x[m][4 * i + 1], ones, xh, false);
-        xl = __builtin_amdgcn_fdot2(st.x[m][4 * i + 2], ones, xl, false);
-        xh = __builtin_amdgcn_fdot2(st.x[m][4 * i + 3], ones, xh, false);
+        xl = __builtin_amdgcn_fdot2(xp[m][4 * i], ones, xl, false);
+        xh = __builtin_amdgcn_fdot2(xp[m][4 * i + 1], ones, xh, false);
+        xl = __builtin_amdgcn_fdot2(xp[m][4 * i + 2], ones, xl, false);
+        xh = __builtin_amdgcn_fdot2(xp[m][4 * i + 3], ones, xh, false);
       }
       cx[m] = __builtin_fmaf(1024.0f, xl, 64.0f * xh);
       sx[m] = xl + xh;
@@ -272,24 +292,18 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t d = wd[i], e = d >> 8;
-        v[4 * i] = as_h2((d & m0) | mag);
-        v[4 * i + 1] = as_h2((d & m1) | mag);
-        v[4 * i + 2] = as_h2((e & m0) | mag);
-        v[4 * i + 3] = as_h2((e & m1) | mag);
+        v[4 * i] = as_h2((d & m0) | mag_lo);       // codes 8i+0, 8i+1: 1024 + q
+        v[4 * i + 1] = as_h2((d & m1) | mag_hi);   // codes 8i+2, 8i+3: 64 + q
+        v[4 * i + 2] = as_h2((e & m0) | mag_lo);   // codes 8i+4, 8i+5
+        v[4 * i + 3] = as_h2((e & m1) | mag_hi);   // codes 8i+6, 8i+7
       }
       const float s = f16_to_f32(st.s[b]), z = f16_to_f32(st.z[b]);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        float lo = 0.f, hi = 0.f;
+        float t = -__builtin_fmaf(z, sx[m], cx[m]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          lo = __builtin_amdgcn_fdot2(v[4 * i], st.x[m][4 * i], lo, false);
-          hi = __builtin_amdgcn_fdot2(v[4 * i + 1], st.x[m][4 * i + 1], hi, false);
-          lo = __builtin_amdgcn_fdot2(v[4 * i + 2], st.x[m][4 * i + 2], lo, false);
-          hi = __builtin_amdgcn_fdot2(v[4 * i + 3], st.x[m][4 * i + 3], hi, false);
-        }
-        const float part = __builtin_fmaf(hi, 0.0625f, lo) - __builtin_fmaf(z, sx[m], cx[m]);
-        acc[b][m] = __builtin_fmaf(s, part, acc[b][m]);
+        for (int p = 0; p < 16; ++p) t = __builtin_amdgcn_fdot2(v[p], xp[m][p], t, false);
+        acc[b][m] = __builtin_fmaf(s, t, acc[b][m]);
       }
     }
   } else if constexpr (FMT == WQ_FMT_W8) {
@@ -300,10 +314,10 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
       float a = 0.f, c = 0.f;
 #pragma unroll
       for (int p = 0; p < P; p += 2) {
-        a = __builtin_amdgcn_fdot2(st.x[m][p], ones, a, false);
-        c = __builtin_amdgcn_fdot2(st.x[m][p + 1], ones, c, false);
+        a = __builtin_amdgcn_fdot2(xp[m][p], ones, a, false);
+        c = __builtin_amdgcn_fdot2(xp[m][p + 1], ones, c, false);
       }
-      sx[m] = 1152.0f * (a + c);
+      sx[m] = -1152.0f * (a + c);
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -316,13 +330,13 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
       }
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        float a = 0.f, c = 0.f;
+        float a = sx[m], c = 0.f;
 #pragma unroll
         for (int p = 0; p < P; p += 2) {
-          a = __builtin_amdgcn_fdot2(v[p], st.x[m][p], a, false);
-          c = __builtin_amdgcn_fdot2(v[p + 1], st.x[m][p + 1], c, false);
+          a = __builtin_amdgcn_fdot2(v[p], xp[m][p], a, false);
+          c = __builtin_amdgcn_fdot2(v[p + 1], xp[m][p + 1], c, false);
         }
-        acc[b][m] += (a + c) - sx[m];
+        acc[b][m] += a + c;
       }
     }
   } else {
@@ -344,8 +358,8 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
         float a = 0.f, c = 0.f;
 #pragma unroll
         for (int p = 0; p < P; p += 2) {
-          a = __builtin_amdgcn_fdot2(v[p], st.x[m][p], a, false);
-          c = __builtin_amdgcn_fdot2(v[p + 1], st.x[m][p + 1], c, false);
+          a = __builtin_amdgcn_fdot2(v[p], xp[m][p], a, false);
+          c = __builtin_amdgcn_fdot2(v[p + 1], xp[m][p + 1], c, false);
         }
         acc[b][m] += a + c;
       }
@@ -353,14 +367,18 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
   }
 }
 
+// One workgroup's work: rows [block*B, block*B + B) of one linear.
+// A workgroup of W waves holds R = W / WK row blocks; the WK waves of each split K.
 template <int FMT, int M, int B>
-__global__ __launch_bounds__(64 * MAX_WAVES) void gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
-                                                              const uint16_t* __restrict__ scales,
-                                                              const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
-                                                              int N, int K) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, WK = blockDim.x >> 6;
+__device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                          const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
+                                          uint16_t* __restrict__ y, int N, int K, int block, int WK) {
+  const int lane = threadIdx.x & 63;
+  const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar arithmetic
+  const int R = (blockDim.x >> 6) / WK;
+  const int sub = wave_id / WK, wave = wave_id - sub * WK;
   const int S = K / seg_codes<FMT>(), C = (S + 63) >> 6;
-  const int row0 = blockIdx.x * B;
+  const int row0 = (block * R + sub) * B;
   const int NI = wave < C ? (C - wave + WK - 1) / WK : 0;   // chunks of this wave (wave-uniform)
   float acc[B][M];
 #pragma unroll
@@ -391,7 +409,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemv_kernel(const uint16_t* __
     }
   }
 
-  if (WK == 1) {
+  if (WK == 1) {   // each wave is its own row block: no cross-wave step
 #pragma unroll
     for (int b = 0; b < B; ++b)
 #pragma unroll
@@ -405,19 +423,19 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemv_kernel(const uint16_t* __
       }
     return;
   }
-  __shared__ float red[MAX_WAVES][B * M];
+  __shared__ float red[GEMV_MAX_WAVES][B * M];
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const float t = wave_sum_to_lane63(acc[b][m]);
-      if (lane == 63) red[wave][b * M + m] = t;
+      if (lane == 63) red[wave_id][b * M + m] = t;
     }
   __syncthreads();
   if (wave == 0 && lane < B * M) {
     const int b = lane / M, m = lane % M, n = row0 + b;
     float t = 0.0f;
-    for (int i = 0; i < WK; ++i) t += red[i][lane];   // fixed order: deterministic
+    for (int i = 0; i < WK; ++i) t += red[sub * WK + i][lane];   // fixed order: deterministic
     if (n < N) {
       if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) t *= f16_to_f32(scales[n]);
       y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)t);
@@ -425,64 +443,146 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemv_kernel(const uint16_t* __
   }
 }
 
-// ---------------------------------------------------------------- MFMA (M up to 16)
-// Workgroup: 16 output rows x all of K; its WK waves take the 128-wide K tiles in turn.
-template <int FMT>
-__global__ __launch_bounds__(64 * MAX_WAVES) void mfma_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
-                                                              const uint16_t* __restrict__ scales,
-                                                              const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
-                                                              int M, int N, int K) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, WK = blockDim.x >> 6;
-  const int nl = lane & 15, q = lane >> 4;
-  const int n = blockIdx.x * 16 + nl, nc = min(n, N - 1);
-  const int U = K >> 5, T = (U + 3) >> 2;
-  f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+template <int FMT, int M, int B>
+__global__ __launch_bounds__(64 * gemv_max_waves(M)) void gemv_kernel(const uint16_t* __restrict__ x,
+                                                                   const uint8_t* __restrict__ w,
+                                                                   const uint16_t* __restrict__ scales,
+                                                                   const uint16_t* __restrict__ zeros,
+                                                                   uint16_t* __restrict__ y, int N, int K, int WK) {
+  gemv_body<FMT, M, B>(x, w, scales, zeros, y, N, K, blockIdx.x, WK);
+}
 
-  for (int t = wave; t < T; t += WK) {
-    const int u = 4 * t + q;
+// Several independent linears of one format and one M in a single launch: the grid is the
+// concatenation of their workgroups, so the machine ramps up and drains once for all of them.
+constexpr int MAX_GROUP = 16;
+struct GemvGroup {
+  int count;
+  int first_block[MAX_GROUP + 1];   // prefix sums of the per-linear workgroup counts
+  const uint16_t* x[MAX_GROUP];
+  const uint8_t* w[MAX_GROUP];
+  const uint16_t* scales[MAX_GROUP];
+  const uint16_t* zeros[MAX_GROUP];
+  uint16_t* y[MAX_GROUP];
+  int N[MAX_GROUP], K[MAX_GROUP], WK[MAX_GROUP];
+};
+
+template <int FMT, int M, int B>
+__global__ __launch_bounds__(64 * gemv_max_waves(M)) void gemv_grouped_kernel(const GemvGroup g) {
+  int j = 0;
+  while (j + 1 < g.count && (int)blockIdx.x >= g.first_block[j + 1]) ++j;   // workgroup-uniform
+  gemv_body<FMT, M, B>(g.x[j], g.w[j], g.scales[j], g.zeros[j], g.y[j], g.N[j], g.K[j], blockIdx.x - g.first_block[j],
+                       g.WK[j]);
+}
+
+// ---------------------------------------------------------------- MFMA (M up to 16)
+// v_mfma_f32_16x16x32_f16 with the weights as the B operand: lane (nl = l%16, q = l/16)
+// decodes unit u = 4t+q of row nl of a 16-row block straight into its B fragment (8 K per
+// MFMA step), and holds x[m = nl][the same K] as the A fragment (rows m >= M are zero).
+// Any permutation of K applied to both operands leaves the product unchanged, so the
+// unit order inside a 128-wide K tile is free. A wave covers RB row blocks (x fragments
+// are shared by them); the workgroup's WK waves take the K tiles t = wave, wave + WK, ...
+// double-buffered like the GEMV, and add their partial tiles through LDS in a fixed order.
+template <int FMT, int RB>
+struct MfmaStage {
+  Raw<FMT> w[RB];
+  uint16_t s[RB], z[RB];
+  h8 xa[4];
+};
+
+template <int FMT, int RB>
+__device__ __forceinline__ void mfma_load(MfmaStage<FMT, RB>& st, const uint16_t* __restrict__ x,
+                                          const uint8_t* __restrict__ w, const uint16_t* __restrict__ scales,
+                                          const uint16_t* __restrict__ zeros, int n0, int M, int N, int K, int t,
+                                          int nl, int q) {
+  const int U = K >> 5;
+  const int u = min(4 * t + q, U - 1);   // lanes past the row end read a valid unit, masked later
+  const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)min(nl, M - 1) * K + 32 * u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.xa[i] = __builtin_bit_cast(h8, xp[i]);
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int n = min(n0 + 16 * r + nl, N - 1);
+    load_unit<FMT>(w, n, u, U, st.w[r]);
+    if constexpr (FMT == WQ_FMT_W4G32) {
+      st.s[r] = scales[(size_t)n * U + u];
+      st.z[r] = zeros[(size_t)n * U + u];
+    }
+  }
+}
+
+template <int FMT, int RB>
+__device__ __forceinline__ void mfma_compute(const MfmaStage<FMT, RB>& st, f4 (&acc)[RB], bool xrow, bool unit_ok) {
+  const h8 zero8 = {};
+  h8 xa[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xa[i] = (xrow && unit_ok) ? st.xa[i] : zero8;
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    h2 zc1 = {}, zc2 = {};
+    if constexpr (FMT == WQ_FMT_W4G32) w4_consts(st.z[r], zc1, zc2);
     h2 wv[16];
-    h8 xa[4];
+    decode<FMT>(st.w[r], zc1, zc2, wv);
+    if constexpr (FMT == WQ_FMT_W4G32) {
+      const _Float16 s = __builtin_bit_cast(_Float16, st.s[r]);
+      const h2 s2 = {s, s};
 #pragma unroll
-    for (int p = 0; p < 16; ++p) wv[p] = h2{};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = h8{};
-    if (u < U) {
-      Raw<FMT> raw;
-      load_unit<FMT>(w, nc, u, U, raw);
-      h2 zc1 = {}, zc2 = {};
-      uint16_t sbits = 0;
-      if constexpr (FMT == WQ_FMT_W4G32) {
-        sbits = scales[(size_t)nc * U + u];
-        w4_consts(zeros[(size_t)nc * U + u], zc1, zc2);
-      }
-      decode<FMT>(raw, zc1, zc2, wv);
-      if constexpr (FMT == WQ_FMT_W4G32) {
-        const _Float16 s = __builtin_bit_cast(_Float16, sbits);
-        const h2 s2 = {s, s};
-#pragma unroll
-        for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
-      }
-      if (nl < M) {
-        const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)nl * K + 32 * u);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xa[i] = __builtin_bit_cast(h8, xp[i]);
-      }
+      for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       h8 bfrag;
 #pragma unroll
       for (int j = 0; j < 4; ++j) { bfrag[2 * j] = wv[4 * i + j][0]; bfrag[2 * j + 1] = wv[4 * i + j][1]; }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[i], bfrag, acc, 0, 0, 0);
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[i], bfrag, acc[r], 0, 0, 0);
+    }
+  }
+}
+
+template <int FMT, int RB>
+__global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_kernel(const uint16_t* __restrict__ x,
+                                                                   const uint8_t* __restrict__ w,
+                                                                   const uint16_t* __restrict__ scales,
+                                                                   const uint16_t* __restrict__ zeros,
+                                                                   uint16_t* __restrict__ y, int M, int N, int K) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, WK = blockDim.x >> 6;
+  const int nl = lane & 15, q = lane >> 4;
+  const int n0 = blockIdx.x * 16 * RB;
+  const int U = K >> 5, T = (U + 3) >> 2;
+  const int NI = wave < T ? (T - wave + WK - 1) / WK : 0;
+  const bool xrow = nl < M;
+  f4 acc[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) acc[r] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  MfmaStage<FMT, RB> A, Bs;
+  auto tile = [&](int i) { return wave + i * WK; };
+  auto ok = [&](int i) { return 4 * tile(i) + q < U; };
+  if (NI > 0) {
+    mfma_load<FMT, RB>(A, x, w, scales, zeros, n0, M, N, K, tile(0), nl, q);
+    int i = 0;
+    for (; i + 2 < NI; i += 2) {
+      mfma_load<FMT, RB>(Bs, x, w, scales, zeros, n0, M, N, K, tile(i + 1), nl, q);
+      mfma_compute<FMT, RB>(A, acc, xrow, ok(i));
+      mfma_load<FMT, RB>(A, x, w, scales, zeros, n0, M, N, K, tile(i + 2), nl, q);
+      mfma_compute<FMT, RB>(Bs, acc, xrow, ok(i + 1));
+    }
+    if (i + 1 < NI) {
+      mfma_load<FMT, RB>(Bs, x, w, scales, zeros, n0, M, N, K, tile(i + 1), nl, q);
+      mfma_compute<FMT, RB>(A, acc, xrow, ok(i));
+      mfma_compute<FMT, RB>(Bs, acc, xrow, ok(i + 1));
+    } else {
+      mfma_compute<FMT, RB>(A, acc, xrow, ok(i));
     }
   }
 
-  __shared__ f4 red[MAX_WAVES][64];
-  red[wave][lane] = acc;
+  __shared__ f4 red[MFMA_MAX_WAVES][RB][64];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) red[wave][r][lane] = acc[r];
   __syncthreads();
-  if (wave == 0) {
-    f4 t = red[0][lane];
-    for (int i = 1; i < WK; ++i) t += red[i][lane];
+  if (wave < RB) {                      // wave r finishes row block r
+    const int r = wave, n = n0 + 16 * r + nl;
+    f4 t = red[0][r][lane];
+    for (int i = 1; i < WK; ++i) t += red[i][r][lane];   // fixed order: deterministic
     if (n < N) {
       float s = 1.0f;
       if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) s = f16_to_f32(scales[n]);
@@ -537,36 +637,67 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 bool valid_fmt(int fmt) { return fmt >= WQ_FMT_F16 && fmt <= WQ_FMT_W6E3M2; }
 
 struct GemvPlan {
-  int B;      // rows per workgroup
+  int B;      // rows per wave
+  int WK;     // waves splitting K for one row block
+  int R;      // row blocks per workgroup
+  int grid;   // workgroups
+};
+
+// Waves splitting K: the fewest that give ~16 waves per CU (4096) over the row blocks,
+// then, among the splits with the same chunks per wave, the smallest (even work).
+int gemv_waves_for(int fmt, int64_t N, int64_t K, int B) {
+  const int64_t L = fmt == WQ_FMT_W8 ? 16 : fmt == WQ_FMT_F16 ? 8 : 32;
+  const int64_t C = (K / L + 63) / 64, blocks = (N + B - 1) / B;
+  static const int cand[] = {1, 2, 3, 4, 6};
+  int WK = 1;
+  for (int w : cand) {
+    if (w > C) break;
+    WK = w;
+    if (blocks * w >= 4096) break;
+  }
+  const int64_t per = (C + WK - 1) / WK;
+  for (int w : cand)
+    if (w <= WK && (C + w - 1) / w == per) { WK = w; break; }
+  return WK;
+}
+
+GemvPlan plan_gemv(int fmt, int64_t N, int64_t K) {
+  int B = 4, WK = gemv_waves_for(fmt, N, K, 4);
+  while (B > 1 && ((N + B - 1) / B) * WK < 2048) {
+    B >>= 1;
+    WK = gemv_waves_for(fmt, N, K, B);
+  }
+  const int R = WK >= 4 ? 1 : 4 / WK;   // ~4 waves per workgroup
+  const int64_t blocks = (N + B - 1) / B;
+  return {B, WK, R, static_cast<int>((blocks + R - 1) / R)};
+}
+
+struct MfmaPlan {
+  int RB;     // 16-row blocks per wave
   int WK;     // waves per workgroup
   int grid;   // workgroups
 };
 
-// Rows per wave B and waves per workgroup WK: four rows per wave (x is loaded once per
-// chunk and reused for every row of the wave), and enough waves to fill the chip: WK grows
-// (up to the number of chunks) until there are ~16 waves per CU, and B shrinks when N is
-// too small to give 8 per CU.
-GemvPlan plan_gemv(int fmt, int64_t N, int64_t K) {
-  const int64_t L = fmt == WQ_FMT_W8 ? 16 : fmt == WQ_FMT_F16 ? 8 : 32;
-  const int64_t C = (K / L + 63) / 64;
-  int B = 4, WK = 1;
-  while (WK < MAX_WAVES && WK < C && ((N + B - 1) / B) * WK < 4096) ++WK;
-  while (B > 1 && ((N + B - 1) / B) * WK < 2048) B >>= 1;
-  return {B, WK, static_cast<int>((N + B - 1) / B)};
-}
-
-int mfma_waves(int64_t K) {
+// Two row blocks per wave (x fragments shared) when N >= 4096, and up to
+// eight waves per workgroup splitting K so that ~16 waves per CU are resident.
+MfmaPlan plan_mfma(int64_t N, int64_t K) {
   const int64_t T = (K / 32 + 3) / 4;
-  return static_cast<int>(T < MAX_WAVES ? T : MAX_WAVES);
+  const int64_t blocks = (N + 15) / 16;
+  const int RB = blocks >= 256 ? 2 : 1;
+  const int64_t wgs = (blocks + RB - 1) / RB;
+  int WK = 1;
+  while (WK < MFMA_MAX_WAVES && WK < T && wgs * WK < 4096) WK *= 2;
+  return {RB, WK, static_cast<int>(wgs)};
 }
 
 template <int FMT, int M>
 hipError_t launch_gemv_m(const GemvPlan& p, hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
                          const uint16_t* z, uint16_t* y, int N, int K) {
+  const dim3 grid(p.grid), block(64 * p.WK * p.R);
   switch (p.B) {
-    case 4: hipLaunchKernelGGL((gemv_kernel<FMT, M, 4>), dim3(p.grid), dim3(64 * p.WK), 0, s, x, w, sc, z, y, N, K); break;
-    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, M, 2>), dim3(p.grid), dim3(64 * p.WK), 0, s, x, w, sc, z, y, N, K); break;
-    default: hipLaunchKernelGGL((gemv_kernel<FMT, M, 1>), dim3(p.grid), dim3(64 * p.WK), 0, s, x, w, sc, z, y, N, K); break;
+    case 4: hipLaunchKernelGGL((gemv_kernel<FMT, M, 4>), grid, block, 0, s, x, w, sc, z, y, N, K, p.WK); break;
+    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, M, 2>), grid, block, 0, s, x, w, sc, z, y, N, K, p.WK); break;
+    default: hipLaunchKernelGGL((gemv_kernel<FMT, M, 1>), grid, block, 0, s, x, w, sc, z, y, N, K, p.WK); break;
   }
   return hipGetLastError();
 }
@@ -583,9 +714,32 @@ hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w,
       default: return launch_gemv_m<FMT, 4>(p, s, x, w, sc, z, y, N, K);
     }
   }
-  const int WK = mfma_waves(K);
-  hipLaunchKernelGGL((mfma_kernel<FMT>), dim3((N + 15) / 16), dim3(64 * WK), 0, s, x, w, sc, z, y, M, N, K);
+  const MfmaPlan p = plan_mfma(N, K);
+  if (p.RB == 2)
+    hipLaunchKernelGGL((mfma_kernel<FMT, 2>), dim3(p.grid), dim3(64 * p.WK), 0, s, x, w, sc, z, y, M, N, K);
+  else
+    hipLaunchKernelGGL((mfma_kernel<FMT, 1>), dim3(p.grid), dim3(64 * p.WK), 0, s, x, w, sc, z, y, M, N, K);
   return hipGetLastError();
+}
+
+template <int FMT, int M>
+hipError_t launch_grouped_m(const GemvGroup& g, int B, int block_waves, int grid, hipStream_t s) {
+  switch (B) {
+    case 4: hipLaunchKernelGGL((gemv_grouped_kernel<FMT, M, 4>), dim3(grid), dim3(64 * block_waves), 0, s, g); break;
+    case 2: hipLaunchKernelGGL((gemv_grouped_kernel<FMT, M, 2>), dim3(grid), dim3(64 * block_waves), 0, s, g); break;
+    default: hipLaunchKernelGGL((gemv_grouped_kernel<FMT, M, 1>), dim3(grid), dim3(64 * block_waves), 0, s, g); break;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_grouped_fmt(const GemvGroup& g, int M, int B, int block_waves, int grid, hipStream_t s) {
+  switch (M) {
+    case 1: return launch_grouped_m<FMT, 1>(g, B, block_waves, grid, s);
+    case 2: return launch_grouped_m<FMT, 2>(g, B, block_waves, grid, s);
+    case 3: return launch_grouped_m<FMT, 3>(g, B, block_waves, grid, s);
+    default: return launch_grouped_m<FMT, 4>(g, B, block_waves, grid, s);
+  }
 }
 
 int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, const uint16_t* z, const uint16_t* y,
@@ -649,6 +803,68 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
   return hipGetLastError() == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
 }
 
+int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt, void* stream) {
+  if (!valid_fmt(fmt)) return WQ_ERR_FMT;
+  if (!items || count < 0 || count > MAX_GROUP) return WQ_ERR_ARG;
+  if (count == 0) return WQ_OK;
+  for (int i = 0; i < count; ++i) {
+    const wq_linear_item& it = items[i];
+    const int st = check_linear_args(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt);
+    if (st != WQ_OK) return st;
+  }
+  if (M > GEMV_MAX_M) {   // the MFMA path has no grouped form: one launch per item
+    for (int i = 0; i < count; ++i) {
+      const wq_linear_item& it = items[i];
+      const int st = wq_linear(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt, stream);
+      if (st != WQ_OK) return st;
+    }
+    return WQ_OK;
+  }
+  // one rows-per-wave B for the whole launch (the smallest any item's own plan picks);
+  // each item keeps the K split its own plan gives for that B
+  int B = 4;
+  for (int i = 0; i < count; ++i) B = std::min(B, plan_gemv(fmt, items[i].N, items[i].K).B);
+  GemvGroup g = {};
+  g.count = count;
+  int block_waves = 1;
+  for (int i = 0; i < count; ++i) {
+    g.WK[i] = gemv_waves_for(fmt, items[i].N, items[i].K, B);
+    block_waves = std::lcm(block_waves, g.WK[i]);
+  }
+  if (block_waves > gemv_max_waves(static_cast<int>(M))) {   // 3 with 4: keep powers of two only
+    block_waves = 1;
+    for (int i = 0; i < count; ++i) {
+      g.WK[i] = g.WK[i] >= 4 ? 4 : g.WK[i] >= 2 ? 2 : 1;
+      block_waves = std::max(block_waves, g.WK[i]);
+    }
+  }
+  while (block_waves < 4) block_waves *= 2;   // 4, 6, 8 or 12 waves
+  int grid = 0;
+  for (int i = 0; i < count; ++i) {
+    const wq_linear_item& it = items[i];
+    const int R = block_waves / g.WK[i];
+    g.first_block[i] = grid;
+    g.x[i] = it.x;
+    g.w[i] = static_cast<const uint8_t*>(it.packed_w);
+    g.scales[i] = it.scales;
+    g.zeros[i] = it.zeros;
+    g.y[i] = it.y;
+    g.N[i] = static_cast<int>(it.N);
+    g.K[i] = static_cast<int>(it.K);
+    grid += static_cast<int>(((it.N + B - 1) / B + R - 1) / R);
+  }
+  g.first_block[count] = grid;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (fmt) {
+    case WQ_FMT_W8: e = launch_grouped_fmt<WQ_FMT_W8>(g, (int)M, B, block_waves, grid, s); break;
+    case WQ_FMT_W4G32: e = launch_grouped_fmt<WQ_FMT_W4G32>(g, (int)M, B, block_waves, grid, s); break;
+    case WQ_FMT_W6E3M2: e = launch_grouped_fmt<WQ_FMT_W6E3M2>(g, (int)M, B, block_waves, grid, s); break;
+    default: e = launch_grouped_fmt<WQ_FMT_F16>(g, (int)M, B, block_waves, grid, s); break;
+  }
+  return e == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
+}
+
 const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   static thread_local char buf[96];
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 32 || K % 32) return "";
@@ -657,8 +873,22 @@ const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
     const GemvPlan p = plan_gemv(fmt, N, K);
     snprintf(buf, sizeof(buf), "gemv_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), p.B);
   } else {
-    snprintf(buf, sizeof(buf), "mfma_kernel<%d>", fmt);
+    snprintf(buf, sizeof(buf), "mfma_kernel<%d, %d>", fmt, plan_mfma(N, K).RB);
   }
+  return buf;
+}
+
+const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, const int64_t* K, int count) {
+  static thread_local char buf[96];
+  if (!valid_fmt(fmt) || M < 1 || !N || !K || count < 1 || count > MAX_GROUP) return "";
+  const int64_t mm = M < MFMA_M ? M : MFMA_M;
+  if (mm > GEMV_MAX_M) return wq_linear_kernel_name(fmt, M, N[0], K[0]);
+  int B = 4;
+  for (int i = 0; i < count; ++i) {
+    if (N[i] < 1 || K[i] < 32 || K[i] % 32) return "";
+    B = std::min(B, plan_gemv(fmt, N[i], K[i]).B);
+  }
+  snprintf(buf, sizeof(buf), "gemv_grouped_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), B);
   return buf;
 }
 

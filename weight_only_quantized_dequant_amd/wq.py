@@ -22,6 +22,12 @@ _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
 
 
+class LinearItem(ctypes.Structure):
+    """wq_linear_item: one linear of a grouped call (device pointers)."""
+    _fields_ = [("x", ctypes.c_void_p), ("packed_w", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
 class WqError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
@@ -48,8 +54,12 @@ def lib():
         L.wq_unpack.argtypes = [ctypes.c_int, _p, _p, _p, _i64, _i64, _p, _p, _p]
         L.wq_dequant.argtypes = [ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _p]
         L.wq_linear.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, ctypes.c_int, _p]
+        L.wq_linear_grouped.argtypes = [ctypes.POINTER(LinearItem), ctypes.c_int, _i64, ctypes.c_int, _p]
+        L.wq_linear_grouped.restype = ctypes.c_int
         L.wq_linear_kernel_name.restype = ctypes.c_char_p
         L.wq_linear_kernel_name.argtypes = [ctypes.c_int, _i64, _i64, _i64]
+        L.wq_linear_grouped_kernel_name.restype = ctypes.c_char_p
+        L.wq_linear_grouped_kernel_name.argtypes = [ctypes.c_int, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.c_int]
         for name in ("wq_pack_int8", "wq_pack_int4", "wq_pack_fp6", "wq_unpack", "wq_dequant", "wq_linear"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -99,6 +109,12 @@ def wq_zeros_bytes(fmt, n, k):
 
 def wq_linear_kernel_name(fmt, m, n, k):
     return lib().wq_linear_kernel_name(fmt, m, n, k).decode()
+
+
+def wq_linear_grouped_kernel_name(fmt, m, shapes):
+    ns = (_i64 * len(shapes))(*[n for n, _ in shapes])
+    ks = (_i64 * len(shapes))(*[k for _, k in shapes])
+    return lib().wq_linear_grouped_kernel_name(fmt, m, ns, ks, len(shapes)).decode()
 
 
 # ------------------------------------------------------------------ host: pack / unpack
@@ -168,3 +184,13 @@ def wq_linear(x, packed_w, scales, zeros, y, m, n, k, fmt, stream=None):
     """Device: y[M,N] = x[M,K] . dequant(W)[N,K]^T on torch device buffers, async on stream."""
     _check(lib().wq_linear(_dev_ptr(x), _dev_ptr(packed_w), _dev_ptr(scales), _dev_ptr(zeros), _dev_ptr(y), m, n, k,
                            fmt, _stream_ptr(stream)), "wq_linear")
+
+
+def wq_linear_grouped(items, m, fmt, stream=None):
+    """Device: several independent linears in one launch. items: sequence of
+    (x, packed_w, scales, zeros, y, n, k) with torch device buffers; async on stream."""
+    arr = (LinearItem * max(1, len(items)))()
+    for i, (x, pw, sc, z, y, n, k) in enumerate(items):
+        arr[i] = LinearItem(x.data_ptr(), pw.data_ptr(), sc.data_ptr() if sc is not None else None,
+                            z.data_ptr() if z is not None else None, y.data_ptr(), n, k)
+    _check(lib().wq_linear_grouped(arr, len(items), m, fmt, _stream_ptr(stream)), "wq_linear_grouped")
