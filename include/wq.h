@@ -39,7 +39,8 @@
  * as uint16_t bit patterns.
  *
  * Conventions for every call:
- *   - K must be a positive multiple of 32; N >= 1; M >= 1. Otherwise WQ_ERR_SHAPE.
+ *   - K must be a positive multiple of 32 and at most 2^26; N >= 1; M >= 1; N*K/32 must fit
+ *     in an int32. Otherwise WQ_ERR_SHAPE.
  *   - Every error is returned synchronously, before anything is launched. The device
  *     calls never synchronize; a fault in a kernel shows up at the caller's next sync.
  *   - Memory is owned by the caller. The library allocates no device memory, keeps no
@@ -131,16 +132,18 @@ typedef struct {
  * sum may run in another order when the items' sizes differ a lot). One launch
  * instead of count means the GPU ramps up and drains once; in a decode step this fits
  * q/k/v or gate/up, and any set of linears whose inputs are ready. Items must not write
- * into one another's inputs. For M > 4 the items run as separate launches. Errors: as
- * wq_linear, per item, all checked before any launch; WQ_ERR_ARG also for count
- * outside 0..16 or items == NULL. */
+ * into one another's inputs. When wq_linear would use the matrix-core kernel for any item
+ * (M >= 5, or M = 4 with W6/W8 and N >= 4096), every item runs as its own wq_linear launch
+ * instead. Errors: as wq_linear, per item, all checked before any launch; WQ_ERR_ARG also
+ * for count outside 0..16 or items == NULL. */
 int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt, void* stream);
 
 /* Name of the kernel wq_linear launches for (fmt, M, N, K) (for profiles), or "" if the
  * arguments are invalid. Host only; static storage. */
 const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
 
-/* Name of the kernel wq_linear_grouped launches for count items of sizes N[i] x K[i], or "". */
+/* Name of the kernel wq_linear_grouped launches for count items of sizes N[i] x K[i] (with
+ * separate launches: the largest item's kernel), or "". */
 const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, const int64_t* K, int count);
 
 #ifdef __cplusplus

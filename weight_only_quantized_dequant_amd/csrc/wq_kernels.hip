@@ -474,38 +474,55 @@ __global__ __launch_bounds__(64 * gemv_max_waves(M)) void gemv_grouped_kernel(co
                        g.WK[j]);
 }
 
-// ---------------------------------------------------------------- MFMA (M up to 16)
+// ---------------------------------------------------------------- MFMA (M = 4..16)
 // v_mfma_f32_16x16x32_f16 with the weights as the B operand: lane (nl = l%16, q = l/16)
 // decodes unit u = 4t+q of row nl of a 16-row block straight into its B fragment (8 K per
 // MFMA step), and holds x[m = nl][the same K] as the A fragment (rows m >= M are zero).
 // Any permutation of K applied to both operands leaves the product unchanged, so the
-// unit order inside a 128-wide K tile is free. A wave covers RB row blocks (x fragments
-// are shared by them); the workgroup's WK waves take the K tiles t = wave, wave + WK, ...
-// double-buffered like the GEMV, and add their partial tiles through LDS in a fixed order.
+// unit order inside a 128-wide K tile is free. A wave covers RB row blocks, which share its
+// x fragments; a workgroup holds R row groups x WK waves that take the K tiles t = kw,
+// kw + WK, ..., double-buffered like the GEMV, and add their partials through LDS in a
+// fixed order. Loads take a wave-uniform base plus a 32-bit lane offset.
 template <int FMT, int RB>
 struct MfmaStage {
-  Raw<FMT> w[RB];
-  uint16_t s[RB], z[RB];
   h8 xa[4];
+  Raw<FMT> w[RB];
+  uint16_t s[FMT == WQ_FMT_W4G32 ? RB : 1], z[FMT == WQ_FMT_W4G32 ? RB : 1];
 };
 
 template <int FMT, int RB>
 __device__ __forceinline__ void mfma_load(MfmaStage<FMT, RB>& st, const uint16_t* __restrict__ x,
-                                          const uint8_t* __restrict__ w, const uint16_t* __restrict__ scales,
-                                          const uint16_t* __restrict__ zeros, int n0, int M, int N, int K, int t,
-                                          int nl, int q) {
+                                           const uint8_t* __restrict__ w, const uint16_t* __restrict__ scales,
+                                           const uint16_t* __restrict__ zeros, int n0, int M, int N, int K, int t,
+                                           int nl, int q) {
+  constexpr int UB = unit_bytes<FMT>();
   const int U = K >> 5;
-  const int u = min(4 * t + q, U - 1);   // lanes past the row end read a valid unit, masked later
-  const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)min(nl, M - 1) * K + 32 * u);
+  const uint32_t u = (uint32_t)min(4 * t + q, U - 1);   // past the row end: a valid unit, masked later
+  const uint32_t xo = (uint32_t)min(nl, M - 1) * (uint32_t)K * 2u + 64u * u;
+  const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) + xo);
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.xa[i] = __builtin_bit_cast(h8, xp[i]);
+  const uint32_t row_bytes = (uint32_t)U * UB;
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
-    const int n = min(n0 + 16 * r + nl, N - 1);
-    load_unit<FMT>(w, n, u, U, st.w[r]);
+    const int nb = min(n0 + 16 * r, N - 1);                        // wave-uniform
+    const uint32_t nn = (uint32_t)(min(n0 + 16 * r + nl, N - 1) - nb);   // 0..15
+    const uint8_t* rowb = w + uniform((size_t)nb * row_bytes);
+    if constexpr (FMT == WQ_FMT_W6E3M2) {
+      uint32_t lo, hi;
+      w6_homes(u, U, lo, hi);
+      st.w[r].a = ld_nt16(rowb + nn * row_bytes + lo);
+      st.w[r].b = ld_nt8(rowb + nn * row_bytes + hi);
+    } else {
+      const uint8_t* p = rowb + nn * row_bytes + UB * u;
+      st.w[r].a = ld_nt16(p);
+      if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_F16) st.w[r].b = ld_nt16(p + 16);
+      if constexpr (FMT == WQ_FMT_F16) { st.w[r].c = ld_nt16(p + 32); st.w[r].d = ld_nt16(p + 48); }
+    }
     if constexpr (FMT == WQ_FMT_W4G32) {
-      st.s[r] = scales[(size_t)n * U + u];
-      st.z[r] = zeros[(size_t)n * U + u];
+      const size_t mb = uniform((size_t)nb * U);
+      st.s[r] = (scales + mb)[nn * U + u];
+      st.z[r] = (zeros + mb)[nn * U + u];
     }
   }
 }
@@ -523,8 +540,8 @@ __device__ __forceinline__ void mfma_compute(const MfmaStage<FMT, RB>& st, f4 (&
     h2 wv[16];
     decode<FMT>(st.w[r], zc1, zc2, wv);
     if constexpr (FMT == WQ_FMT_W4G32) {
-      const _Float16 s = __builtin_bit_cast(_Float16, st.s[r]);
-      const h2 s2 = {s, s};
+      const _Float16 sv = __builtin_bit_cast(_Float16, st.s[r]);
+      const h2 s2 = {sv, sv};
 #pragma unroll
       for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
     }
@@ -539,35 +556,40 @@ __device__ __forceinline__ void mfma_compute(const MfmaStage<FMT, RB>& st, f4 (&
 }
 
 template <int FMT, int RB>
-__global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_kernel(const uint16_t* __restrict__ x,
-                                                                   const uint8_t* __restrict__ w,
-                                                                   const uint16_t* __restrict__ scales,
-                                                                   const uint16_t* __restrict__ zeros,
-                                                                   uint16_t* __restrict__ y, int M, int N, int K) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, WK = blockDim.x >> 6;
+__device__ __forceinline__ void mfma_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                           const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
+                                           uint16_t* __restrict__ y, int M, int N, int K, int block, int WK) {
+  const int lane = threadIdx.x & 63;
+  const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int R = (blockDim.x >> 6) / WK;
+  const int sub = wave_id / WK, kw = wave_id - sub * WK;
   const int nl = lane & 15, q = lane >> 4;
-  const int n0 = blockIdx.x * 16 * RB;
   const int U = K >> 5, T = (U + 3) >> 2;
-  const int NI = wave < T ? (T - wave + WK - 1) / WK : 0;
+  const int n0 = (block * R + sub) * 16 * RB;
+  const int NI = kw < T ? (T - kw + WK - 1) / WK : 0;
   const bool xrow = nl < M;
   f4 acc[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) acc[r] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   MfmaStage<FMT, RB> A, Bs;
-  auto tile = [&](int i) { return wave + i * WK; };
+  auto tile = [&](int i) { return kw + i * WK; };
   auto ok = [&](int i) { return 4 * tile(i) + q < U; };
   if (NI > 0) {
     mfma_load<FMT, RB>(A, x, w, scales, zeros, n0, M, N, K, tile(0), nl, q);
+    __builtin_amdgcn_sched_barrier(0);   // keep the stage's loads ahead of the compute
     int i = 0;
     for (; i + 2 < NI; i += 2) {
       mfma_load<FMT, RB>(Bs, x, w, scales, zeros, n0, M, N, K, tile(i + 1), nl, q);
+      __builtin_amdgcn_sched_barrier(0);   // keep the stage's loads ahead of the compute
       mfma_compute<FMT, RB>(A, acc, xrow, ok(i));
       mfma_load<FMT, RB>(A, x, w, scales, zeros, n0, M, N, K, tile(i + 2), nl, q);
+      __builtin_amdgcn_sched_barrier(0);   // keep the stage's loads ahead of the compute
       mfma_compute<FMT, RB>(Bs, acc, xrow, ok(i + 1));
     }
     if (i + 1 < NI) {
       mfma_load<FMT, RB>(Bs, x, w, scales, zeros, n0, M, N, K, tile(i + 1), nl, q);
+      __builtin_amdgcn_sched_barrier(0);   // keep the stage's loads ahead of the compute
       mfma_compute<FMT, RB>(A, acc, xrow, ok(i));
       mfma_compute<FMT, RB>(Bs, acc, xrow, ok(i + 1));
     } else {
@@ -575,24 +597,45 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_kernel(const uint16_
     }
   }
 
+  // D[m][n] sits in lane (n + 16*(m/4)), register m%4. Row block r of this group is finished
+  // by the group's wave r % WK, which adds the WK partials in a fixed order.
+  auto store = [&](int r, const f4& t) {
+    const int n = n0 + 16 * r + nl;
+    if (n >= N) return;
+    float sc = 1.0f;
+    if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) sc = f16_to_f32(scales[n]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * q + i;
+      if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(t[i] * sc));
+    }
+  };
+  if (WK == 1) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) store(r, acc[r]);
+    return;
+  }
   __shared__ f4 red[MFMA_MAX_WAVES][RB][64];
 #pragma unroll
-  for (int r = 0; r < RB; ++r) red[wave][r][lane] = acc[r];
+  for (int r = 0; r < RB; ++r) red[wave_id][r][lane] = acc[r];
   __syncthreads();
-  if (wave < RB) {                      // wave r finishes row block r
-    const int r = wave, n = n0 + 16 * r + nl;
-    f4 t = red[0][r][lane];
-    for (int i = 1; i < WK; ++i) t += red[i][r][lane];   // fixed order: deterministic
-    if (n < N) {
-      float s = 1.0f;
-      if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) s = f16_to_f32(scales[n]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * q + i;   // D[m][n] sits in lane (n + 16*(m/4)), register m%4
-        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(t[i] * s));
-      }
-    }
+  for (int r = 0; r < RB; ++r) {
+    if (r % WK != kw) continue;
+    f4 t = red[sub * WK][r][lane];
+    for (int i = 1; i < WK; ++i) t += red[sub * WK + i][r][lane];   // fixed order: deterministic
+    store(r, t);
   }
+}
+
+template <int FMT, int RB>
+__global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint8_t* __restrict__ w,
+                                                                     const uint16_t* __restrict__ scales,
+                                                                     const uint16_t* __restrict__ zeros,
+                                                                     uint16_t* __restrict__ y, int M, int N, int K,
+                                                                     int WK) {
+  mfma_body<FMT, RB>(x, w, scales, zeros, y, M, N, K, blockIdx.x, WK);
 }
 
 // ---------------------------------------------------------------- dequant
@@ -674,20 +717,28 @@ GemvPlan plan_gemv(int fmt, int64_t N, int64_t K) {
 
 struct MfmaPlan {
   int RB;     // 16-row blocks per wave
-  int WK;     // waves per workgroup
+  int WK;     // waves per workgroup, splitting K
   int grid;   // workgroups
 };
 
-// Two row blocks per wave (x fragments shared) when N >= 4096, and up to
-// eight waves per workgroup splitting K so that ~16 waves per CU are resident.
-MfmaPlan plan_mfma(int64_t N, int64_t K) {
+// The matrix-core kernel serves M >= 5, and M = 4 for W6/W8 rows of 4096 or more, where
+// it beats the VALU GEMV (which then spends four dot products per weight pair).
+bool use_mfma(int fmt, int64_t M, int64_t N) {
+  if (M > GEMV_MAX_M) return true;
+  return M == GEMV_MAX_M && (fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W8) && N >= 4096;
+}
+
+// RB: as many row blocks per wave as keeps >= 256 row groups (W4 and F16, whose decode
+// is heavier per byte, take one or two). WK: doubled up to 8 until ~2048 waves.
+MfmaPlan plan_mfma(int fmt, int64_t N, int64_t K) {
   const int64_t T = (K / 32 + 3) / 4;
-  const int64_t blocks = (N + 15) / 16;
-  const int RB = blocks >= 256 ? 2 : 1;
-  const int64_t wgs = (blocks + RB - 1) / RB;
+  int RB = 1;
+  if (fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W8) RB = N >= 16384 ? 4 : N >= 8192 ? 2 : 1;
+  else if (fmt == WQ_FMT_F16) RB = N >= 8192 ? 2 : 1;
+  const int64_t groups = (N + 16 * RB - 1) / (16 * RB);
   int WK = 1;
-  while (WK < MFMA_MAX_WAVES && WK < T && wgs * WK < 4096) WK *= 2;
-  return {RB, WK, static_cast<int>(wgs)};
+  while (WK < MFMA_MAX_WAVES && WK < T && groups * WK < 2048) WK *= 2;
+  return {RB, WK, static_cast<int>(groups)};
 }
 
 template <int FMT, int M>
@@ -705,7 +756,7 @@ hipError_t launch_gemv_m(const GemvPlan& p, hipStream_t s, const uint16_t* x, co
 template <int FMT>
 hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
                              uint16_t* y, int M, int N, int K) {
-  if (M <= GEMV_MAX_M) {
+  if (!use_mfma(FMT, M, N)) {
     const GemvPlan p = plan_gemv(FMT, N, K);
     switch (M) {
       case 1: return launch_gemv_m<FMT, 1>(p, s, x, w, sc, z, y, N, K);
@@ -714,11 +765,13 @@ hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w,
       default: return launch_gemv_m<FMT, 4>(p, s, x, w, sc, z, y, N, K);
     }
   }
-  const MfmaPlan p = plan_mfma(N, K);
-  if (p.RB == 2)
-    hipLaunchKernelGGL((mfma_kernel<FMT, 2>), dim3(p.grid), dim3(64 * p.WK), 0, s, x, w, sc, z, y, M, N, K);
-  else
-    hipLaunchKernelGGL((mfma_kernel<FMT, 1>), dim3(p.grid), dim3(64 * p.WK), 0, s, x, w, sc, z, y, M, N, K);
+  const MfmaPlan p = plan_mfma(FMT, N, K);
+  const dim3 grid(p.grid), block(64 * p.WK);
+  switch (p.RB) {
+    case 4: hipLaunchKernelGGL((mfma_kernel<FMT, 4>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
+    case 2: hipLaunchKernelGGL((mfma_kernel<FMT, 2>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
+    default: hipLaunchKernelGGL((mfma_kernel<FMT, 1>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
+  }
   return hipGetLastError();
 }
 
@@ -742,6 +795,13 @@ hipError_t launch_grouped_fmt(const GemvGroup& g, int M, int B, int block_waves,
   }
 }
 
+int grouped_rows_per_wave(int fmt, const wq_linear_item* items, int count) {
+  int big = 0;
+  for (int i = 1; i < count; ++i)
+    if (items[i].N * items[i].K > items[big].N * items[big].K) big = i;
+  return plan_gemv(fmt, items[big].N, items[big].K).B;
+}
+
 int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, const uint16_t* z, const uint16_t* y,
                       int64_t M, int64_t N, int64_t K, int fmt) {
   if (!valid_fmt(fmt)) return WQ_ERR_FMT;
@@ -749,7 +809,7 @@ int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, cons
   if (fmt != WQ_FMT_F16 && !sc) return WQ_ERR_ARG;
   if (fmt == WQ_FMT_W4G32 && !z) return WQ_ERR_ARG;
   if (M < 1 || N < 1 || K < 32 || K % 32) return WQ_ERR_SHAPE;
-  if (N > INT32_MAX / 2 || K > INT32_MAX / 2 || (N * (K / 32)) > INT32_MAX) return WQ_ERR_SHAPE;
+  if (N > INT32_MAX / 2 || K > (int64_t(1) << 26) || (N * (K / 32)) > INT32_MAX) return WQ_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (sc && !aligned16(sc)) || (z && !aligned16(z))) return WQ_ERR_ALIGN;
   return WQ_OK;
 }
@@ -812,7 +872,9 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
     const int st = check_linear_args(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt);
     if (st != WQ_OK) return st;
   }
-  if (M > GEMV_MAX_M) {   // the MFMA path has no grouped form: one launch per item
+  bool mfma = false;
+  for (int i = 0; i < count; ++i) mfma = mfma || use_mfma(fmt, M, items[i].N);
+  if (mfma) {   // the MFMA path has no grouped form: one launch per item
     for (int i = 0; i < count; ++i) {
       const wq_linear_item& it = items[i];
       const int st = wq_linear(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt, stream);
@@ -820,10 +882,10 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
     }
     return WQ_OK;
   }
-  // one rows-per-wave B for the whole launch (the smallest any item's own plan picks);
-  // each item keeps the K split its own plan gives for that B
-  int B = 4;
-  for (int i = 0; i < count; ++i) B = std::min(B, plan_gemv(fmt, items[i].N, items[i].K).B);
+  // one rows-per-wave B for the whole launch: the one the largest item's plan picks (the
+  // small items alone would pick fewer rows per wave to get enough waves, which the
+  // launch has anyway); each item keeps the K split its own plan gives for that B
+  int B = grouped_rows_per_wave(fmt, items, count);
   GemvGroup g = {};
   g.count = count;
   int block_waves = 1;
@@ -869,11 +931,11 @@ const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   static thread_local char buf[96];
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 32 || K % 32) return "";
   const int64_t mm = M < MFMA_M ? M : MFMA_M;
-  if (mm <= GEMV_MAX_M) {
+  if (!use_mfma(fmt, mm, N)) {
     const GemvPlan p = plan_gemv(fmt, N, K);
     snprintf(buf, sizeof(buf), "gemv_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), p.B);
   } else {
-    snprintf(buf, sizeof(buf), "mfma_kernel<%d, %d>", fmt, plan_mfma(N, K).RB);
+    snprintf(buf, sizeof(buf), "mfma_kernel<%d, %d>", fmt, plan_mfma(fmt, N, K).RB);
   }
   return buf;
 }
@@ -882,13 +944,15 @@ const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, 
   static thread_local char buf[96];
   if (!valid_fmt(fmt) || M < 1 || !N || !K || count < 1 || count > MAX_GROUP) return "";
   const int64_t mm = M < MFMA_M ? M : MFMA_M;
-  if (mm > GEMV_MAX_M) return wq_linear_kernel_name(fmt, M, N[0], K[0]);
-  int B = 4;
+  int big = 0;
+  bool mfma = false;
   for (int i = 0; i < count; ++i) {
     if (N[i] < 1 || K[i] < 32 || K[i] % 32) return "";
-    B = std::min(B, plan_gemv(fmt, N[i], K[i]).B);
+    if (N[i] * K[i] > N[big] * K[big]) big = i;
+    mfma = mfma || use_mfma(fmt, mm, N[i]);
   }
-  snprintf(buf, sizeof(buf), "gemv_grouped_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), B);
+  if (mfma) return wq_linear_kernel_name(fmt, M, N[big], K[big]);   // separate launches: the largest item's
+  snprintf(buf, sizeof(buf), "gemv_grouped_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), plan_gemv(fmt, N[big], K[big]).B);
   return buf;
 }
 
