@@ -686,17 +686,19 @@ struct GemvPlan {
   int grid;   // workgroups
 };
 
-// Waves splitting K: the fewest that give ~16 waves per CU (4096) over the row blocks,
-// then, among the splits with the same chunks per wave, the smallest (even work).
+// Waves splitting K: the fewest that give enough waves over the row blocks (W4, with the
+// most decode work per byte, runs best at ~4 waves per CU, the others at ~16), then,
+// among the splits with the same chunks per wave, the smallest (even work).
 int gemv_waves_for(int fmt, int64_t N, int64_t K, int B) {
   const int64_t L = fmt == WQ_FMT_W8 ? 16 : fmt == WQ_FMT_F16 ? 8 : 32;
   const int64_t C = (K / L + 63) / 64, blocks = (N + B - 1) / B;
+  const int64_t target = fmt == WQ_FMT_W4G32 ? 1024 : 4096;
   static const int cand[] = {1, 2, 3, 4, 6};
   int WK = 1;
   for (int w : cand) {
     if (w > C) break;
     WK = w;
-    if (blocks * w >= 4096) break;
+    if (blocks * w >= target) break;
   }
   const int64_t per = (C + WK - 1) / WK;
   for (int w : cand)
