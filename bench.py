@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-baselines", action="store_true", help="skip the fp16 baselines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--sweep", choices=["llama2_7b", "llama70b_w6"], default=None,
+                    help="time a whole decode step's linears of a random-init model instead of --workload: "
+                         "llama2_7b (32 layers, fp16/W8/W4/W6, M=1) or llama70b_w6 (80 layers, W6, M=1..16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 512 MiB (a known-size kernel for counter calibration)")
     return ap.parse_args()
@@ -189,6 +192,90 @@ def cpu_baseline(fmt, linears_host, seconds):
                       "elementwise steps single-threaded, the product on %d BLAS threads" % (rows, reps, dt, blas_threads)}
 
 
+SWEEPS = {
+    # name: (layer shapes, layers, formats, Ms)
+    "llama2_7b": (inputs.LLAMA2_7B_LINEARS, 32, ["f16", "w8", "w4g32", "w6e3m2"], [1]),
+    "llama70b_w6": (inputs.LLAMA_70B_LINEARS, 80, ["w6e3m2", "f16"], [1, 2, 4, 8, 16]),
+}
+
+
+def run_sweep(args, torch):
+    """A decode step's linears of a random-init model: per layer q/k/v in one grouped call, o,
+    gate/up in one grouped call, down. Every layer has its own weight memory (device copies
+    of one seeded draw per shape: time depends only on shapes and bytes), so the step streams
+    the whole model from HBM. Timed as replays of a graph that holds one step."""
+    shapes, layers, fmts, ms_list = SWEEPS[args.sweep]
+    if args.m is not None:
+        ms_list = [args.m]
+    name = {"llama2_7b": "llama2_7b_decode_sweep", "llama70b_w6": "llama70b_w6e3m2_decode_sweep"}[args.sweep]
+    distinct = sorted({(n, k) for _, n, k in shapes})
+    draws = {}
+    for i, (n, k) in enumerate(distinct):
+        draws[(n, k)] = inputs.weights_and_x(inputs.rng_for(10 + list(SWEEPS).index(args.sweep), i), n, k, max(ms_list))
+    mmax = max(ms_list)
+    xs = {k: torch.from_numpy(draws[next(s for s in distinct if s[1] == k)][1].view(np.int16).copy()).to("cuda")
+          for k in {k for _, k in distinct}}
+    ys = {n: torch.empty((mmax, n), dtype=torch.int16, device="cuda") for n in {n for n, _ in distinct}}
+    results, steps = {}, max(1, args.steps // 20)
+    for fname in fmts:
+        fmt = FMT_OF[fname]
+        proto = {}
+        for (n, k), (w, _) in draws.items():
+            if fmt == wq.FMT_W8:
+                p, sc = wq.wq_pack_int8(w); z = None
+            elif fmt == wq.FMT_W4G32:
+                p, sc, z = wq.wq_pack_int4(w)
+            elif fmt == wq.FMT_W6E3M2:
+                p, sc = wq.wq_pack_fp6(w); z = None
+            else:
+                p, sc, z = w.astype(np.float16).view(np.uint8).reshape(-1), None, None
+            dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).to("cuda")
+            proto[(n, k)] = (dev(p), dev(sc), dev(z))
+        # one copy of every linear of every layer
+        model = [{nm: tuple(None if t is None else t.clone() for t in proto[(n, k)]) + (n, k) for nm, n, k in shapes}
+                 for _ in range(layers)]
+        del proto
+        step_bytes = layers * sum(wq.wq_packed_bytes(fmt, n, k) + metadata_bytes(fmt, n, k) for _, n, k in shapes)
+        for m in (ms_list if fname != "f16" else ms_list[:1]):
+            def item(lin):
+                p, sc, z, n, k = lin
+                return (xs[k][:m], p, sc, z, ys[n][:m], n, k)
+
+            def step(_i):
+                for L in model:
+                    wq.wq_linear_grouped([item(L["q"]), item(L["k"]), item(L["v"])], m, fmt)
+                    wq.wq_linear_grouped([item(L["o"])], m, fmt)
+                    wq.wq_linear_grouped([item(L["gate"]), item(L["up"])], m, fmt)
+                    wq.wq_linear_grouped([item(L["down"])], m, fmt)
+            ms_total = time_steps(torch, step, steps, max(2, args.warmup // 20), 1)
+            t = ms_total / steps
+            results["%s_m%d" % (fname, m)] = {"ms_per_step": round(t, 4), "GB/s": round(step_bytes / (t * 1e-3) / 1e9, 1),
+                                             "pct_of_peak": round(100 * step_bytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                                             "tok_per_s": round(m / (t * 1e-3), 1), "weight_GB": round(step_bytes / 1e9, 3),
+                                             "launches_per_step": 4 * layers}
+        del model
+        torch.cuda.empty_cache()
+    for key, r in results.items():
+        f16 = results.get("f16_m" + key.split("_m")[1])
+        if f16 and not key.startswith("f16"):
+            r["speedup_vs_f16"] = round(f16["ms_per_step"] / r["ms_per_step"], 3)
+    head = "w4g32_m1" if args.sweep == "llama2_7b" else "w6e3m2_m%d" % ms_list[0]
+    h = results[head]
+    out = {"metric": METRIC, "value": h["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": max(2, args.warmup // 20),
+           "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f16", "data": "synthetic", "pct_of_peak": h["pct_of_peak"],
+           "config": {"workload": name, "weights": head.split("_m")[0], "M": int(head.split("_m")[1]), "layers": layers,
+                      "linears_per_layer": [nm for nm, _, _ in shapes],
+                      "launch": "per layer: grouped q/k/v, o, grouped gate/up, down",
+                      "timing": "HIP graph of one decode step's linears, replayed; events on the launch stream"},
+           "roofline": {"bound": "hbm", "achieved": h["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(h["GB/s"] / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "decode step (mixed)",
+                        "launches_per_step": h["launches_per_step"]},
+           "cpu_baseline": None, "sweep": results}
+    print(json.dumps(out))
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -200,6 +287,8 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 1
     wq.lib()
+    if args.sweep:
+        return run_sweep(args, torch)
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
