@@ -279,7 +279,7 @@ def run_sweep(args, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs the path on a single MI355X "
+        print("bench.py measures one GPU only: libwq runs the linear on a single MI355X "
               "(no collectives); --gpus %d is not supported" % args.gpus, file=sys.stderr)
         return 2
     import torch
