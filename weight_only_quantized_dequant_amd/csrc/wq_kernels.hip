@@ -47,9 +47,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int GEMV_MAX_M = 4;   // largest M served by the VALU GEMV; above it the MFMA kernel runs
 constexpr int MFMA_M = 16;      // rows of x per MFMA launch
-constexpr int GEMV_MAX_WAVES = 12;  // waves per workgroup of the GEMV (row blocks x split of K)
-// M = 3, 4 keep more x in registers: 8 waves per workgroup, so 256 VGPRs per lane.
-constexpr int gemv_max_waves(int M) { return M <= 2 ? GEMV_MAX_WAVES : 8; }
+constexpr int GEMV_WAVES = 4;   // waves per workgroup of the GEMV (row blocks x split of K)
 constexpr int MFMA_MAX_WAVES = 8;   // waves per workgroup of the MFMA kernel
 
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
@@ -197,9 +195,10 @@ __device__ __forceinline__ uint2 ld_nt8(const uint8_t* p) {
 // so every load instruction of a wave reads one contiguous block:
 //   W4: SEG = 32 (one unit = one zero-point group)   W6: SEG = 32 (one unit, two planes)
 //   W8: SEG = 16 (half a unit)                       F16: SEG = 8
-// A wave covers a chunk of 64 segments of B rows. The workgroup is B rows x all of K; its
-// WK waves take the chunks c = wave, wave + WK, ... and double-buffer them: while chunk i
-// is decoded, the loads of chunk i+1 (x first, then the B rows) are in flight.
+// A wave covers a chunk of 64 segments of B rows. A workgroup of 4 waves holds 4 / WK row
+// blocks of B rows; the WK waves of a block take the chunks c = wave, wave + WK, ... and
+// double-buffer them: while chunk i is decoded, the loads of chunk i+1 (x first, then the
+// B rows) are in flight.
 //
 // The decode skips the per-weight bias and zero-point subtraction. A lane dots x with
 // the biased fp16 values it forms in one v_and_or_b32 / v_perm_b32:
@@ -367,8 +366,8 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
   }
 }
 
-// One workgroup's work: rows [block*B, block*B + B) of one linear.
-// A workgroup of W waves holds R = W / WK row blocks; the WK waves of each split K.
+// One workgroup's work: R = 4 / WK row blocks of B rows of one linear; the WK waves of
+// each block split K.
 template <int FMT, int M, int B>
 __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                           const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
@@ -423,7 +422,7 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const 
       }
     return;
   }
-  __shared__ float red[GEMV_MAX_WAVES][B * M];
+  __shared__ float red[GEMV_WAVES][B * M];
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
@@ -444,7 +443,7 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const 
 }
 
 template <int FMT, int M, int B>
-__global__ __launch_bounds__(64 * gemv_max_waves(M)) void gemv_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_kernel(const uint16_t* __restrict__ x,
                                                                    const uint8_t* __restrict__ w,
                                                                    const uint16_t* __restrict__ scales,
                                                                    const uint16_t* __restrict__ zeros,
@@ -467,7 +466,7 @@ struct GemvGroup {
 };
 
 template <int FMT, int M, int B>
-__global__ __launch_bounds__(64 * gemv_max_waves(M)) void gemv_grouped_kernel(const GemvGroup g) {
+__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_grouped_kernel(const GemvGroup g) {
   int j = 0;
   while (j + 1 < g.count && (int)blockIdx.x >= g.first_block[j + 1]) ++j;   // workgroup-uniform
   gemv_body<FMT, M, B>(g.x[j], g.w[j], g.scales[j], g.zeros[j], g.y[j], g.N[j], g.K[j], blockIdx.x - g.first_block[j],
@@ -849,12 +848,14 @@ struct GemvPlan {
 
 // Waves splitting K: the fewest that give enough waves over the row blocks (W4, with the
 // most decode work per byte, runs best at ~4 waves per CU, the others at ~16), then,
-// among the splits with the same chunks per wave, the smallest (even work).
+// among the splits with the same chunks per wave, the smallest (even work). Only powers
+// of two, so that workgroups hold a multiple of 4 waves and spread evenly over a CU's
+// four SIMDs (a 6-wave workgroup puts two waves on two SIMDs and one on the others).
 int gemv_waves_for(int fmt, int64_t N, int64_t K, int B) {
   const int64_t L = fmt == WQ_FMT_W8 ? 16 : fmt == WQ_FMT_F16 ? 8 : 32;
   const int64_t C = (K / L + 63) / 64, blocks = (N + B - 1) / B;
   const int64_t target = fmt == WQ_FMT_W4G32 ? 1024 : 4096;
-  static const int cand[] = {1, 2, 3, 4, 6};
+  static const int cand[] = {1, 2, 4};
   int WK = 1;
   for (int w : cand) {
     if (w > C) break;
@@ -867,13 +868,19 @@ int gemv_waves_for(int fmt, int64_t N, int64_t K, int B) {
   return WK;
 }
 
+// Rows per wave: 4, halved while the launch would have fewer than 1024 waves. F16 rows of
+// 10240 or more outputs take one row per wave (the weight stream needs more waves in flight
+// when nothing is decoded).
+int gemv_rows_per_wave(int fmt, int64_t N, int64_t K) {
+  if (fmt == WQ_FMT_F16 && N >= 10240) return 1;
+  int B = 4;
+  while (B > 1 && ((N + B - 1) / B) * gemv_waves_for(fmt, N, K, B) < 1024) B >>= 1;
+  return B;
+}
+
 GemvPlan plan_gemv(int fmt, int64_t N, int64_t K) {
-  int B = 4, WK = gemv_waves_for(fmt, N, K, 4);
-  while (B > 1 && ((N + B - 1) / B) * WK < 2048) {
-    B >>= 1;
-    WK = gemv_waves_for(fmt, N, K, B);
-  }
-  const int R = WK >= 4 ? 1 : 4 / WK;   // ~4 waves per workgroup
+  const int B = gemv_rows_per_wave(fmt, N, K), WK = gemv_waves_for(fmt, N, K, B);
+  const int R = GEMV_WAVES / WK;
   const int64_t blocks = (N + B - 1) / B;
   return {B, WK, R, static_cast<int>((blocks + R - 1) / R)};
 }
@@ -987,7 +994,14 @@ int grouped_rows_per_wave(int fmt, const wq_linear_item* items, int count) {
   int big = 0;
   for (int i = 1; i < count; ++i)
     if (items[i].N * items[i].K > items[big].N * items[big].K) big = i;
-  return plan_gemv(fmt, items[big].N, items[big].K).B;
+  return gemv_rows_per_wave(fmt, items[big].N, items[big].K);
+}
+
+// Launch order of a grouped call: the items with the longest rows (most chunks per wave)
+// first, so that the waves that finish last are the short ones. Ties keep the caller's order.
+void grouped_order(const wq_linear_item* items, int count, int (&order)[MAX_GROUP]) {
+  for (int i = 0; i < count; ++i) order[i] = i;
+  std::stable_sort(order, order + count, [&](int a, int b) { return items[a].K > items[b].K; });
 }
 
 int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, const uint16_t* z, const uint16_t* y,
@@ -1073,25 +1087,16 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
   // one rows-per-wave B for the whole launch: the one the largest item's plan picks (the
   // small items alone would pick fewer rows per wave to get enough waves, which the
   // launch has anyway); each item keeps the K split its own plan gives for that B
-  int B = grouped_rows_per_wave(fmt, items, count);
+  const int B = grouped_rows_per_wave(fmt, items, count);
+  int order[MAX_GROUP];
+  grouped_order(items, count, order);
   GemvGroup g = {};
   g.count = count;
-  int block_waves = 1;
-  for (int i = 0; i < count; ++i) {
-    g.WK[i] = gemv_waves_for(fmt, items[i].N, items[i].K, B);
-    block_waves = std::lcm(block_waves, g.WK[i]);
-  }
-  if (block_waves > gemv_max_waves(static_cast<int>(M))) {   // 3 with 4: keep powers of two only
-    block_waves = 1;
-    for (int i = 0; i < count; ++i) {
-      g.WK[i] = g.WK[i] >= 4 ? 4 : g.WK[i] >= 2 ? 2 : 1;
-      block_waves = std::max(block_waves, g.WK[i]);
-    }
-  }
-  while (block_waves < 4) block_waves *= 2;   // 4, 6, 8 or 12 waves
+  for (int i = 0; i < count; ++i) g.WK[i] = gemv_waves_for(fmt, items[order[i]].N, items[order[i]].K, B);
+  const int block_waves = GEMV_WAVES;   // every split is 1, 2 or 4
   int grid = 0;
   for (int i = 0; i < count; ++i) {
-    const wq_linear_item& it = items[i];
+    const wq_linear_item& it = items[order[i]];
     const int R = block_waves / g.WK[i];
     g.first_block[i] = grid;
     g.x[i] = it.x;
@@ -1141,7 +1146,7 @@ const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, 
     mfma = mfma || use_mfma(fmt, mm, N[i]);
   }
   if (mfma) return wq_linear_kernel_name(fmt, M, N[big], K[big]);   // separate launches: the largest item's
-  snprintf(buf, sizeof(buf), "gemv_grouped_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), plan_gemv(fmt, N[big], K[big]).B);
+  snprintf(buf, sizeof(buf), "gemv_grouped_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), gemv_rows_per_wave(fmt, N[big], K[big]));
   return buf;
 }
 
