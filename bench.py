@@ -16,6 +16,9 @@ Method:
   that holds R steps (no host gaps), bracketed by synchronize + events on the launch
   stream. The other launch style and each linear alone are timed the same way and
   reported beside it.
+* Warm-up: W untimed steps first (default 10000, about 0.15 s). A step lasts microseconds,
+  and the GPU's clocks need that long under load to settle: with a few dozen warm-up steps
+  the same run varied by +-5%.
 * Roofline: the step holds only the dominant kernel's launches, back to back, so its
   average launch duration is the timed-region time per step over its launches.
 * fp16 baselines: libwq's own fp16 kernel (grouped and separate) and torch's F.linear
@@ -48,8 +51,9 @@ ROTATE_BYTES = 1 << 30
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=4000)
+    ap.add_argument("--warmup", type=int, default=10000,
+                    help="untimed steps first; steps are microseconds long, and the GPU clocks need ~0.1 s of load to settle")
     ap.add_argument("--workload", default="llama7b_w4g32_linears", choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--m", type=int, default=None, help="rows of x (default: the workload's first M)")
     ap.add_argument("--separate", action="store_true",
@@ -216,7 +220,7 @@ def run_sweep(args, torch):
     xs = {k: torch.from_numpy(draws[next(s for s in distinct if s[1] == k)][1].view(np.int16).copy()).to("cuda")
           for k in {k for _, k in distinct}}
     ys = {n: torch.empty((mmax, n), dtype=torch.int16, device="cuda") for n in {n for n, _ in distinct}}
-    results, steps = {}, max(1, args.steps // 20)
+    results, steps = {}, max(1, args.steps // 100)
     for fname in fmts:
         fmt = FMT_OF[fname]
         proto = {}
@@ -247,7 +251,7 @@ def run_sweep(args, torch):
                     wq.wq_linear_grouped([item(L["o"])], m, fmt)
                     wq.wq_linear_grouped([item(L["gate"]), item(L["up"])], m, fmt)
                     wq.wq_linear_grouped([item(L["down"])], m, fmt)
-            ms_total = time_steps(torch, step, steps, max(2, args.warmup // 20), 1)
+            ms_total = time_steps(torch, step, steps, max(2, args.warmup // 100), 1)
             t = ms_total / steps
             results["%s_m%d" % (fname, m)] = {"ms_per_step": round(t, 4), "GB/s": round(step_bytes / (t * 1e-3) / 1e9, 1),
                                              "pct_of_peak": round(100 * step_bytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
@@ -261,7 +265,7 @@ def run_sweep(args, torch):
             r["speedup_vs_f16"] = round(f16["ms_per_step"] / r["ms_per_step"], 3)
     head = "w4g32_m1" if args.sweep == "llama2_7b" else "w6e3m2_m%d" % ms_list[0]
     h = results[head]
-    out = {"metric": METRIC, "value": h["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": max(2, args.warmup // 20),
+    out = {"metric": METRIC, "value": h["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": max(2, args.warmup // 100),
            "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "f16", "data": "synthetic", "pct_of_peak": h["pct_of_peak"],
            "config": {"workload": name, "weights": head.split("_m")[0], "M": int(head.split("_m")[1]), "layers": layers,

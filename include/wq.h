@@ -132,9 +132,9 @@ typedef struct {
  * sum may run in another order when the items' sizes differ a lot). One launch
  * instead of count means the GPU ramps up and drains once; in a decode step this fits
  * q/k/v or gate/up, and any set of linears whose inputs are ready. Items must not write
- * into one another's inputs. When wq_linear would use the matrix-core kernel for any item
- * (M >= 5, or M = 4 with W6/W8 and N >= 4096), every item runs as its own wq_linear launch
- * instead. Errors: as wq_linear, per item, all checked before any launch; WQ_ERR_ARG also
+ * into one another's inputs. When wq_linear would use a matrix-core kernel for any item
+ * (M >= 5; M = 4 with W6/W8 and N >= 4096, or with W4, K a multiple of 256 and N*K >= 2^26),
+ * every item runs as its own wq_linear launch instead. Errors: as wq_linear, per item, all checked before any launch; WQ_ERR_ARG also
  * for count outside 0..16 or items == NULL. */
 int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt, void* stream);
 

@@ -79,7 +79,11 @@ def test_linear_every_m(fmt, m):
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
 @pytest.mark.parametrize("n,k,m", [(1, 32, 1), (1, 32, 16), (3, 64, 2), (16, 128, 5), (33, 2048, 1), (33, 2048, 9),
                                    (130, 8192, 1), (130, 8192, 16), (5, 96, 37), (64, 1024, 20), (4100, 256, 4),
-                                   (16500, 128, 5)])
+                                   (16500, 128, 5),
+                                   # K a multiple of 256 (W4 through LDS): a ragged last 32-unit stage
+                                   # (2304 = 72 units), ragged 16-row blocks, two blocks per wave from
+                                   # 8192 rows, a single stage (K = 256)
+                                   (37, 2304, 5), (37, 2304, 16), (8200, 2304, 8), (40, 11008, 13), (48, 256, 6)])
 def test_linear_shapes(fmt, n, k, m):
     w = _weights(n, k, 3 * n + k)
     _, x = inputs.small_case(2000 + n + m, 1, k, m)
@@ -130,6 +134,18 @@ def test_linear_rows_of_a_batch_match_single_rows():
             yi = dw.linear(x[i:i + 1])
             check_linear(yi, x[i:i + 1], wd)
             check_linear(yb[i:i + 1], x[i:i + 1], wd)
+
+
+@pytest.mark.parametrize("n,k,m", [(8192, 8192, 4), (8192, 8192, 3), (12000, 4096, 4)])
+def test_w4_m4_kernel_choice_sampled(n, k, m):
+    # W4 at M = 4 runs on the matrix cores from N*K = 2^26 on, on the GEMV below; both agree
+    # with the oracle on sampled rows
+    w, x = inputs.weights_and_x(inputs.rng_for(90, n + m), n, k, m)
+    dw = DeviceWeights(wq.FMT_W4G32, w)
+    rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(n).choice(n, 62, replace=False)]))
+    wd = oracle_rows(wq.FMT_W4G32, w[rows])[0]
+    y = dw.linear(x)
+    check_linear(y[:, rows], x, wd, "%s n %d k %d m %d" % (wq.wq_linear_kernel_name(wq.FMT_W4G32, m, n, k), n, k, m))
 
 
 # ------------------------------------------------------------------ full-size workloads (sampled rows)

@@ -208,15 +208,22 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert L.wq_linear(a, a, a, a, a, 1, 64, (1 << 26) + 32, 1, None) == -2    # K above 2^26
     assert L.wq_linear(a, a, a, a, a, 1, 1 << 22, 1 << 20, 1, None) == -2       # N*K/32 above int32
     assert wq.wq_linear_kernel_name(2, 1, 4096, 4096).startswith("gemv_kernel")
-    assert wq.wq_linear_kernel_name(3, 16, 4096, 4096).startswith("w6_lds_kernel")
+    assert wq.wq_linear_kernel_name(3, 16, 4096, 4096) == "lm_kernel<3, 1>"
+    assert wq.wq_linear_kernel_name(3, 16, 8192, 4096) == "lm_kernel<3, 2>"
     assert wq.wq_linear_kernel_name(1, 16, 4096, 4096).startswith("mfma_kernel")
+    assert wq.wq_linear_kernel_name(0, 16, 4096, 4096).startswith("mfma_kernel")
+    # W4 on the matrix cores: through LDS when K is a multiple of 256, else fragment loads
+    assert wq.wq_linear_kernel_name(2, 8, 4096, 4096) == "lm_kernel<2, 1>"
+    assert wq.wq_linear_kernel_name(2, 8, 4096, 4128) == "mfma_kernel<2, 1>"
     assert wq.wq_linear_kernel_name(3, 3, 4096, 4096).startswith("gemv_kernel")
-    # M = 4: the matrix cores for W6/W8 with N >= 4096, the GEMV otherwise
-    assert wq.wq_linear_kernel_name(3, 4, 4096, 4096).startswith("w6_lds_kernel")
+    # M = 4: the matrix cores for W6/W8 with N >= 4096 and for W4 from N*K = 2^26, the GEMV otherwise
+    assert wq.wq_linear_kernel_name(3, 4, 4096, 4096).startswith("lm_kernel")
     assert wq.wq_linear_kernel_name(1, 4, 8192, 4096).startswith("mfma_kernel")
     assert wq.wq_linear_kernel_name(3, 4, 1024, 4096).startswith("gemv_kernel")
     assert wq.wq_linear_kernel_name(2, 4, 8192, 4096).startswith("gemv_kernel")
+    assert wq.wq_linear_kernel_name(2, 4, 8192, 8192) == "lm_kernel<2, 2>"
     assert wq.wq_linear_kernel_name(3, 16, 4096, 40) == ""
     # grouped: the GEMV takes its rows per wave from the largest item
     assert wq.wq_linear_grouped_kernel_name(3, 1, [(8192, 8192), (1024, 8192)]) == "gemv_grouped_kernel<3, 1, 4>"
-    assert wq.wq_linear_grouped_kernel_name(3, 8, [(1024, 8192), (8192, 8192)]) == "w6_lds_kernel<2>"
+    assert wq.wq_linear_grouped_kernel_name(3, 8, [(1024, 8192), (8192, 8192)]) == "lm_kernel<3, 2>"
+    assert wq.wq_linear_grouped_kernel_name(2, 4, [(8192, 8192), (1024, 8192)]) == "lm_kernel<2, 2>"

@@ -637,147 +637,200 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_kernel(const uint16_
   mfma_body<FMT, RB>(x, w, scales, zeros, y, M, N, K, blockIdx.x, WK);
 }
 
-// ---------------------------------------------------------------- W6 on the matrix cores through LDS (M = 4..16)
-// The fragment-shaped loads of mfma_kernel read 16 rows x 64 (lo plane) and 16 rows x 32
-// (hi plane) bytes per wave instruction, a pattern that HBM serves at roughly half the
-// rate of contiguous reads. Here each wave reads its rows contiguously instead, 32 units
-// (a half of a 64-unit plane chunk) at a time: the lo slices as 2 rows x 512 B per
-// instruction and the hi slices as 4 rows x 256 B, parks them in its own LDS region, and
-// reads the MFMA B fragments from there. No barriers: the region belongs to one wave,
-// and LDS operations of a wave complete in order.
-// LDS image of one 16-row block: lo slice of unit u (0..31) of row r at 512 r + 16 (u ^ r),
-// hi slice at 8192 + 256 r + 8 (u ^ (2r & 31)). The XOR swizzles put the 16 rows of a
-// fragment read in different banks.
-// x fragments of K tile t (4 units; tile t = 8 i + j of stage i) sit in register ring slot
-// t % 4 and are loaded three tiles ahead.
-constexpr int W6L_BLOCK = 16 * 512 + 16 * 256;   // LDS bytes of one row block's stage (12 KB)
-constexpr int W6L_WAVES = 4;                     // waves per workgroup
+// ---------------------------------------------------------------- W4 / W6 on the matrix cores through LDS
+// The fragment-shaped loads of mfma_kernel read, per wave instruction, 16 rows x 16 bytes
+// (W4) or 16 rows x 64 + 32 bytes (W6), a pattern that HBM serves far below the rate of
+// contiguous reads (16-byte row pieces at about a fifth). Here each wave reads its rows
+// contiguously instead, 32 units (a "stage") of each of the 16 rows of a row block at a
+// time, parks them in its own LDS region, and reads the MFMA B fragments from there. No
+// barriers: the region belongs to one wave, and LDS operations of a wave complete in order.
+//   W4: one wave instruction reads 2 rows x 512 B; the stage's scales and zeros (16 rows x
+//       32 groups) come straight into registers, lane (n, q) holding groups 8q..8q+7 of
+//       row n, which are exactly the groups its fragments need.
+//   W6: the lo slices as 2 rows x 512 B per instruction, the hi slices as 4 rows x 256 B.
+// LDS image of one 16-row block (XOR swizzles put the 16 rows of a fragment read in
+// different banks):
+//   W4: unit u (0..31) of row r at 512 r + 16 (u ^ r)                              8 KB
+//   W6: lo slice of unit u at 512 r + 16 (u ^ r), hi slice at 8192 + 256 r + 8 (u ^ (2r & 31))   12 KB
+// K tile j (0..7) of a stage is 4 units, one per lane quad q: unit 8q + j. Its x fragments
+// sit in register ring slot j % 4 and are loaded three tiles ahead.
+template <int FMT> constexpr int lm_block() { return FMT == WQ_FMT_W4G32 ? 16 * 512 : 16 * 512 + 16 * 256; }
+template <int FMT> constexpr int lm_loads() { return FMT == WQ_FMT_W4G32 ? 8 : 12; }
+constexpr int LM_WAVES = 4;   // waves per workgroup
 
-template <int RB> struct W6lStage { uint4 lo[RB][8]; uint4 hi[RB][4]; };
+template <int FMT, int RB>
+struct LmStage {
+  uint4 v[RB][lm_loads<FMT>()];
+  uint4 s[FMT == WQ_FMT_W4G32 ? RB : 1], z[FMT == WQ_FMT_W4G32 ? RB : 1];   // W4: 8 groups' fp16 scales / zeros
+};
 
-template <int RB>
-__device__ __forceinline__ void w6l_load(W6lStage<RB>& st, const uint8_t* __restrict__ w, int n0, int N, int K, int h,
-                                         int lane) {
+// Global loads of stage h (units 32h .. 32h+31 of each row) of RB row blocks.
+template <int FMT, int RB>
+__device__ __forceinline__ void lm_load(LmStage<FMT, RB>& st, const uint8_t* __restrict__ w,
+                                        const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int n0,
+                                        int N, int K, int h, int lane) {
   const int U = K >> 5;
-  const uint32_t row_bytes = (uint32_t)U * 24;
-  const int c = h >> 1, half = h & 1;                  // 64-unit chunk and which half of it
-  const int uc = min(64, U - 64 * c);                   // units in the chunk
-  const uint32_t cbase = 64u * 24 * c;
+  const uint32_t row_bytes = (uint32_t)U * unit_bytes<FMT>();
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const int nb = min(n0 + 16 * r, N - 1);
     const uint8_t* rowb = w + uniform((size_t)nb * row_bytes);
+    if constexpr (FMT == WQ_FMT_W4G32) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {   // lo: lane l -> row 2i + l/32, unit l%32
-      const int rr = 2 * i + (lane >> 5);
-      const uint32_t nn = (uint32_t)(min(n0 + 16 * r + rr, N - 1) - nb);
-      const int j = min(32 * half + (lane & 31), uc - 1);   // past the chunk end: a valid unit, masked later
-      st.lo[r][i] = ld_nt16(rowb + nn * row_bytes + cbase + 16u * j);
-    }
+      for (int i = 0; i < 8; ++i) {   // lane l -> row 2i + l/32, unit l%32
+        const uint32_t nn = (uint32_t)(min(n0 + 16 * r + 2 * i + (lane >> 5), N - 1) - nb);
+        const uint32_t j = (uint32_t)min(32 * h + (lane & 31), U - 1);   // past the row end: a valid unit, masked later
+        st.v[r][i] = ld_nt16(rowb + nn * row_bytes + 16u * j);
+      }
+      // lane (n, q): groups 32h + 8q .. +7 of row n (U is a multiple of 8, so a group of 8 lies
+      // wholly inside the row or wholly past its end; one past the end reads the row's last 8)
+      const uint32_t nn = (uint32_t)(min(n0 + 16 * r + (lane & 15), N - 1) - nb);
+      const int g0 = min(32 * h + 8 * (lane >> 4), U - 8);
+      const size_t mb = uniform((size_t)nb * U * 2);
+      const uint32_t mo = 2u * (nn * (uint32_t)U + (uint32_t)g0);
+      st.s[r] = ld_nt16(reinterpret_cast<const uint8_t*>(scales) + mb + mo);
+      st.z[r] = ld_nt16(reinterpret_cast<const uint8_t*>(zeros) + mb + mo);
+    } else {
+      const int c = h >> 1, half = h & 1;                  // 64-unit chunk and which half of it
+      const int uc = min(64, U - 64 * c);                   // units in the chunk
+      const uint32_t cbase = 64u * 24 * c;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {   // hi: lane l -> row 4i + l/16, units 2(l%16), 2(l%16)+1
-      const int rr = 4 * i + (lane >> 4);
-      const uint32_t nn = (uint32_t)(min(n0 + 16 * r + rr, N - 1) - nb);
-      // when j0 is the chunk's last unit (odd uc), read units j0-1, j0 and keep the second
-      const int j0 = min(32 * half + 2 * (lane & 15), uc - 1);
-      const int sh = (j0 + 1 >= uc && j0 > 0) ? 1 : 0;
-      const uint4 v = ld_nt16(rowb + nn * row_bytes + cbase + 16u * uc + 8u * (j0 - sh));
-      st.hi[r][i] = sh ? make_uint4(v.z, v.w, v.z, v.w) : v;
+      for (int i = 0; i < 8; ++i) {   // lo: lane l -> row 2i + l/32, unit l%32
+        const uint32_t nn = (uint32_t)(min(n0 + 16 * r + 2 * i + (lane >> 5), N - 1) - nb);
+        const int j = min(32 * half + (lane & 31), uc - 1);   // past the chunk end: a valid unit, masked later
+        st.v[r][i] = ld_nt16(rowb + nn * row_bytes + cbase + 16u * j);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // hi: lane l -> row 4i + l/16, units 2(l%16), 2(l%16)+1
+        const uint32_t nn = (uint32_t)(min(n0 + 16 * r + 4 * i + (lane >> 4), N - 1) - nb);
+        // when j0 is the chunk's last unit (odd uc), read units j0-1, j0 and keep the second
+        const int j0 = min(32 * half + 2 * (lane & 15), uc - 1);
+        const int sh = (j0 + 1 >= uc && j0 > 0) ? 1 : 0;
+        const uint4 v = ld_nt16(rowb + nn * row_bytes + cbase + 16u * uc + 8u * (j0 - sh));
+        st.v[r][8 + i] = sh ? make_uint4(v.z, v.w, v.z, v.w) : v;
+      }
     }
   }
 }
 
-template <int RB>
-__device__ __forceinline__ void w6l_store(const W6lStage<RB>& st, uint8_t* lds, int lane) {
+template <int FMT, int RB>
+__device__ __forceinline__ void lm_store(const LmStage<FMT, RB>& st, uint8_t* lds, int lane) {
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
-    uint8_t* base = lds + r * W6L_BLOCK;
+    uint8_t* base = lds + r * lm_block<FMT>();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int rr = 2 * i + (lane >> 5), u = lane & 31;
-      *reinterpret_cast<uint4*>(base + 512 * rr + 16 * (u ^ rr)) = st.lo[r][i];
+      *reinterpret_cast<uint4*>(base + 512 * rr + 16 * (u ^ rr)) = st.v[r][i];
     }
+    if constexpr (FMT == WQ_FMT_W6E3M2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 4 * i + (lane >> 4), u = 2 * (lane & 15), sw = (2 * rr) & 31;
-      *reinterpret_cast<uint2*>(base + 8192 + 256 * rr + 8 * (u ^ sw)) = make_uint2(st.hi[r][i].x, st.hi[r][i].y);
-      *reinterpret_cast<uint2*>(base + 8192 + 256 * rr + 8 * ((u + 1) ^ sw)) = make_uint2(st.hi[r][i].z, st.hi[r][i].w);
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * i + (lane >> 4), u = 2 * (lane & 15), sw = (2 * rr) & 31;
+        *reinterpret_cast<uint2*>(base + 8192 + 256 * rr + 8 * (u ^ sw)) = make_uint2(st.v[r][8 + i].x, st.v[r][8 + i].y);
+        *reinterpret_cast<uint2*>(base + 8192 + 256 * rr + 8 * ((u + 1) ^ sw)) = make_uint2(st.v[r][8 + i].z, st.v[r][8 + i].w);
+      }
     }
   }
 }
 
-// A workgroup of W6L_WAVES waves holds R = W6L_WAVES / WK row groups of 16 RB rows; the
-// WK waves of a group take the stages (32-unit K slices) h = kw, kw + WK, ...
-template <int RB>
-__global__ __launch_bounds__(64 * W6L_WAVES) void w6_lds_kernel(const uint16_t* __restrict__ x,
-                                                                const uint8_t* __restrict__ w,
-                                                                const uint16_t* __restrict__ scales,
-                                                                uint16_t* __restrict__ y, int M, int N, int K, int WK) {
-  extern __shared__ uint4 w6l_lds[];
+__device__ __forceinline__ uint16_t half_of(const uint4& v, int j) {   // 16-bit element j (0..7) of v
+  const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+  return static_cast<uint16_t>((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+// A workgroup of LM_WAVES waves holds R = LM_WAVES / WK row groups of 16 RB rows; the WK
+// waves of a group take the stages h = kw, kw + WK, ...
+template <int FMT, int RB>
+__global__ __launch_bounds__(64 * LM_WAVES) void lm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                                          const uint16_t* __restrict__ scales,
+                                                          const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
+                                                          int M, int N, int K, int WK) {
+  extern __shared__ uint4 lm_lds[];
   const int lane = threadIdx.x & 63;
   const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int R = W6L_WAVES / WK;
+  const int R = LM_WAVES / WK;
   const int sub = wave_id / WK, kw = wave_id - sub * WK;
   const int nl = lane & 15, q = lane >> 4;
   const int U = K >> 5, H = (U + 31) >> 5;
   const int n0 = (blockIdx.x * R + sub) * 16 * RB;
   const int NI = kw < H ? (H - kw + WK - 1) / WK : 0;
-  uint8_t* lds = reinterpret_cast<uint8_t*>(w6l_lds) + wave_id * RB * W6L_BLOCK;
+  uint8_t* lds = reinterpret_cast<uint8_t*>(lm_lds) + wave_id * RB * lm_block<FMT>();
   const bool xrow = nl < M;
   f4 acc[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) acc[r] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  W6lStage<RB> st;
+  LmStage<FMT, RB> st;
+  constexpr int MS = FMT == WQ_FMT_W4G32 ? RB : 1;
+  uint4 cs[MS], cz[MS];   // W4: the metadata of the stage in LDS
   h8 xr[4][4];
-  auto xload = [&](int t) {   // x[m = nl][unit 32h + 4j + q] of K tile t = 8i + j
+  auto xload = [&](int t) {   // x[m = nl][unit 32h + 8q + j] of K tile t = 8i + j
     const int h = kw + (t >> 3) * WK, j = t & 7;
-    const uint32_t u = (uint32_t)min(32 * h + 4 * j + q, U - 1);
+    const uint32_t u = (uint32_t)min(32 * h + 8 * q + j, U - 1);
     const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) +
                                                      (uint32_t)min(nl, M - 1) * (uint32_t)K * 2u + 64u * u);
 #pragma unroll
     for (int k = 0; k < 4; ++k) xr[t & 3][k] = __builtin_bit_cast(h8, xp[k]);
   };
+  auto park = [&]() {   // the loaded stage -> LDS (and W4 metadata -> cs, cz)
+    lm_store<FMT, RB>(st, lds, lane);
+    if constexpr (FMT == WQ_FMT_W4G32) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) { cs[r] = st.s[r]; cz[r] = st.z[r]; }
+    }
+  };
   if (NI > 0) {
     xload(0); xload(1); xload(2);
-    w6l_load<RB>(st, w, n0, N, K, kw, lane);
-    w6l_store<RB>(st, lds, lane);
+    lm_load<FMT, RB>(st, w, scales, zeros, n0, N, K, kw, lane);
+    park();
   }
   for (int i = 0; i < NI; ++i) {
     const int h = kw + i * WK;
-    if (i + 1 < NI) w6l_load<RB>(st, w, n0, N, K, h + WK, lane);
+    if (i + 1 < NI) lm_load<FMT, RB>(st, w, scales, zeros, n0, N, K, h + WK, lane);
     __builtin_amdgcn_sched_barrier(0);   // keep the next stage's loads ahead of the compute
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int t = 8 * i + j;
       if (j + 3 < 8 || i + 1 < NI) xload(t + 3);
-      const bool ok = xrow && (32 * h + 4 * j + q < U);
+      const int u = 8 * q + j;   // unit within the stage
+      const bool ok = xrow && (32 * h + u < U);
       const h8 zero8 = {};
-      const int u = 4 * j + q;   // unit within the stage
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
-        const uint8_t* base = lds + r * W6L_BLOCK;
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + 512 * nl + 16 * (u ^ nl));
-        const uint2 hi = *reinterpret_cast<const uint2*>(base + 8192 + 256 * nl + 8 * (u ^ ((2 * nl) & 31)));
-        u32x6 v;
-        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y;
-        const h32 hv = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(v, 1.0f);
+        const uint8_t* base = lds + r * lm_block<FMT>();
+        Raw<FMT> raw;
+        h2 zc1 = {}, zc2 = {};
+        raw.a = *reinterpret_cast<const uint4*>(base + 512 * nl + 16 * (u ^ nl));
+        if constexpr (FMT == WQ_FMT_W6E3M2) {
+          raw.b = *reinterpret_cast<const uint2*>(base + 8192 + 256 * nl + 8 * (u ^ ((2 * nl) & 31)));
+        } else {
+          w4_consts(half_of(cz[r], j), zc1, zc2);
+        }
+        h2 wv[16];
+        decode<FMT>(raw, zc1, zc2, wv);
+        if constexpr (FMT == WQ_FMT_W4G32) {
+          const _Float16 sv = __builtin_bit_cast(_Float16, half_of(cs[r], j));
+          const h2 s2 = {sv, sv};
+#pragma unroll
+          for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           h8 b;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) b[e] = hv[8 * k + e];
+          for (int e = 0; e < 4; ++e) { b[2 * e] = wv[4 * k + e][0]; b[2 * e + 1] = wv[4 * k + e][1]; }
           acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ok ? xr[t & 3][k] : zero8, b, acc[r], 0, 0, 0);
         }
       }
     }
-    if (i + 1 < NI) w6l_store<RB>(st, lds, lane);
+    if (i + 1 < NI) park();
   }
 
   // WK partials through LDS (every wave is done with its region after the barrier), fixed
   // order; D[m][n] sits in lane (n + 16*(m/4)), register m%4
   __syncthreads();
-  f4* red = reinterpret_cast<f4*>(w6l_lds);
+  f4* red = reinterpret_cast<f4*>(lm_lds);
 #pragma unroll
   for (int r = 0; r < RB; ++r) red[(wave_id * RB + r) * 64 + lane] = acc[r];
   __syncthreads();
@@ -788,7 +841,7 @@ __global__ __launch_bounds__(64 * W6L_WAVES) void w6_lds_kernel(const uint16_t* 
     for (int k = 1; k < WK; ++k) t += red[((sub * WK + k) * RB + r) * 64 + lane];
     const int n = n0 + 16 * r + nl;
     if (n < N) {
-      const float sc = f16_to_f32(scales[n]);
+      const float sc = FMT == WQ_FMT_W6E3M2 ? f16_to_f32(scales[n]) : 1.0f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int m = 4 * q + k;
@@ -891,8 +944,9 @@ struct MfmaPlan {
   int grid;   // workgroups
 };
 
-// The matrix-core kernel serves M >= 5, and M = 4 for W6/W8 rows of 4096 or more, where
-// it beats the VALU GEMV (which then spends four dot products per weight pair).
+// The matrix cores serve M >= 5, and M = 4 for W6/W8 rows of 4096 or more, where they beat
+// the VALU GEMV (which then spends four dot products per weight pair): lm_kernel for W6 and
+// for W4 with K a multiple of 256 (see use_lm), mfma_kernel for the rest.
 bool use_mfma(int fmt, int64_t M, int64_t N) {
   if (M > GEMV_MAX_M) return true;
   return M == GEMV_MAX_M && (fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W8) && N >= 4096;
@@ -911,20 +965,29 @@ MfmaPlan plan_mfma(int fmt, int64_t N, int64_t K) {
   return {RB, WK, static_cast<int>(groups)};
 }
 
-struct W6lPlan {
+struct LmPlan {
   int RB;     // 16-row blocks per wave
   int WK;     // waves of a row group splitting K (1, 2 or 4)
   int grid;   // workgroups
 };
 
+// The LDS-staged kernel serves W6 and W4 wherever the matrix cores run for them (W4 only when
+// K is a multiple of 256, so that a lane's 8 groups of metadata are one aligned 16-byte load),
+// and W4 at M = 4 from N*K = 2^26 on, where it beats the VALU GEMV.
+bool use_lm(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (fmt == WQ_FMT_W6E3M2) return use_mfma(fmt, M, N);
+  if (fmt != WQ_FMT_W4G32 || K % 256) return false;
+  return M > GEMV_MAX_M || (M == GEMV_MAX_M && N * K >= (int64_t(1) << 26));
+}
+
 // Two row blocks per wave from 8192 rows; WK doubled until ~1024 waves.
-W6lPlan plan_w6l(int64_t N, int64_t K) {
+LmPlan plan_lm(int64_t N, int64_t K) {
   const int RB = N >= 8192 ? 2 : 1;
   const int64_t H = (K / 32 + 31) / 32;
   const int64_t groups = (N + 16 * RB - 1) / (16 * RB);
   int WK = 1;
-  while (WK < W6L_WAVES && WK < H && groups * WK < 1024) WK *= 2;
-  const int R = W6L_WAVES / WK;
+  while (WK < LM_WAVES && WK < H && groups * WK < 1024) WK *= 2;
+  const int R = LM_WAVES / WK;
   return {RB, WK, static_cast<int>((groups + R - 1) / R)};
 }
 
@@ -943,6 +1006,16 @@ hipError_t launch_gemv_m(const GemvPlan& p, hipStream_t s, const uint16_t* x, co
 template <int FMT>
 hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
                              uint16_t* y, int M, int N, int K) {
+  if constexpr (FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W6E3M2) {
+    if (use_lm(FMT, M, N, K)) {
+      const LmPlan p = plan_lm(N, K);
+      const dim3 grid(p.grid), block(64 * LM_WAVES);
+      const size_t shm = (size_t)LM_WAVES * p.RB * lm_block<FMT>();
+      if (p.RB == 2) hipLaunchKernelGGL((lm_kernel<FMT, 2>), grid, block, shm, s, x, w, sc, z, y, M, N, K, p.WK);
+      else hipLaunchKernelGGL((lm_kernel<FMT, 1>), grid, block, shm, s, x, w, sc, z, y, M, N, K, p.WK);
+      return hipGetLastError();
+    }
+  }
   if (!use_mfma(FMT, M, N)) {
     const GemvPlan p = plan_gemv(FMT, N, K);
     switch (M) {
@@ -951,14 +1024,6 @@ hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w,
       case 3: return launch_gemv_m<FMT, 3>(p, s, x, w, sc, z, y, N, K);
       default: return launch_gemv_m<FMT, 4>(p, s, x, w, sc, z, y, N, K);
     }
-  }
-  if constexpr (FMT == WQ_FMT_W6E3M2) {
-    const W6lPlan p = plan_w6l(N, K);
-    const dim3 grid(p.grid), block(64 * W6L_WAVES);
-    const size_t shm = (size_t)W6L_WAVES * p.RB * W6L_BLOCK;
-    if (p.RB == 2) hipLaunchKernelGGL((w6_lds_kernel<2>), grid, block, shm, s, x, w, sc, y, M, N, K, p.WK);
-    else hipLaunchKernelGGL((w6_lds_kernel<1>), grid, block, shm, s, x, w, sc, y, M, N, K, p.WK);
-    return hipGetLastError();
   }
   const MfmaPlan p = plan_mfma(FMT, N, K);
   const dim3 grid(p.grid), block(64 * p.WK);
@@ -1075,7 +1140,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
     if (st != WQ_OK) return st;
   }
   bool mfma = false;
-  for (int i = 0; i < count; ++i) mfma = mfma || use_mfma(fmt, M, items[i].N);
+  for (int i = 0; i < count; ++i) mfma = mfma || use_mfma(fmt, M, items[i].N) || use_lm(fmt, M, items[i].N, items[i].K);
   if (mfma) {   // the MFMA path has no grouped form: one launch per item
     for (int i = 0; i < count; ++i) {
       const wq_linear_item& it = items[i];
@@ -1124,12 +1189,13 @@ const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   static thread_local char buf[96];
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 32 || K % 32) return "";
   const int64_t mm = M < MFMA_M ? M : MFMA_M;
-  if (!use_mfma(fmt, mm, N)) {
+  if (use_lm(fmt, mm, N, K)) {
+    snprintf(buf, sizeof(buf), "lm_kernel<%d, %d>", fmt, plan_lm(N, K).RB);
+  } else if (!use_mfma(fmt, mm, N)) {
     const GemvPlan p = plan_gemv(fmt, N, K);
     snprintf(buf, sizeof(buf), "gemv_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), p.B);
   } else {
-    if (fmt == WQ_FMT_W6E3M2) snprintf(buf, sizeof(buf), "w6_lds_kernel<%d>", plan_w6l(N, K).RB);
-    else snprintf(buf, sizeof(buf), "mfma_kernel<%d, %d>", fmt, plan_mfma(fmt, N, K).RB);
+    snprintf(buf, sizeof(buf), "mfma_kernel<%d, %d>", fmt, plan_mfma(fmt, N, K).RB);
   }
   return buf;
 }
@@ -1143,7 +1209,7 @@ const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, 
   for (int i = 0; i < count; ++i) {
     if (N[i] < 1 || K[i] < 32 || K[i] % 32) return "";
     if (N[i] * K[i] > N[big] * K[big]) big = i;
-    mfma = mfma || use_mfma(fmt, mm, N[i]);
+    mfma = mfma || use_mfma(fmt, mm, N[i]) || use_lm(fmt, mm, N[i], K[i]);
   }
   if (mfma) return wq_linear_kernel_name(fmt, M, N[big], K[big]);   // separate launches: the largest item's
   snprintf(buf, sizeof(buf), "gemv_grouped_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), gemv_rows_per_wave(fmt, N[big], K[big]));
