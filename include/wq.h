@@ -132,18 +132,18 @@ typedef struct {
  * sum may run in another order when the items' sizes differ a lot). One launch
  * instead of count means the GPU ramps up and drains once; in a decode step this fits
  * q/k/v or gate/up, and any set of linears whose inputs are ready. Items must not write
- * into one another's inputs. When wq_linear would use a matrix-core kernel for any item
- * (M >= 5; M = 4 with W6/W8 and N >= 4096, or with W4, K a multiple of 256 and N*K >= 2^26),
- * every item runs as its own wq_linear launch instead. Errors: as wq_linear, per item, all checked before any launch; WQ_ERR_ARG also
- * for count outside 0..16 or items == NULL. */
+ * into one another's inputs. The launch uses the kernel wq_linear would use for the
+ * largest item (by N*K) for every item. M above 16: every item runs as its own wq_linear
+ * call instead. Errors: as wq_linear, per item, all checked before any launch; WQ_ERR_ARG
+ * also for count outside 0..16 or items == NULL. */
 int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt, void* stream);
 
 /* Name of the kernel wq_linear launches for (fmt, M, N, K) (for profiles), or "" if the
  * arguments are invalid. Host only; static storage. */
 const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
 
-/* Name of the kernel wq_linear_grouped launches for count items of sizes N[i] x K[i] (with
- * separate launches: the largest item's kernel), or "". */
+/* Name of the kernel wq_linear_grouped launches for count items of sizes N[i] x K[i] (above
+ * 16 rows, with separate launches: the largest item's kernel), or "". */
 const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, const int64_t* K, int count);
 
 #ifdef __cplusplus

@@ -136,9 +136,9 @@ def test_linear_rows_of_a_batch_match_single_rows():
             check_linear(yb[i:i + 1], x[i:i + 1], wd)
 
 
-@pytest.mark.parametrize("n,k,m", [(8192, 8192, 4), (8192, 8192, 3), (12000, 4096, 4)])
+@pytest.mark.parametrize("n,k,m", [(8192, 8192, 4), (8192, 8192, 3), (12000, 4096, 4), (2048, 4096, 4)])
 def test_w4_m4_kernel_choice_sampled(n, k, m):
-    # W4 at M = 4 runs on the matrix cores from N*K = 2^26 on, on the GEMV below; both agree
+    # W4 at M = 4 runs on the matrix cores from N*K = 2^24 on, on the GEMV below; both agree
     # with the oracle on sampled rows
     w, x = inputs.weights_and_x(inputs.rng_for(90, n + m), n, k, m)
     dw = DeviceWeights(wq.FMT_W4G32, w)
@@ -177,11 +177,19 @@ def test_workload_full_size_sampled(name, fmt):
 
 
 # ------------------------------------------------------------------ grouped launches
+GROUP_SETS = {
+    "mixed_k": [(40, 2080), (300, 4096), (64, 6144), (17, 96)],
+    # every K a multiple of 256 (W4 through LDS), 8200 rows (two 16-row blocks per wave)
+    "k256": [(40, 2304), (300, 4096), (8200, 256), (17, 512)],
+}
+
+
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
-@pytest.mark.parametrize("m", [1, 3, 7])
-def test_grouped_matches_separate_calls(fmt, m):
+@pytest.mark.parametrize("m", [1, 3, 4, 7, 16, 20])
+@pytest.mark.parametrize("set_name", sorted(GROUP_SETS))
+def test_grouped_matches_separate_calls(fmt, m, set_name):
     torch = torch_cuda()
-    shapes = [(40, 2080), (300, 4096), (64, 6144), (17, 96)]
+    shapes = GROUP_SETS[set_name]
     dws, xs = [], []
     for i, (n, k) in enumerate(shapes):
         w = _weights(n, k, 50 + i)
@@ -198,11 +206,15 @@ def test_grouped_matches_separate_calls(fmt, m):
         got = host_bits(ys[i])
         wd = dw.packed_host.view(np.uint16).reshape(dw.n, dw.k) if fmt == wq.FMT_F16 else oracle_rows(fmt, _weights(dw.n, dw.k, 50 + i))[0]
         check_linear(got, xs[i], wd, "grouped item %d" % i)
-        # an item whose own plan picks the launch's rows per wave runs the same kernel body
-        # with the same K split as its separate call (or is a separate call): identical bits
+        # an item whose own plan picks the launch's kernel family and rows per wave runs the
+        # same kernel body with the same K split as its separate call (or is a separate call):
+        # identical bits
         own = wq.wq_linear_kernel_name(fmt, m, dw.n, dw.k)
-        if not grouped.startswith("gemv_grouped") or own.split("<")[1] == grouped.split("<")[1]:
-            assert np.array_equal(got, sep[i]), "item %d differs from its separate call" % i
+        separate = "_grouped_kernel" not in grouped
+        same_body = own.split("_kernel<")[0] == grouped.split("_grouped_kernel<")[0] and \
+            own.split("<")[1] == grouped.split("<")[1]
+        if separate or same_body:
+            assert np.array_equal(got, sep[i]), "item %d differs from its separate call (%s, %s)" % (i, own, grouped)
 
 
 def test_grouped_llama7b_w4_linears_bit_identical_to_separate_calls():

@@ -637,6 +637,16 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_kernel(const uint16_
   mfma_body<FMT, RB>(x, w, scales, zeros, y, M, N, K, blockIdx.x, WK);
 }
 
+// Several linears of one format and one M in a single launch (see GemvGroup); each item keeps
+// its own K split, and a workgroup holds blockDim / 64 / WK of its row groups.
+template <int FMT, int RB>
+__global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_grouped_kernel(const GemvGroup g, int M) {
+  int j = 0;
+  while (j + 1 < g.count && (int)blockIdx.x >= g.first_block[j + 1]) ++j;   // workgroup-uniform
+  mfma_body<FMT, RB>(g.x[j], g.w[j], g.scales[j], g.zeros[j], g.y[j], M, g.N[j], g.K[j], blockIdx.x - g.first_block[j],
+                     g.WK[j]);
+}
+
 // ---------------------------------------------------------------- W4 / W6 on the matrix cores through LDS
 // The fragment-shaped loads of mfma_kernel read, per wave instruction, 16 rows x 16 bytes
 // (W4) or 16 rows x 64 + 32 bytes (W6), a pattern that HBM serves far below the rate of
@@ -653,9 +663,11 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_kernel(const uint16_
 //   W4: unit u (0..31) of row r at 512 r + 16 (u ^ r)                              8 KB
 //   W6: lo slice of unit u at 512 r + 16 (u ^ r), hi slice at 8192 + 256 r + 8 (u ^ (2r & 31))   12 KB
 // K tile j (0..7) of a stage is 4 units, one per lane quad q: unit 8q + j. Its x fragments
-// sit in register ring slot j % 4 and are loaded three tiles ahead.
+// sit in a register ring of lm_xring slots and are loaded lm_xring - 1 tiles ahead (W4 keeps
+// the ring at 2 so that its two-block kernel fits 256 VGPRs: two waves per SIMD).
 template <int FMT> constexpr int lm_block() { return FMT == WQ_FMT_W4G32 ? 16 * 512 : 16 * 512 + 16 * 256; }
 template <int FMT> constexpr int lm_loads() { return FMT == WQ_FMT_W4G32 ? 8 : 12; }
+template <int FMT> constexpr int lm_xring() { return FMT == WQ_FMT_W4G32 ? 2 : 4; }
 constexpr int LM_WAVES = 4;   // waves per workgroup
 
 template <int FMT, int RB>
@@ -742,10 +754,9 @@ __device__ __forceinline__ uint16_t half_of(const uint4& v, int j) {   // 16-bit
 // A workgroup of LM_WAVES waves holds R = LM_WAVES / WK row groups of 16 RB rows; the WK
 // waves of a group take the stages h = kw, kw + WK, ...
 template <int FMT, int RB>
-__global__ __launch_bounds__(64 * LM_WAVES) void lm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
-                                                          const uint16_t* __restrict__ scales,
-                                                          const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
-                                                          int M, int N, int K, int WK) {
+__device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                        const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
+                                        uint16_t* __restrict__ y, int M, int N, int K, int block, int WK) {
   extern __shared__ uint4 lm_lds[];
   const int lane = threadIdx.x & 63;
   const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -753,7 +764,7 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lm_kernel(const uint16_t* __res
   const int sub = wave_id / WK, kw = wave_id - sub * WK;
   const int nl = lane & 15, q = lane >> 4;
   const int U = K >> 5, H = (U + 31) >> 5;
-  const int n0 = (blockIdx.x * R + sub) * 16 * RB;
+  const int n0 = (block * R + sub) * 16 * RB;
   const int NI = kw < H ? (H - kw + WK - 1) / WK : 0;
   uint8_t* lds = reinterpret_cast<uint8_t*>(lm_lds) + wave_id * RB * lm_block<FMT>();
   const bool xrow = nl < M;
@@ -764,14 +775,15 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lm_kernel(const uint16_t* __res
   LmStage<FMT, RB> st;
   constexpr int MS = FMT == WQ_FMT_W4G32 ? RB : 1;
   uint4 cs[MS], cz[MS];   // W4: the metadata of the stage in LDS
-  h8 xr[4][4];
+  constexpr int XR = lm_xring<FMT>();
+  h8 xr[XR][4];
   auto xload = [&](int t) {   // x[m = nl][unit 32h + 8q + j] of K tile t = 8i + j
     const int h = kw + (t >> 3) * WK, j = t & 7;
     const uint32_t u = (uint32_t)min(32 * h + 8 * q + j, U - 1);
     const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) +
                                                      (uint32_t)min(nl, M - 1) * (uint32_t)K * 2u + 64u * u);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) xr[t & 3][k] = __builtin_bit_cast(h8, xp[k]);
+    for (int k = 0; k < 4; ++k) xr[t % XR][k] = __builtin_bit_cast(h8, xp[k]);
   };
   auto park = [&]() {   // the loaded stage -> LDS (and W4 metadata -> cs, cz)
     lm_store<FMT, RB>(st, lds, lane);
@@ -781,7 +793,8 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lm_kernel(const uint16_t* __res
     }
   };
   if (NI > 0) {
-    xload(0); xload(1); xload(2);
+#pragma unroll
+    for (int t = 0; t + 1 < XR; ++t) xload(t);
     lm_load<FMT, RB>(st, w, scales, zeros, n0, N, K, kw, lane);
     park();
   }
@@ -792,7 +805,7 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lm_kernel(const uint16_t* __res
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int t = 8 * i + j;
-      if (j + 3 < 8 || i + 1 < NI) xload(t + 3);
+      if (j + XR - 1 < 8 || i + 1 < NI) xload(t + XR - 1);
       const int u = 8 * q + j;   // unit within the stage
       const bool ok = xrow && (32 * h + u < U);
       const h8 zero8 = {};
@@ -820,7 +833,7 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lm_kernel(const uint16_t* __res
           h8 b;
 #pragma unroll
           for (int e = 0; e < 4; ++e) { b[2 * e] = wv[4 * k + e][0]; b[2 * e + 1] = wv[4 * k + e][1]; }
-          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ok ? xr[t & 3][k] : zero8, b, acc[r], 0, 0, 0);
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ok ? xr[t % XR][k] : zero8, b, acc[r], 0, 0, 0);
         }
       }
     }
@@ -849,6 +862,23 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lm_kernel(const uint16_t* __res
       }
     }
   }
+}
+
+template <int FMT, int RB>
+__global__ __launch_bounds__(64 * LM_WAVES) void lm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                                          const uint16_t* __restrict__ scales,
+                                                          const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
+                                                          int M, int N, int K, int WK) {
+  lm_body<FMT, RB>(x, w, scales, zeros, y, M, N, K, blockIdx.x, WK);
+}
+
+// Several linears in a single launch (see GemvGroup), each with its own K split.
+template <int FMT, int RB>
+__global__ __launch_bounds__(64 * LM_WAVES) void lm_grouped_kernel(const GemvGroup g, int M) {
+  int j = 0;
+  while (j + 1 < g.count && (int)blockIdx.x >= g.first_block[j + 1]) ++j;   // workgroup-uniform
+  lm_body<FMT, RB>(g.x[j], g.w[j], g.scales[j], g.zeros[j], g.y[j], M, g.N[j], g.K[j], blockIdx.x - g.first_block[j],
+                   g.WK[j]);
 }
 
 // ---------------------------------------------------------------- dequant
@@ -944,9 +974,9 @@ struct MfmaPlan {
   int grid;   // workgroups
 };
 
-// The matrix cores serve M >= 5, and M = 4 for W6/W8 rows of 4096 or more, where they beat
-// the VALU GEMV (which then spends four dot products per weight pair): lm_kernel for W6 and
-// for W4 with K a multiple of 256 (see use_lm), mfma_kernel for the rest.
+// The matrix cores serve M >= 5, and M = 4 for W6/W8 rows of 4096 or more (and larger W4),
+// where they beat the VALU GEMV (which then spends four dot products per weight pair):
+// lm_kernel for W6 and for W4 with K a multiple of 256 (see use_lm), mfma_kernel for the rest.
 bool use_mfma(int fmt, int64_t M, int64_t N) {
   if (M > GEMV_MAX_M) return true;
   return M == GEMV_MAX_M && (fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W8) && N >= 4096;
@@ -954,15 +984,22 @@ bool use_mfma(int fmt, int64_t M, int64_t N) {
 
 // RB: as many row blocks per wave as keeps >= 256 row groups (W4 and F16, whose decode
 // is heavier per byte, take one or two). WK: doubled up to 8 until ~2048 waves.
-MfmaPlan plan_mfma(int fmt, int64_t N, int64_t K) {
+int mfma_rows(int fmt, int64_t N) {
+  if (fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W8) return N >= 16384 ? 4 : N >= 8192 ? 2 : 1;
+  return fmt == WQ_FMT_F16 && N >= 8192 ? 2 : 1;
+}
+
+int mfma_waves_for(int64_t N, int64_t K, int RB) {
   const int64_t T = (K / 32 + 3) / 4;
-  int RB = 1;
-  if (fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W8) RB = N >= 16384 ? 4 : N >= 8192 ? 2 : 1;
-  else if (fmt == WQ_FMT_F16) RB = N >= 8192 ? 2 : 1;
   const int64_t groups = (N + 16 * RB - 1) / (16 * RB);
   int WK = 1;
   while (WK < MFMA_MAX_WAVES && WK < T && groups * WK < 2048) WK *= 2;
-  return {RB, WK, static_cast<int>(groups)};
+  return WK;
+}
+
+MfmaPlan plan_mfma(int fmt, int64_t N, int64_t K) {
+  const int RB = mfma_rows(fmt, N);
+  return {RB, mfma_waves_for(N, K, RB), static_cast<int>((N + 16 * RB - 1) / (16 * RB))};
 }
 
 struct LmPlan {
@@ -973,20 +1010,27 @@ struct LmPlan {
 
 // The LDS-staged kernel serves W6 and W4 wherever the matrix cores run for them (W4 only when
 // K is a multiple of 256, so that a lane's 8 groups of metadata are one aligned 16-byte load),
-// and W4 at M = 4 from N*K = 2^26 on, where it beats the VALU GEMV.
+// and W4 at M = 4 from N*K = 2^24 on, where it beats the VALU GEMV.
 bool use_lm(int fmt, int64_t M, int64_t N, int64_t K) {
   if (fmt == WQ_FMT_W6E3M2) return use_mfma(fmt, M, N);
   if (fmt != WQ_FMT_W4G32 || K % 256) return false;
-  return M > GEMV_MAX_M || (M == GEMV_MAX_M && N * K >= (int64_t(1) << 26));
+  return M > GEMV_MAX_M || (M == GEMV_MAX_M && N * K >= (int64_t(1) << 24));
 }
 
 // Two row blocks per wave from 8192 rows; WK doubled until ~1024 waves.
-LmPlan plan_lm(int64_t N, int64_t K) {
-  const int RB = N >= 8192 ? 2 : 1;
+int lm_rows(int64_t N) { return N >= 8192 ? 2 : 1; }
+
+int lm_waves_for(int64_t N, int64_t K, int RB) {
   const int64_t H = (K / 32 + 31) / 32;
   const int64_t groups = (N + 16 * RB - 1) / (16 * RB);
   int WK = 1;
   while (WK < LM_WAVES && WK < H && groups * WK < 1024) WK *= 2;
+  return WK;
+}
+
+LmPlan plan_lm(int64_t N, int64_t K) {
+  const int RB = lm_rows(N), WK = lm_waves_for(N, K, RB);
+  const int64_t groups = (N + 16 * RB - 1) / (16 * RB);
   const int R = LM_WAVES / WK;
   return {RB, WK, static_cast<int>((groups + R - 1) / R)};
 }
@@ -1055,18 +1099,43 @@ hipError_t launch_grouped_fmt(const GemvGroup& g, int M, int B, int block_waves,
   }
 }
 
-int grouped_rows_per_wave(int fmt, const wq_linear_item* items, int count) {
-  int big = 0;
-  for (int i = 1; i < count; ++i)
-    if (items[i].N * items[i].K > items[big].N * items[big].K) big = i;
-  return gemv_rows_per_wave(fmt, items[big].N, items[big].K);
-}
-
 // Launch order of a grouped call: the items with the longest rows (most chunks per wave)
 // first, so that the waves that finish last are the short ones. Ties keep the caller's order.
 void grouped_order(const wq_linear_item* items, int count, int (&order)[MAX_GROUP]) {
   for (int i = 0; i < count; ++i) order[i] = i;
   std::stable_sort(order, order + count, [&](int a, int b) { return items[a].K > items[b].K; });
+}
+
+// Which kernel family runs a linear of M <= 16 rows, and which runs a grouped call: the
+// largest item's (by N*K), except that W4 on the LDS path needs every K a multiple of 256
+// and otherwise takes the fragment-load kernel. Every family computes any shape correctly.
+enum Family { FAM_GEMV, FAM_LM, FAM_MFMA };
+
+Family family_of(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (use_lm(fmt, M, N, K)) return FAM_LM;
+  return use_mfma(fmt, M, N) ? FAM_MFMA : FAM_GEMV;
+}
+
+int largest_item(const int64_t* N, const int64_t* K, int count) {
+  int big = 0;
+  for (int i = 1; i < count; ++i)
+    if (N[i] * K[i] > N[big] * K[big]) big = i;
+  return big;
+}
+
+Family group_family(int fmt, int64_t M, const int64_t* N, const int64_t* K, int count) {
+  const int big = largest_item(N, K, count);
+  Family f = family_of(fmt, M, N[big], K[big]);
+  if (f == FAM_LM && fmt == WQ_FMT_W4G32)
+    for (int i = 0; i < count; ++i)
+      if (K[i] % 256) f = FAM_MFMA;
+  return f;
+}
+
+// rows per wave (GEMV) or 16-row blocks per wave (matrix cores) of a grouped launch
+int group_rows(Family f, int fmt, const int64_t* N, const int64_t* K, int count) {
+  const int big = largest_item(N, K, count);
+  return f == FAM_GEMV ? gemv_rows_per_wave(fmt, N[big], K[big]) : f == FAM_LM ? lm_rows(N[big]) : mfma_rows(fmt, N[big]);
 }
 
 int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, const uint16_t* z, const uint16_t* y,
@@ -1079,6 +1148,25 @@ int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, cons
   if (N > INT32_MAX / 2 || K > (int64_t(1) << 26) || (N * (K / 32)) > INT32_MAX) return WQ_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (sc && !aligned16(sc)) || (z && !aligned16(z))) return WQ_ERR_ALIGN;
   return WQ_OK;
+}
+
+template <int FMT>
+hipError_t launch_grouped_mc(Family f, const GemvGroup& g, int M, int RB, int block_waves, int grid, hipStream_t s) {
+  if (f == FAM_LM) {
+    if constexpr (FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W6E3M2) {
+      const size_t shm = (size_t)LM_WAVES * RB * lm_block<FMT>();
+      if (RB == 2) hipLaunchKernelGGL((lm_grouped_kernel<FMT, 2>), dim3(grid), dim3(64 * LM_WAVES), shm, s, g, M);
+      else hipLaunchKernelGGL((lm_grouped_kernel<FMT, 1>), dim3(grid), dim3(64 * LM_WAVES), shm, s, g, M);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (RB) {
+    case 4: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 4>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
+    case 2: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 2>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
+    default: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 1>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -1139,9 +1227,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
     const int st = check_linear_args(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt);
     if (st != WQ_OK) return st;
   }
-  bool mfma = false;
-  for (int i = 0; i < count; ++i) mfma = mfma || use_mfma(fmt, M, items[i].N) || use_lm(fmt, M, items[i].N, items[i].K);
-  if (mfma) {   // the MFMA path has no grouped form: one launch per item
+  if (M > MFMA_M) {   // several 16-row slabs: one wq_linear per item
     for (int i = 0; i < count; ++i) {
       const wq_linear_item& it = items[i];
       const int st = wq_linear(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt, stream);
@@ -1149,16 +1235,24 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
     }
     return WQ_OK;
   }
-  // one rows-per-wave B for the whole launch: the one the largest item's plan picks (the
-  // small items alone would pick fewer rows per wave to get enough waves, which the
-  // launch has anyway); each item keeps the K split its own plan gives for that B
-  const int B = grouped_rows_per_wave(fmt, items, count);
+  int64_t Ns[MAX_GROUP], Ks[MAX_GROUP];
+  for (int i = 0; i < count; ++i) { Ns[i] = items[i].N; Ks[i] = items[i].K; }
+  // one family and one rows-per-wave (B or RB) for the whole launch: the largest item's (the
+  // small items alone would pick fewer rows per wave to get enough waves, which the launch
+  // has anyway); each item keeps the K split its own plan gives for that B / RB
+  const Family fam = group_family(fmt, M, Ns, Ks, count);
+  const int B = group_rows(fam, fmt, Ns, Ks, count);
   int order[MAX_GROUP];
   grouped_order(items, count, order);
   GemvGroup g = {};
   g.count = count;
-  for (int i = 0; i < count; ++i) g.WK[i] = gemv_waves_for(fmt, items[order[i]].N, items[order[i]].K, B);
-  const int block_waves = GEMV_WAVES;   // every split is 1, 2 or 4
+  int block_waves = fam == FAM_GEMV ? GEMV_WAVES : fam == FAM_LM ? LM_WAVES : 1;
+  for (int i = 0; i < count; ++i) {
+    const int64_t n = items[order[i]].N, k = items[order[i]].K;
+    g.WK[i] = fam == FAM_GEMV ? gemv_waves_for(fmt, n, k, B) : fam == FAM_LM ? lm_waves_for(n, k, B) : mfma_waves_for(n, k, B);
+    if (fam == FAM_MFMA) block_waves = std::max(block_waves, g.WK[i]);   // powers of two up to MFMA_MAX_WAVES
+  }
+  const int rows_per_block = fam == FAM_GEMV ? B : 16 * B;
   int grid = 0;
   for (int i = 0; i < count; ++i) {
     const wq_linear_item& it = items[order[i]];
@@ -1171,16 +1265,25 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
     g.y[i] = it.y;
     g.N[i] = static_cast<int>(it.N);
     g.K[i] = static_cast<int>(it.K);
-    grid += static_cast<int>(((it.N + B - 1) / B + R - 1) / R);
+    grid += static_cast<int>(((it.N + rows_per_block - 1) / rows_per_block + R - 1) / R);
   }
   g.first_block[count] = grid;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  switch (fmt) {
-    case WQ_FMT_W8: e = launch_grouped_fmt<WQ_FMT_W8>(g, (int)M, B, block_waves, grid, s); break;
-    case WQ_FMT_W4G32: e = launch_grouped_fmt<WQ_FMT_W4G32>(g, (int)M, B, block_waves, grid, s); break;
-    case WQ_FMT_W6E3M2: e = launch_grouped_fmt<WQ_FMT_W6E3M2>(g, (int)M, B, block_waves, grid, s); break;
-    default: e = launch_grouped_fmt<WQ_FMT_F16>(g, (int)M, B, block_waves, grid, s); break;
+  if (fam == FAM_GEMV) {
+    switch (fmt) {
+      case WQ_FMT_W8: e = launch_grouped_fmt<WQ_FMT_W8>(g, (int)M, B, block_waves, grid, s); break;
+      case WQ_FMT_W4G32: e = launch_grouped_fmt<WQ_FMT_W4G32>(g, (int)M, B, block_waves, grid, s); break;
+      case WQ_FMT_W6E3M2: e = launch_grouped_fmt<WQ_FMT_W6E3M2>(g, (int)M, B, block_waves, grid, s); break;
+      default: e = launch_grouped_fmt<WQ_FMT_F16>(g, (int)M, B, block_waves, grid, s); break;
+    }
+  } else {
+    switch (fmt) {
+      case WQ_FMT_W8: e = launch_grouped_mc<WQ_FMT_W8>(fam, g, (int)M, B, block_waves, grid, s); break;
+      case WQ_FMT_W4G32: e = launch_grouped_mc<WQ_FMT_W4G32>(fam, g, (int)M, B, block_waves, grid, s); break;
+      case WQ_FMT_W6E3M2: e = launch_grouped_mc<WQ_FMT_W6E3M2>(fam, g, (int)M, B, block_waves, grid, s); break;
+      default: e = launch_grouped_mc<WQ_FMT_F16>(fam, g, (int)M, B, block_waves, grid, s); break;
+    }
   }
   return e == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
 }
@@ -1203,16 +1306,14 @@ const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
 const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, const int64_t* K, int count) {
   static thread_local char buf[96];
   if (!valid_fmt(fmt) || M < 1 || !N || !K || count < 1 || count > MAX_GROUP) return "";
-  const int64_t mm = M < MFMA_M ? M : MFMA_M;
-  int big = 0;
-  bool mfma = false;
-  for (int i = 0; i < count; ++i) {
+  for (int i = 0; i < count; ++i)
     if (N[i] < 1 || K[i] < 32 || K[i] % 32) return "";
-    if (N[i] * K[i] > N[big] * K[big]) big = i;
-    mfma = mfma || use_mfma(fmt, mm, N[i]) || use_lm(fmt, mm, N[i], K[i]);
-  }
-  if (mfma) return wq_linear_kernel_name(fmt, M, N[big], K[big]);   // separate launches: the largest item's
-  snprintf(buf, sizeof(buf), "gemv_grouped_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), gemv_rows_per_wave(fmt, N[big], K[big]));
+  const int big = largest_item(N, K, count);
+  if (M > MFMA_M) return wq_linear_kernel_name(fmt, M, N[big], K[big]);   // separate launches: the largest item's
+  const Family fam = group_family(fmt, M, N, K, count);
+  const int B = group_rows(fam, fmt, N, K, count);
+  if (fam == FAM_GEMV) snprintf(buf, sizeof(buf), "gemv_grouped_kernel<%d, %d, %d>", fmt, static_cast<int>(M), B);
+  else snprintf(buf, sizeof(buf), "%s_grouped_kernel<%d, %d>", fam == FAM_LM ? "lm" : "mfma", fmt, B);
   return buf;
 }
 
