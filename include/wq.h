@@ -110,8 +110,9 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
 /* On the device: y[M,N] = x[M,K] . dequant(packed_w)[N,K]^T with fp16 x and y (row-major,
  * row strides K and N) and fp32 accumulation; the one fused kernel reads every packed
  * byte once and never writes dequantized weights to memory. All pointers are device
- * pointers, 16-byte aligned; zeros only for W4 (else may be NULL). M of any size; M up to
- * 16 is one launch, larger M runs in slabs of 16 rows. y must not overlap the inputs.
+ * pointers, 16-byte aligned; zeros only for W4 (else may be NULL). M of any size; one launch
+ * takes up to 64 rows of x for W6 and for W4 with K a multiple of 256, up to 16 otherwise,
+ * and larger M runs as several launches. y must not overlap the inputs.
  * Asynchronous on stream. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT, WQ_ERR_ALIGN,
  * WQ_ERR_DEVICE. */
 int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros, uint16_t* y,
@@ -133,8 +134,8 @@ typedef struct {
  * instead of count means the GPU ramps up and drains once; in a decode step this fits
  * q/k/v or gate/up, and any set of linears whose inputs are ready. Items must not write
  * into one another's inputs. The launch uses the kernel wq_linear would use for the
- * largest item (by N*K) for every item. M above 16: every item runs as its own wq_linear
- * call instead. Errors: as wq_linear, per item, all checked before any launch; WQ_ERR_ARG
+ * largest item (by N*K) for every item. When M is more than that kernel takes in one
+ * launch (see wq_linear), every item runs as its own wq_linear call instead. Errors: as wq_linear, per item, all checked before any launch; WQ_ERR_ARG
  * also for count outside 0..16 or items == NULL. */
 int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt, void* stream);
 
@@ -142,8 +143,8 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
  * arguments are invalid. Host only; static storage. */
 const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K);
 
-/* Name of the kernel wq_linear_grouped launches for count items of sizes N[i] x K[i] (above
- * 16 rows, with separate launches: the largest item's kernel), or "". */
+/* Name of the kernel wq_linear_grouped launches for count items of sizes N[i] x K[i] (with
+ * separate launches: the largest item's kernel), or "". */
 const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, const int64_t* K, int count);
 
 #ifdef __cplusplus

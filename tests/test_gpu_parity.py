@@ -83,7 +83,9 @@ def test_linear_every_m(fmt, m):
                                    # K a multiple of 256 (W4 through LDS): a ragged last 32-unit stage
                                    # (2304 = 72 units), ragged 16-row blocks, two blocks per wave from
                                    # 8192 rows, a single stage (K = 256)
-                                   (37, 2304, 5), (37, 2304, 16), (8200, 2304, 8), (40, 11008, 13), (48, 256, 6)])
+                                   (37, 2304, 5), (37, 2304, 16), (8200, 2304, 8), (40, 11008, 13), (48, 256, 6),
+                                   # 17..64 rows of x in one launch (2 or 4 tiles of 16), and slabs beyond
+                                   (130, 8192, 64), (37, 2304, 33), (8200, 256, 50), (40, 4352, 17), (33, 512, 130)])
 def test_linear_shapes(fmt, n, k, m):
     w = _weights(n, k, 3 * n + k)
     _, x = inputs.small_case(2000 + n + m, 1, k, m)
@@ -185,7 +187,7 @@ GROUP_SETS = {
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
-@pytest.mark.parametrize("m", [1, 3, 4, 7, 16, 20])
+@pytest.mark.parametrize("m", [1, 3, 4, 7, 16, 20, 40, 64, 70])
 @pytest.mark.parametrize("set_name", sorted(GROUP_SETS))
 def test_grouped_matches_separate_calls(fmt, m, set_name):
     torch = torch_cuda()

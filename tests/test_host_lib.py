@@ -208,12 +208,12 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert L.wq_linear(a, a, a, a, a, 1, 64, (1 << 26) + 32, 1, None) == -2    # K above 2^26
     assert L.wq_linear(a, a, a, a, a, 1, 1 << 22, 1 << 20, 1, None) == -2       # N*K/32 above int32
     assert wq.wq_linear_kernel_name(2, 1, 4096, 4096).startswith("gemv_kernel")
-    assert wq.wq_linear_kernel_name(3, 16, 4096, 4096) == "lm_kernel<3, 1>"
-    assert wq.wq_linear_kernel_name(3, 16, 8192, 4096) == "lm_kernel<3, 2>"
+    assert wq.wq_linear_kernel_name(3, 16, 4096, 4096) == "lm_kernel<3, 1, 1>"
+    assert wq.wq_linear_kernel_name(3, 16, 8192, 4096) == "lm_kernel<3, 2, 1>"
     assert wq.wq_linear_kernel_name(1, 16, 4096, 4096).startswith("mfma_kernel")
     assert wq.wq_linear_kernel_name(0, 16, 4096, 4096).startswith("mfma_kernel")
     # W4 on the matrix cores: through LDS when K is a multiple of 256, else fragment loads
-    assert wq.wq_linear_kernel_name(2, 8, 4096, 4096) == "lm_kernel<2, 1>"
+    assert wq.wq_linear_kernel_name(2, 8, 4096, 4096) == "lm_kernel<2, 1, 1>"
     assert wq.wq_linear_kernel_name(2, 8, 4096, 4128) == "mfma_kernel<2, 1>"
     assert wq.wq_linear_kernel_name(3, 3, 4096, 4096).startswith("gemv_kernel")
     # M = 4: the matrix cores for W6/W8 with N >= 4096 and for W4 from N*K = 2^24, the GEMV otherwise
@@ -221,15 +221,23 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_kernel_name(1, 4, 8192, 4096).startswith("mfma_kernel")
     assert wq.wq_linear_kernel_name(3, 4, 1024, 4096).startswith("gemv_kernel")
     assert wq.wq_linear_kernel_name(2, 4, 2048, 4096).startswith("gemv_kernel")
-    assert wq.wq_linear_kernel_name(2, 4, 4096, 4096) == "lm_kernel<2, 1>"
-    assert wq.wq_linear_kernel_name(2, 4, 8192, 8192) == "lm_kernel<2, 2>"
+    assert wq.wq_linear_kernel_name(2, 4, 4096, 4096) == "lm_kernel<2, 1, 1>"
+    assert wq.wq_linear_kernel_name(2, 4, 8192, 8192) == "lm_kernel<2, 2, 1>"
     assert wq.wq_linear_kernel_name(3, 16, 4096, 40) == ""
     # grouped: the GEMV takes its rows per wave from the largest item
     assert wq.wq_linear_grouped_kernel_name(3, 1, [(8192, 8192), (1024, 8192)]) == "gemv_grouped_kernel<3, 1, 4>"
     # ... and the matrix-core kernels take their family and row blocks from it too
-    assert wq.wq_linear_grouped_kernel_name(3, 8, [(1024, 8192), (8192, 8192)]) == "lm_grouped_kernel<3, 2>"
-    assert wq.wq_linear_grouped_kernel_name(2, 4, [(8192, 8192), (1024, 8192)]) == "lm_grouped_kernel<2, 2>"
+    assert wq.wq_linear_grouped_kernel_name(3, 8, [(1024, 8192), (8192, 8192)]) == "lm_grouped_kernel<3, 2, 1>"
+    assert wq.wq_linear_grouped_kernel_name(2, 4, [(8192, 8192), (1024, 8192)]) == "lm_grouped_kernel<2, 2, 1>"
     assert wq.wq_linear_grouped_kernel_name(2, 8, [(8192, 8192), (1024, 8224)]) == "mfma_grouped_kernel<2, 1>"
     assert wq.wq_linear_grouped_kernel_name(1, 16, [(4096, 4096), (16384, 4096)]) == "mfma_grouped_kernel<1, 4>"
-    # above 16 rows of x: one wq_linear per item (the largest item's kernel)
-    assert wq.wq_linear_grouped_kernel_name(3, 20, [(1024, 8192), (8192, 8192)]) == "lm_kernel<3, 2>"
+    # 17..64 rows of x: the LDS-staged kernel takes 2 or 4 tiles of 16 rows in one launch
+    # (W4 when K is a multiple of 256); the others, and more than 64 rows, run in slabs
+    assert wq.wq_linear_kernel_name(3, 20, 8192, 8192) == "lm_kernel<3, 2, 2>"
+    assert wq.wq_linear_kernel_name(2, 64, 4096, 4096) == "lm_kernel<2, 1, 4>"
+    assert wq.wq_linear_kernel_name(2, 64, 4096, 4128) == "mfma_kernel<2, 1>"
+    assert wq.wq_linear_kernel_name(1, 40, 4096, 4096) == "mfma_kernel<1, 1>"
+    assert wq.wq_linear_kernel_name(3, 100, 4096, 4096) == "lm_kernel<3, 1, 4>"
+    assert wq.wq_linear_grouped_kernel_name(3, 20, [(1024, 8192), (8192, 8192)]) == "lm_grouped_kernel<3, 2, 2>"
+    assert wq.wq_linear_grouped_kernel_name(3, 65, [(1024, 8192), (8192, 8192)]) == "lm_kernel<3, 2, 4>"
+    assert wq.wq_linear_grouped_kernel_name(1, 20, [(1024, 8192), (8192, 8192)]) == "mfma_kernel<1, 2>"

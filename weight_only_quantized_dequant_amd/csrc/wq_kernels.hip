@@ -667,7 +667,8 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_grouped_kernel(const
 // the ring at 2 so that its two-block kernel fits 256 VGPRs: two waves per SIMD).
 template <int FMT> constexpr int lm_block() { return FMT == WQ_FMT_W4G32 ? 16 * 512 : 16 * 512 + 16 * 256; }
 template <int FMT> constexpr int lm_loads() { return FMT == WQ_FMT_W4G32 ? 8 : 12; }
-template <int FMT> constexpr int lm_xring() { return FMT == WQ_FMT_W4G32 ? 2 : 4; }
+template <int FMT, int MT> constexpr int lm_xring() { return FMT == WQ_FMT_W4G32 || MT > 1 ? 2 : 4; }
+constexpr int LM_MAX_MT = 4;   // 16-row tiles of x per launch (M up to 64 reads the weights once)
 constexpr int LM_WAVES = 4;   // waves per workgroup
 
 template <int FMT, int RB>
@@ -753,7 +754,7 @@ __device__ __forceinline__ uint16_t half_of(const uint4& v, int j) {   // 16-bit
 
 // A workgroup of LM_WAVES waves holds R = LM_WAVES / WK row groups of 16 RB rows; the WK
 // waves of a group take the stages h = kw, kw + WK, ...
-template <int FMT, int RB>
+template <int FMT, int RB, int MT>
 __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                         const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
                                         uint16_t* __restrict__ y, int M, int N, int K, int block, int WK) {
@@ -767,23 +768,27 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
   const int n0 = (block * R + sub) * 16 * RB;
   const int NI = kw < H ? (H - kw + WK - 1) / WK : 0;
   uint8_t* lds = reinterpret_cast<uint8_t*>(lm_lds) + wave_id * RB * lm_block<FMT>();
-  const bool xrow = nl < M;
-  f4 acc[RB];
+  f4 acc[RB][MT];
 #pragma unroll
-  for (int r = 0; r < RB; ++r) acc[r] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[r][mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   LmStage<FMT, RB> st;
   constexpr int MS = FMT == WQ_FMT_W4G32 ? RB : 1;
   uint4 cs[MS], cz[MS];   // W4: the metadata of the stage in LDS
-  constexpr int XR = lm_xring<FMT>();
-  h8 xr[XR][4];
-  auto xload = [&](int t) {   // x[m = nl][unit 32h + 8q + j] of K tile t = 8i + j
+  constexpr int XR = lm_xring<FMT, MT>();
+  h8 xr[XR][MT][4];
+  auto xload = [&](int t) {   // x[m = 16 mt + nl][unit 32h + 8q + j] of K tile t = 8i + j
     const int h = kw + (t >> 3) * WK, j = t & 7;
     const uint32_t u = (uint32_t)min(32 * h + 8 * q + j, U - 1);
-    const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) +
-                                                     (uint32_t)min(nl, M - 1) * (uint32_t)K * 2u + 64u * u);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) xr[t % XR][k] = __builtin_bit_cast(h8, xp[k]);
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) +
+                                                       (uint32_t)min(16 * mt + nl, M - 1) * (uint32_t)K * 2u + 64u * u);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xr[t % XR][mt][k] = __builtin_bit_cast(h8, xp[k]);
+    }
   };
   auto park = [&]() {   // the loaded stage -> LDS (and W4 metadata -> cs, cz)
     lm_store<FMT, RB>(st, lds, lane);
@@ -807,7 +812,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
       const int t = 8 * i + j;
       if (j + XR - 1 < 8 || i + 1 < NI) xload(t + XR - 1);
       const int u = 8 * q + j;   // unit within the stage
-      const bool ok = xrow && (32 * h + u < U);
+      const bool uok = 32 * h + u < U;
       const h8 zero8 = {};
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
@@ -833,7 +838,11 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
           h8 b;
 #pragma unroll
           for (int e = 0; e < 4; ++e) { b[2 * e] = wv[4 * k + e][0]; b[2 * e + 1] = wv[4 * k + e][1]; }
-          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ok ? xr[t % XR][k] : zero8, b, acc[r], 0, 0, 0);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const bool ok = uok && 16 * mt + nl < M;
+            acc[r][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ok ? xr[t % XR][mt][k] : zero8, b, acc[r][mt], 0, 0, 0);
+          }
         }
       }
     }
@@ -841,44 +850,51 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
   }
 
   // WK partials through LDS (every wave is done with its region after the barrier), fixed
-  // order; D[m][n] sits in lane (n + 16*(m/4)), register m%4
+  // order; D[m][n] of x tile mt sits in lane (n + 16*(m/4)), register m%4
   __syncthreads();
   f4* red = reinterpret_cast<f4*>(lm_lds);
 #pragma unroll
-  for (int r = 0; r < RB; ++r) red[(wave_id * RB + r) * 64 + lane] = acc[r];
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[((wave_id * RB + r) * MT + mt) * 64 + lane] = acc[r][mt];
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     if (r % WK != kw) continue;
-    f4 t = red[((sub * WK) * RB + r) * 64 + lane];
-    for (int k = 1; k < WK; ++k) t += red[((sub * WK + k) * RB + r) * 64 + lane];
     const int n = n0 + 16 * r + nl;
-    if (n < N) {
-      const float sc = FMT == WQ_FMT_W6E3M2 ? f16_to_f32(scales[n]) : 1.0f;
+    const float sc = FMT == WQ_FMT_W6E3M2 && n < N ? f16_to_f32(scales[n]) : 1.0f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int m = 4 * q + k;
-        if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(t[k] * sc));
+    for (int mt = 0; mt < MT; ++mt) {
+      f4 t = red[(((sub * WK) * RB + r) * MT + mt) * 64 + lane];
+      for (int k = 1; k < WK; ++k) t += red[(((sub * WK + k) * RB + r) * MT + mt) * 64 + lane];
+      if (n < N) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int m = 16 * mt + 4 * q + k;
+          if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(t[k] * sc));
+        }
       }
     }
   }
 }
 
-template <int FMT, int RB>
+// MT 16-row tiles of x (M <= 16 MT) share each decoded weight fragment, so the weights are
+// read once for up to 64 rows of x.
+template <int FMT, int RB, int MT>
 __global__ __launch_bounds__(64 * LM_WAVES) void lm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
                                                           int M, int N, int K, int WK) {
-  lm_body<FMT, RB>(x, w, scales, zeros, y, M, N, K, blockIdx.x, WK);
+  lm_body<FMT, RB, MT>(x, w, scales, zeros, y, M, N, K, blockIdx.x, WK);
 }
 
 // Several linears in a single launch (see GemvGroup), each with its own K split.
-template <int FMT, int RB>
+template <int FMT, int RB, int MT>
 __global__ __launch_bounds__(64 * LM_WAVES) void lm_grouped_kernel(const GemvGroup g, int M) {
   int j = 0;
   while (j + 1 < g.count && (int)blockIdx.x >= g.first_block[j + 1]) ++j;   // workgroup-uniform
-  lm_body<FMT, RB>(g.x[j], g.w[j], g.scales[j], g.zeros[j], g.y[j], M, g.N[j], g.K[j], blockIdx.x - g.first_block[j],
-                   g.WK[j]);
+  lm_body<FMT, RB, MT>(g.x[j], g.w[j], g.scales[j], g.zeros[j], g.y[j], M, g.N[j], g.K[j],
+                       blockIdx.x - g.first_block[j], g.WK[j]);
 }
 
 // ---------------------------------------------------------------- dequant
@@ -1035,6 +1051,15 @@ LmPlan plan_lm(int64_t N, int64_t K) {
   return {RB, WK, static_cast<int>((groups + R - 1) / R)};
 }
 
+// 16-row tiles of x one LDS-staged launch takes (1, 2 or 4)
+int lm_tiles(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
+
+// Rows of x per launch: 64 where the LDS-staged kernel serves the shape (W6; W4 with K a
+// multiple of 256), else 16.
+int64_t slab_rows(int fmt, int64_t K) {
+  return fmt == WQ_FMT_W6E3M2 || (fmt == WQ_FMT_W4G32 && K % 256 == 0) ? 16 * LM_MAX_MT : MFMA_M;
+}
+
 template <int FMT, int M>
 hipError_t launch_gemv_m(const GemvPlan& p, hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
                          const uint16_t* z, uint16_t* y, int N, int K) {
@@ -1047,18 +1072,41 @@ hipError_t launch_gemv_m(const GemvPlan& p, hipStream_t s, const uint16_t* x, co
   return hipGetLastError();
 }
 
+// The LDS-staged kernel for (RB, MT) as template arguments: one launch, or (GemvGroup) a
+// grouped one.
+template <int FMT, int RB, int MT>
+void lm_launch(dim3 grid, size_t shm, hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
+               const uint16_t* z, uint16_t* y, int M, int N, int K, int WK, const GemvGroup* g) {
+  if (g) hipLaunchKernelGGL((lm_grouped_kernel<FMT, RB, MT>), grid, dim3(64 * LM_WAVES), shm, s, *g, M);
+  else hipLaunchKernelGGL((lm_kernel<FMT, RB, MT>), grid, dim3(64 * LM_WAVES), shm, s, x, w, sc, z, y, M, N, K, WK);
+}
+
+template <int FMT>
+hipError_t launch_lm(int RB, int M, dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
+                     const uint16_t* z, uint16_t* y, int N, int K, int WK, const GemvGroup* g) {
+  if constexpr (FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W6E3M2) {
+    const size_t shm = (size_t)LM_WAVES * RB * lm_block<FMT>();
+    const int MT = lm_tiles(M);
+    if (RB == 2) {
+      if (MT == 1) lm_launch<FMT, 2, 1>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
+      else if (MT == 2) lm_launch<FMT, 2, 2>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
+      else lm_launch<FMT, 2, 4>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
+    } else {
+      if (MT == 1) lm_launch<FMT, 1, 1>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
+      else if (MT == 2) lm_launch<FMT, 1, 2>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
+      else lm_launch<FMT, 1, 4>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
+    }
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int FMT>
 hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
                              uint16_t* y, int M, int N, int K) {
-  if constexpr (FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W6E3M2) {
-    if (use_lm(FMT, M, N, K)) {
-      const LmPlan p = plan_lm(N, K);
-      const dim3 grid(p.grid), block(64 * LM_WAVES);
-      const size_t shm = (size_t)LM_WAVES * p.RB * lm_block<FMT>();
-      if (p.RB == 2) hipLaunchKernelGGL((lm_kernel<FMT, 2>), grid, block, shm, s, x, w, sc, z, y, M, N, K, p.WK);
-      else hipLaunchKernelGGL((lm_kernel<FMT, 1>), grid, block, shm, s, x, w, sc, z, y, M, N, K, p.WK);
-      return hipGetLastError();
-    }
+  if (use_lm(FMT, M, N, K)) {
+    const LmPlan p = plan_lm(N, K);
+    return launch_lm<FMT>(p.RB, M, dim3(p.grid), s, x, w, sc, z, y, N, K, p.WK, nullptr);
   }
   if (!use_mfma(FMT, M, N)) {
     const GemvPlan p = plan_gemv(FMT, N, K);
@@ -1152,15 +1200,7 @@ int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, cons
 
 template <int FMT>
 hipError_t launch_grouped_mc(Family f, const GemvGroup& g, int M, int RB, int block_waves, int grid, hipStream_t s) {
-  if (f == FAM_LM) {
-    if constexpr (FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W6E3M2) {
-      const size_t shm = (size_t)LM_WAVES * RB * lm_block<FMT>();
-      if (RB == 2) hipLaunchKernelGGL((lm_grouped_kernel<FMT, 2>), dim3(grid), dim3(64 * LM_WAVES), shm, s, g, M);
-      else hipLaunchKernelGGL((lm_grouped_kernel<FMT, 1>), dim3(grid), dim3(64 * LM_WAVES), shm, s, g, M);
-      return hipGetLastError();
-    }
-    return hipErrorInvalidValue;
-  }
+  if (f == FAM_LM) return launch_lm<FMT>(RB, M, dim3(grid), s, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, &g);
   switch (RB) {
     case 4: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 4>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
     case 2: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 2>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
@@ -1179,8 +1219,9 @@ int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, c
   if (st != WQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* w = static_cast<const uint8_t*>(packed_w);
-  for (int64_t m0 = 0; m0 < M; m0 += MFMA_M) {
-    const int mm = static_cast<int>(M - m0 < MFMA_M ? M - m0 : MFMA_M);
+  const int64_t slab = slab_rows(fmt, K);
+  for (int64_t m0 = 0; m0 < M; m0 += slab) {
+    const int mm = static_cast<int>(M - m0 < slab ? M - m0 : slab);
     const uint16_t* xs = x + m0 * K;
     uint16_t* ys = y + m0 * N;
     hipError_t e = hipSuccess;
@@ -1227,7 +1268,13 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
     const int st = check_linear_args(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt);
     if (st != WQ_OK) return st;
   }
-  if (M > MFMA_M) {   // several 16-row slabs: one wq_linear per item
+  int64_t Ns[MAX_GROUP], Ks[MAX_GROUP];
+  for (int i = 0; i < count; ++i) { Ns[i] = items[i].N; Ks[i] = items[i].K; }
+  // one family and one rows-per-wave (B or RB) for the whole launch: the largest item's (the
+  // small items alone would pick fewer rows per wave to get enough waves, which the launch
+  // has anyway); each item keeps the K split its own plan gives for that B / RB
+  const Family fam = group_family(fmt, M, Ns, Ks, count);
+  if (M > MFMA_M && (fam != FAM_LM || M > 16 * LM_MAX_MT)) {   // several slabs: one wq_linear per item
     for (int i = 0; i < count; ++i) {
       const wq_linear_item& it = items[i];
       const int st = wq_linear(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt, stream);
@@ -1235,12 +1282,6 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
     }
     return WQ_OK;
   }
-  int64_t Ns[MAX_GROUP], Ks[MAX_GROUP];
-  for (int i = 0; i < count; ++i) { Ns[i] = items[i].N; Ks[i] = items[i].K; }
-  // one family and one rows-per-wave (B or RB) for the whole launch: the largest item's (the
-  // small items alone would pick fewer rows per wave to get enough waves, which the launch
-  // has anyway); each item keeps the K split its own plan gives for that B / RB
-  const Family fam = group_family(fmt, M, Ns, Ks, count);
   const int B = group_rows(fam, fmt, Ns, Ks, count);
   int order[MAX_GROUP];
   grouped_order(items, count, order);
@@ -1291,9 +1332,9 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
 const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   static thread_local char buf[96];
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 32 || K % 32) return "";
-  const int64_t mm = M < MFMA_M ? M : MFMA_M;
+  const int64_t mm = M < slab_rows(fmt, K) ? M : slab_rows(fmt, K);   // the first launch's rows
   if (use_lm(fmt, mm, N, K)) {
-    snprintf(buf, sizeof(buf), "lm_kernel<%d, %d>", fmt, plan_lm(N, K).RB);
+    snprintf(buf, sizeof(buf), "lm_kernel<%d, %d, %d>", fmt, plan_lm(N, K).RB, lm_tiles(mm));
   } else if (!use_mfma(fmt, mm, N)) {
     const GemvPlan p = plan_gemv(fmt, N, K);
     snprintf(buf, sizeof(buf), "gemv_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), p.B);
@@ -1309,11 +1350,13 @@ const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, 
   for (int i = 0; i < count; ++i)
     if (N[i] < 1 || K[i] < 32 || K[i] % 32) return "";
   const int big = largest_item(N, K, count);
-  if (M > MFMA_M) return wq_linear_kernel_name(fmt, M, N[big], K[big]);   // separate launches: the largest item's
   const Family fam = group_family(fmt, M, N, K, count);
+  if (M > MFMA_M && (fam != FAM_LM || M > 16 * LM_MAX_MT))
+    return wq_linear_kernel_name(fmt, M, N[big], K[big]);   // separate launches: the largest item's
   const int B = group_rows(fam, fmt, N, K, count);
   if (fam == FAM_GEMV) snprintf(buf, sizeof(buf), "gemv_grouped_kernel<%d, %d, %d>", fmt, static_cast<int>(M), B);
-  else snprintf(buf, sizeof(buf), "%s_grouped_kernel<%d, %d>", fam == FAM_LM ? "lm" : "mfma", fmt, B);
+  else if (fam == FAM_LM) snprintf(buf, sizeof(buf), "lm_grouped_kernel<%d, %d, %d>", fmt, B, lm_tiles(M));
+  else snprintf(buf, sizeof(buf), "mfma_grouped_kernel<%d, %d>", fmt, B);
   return buf;
 }
 
