@@ -31,6 +31,7 @@ Prints one JSON line.
 import argparse
 import json
 import math
+import subprocess
 import os
 import sys
 import time
@@ -143,8 +144,10 @@ def graph_of_steps(torch, run_step, first, count):
     return g
 
 
-def time_steps(torch, run_step, steps, warmup, rot):
-    """Run `steps` steps as replays of graphs of `rot` steps; returns elapsed ms for exactly `steps` steps."""
+def time_steps(torch, run_step, steps, warmup, rot, spread=None):
+    """Run `steps` steps as replays of graphs of `rot` steps; returns elapsed ms for exactly `steps` steps.
+    With a list as `spread`, an event after every full replay also gives each replay's time per
+    step in microseconds (appended to the list); the timed work is the same."""
     full = graph_of_steps(torch, run_step, 0, rot)
     rem = steps % rot
     tail = graph_of_steps(torch, run_step, 0, rem) if rem else None
@@ -152,14 +155,37 @@ def time_steps(torch, run_step, steps, warmup, rot):
         full.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = []
     e0.record()
     for _ in range(steps // rot):
         full.replay()
+        if spread is not None:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record()
     if tail is not None:
         tail.replay()
     e1.record()
     torch.cuda.synchronize()
+    prev = e0
+    for ev in marks:
+        spread.append(1e3 * prev.elapsed_time(ev) / rot)
+        prev = ev
     return e0.elapsed_time(e1)
+
+
+def gpu_state(torch):
+    """The device and, where rocm-smi answers, its current clocks and power (best effort)."""
+    props = torch.cuda.get_device_properties(0)
+    state = {"name": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        cards = json.loads(r.stdout) if r.returncode == 0 else {}
+        card = next((v for k, v in cards.items() if k.startswith("card")), {})
+        state["rocm_smi"] = {k: v for k, v in card.items() if "clk" in k.lower() or "power" in k.lower()}
+    except Exception as e:  # the tool may be absent or refuse; the state is context only
+        state["rocm_smi"] = "unavailable (%s)" % type(e).__name__
+    return state
 
 
 def cpu_baseline(fmt, linears_host, seconds):
@@ -191,9 +217,22 @@ def cpu_baseline(fmt, linears_host, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": "%d rows of each linear (unpack + dequant + float64 product), %d passes in %.1f s; "
-                      "elementwise steps single-threaded, the product on %d BLAS threads" % (rows, reps, dt, blas_threads)}
+    out = {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+           "sample": "%d rows of each linear (unpack + dequant + float64 product), %d passes in %.1f s; "
+                     "elementwise steps single-threaded, the product on %d BLAS threads" % (rows, reps, dt, blas_threads)}
+    try:  # the same sample with the product on one thread, for a quarter of the time
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            b1, t1, r1 = 0, time.perf_counter(), 0
+            while time.perf_counter() - t1 < seconds / 4:
+                for (pp, ss, zz, r, k, x, b) in work:
+                    oracle.linear_ref(x, oracle.dequant_fp16(fmt, oracle.unpack_vectorized(fmt, pp, r, k), ss, zz))
+                    b1 += b
+                r1 += 1
+            out["single_thread"] = {"value": b1 / (time.perf_counter() - t1) / 1e9, "unit": "GB/s", "passes": r1}
+    except Exception as e:
+        out["single_thread"] = "unavailable (%s)" % type(e).__name__
+    return out
 
 
 SWEEPS = {
@@ -333,8 +372,10 @@ def main():
     steps = args.steps
     grouped = not args.separate
     step_fn = grouped_step(lins, rot) if grouped else separate_step(lins, rot)
-    ms_total = time_steps(torch, step_fn, steps, args.warmup, rot)
+    per_replay = []
+    ms_total = time_steps(torch, step_fn, steps, args.warmup, rot, per_replay)
     value = step_weight_bytes * steps / (ms_total * 1e-3) / 1e9
+    state = gpu_state(torch)   # right after the timed region, while the clocks are still up
 
     # roofline of the dominant kernel, from the same timed region: the step holds only this
     # kernel's launches, back to back in the graph, so its average duration is the step time
@@ -418,6 +459,11 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if per_replay:
+        q = np.percentile(per_replay, [10, 50, 90])
+        out["step_us_spread"] = {"p10": round(float(q[0]), 3), "p50": round(float(q[1]), 3), "p90": round(float(q[2]), 3),
+                                 "replays": len(per_replay), "steps_per_replay": rot}
+    out["gpu"] = state
     out.update(extras)
     print(json.dumps(out))
     return 0

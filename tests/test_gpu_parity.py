@@ -155,6 +155,7 @@ FULL = [
     ("w8_single_1024x1024", wq.FMT_W8),
     ("llama7b_w4g32_linears", wq.FMT_W4G32),
     ("llama70b_w6e3m2_linears", wq.FMT_W6E3M2),
+    ("llama70b_w6e3m2_tp8_shard", wq.FMT_W6E3M2),
 ]
 
 

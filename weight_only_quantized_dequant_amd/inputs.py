@@ -28,9 +28,14 @@ WORKLOADS = {
     "w8_single_1024x1024": ("w8", [(1024, 1024)], [1]),
     "llama7b_w4g32_linears": ("w4g32", [(4096, 4096), (11008, 4096), (4096, 11008)], [1]),
     "llama70b_w6e3m2_linears": ("w6e3m2", [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)], [1, 4, 8, 16]),
+    # one GPU's shard of the 70B layer under 8-way tensor parallelism: fused q/k/v and gate/up
+    # split by output rows (column-parallel), o and down split along K (row-parallel)
+    "llama70b_w6e3m2_tp8_shard": ("w6e3m2", [(1280, 8192), (8192, 1024), (3584, 8192), (3584, 8192), (8192, 3584)],
+                                  [1, 4, 8, 16]),
 }
 # stream index of each workload, so that every workload draws from its own stream
-WORKLOAD_STREAM = {"w8_single_1024x1024": 0, "llama7b_w4g32_linears": 1, "llama70b_w6e3m2_linears": 2}
+WORKLOAD_STREAM = {"w8_single_1024x1024": 0, "llama7b_w4g32_linears": 1, "llama70b_w6e3m2_linears": 2,
+                   "llama70b_w6e3m2_tp8_shard": 3}
 
 
 def rng_for(stream, linear):
