@@ -238,6 +238,11 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_kernel_name(2, 64, 4096, 4128) == "mfma_kernel<2, 1>"
     assert wq.wq_linear_kernel_name(1, 40, 4096, 4096) == "mfma_kernel<1, 1>"
     assert wq.wq_linear_kernel_name(3, 100, 4096, 4096) == "lm_kernel<3, 1, 4>"
+    # rows of 2^25 + 256 and more: 16-row slabs (32-bit x offsets stay in range)
+    assert wq.wq_linear_kernel_name(3, 64, 64, (1 << 25) + 256) == "lm_kernel<3, 1, 1>"
+    assert wq.wq_linear_kernel_name(3, 64, 64, 1 << 25) == "lm_kernel<3, 1, 4>"
+    assert wq.wq_linear_grouped_kernel_name(3, 40, [(64, 4096), (64, (1 << 25) + 256)]) == "lm_kernel<3, 1, 1>"
+    assert wq.wq_linear_grouped_kernel_name(3, 16, [(64, 4096), (64, (1 << 25) + 256)]) == "lm_grouped_kernel<3, 1, 1>"
     assert wq.wq_linear_grouped_kernel_name(3, 20, [(1024, 8192), (8192, 8192)]) == "lm_grouped_kernel<3, 2, 2>"
     assert wq.wq_linear_grouped_kernel_name(3, 65, [(1024, 8192), (8192, 8192)]) == "lm_kernel<3, 2, 4>"
     assert wq.wq_linear_grouped_kernel_name(1, 20, [(1024, 8192), (8192, 8192)]) == "mfma_kernel<1, 2>"

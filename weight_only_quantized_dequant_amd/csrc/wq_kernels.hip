@@ -1055,9 +1055,11 @@ LmPlan plan_lm(int64_t N, int64_t K) {
 int lm_tiles(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 
 // Rows of x per launch: 64 where the LDS-staged kernel serves the shape (W6; W4 with K a
-// multiple of 256), else 16.
+// multiple of 256), else 16. The kernels address x with 32-bit lane offsets (row * 2K + 64 u),
+// which hold 64 rows only while K <= 2^25; longer rows take 16-row slabs.
 int64_t slab_rows(int fmt, int64_t K) {
-  return fmt == WQ_FMT_W6E3M2 || (fmt == WQ_FMT_W4G32 && K % 256 == 0) ? 16 * LM_MAX_MT : MFMA_M;
+  const bool lm = fmt == WQ_FMT_W6E3M2 || (fmt == WQ_FMT_W4G32 && K % 256 == 0);
+  return lm && K <= (int64_t(1) << 25) ? 16 * LM_MAX_MT : MFMA_M;
 }
 
 template <int FMT, int M>
@@ -1186,6 +1188,14 @@ int group_rows(Family f, int fmt, const int64_t* N, const int64_t* K, int count)
   return f == FAM_GEMV ? gemv_rows_per_wave(fmt, N[big], K[big]) : f == FAM_LM ? lm_rows(N[big]) : mfma_rows(fmt, N[big]);
 }
 
+// rows of x one grouped launch of this family takes for every item
+int64_t group_launch_rows(Family f, int fmt, const int64_t* K, int count) {
+  if (f != FAM_LM) return MFMA_M;
+  int64_t rows = 16 * LM_MAX_MT;
+  for (int i = 0; i < count; ++i) rows = std::min(rows, slab_rows(fmt, K[i]));
+  return rows;
+}
+
 int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, const uint16_t* z, const uint16_t* y,
                       int64_t M, int64_t N, int64_t K, int fmt) {
   if (!valid_fmt(fmt)) return WQ_ERR_FMT;
@@ -1274,7 +1284,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
   // small items alone would pick fewer rows per wave to get enough waves, which the launch
   // has anyway); each item keeps the K split its own plan gives for that B / RB
   const Family fam = group_family(fmt, M, Ns, Ks, count);
-  if (M > MFMA_M && (fam != FAM_LM || M > 16 * LM_MAX_MT)) {   // several slabs: one wq_linear per item
+  if (M > group_launch_rows(fam, fmt, Ks, count)) {   // several slabs: one wq_linear per item
     for (int i = 0; i < count; ++i) {
       const wq_linear_item& it = items[i];
       const int st = wq_linear(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt, stream);
@@ -1351,7 +1361,7 @@ const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, 
     if (N[i] < 1 || K[i] < 32 || K[i] % 32) return "";
   const int big = largest_item(N, K, count);
   const Family fam = group_family(fmt, M, N, K, count);
-  if (M > MFMA_M && (fam != FAM_LM || M > 16 * LM_MAX_MT))
+  if (M > group_launch_rows(fam, fmt, K, count))
     return wq_linear_kernel_name(fmt, M, N[big], K[big]);   // separate launches: the largest item's
   const int B = group_rows(fam, fmt, N, K, count);
   if (fam == FAM_GEMV) snprintf(buf, sizeof(buf), "gemv_grouped_kernel<%d, %d, %d>", fmt, static_cast<int>(M), B);
