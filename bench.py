@@ -31,7 +31,6 @@ Prints one JSON line.
 import argparse
 import json
 import math
-import subprocess
 import os
 import sys
 import time
@@ -174,17 +173,27 @@ def time_steps(torch, run_step, steps, warmup, rot, spread=None):
 
 
 def gpu_state(torch):
-    """The device and, where rocm-smi answers, its current clocks and power (best effort)."""
+    """The device and its current clock levels and power as the kernel driver's sysfs files show
+    them (plain file reads, best effort: no helper program is started)."""
+    import glob
     props = torch.cuda.get_device_properties(0)
     state = {"name": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count}
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
-                           timeout=20)
-        cards = json.loads(r.stdout) if r.returncode == 0 else {}
-        card = next((v for k, v in cards.items() if k.startswith("card")), {})
-        state["rocm_smi"] = {k: v for k, v in card.items() if "clk" in k.lower() or "power" in k.lower()}
-    except Exception as e:  # the tool may be absent or refuse; the state is context only
-        state["rocm_smi"] = "unavailable (%s)" % type(e).__name__
+    sysfs = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            for clk in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+                path = os.path.join(dev, clk)
+                if os.path.exists(path):
+                    cur = [l.strip() for l in open(path).read().splitlines() if l.strip().endswith("*")]
+                    sysfs[clk] = cur[0] if cur else None
+            for pw in glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_average")) + \
+                    glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_input")):
+                sysfs[os.path.basename(pw) + "_W"] = round(int(open(pw).read().strip()) / 1e6, 1)
+        except (OSError, ValueError):
+            continue
+        if sysfs:
+            break
+    state["sysfs"] = sysfs or "unavailable"
     return state
 
 
