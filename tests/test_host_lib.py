@@ -216,10 +216,12 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_kernel_name(2, 8, 4096, 4096) == "lm_kernel<2, 1, 1>"
     assert wq.wq_linear_kernel_name(2, 8, 4096, 4128) == "mfma_kernel<2, 1>"
     assert wq.wq_linear_kernel_name(3, 3, 4096, 4096).startswith("gemv_kernel")
-    # M = 4: the matrix cores for W6/W8 with N >= 4096 and for W4 from N*K = 2^24, the GEMV otherwise
+    # M = 4: the matrix cores for W6 with N >= 2048, W8 with N >= 4096 and W4 from N*K = 2^24, the GEMV otherwise
     assert wq.wq_linear_kernel_name(3, 4, 4096, 4096).startswith("lm_kernel")
+    assert wq.wq_linear_kernel_name(3, 4, 2048, 4096).startswith("lm_kernel")
     assert wq.wq_linear_kernel_name(1, 4, 8192, 4096).startswith("mfma_kernel")
-    assert wq.wq_linear_kernel_name(3, 4, 1024, 4096).startswith("gemv_kernel")
+    assert wq.wq_linear_kernel_name(1, 4, 2048, 4096).startswith("gemv_kernel")
+    assert wq.wq_linear_kernel_name(3, 4, 1280, 8192).startswith("gemv_kernel")
     assert wq.wq_linear_kernel_name(2, 4, 2048, 4096).startswith("gemv_kernel")
     assert wq.wq_linear_kernel_name(2, 4, 4096, 4096) == "lm_kernel<2, 1, 1>"
     assert wq.wq_linear_kernel_name(2, 4, 8192, 8192) == "lm_kernel<2, 2, 1>"

@@ -990,12 +990,12 @@ struct MfmaPlan {
   int grid;   // workgroups
 };
 
-// The matrix cores serve M >= 5, and M = 4 for W6/W8 rows of 4096 or more (and larger W4),
+// The matrix cores serve M >= 5, and M = 4 for N >= 2048 (W6) / 4096 (W8) and larger W4,
 // where they beat the VALU GEMV (which then spends four dot products per weight pair):
 // lm_kernel for W6 and for W4 with K a multiple of 256 (see use_lm), mfma_kernel for the rest.
 bool use_mfma(int fmt, int64_t M, int64_t N) {
   if (M > GEMV_MAX_M) return true;
-  return M == GEMV_MAX_M && (fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W8) && N >= 4096;
+  return M == GEMV_MAX_M && ((fmt == WQ_FMT_W6E3M2 && N >= 2048) || (fmt == WQ_FMT_W8 && N >= 4096));
 }
 
 // RB: as many row blocks per wave as keeps >= 256 row groups (W4 and F16, whose decode
