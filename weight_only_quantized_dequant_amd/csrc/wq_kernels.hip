@@ -22,9 +22,12 @@
 //  * M <= GEMV_MAX_M: VALU GEMV. v_dot2_f32_f16 accumulates in fp32, lanes run along K,
 //    and each row's sum finishes with a DPP + cross-row shuffle wave reduction; waves of a
 //    workgroup split K and add their partials through LDS in a fixed order.
-//  * Larger M: v_mfma_f32_16x16x32_f16. Lane (n = l%16, q = l/16) decodes its own unit
-//    straight into the B fragment; the A fragment is x at the same K positions, since any
-//    permutation of K applied to both operands leaves the product unchanged.
+//  * Larger M: v_mfma_f32_16x16x32_f16. Lane (n = l%16, q = l/16) decodes a unit into the B
+//    fragment; the A fragment is x at the same K positions, since any permutation of K
+//    applied to both operands leaves the product unchanged. W6 and W4 (K % 256 == 0) read
+//    their weights row-contiguously into per-wave LDS first (lm_kernel); W8, F16 and the
+//    other W4 shapes load fragments straight from HBM (mfma_kernel).
+//  * A grouped call runs several linears in one launch with one of these kernel families.
 //  * No atomics anywhere, so every result is deterministic.
 #include <hip/hip_runtime.h>
 
@@ -473,7 +476,7 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_grouped_kernel(const Gem
                        g.WK[j]);
 }
 
-// ---------------------------------------------------------------- MFMA (M = 4..16)
+// ---------------------------------------------------------------- MFMA, fragment loads (W8, F16, W4 with K % 256 != 0)
 // v_mfma_f32_16x16x32_f16 with the weights as the B operand: lane (nl = l%16, q = l/16)
 // decodes unit u = 4t+q of row nl of a 16-row block straight into its B fragment (8 K per
 // MFMA step), and holds x[m = nl][the same K] as the A fragment (rows m >= M are zero).
@@ -507,17 +510,11 @@ __device__ __forceinline__ void mfma_load(MfmaStage<FMT, RB>& st, const uint16_t
     const int nb = min(n0 + 16 * r, N - 1);                        // wave-uniform
     const uint32_t nn = (uint32_t)(min(n0 + 16 * r + nl, N - 1) - nb);   // 0..15
     const uint8_t* rowb = w + uniform((size_t)nb * row_bytes);
-    if constexpr (FMT == WQ_FMT_W6E3M2) {
-      uint32_t lo, hi;
-      w6_homes(u, U, lo, hi);
-      st.w[r].a = ld_nt16(rowb + nn * row_bytes + lo);
-      st.w[r].b = ld_nt8(rowb + nn * row_bytes + hi);
-    } else {
-      const uint8_t* p = rowb + nn * row_bytes + UB * u;
-      st.w[r].a = ld_nt16(p);
-      if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_F16) st.w[r].b = ld_nt16(p + 16);
-      if constexpr (FMT == WQ_FMT_F16) { st.w[r].c = ld_nt16(p + 32); st.w[r].d = ld_nt16(p + 48); }
-    }
+    static_assert(FMT != WQ_FMT_W6E3M2, "W6 on the matrix cores takes lm_kernel");
+    const uint8_t* p = rowb + nn * row_bytes + UB * u;
+    st.w[r].a = ld_nt16(p);
+    if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_F16) st.w[r].b = ld_nt16(p + 16);
+    if constexpr (FMT == WQ_FMT_F16) { st.w[r].c = ld_nt16(p + 32); st.w[r].d = ld_nt16(p + 48); }
     if constexpr (FMT == WQ_FMT_W4G32) {
       const size_t mb = uniform((size_t)nb * U);
       st.s[r] = (scales + mb)[nn * U + u];
@@ -1119,14 +1116,18 @@ hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w,
       default: return launch_gemv_m<FMT, 4>(p, s, x, w, sc, z, y, N, K);
     }
   }
-  const MfmaPlan p = plan_mfma(FMT, N, K);
-  const dim3 grid(p.grid), block(64 * p.WK);
-  switch (p.RB) {
-    case 4: hipLaunchKernelGGL((mfma_kernel<FMT, 4>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
-    case 2: hipLaunchKernelGGL((mfma_kernel<FMT, 2>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
-    default: hipLaunchKernelGGL((mfma_kernel<FMT, 1>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
+  if constexpr (FMT == WQ_FMT_W6E3M2) {
+    return hipErrorInvalidValue;   // W6 on the matrix cores always takes lm_kernel (use_lm)
+  } else {
+    const MfmaPlan p = plan_mfma(FMT, N, K);
+    const dim3 grid(p.grid), block(64 * p.WK);
+    switch (p.RB) {
+      case 4: hipLaunchKernelGGL((mfma_kernel<FMT, 4>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
+      case 2: hipLaunchKernelGGL((mfma_kernel<FMT, 2>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
+      default: hipLaunchKernelGGL((mfma_kernel<FMT, 1>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
+    }
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 template <int FMT, int M>
@@ -1211,12 +1212,16 @@ int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, cons
 template <int FMT>
 hipError_t launch_grouped_mc(Family f, const GemvGroup& g, int M, int RB, int block_waves, int grid, hipStream_t s) {
   if (f == FAM_LM) return launch_lm<FMT>(RB, M, dim3(grid), s, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, &g);
-  switch (RB) {
-    case 4: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 4>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
-    case 2: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 2>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
-    default: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 1>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
+  if constexpr (FMT == WQ_FMT_W6E3M2) {
+    return hipErrorInvalidValue;   // W6 groups on the matrix cores are always FAM_LM
+  } else {
+    switch (RB) {
+      case 4: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 4>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
+      case 2: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 2>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
+      default: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 1>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
+    }
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 }  // namespace
