@@ -1,4 +1,4 @@
-"""Number formats: fp16 rounding and the FP6 e3m2 code.
+"""Number formats: fp16 rounding, the FP6 e3m2 code and the FP4 e2m1 code.
 
 Test infrastructure only (see the package docstring for who may import it).
 
@@ -6,12 +6,19 @@ FP6 is named, with no bit layout, on the FP6-LLM news page (m.zhengruan.com),
 sections "用FP6跑Llama，单卡比双卡还快" and "重新设计内核方案". The reading used here
 is e3m2: 1 sign bit, 3 exponent bits with bias 3, 2 mantissa bits, subnormals when the
 exponent field is 0, no infinities or NaNs, largest magnitude 28.
+
+The same page says the kernel design serves weights of other bit widths as well, and
+names none. FP4 is taken here as e2m1: 1 sign bit, 2 exponent bits with bias 1, 1
+mantissa bit, subnormals when the exponent field is 0, no infinities or NaNs, largest
+magnitude 6 (the eight magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
 """
 
 import numpy as np
 
 E3M2_BIAS = 3
 E3M2_MAX = 28.0
+E2M1_BIAS = 1
+E2M1_MAX = 6.0
 
 
 def fp16_bits(values):
@@ -79,4 +86,51 @@ def e3m2_encode(t):
         mag_code = np.where(n_min > 1, np.argmax(is_min & even, axis=1), np.argmax(is_min, axis=1))
         sign = np.signbit(flat[i:i + step]).astype(np.uint8)
         out[i:i + step] = mag_code.astype(np.uint8) | (sign << 5)
+    return out.reshape(t.shape)
+
+
+def e2m1_value(code):
+    """Value of one 4-bit e2m1 code ``s e1 e0 m0`` (closed form, exact in float64)."""
+    code = int(code)
+    if not 0 <= code < 16:
+        raise ValueError("e2m1 code out of range: %r" % code)
+    sign = -1.0 if (code >> 3) & 1 else 1.0
+    e = (code >> 1) & 3
+    m = code & 1
+    if e == 0:
+        mag = m * 2.0 ** (1 - E2M1_BIAS) / 2.0          # subnormal: 0.m x 2^(1-bias)
+    else:
+        mag = (1.0 + m / 2.0) * 2.0 ** (e - E2M1_BIAS)  # normal: 1.m x 2^(e-bias)
+    return sign * mag
+
+
+def e2m1_table():
+    """All 16 code values as float64 (code 8 is -0.0)."""
+    return np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def e2m1_encode(t):
+    """Encode float64 values as e2m1 codes: nearest magnitude, ties to the even code, saturating.
+
+    As for e3m2: the sign bit is the sign bit of ``t`` (a negative value that rounds to
+    zero gives code 8, i.e. -0), the magnitude is the nearest of the 8 non-negative
+    values, a tie goes to the even code, and magnitudes above 6 saturate at 6. Written as
+    a brute-force search over the 8 magnitudes.
+    """
+    t = np.asarray(t, dtype=np.float64)
+    if not np.all(np.isfinite(t)):
+        raise ValueError("e2m1_encode: non-finite input")
+    mags = e2m1_table()[:8].reshape(1, -1)        # increasing: 0, 0.5, 1, 1.5, 2, 3, 4, 6
+    even = (np.arange(8) % 2 == 0).reshape(1, -1)
+    flat = t.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 1 << 16
+    for i in range(0, flat.size, step):
+        a = np.minimum(np.abs(flat[i:i + step]), E2M1_MAX).reshape(-1, 1)
+        dist = np.abs(a - mags)
+        is_min = dist == dist.min(axis=1, keepdims=True)
+        n_min = is_min.sum(axis=1)
+        mag_code = np.where(n_min > 1, np.argmax(is_min & even, axis=1), np.argmax(is_min, axis=1))
+        sign = np.signbit(flat[i:i + step]).astype(np.uint8)
+        out[i:i + step] = mag_code.astype(np.uint8) | (sign << 3)
     return out.reshape(t.shape)

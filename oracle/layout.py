@@ -18,6 +18,9 @@ kernel consumes them. It gives no concrete layout. The layout used here is:
       being bits 4p .. 4p+3 of the word.
     - W6 (24 bytes): one 192-bit little-endian number; code j sits in bits 6j .. 6j+5.
       These 24 bytes are not stored in one piece (see below).
+    - FP4 (16 bytes): one 128-bit little-endian number; code j sits in bits 4j .. 4j+3,
+      so byte p holds code 2p in its low nibble and code 2p+1 in its high nibble (the
+      order in which gfx950's packed FP4 convert takes a byte).
     - F16 (64 bytes, the unquantized baseline): bytes 2j, 2j+1 hold the fp16 bits of
       weight j, little-endian.
 * W6 only, split by planes: the units of a row are taken 64 at a time ("chunks"; the
@@ -25,11 +28,11 @@ kernel consumes them. It gives no concrete layout. The layout used here is:
   come first, unit after unit (16*Uc bytes), then bytes 16..23 of its units (8*Uc
   bytes). A chunk with one unit is therefore stored exactly as that unit. (A device
   lane reads one unit, so each of the two loads of a wave reads one contiguous block.)
-* Metadata stays in logical order: W8/W6 scales [N]; W4 scales and zeros [N][K/32],
+* Metadata stays in logical order: W8/W6/FP4 scales [N]; W4 scales and zeros [N][K/32],
   row-major (group g of row n covers the same 32 K as unit g).
 
 Codes given to and returned by these functions are the logical codes: int8 q for W8,
-0..15 for W4, 0..63 for W6, uint16 fp16 bits for F16.
+0..15 for W4 and FP4, 0..63 for W6, uint16 fp16 bits for F16.
 """
 
 import numpy as np
@@ -38,8 +41,9 @@ FMT_F16 = 0
 FMT_W8 = 1
 FMT_W4G32 = 2
 FMT_W6E3M2 = 3
+FMT_W4E2M1 = 4
 
-_BITS = {FMT_F16: 16, FMT_W8: 8, FMT_W4G32: 4, FMT_W6E3M2: 6}
+_BITS = {FMT_F16: 16, FMT_W8: 8, FMT_W4G32: 4, FMT_W6E3M2: 6, FMT_W4E2M1: 4}
 UNIT = 32
 CHUNK = 64          # units per W6 plane chunk
 
@@ -83,6 +87,8 @@ def code_field(fmt, j):
         return 32 * d + 4 * nibble, 4
     if fmt == FMT_W6E3M2:
         return 6 * j, 6
+    if fmt == FMT_W4E2M1:
+        return 4 * j, 4
     if fmt == FMT_F16:
         return 16 * j, 16
     raise ValueError("unknown format %r" % fmt)
@@ -95,7 +101,7 @@ def _stored(fmt, code):
         if not -127 <= code <= 127:
             raise ValueError("int8 code out of range")
         return code + 128
-    limit = {FMT_W4G32: 16, FMT_W6E3M2: 64, FMT_F16: 65536}[fmt]
+    limit = {FMT_W4G32: 16, FMT_W6E3M2: 64, FMT_W4E2M1: 16, FMT_F16: 65536}[fmt]
     if not 0 <= code < limit:
         raise ValueError("code out of range")
     return code
@@ -151,7 +157,7 @@ def unpack_scalar(fmt, packed, n, k):
     if packed.size != packed_bytes(fmt, n, k):
         raise ValueError("packed size mismatch")
     ub = unit_bytes(fmt)
-    dtype = {FMT_W8: np.int8, FMT_W4G32: np.uint8, FMT_W6E3M2: np.uint8, FMT_F16: np.uint16}[fmt]
+    dtype = {FMT_W8: np.int8, FMT_W4G32: np.uint8, FMT_W6E3M2: np.uint8, FMT_W4E2M1: np.uint8, FMT_F16: np.uint16}[fmt]
     codes = np.zeros((n, k), dtype=dtype)
     for r in range(n):
         for u in range(k // UNIT):
@@ -194,6 +200,12 @@ def pack_vectorized(fmt, codes):
         v = c[:, :, 0] | (c[:, :, 1] << 6) | (c[:, :, 2] << 12) | (c[:, :, 3] << 18)
         b = np.stack([v & 0xFF, (v >> 8) & 0xFF, (v >> 16) & 0xFF], axis=-1).astype(np.uint8)
         return _w6_to_planes(b.reshape(n, k // UNIT, 24)).reshape(-1)
+    if fmt == FMT_W4E2M1:
+        c = codes.astype(np.uint8)
+        if c.max(initial=0) > 15:
+            raise ValueError("fp4 code out of range")
+        c = c.reshape(n, k // 2, 2)
+        return (c[:, :, 0] | (c[:, :, 1] << 4)).astype(np.uint8).reshape(-1)
     if fmt == FMT_F16:
         return codes.astype(np.uint16).astype("<u2").view(np.uint8).reshape(-1)
     raise ValueError("unknown format %r" % fmt)
@@ -216,6 +228,9 @@ def unpack_vectorized(fmt, packed, n, k):
         v = b[:, :, 0] | (b[:, :, 1] << 8) | (b[:, :, 2] << 16)
         out = np.stack([(v >> s) & 0x3F for s in (0, 6, 12, 18)], axis=-1).astype(np.uint8)
         return out.reshape(n, k)
+    if fmt == FMT_W4E2M1:
+        b = packed.reshape(n, k // 2)
+        return np.stack([b & 0xF, b >> 4], axis=-1).astype(np.uint8).reshape(n, k)
     if fmt == FMT_F16:
         return packed.view("<u2").reshape(n, k).astype(np.uint16)
     raise ValueError("unknown format %r" % fmt)

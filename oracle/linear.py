@@ -13,16 +13,16 @@ bound given by ``error_bound``.
 
 import numpy as np
 
-from .formats import fp16_bits, fp16_from_bits, e3m2_table
-from .layout import FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, pack_vectorized
-from .quantize import quantize_int8, quantize_int4_g32, quantize_fp6
+from .formats import fp16_bits, fp16_from_bits, e3m2_table, e2m1_table
+from .layout import FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, pack_vectorized
+from .quantize import quantize_int8, quantize_int4_g32, quantize_fp6, quantize_fp4
 
 
 def dequant_fp16(fmt, codes, scales=None, zeros=None):
     """Logical codes + fp16 metadata bits -> dequantised weights as fp16 bits [N,K].
 
     W8: fp16(q * s). W4: fp16((q - z) * s) with s, z of the weight's group.
-    W6: fp16(e3m2(c) * s). F16: the weights themselves.
+    W6: fp16(e3m2(c) * s). FP4: fp16(e2m1(c) * s). F16: the weights themselves.
     Each product is formed exactly in float64 (the factors have at most 11 and 8
     significant bits) and then rounded once to fp16.
     """
@@ -39,6 +39,8 @@ def dequant_fp16(fmt, codes, scales=None, zeros=None):
         v = ((q - z) * s.reshape(n, k // 32, 1)).reshape(n, k)
     elif fmt == FMT_W6E3M2:
         v = e3m2_table()[codes.astype(np.int64)] * s.reshape(n, 1)
+    elif fmt == FMT_W4E2M1:
+        v = e2m1_table()[codes.astype(np.int64)] * s.reshape(n, 1)
     else:
         raise ValueError("unknown format %r" % fmt)
     return fp16_bits(v)
@@ -80,6 +82,9 @@ def quantize_and_pack(fmt, w):
         codes, s, z = quantize_int4_g32(w)
     elif fmt == FMT_W6E3M2:
         codes, s = quantize_fp6(w)
+        z = np.zeros(0, dtype=np.uint16)
+    elif fmt == FMT_W4E2M1:
+        codes, s = quantize_fp4(w)
         z = np.zeros(0, dtype=np.uint16)
     elif fmt == FMT_F16:
         codes = fp16_bits(w.astype(np.float64))

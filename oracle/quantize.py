@@ -17,7 +17,9 @@ The pages give no formulas. The readings are:
   and the dequantised weight is ``(q - z) * s``.
 * FP6: one fp16 scale per output row, ``s = fp16(max|w| / 28)``, code = e3m2 encoding of
   ``w / s`` (nearest, ties to even code, saturating at 28).
-* In all three a scale that rounds to 0 makes every code of its row (or group) 0, and
+* FP4 (a further bit width through the same design; the page names none): e2m1 with one
+  fp16 scale per output row, ``s = fp16(max|w| / 6)``, code = e2m1 encoding of ``w / s``.
+* In all of them a scale that rounds to 0 makes every code of its row (or group) 0, and
   z = 0. A scale that overflows fp16 is an error.
 
 Arithmetic: each quotient is one IEEE float64 operation on float64 copies of the fp32
@@ -26,7 +28,7 @@ weights and of the fp16 scale, then one rounding (``rint`` ties to even, or fp16
 
 import numpy as np
 
-from .formats import fp16_bits, fp16_from_bits, e3m2_encode
+from .formats import fp16_bits, fp16_from_bits, e3m2_encode, e2m1_encode, E2M1_MAX
 
 
 class OracleRangeError(ValueError):
@@ -91,4 +93,17 @@ def quantize_fp6(w):
     nz = s > 0
     if np.any(nz):
         codes[nz] = e3m2_encode(w[nz] / s[nz, None])
+    return codes, s_bits
+
+
+def quantize_fp4(w):
+    """FP4 e2m1 per output row. Returns (codes uint8 [N,K] in 0..15, scale bits uint16 [N])."""
+    w = _check_w(w)
+    amax = np.max(np.abs(w), axis=1)
+    s_bits = _scale16(amax / E2M1_MAX)
+    s = fp16_from_bits(s_bits)
+    codes = np.zeros(w.shape, dtype=np.uint8)
+    nz = s > 0
+    if np.any(nz):
+        codes[nz] = e2m1_encode(w[nz] / s[nz, None])
     return codes, s_bits

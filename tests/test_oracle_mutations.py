@@ -20,6 +20,44 @@ def test_pins_accept_the_oracle():
     assert pins.check_quantizer("w8", oracle.quantize_int8, w)
     assert pins.check_quantizer("w4", oracle.quantize_int4_g32, w)
     assert pins.check_quantizer("w6", oracle.quantize_fp6, w)
+    assert pins.check_e2m1_table(oracle.e2m1_value)
+    assert pins.check_quantizer("fp4", oracle.quantize_fp4, w)
+
+
+def test_e2m1_wrong_bias_is_caught():
+    assert not pins.check_e2m1_table(lambda c: oracle.e2m1_value(c) * 2)
+
+
+def test_e2m1_subnormal_as_normal_is_caught():
+    def bad(c):
+        e, m = (c >> 1) & 3, c & 1
+        v = (1 + m / 2) * 2.0 ** (e - 1)          # forgets that exponent field 0 is subnormal
+        return -v if c & 8 else v
+    assert not pins.check_e2m1_table(bad)
+
+
+def test_fp4_ties_away_from_zero_is_caught():
+    def bad_quant(w):
+        w64 = w.astype(np.float64)
+        s_bits = oracle.fp16_bits(np.abs(w64).max(axis=1) / 6.0)
+        s = oracle.fp16_from_bits(s_bits)
+        t = w64 / s[:, None]
+        tab = oracle.e2m1_table()[:8]
+        d = np.abs(np.abs(t)[..., None] - tab)
+        code = (7 - np.argmin(d[..., ::-1], axis=-1)).astype(np.uint8)   # ties to the larger magnitude
+        return code | (np.signbit(t).astype(np.uint8) << 3), s_bits
+    w = np.zeros((1, 32), dtype=np.float32)
+    w[0, 0] = 6.0
+    w[0, 1:4] = [2.5, 0.25, 5.0]                      # three exact ties (scale is 1)
+    assert not pins.check_quantizer("fp4", bad_quant, w)
+
+
+def test_fp4_swapped_nibbles_are_caught():
+    for name, codes, expected in pins.golden_pack_examples():
+        if name != "FP4":
+            continue
+        c = np.array(codes, dtype=np.uint8).reshape(16, 2)
+        assert bytes((c[:, 1] | (c[:, 0] << 4)).tolist()) != expected    # code 2p in the high nibble
 
 
 def test_e3m2_wrong_bias_is_caught():

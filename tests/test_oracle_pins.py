@@ -7,10 +7,10 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2
+from oracle import FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1
 from tests import pins
 
-FMTS = {"w8": FMT_W8, "w4": FMT_W4G32, "w6": FMT_W6E3M2, "f16": FMT_F16}
+FMTS = {"w8": FMT_W8, "w4": FMT_W4G32, "w6": FMT_W6E3M2, "f16": FMT_F16, "fp4": FMT_W4E2M1}
 
 
 # ------------------------------------------------------------------ e3m2
@@ -65,6 +65,55 @@ def test_e3m2_encode_vs_exact_brute_force():
         assert int(g) == pins.brute_fp6_code(float(v)), v
 
 
+# ------------------------------------------------------------------ e2m1 (FP4)
+def test_e2m1_table_matches_hand_typed_table():
+    assert pins.check_e2m1_table(oracle.e2m1_value)
+
+
+def test_e2m1_special_values():
+    t = oracle.e2m1_table()
+    assert t[7] == 6.0 and t[15] == -6.0                    # largest magnitude, no inf/NaN
+    assert t[1] == 0.5                                      # the one subnormal, 2^(1-1) / 2
+    assert t[2] == 1.0                                      # smallest normal
+    assert t[0] == 0.0 and not math.copysign(1, t[0]) < 0
+    assert t[8] == 0.0 and math.copysign(1, t[8]) < 0       # -0
+    assert np.all(np.diff(t[:8]) > 0)
+    assert np.array_equal(t[8:], -t[:8])
+
+
+def test_e2m1_fp16_bit_placement_identity():
+    # code bits s.ee.m placed at fp16 bits 15 and 11..9 give e2m1(c) * 2^-14 exactly,
+    # the subnormal and -0 included (fp16 exponent bias 15 = e2m1 bias 1 + 14)
+    for c in range(16):
+        bits = ((c & 0x8) << 12) | ((c & 0x7) << 9)
+        v = float(np.uint16(bits).view(np.float16))
+        assert v * 16384.0 == oracle.e2m1_value(c)
+        assert math.copysign(1, v) == math.copysign(1, oracle.e2m1_value(c))
+
+
+@pytest.mark.parametrize("t,code", [
+    (0.25, 0), (-0.25, 8),            # tie between 0 and 0.5: code 0, sign kept
+    (0.75, 2), (1.25, 2), (1.75, 4),  # ties between neighbours go to the even code
+    (2.5, 4), (3.5, 6), (5.0, 6),
+    (5.01, 7), (6.0, 7), (1e6, 7), (-1e6, 15),
+    (-1e-9, 8), (-0.0, 8), (0.0, 0), (0.74, 1), (0.76, 2),
+])
+def test_e2m1_encode_examples(t, code):
+    assert int(oracle.e2m1_encode(np.array([t]))[0]) == code
+
+
+def test_e2m1_encode_vs_exact_brute_force():
+    rng = np.random.default_rng(17)
+    tab = oracle.e2m1_table()
+    mids = [(tab[c] + tab[c + 1]) / 2 for c in range(7)]
+    vals = list(rng.standard_normal(1000) * 3) + mids + [-m for m in mids]
+    vals += [m + d for m in mids for d in (1e-12, -1e-12)]
+    vals += [tab[c] for c in range(16)] + [7.0, -6.5, 6.01, 1e-30, -1e-30]
+    got = oracle.e2m1_encode(np.array(vals))
+    for v, g in zip(vals, got):
+        assert int(g) == pins.brute_fp4_code(float(v)), v
+
+
 # ------------------------------------------------------------------ fp16 rounding
 def test_fp16_rounding_vs_exact():
     rng = np.random.default_rng(3)
@@ -89,11 +138,12 @@ def _adversarial(n, k, rng):
     return w
 
 
-@pytest.mark.parametrize("name", ["w8", "w4", "w6"])
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4"])
 def test_quantizer_vs_brute_force(name):
     rng = np.random.default_rng(11)
     w = _adversarial(8, 64, rng)
-    fn = {"w8": oracle.quantize_int8, "w4": oracle.quantize_int4_g32, "w6": oracle.quantize_fp6}[name]
+    fn = {"w8": oracle.quantize_int8, "w4": oracle.quantize_int4_g32, "w6": oracle.quantize_fp6,
+          "fp4": oracle.quantize_fp4}[name]
     assert pins.check_quantizer(name, fn, w)
 
 
@@ -133,6 +183,18 @@ def test_fp6_saturation_and_negative_zero():
     assert codes[0, :4].tolist() == [31, 63, 32, 16]
 
 
+def test_fp4_saturation_and_negative_zero():
+    w = np.zeros((1, 32), dtype=np.float32)
+    w[0, 0] = 6.0           # scale 1
+    w[0, 1] = -6.0
+    w[0, 2] = -0.001        # rounds to -0
+    w[0, 3] = 2.5           # tie between 2 (code 4) and 3 (code 5) -> 4
+    w[0, 4] = 0.25          # tie between 0 and 0.5 -> 0
+    codes, s = oracle.quantize_fp4(w)
+    assert int(s[0]) == 0x3C00
+    assert codes[0, :5].tolist() == [7, 15, 8, 4, 0]
+
+
 def test_quantizer_errors():
     with pytest.raises(oracle.OracleRangeError):
         oracle.quantize_int8(np.array([[np.nan] * 32], dtype=np.float32))
@@ -149,14 +211,14 @@ def test_pack_matches_hand_derived_bytes():
         assert bytes(oracle.pack_vectorized(fmt, c)) == expected, name
 
 
-@pytest.mark.parametrize("name", ["w8", "w4", "w6", "f16"])
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "f16", "fp4"])
 @pytest.mark.parametrize("n,k", [(3, 96), (2, 32 * 130)])       # 130 units: two full chunks of 64 and one of 2
 def test_pack_scalar_equals_vectorized_and_round_trips(name, n, k):
     fmt = FMTS[name]
     rng = np.random.default_rng(5)
     if name == "w8":
         codes = rng.integers(-127, 128, (n, k)).astype(np.int8)
-    elif name == "w4":
+    elif name in ("w4", "fp4"):
         codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
     elif name == "w6":
         codes = rng.integers(0, 64, (n, k)).astype(np.uint8)
@@ -164,7 +226,7 @@ def test_pack_scalar_equals_vectorized_and_round_trips(name, n, k):
         codes = rng.integers(0, 65536, (n, k)).astype(np.uint16)
     a = oracle.pack_scalar(fmt, codes)
     b = oracle.pack_vectorized(fmt, codes)
-    assert a.size == oracle.packed_bytes(fmt, n, k) == n * k * {"w8": 8, "w4": 4, "w6": 6, "f16": 16}[name] // 8
+    assert a.size == oracle.packed_bytes(fmt, n, k) == n * k * {"w8": 8, "w4": 4, "w6": 6, "f16": 16, "fp4": 4}[name] // 8
     assert np.array_equal(a, b)
     assert np.array_equal(oracle.unpack_scalar(fmt, a, n, k), codes)
     assert np.array_equal(oracle.unpack_vectorized(fmt, b, n, k), codes)
@@ -175,10 +237,11 @@ def test_metadata_counts():
     assert oracle.scales_count(FMT_W6E3M2, 7, 64) == 7
     assert oracle.scales_count(FMT_W4G32, 7, 64) == 14 and oracle.zeros_count(FMT_W4G32, 7, 64) == 14
     assert oracle.scales_count(FMT_F16, 7, 64) == 0
+    assert oracle.scales_count(FMT_W4E2M1, 7, 64) == 7 and oracle.zeros_count(FMT_W4E2M1, 7, 64) == 0
 
 
 # ------------------------------------------------------------------ dequant
-@pytest.mark.parametrize("name", ["w8", "w4", "w6"])
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4"])
 def test_dequant_exact_vs_fraction_and_fp32(name):
     fmt = FMTS[name]
     rng = np.random.default_rng(9)
@@ -194,7 +257,7 @@ def test_dequant_exact_vs_fraction_and_fp32(name):
             g = c // 32 if name == "w4" else 0
             want = pins.exact_dequant(name, int(codes[r, c]), int(sv[r, g]), int(zv[r, g]) if zv is not None else 0)
             got = int(d[r, c])
-            assert got == want or (want in (0, 0x8000) and got in (0, 0x8000) and name != "w6"), (r, c)
+            assert got == want or (want in (0, 0x8000) and got in (0, 0x8000) and name not in ("w6", "fp4")), (r, c)
     # the product is exact in fp32 as well, so an fp32 multiply then one rounding agrees bit for bit
     s32 = oracle.fp16_from_bits(sv).astype(np.float32)
     if name == "w8":
@@ -202,8 +265,10 @@ def test_dequant_exact_vs_fraction_and_fp32(name):
     elif name == "w4":
         zz = oracle.fp16_from_bits(zv).astype(np.float32)
         v32 = (codes.astype(np.float32) - np.repeat(zz, 32, axis=1)) * np.repeat(s32, 32, axis=1)
-    else:
+    elif name == "w6":
         v32 = oracle.e3m2_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
+    else:
+        v32 = oracle.e2m1_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
     assert np.array_equal(v32.astype(np.float16).view(np.uint16), d)
 
 
