@@ -8,7 +8,8 @@
  *   - gpt-fast guide (www.jsqmd.com), section "量化技术深度解析": int4, group size 32.
  *   - FP6-LLM news (m.zhengruan.com), section "重新设计内核方案": FP6 weights with fp16
  *     activations; dequantization fused with the matrix product in one kernel, and the
- *     weights re-packed offline into aligned 32/64-bit blocks.
+ *     weights re-packed offline into aligned 32/64-bit blocks; one kernel design for
+ *     weights of several bit widths.
  *
  * Formats (the pages give names, not bit formats; these are this library's readings):
  *   WQ_FMT_W8      int8, symmetric, one fp16 scale per output row: s = fp16(max|w|/127),
@@ -20,6 +21,10 @@
  *   WQ_FMT_W6E3M2  FP6 e3m2 (sign, 3 exponent bits with bias 3, 2 mantissa bits, subnormals,
  *                  no inf/NaN, max 28), one fp16 scale per row: s = fp16(max|w|/28), code =
  *                  nearest e3m2 to w/s (ties to even code, saturating); w^ = e3m2(code)*s.
+ *   WQ_FMT_W4E2M1  FP4 e2m1 (sign, 2 exponent bits with bias 1, 1 mantissa bit, a subnormal,
+ *                  no inf/NaN, max 6), one fp16 scale per row: s = fp16(max|w|/6), code =
+ *                  nearest e2m1 to w/s (ties to even code, saturating); w^ = e2m1(code)*s.
+ *                  A further bit width through the same kernels; the pages name none.
  *   WQ_FMT_F16     plain fp16 weights W[N,K] (the unquantized baseline); no metadata.
  *   Quotients are IEEE float64 operations; rint and fp16 conversion round to nearest even.
  *   A scale that rounds to 0 makes the codes of its row or group 0 (and z = 0).
@@ -33,8 +38,10 @@
  *       stored split by planes: a row's units are taken 64 at a time (a chunk; the last
  *       chunk of a row may hold fewer, Uc), and in a chunk bytes 0..15 of its Uc units
  *       come first, unit after unit, then bytes 16..23 of the same units.
+ *   FP4 16 B: code j in bits 4j..4j+3 of the unit read as a little-endian number (byte p:
+ *       code 2p in the low nibble, code 2p+1 in the high nibble).
  *   F16 64 B: fp16 weight j at bytes 2j..2j+1 (so F16 is the plain row-major matrix).
- * So packed_w is exactly N*K*bits/8 bytes. scales: W8/W6 [N]; W4 [N][K/32] row-major.
+ * So packed_w is exactly N*K*bits/8 bytes. scales: W8/W6/FP4 [N]; W4 [N][K/32] row-major.
  * zeros: W4 [N][K/32] row-major; otherwise unused (may be NULL). fp16 values are passed
  * as uint16_t bit patterns.
  *
@@ -57,7 +64,7 @@
 extern "C" {
 #endif
 
-typedef enum { WQ_FMT_F16 = 0, WQ_FMT_W8 = 1, WQ_FMT_W4G32 = 2, WQ_FMT_W6E3M2 = 3 } wq_fmt;
+typedef enum { WQ_FMT_F16 = 0, WQ_FMT_W8 = 1, WQ_FMT_W4G32 = 2, WQ_FMT_W6E3M2 = 3, WQ_FMT_W4E2M1 = 4 } wq_fmt;
 
 typedef enum {
   WQ_OK = 0,
@@ -91,9 +98,10 @@ size_t wq_zeros_bytes(int fmt, int64_t N, int64_t K);
 int wq_pack_int8(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
 int wq_pack_int4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales, uint16_t* zeros);
 int wq_pack_fp6(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
+int wq_pack_fp4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
 
 /* Inverse of the packers' layout step, on the host: packed -> logical codes [N,K]
- * (int8 for W8; 0..15 for W4; 0..63 for W6, one byte each; uint16 fp16 bits for F16) and
+ * (int8 for W8; 0..15 for W4 and FP4; 0..63 for W6, one byte each; uint16 fp16 bits for F16) and
  * a copy of the metadata in logical order (scales_out/zeros_out may be NULL to skip).
  * A test hook. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT. */
 int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,

@@ -38,6 +38,9 @@ def pack_with_library(fmt, w):
     if fmt == wq.FMT_W6E3M2:
         p, s = wq.wq_pack_fp6(w)
         return p, s, None
+    if fmt == wq.FMT_W4E2M1:
+        p, s = wq.wq_pack_fp4(w)
+        return p, s, None
     if fmt == wq.FMT_F16:
         return np.asarray(w, dtype=np.float32).astype(np.float16).view(np.uint8).reshape(-1), None, None
     raise ValueError(fmt)

@@ -36,7 +36,7 @@ def test_version_and_status_strings():
         assert wq.wq_status_string(s) and wq.wq_status_string(s) != "unknown status"
 
 
-@pytest.mark.parametrize("fmt", [wq.FMT_F16, wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2])
+@pytest.mark.parametrize("fmt", [wq.FMT_F16, wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1])
 @pytest.mark.parametrize("n,k", [(1, 32), (7, 64), (33, 96), (4096, 11008)])
 def test_sizes_match_oracle(fmt, n, k):
     assert wq.wq_packed_bytes(fmt, n, k) == oracle.packed_bytes(fmt, n, k)
@@ -45,7 +45,7 @@ def test_sizes_match_oracle(fmt, n, k):
 
 
 def test_sizes_reject_bad_shapes():
-    for fmt in range(4):
+    for fmt in range(5):
         assert wq.wq_packed_bytes(fmt, 4, 48) == 0
         assert wq.wq_packed_bytes(fmt, 0, 64) == 0
         assert wq.wq_packed_bytes(fmt, 4, 0) == 0
@@ -77,13 +77,18 @@ def _exact_ties(fmt):
         r = np.zeros(64, dtype=np.float32); r[0] = 28.0
         r[1:12] = [1.875, 0.03125, 0.09375, 26.0, -26.0, 5.5, -0.0, -0.01, 3.25, 0.40625, 14.999]
         rows.append(r)
+    if fmt == wq.FMT_W4E2M1:
+        # s = 1: midpoints between neighbouring e2m1 values, both signs, and past-max values
+        r = np.zeros(64, dtype=np.float32); r[0] = 6.0
+        r[1:14] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -1.75, -5.0, -0.0, 0.2499, 5.0001]
+        rows.append(r)
     if fmt == wq.FMT_W4G32:
         r = np.zeros(64, dtype=np.float32); r[0] = -7.5; r[1] = 7.5; r[2:6] = [0.5, 1.5, -0.5, 2.5]   # s = 1, z = 8 (7.5 -> even)
         rows.append(r)
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2])
+@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1])
 @pytest.mark.parametrize("n,k,seed", [(8, 64, 0), (9, 96, 1), (33, 128, 2), (300, 4096, 3)])
 def test_pack_bit_identical_to_oracle(fmt, n, k, seed):
     w = _adversarial(n, k, seed)
@@ -93,8 +98,11 @@ def test_pack_bit_identical_to_oracle(fmt, n, k, seed):
         z = None
     elif fmt == wq.FMT_W4G32:
         packed, s, z = wq.wq_pack_int4(w)
-    else:
+    elif fmt == wq.FMT_W6E3M2:
         packed, s = wq.wq_pack_fp6(w)
+        z = None
+    else:
+        packed, s = wq.wq_pack_fp4(w)
         z = None
     assert np.array_equal(packed, packed_o)
     assert np.array_equal(s, s_o.reshape(-1))
@@ -105,11 +113,12 @@ def test_pack_bit_identical_to_oracle(fmt, n, k, seed):
     assert np.array_equal(s2, s)
 
 
-@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2])
+@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1])
 def test_pack_exact_ties_identical_to_oracle(fmt):
     w = _exact_ties(fmt)
     packed_o, s_o, z_o, _ = oracle.quantize_and_pack(fmt, w)
-    fn = {wq.FMT_W8: wq.wq_pack_int8, wq.FMT_W4G32: wq.wq_pack_int4, wq.FMT_W6E3M2: wq.wq_pack_fp6}[fmt]
+    fn = {wq.FMT_W8: wq.wq_pack_int8, wq.FMT_W4G32: wq.wq_pack_int4, wq.FMT_W6E3M2: wq.wq_pack_fp6,
+          wq.FMT_W4E2M1: wq.wq_pack_fp4}[fmt]
     out = fn(w)
     assert np.array_equal(out[0], packed_o)
     assert np.array_equal(out[1], s_o.reshape(-1))
@@ -138,6 +147,7 @@ def test_unpack_f16_and_round_trip_of_oracle_packing():
     for fmt, codes in ((wq.FMT_W8, rng.integers(-127, 128, (3, 96)).astype(np.int8)),
                        (wq.FMT_W4G32, rng.integers(0, 16, (3, 96)).astype(np.uint8)),
                        (wq.FMT_W6E3M2, rng.integers(0, 64, (3, 96)).astype(np.uint8)),
+                       (wq.FMT_W4E2M1, rng.integers(0, 16, (3, 96)).astype(np.uint8)),
                        (wq.FMT_F16, rng.integers(0, 65536, (3, 96)).astype(np.uint16))):
         packed = oracle.pack_scalar(fmt, codes)
         got, _, _ = wq.wq_unpack(fmt, packed, np.zeros(9, np.uint16), np.zeros(9, np.uint16), 3, 96)

@@ -10,6 +10,7 @@
 //   int4  per 32 along K: s = fp16((hi - lo) / 15), z = clamp(rint(-lo/s), 0, 15),
 //                        q = clamp(rint(w/s) + z, 0, 15), lo/hi widened to include 0
 //   fp6   per row:       s = fp16(max|w| / 28),       code = e3m2 nearest to w/s
+//   fp4   per row:       s = fp16(max|w| / 6),        code = e2m1 nearest to w/s
 // Every quotient is one IEEE float64 operation; every rounding is to nearest even.
 
 #include "wq_internal.h"
@@ -75,6 +76,23 @@ uint8_t e3m2_encode(double t) {
   return sign | static_cast<uint8_t>(code);
 }
 
+// e2m1 code of a finite float64 t, by the same rules as e3m2_encode (sign kept, ties to the
+// even code, saturating at 6). Below 1 the values are multiples of 1/2 (codes 0..2, code 2
+// being 1); from 1 up, exponent E in [0, 2] and one mantissa bit.
+uint8_t e2m1_encode(double t) {
+  const uint8_t sign = std::signbit(t) ? 0x8 : 0;
+  const double a = std::fabs(t);
+  if (a >= 6.0) return sign | 7;
+  if (a < 1.0) return sign | static_cast<uint8_t>(std::nearbyint(a * 2.0));   // exact product; 0..2
+  int e2 = 0;
+  (void)std::frexp(a, &e2);
+  const int E = e2 - 1;                                                 // 0 .. 2
+  const double m = std::nearbyint((std::ldexp(a, -E) - 1.0) * 2.0);     // 0..2, ties to even
+  int code = 2 * (E + 1) + static_cast<int>(m);                         // m == 2 carries into the next binade
+  if (code > 7) code = 7;
+  return sign | static_cast<uint8_t>(code);
+}
+
 namespace {
 
 bool shape_ok(int64_t N, int64_t K) { return N >= 1 && K >= 32 && K % 32 == 0; }
@@ -85,6 +103,7 @@ int fmt_bits(int fmt) {
     case WQ_FMT_W8: return 8;
     case WQ_FMT_W4G32: return 4;
     case WQ_FMT_W6E3M2: return 6;
+    case WQ_FMT_W4E2M1: return 4;
     default: return 0;
   }
 }
@@ -287,6 +306,31 @@ int wq_pack_fp6(const float* w, int64_t N, int64_t K, void* packed, uint16_t* sc
   });
 }
 
+int wq_pack_fp4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales) {
+  if (!w || !packed || !scales || N < 0 || K < 0) return WQ_ERR_ARG;
+  if (!shape_ok(N, K)) return WQ_ERR_SHAPE;
+  uint8_t* out = static_cast<uint8_t*>(packed);
+  return parallel_rows(N, K, [&](int64_t r0, int64_t r1) {
+    for (int64_t r = r0; r < r1; ++r) {
+      if (check_weights(w, K, r)) return static_cast<int>(WQ_ERR_NONFINITE);
+      const float* row = w + r * K;
+      float amax = 0.0f;
+      for (int64_t k = 0; k < K; ++k) amax = std::max(amax, std::fabs(row[k]));
+      const uint16_t sb = f64_to_f16_bits(static_cast<double>(amax) / 6.0);
+      if ((sb & 0x7FFF) == 0x7C00) return static_cast<int>(WQ_ERR_RANGE);
+      const double s = f16_bits_to_f64(sb);
+      scales[r] = sb;
+      // byte p of the row holds code 2p in its low nibble and code 2p+1 in its high nibble
+      for (int64_t k = 0; k < K; k += 2) {
+        const uint8_t lo = s > 0 ? e2m1_encode(static_cast<double>(row[k]) / s) : 0;
+        const uint8_t hi = s > 0 ? e2m1_encode(static_cast<double>(row[k + 1]) / s) : 0;
+        out[(r * K + k) / 2] = static_cast<uint8_t>(lo | (hi << 4));
+      }
+    }
+    return static_cast<int>(WQ_OK);
+  });
+}
+
 int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,
               void* codes, uint16_t* scales_out, uint16_t* zeros_out) {
   if (!fmt_bits(fmt)) return WQ_ERR_FMT;
@@ -328,6 +372,12 @@ int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_
           o[r * K + 32 * u + j] = static_cast<uint8_t>(v);
         }
       }
+  } else if (fmt == WQ_FMT_W4E2M1) {
+    uint8_t* o = static_cast<uint8_t*>(codes);
+    for (int64_t i = 0; i < N * K / 2; ++i) {
+      o[2 * i] = in[i] & 15;
+      o[2 * i + 1] = in[i] >> 4;
+    }
   } else {
     std::memcpy(codes, packed, static_cast<size_t>(N) * K * 2);
   }

@@ -11,8 +11,8 @@ import os
 
 import numpy as np
 
-FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2 = 0, 1, 2, 3
-FMT_NAMES = {"f16": FMT_F16, "w8": FMT_W8, "w4g32": FMT_W4G32, "w6e3m2": FMT_W6E3M2}
+FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1 = 0, 1, 2, 3, 4
+FMT_NAMES = {"f16": FMT_F16, "w8": FMT_W8, "w4g32": FMT_W4G32, "w6e3m2": FMT_W6E3M2, "w4e2m1": FMT_W4E2M1}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwq.so")
@@ -51,6 +51,7 @@ def lib():
         L.wq_pack_int8.argtypes = [_p, _i64, _i64, _p, _p]
         L.wq_pack_int4.argtypes = [_p, _i64, _i64, _p, _p, _p]
         L.wq_pack_fp6.argtypes = [_p, _i64, _i64, _p, _p]
+        L.wq_pack_fp4.argtypes = [_p, _i64, _i64, _p, _p]
         L.wq_unpack.argtypes = [ctypes.c_int, _p, _p, _p, _i64, _i64, _p, _p, _p]
         L.wq_dequant.argtypes = [ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _p]
         L.wq_linear.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, ctypes.c_int, _p]
@@ -60,7 +61,7 @@ def lib():
         L.wq_linear_kernel_name.argtypes = [ctypes.c_int, _i64, _i64, _i64]
         L.wq_linear_grouped_kernel_name.restype = ctypes.c_char_p
         L.wq_linear_grouped_kernel_name.argtypes = [ctypes.c_int, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.c_int]
-        for name in ("wq_pack_int8", "wq_pack_int4", "wq_pack_fp6", "wq_unpack", "wq_dequant", "wq_linear"):
+        for name in ("wq_pack_int8", "wq_pack_int4", "wq_pack_fp6", "wq_pack_fp4", "wq_unpack", "wq_dequant", "wq_linear"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -159,9 +160,19 @@ def wq_pack_fp6(w):
     return packed, scales
 
 
+def wq_pack_fp4(w):
+    """fp32 W [N,K] -> (packed uint8, scales uint16 [N])."""
+    w = _w_host(w)
+    n, k = w.shape
+    packed, scales, _ = _alloc(FMT_W4E2M1, n, k)
+    _check(lib().wq_pack_fp4(_host_ptr(w), n, k, _host_ptr(packed), _host_ptr(scales)), "wq_pack_fp4")
+    return packed, scales
+
+
 def wq_unpack(fmt, packed, scales, zeros, n, k):
     """packed (host) -> (logical codes [N,K], scales copy, zeros copy)."""
-    dtype = {FMT_W8: np.int8, FMT_W4G32: np.uint8, FMT_W6E3M2: np.uint8, FMT_F16: np.uint16}.get(fmt, np.uint8)
+    dtype = {FMT_W8: np.int8, FMT_W4G32: np.uint8, FMT_W6E3M2: np.uint8, FMT_W4E2M1: np.uint8,
+             FMT_F16: np.uint16}.get(fmt, np.uint8)
     codes = np.empty((n, k), dtype=dtype)
     s_out = np.empty(max(wq_scales_bytes(fmt, n, k) // 2, 1), dtype=np.uint16)
     z_out = np.empty(max(wq_zeros_bytes(fmt, n, k) // 2, 1), dtype=np.uint16)
