@@ -44,7 +44,7 @@ from weight_only_quantized_dequant_amd import inputs, wq  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "weight-stream HBM GB/s (% of peak) for W8/W6/W4-A16 linear, M=1..16"
-FMT_OF = {"w8": wq.FMT_W8, "w4g32": wq.FMT_W4G32, "w6e3m2": wq.FMT_W6E3M2, "f16": wq.FMT_F16}
+FMT_OF = {"w8": wq.FMT_W8, "w4g32": wq.FMT_W4G32, "w6e3m2": wq.FMT_W6E3M2, "w4e2m1": wq.FMT_W4E2M1, "f16": wq.FMT_F16}
 ROTATE_BYTES = 1 << 30
 
 
@@ -98,6 +98,19 @@ def metadata_bytes(fmt, n, k):
     return wq.wq_scales_bytes(fmt, n, k) + wq.wq_zeros_bytes(fmt, n, k)
 
 
+def pack(fmt, w):
+    """Quantize + pack fp32 W with libwq's host packers: (packed, scales or None, zeros or None)."""
+    if fmt == wq.FMT_W8:
+        return wq.wq_pack_int8(w) + (None,)
+    if fmt == wq.FMT_W4G32:
+        return wq.wq_pack_int4(w)
+    if fmt == wq.FMT_W6E3M2:
+        return wq.wq_pack_fp6(w) + (None,)
+    if fmt == wq.FMT_W4E2M1:
+        return wq.wq_pack_fp4(w) + (None,)
+    return w.astype(np.float16).view(np.uint8).reshape(-1), None, None
+
+
 class Linear:
     """One linear: packed weights (R rotation copies on the device) and its x, y buffers."""
 
@@ -105,14 +118,7 @@ class Linear:
         self.fmt = fmt
         self.n, self.k = w.shape
         self.m = x_bits.shape[0]
-        if fmt == wq.FMT_W8:
-            p, s = wq.wq_pack_int8(w); z = None
-        elif fmt == wq.FMT_W4G32:
-            p, s, z = wq.wq_pack_int4(w)
-        elif fmt == wq.FMT_W6E3M2:
-            p, s = wq.wq_pack_fp6(w); z = None
-        else:
-            p, s, z = w.astype(np.float16).view(np.uint8).reshape(-1), None, None
+        p, s, z = pack(fmt, w)
         dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).to("cuda")
         p0, s0, z0 = dev(p), dev(s), dev(z)
         self.copies = [(p0, s0, z0)] + [(p0.clone(), None if s0 is None else s0.clone(), None if z0 is None else z0.clone())
@@ -246,7 +252,7 @@ def cpu_baseline(fmt, linears_host, seconds):
 
 SWEEPS = {
     # name: (layer shapes, layers, formats, Ms)
-    "llama2_7b": (inputs.LLAMA2_7B_LINEARS, 32, ["f16", "w8", "w4g32", "w6e3m2"], [1]),
+    "llama2_7b": (inputs.LLAMA2_7B_LINEARS, 32, ["f16", "w8", "w4g32", "w6e3m2", "w4e2m1"], [1]),
     "llama70b_w6": (inputs.LLAMA_70B_LINEARS, 80, ["w6e3m2", "f16"], [1, 2, 4, 8, 16]),
 }
 
@@ -273,14 +279,7 @@ def run_sweep(args, torch):
         fmt = FMT_OF[fname]
         proto = {}
         for (n, k), (w, _) in draws.items():
-            if fmt == wq.FMT_W8:
-                p, sc = wq.wq_pack_int8(w); z = None
-            elif fmt == wq.FMT_W4G32:
-                p, sc, z = wq.wq_pack_int4(w)
-            elif fmt == wq.FMT_W6E3M2:
-                p, sc = wq.wq_pack_fp6(w); z = None
-            else:
-                p, sc, z = w.astype(np.float16).view(np.uint8).reshape(-1), None, None
+            p, sc, z = pack(fmt, w)
             dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).to("cuda")
             proto[(n, k)] = (dev(p), dev(sc), dev(z))
         # one copy of every linear of every layer

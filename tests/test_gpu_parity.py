@@ -17,8 +17,8 @@ from tests.gpu_util import DeviceWeights, check_linear, dev, host_bits, oracle_r
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_F16]
-FMT_ID = {wq.FMT_W8: "w8", wq.FMT_W4G32: "w4", wq.FMT_W6E3M2: "w6", wq.FMT_F16: "f16"}
+FMTS = [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_F16]
+FMT_ID = {wq.FMT_W8: "w8", wq.FMT_W4G32: "w4", wq.FMT_W6E3M2: "w6", wq.FMT_W4E2M1: "fp4", wq.FMT_F16: "f16"}
 
 
 def _weights(n, k, seed, adversarial=True):
@@ -48,18 +48,21 @@ def test_dequant_bit_exact(fmt, n, k):
     assert np.array_equal(got, want), "%d of %d differ" % (int((got != want).sum()), got.size)
 
 
-def test_dequant_w6_all_codes():
-    # every one of the 64 codes, at scale 1 and at a non-power-of-two scale
+@pytest.mark.parametrize("fmt,ncodes", [(wq.FMT_W6E3M2, 64), (wq.FMT_W4E2M1, 16)], ids=["w6", "fp4"])
+def test_dequant_all_codes(fmt, ncodes):
+    # every code in every position of a unit (codes run 0, 1, ..., shifted by one per row), at
+    # scale 1, at a non-power-of-two scale and at a subnormal scale
     torch = torch_cuda()
-    codes = np.tile(np.arange(64, dtype=np.uint8), 2).reshape(2, 64)
-    packed = oracle.pack_vectorized(wq.FMT_W6E3M2, codes)
-    for s in (0x3C00, 0x2E66):
-        sc = np.array([s, s], dtype=np.uint16)
-        out = torch.empty((2, 64), dtype=torch.int16, device="cuda:0")
-        wq.wq_dequant(wq.FMT_W6E3M2, dev(packed), dev(sc), None, out, 2, 64)
+    rows = ncodes
+    codes = ((np.arange(64)[None, :] + np.arange(rows)[:, None]) % ncodes).astype(np.uint8)
+    packed = oracle.pack_vectorized(fmt, codes)
+    for s in (0x3C00, 0x2E66, 0x0003):
+        sc = np.full(rows, s, dtype=np.uint16)
+        out = torch.empty((rows, 64), dtype=torch.int16, device="cuda:0")
+        wq.wq_dequant(fmt, dev(packed), dev(sc), None, out, rows, 64)
         torch.cuda.synchronize()
-        want = oracle.dequant_fp16(wq.FMT_W6E3M2, codes, sc)
-        assert np.array_equal(host_bits(out), want)
+        want = oracle.dequant_fp16(fmt, codes, sc)
+        assert np.array_equal(host_bits(out), want), hex(s)
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
@@ -127,7 +130,7 @@ def test_linear_zero_x_and_repeatability(fmt):
 def test_linear_rows_of_a_batch_match_single_rows():
     n, k = 48, 4096
     w = _weights(n, k, 21)
-    for fmt in (wq.FMT_W4G32, wq.FMT_W6E3M2):
+    for fmt in (wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1):
         dw = DeviceWeights(fmt, w)
         _, x = inputs.small_case(5, 1, k, 16)
         wd = oracle_rows(fmt, w)[0]
@@ -156,6 +159,7 @@ FULL = [
     ("llama7b_w4g32_linears", wq.FMT_W4G32),
     ("llama70b_w6e3m2_linears", wq.FMT_W6E3M2),
     ("llama70b_w6e3m2_tp8_shard", wq.FMT_W6E3M2),
+    ("llama7b_w4e2m1_linears", wq.FMT_W4E2M1),
 ]
 
 

@@ -9,7 +9,7 @@
 // parameter set the speed.
 //
 // gfx950 design:
-//  * Layout: row-major, 32-code units (32/16/24/64 bytes for W8/W4/W6/F16). Lane l of a
+//  * Layout: row-major, 32-code units (32/16/24/16/64 bytes for W8/W4/W6/FP4/F16). Lane l of a
 //    wave reads unit l of a 64-unit "chunk" of one row, so one wave-load covers 1-4 KB
 //    contiguously.
 //  * Decode in VGPRs, exact:
@@ -19,14 +19,16 @@
 //          v_pk_fma_f16 gives q-z.
 //      W6  the 192-bit unit goes through gfx950's v_cvt_scalef32_pk32_f16_bf6 at scale 1.0,
 //          which yields the 32 e3m2 values as exact fp16.
+//      FP4 each byte (two e2m1 codes) goes through gfx950's v_cvt_scalef32_pk_f16_fp4 at
+//          scale 1.0: two exact fp16 values per instruction.
 //  * M <= GEMV_MAX_M: VALU GEMV. v_dot2_f32_f16 accumulates in fp32, lanes run along K,
 //    and each row's sum finishes with a DPP + cross-row shuffle wave reduction; waves of a
 //    workgroup split K and add their partials through LDS in a fixed order.
 //  * Larger M: v_mfma_f32_16x16x32_f16. Lane (n = l%16, q = l/16) decodes a unit into the B
 //    fragment; the A fragment is x at the same K positions, since any permutation of K
-//    applied to both operands leaves the product unchanged. W6 and W4 (K % 256 == 0) read
-//    their weights row-contiguously into per-wave LDS first (lm_kernel); W8, F16 and the
-//    other W4 shapes load fragments straight from HBM (mfma_kernel).
+//    applied to both operands leaves the product unchanged. W6, FP4 and W4 (K % 256 == 0)
+//    read their weights row-contiguously into per-wave LDS first (lm_kernel); W8, F16 and
+//    the other W4 shapes load fragments straight from HBM (mfma_kernel).
 //  * A grouped call runs several linears in one launch with one of these kernel families.
 //  * No atomics anywhere, so every result is deterministic.
 #include <hip/hip_runtime.h>
@@ -63,10 +65,16 @@ template <int FMT> struct Raw;
 template <> struct Raw<WQ_FMT_W8> { uint4 a, b; };
 template <> struct Raw<WQ_FMT_W4G32> { uint4 a; };
 template <> struct Raw<WQ_FMT_W6E3M2> { uint4 a; uint2 b; };
+template <> struct Raw<WQ_FMT_W4E2M1> { uint4 a; };
 template <> struct Raw<WQ_FMT_F16> { uint4 a, b, c, d; };
 
 template <int FMT> constexpr int unit_bytes() {
-  return FMT == WQ_FMT_W8 ? 32 : FMT == WQ_FMT_W4G32 ? 16 : FMT == WQ_FMT_W6E3M2 ? 24 : 64;
+  return FMT == WQ_FMT_W8 ? 32 : FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W4E2M1 ? 16 : FMT == WQ_FMT_W6E3M2 ? 24 : 64;
+}
+
+// Formats with one fp16 scale per output row, applied to the finished fp32 sum.
+template <int FMT> constexpr bool row_scaled() {
+  return FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2 || FMT == WQ_FMT_W4E2M1;
 }
 
 // Byte offsets, from the start of row n, of the two plane slices of W6 unit u (U units per row).
@@ -84,7 +92,7 @@ __device__ __forceinline__ void load_unit(const uint8_t* __restrict__ w, int n, 
   if constexpr (FMT == WQ_FMT_W8) {
     const uint4* q = reinterpret_cast<const uint4*>(row + (size_t)u * UB);
     r.a = q[0]; r.b = q[1];
-  } else if constexpr (FMT == WQ_FMT_W4G32) {
+  } else if constexpr (FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W4E2M1) {
     r.a = *reinterpret_cast<const uint4*>(row + (size_t)u * UB);
   } else if constexpr (FMT == WQ_FMT_W6E3M2) {
     uint32_t lo, hi;
@@ -99,7 +107,7 @@ __device__ __forceinline__ void load_unit(const uint8_t* __restrict__ w, int n, 
 
 // ---------------------------------------------------------------- exact decode to fp16 pairs
 // out[p] holds the values of codes 2p and 2p+1 of the unit:
-//   W8: q      W4: q - z      W6: e3m2(code)      F16: the weights
+//   W8: q      W4: q - z      W6: e3m2(code)      FP4: e2m1(code)      F16: the weights
 // zc1 = -(1024 + z), zc2 = -(64 + z) as fp16 pairs (W4 only; exact small integers).
 __device__ __forceinline__ void decode_w8_word(uint32_t d, h2& lo, h2& hi) {
   const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
@@ -114,6 +122,15 @@ __device__ __forceinline__ void decode_w4_word(uint32_t d, h2 zc1, h2 zc2, h2& o
   o1 = __builtin_elementwise_fma(as_h2((d & 0x00F000F0u) | 0x64006400u), sixteenth, zc2);   // 1024+16q
   o2 = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + zc1;
   o3 = __builtin_elementwise_fma(as_h2((d8 & 0x00F000F0u) | 0x64006400u), sixteenth, zc2);
+}
+
+// Byte b of d holds codes 2b (low nibble) and 2b+1 (high nibble); the convert takes the
+// byte index as an immediate and returns them in that order.
+__device__ __forceinline__ void decode_fp4_word(uint32_t d, h2& o0, h2& o1, h2& o2, h2& o3) {
+  o0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0);
+  o1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1);
+  o2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2);
+  o3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3);
 }
 
 template <int FMT>
@@ -132,6 +149,10 @@ __device__ __forceinline__ void decode(const Raw<FMT>& r, h2 zc1, h2 zc2, h2 (&o
     const h32 h = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(v, 1.0f);
 #pragma unroll
     for (int p = 0; p < 16; ++p) { out[p][0] = h[2 * p]; out[p][1] = h[2 * p + 1]; }
+  } else if constexpr (FMT == WQ_FMT_W4E2M1) {
+    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) decode_fp4_word(w[i], out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
   } else {
     const uint32_t w[16] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w,
                             r.c.x, r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w};
@@ -197,7 +218,7 @@ __device__ __forceinline__ uint2 ld_nt8(const uint8_t* p) {
 // and reads its weight bytes with one 16-byte load (W6: a 16-byte and an 8-byte load),
 // so every load instruction of a wave reads one contiguous block:
 //   W4: SEG = 32 (one unit = one zero-point group)   W6: SEG = 32 (one unit, two planes)
-//   W8: SEG = 16 (half a unit)                       F16: SEG = 8
+//   FP4: SEG = 32 (one unit)    W8: SEG = 16 (half a unit)    F16: SEG = 8
 // A wave covers a chunk of 64 segments of B rows. A workgroup of 4 waves holds 4 / WK row
 // blocks of B rows; the WK waves of a block take the chunks c = wave, wave + WK, ... and
 // double-buffer them: while chunk i is decoded, the loads of chunk i+1 (x first, then the
@@ -352,6 +373,10 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
         const h32 h = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(u, 1.0f);
 #pragma unroll
         for (int p = 0; p < 16; ++p) { v[p][0] = h[2 * p]; v[p][1] = h[2 * p + 1]; }
+      } else if constexpr (FMT == WQ_FMT_W4E2M1) {
+        const uint32_t wd[4] = {st.w[b].a.x, st.w[b].a.y, st.w[b].a.z, st.w[b].a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) decode_fp4_word(wd[i], v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
       } else {
         v[0] = as_h2(st.w[b].a.x); v[1] = as_h2(st.w[b].a.y); v[2] = as_h2(st.w[b].a.z); v[3] = as_h2(st.w[b].a.w);
       }
@@ -419,7 +444,7 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const 
         float t = wave_sum_to_lane63(acc[b][m]);
         const int n = row0 + b;
         if (lane == 63 && n < N) {
-          if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) t *= f16_to_f32(scales[n]);
+          if constexpr (row_scaled<FMT>()) t *= f16_to_f32(scales[n]);
           y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)t);
         }
       }
@@ -439,7 +464,7 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const 
     float t = 0.0f;
     for (int i = 0; i < WK; ++i) t += red[sub * WK + i][lane];   // fixed order: deterministic
     if (n < N) {
-      if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) t *= f16_to_f32(scales[n]);
+      if constexpr (row_scaled<FMT>()) t *= f16_to_f32(scales[n]);
       y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)t);
     }
   }
@@ -510,7 +535,7 @@ __device__ __forceinline__ void mfma_load(MfmaStage<FMT, RB>& st, const uint16_t
     const int nb = min(n0 + 16 * r, N - 1);                        // wave-uniform
     const uint32_t nn = (uint32_t)(min(n0 + 16 * r + nl, N - 1) - nb);   // 0..15
     const uint8_t* rowb = w + uniform((size_t)nb * row_bytes);
-    static_assert(FMT != WQ_FMT_W6E3M2, "W6 on the matrix cores takes lm_kernel");
+    static_assert(FMT != WQ_FMT_W6E3M2 && FMT != WQ_FMT_W4E2M1, "W6 and FP4 on the matrix cores take lm_kernel");
     const uint8_t* p = rowb + nn * row_bytes + UB * u;
     st.w[r].a = ld_nt16(p);
     if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_F16) st.w[r].b = ld_nt16(p + 16);
@@ -599,7 +624,7 @@ __device__ __forceinline__ void mfma_body(const uint16_t* __restrict__ x, const 
     const int n = n0 + 16 * r + nl;
     if (n >= N) return;
     float sc = 1.0f;
-    if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) sc = f16_to_f32(scales[n]);
+    if constexpr (row_scaled<FMT>()) sc = f16_to_f32(scales[n]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * q + i;
@@ -644,7 +669,7 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_grouped_kernel(const
                      g.WK[j]);
 }
 
-// ---------------------------------------------------------------- W4 / W6 on the matrix cores through LDS
+// ---------------------------------------------------------------- W4 / W6 / FP4 on the matrix cores through LDS
 // The fragment-shaped loads of mfma_kernel read, per wave instruction, 16 rows x 16 bytes
 // (W4) or 16 rows x 64 + 32 bytes (W6), a pattern that HBM serves far below the rate of
 // contiguous reads (16-byte row pieces at about a fifth). Here each wave reads its rows
@@ -655,15 +680,17 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_grouped_kernel(const
 //       32 groups) come straight into registers, lane (n, q) holding groups 8q..8q+7 of
 //       row n, which are exactly the groups its fragments need.
 //   W6: the lo slices as 2 rows x 512 B per instruction, the hi slices as 4 rows x 256 B.
+//   FP4: as W4 (16-byte units), with no metadata.
 // LDS image of one 16-row block (XOR swizzles put the 16 rows of a fragment read in
 // different banks):
-//   W4: unit u (0..31) of row r at 512 r + 16 (u ^ r)                              8 KB
+//   W4, FP4: unit u (0..31) of row r at 512 r + 16 (u ^ r)                         8 KB
 //   W6: lo slice of unit u at 512 r + 16 (u ^ r), hi slice at 8192 + 256 r + 8 (u ^ (2r & 31))   12 KB
 // K tile j (0..7) of a stage is 4 units, one per lane quad q: unit 8q + j. Its x fragments
 // sit in a register ring of lm_xring slots and are loaded lm_xring - 1 tiles ahead (W4 keeps
 // the ring at 2 so that its two-block kernel fits 256 VGPRs: two waves per SIMD).
-template <int FMT> constexpr int lm_block() { return FMT == WQ_FMT_W4G32 ? 16 * 512 : 16 * 512 + 16 * 256; }
-template <int FMT> constexpr int lm_loads() { return FMT == WQ_FMT_W4G32 ? 8 : 12; }
+template <int FMT> constexpr bool lm_w6() { return FMT == WQ_FMT_W6E3M2; }   // two plane slices per unit
+template <int FMT> constexpr int lm_block() { return lm_w6<FMT>() ? 16 * 512 + 16 * 256 : 16 * 512; }
+template <int FMT> constexpr int lm_loads() { return lm_w6<FMT>() ? 12 : 8; }
 template <int FMT, int MT> constexpr int lm_xring() { return FMT == WQ_FMT_W4G32 || MT > 1 ? 2 : 4; }
 constexpr int LM_MAX_MT = 4;   // 16-row tiles of x per launch (M up to 64 reads the weights once)
 constexpr int LM_WAVES = 4;   // waves per workgroup
@@ -685,13 +712,15 @@ __device__ __forceinline__ void lm_load(LmStage<FMT, RB>& st, const uint8_t* __r
   for (int r = 0; r < RB; ++r) {
     const int nb = min(n0 + 16 * r, N - 1);
     const uint8_t* rowb = w + uniform((size_t)nb * row_bytes);
-    if constexpr (FMT == WQ_FMT_W4G32) {
+    if constexpr (!lm_w6<FMT>()) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {   // lane l -> row 2i + l/32, unit l%32
         const uint32_t nn = (uint32_t)(min(n0 + 16 * r + 2 * i + (lane >> 5), N - 1) - nb);
         const uint32_t j = (uint32_t)min(32 * h + (lane & 31), U - 1);   // past the row end: a valid unit, masked later
         st.v[r][i] = ld_nt16(rowb + nn * row_bytes + 16u * j);
       }
+    }
+    if constexpr (FMT == WQ_FMT_W4G32) {
       // lane (n, q): groups 32h + 8q .. +7 of row n (U is a multiple of 8, so a group of 8 lies
       // wholly inside the row or wholly past its end; one past the end reads the row's last 8)
       const uint32_t nn = (uint32_t)(min(n0 + 16 * r + (lane & 15), N - 1) - nb);
@@ -700,7 +729,8 @@ __device__ __forceinline__ void lm_load(LmStage<FMT, RB>& st, const uint8_t* __r
       const uint32_t mo = 2u * (nn * (uint32_t)U + (uint32_t)g0);
       st.s[r] = ld_nt16(reinterpret_cast<const uint8_t*>(scales) + mb + mo);
       st.z[r] = ld_nt16(reinterpret_cast<const uint8_t*>(zeros) + mb + mo);
-    } else {
+    }
+    if constexpr (lm_w6<FMT>()) {
       const int c = h >> 1, half = h & 1;                  // 64-unit chunk and which half of it
       const int uc = min(64, U - 64 * c);                   // units in the chunk
       const uint32_t cbase = 64u * 24 * c;
@@ -733,7 +763,7 @@ __device__ __forceinline__ void lm_store(const LmStage<FMT, RB>& st, uint8_t* ld
       const int rr = 2 * i + (lane >> 5), u = lane & 31;
       *reinterpret_cast<uint4*>(base + 512 * rr + 16 * (u ^ rr)) = st.v[r][i];
     }
-    if constexpr (FMT == WQ_FMT_W6E3M2) {
+    if constexpr (lm_w6<FMT>()) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 4 * i + (lane >> 4), u = 2 * (lane & 15), sw = (2 * rr) & 31;
@@ -819,7 +849,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
         raw.a = *reinterpret_cast<const uint4*>(base + 512 * nl + 16 * (u ^ nl));
         if constexpr (FMT == WQ_FMT_W6E3M2) {
           raw.b = *reinterpret_cast<const uint2*>(base + 8192 + 256 * nl + 8 * (u ^ ((2 * nl) & 31)));
-        } else {
+        } else if constexpr (FMT == WQ_FMT_W4G32) {
           w4_consts(half_of(cz[r], j), zc1, zc2);
         }
         h2 wv[16];
@@ -859,7 +889,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
   for (int r = 0; r < RB; ++r) {
     if (r % WK != kw) continue;
     const int n = n0 + 16 * r + nl;
-    const float sc = FMT == WQ_FMT_W6E3M2 && n < N ? f16_to_f32(scales[n]) : 1.0f;
+    const float sc = row_scaled<FMT>() && n < N ? f16_to_f32(scales[n]) : 1.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f4 t = red[(((sub * WK) * RB + r) * MT + mt) * 64 + lane];
@@ -911,7 +941,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   if constexpr (FMT == WQ_FMT_W4G32) {
     w4_consts(zeros[gid], zc1, zc2);
     s = f16_to_f32(scales[gid]);
-  } else if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2) {
+  } else if constexpr (row_scaled<FMT>()) {
     s = f16_to_f32(scales[n]);
   }
   h2 wv[16];
@@ -933,7 +963,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 
 // ---------------------------------------------------------------- host-side planning
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
-bool valid_fmt(int fmt) { return fmt >= WQ_FMT_F16 && fmt <= WQ_FMT_W6E3M2; }
+bool valid_fmt(int fmt) { return fmt >= WQ_FMT_F16 && fmt <= WQ_FMT_W4E2M1; }
 
 struct GemvPlan {
   int B;      // rows per wave
@@ -950,7 +980,7 @@ struct GemvPlan {
 int gemv_waves_for(int fmt, int64_t N, int64_t K, int B) {
   const int64_t L = fmt == WQ_FMT_W8 ? 16 : fmt == WQ_FMT_F16 ? 8 : 32;
   const int64_t C = (K / L + 63) / 64, blocks = (N + B - 1) / B;
-  const int64_t target = fmt == WQ_FMT_W4G32 ? 1024 : 4096;
+  const int64_t target = fmt == WQ_FMT_W4G32 || fmt == WQ_FMT_W4E2M1 ? 1024 : 4096;
   static const int cand[] = {1, 2, 4};
   int WK = 1;
   for (int w : cand) {
@@ -1021,12 +1051,13 @@ struct LmPlan {
   int grid;   // workgroups
 };
 
-// The LDS-staged kernel serves W6 and W4 wherever the matrix cores run for them (W4 only when
-// K is a multiple of 256, so that a lane's 8 groups of metadata are one aligned 16-byte load),
-// and W4 at M = 4 from N*K = 2^24 on, where it beats the VALU GEMV.
+// The LDS-staged kernel serves W6, FP4 and W4 wherever the matrix cores run for them (W4 only
+// when K is a multiple of 256, so that a lane's 8 groups of metadata are one aligned 16-byte
+// load), and W4 and FP4 at M = 4 from N*K = 2^24 on, where it beats the VALU GEMV.
 bool use_lm(int fmt, int64_t M, int64_t N, int64_t K) {
   if (fmt == WQ_FMT_W6E3M2) return use_mfma(fmt, M, N);
-  if (fmt != WQ_FMT_W4G32 || K % 256) return false;
+  if (fmt == WQ_FMT_W4G32 && K % 256) return false;
+  if (fmt != WQ_FMT_W4G32 && fmt != WQ_FMT_W4E2M1) return false;
   return M > GEMV_MAX_M || (M == GEMV_MAX_M && N * K >= (int64_t(1) << 24));
 }
 
@@ -1051,11 +1082,11 @@ LmPlan plan_lm(int64_t N, int64_t K) {
 // 16-row tiles of x one LDS-staged launch takes (1, 2 or 4)
 int lm_tiles(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 
-// Rows of x per launch: 64 where the LDS-staged kernel serves the shape (W6; W4 with K a
-// multiple of 256), else 16. The kernels address x with 32-bit lane offsets (row * 2K + 64 u),
+// Rows of x per launch: 64 where the LDS-staged kernel serves the shape (W6, FP4; W4 with K
+// a multiple of 256), else 16. The kernels address x with 32-bit lane offsets (row * 2K + 64 u),
 // which hold 64 rows only while K <= 2^25; longer rows take 16-row slabs.
 int64_t slab_rows(int fmt, int64_t K) {
-  const bool lm = fmt == WQ_FMT_W6E3M2 || (fmt == WQ_FMT_W4G32 && K % 256 == 0);
+  const bool lm = fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W4E2M1 || (fmt == WQ_FMT_W4G32 && K % 256 == 0);
   return lm && K <= (int64_t(1) << 25) ? 16 * LM_MAX_MT : MFMA_M;
 }
 
@@ -1083,7 +1114,7 @@ void lm_launch(dim3 grid, size_t shm, hipStream_t s, const uint16_t* x, const ui
 template <int FMT>
 hipError_t launch_lm(int RB, int M, dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
                      const uint16_t* z, uint16_t* y, int N, int K, int WK, const GemvGroup* g) {
-  if constexpr (FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W6E3M2) {
+  if constexpr (FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W6E3M2 || FMT == WQ_FMT_W4E2M1) {
     const size_t shm = (size_t)LM_WAVES * RB * lm_block<FMT>();
     const int MT = lm_tiles(M);
     if (RB == 2) {
@@ -1116,8 +1147,8 @@ hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w,
       default: return launch_gemv_m<FMT, 4>(p, s, x, w, sc, z, y, N, K);
     }
   }
-  if constexpr (FMT == WQ_FMT_W6E3M2) {
-    return hipErrorInvalidValue;   // W6 on the matrix cores always takes lm_kernel (use_lm)
+  if constexpr (FMT == WQ_FMT_W6E3M2 || FMT == WQ_FMT_W4E2M1) {
+    return hipErrorInvalidValue;   // W6 and FP4 on the matrix cores always take lm_kernel (use_lm)
   } else {
     const MfmaPlan p = plan_mfma(FMT, N, K);
     const dim3 grid(p.grid), block(64 * p.WK);
@@ -1212,8 +1243,8 @@ int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, cons
 template <int FMT>
 hipError_t launch_grouped_mc(Family f, const GemvGroup& g, int M, int RB, int block_waves, int grid, hipStream_t s) {
   if (f == FAM_LM) return launch_lm<FMT>(RB, M, dim3(grid), s, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, &g);
-  if constexpr (FMT == WQ_FMT_W6E3M2) {
-    return hipErrorInvalidValue;   // W6 groups on the matrix cores are always FAM_LM
+  if constexpr (FMT == WQ_FMT_W6E3M2 || FMT == WQ_FMT_W4E2M1) {
+    return hipErrorInvalidValue;   // W6 and FP4 groups on the matrix cores are always FAM_LM
   } else {
     switch (RB) {
       case 4: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 4>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
@@ -1244,6 +1275,7 @@ int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, c
       case WQ_FMT_W8: e = launch_linear_fmt<WQ_FMT_W8>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
       case WQ_FMT_W4G32: e = launch_linear_fmt<WQ_FMT_W4G32>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
       case WQ_FMT_W6E3M2: e = launch_linear_fmt<WQ_FMT_W6E3M2>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
+      case WQ_FMT_W4E2M1: e = launch_linear_fmt<WQ_FMT_W4E2M1>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
       default: e = launch_linear_fmt<WQ_FMT_F16>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
     }
     if (e != hipSuccess) return WQ_ERR_DEVICE;
@@ -1269,6 +1301,7 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
     case WQ_FMT_W8: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_W8>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
     case WQ_FMT_W4G32: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_W4G32>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
     case WQ_FMT_W6E3M2: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_W6E3M2>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
+    case WQ_FMT_W4E2M1: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_W4E2M1>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
     default: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_F16>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
   }
   return hipGetLastError() == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
@@ -1331,6 +1364,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
       case WQ_FMT_W8: e = launch_grouped_fmt<WQ_FMT_W8>(g, (int)M, B, block_waves, grid, s); break;
       case WQ_FMT_W4G32: e = launch_grouped_fmt<WQ_FMT_W4G32>(g, (int)M, B, block_waves, grid, s); break;
       case WQ_FMT_W6E3M2: e = launch_grouped_fmt<WQ_FMT_W6E3M2>(g, (int)M, B, block_waves, grid, s); break;
+      case WQ_FMT_W4E2M1: e = launch_grouped_fmt<WQ_FMT_W4E2M1>(g, (int)M, B, block_waves, grid, s); break;
       default: e = launch_grouped_fmt<WQ_FMT_F16>(g, (int)M, B, block_waves, grid, s); break;
     }
   } else {
@@ -1338,6 +1372,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
       case WQ_FMT_W8: e = launch_grouped_mc<WQ_FMT_W8>(fam, g, (int)M, B, block_waves, grid, s); break;
       case WQ_FMT_W4G32: e = launch_grouped_mc<WQ_FMT_W4G32>(fam, g, (int)M, B, block_waves, grid, s); break;
       case WQ_FMT_W6E3M2: e = launch_grouped_mc<WQ_FMT_W6E3M2>(fam, g, (int)M, B, block_waves, grid, s); break;
+      case WQ_FMT_W4E2M1: e = launch_grouped_mc<WQ_FMT_W4E2M1>(fam, g, (int)M, B, block_waves, grid, s); break;
       default: e = launch_grouped_mc<WQ_FMT_F16>(fam, g, (int)M, B, block_waves, grid, s); break;
     }
   }

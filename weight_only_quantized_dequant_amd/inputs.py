@@ -32,10 +32,12 @@ WORKLOADS = {
     # split by output rows (column-parallel), o and down split along K (row-parallel)
     "llama70b_w6e3m2_tp8_shard": ("w6e3m2", [(1280, 8192), (8192, 1024), (3584, 8192), (3584, 8192), (8192, 3584)],
                                   [1, 4, 8, 16]),
+    # the Llama-7B linears again with FP4 e2m1 weights (a further bit width)
+    "llama7b_w4e2m1_linears": ("w4e2m1", [(4096, 4096), (11008, 4096), (4096, 11008)], [1, 4, 8, 16]),
 }
 # stream index of each workload, so that every workload draws from its own stream
 WORKLOAD_STREAM = {"w8_single_1024x1024": 0, "llama7b_w4g32_linears": 1, "llama70b_w6e3m2_linears": 2,
-                   "llama70b_w6e3m2_tp8_shard": 3}
+                   "llama70b_w6e3m2_tp8_shard": 3, "llama7b_w4e2m1_linears": 4}
 
 
 def rng_for(stream, linear):
