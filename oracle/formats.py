@@ -1,4 +1,4 @@
-"""Number formats: fp16 rounding, the FP6 e3m2 code and the FP4 e2m1 code.
+"""Number formats: fp16 and bfloat16 rounding, the FP6 e3m2 code and the FP4 e2m1 code.
 
 Test infrastructure only (see the package docstring for who may import it).
 
@@ -11,6 +11,10 @@ The same page says the kernel design serves weights of other bit widths as well,
 names none. FP4 is taken here as e2m1: 1 sign bit, 2 exponent bits with bias 1, 1
 mantissa bit, subnormals when the exponent field is 0, no infinities or NaNs, largest
 magnitude 6 (the eight magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+
+bfloat16 is the activation type the gpt-fast guide (www.jsqmd.com, section
+"量化技术深度解析") offers besides fp16: the 8-bit exponent of binary32 with 8
+significant bits (7 stored), rounded to nearest with ties to even.
 """
 
 import numpy as np
@@ -36,6 +40,37 @@ def fp16_from_bits(bits):
     """fp16 bit patterns (uint16) -> exact float64 values."""
     b = np.asarray(bits, dtype=np.uint16)
     return b.view(np.float16).astype(np.float64)
+
+
+BF16_MIN_EXP = -126          # smallest normal binade 2^-126; below it the spacing stays 2^-133
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def bf16_bits(values):
+    """Round float64 values to bfloat16 (round to nearest, ties to even) and return the bit patterns.
+
+    Written from the definition: a finite value in [2^e, 2^(e+1)) lies on a grid of
+    spacing 2^(e-7) (8 significant bits), and below 2^-126 on the subnormal grid of
+    spacing 2^-133. The value divided by its spacing is rounded to the nearest integer,
+    ties to even (an even multiple has an even last stored bit), and scaled back; both
+    steps are exact in float64. A result above the largest finite value becomes +-inf.
+    The sign of zero is kept. The rounded value is exact in binary32, whose upper 16
+    bits are then the bfloat16 pattern.
+    """
+    a = np.asarray(values, dtype=np.float64)
+    _, ex = np.frexp(np.abs(a))                   # |a| = f 2^ex with f in [0.5, 1)
+    e = np.maximum(ex.astype(np.int64) - 1, BF16_MIN_EXP)
+    spacing = np.ldexp(1.0, e - 7)
+    with np.errstate(invalid="ignore"):
+        r = np.rint(a / spacing) * spacing
+    r = np.where(np.abs(r) > BF16_MAX, np.copysign(np.inf, a), r)
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_from_bits(bits):
+    """bfloat16 bit patterns (uint16) -> exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
 
 
 def e3m2_value(code):

@@ -23,6 +23,8 @@ kernel consumes them. It gives no concrete layout. The layout used here is:
       order in which gfx950's packed FP4 convert takes a byte).
     - F16 (64 bytes, the unquantized baseline): bytes 2j, 2j+1 hold the fp16 bits of
       weight j, little-endian.
+    - BF16 (64 bytes, the unquantized baseline for bfloat16 activations): the same with
+      bfloat16 bits.
 * W6 only, split by planes: the units of a row are taken 64 at a time ("chunks"; the
   last chunk of a row may hold fewer, Uc units). In a chunk, bytes 0..15 of its units
   come first, unit after unit (16*Uc bytes), then bytes 16..23 of its units (8*Uc
@@ -32,7 +34,7 @@ kernel consumes them. It gives no concrete layout. The layout used here is:
   row-major (group g of row n covers the same 32 K as unit g).
 
 Codes given to and returned by these functions are the logical codes: int8 q for W8,
-0..15 for W4 and FP4, 0..63 for W6, uint16 fp16 bits for F16.
+0..15 for W4 and FP4, 0..63 for W6, uint16 fp16 bits for F16, uint16 bfloat16 bits for BF16.
 """
 
 import numpy as np
@@ -42,8 +44,9 @@ FMT_W8 = 1
 FMT_W4G32 = 2
 FMT_W6E3M2 = 3
 FMT_W4E2M1 = 4
+FMT_BF16 = 5
 
-_BITS = {FMT_F16: 16, FMT_W8: 8, FMT_W4G32: 4, FMT_W6E3M2: 6, FMT_W4E2M1: 4}
+_BITS = {FMT_F16: 16, FMT_W8: 8, FMT_W4G32: 4, FMT_W6E3M2: 6, FMT_W4E2M1: 4, FMT_BF16: 16}
 UNIT = 32
 CHUNK = 64          # units per W6 plane chunk
 
@@ -65,7 +68,7 @@ def packed_bytes(fmt, n, k):
 def scales_count(fmt, n, k):
     """Number of fp16 scales."""
     _bits(fmt)
-    if fmt == FMT_F16:
+    if fmt in (FMT_F16, FMT_BF16):
         return 0
     return n * (k // 32) if fmt == FMT_W4G32 else n
 
@@ -89,7 +92,7 @@ def code_field(fmt, j):
         return 6 * j, 6
     if fmt == FMT_W4E2M1:
         return 4 * j, 4
-    if fmt == FMT_F16:
+    if fmt in (FMT_F16, FMT_BF16):
         return 16 * j, 16
     raise ValueError("unknown format %r" % fmt)
 
@@ -101,7 +104,7 @@ def _stored(fmt, code):
         if not -127 <= code <= 127:
             raise ValueError("int8 code out of range")
         return code + 128
-    limit = {FMT_W4G32: 16, FMT_W6E3M2: 64, FMT_W4E2M1: 16, FMT_F16: 65536}[fmt]
+    limit = {FMT_W4G32: 16, FMT_W6E3M2: 64, FMT_W4E2M1: 16, FMT_F16: 65536, FMT_BF16: 65536}[fmt]
     if not 0 <= code < limit:
         raise ValueError("code out of range")
     return code
@@ -157,7 +160,8 @@ def unpack_scalar(fmt, packed, n, k):
     if packed.size != packed_bytes(fmt, n, k):
         raise ValueError("packed size mismatch")
     ub = unit_bytes(fmt)
-    dtype = {FMT_W8: np.int8, FMT_W4G32: np.uint8, FMT_W6E3M2: np.uint8, FMT_W4E2M1: np.uint8, FMT_F16: np.uint16}[fmt]
+    dtype = {FMT_W8: np.int8, FMT_W4G32: np.uint8, FMT_W6E3M2: np.uint8, FMT_W4E2M1: np.uint8, FMT_F16: np.uint16,
+             FMT_BF16: np.uint16}[fmt]
     codes = np.zeros((n, k), dtype=dtype)
     for r in range(n):
         for u in range(k // UNIT):
@@ -206,7 +210,7 @@ def pack_vectorized(fmt, codes):
             raise ValueError("fp4 code out of range")
         c = c.reshape(n, k // 2, 2)
         return (c[:, :, 0] | (c[:, :, 1] << 4)).astype(np.uint8).reshape(-1)
-    if fmt == FMT_F16:
+    if fmt in (FMT_F16, FMT_BF16):
         return codes.astype(np.uint16).astype("<u2").view(np.uint8).reshape(-1)
     raise ValueError("unknown format %r" % fmt)
 
@@ -231,7 +235,7 @@ def unpack_vectorized(fmt, packed, n, k):
     if fmt == FMT_W4E2M1:
         b = packed.reshape(n, k // 2)
         return np.stack([b & 0xF, b >> 4], axis=-1).astype(np.uint8).reshape(n, k)
-    if fmt == FMT_F16:
+    if fmt in (FMT_F16, FMT_BF16):
         return packed.view("<u2").reshape(n, k).astype(np.uint16)
     raise ValueError("unknown format %r" % fmt)
 

@@ -51,6 +51,75 @@ def fp16_round(fr):
     return sign * v
 
 
+def bf16_round(fr):
+    """Round a Fraction to the nearest bfloat16 value (ties to even). Returns a Fraction, or +-inf as float.
+
+    bfloat16: 8 significant bits; normal binades from 2^-126 up, below that the spacing
+    stays 2^-133; the largest finite value is (2 - 2^-7) 2^127.
+    """
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    quantum = Fraction(2) ** (e - 7)
+    v = rint_even(a / quantum) * quantum
+    if v > (2 - Fraction(1, 128)) * Fraction(2) ** 127:
+        return sign * math.inf
+    return sign * v
+
+
+def check_bf16_rounding(round_fn, values):
+    """round_fn(float64 array) -> bfloat16 bits must be the exact round-to-nearest-even of every value."""
+    got = round_fn(np.array(values, dtype=np.float64))
+    for v, g in zip(values, got):
+        r = bf16_round(Fraction(v))
+        want = (0x8000 if math.copysign(1.0, v) < 0 else 0) if r == 0 else fraction_to_bf16_bits(r)
+        if int(g) != want:
+            return False
+    return True
+
+
+def bf16_bits_to_fraction(b):
+    """Exact value of a bfloat16 bit pattern from its fields: sign, 8 exponent bits (bias 127), 7 mantissa bits."""
+    b = int(b)
+    s = -1 if b >> 15 else 1
+    e = (b >> 7) & 0xFF
+    m = b & 0x7F
+    if e == 0xFF:
+        raise ValueError("inf/nan")
+    if e == 0:
+        return s * Fraction(m) * Fraction(2) ** -133
+    return s * (1 + Fraction(m, 128)) * Fraction(2) ** (e - 127)
+
+
+def fraction_to_bf16_bits(v):
+    """Exact bfloat16 value (Fraction, or inf) -> bit pattern, built from the fields; v must be representable."""
+    if isinstance(v, float) and math.isinf(v):
+        return 0x7F80 if v > 0 else 0xFF80
+    if v == 0:
+        return 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(Fraction(v))
+    if a < Fraction(2) ** -126:
+        m = a / Fraction(2) ** -133
+        assert m.denominator == 1
+        return sign | int(m)
+    e = 0
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    m = (a / Fraction(2) ** e - 1) * 128
+    assert m.denominator == 1 and 0 <= m < 128
+    return sign | ((e + 127) << 7) | int(m)
+
+
 def f16_bits_to_fraction(b):
     b = int(b)
     s = -1 if b >> 15 else 1
@@ -281,8 +350,8 @@ def golden_pack_examples():
 
 
 # ---------------------------------------------------------------- exact linear and dequant
-def exact_dequant(fmt_name, code, scale_bits, zero_bits=0):
-    """Exact dequantized value (Fraction) rounded once to fp16, returned as bits."""
+def exact_dequant(fmt_name, code, scale_bits, zero_bits=0, act="f16"):
+    """Exact dequantized value (Fraction) rounded once to fp16 (or bfloat16), returned as bits."""
     s = f16_bits_to_fraction(scale_bits)
     if fmt_name == "w8":
         v = code * s
@@ -295,13 +364,13 @@ def exact_dequant(fmt_name, code, scale_bits, zero_bits=0):
             return 0x8000 if (neg and s > 0) or (not neg and s < 0) else 0
     else:
         raise ValueError(fmt_name)
-    r = fp16_round(v)
+    r = fp16_round(v) if act == "f16" else bf16_round(v)
     if r == 0:
         return 0x8000 if v < 0 else 0
-    return fraction_to_f16_bits(r)
+    return fraction_to_f16_bits(r) if act == "f16" else fraction_to_bf16_bits(r)
 
 
-def exact_linear(x_bits, w_bits):
+def exact_linear(x_bits, w_bits, value=f16_bits_to_fraction):
     """y[m][n] = sum_k x*w as exact Fractions, by a plain triple loop."""
     m, k = x_bits.shape
     n = w_bits.shape[0]
@@ -310,21 +379,21 @@ def exact_linear(x_bits, w_bits):
         for j in range(n):
             acc = Fraction(0)
             for t in range(k):
-                acc += f16_bits_to_fraction(x_bits[i, t]) * f16_bits_to_fraction(w_bits[j, t])
+                acc += value(x_bits[i, t]) * value(w_bits[j, t])
             y[i][j] = acc
     return y
 
 
-def check_linear(linear_fn, x_bits, w_bits):
+def check_linear(linear_fn, x_bits, w_bits, value=f16_bits_to_fraction):
     """linear_fn(x, w) (float64) must equal the exact sum to within float64 rounding."""
     y = np.asarray(linear_fn(x_bits, w_bits), dtype=np.float64)
-    ye = exact_linear(x_bits, w_bits)
+    ye = exact_linear(x_bits, w_bits, value)
     if y.shape != (x_bits.shape[0], w_bits.shape[0]):
         return False
     k = x_bits.shape[1]
     for i in range(y.shape[0]):
         for j in range(y.shape[1]):
-            mag = sum(abs(f16_bits_to_fraction(x_bits[i, t]) * f16_bits_to_fraction(w_bits[j, t])) for t in range(k))
+            mag = sum(abs(value(x_bits[i, t]) * value(w_bits[j, t])) for t in range(k))
             if abs(Fraction(float(y[i, j])) - ye[i][j]) > mag * Fraction(k + 1, 2 ** 52):
                 return False
     return True

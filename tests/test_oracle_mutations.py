@@ -10,7 +10,7 @@ import numpy as np
 import oracle
 from oracle import FMT_W4G32, FMT_W6E3M2
 from tests import pins
-from tests.test_oracle_pins import _adversarial
+from tests.test_oracle_pins import _adversarial, _bf16_probe_values
 
 
 def test_pins_accept_the_oracle():
@@ -184,3 +184,33 @@ def test_w6_units_stored_whole_is_caught():
             continue
         whole = b"".join(oracle.pack_scalar(FMT_W6E3M2, np.array([codes[32 * i:32 * i + 32]])).tobytes() for i in range(2))
         assert whole != expected and len(whole) == len(expected)
+
+
+def test_bf16_truncation_is_caught():
+    def bad(a):   # keeps the upper 16 bits of the binary32 value: rounds toward zero
+        with np.errstate(over="ignore"):
+            f = np.asarray(a, dtype=np.float64).astype(np.float32)
+        return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    vals = _bf16_probe_values(np.random.default_rng(5))
+    assert pins.check_bf16_rounding(oracle.bf16_bits, vals)
+    assert not pins.check_bf16_rounding(bad, vals)
+
+
+def test_bf16_ties_away_from_zero_is_caught():
+    def bad(a):
+        a = np.asarray(a, dtype=np.float64)
+        _, ex = np.frexp(np.abs(a))
+        q = np.ldexp(1.0, np.maximum(ex.astype(np.int64) - 1, -126) - 7)
+        r = np.sign(a) * np.floor(np.abs(a) / q + 0.5) * q                 # half away from zero
+        return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    assert not pins.check_bf16_rounding(bad, [1 + 2.0 ** -8, -(1 + 2.0 ** -8), 1.5])
+
+
+def test_bf16_linear_reading_fp16_bits_is_caught():
+    rng = np.random.default_rng(8)
+    x = oracle.bf16_bits(rng.standard_normal((1, 32)))
+    w = oracle.bf16_bits(rng.standard_normal((3, 32)) * 0.1)
+    good = lambda a, b: oracle.linear_ref(a, b, act=oracle.ACT_BF16)
+    bad = lambda a, b: oracle.linear_ref(a, b)                         # the bits taken as fp16
+    assert pins.check_linear(good, x, w, value=pins.bf16_bits_to_fraction)
+    assert not pins.check_linear(bad, x, w, value=pins.bf16_bits_to_fraction)

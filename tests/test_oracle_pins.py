@@ -7,10 +7,10 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1
+from oracle import FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, FMT_BF16
 from tests import pins
 
-FMTS = {"w8": FMT_W8, "w4": FMT_W4G32, "w6": FMT_W6E3M2, "f16": FMT_F16, "fp4": FMT_W4E2M1}
+FMTS = {"w8": FMT_W8, "w4": FMT_W4G32, "w6": FMT_W6E3M2, "f16": FMT_F16, "fp4": FMT_W4E2M1, "bf16": FMT_BF16}
 
 
 # ------------------------------------------------------------------ e3m2
@@ -126,6 +126,44 @@ def test_fp16_rounding_vs_exact():
         assert int(g) == pins.fraction_to_f16_bits(r) or (r == 0 and int(g) in (0, 0x8000)), v
 
 
+# ------------------------------------------------------------------ bfloat16 rounding
+def _bf16_probe_values(rng):
+    vals = list(rng.standard_normal(400) * 1e-3) + list(rng.standard_normal(400) * 300)
+    vals += [1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -40, 1 + 2.0 ** -8 - 2.0 ** -40,   # ties, near-ties
+             2 - 2.0 ** -9, 2 - 2.0 ** -10, -(1 + 5 * 2.0 ** -8),
+             2.0 ** -126, 2.0 ** -127 + 2.0 ** -134, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135, 2.0 ** -135,
+             -(2.0 ** -134),                                                     # rounds to -0
+             (2 - 2.0 ** -7) * 2.0 ** 127, (2 - 2.0 ** -8) * 2.0 ** 127,          # largest; the tie above it -> inf
+             (2 - 2.0 ** -8) * 2.0 ** 127 * (1 - 2.0 ** -40), 1e39, -1e39,
+             0.1, -0.1, 1e-40, -3.5e-39, 65504.0, 1e30, 0.0, -0.0]
+    return vals
+
+
+def test_bf16_rounding_vs_exact():
+    assert pins.check_bf16_rounding(oracle.bf16_bits, _bf16_probe_values(np.random.default_rng(5)))
+
+
+def test_bf16_rounding_vs_torch_float32_conversion():
+    # torch rounds float32 to bfloat16 to nearest, ties to even, in one step: a library routine
+    import torch
+    rng = np.random.default_rng(6)
+    f = rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    ties = ((rng.integers(0, 2 ** 16, 4000, dtype=np.uint64).astype(np.uint32) << np.uint32(16))
+            | np.uint32(0x8000)).view(np.float32)                  # exactly half way, both parities of the last bit
+    f = np.concatenate([f, ties])
+    f = f[np.isfinite(f)]
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_bits(f.astype(np.float64)), want)
+
+
+def test_bf16_from_bits_matches_the_fields():
+    for b in list(range(0, 0x7F80, 97)) + [0x0001, 0x007F, 0x0080, 0x3F80, 0x7F7F]:
+        for sb in (b, b | 0x8000):
+            v = oracle.bf16_from_bits(np.array([sb], dtype=np.uint16))[0]
+            assert Fraction(float(v)) == pins.bf16_bits_to_fraction(sb), hex(sb)
+            assert int(oracle.bf16_bits(np.array([v]))[0]) == sb or (v == 0 and sb in (0, 0x8000))
+
+
 # ------------------------------------------------------------------ quantizers
 def _adversarial(n, k, rng):
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
@@ -211,7 +249,7 @@ def test_pack_matches_hand_derived_bytes():
         assert bytes(oracle.pack_vectorized(fmt, c)) == expected, name
 
 
-@pytest.mark.parametrize("name", ["w8", "w4", "w6", "f16", "fp4"])
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "f16", "fp4", "bf16"])
 @pytest.mark.parametrize("n,k", [(3, 96), (2, 32 * 130)])       # 130 units: two full chunks of 64 and one of 2
 def test_pack_scalar_equals_vectorized_and_round_trips(name, n, k):
     fmt = FMTS[name]
@@ -226,7 +264,8 @@ def test_pack_scalar_equals_vectorized_and_round_trips(name, n, k):
         codes = rng.integers(0, 65536, (n, k)).astype(np.uint16)
     a = oracle.pack_scalar(fmt, codes)
     b = oracle.pack_vectorized(fmt, codes)
-    assert a.size == oracle.packed_bytes(fmt, n, k) == n * k * {"w8": 8, "w4": 4, "w6": 6, "f16": 16, "fp4": 4}[name] // 8
+    assert a.size == oracle.packed_bytes(fmt, n, k) == n * k * {"w8": 8, "w4": 4, "w6": 6, "f16": 16, "fp4": 4,
+                                                                "bf16": 16}[name] // 8
     assert np.array_equal(a, b)
     assert np.array_equal(oracle.unpack_scalar(fmt, a, n, k), codes)
     assert np.array_equal(oracle.unpack_vectorized(fmt, b, n, k), codes)
@@ -238,6 +277,7 @@ def test_metadata_counts():
     assert oracle.scales_count(FMT_W4G32, 7, 64) == 14 and oracle.zeros_count(FMT_W4G32, 7, 64) == 14
     assert oracle.scales_count(FMT_F16, 7, 64) == 0
     assert oracle.scales_count(FMT_W4E2M1, 7, 64) == 7 and oracle.zeros_count(FMT_W4E2M1, 7, 64) == 0
+    assert oracle.scales_count(FMT_BF16, 7, 64) == 0 and oracle.zeros_count(FMT_BF16, 7, 64) == 0
 
 
 # ------------------------------------------------------------------ dequant
@@ -272,6 +312,40 @@ def test_dequant_exact_vs_fraction_and_fp32(name):
     assert np.array_equal(v32.astype(np.float16).view(np.uint16), d)
 
 
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4"])
+def test_dequant_bf16_exact_vs_fraction_and_fp32(name):
+    import torch
+    fmt = FMTS[name]
+    rng = np.random.default_rng(19)
+    w = _adversarial(8, 64, rng)
+    w[6, :] *= 1e-4
+    _, s, z, codes = oracle.quantize_and_pack(fmt, w)
+    d = oracle.dequant_bf16(fmt, codes, s, z)
+    n, k = codes.shape
+    sv = np.asarray(s).reshape(n, -1)
+    zv = np.asarray(z).reshape(n, -1) if name == "w4" else None
+    for r in range(n):
+        for c in range(k):
+            g = c // 32 if name == "w4" else 0
+            want = pins.exact_dequant(name, int(codes[r, c]), int(sv[r, g]), int(zv[r, g]) if zv is not None else 0,
+                                      act="bf16")
+            got = int(d[r, c])
+            assert got == want or (want in (0, 0x8000) and got in (0, 0x8000) and name not in ("w6", "fp4")), (r, c)
+    # exact in fp32 too: an fp32 product rounded once by torch gives the same bits
+    s32 = oracle.fp16_from_bits(sv).astype(np.float32)
+    if name == "w8":
+        v32 = codes.astype(np.float32) * np.repeat(s32, k, axis=1)
+    elif name == "w4":
+        zz = oracle.fp16_from_bits(zv).astype(np.float32)
+        v32 = (codes.astype(np.float32) - np.repeat(zz, 32, axis=1)) * np.repeat(s32, 32, axis=1)
+    elif name == "w6":
+        v32 = oracle.e3m2_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
+    else:
+        v32 = oracle.e2m1_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
+    t = torch.from_numpy(np.ascontiguousarray(v32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(t, d)
+
+
 def test_dequant_w6_keeps_negative_zero():
     codes = np.full((1, 32), 32, dtype=np.uint8)
     d = oracle.dequant_fp16(FMT_W6E3M2, codes, np.array([0x3C00], dtype=np.uint16))
@@ -285,6 +359,15 @@ def test_linear_vs_exact_triple_loop(m, n, k):
     x = rng.standard_normal((m, k)).astype(np.float16).view(np.uint16)
     w = (rng.standard_normal((n, k)) * 0.1).astype(np.float16).view(np.uint16)
     assert pins.check_linear(oracle.linear_ref, x, w)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 3, 32), (2, 5, 64)])
+def test_linear_bf16_vs_exact_triple_loop(m, n, k):
+    rng = np.random.default_rng(m * 100 + n + 7)
+    x = oracle.bf16_bits(rng.standard_normal((m, k)) * 3)
+    w = oracle.bf16_bits(rng.standard_normal((n, k)) * 0.1)
+    fn = lambda a, b: oracle.linear_ref(a, b, act=oracle.ACT_BF16)
+    assert pins.check_linear(fn, x, w, value=pins.bf16_bits_to_fraction)
 
 
 def test_linear_one_hot_returns_a_column():
@@ -333,4 +416,38 @@ def test_error_bound_accepts_fp32_accumulation_and_rejects_one_code_off():
     yo = oracle.linear_ref(xo, wd)
     bo = oracle.error_bound(xo, wd, yo)
     off = float(oracle.fp16_from_bits(s[0])) * (int(codes[0, 10]) + 1)
+    assert abs(off - yo[0, 0]) > bo[0, 0]
+
+
+def test_error_bound_bf16_accepts_fp32_accumulation_and_rejects_one_code_off():
+    # W4 with bfloat16 activations: the group scale applied after each group's fp32 sum, the
+    # output rounded once to bfloat16, against the reference on bfloat16-dequantised weights
+    rng = np.random.default_rng(14)
+    n, k = 16, 4096
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    x = oracle.bf16_bits(rng.standard_normal((1, k)) * 2)
+    _, s, z, codes = oracle.quantize_and_pack(FMT_W4G32, w)
+    wd = oracle.dequant_bf16(FMT_W4G32, codes, s, z)
+    yref = oracle.linear_ref(x, wd, act=oracle.ACT_BF16)
+    bound = oracle.error_bound(x, wd, yref, act=oracle.ACT_BF16)
+    assert np.all(bound < oracle.error_bound(x, wd, yref) * 16)          # looser than fp16 by about 2^3
+    xf = oracle.bf16_from_bits(x).astype(np.float32)[0]
+    sv = oracle.fp16_from_bits(s).reshape(n, k // 32).astype(np.float32)
+    zv = oracle.fp16_from_bits(z).reshape(n, k // 32).astype(np.float32)
+    for r in range(n):
+        acc = np.float32(0)
+        for g in rng.permutation(k // 32):
+            part = np.float32(0)
+            for t in range(32 * g, 32 * g + 32):
+                part = np.float32(part + np.float32(xf[t] * np.float32(np.float32(codes[r, t]) - zv[r, g])))
+            acc = np.float32(acc + np.float32(part * sv[r, g]))
+        y = float(oracle.bf16_from_bits(oracle.bf16_bits(np.array([float(acc)])))[0])
+        assert abs(y - yref[0, r]) <= bound[0, r]
+    # a weight one code off, seen through a one-hot x, is far outside the bound
+    xo = np.zeros((1, k))
+    xo[0, 10] = 1.0
+    xo = oracle.bf16_bits(xo)
+    yo = oracle.linear_ref(xo, wd, act=oracle.ACT_BF16)
+    bo = oracle.error_bound(xo, wd, yo, act=oracle.ACT_BF16)
+    off = float(sv[0, 0]) * (int(codes[0, 10]) + 1 - float(zv[0, 0]))
     assert abs(off - yo[0, 0]) > bo[0, 0]
