@@ -26,6 +26,8 @@
  *                  nearest e2m1 to w/s (ties to even code, saturating); w^ = e2m1(code)*s.
  *                  A further bit width through the same kernels; the pages name none.
  *   WQ_FMT_F16     plain fp16 weights W[N,K] (the unquantized baseline); no metadata.
+ *   WQ_FMT_BF16    plain bfloat16 weights W[N,K], the unquantized baseline for bfloat16
+ *                  activations (WQ_ACT_BF16 below); no metadata.
  *   Quotients are IEEE float64 operations; rint and fp16 conversion round to nearest even.
  *   A scale that rounds to 0 makes the codes of its row or group 0 (and z = 0).
  *
@@ -40,10 +42,20 @@
  *       come first, unit after unit, then bytes 16..23 of the same units.
  *   FP4 16 B: code j in bits 4j..4j+3 of the unit read as a little-endian number (byte p:
  *       code 2p in the low nibble, code 2p+1 in the high nibble).
- *   F16 64 B: fp16 weight j at bytes 2j..2j+1 (so F16 is the plain row-major matrix).
+ *   F16 64 B: fp16 weight j at bytes 2j..2j+1 (so F16 is the plain row-major matrix); BF16 the same
+ *       with bfloat16 bits.
  * So packed_w is exactly N*K*bits/8 bytes. scales: W8/W6/FP4 [N]; W4 [N][K/32] row-major.
  * zeros: W4 [N][K/32] row-major; otherwise unused (may be NULL). fp16 values are passed
  * as uint16_t bit patterns.
+ *
+ * Activations: by default x, y and dequantized weights are fp16. OR-ing WQ_ACT_BF16 into the
+ * fmt argument of wq_dequant, wq_linear, wq_linear_grouped and the kernel-name calls makes them
+ * bfloat16 (the other activation type the gpt-fast guide, www.jsqmd.com, section
+ * "量化技术深度解析", offers). The packed weights and their fp16 metadata are the same for both;
+ * the product still accumulates in fp32, and the dequantized value of a weight is its exact
+ * value rounded once to bfloat16. Valid codes with the flag: W8, W4G32, W6E3M2, W4E2M1 and BF16;
+ * F16 weights take fp16 activations only and BF16 weights bfloat16 ones (else WQ_ERR_FMT).
+ * The size calls ignore the flag.
  *
  * Conventions for every call:
  *   - K must be a positive multiple of 32 and at most 2^26; N >= 1; M >= 1; N*K/32 must fit
@@ -64,7 +76,10 @@
 extern "C" {
 #endif
 
-typedef enum { WQ_FMT_F16 = 0, WQ_FMT_W8 = 1, WQ_FMT_W4G32 = 2, WQ_FMT_W6E3M2 = 3, WQ_FMT_W4E2M1 = 4 } wq_fmt;
+typedef enum { WQ_FMT_F16 = 0, WQ_FMT_W8 = 1, WQ_FMT_W4G32 = 2, WQ_FMT_W6E3M2 = 3, WQ_FMT_W4E2M1 = 4, WQ_FMT_BF16 = 5 } wq_fmt;
+
+/* Activation-type flag, OR-ed into a format code: bfloat16 x and y instead of fp16. */
+typedef enum { WQ_ACT_F16 = 0, WQ_ACT_BF16 = 0x100 } wq_act;
 
 typedef enum {
   WQ_OK = 0,
@@ -103,20 +118,20 @@ int wq_pack_fp4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* sc
 /* Inverse of the packers' layout step, on the host: packed -> logical codes [N,K]
  * (int8 for W8; 0..15 for W4 and FP4; 0..63 for W6, one byte each; uint16 fp16 bits for F16) and
  * a copy of the metadata in logical order (scales_out/zeros_out may be NULL to skip).
- * A test hook. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT. */
+ * BF16: uint16 bfloat16 bits. A test hook. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT. */
 int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,
               void* codes, uint16_t* scales_out, uint16_t* zeros_out);
 
 /* On the device: dequantize packed weights to fp16 W^[N,K] row-major, w_out[n*K+k] =
  * fp16(w^[n,k]) rounded once to nearest even (bit-exact by construction: each product
- * is exact in fp32). All pointers are device pointers, 16-byte aligned; zeros only for
- * W4. Asynchronous on stream. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT,
- * WQ_ERR_ALIGN, WQ_ERR_DEVICE. */
+ * is exact in fp32); with WQ_ACT_BF16 in fmt, bfloat16 rounded once to nearest even. All
+ * pointers are device pointers, 16-byte aligned; zeros only for W4. Asynchronous on
+ * stream. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT, WQ_ERR_ALIGN, WQ_ERR_DEVICE. */
 int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, uint16_t* w_out,
                int64_t N, int64_t K, void* stream);
 
-/* On the device: y[M,N] = x[M,K] . dequant(packed_w)[N,K]^T with fp16 x and y (row-major,
- * row strides K and N) and fp32 accumulation; the one fused kernel reads every packed
+/* On the device: y[M,N] = x[M,K] . dequant(packed_w)[N,K]^T with fp16 x and y (bfloat16 with
+ * WQ_ACT_BF16 in fmt; row-major, row strides K and N) and fp32 accumulation; the one fused kernel reads every packed
  * byte once and never writes dequantized weights to memory. All pointers are device
  * pointers, 16-byte aligned; zeros only for W4 (else may be NULL). M of any size; one launch
  * takes up to 64 rows of x for W6 and for W4 with K a multiple of 256, up to 16 otherwise,

@@ -1,0 +1,197 @@
+"""GPU parity with bfloat16 activations (WQ_ACT_BF16): libwq's device path against the CPU oracle.
+
+The packed weights are the same as with fp16 activations; x, y and the dequantized
+weights are bfloat16. x comes from the same seeded fp16 draws, rounded to bfloat16 by
+torch. Criteria as for fp16, with the bfloat16 unit roundoff in the closed-form bound:
+
+* wq_dequant: bit-exact bfloat16 patterns, every code of W6 and FP4 included.
+* wq_linear: every M in 1..16 and slabs beyond, ragged N and K, both kernel families;
+  one-hot x bit-exact; x = 0 exact; repeat calls bit-identical; activations far outside
+  the fp16 range.
+* Grouped launches bit-identical to separate ones; a full-size workload on sampled rows.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_quantized_dequant_amd import inputs, wq
+from tests.gpu_util import (DeviceWeights, bf16_bits_torch, check_linear, dev, host_bits, oracle_rows, torch_cuda,
+                            x_as_bf16)
+
+pytestmark = pytest.mark.gpu
+
+BF = wq.ACT_BF16
+FMTS = [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_BF16]
+FMT_ID = {wq.FMT_W8: "w8", wq.FMT_W4G32: "w4", wq.FMT_W6E3M2: "w6", wq.FMT_W4E2M1: "fp4", wq.FMT_BF16: "bf16"}
+
+
+def _weights(n, k, seed, adversarial=True):
+    w, _ = inputs.small_case(seed, n, k, 1)
+    if adversarial and n >= 8:
+        w[0, :] = 0.0                       # zero row: scale 0
+        w[1, 3] = 0.7                       # one outlier
+        w[2, :] = np.abs(w[2, :])           # one-signed rows / groups
+        w[3, :] = -np.abs(w[3, :])
+        w[4, :32] = 1e-9                    # subnormal fp16 scale
+        w[5, :] *= 1e-4                     # small dequantized values
+        w[6, 1] = -0.0
+    return w
+
+
+def _x(seed, k, m):
+    return x_as_bf16(inputs.small_case(seed, 1, k, m)[1])
+
+
+def _ref_weights(fmt, w):
+    """The oracle's bfloat16 dequantized weights (BF16 weights: the rounded weights themselves)."""
+    if fmt == wq.FMT_BF16:
+        return bf16_bits_torch(w)
+    return oracle_rows(fmt, w, BF)[0]
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("n,k", [(1, 32), (15, 64), (17, 96), (64, 4096), (1000, 2080)])
+def test_dequant_bf16_bit_exact(fmt, n, k):
+    torch_cuda()
+    w = _weights(n, k, n + k)
+    dw = DeviceWeights(fmt, w, BF)
+    got = dw.dequant()
+    want = _ref_weights(fmt, w)
+    assert np.array_equal(got, want), "%d of %d differ" % (int((got != want).sum()), got.size)
+
+
+@pytest.mark.parametrize("fmt,ncodes", [(wq.FMT_W6E3M2, 64), (wq.FMT_W4E2M1, 16)], ids=["w6", "fp4"])
+def test_dequant_bf16_all_codes(fmt, ncodes):
+    torch = torch_cuda()
+    rows = ncodes
+    codes = ((np.arange(64)[None, :] + np.arange(rows)[:, None]) % ncodes).astype(np.uint8)
+    packed = oracle.pack_vectorized(fmt, codes)
+    for s in (0x3C00, 0x2E66, 0x0003):
+        sc = np.full(rows, s, dtype=np.uint16)
+        out = torch.empty((rows, 64), dtype=torch.int16, device="cuda:0")
+        wq.wq_dequant(fmt | BF, dev(packed), dev(sc), None, out, rows, 64)
+        torch.cuda.synchronize()
+        want = oracle.dequant_bf16(fmt, codes, sc)
+        assert np.array_equal(host_bits(out), want), hex(s)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("m", list(range(1, 17)))
+def test_linear_bf16_every_m(fmt, m):
+    n, k = 37, 4256
+    w = _weights(n, k, 7)
+    x = _x(1000 + m, k, m)
+    dw = DeviceWeights(fmt, w, BF)
+    check_linear(dw.linear(x), x, _ref_weights(fmt, w), "fmt %d m %d" % (fmt, m), act=BF)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("n,k,m", [(1, 32, 1), (1, 32, 16), (16, 128, 5), (33, 2048, 1), (33, 2048, 9),
+                                   (130, 8192, 1), (130, 8192, 16), (4100, 256, 4), (16500, 128, 5),
+                                   (37, 2304, 5), (8200, 2304, 8), (40, 11008, 13), (48, 256, 6),
+                                   (130, 8192, 64), (37, 2304, 33), (33, 512, 130)])
+def test_linear_bf16_shapes(fmt, n, k, m):
+    w = _weights(n, k, 3 * n + k)
+    x = _x(2000 + n + m, k, m)
+    dw = DeviceWeights(fmt, w, BF)
+    check_linear(dw.linear(x), x, _ref_weights(fmt, w), "fmt %d n %d k %d m %d" % (fmt, n, k, m), act=BF)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("m", [1, 3, 16])
+def test_linear_bf16_one_hot_is_bit_exact(fmt, m):
+    n, k = 40, 2080
+    w = _weights(n, k, 11)
+    dw = DeviceWeights(fmt, w, BF)
+    wd = _ref_weights(fmt, w)
+    for kk in (0, 31, 32, 1000, k - 1):
+        x = np.zeros((m, k), dtype=np.uint16)
+        x[:, kk] = 0x3F80                    # bfloat16 1.0
+        y = dw.linear(x)
+        want = np.tile(wd[:, kk], (m, 1))
+        same = (y == want) | ((y & 0x7FFF) == 0) & ((want & 0x7FFF) == 0)
+        assert same.all(), (kk, np.argwhere(~same)[:3].tolist())
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+def test_linear_bf16_zero_x_and_repeatability(fmt):
+    n, k = 70, 4096
+    w = _weights(n, k, 13)
+    dw = DeviceWeights(fmt, w, BF)
+    for m in (1, 16):
+        y0 = dw.linear(np.zeros((m, k), dtype=np.uint16))
+        assert np.all((y0 & 0x7FFF) == 0)
+        x = _x(77, k, m)
+        ys = [dw.linear(x) for _ in range(3)]
+        assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("m", [1, 8])
+def test_linear_bf16_activations_beyond_fp16_range(fmt, m):
+    # x of order 1e6 (fp16 overflows at 65520): bfloat16 keeps float32's exponent range. Scaling
+    # x by 2^20 scales every product and partial sum exactly, so y must scale exactly too; the
+    # scaled result also meets the closed-form bound (the fixed atol does not apply at this scale).
+    n, k = 33, 2048
+    w = _weights(n, k, 17)
+    x16 = inputs.small_case(3000 + m, 1, k, m)[1]
+    x1 = bf16_bits_torch(x16.view(np.float16).astype(np.float32))
+    xb = bf16_bits_torch(x16.view(np.float16).astype(np.float32) * np.float32(2.0 ** 20))
+    dw = DeviceWeights(fmt, w, BF)
+    wd = _ref_weights(fmt, w)
+    y1, yb = dw.linear(x1), dw.linear(xb)
+    check_linear(y1, x1, wd, "fmt %d m %d" % (fmt, m), act=BF)
+    check_linear(yb, xb, wd, "fmt %d m %d, x ~ 1e6" % (fmt, m), act=BF, fixed_tol=False)
+    assert np.array_equal(oracle.bf16_from_bits(yb), oracle.bf16_from_bits(y1) * 2.0 ** 20)
+
+
+GROUP_SETS = {
+    "mixed_k": [(40, 2080), (300, 4096), (64, 6144), (17, 96)],
+    "k256": [(40, 2304), (300, 4096), (8200, 256), (17, 512)],
+}
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("m", [1, 4, 7, 16, 40, 70])
+@pytest.mark.parametrize("set_name", sorted(GROUP_SETS))
+def test_grouped_bf16_matches_separate_calls(fmt, m, set_name):
+    torch = torch_cuda()
+    shapes = GROUP_SETS[set_name]
+    dws, xs = [], []
+    for i, (n, k) in enumerate(shapes):
+        dws.append(DeviceWeights(fmt, _weights(n, k, 50 + i), BF))
+        xs.append(_x(60 + i, k, m))
+    sep = [dw.linear(x) for dw, x in zip(dws, xs)]
+    xd = [dev(x) for x in xs]
+    ys = [torch.empty((m, dw.n), dtype=torch.int16, device="cuda:0") for dw in dws]
+    items = [(xd[i], dw.packed, dw.scales, dw.zeros, ys[i], dw.n, dw.k) for i, dw in enumerate(dws)]
+    wq.wq_linear_grouped(items, m, fmt | BF)
+    torch.cuda.synchronize()
+    grouped = wq.wq_linear_grouped_kernel_name(fmt | BF, m, shapes)
+    for i, dw in enumerate(dws):
+        got = host_bits(ys[i])
+        check_linear(got, xs[i], _ref_weights(fmt, _weights(dw.n, dw.k, 50 + i)), "%s item %d" % (grouped, i), act=BF)
+        # the same kernel body and K split as the item's own call (or a separate call): identical bits
+        own = wq.wq_linear_kernel_name(fmt | BF, m, dw.n, dw.k)
+        separate = "_grouped_kernel" not in grouped
+        same_body = own.split("_kernel<")[0] == grouped.split("_grouped_kernel<")[0] and \
+            own.split("<")[1] == grouped.split("<")[1]
+        if separate or same_body:
+            assert np.array_equal(got, sep[i]), "item %d differs from its separate call (%s, %s)" % (i, own, grouped)
+
+
+def test_llama7b_w4_bf16_full_size_sampled():
+    _, shapes, _ = inputs.WORKLOADS["llama7b_w4g32_linears"]
+    for li, (n, k) in enumerate(shapes):
+        w, x16 = inputs.weights_and_x(inputs.rng_for(inputs.WORKLOAD_STREAM["llama7b_w4g32_linears"], li), n, k, 16)
+        x = x_as_bf16(x16)
+        dw = DeviceWeights(wq.FMT_W4G32, w, BF)
+        rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(li).choice(n, 62, replace=False)]))
+        wd = oracle_rows(wq.FMT_W4G32, w[rows], BF)[0]
+        for m in (1, 4, 16):
+            y = dw.linear(x[:m])
+            check_linear(y[:, rows], x[:m], wd, "linear %d (%dx%d) m %d" % (li, n, k, m), act=BF)
+        del dw
+        torch_cuda().cuda.empty_cache()
+

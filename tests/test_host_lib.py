@@ -36,16 +36,21 @@ def test_version_and_status_strings():
         assert wq.wq_status_string(s) and wq.wq_status_string(s) != "unknown status"
 
 
-@pytest.mark.parametrize("fmt", [wq.FMT_F16, wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1])
+@pytest.mark.parametrize("fmt", [wq.FMT_F16, wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_BF16])
 @pytest.mark.parametrize("n,k", [(1, 32), (7, 64), (33, 96), (4096, 11008)])
 def test_sizes_match_oracle(fmt, n, k):
     assert wq.wq_packed_bytes(fmt, n, k) == oracle.packed_bytes(fmt, n, k)
     assert wq.wq_scales_bytes(fmt, n, k) == 2 * oracle.scales_count(fmt, n, k)
     assert wq.wq_zeros_bytes(fmt, n, k) == 2 * oracle.zeros_count(fmt, n, k)
+    # the size calls ignore the activation flag
+    assert wq.wq_packed_bytes(fmt | wq.ACT_BF16, n, k) == oracle.packed_bytes(fmt, n, k)
+    assert wq.wq_scales_bytes(fmt | wq.ACT_BF16, n, k) == 2 * oracle.scales_count(fmt, n, k)
+    assert wq.wq_zeros_bytes(fmt | wq.ACT_BF16, n, k) == 2 * oracle.zeros_count(fmt, n, k)
 
 
 def test_sizes_reject_bad_shapes():
-    for fmt in range(5):
+    assert wq.wq_packed_bytes(wq.FMT_W8 | 0x200, 4, 64) == 0
+    for fmt in range(6):
         assert wq.wq_packed_bytes(fmt, 4, 48) == 0
         assert wq.wq_packed_bytes(fmt, 0, 64) == 0
         assert wq.wq_packed_bytes(fmt, 4, 0) == 0
@@ -213,6 +218,16 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert L.wq_linear(a, a, a, a, a + 2, 1, 64, 64, 1, None) == -5
     assert L.wq_dequant(1, a, a, a, a, 64, 40, None) == -2
     assert L.wq_dequant(5, a, a, a, a, 64, 64, None) == -3
+    # the activation flag: bfloat16 x with fp16 weights, fp16 x with bfloat16 weights and unknown
+    # flags are format errors; a bfloat16 code otherwise passes the same checks
+    assert L.wq_linear(a, a, a, a, a, 1, 64, 64, wq.FMT_F16 | wq.ACT_BF16, None) == -3
+    assert L.wq_linear(a, a, a, a, a, 1, 64, 64, wq.FMT_BF16, None) == -3
+    assert L.wq_linear(a, a, a, a, a, 1, 64, 64, wq.FMT_W8 | 0x200, None) == -3
+    assert L.wq_dequant(wq.FMT_F16 | wq.ACT_BF16, a, a, a, a, 64, 64, None) == -3
+    assert L.wq_linear(a, a, a, None, a, 1, 64, 64, wq.FMT_W4G32 | wq.ACT_BF16, None) == -1
+    assert L.wq_linear(a, a, None, None, a, 1, 64, 64, wq.FMT_W8 | wq.ACT_BF16, None) == -1
+    assert L.wq_linear(a, a, a, a, a, 1, 64, 48, wq.FMT_BF16 | wq.ACT_BF16, None) == -2
+    assert L.wq_linear(a + 8, a, a, a, a, 1, 64, 64, wq.FMT_W6E3M2 | wq.ACT_BF16, None) == -5
     assert L.wq_dequant(2, a, a, None, a, 64, 64, None) == -1
     assert L.wq_dequant(1, a + 4, a, a, a, 64, 64, None) == -5
     assert L.wq_linear(a, a, a, a, a, 1, 64, (1 << 26) + 32, 1, None) == -2    # K above 2^26
@@ -268,3 +283,16 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_kernel_name(4, 100, 4096, 4096) == "lm_kernel<4, 1, 4>"
     assert wq.wq_linear_grouped_kernel_name(4, 1, [(4096, 4096), (11008, 4096)]) == "gemv_grouped_kernel<4, 1, 4>"
     assert wq.wq_linear_grouped_kernel_name(4, 8, [(1024, 8192), (8192, 8224)]) == "lm_grouped_kernel<4, 2, 1>"
+    # bfloat16 activations: the same plan, named with the combined code (format | 0x100)
+    bf = wq.ACT_BF16
+    assert wq.wq_linear_kernel_name(2 | bf, 1, 4096, 4096) == "gemv_kernel<258, 1, 4>"
+    assert wq.wq_linear_kernel_name(2 | bf, 8, 4096, 4096) == "lm_kernel<258, 1, 1>"
+    assert wq.wq_linear_kernel_name(2 | bf, 8, 4096, 4128) == "mfma_kernel<258, 1>"
+    assert wq.wq_linear_kernel_name(3 | bf, 16, 8192, 4096) == "lm_kernel<259, 2, 1>"
+    assert wq.wq_linear_kernel_name(1 | bf, 16, 4096, 4096) == "mfma_kernel<257, 1>"
+    assert wq.wq_linear_kernel_name(5 | bf, 1, 16384, 4096) == "gemv_kernel<261, 1, 1>"
+    assert wq.wq_linear_kernel_name(5 | bf, 16, 8192, 4096) == "mfma_kernel<261, 2>"
+    assert wq.wq_linear_kernel_name(4 | bf, 64, 4096, 4096) == "lm_kernel<260, 1, 4>"
+    assert wq.wq_linear_kernel_name(0 | bf, 1, 4096, 4096) == ""
+    assert wq.wq_linear_kernel_name(5, 1, 4096, 4096) == ""
+    assert wq.wq_linear_grouped_kernel_name(2 | bf, 1, [(4096, 4096), (11008, 4096)]) == "gemv_grouped_kernel<258, 1, 4>"

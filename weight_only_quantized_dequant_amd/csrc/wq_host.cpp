@@ -104,9 +104,13 @@ int fmt_bits(int fmt) {
     case WQ_FMT_W4G32: return 4;
     case WQ_FMT_W6E3M2: return 6;
     case WQ_FMT_W4E2M1: return 4;
+    case WQ_FMT_BF16: return 16;
     default: return 0;
   }
 }
+
+// The size calls take a format code with or without the activation flag.
+int weight_fmt(int fmt) { return (fmt & ~0xFF) == WQ_ACT_BF16 ? (fmt & 0xFF) : fmt; }
 
 // Run f(row_begin, row_end) over [0, N) on up to hardware_concurrency threads and return the
 // first non-OK status.
@@ -197,17 +201,20 @@ const char* wq_status_string(int s) {
 }
 
 size_t wq_packed_bytes(int fmt, int64_t N, int64_t K) {
+  fmt = weight_fmt(fmt);
   int b = fmt_bits(fmt);
   if (!b || !shape_ok(N, K)) return 0;
   return static_cast<size_t>(N) * static_cast<size_t>(K) * b / 8;
 }
 
 size_t wq_scales_bytes(int fmt, int64_t N, int64_t K) {
-  if (!fmt_bits(fmt) || !shape_ok(N, K) || fmt == WQ_FMT_F16) return 0;
+  fmt = weight_fmt(fmt);
+  if (!fmt_bits(fmt) || !shape_ok(N, K) || fmt == WQ_FMT_F16 || fmt == WQ_FMT_BF16) return 0;
   return fmt == WQ_FMT_W4G32 ? static_cast<size_t>(N) * (K / 32) * 2 : static_cast<size_t>(N) * 2;
 }
 
 size_t wq_zeros_bytes(int fmt, int64_t N, int64_t K) {
+  fmt = weight_fmt(fmt);
   if (fmt != WQ_FMT_W4G32 || !shape_ok(N, K)) return 0;
   return static_cast<size_t>(N) * (K / 32) * 2;
 }

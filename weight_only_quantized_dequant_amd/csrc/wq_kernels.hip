@@ -29,6 +29,10 @@
 //    applied to both operands leaves the product unchanged. W6, FP4 and W4 (K % 256 == 0)
 //    read their weights row-contiguously into per-wave LDS first (lm_kernel); W8, F16 and
 //    the other W4 shapes load fragments straight from HBM (mfma_kernel).
+//  * bfloat16 activations (WQ_ACT_BF16 in the format code) run the same kernels with
+//    v_dot2_f32_bf16 and v_mfma_f32_16x16x32_bf16: the decode yields bfloat16 pairs (gfx950's
+//    bf6 and fp4 converts have bf16 forms; W4 (128 + q) by the same nibble placement against
+//    128.0; W8 through byte-to-float converts), and y is rounded once to bfloat16.
 //  * A grouped call runs several linears in one launch with one of these kernel families.
 //  * No atomics anywhere, so every result is deterministic.
 #include <hip/hip_runtime.h>
@@ -45,10 +49,14 @@ namespace {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h32 __attribute__((ext_vector_type(32)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b32 __attribute__((ext_vector_type(32)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x6 __attribute__((ext_vector_type(6)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int GEMV_MAX_M = 4;   // largest M served by the VALU GEMV; above it the MFMA kernel runs
 constexpr int MFMA_M = 16;      // rows of x per MFMA launch
@@ -57,6 +65,41 @@ constexpr int MFMA_MAX_WAVES = 8;   // waves per workgroup of the MFMA kernel
 
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// A kernel's format code: the weight format in the low byte, WQ_ACT_BF16 for bfloat16
+// activations. Registers hold 16-bit pairs as h2 whatever their type; only the dot products,
+// the matrix instructions and the output conversion look at the type. wfmt() is the weight
+// layout (BF16 weights are laid out and loaded as F16 ones).
+constexpr int wfmt(int c) { return (c & 0xFF) == WQ_FMT_BF16 ? WQ_FMT_F16 : (c & 0xFF); }
+constexpr bool bf16_act(int c) { return (c & WQ_ACT_BF16) != 0; }
+
+__device__ __forceinline__ float dot2_bf16(h2 a, h2 b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
+}
+// Pairs 4k .. 4k+3 of a decoded unit as one 8-element MFMA fragment (32-bit moves only).
+__device__ __forceinline__ h8 frag_of(const h2 (&wv)[16], int k) {
+  return __builtin_bit_cast(h8, make_uint4(as_u32(wv[4 * k]), as_u32(wv[4 * k + 1]), as_u32(wv[4 * k + 2]),
+                                           as_u32(wv[4 * k + 3])));
+}
+
+__device__ __forceinline__ h2 pack_bf16(float lo, float hi) {   // two values rounded to nearest even
+  const b2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(h2, v);
+}
+
+template <int FMT>
+__device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {   // 16x16x32 product of the activation type
+  if constexpr (bf16_act(FMT))
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint16_t out16(float v) {   // y: rounded once to the activation type
+  if constexpr (bf16_act(FMT)) return __builtin_bit_cast(uint16_t, (__bf16)v);
+  else return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
 
 // ---------------------------------------------------------------- raw units and loads
 // A 32-code unit in registers. W6 keeps its two plane slices (16 + 8 bytes), which read in
@@ -69,12 +112,12 @@ template <> struct Raw<WQ_FMT_W4E2M1> { uint4 a; };
 template <> struct Raw<WQ_FMT_F16> { uint4 a, b, c, d; };
 
 template <int FMT> constexpr int unit_bytes() {
-  return FMT == WQ_FMT_W8 ? 32 : FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W4E2M1 ? 16 : FMT == WQ_FMT_W6E3M2 ? 24 : 64;
+  return wfmt(FMT) == WQ_FMT_W8 ? 32 : wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W4E2M1 ? 16 : wfmt(FMT) == WQ_FMT_W6E3M2 ? 24 : 64;
 }
 
 // Formats with one fp16 scale per output row, applied to the finished fp32 sum.
 template <int FMT> constexpr bool row_scaled() {
-  return FMT == WQ_FMT_W8 || FMT == WQ_FMT_W6E3M2 || FMT == WQ_FMT_W4E2M1;
+  return wfmt(FMT) == WQ_FMT_W8 || wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1;
 }
 
 // Byte offsets, from the start of row n, of the two plane slices of W6 unit u (U units per row).
@@ -86,15 +129,15 @@ __device__ __forceinline__ void w6_homes(int u, int U, uint32_t& lo, uint32_t& h
 
 // Unit u of row n (used by the MFMA and dequant kernels, where a lane owns a whole unit).
 template <int FMT>
-__device__ __forceinline__ void load_unit(const uint8_t* __restrict__ w, int n, int u, int U, Raw<FMT>& r) {
+__device__ __forceinline__ void load_unit(const uint8_t* __restrict__ w, int n, int u, int U, Raw<wfmt(FMT)>& r) {
   constexpr int UB = unit_bytes<FMT>();
   const uint8_t* row = w + (size_t)n * U * UB;
-  if constexpr (FMT == WQ_FMT_W8) {
+  if constexpr (wfmt(FMT) == WQ_FMT_W8) {
     const uint4* q = reinterpret_cast<const uint4*>(row + (size_t)u * UB);
     r.a = q[0]; r.b = q[1];
-  } else if constexpr (FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W4E2M1) {
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W4E2M1) {
     r.a = *reinterpret_cast<const uint4*>(row + (size_t)u * UB);
-  } else if constexpr (FMT == WQ_FMT_W6E3M2) {
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2) {
     uint32_t lo, hi;
     w6_homes(u, U, lo, hi);
     r.a = *reinterpret_cast<const uint4*>(row + lo);
@@ -134,22 +177,22 @@ __device__ __forceinline__ void decode_fp4_word(uint32_t d, h2& o0, h2& o1, h2& 
 }
 
 template <int FMT>
-__device__ __forceinline__ void decode(const Raw<FMT>& r, h2 zc1, h2 zc2, h2 (&out)[16]) {
-  if constexpr (FMT == WQ_FMT_W8) {
+__device__ __forceinline__ void decode(const Raw<wfmt(FMT)>& r, h2 zc1, h2 zc2, h2 (&out)[16]) {
+  if constexpr (wfmt(FMT) == WQ_FMT_W8) {
     const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) decode_w8_word(w[i], out[2 * i], out[2 * i + 1]);
-  } else if constexpr (FMT == WQ_FMT_W4G32) {
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
     const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) decode_w4_word(w[i], zc1, zc2, out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-  } else if constexpr (FMT == WQ_FMT_W6E3M2) {
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2) {
     u32x6 v;
     v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w; v[4] = r.b.x; v[5] = r.b.y;
     const h32 h = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(v, 1.0f);
 #pragma unroll
     for (int p = 0; p < 16; ++p) { out[p][0] = h[2 * p]; out[p][1] = h[2 * p + 1]; }
-  } else if constexpr (FMT == WQ_FMT_W4E2M1) {
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W4E2M1) {
     const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) decode_fp4_word(w[i], out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
@@ -162,6 +205,57 @@ __device__ __forceinline__ void decode(const Raw<FMT>& r, h2 zc1, h2 zc2, h2 (&o
 }
 
 __device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// The weights of a unit as bfloat16 pairs for bfloat16 activations (same pair order as
+// decode): W8 q, W6 e3m2(code), FP4 e2m1(code), BF16 the weights, all exact, with the row
+// scale applied after the sum; W4 (q - z) s rounded once to bfloat16, since its scale changes
+// along K. For W4, the nibble placed at bit 16 of 128.0f gives (128 + q) in fp32, and one fma
+// with s and c = -(128 + z) s gives (q - z) s exactly (every product is exact in fp32).
+template <int FMT>
+__device__ __forceinline__ void decode_bf16(const Raw<wfmt(FMT)>& r, uint16_t sbits, uint16_t zbits, h2 (&out)[16]) {
+  constexpr int F = wfmt(FMT);
+  if constexpr (F == WQ_FMT_W8) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      out[2 * i] = pack_bf16((float)(w[i] & 0xFFu) - 128.0f, (float)((w[i] >> 8) & 0xFFu) - 128.0f);
+      out[2 * i + 1] = pack_bf16((float)((w[i] >> 16) & 0xFFu) - 128.0f, (float)(w[i] >> 24) - 128.0f);
+    }
+  } else if constexpr (F == WQ_FMT_W4G32) {
+    const float s = f16_to_f32(sbits);
+    const float c = -(128.0f + f16_to_f32(zbits)) * s;
+    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {   // codes 8i+2t (nibble t) and 8i+2t+1 (nibble t+4)
+        const float lo = __builtin_bit_cast(float, ((w[i] << (16 - 4 * t)) & 0x000F0000u) | 0x43000000u);
+        const float hi = __builtin_bit_cast(float, ((w[i] >> (4 * t)) & 0x000F0000u) | 0x43000000u);
+        out[4 * i + t] = pack_bf16(__builtin_fmaf(lo, s, c), __builtin_fmaf(hi, s, c));
+      }
+    }
+  } else if constexpr (F == WQ_FMT_W6E3M2) {
+    u32x6 v;
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w; v[4] = r.b.x; v[5] = r.b.y;
+    const u32x16 h = __builtin_bit_cast(u32x16, __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(v, 1.0f));
+#pragma unroll
+    for (int p = 0; p < 16; ++p) out[p] = as_h2(h[p]);
+  } else if constexpr (F == WQ_FMT_W4E2M1) {
+    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[4 * i] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 0));
+      out[4 * i + 1] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 1));
+      out[4 * i + 2] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 2));
+      out[4 * i + 3] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 3));
+    }
+  } else {
+    const uint32_t w[16] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w,
+                            r.c.x, r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w};
+#pragma unroll
+    for (int p = 0; p < 16; ++p) out[p] = as_h2(w[p]);
+  }
+}
 
 // zero-point constants of one W4 group
 __device__ __forceinline__ void w4_consts(uint16_t zbits, h2& zc1, h2& zc2) {
@@ -233,7 +327,7 @@ __device__ __forceinline__ uint2 ld_nt8(const uint8_t* p) {
 //                                             -(1024 X_lo + 64 X_hi + z (X_lo + X_hi))
 // where X, X_lo, X_hi are sums of x over the segment, shared by all rows of the wave.
 // Every product is exact in fp32; one-hot inputs give exact results.
-template <int FMT> constexpr int seg_codes() { return FMT == WQ_FMT_W8 ? 16 : FMT == WQ_FMT_F16 ? 8 : 32; }
+template <int FMT> constexpr int seg_codes() { return wfmt(FMT) == WQ_FMT_W8 ? 16 : wfmt(FMT) == WQ_FMT_F16 ? 8 : 32; }
 
 template <int FMT> struct Seg { uint4 a; };
 template <> struct Seg<WQ_FMT_W6E3M2> { uint4 a; uint2 b; };
@@ -241,8 +335,8 @@ template <> struct Seg<WQ_FMT_W6E3M2> { uint4 a; uint2 b; };
 template <int FMT, int M, int B>
 struct GemvStage {
   h2 x[M][seg_codes<FMT>() / 2];
-  Seg<FMT> w[B];
-  uint16_t s[FMT == WQ_FMT_W4G32 ? B : 1], z[FMT == WQ_FMT_W4G32 ? B : 1];   // W4 group scale / zero
+  Seg<wfmt(FMT)> w[B];
+  uint16_t s[wfmt(FMT) == WQ_FMT_W4G32 ? B : 1], z[wfmt(FMT) == WQ_FMT_W4G32 ? B : 1];   // W4 group scale / zero
 };
 
 // Base pointers are a kernel argument plus a wave-uniform offset (uniform() keeps it in
@@ -270,7 +364,7 @@ __device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16
   for (int b = 0; b < B; ++b) {
     const int n = min(row0 + b, N - 1);
     const uint8_t* row = w + uniform((size_t)n * row_bytes);
-    if constexpr (FMT == WQ_FMT_W6E3M2) {
+    if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2) {
       uint32_t lo, hi;
       w6_homes(sg, S, lo, hi);
       st.w[b].a = ld_nt16(row + lo);
@@ -278,9 +372,93 @@ __device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16
     } else {
       st.w[b].a = ld_nt16(row + 16u * sg);
     }
-    if constexpr (FMT == WQ_FMT_W4G32) {
+    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
       st.s[b] = (scales + uniform((size_t)n * S))[sg];
       st.z[b] = (zeros + uniform((size_t)n * S))[sg];
+    }
+  }
+}
+
+// bfloat16 activations: W4 (128 + q) in one v_and_or_b32 per pair (against 128.0, whose bfloat16
+// mantissa step is 1), the chain starting at -(128 + z) X; W8 (128 + q) through byte-to-float
+// converts, the sum starting at -128 X; W6 and FP4 through the bf16 forms of the converts.
+template <int FMT, int M, int B>
+__device__ __forceinline__ void gemv_compute_bf16(const GemvStage<FMT, M, B>& st, float (&acc)[B][M]) {
+  constexpr int F = wfmt(FMT);
+  constexpr int P = seg_codes<FMT>() / 2;   // pairs per segment
+  const h2 ones = as_h2(0x3F803F80u);       // bfloat16 (1, 1)
+  const auto& xp = st.x;
+  float sx[M];
+  if constexpr (F == WQ_FMT_W4G32 || F == WQ_FMT_W8) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float a = 0.f, c = 0.f;
+#pragma unroll
+      for (int p = 0; p < P; p += 2) {
+        a = dot2_bf16(xp[m][p], ones, a);
+        c = dot2_bf16(xp[m][p + 1], ones, c);
+      }
+      sx[m] = a + c;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    h2 v[P];
+    if constexpr (F == WQ_FMT_W4G32) {
+      const uint32_t m0 = in_vgpr(0x000F000Fu), mag = in_vgpr(0x43004300u);
+      const uint32_t wd[4] = {st.w[b].a.x, st.w[b].a.y, st.w[b].a.z, st.w[b].a.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // pair t of word i: codes 8i+2t (nibble t), 8i+2t+1 (nibble t+4)
+        v[4 * i] = as_h2((wd[i] & m0) | mag);
+        v[4 * i + 1] = as_h2(((wd[i] >> 4) & m0) | mag);
+        v[4 * i + 2] = as_h2(((wd[i] >> 8) & m0) | mag);
+        v[4 * i + 3] = as_h2(((wd[i] >> 12) & m0) | mag);
+      }
+      const float s = f16_to_f32(st.s[b]), z = f16_to_f32(st.z[b]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float t = -(128.0f + z) * sx[m];
+#pragma unroll
+        for (int p = 0; p < 16; ++p) t = dot2_bf16(v[p], xp[m][p], t);
+        acc[b][m] = __builtin_fmaf(s, t, acc[b][m]);
+      }
+      continue;
+    } else if constexpr (F == WQ_FMT_W8) {
+      const uint32_t wd[4] = {st.w[b].a.x, st.w[b].a.y, st.w[b].a.z, st.w[b].a.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // offset-binary bytes u = q + 128, exact in bfloat16
+        v[2 * i] = pack_bf16((float)(wd[i] & 0xFFu), (float)((wd[i] >> 8) & 0xFFu));
+        v[2 * i + 1] = pack_bf16((float)((wd[i] >> 16) & 0xFFu), (float)(wd[i] >> 24));
+      }
+    } else if constexpr (F == WQ_FMT_W6E3M2) {
+      u32x6 u;
+      u[0] = st.w[b].a.x; u[1] = st.w[b].a.y; u[2] = st.w[b].a.z; u[3] = st.w[b].a.w;
+      u[4] = st.w[b].b.x; u[5] = st.w[b].b.y;
+      const u32x16 h = __builtin_bit_cast(u32x16, __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(u, 1.0f));
+#pragma unroll
+      for (int p = 0; p < 16; ++p) v[p] = as_h2(h[p]);
+    } else if constexpr (F == WQ_FMT_W4E2M1) {
+      const uint32_t wd[4] = {st.w[b].a.x, st.w[b].a.y, st.w[b].a.z, st.w[b].a.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[4 * i] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[i], 1.0f, 0));
+        v[4 * i + 1] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[i], 1.0f, 1));
+        v[4 * i + 2] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[i], 1.0f, 2));
+        v[4 * i + 3] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[i], 1.0f, 3));
+      }
+    } else {   // BF16 weights
+      v[0] = as_h2(st.w[b].a.x); v[1] = as_h2(st.w[b].a.y); v[2] = as_h2(st.w[b].a.z); v[3] = as_h2(st.w[b].a.w);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float a = 0.f, c = 0.f;
+      if constexpr (F == WQ_FMT_W8) a = -128.0f * sx[m];
+#pragma unroll
+      for (int p = 0; p < P; p += 2) {
+        a = dot2_bf16(v[p], xp[m][p], a);
+        c = dot2_bf16(v[p + 1], xp[m][p + 1], c);
+      }
+      acc[b][m] += a + c;
     }
   }
 }
@@ -288,10 +466,14 @@ __device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16
 template <int FMT, int M, int B>
 __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, float (&acc)[B][M], bool active) {
   if (!active) return;
+  if constexpr (bf16_act(FMT)) {
+    gemv_compute_bf16<FMT, M, B>(st, acc);
+    return;
+  }
   constexpr int P = seg_codes<FMT>() / 2;   // fp16 pairs per segment
   const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
   const auto& xp = st.x;
-  if constexpr (FMT == WQ_FMT_W4G32) {
+  if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
     const uint32_t m0 = in_vgpr(0x000F000Fu), m1 = in_vgpr(0x00F000F0u);
     const uint32_t mag_lo = in_vgpr(0x64006400u), mag_hi = in_vgpr(0x54005400u);
     float cx[M], sx[M];
@@ -329,7 +511,7 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
         acc[b][m] = __builtin_fmaf(s, t, acc[b][m]);
       }
     }
-  } else if constexpr (FMT == WQ_FMT_W8) {
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W8) {
     const uint32_t mag = in_vgpr(0x64646464u);
     float sx[M];
 #pragma unroll
@@ -366,14 +548,14 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       h2 v[P];
-      if constexpr (FMT == WQ_FMT_W6E3M2) {
+      if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2) {
         u32x6 u;
         u[0] = st.w[b].a.x; u[1] = st.w[b].a.y; u[2] = st.w[b].a.z; u[3] = st.w[b].a.w;
         u[4] = st.w[b].b.x; u[5] = st.w[b].b.y;
         const h32 h = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(u, 1.0f);
 #pragma unroll
         for (int p = 0; p < 16; ++p) { v[p][0] = h[2 * p]; v[p][1] = h[2 * p + 1]; }
-      } else if constexpr (FMT == WQ_FMT_W4E2M1) {
+      } else if constexpr (wfmt(FMT) == WQ_FMT_W4E2M1) {
         const uint32_t wd[4] = {st.w[b].a.x, st.w[b].a.y, st.w[b].a.z, st.w[b].a.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) decode_fp4_word(wd[i], v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
@@ -445,7 +627,7 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const 
         const int n = row0 + b;
         if (lane == 63 && n < N) {
           if constexpr (row_scaled<FMT>()) t *= f16_to_f32(scales[n]);
-          y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)t);
+          y[(size_t)m * N + n] = out16<FMT>(t);
         }
       }
     return;
@@ -465,7 +647,7 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const 
     for (int i = 0; i < WK; ++i) t += red[sub * WK + i][lane];   // fixed order: deterministic
     if (n < N) {
       if constexpr (row_scaled<FMT>()) t *= f16_to_f32(scales[n]);
-      y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)t);
+      y[(size_t)m * N + n] = out16<FMT>(t);
     }
   }
 }
@@ -513,8 +695,8 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_grouped_kernel(const Gem
 template <int FMT, int RB>
 struct MfmaStage {
   h8 xa[4];
-  Raw<FMT> w[RB];
-  uint16_t s[FMT == WQ_FMT_W4G32 ? RB : 1], z[FMT == WQ_FMT_W4G32 ? RB : 1];
+  Raw<wfmt(FMT)> w[RB];
+  uint16_t s[wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1], z[wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1];
 };
 
 template <int FMT, int RB>
@@ -535,12 +717,12 @@ __device__ __forceinline__ void mfma_load(MfmaStage<FMT, RB>& st, const uint16_t
     const int nb = min(n0 + 16 * r, N - 1);                        // wave-uniform
     const uint32_t nn = (uint32_t)(min(n0 + 16 * r + nl, N - 1) - nb);   // 0..15
     const uint8_t* rowb = w + uniform((size_t)nb * row_bytes);
-    static_assert(FMT != WQ_FMT_W6E3M2 && FMT != WQ_FMT_W4E2M1, "W6 and FP4 on the matrix cores take lm_kernel");
+    static_assert(wfmt(FMT) != WQ_FMT_W6E3M2 && wfmt(FMT) != WQ_FMT_W4E2M1, "W6 and FP4 on the matrix cores take lm_kernel");
     const uint8_t* p = rowb + nn * row_bytes + UB * u;
     st.w[r].a = ld_nt16(p);
-    if constexpr (FMT == WQ_FMT_W8 || FMT == WQ_FMT_F16) st.w[r].b = ld_nt16(p + 16);
-    if constexpr (FMT == WQ_FMT_F16) { st.w[r].c = ld_nt16(p + 32); st.w[r].d = ld_nt16(p + 48); }
-    if constexpr (FMT == WQ_FMT_W4G32) {
+    if constexpr (wfmt(FMT) == WQ_FMT_W8 || wfmt(FMT) == WQ_FMT_F16) st.w[r].b = ld_nt16(p + 16);
+    if constexpr (wfmt(FMT) == WQ_FMT_F16) { st.w[r].c = ld_nt16(p + 32); st.w[r].d = ld_nt16(p + 48); }
+    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
       const size_t mb = uniform((size_t)nb * U);
       st.s[r] = (scales + mb)[nn * U + u];
       st.z[r] = (zeros + mb)[nn * U + u];
@@ -556,23 +738,23 @@ __device__ __forceinline__ void mfma_compute(const MfmaStage<FMT, RB>& st, f4 (&
   for (int i = 0; i < 4; ++i) xa[i] = (xrow && unit_ok) ? st.xa[i] : zero8;
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
-    h2 zc1 = {}, zc2 = {};
-    if constexpr (FMT == WQ_FMT_W4G32) w4_consts(st.z[r], zc1, zc2);
     h2 wv[16];
-    decode<FMT>(st.w[r], zc1, zc2, wv);
-    if constexpr (FMT == WQ_FMT_W4G32) {
-      const _Float16 sv = __builtin_bit_cast(_Float16, st.s[r]);
-      const h2 s2 = {sv, sv};
+    if constexpr (bf16_act(FMT)) {
+      if constexpr (wfmt(FMT) == WQ_FMT_W4G32) decode_bf16<FMT>(st.w[r], st.s[r], st.z[r], wv);
+      else decode_bf16<FMT>(st.w[r], 0, 0, wv);
+    } else {
+      h2 zc1 = {}, zc2 = {};
+      if constexpr (wfmt(FMT) == WQ_FMT_W4G32) w4_consts(st.z[r], zc1, zc2);
+      decode<FMT>(st.w[r], zc1, zc2, wv);
+      if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+        const _Float16 sv = __builtin_bit_cast(_Float16, st.s[r]);
+        const h2 s2 = {sv, sv};
 #pragma unroll
-      for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
+        for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h8 bfrag;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { bfrag[2 * j] = wv[4 * i + j][0]; bfrag[2 * j + 1] = wv[4 * i + j][1]; }
-      acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[i], bfrag, acc[r], 0, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i) acc[r] = mfma16<FMT>(xa[i], frag_of(wv, i), acc[r]);
   }
 }
 
@@ -628,7 +810,7 @@ __device__ __forceinline__ void mfma_body(const uint16_t* __restrict__ x, const 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * q + i;
-      if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(t[i] * sc));
+      if (m < M) y[(size_t)m * N + n] = out16<FMT>(t[i] * sc);
     }
   };
   if (WK == 1) {
@@ -688,17 +870,17 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_grouped_kernel(const
 // K tile j (0..7) of a stage is 4 units, one per lane quad q: unit 8q + j. Its x fragments
 // sit in a register ring of lm_xring slots and are loaded lm_xring - 1 tiles ahead (W4 keeps
 // the ring at 2 so that its two-block kernel fits 256 VGPRs: two waves per SIMD).
-template <int FMT> constexpr bool lm_w6() { return FMT == WQ_FMT_W6E3M2; }   // two plane slices per unit
+template <int FMT> constexpr bool lm_w6() { return wfmt(FMT) == WQ_FMT_W6E3M2; }   // two plane slices per unit
 template <int FMT> constexpr int lm_block() { return lm_w6<FMT>() ? 16 * 512 + 16 * 256 : 16 * 512; }
 template <int FMT> constexpr int lm_loads() { return lm_w6<FMT>() ? 12 : 8; }
-template <int FMT, int MT> constexpr int lm_xring() { return FMT == WQ_FMT_W4G32 || MT > 1 ? 2 : 4; }
+template <int FMT, int MT> constexpr int lm_xring() { return wfmt(FMT) == WQ_FMT_W4G32 || MT > 1 ? 2 : 4; }
 constexpr int LM_MAX_MT = 4;   // 16-row tiles of x per launch (M up to 64 reads the weights once)
 constexpr int LM_WAVES = 4;   // waves per workgroup
 
 template <int FMT, int RB>
 struct LmStage {
   uint4 v[RB][lm_loads<FMT>()];
-  uint4 s[FMT == WQ_FMT_W4G32 ? RB : 1], z[FMT == WQ_FMT_W4G32 ? RB : 1];   // W4: 8 groups' fp16 scales / zeros
+  uint4 s[wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1], z[wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1];   // W4: 8 groups' fp16 scales / zeros
 };
 
 // Global loads of stage h (units 32h .. 32h+31 of each row) of RB row blocks.
@@ -720,7 +902,7 @@ __device__ __forceinline__ void lm_load(LmStage<FMT, RB>& st, const uint8_t* __r
         st.v[r][i] = ld_nt16(rowb + nn * row_bytes + 16u * j);
       }
     }
-    if constexpr (FMT == WQ_FMT_W4G32) {
+    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
       // lane (n, q): groups 32h + 8q .. +7 of row n (U is a multiple of 8, so a group of 8 lies
       // wholly inside the row or wholly past its end; one past the end reads the row's last 8)
       const uint32_t nn = (uint32_t)(min(n0 + 16 * r + (lane & 15), N - 1) - nb);
@@ -802,7 +984,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
     for (int mt = 0; mt < MT; ++mt) acc[r][mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   LmStage<FMT, RB> st;
-  constexpr int MS = FMT == WQ_FMT_W4G32 ? RB : 1;
+  constexpr int MS = wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1;
   uint4 cs[MS], cz[MS];   // W4: the metadata of the stage in LDS
   constexpr int XR = lm_xring<FMT, MT>();
   h8 xr[XR][MT][4];
@@ -819,7 +1001,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
   };
   auto park = [&]() {   // the loaded stage -> LDS (and W4 metadata -> cs, cz)
     lm_store<FMT, RB>(st, lds, lane);
-    if constexpr (FMT == WQ_FMT_W4G32) {
+    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
 #pragma unroll
       for (int r = 0; r < RB; ++r) { cs[r] = st.s[r]; cz[r] = st.z[r]; }
     }
@@ -844,31 +1026,32 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const uint8_t* base = lds + r * lm_block<FMT>();
-        Raw<FMT> raw;
-        h2 zc1 = {}, zc2 = {};
+        Raw<wfmt(FMT)> raw;
         raw.a = *reinterpret_cast<const uint4*>(base + 512 * nl + 16 * (u ^ nl));
-        if constexpr (FMT == WQ_FMT_W6E3M2) {
+        if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2)
           raw.b = *reinterpret_cast<const uint2*>(base + 8192 + 256 * nl + 8 * (u ^ ((2 * nl) & 31)));
-        } else if constexpr (FMT == WQ_FMT_W4G32) {
-          w4_consts(half_of(cz[r], j), zc1, zc2);
-        }
         h2 wv[16];
-        decode<FMT>(raw, zc1, zc2, wv);
-        if constexpr (FMT == WQ_FMT_W4G32) {
-          const _Float16 sv = __builtin_bit_cast(_Float16, half_of(cs[r], j));
-          const h2 s2 = {sv, sv};
+        if constexpr (bf16_act(FMT)) {
+          if constexpr (wfmt(FMT) == WQ_FMT_W4G32) decode_bf16<FMT>(raw, half_of(cs[r], j), half_of(cz[r], j), wv);
+          else decode_bf16<FMT>(raw, 0, 0, wv);
+        } else {
+          h2 zc1 = {}, zc2 = {};
+          if constexpr (wfmt(FMT) == WQ_FMT_W4G32) w4_consts(half_of(cz[r], j), zc1, zc2);
+          decode<FMT>(raw, zc1, zc2, wv);
+          if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+            const _Float16 sv = __builtin_bit_cast(_Float16, half_of(cs[r], j));
+            const h2 s2 = {sv, sv};
 #pragma unroll
-          for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
+            for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
+          }
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          h8 b;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { b[2 * e] = wv[4 * k + e][0]; b[2 * e + 1] = wv[4 * k + e][1]; }
+          const h8 b = frag_of(wv, k);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const bool ok = uok && 16 * mt + nl < M;
-            acc[r][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ok ? xr[t % XR][mt][k] : zero8, b, acc[r][mt], 0, 0, 0);
+            acc[r][mt] = mfma16<FMT>(ok ? xr[t % XR][mt][k] : zero8, b, acc[r][mt]);
           }
         }
       }
@@ -898,7 +1081,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int m = 16 * mt + 4 * q + k;
-          if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)(t[k] * sc));
+          if (m < M) y[(size_t)m * N + n] = out16<FMT>(t[k] * sc);
         }
       }
     }
@@ -934,11 +1117,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (size_t)N * U) return;
   const int n = (int)(gid / U), u = (int)(gid % U);
-  Raw<FMT> raw;
+  Raw<wfmt(FMT)> raw;
   load_unit<FMT>(w, n, u, U, raw);
   h2 zc1 = {}, zc2 = {};
   float s = 1.0f;
-  if constexpr (FMT == WQ_FMT_W4G32) {
+  if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
     w4_consts(zeros[gid], zc1, zc2);
     s = f16_to_f32(scales[gid]);
   } else if constexpr (row_scaled<FMT>()) {
@@ -949,8 +1132,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   uint32_t o[16];
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
-    if constexpr (FMT == WQ_FMT_F16) {
-      o[p] = as_u32(wv[p]);
+    if constexpr (wfmt(FMT) == WQ_FMT_F16) {
+      o[p] = as_u32(wv[p]);   // F16 and BF16 weights: a copy
+    } else if constexpr (bf16_act(FMT)) {
+      o[p] = as_u32(pack_bf16((float)wv[p][0] * s, (float)wv[p][1] * s));
     } else {
       const _Float16 a = (_Float16)((float)wv[p][0] * s), b = (_Float16)((float)wv[p][1] * s);
       o[p] = as_u32(h2{a, b});
@@ -963,7 +1148,24 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 
 // ---------------------------------------------------------------- host-side planning
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
-bool valid_fmt(int fmt) { return fmt >= WQ_FMT_F16 && fmt <= WQ_FMT_W4E2M1; }
+// Every kernel code: the weight formats with fp16 activations, and with bfloat16 ones.
+#define WQ_KERNEL_CODES(X)                                                                              \
+  X(WQ_FMT_F16) X(WQ_FMT_W8) X(WQ_FMT_W4G32) X(WQ_FMT_W6E3M2) X(WQ_FMT_W4E2M1)                          \
+  X(WQ_FMT_W8 | WQ_ACT_BF16) X(WQ_FMT_W4G32 | WQ_ACT_BF16) X(WQ_FMT_W6E3M2 | WQ_ACT_BF16)              \
+  X(WQ_FMT_W4E2M1 | WQ_ACT_BF16) X(WQ_FMT_BF16 | WQ_ACT_BF16)
+
+bool valid_fmt(int code) {
+  switch (code) {
+#define WQ_CASE(C) case C:
+    WQ_KERNEL_CODES(WQ_CASE)
+#undef WQ_CASE
+    return true;
+    default: return false;
+  }
+}
+
+// The planner below decides by weight layout (wfmt of a kernel code): the activation type
+// changes the decode, not the bytes or the shape of the work.
 
 struct GemvPlan {
   int B;      // rows per wave
@@ -1114,7 +1316,7 @@ void lm_launch(dim3 grid, size_t shm, hipStream_t s, const uint16_t* x, const ui
 template <int FMT>
 hipError_t launch_lm(int RB, int M, dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
                      const uint16_t* z, uint16_t* y, int N, int K, int WK, const GemvGroup* g) {
-  if constexpr (FMT == WQ_FMT_W4G32 || FMT == WQ_FMT_W6E3M2 || FMT == WQ_FMT_W4E2M1) {
+  if constexpr (wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1) {
     const size_t shm = (size_t)LM_WAVES * RB * lm_block<FMT>();
     const int MT = lm_tiles(M);
     if (RB == 2) {
@@ -1134,12 +1336,12 @@ hipError_t launch_lm(int RB, int M, dim3 grid, hipStream_t s, const uint16_t* x,
 template <int FMT>
 hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
                              uint16_t* y, int M, int N, int K) {
-  if (use_lm(FMT, M, N, K)) {
+  if (use_lm(wfmt(FMT), M, N, K)) {
     const LmPlan p = plan_lm(N, K);
     return launch_lm<FMT>(p.RB, M, dim3(p.grid), s, x, w, sc, z, y, N, K, p.WK, nullptr);
   }
-  if (!use_mfma(FMT, M, N)) {
-    const GemvPlan p = plan_gemv(FMT, N, K);
+  if (!use_mfma(wfmt(FMT), M, N)) {
+    const GemvPlan p = plan_gemv(wfmt(FMT), N, K);
     switch (M) {
       case 1: return launch_gemv_m<FMT, 1>(p, s, x, w, sc, z, y, N, K);
       case 2: return launch_gemv_m<FMT, 2>(p, s, x, w, sc, z, y, N, K);
@@ -1147,10 +1349,10 @@ hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w,
       default: return launch_gemv_m<FMT, 4>(p, s, x, w, sc, z, y, N, K);
     }
   }
-  if constexpr (FMT == WQ_FMT_W6E3M2 || FMT == WQ_FMT_W4E2M1) {
+  if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1) {
     return hipErrorInvalidValue;   // W6 and FP4 on the matrix cores always take lm_kernel (use_lm)
   } else {
-    const MfmaPlan p = plan_mfma(FMT, N, K);
+    const MfmaPlan p = plan_mfma(wfmt(FMT), N, K);
     const dim3 grid(p.grid), block(64 * p.WK);
     switch (p.RB) {
       case 4: hipLaunchKernelGGL((mfma_kernel<FMT, 4>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
@@ -1232,8 +1434,8 @@ int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, cons
                       int64_t M, int64_t N, int64_t K, int fmt) {
   if (!valid_fmt(fmt)) return WQ_ERR_FMT;
   if (!x || !w || !y || M < 0 || N < 0 || K < 0) return WQ_ERR_ARG;
-  if (fmt != WQ_FMT_F16 && !sc) return WQ_ERR_ARG;
-  if (fmt == WQ_FMT_W4G32 && !z) return WQ_ERR_ARG;
+  if (wfmt(fmt) != WQ_FMT_F16 && !sc) return WQ_ERR_ARG;
+  if (wfmt(fmt) == WQ_FMT_W4G32 && !z) return WQ_ERR_ARG;
   if (M < 1 || N < 1 || K < 32 || K % 32) return WQ_ERR_SHAPE;
   if (N > INT32_MAX / 2 || K > (int64_t(1) << 26) || (N * (K / 32)) > INT32_MAX) return WQ_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (sc && !aligned16(sc)) || (z && !aligned16(z))) return WQ_ERR_ALIGN;
@@ -1243,7 +1445,7 @@ int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, cons
 template <int FMT>
 hipError_t launch_grouped_mc(Family f, const GemvGroup& g, int M, int RB, int block_waves, int grid, hipStream_t s) {
   if (f == FAM_LM) return launch_lm<FMT>(RB, M, dim3(grid), s, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, &g);
-  if constexpr (FMT == WQ_FMT_W6E3M2 || FMT == WQ_FMT_W4E2M1) {
+  if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1) {
     return hipErrorInvalidValue;   // W6 and FP4 groups on the matrix cores are always FAM_LM
   } else {
     switch (RB) {
@@ -1265,18 +1467,17 @@ int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, c
   if (st != WQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* w = static_cast<const uint8_t*>(packed_w);
-  const int64_t slab = slab_rows(fmt, K);
+  const int64_t slab = slab_rows(wfmt(fmt), K);
   for (int64_t m0 = 0; m0 < M; m0 += slab) {
     const int mm = static_cast<int>(M - m0 < slab ? M - m0 : slab);
     const uint16_t* xs = x + m0 * K;
     uint16_t* ys = y + m0 * N;
     hipError_t e = hipSuccess;
     switch (fmt) {
-      case WQ_FMT_W8: e = launch_linear_fmt<WQ_FMT_W8>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
-      case WQ_FMT_W4G32: e = launch_linear_fmt<WQ_FMT_W4G32>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
-      case WQ_FMT_W6E3M2: e = launch_linear_fmt<WQ_FMT_W6E3M2>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
-      case WQ_FMT_W4E2M1: e = launch_linear_fmt<WQ_FMT_W4E2M1>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
-      default: e = launch_linear_fmt<WQ_FMT_F16>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
+#define WQ_CASE(C) case C: e = launch_linear_fmt<C>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
+      WQ_KERNEL_CODES(WQ_CASE)
+#undef WQ_CASE
+      default: return WQ_ERR_FMT;
     }
     if (e != hipSuccess) return WQ_ERR_DEVICE;
   }
@@ -1287,8 +1488,8 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
                int64_t K, void* stream) {
   if (!valid_fmt(fmt)) return WQ_ERR_FMT;
   if (!packed || !w_out || N < 0 || K < 0) return WQ_ERR_ARG;
-  if (fmt != WQ_FMT_F16 && !scales) return WQ_ERR_ARG;
-  if (fmt == WQ_FMT_W4G32 && !zeros) return WQ_ERR_ARG;
+  if (wfmt(fmt) != WQ_FMT_F16 && !scales) return WQ_ERR_ARG;
+  if (wfmt(fmt) == WQ_FMT_W4G32 && !zeros) return WQ_ERR_ARG;
   if (N < 1 || K < 32 || K % 32) return WQ_ERR_SHAPE;
   if (N * (K / 32) > INT32_MAX) return WQ_ERR_SHAPE;
   if (!aligned16(packed) || !aligned16(w_out) || (scales && !aligned16(scales)) || (zeros && !aligned16(zeros)))
@@ -1298,11 +1499,11 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
   const int64_t units = N * (K / 32);
   const dim3 grid(static_cast<unsigned>((units + 255) / 256)), block(256);
   switch (fmt) {
-    case WQ_FMT_W8: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_W8>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
-    case WQ_FMT_W4G32: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_W4G32>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
-    case WQ_FMT_W6E3M2: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_W6E3M2>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
-    case WQ_FMT_W4E2M1: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_W4E2M1>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
-    default: hipLaunchKernelGGL(dequant_kernel<WQ_FMT_F16>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
+#define WQ_CASE(C) \
+  case C: hipLaunchKernelGGL(dequant_kernel<C>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
+    WQ_KERNEL_CODES(WQ_CASE)
+#undef WQ_CASE
+    default: return WQ_ERR_FMT;
   }
   return hipGetLastError() == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
 }
@@ -1321,8 +1522,9 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
   // one family and one rows-per-wave (B or RB) for the whole launch: the largest item's (the
   // small items alone would pick fewer rows per wave to get enough waves, which the launch
   // has anyway); each item keeps the K split its own plan gives for that B / RB
-  const Family fam = group_family(fmt, M, Ns, Ks, count);
-  if (M > group_launch_rows(fam, fmt, Ks, count)) {   // several slabs: one wq_linear per item
+  const int pf = wfmt(fmt);
+  const Family fam = group_family(pf, M, Ns, Ks, count);
+  if (M > group_launch_rows(fam, pf, Ks, count)) {   // several slabs: one wq_linear per item
     for (int i = 0; i < count; ++i) {
       const wq_linear_item& it = items[i];
       const int st = wq_linear(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt, stream);
@@ -1330,7 +1532,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
     }
     return WQ_OK;
   }
-  const int B = group_rows(fam, fmt, Ns, Ks, count);
+  const int B = group_rows(fam, pf, Ns, Ks, count);
   int order[MAX_GROUP];
   grouped_order(items, count, order);
   GemvGroup g = {};
@@ -1338,7 +1540,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
   int block_waves = fam == FAM_GEMV ? GEMV_WAVES : fam == FAM_LM ? LM_WAVES : 1;
   for (int i = 0; i < count; ++i) {
     const int64_t n = items[order[i]].N, k = items[order[i]].K;
-    g.WK[i] = fam == FAM_GEMV ? gemv_waves_for(fmt, n, k, B) : fam == FAM_LM ? lm_waves_for(n, k, B) : mfma_waves_for(n, k, B);
+    g.WK[i] = fam == FAM_GEMV ? gemv_waves_for(pf, n, k, B) : fam == FAM_LM ? lm_waves_for(n, k, B) : mfma_waves_for(n, k, B);
     if (fam == FAM_MFMA) block_waves = std::max(block_waves, g.WK[i]);   // powers of two up to MFMA_MAX_WAVES
   }
   const int rows_per_block = fam == FAM_GEMV ? B : 16 * B;
@@ -1361,19 +1563,17 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
   hipError_t e;
   if (fam == FAM_GEMV) {
     switch (fmt) {
-      case WQ_FMT_W8: e = launch_grouped_fmt<WQ_FMT_W8>(g, (int)M, B, block_waves, grid, s); break;
-      case WQ_FMT_W4G32: e = launch_grouped_fmt<WQ_FMT_W4G32>(g, (int)M, B, block_waves, grid, s); break;
-      case WQ_FMT_W6E3M2: e = launch_grouped_fmt<WQ_FMT_W6E3M2>(g, (int)M, B, block_waves, grid, s); break;
-      case WQ_FMT_W4E2M1: e = launch_grouped_fmt<WQ_FMT_W4E2M1>(g, (int)M, B, block_waves, grid, s); break;
-      default: e = launch_grouped_fmt<WQ_FMT_F16>(g, (int)M, B, block_waves, grid, s); break;
+#define WQ_CASE(C) case C: e = launch_grouped_fmt<C>(g, (int)M, B, block_waves, grid, s); break;
+      WQ_KERNEL_CODES(WQ_CASE)
+#undef WQ_CASE
+      default: return WQ_ERR_FMT;
     }
   } else {
     switch (fmt) {
-      case WQ_FMT_W8: e = launch_grouped_mc<WQ_FMT_W8>(fam, g, (int)M, B, block_waves, grid, s); break;
-      case WQ_FMT_W4G32: e = launch_grouped_mc<WQ_FMT_W4G32>(fam, g, (int)M, B, block_waves, grid, s); break;
-      case WQ_FMT_W6E3M2: e = launch_grouped_mc<WQ_FMT_W6E3M2>(fam, g, (int)M, B, block_waves, grid, s); break;
-      case WQ_FMT_W4E2M1: e = launch_grouped_mc<WQ_FMT_W4E2M1>(fam, g, (int)M, B, block_waves, grid, s); break;
-      default: e = launch_grouped_mc<WQ_FMT_F16>(fam, g, (int)M, B, block_waves, grid, s); break;
+#define WQ_CASE(C) case C: e = launch_grouped_mc<C>(fam, g, (int)M, B, block_waves, grid, s); break;
+      WQ_KERNEL_CODES(WQ_CASE)
+#undef WQ_CASE
+      default: return WQ_ERR_FMT;
     }
   }
   return e == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
@@ -1382,14 +1582,15 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
 const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   static thread_local char buf[96];
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 32 || K % 32) return "";
-  const int64_t mm = M < slab_rows(fmt, K) ? M : slab_rows(fmt, K);   // the first launch's rows
-  if (use_lm(fmt, mm, N, K)) {
+  const int pf = wfmt(fmt);
+  const int64_t mm = M < slab_rows(pf, K) ? M : slab_rows(pf, K);   // the first launch's rows
+  if (use_lm(pf, mm, N, K)) {
     snprintf(buf, sizeof(buf), "lm_kernel<%d, %d, %d>", fmt, plan_lm(N, K).RB, lm_tiles(mm));
-  } else if (!use_mfma(fmt, mm, N)) {
-    const GemvPlan p = plan_gemv(fmt, N, K);
+  } else if (!use_mfma(pf, mm, N)) {
+    const GemvPlan p = plan_gemv(pf, N, K);
     snprintf(buf, sizeof(buf), "gemv_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), p.B);
   } else {
-    snprintf(buf, sizeof(buf), "mfma_kernel<%d, %d>", fmt, plan_mfma(fmt, N, K).RB);
+    snprintf(buf, sizeof(buf), "mfma_kernel<%d, %d>", fmt, plan_mfma(pf, N, K).RB);
   }
   return buf;
 }
@@ -1400,10 +1601,11 @@ const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, 
   for (int i = 0; i < count; ++i)
     if (N[i] < 1 || K[i] < 32 || K[i] % 32) return "";
   const int big = largest_item(N, K, count);
-  const Family fam = group_family(fmt, M, N, K, count);
-  if (M > group_launch_rows(fam, fmt, K, count))
+  const int pf = wfmt(fmt);
+  const Family fam = group_family(pf, M, N, K, count);
+  if (M > group_launch_rows(fam, pf, K, count))
     return wq_linear_kernel_name(fmt, M, N[big], K[big]);   // separate launches: the largest item's
-  const int B = group_rows(fam, fmt, N, K, count);
+  const int B = group_rows(fam, pf, N, K, count);
   if (fam == FAM_GEMV) snprintf(buf, sizeof(buf), "gemv_grouped_kernel<%d, %d, %d>", fmt, static_cast<int>(M), B);
   else if (fam == FAM_LM) snprintf(buf, sizeof(buf), "lm_grouped_kernel<%d, %d, %d>", fmt, B, lm_tiles(M));
   else snprintf(buf, sizeof(buf), "mfma_grouped_kernel<%d, %d>", fmt, B);

@@ -11,8 +11,11 @@ import os
 
 import numpy as np
 
-FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1 = 0, 1, 2, 3, 4
-FMT_NAMES = {"f16": FMT_F16, "w8": FMT_W8, "w4g32": FMT_W4G32, "w6e3m2": FMT_W6E3M2, "w4e2m1": FMT_W4E2M1}
+FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, FMT_BF16 = 0, 1, 2, 3, 4, 5
+FMT_NAMES = {"f16": FMT_F16, "w8": FMT_W8, "w4g32": FMT_W4G32, "w6e3m2": FMT_W6E3M2, "w4e2m1": FMT_W4E2M1,
+             "bf16": FMT_BF16}
+# OR-ed into a format code: bfloat16 activations (x, y and dequantized weights) instead of fp16
+ACT_F16, ACT_BF16 = 0, 0x100
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwq.so")
@@ -172,7 +175,7 @@ def wq_pack_fp4(w):
 def wq_unpack(fmt, packed, scales, zeros, n, k):
     """packed (host) -> (logical codes [N,K], scales copy, zeros copy)."""
     dtype = {FMT_W8: np.int8, FMT_W4G32: np.uint8, FMT_W6E3M2: np.uint8, FMT_W4E2M1: np.uint8,
-             FMT_F16: np.uint16}.get(fmt, np.uint8)
+             FMT_F16: np.uint16, FMT_BF16: np.uint16}.get(fmt, np.uint8)
     codes = np.empty((n, k), dtype=dtype)
     s_out = np.empty(max(wq_scales_bytes(fmt, n, k) // 2, 1), dtype=np.uint16)
     z_out = np.empty(max(wq_zeros_bytes(fmt, n, k) // 2, 1), dtype=np.uint16)
