@@ -45,6 +45,20 @@ from weight_only_quantized_dequant_amd import inputs, wq  # noqa: E402
 PEAK_HBM_GBS = 8000.0
 METRIC = "weight-stream HBM GB/s (% of peak) for W8/W6/W4-A16 linear, M=1..16"
 FMT_OF = {"w8": wq.FMT_W8, "w4g32": wq.FMT_W4G32, "w6e3m2": wq.FMT_W6E3M2, "w4e2m1": wq.FMT_W4E2M1, "f16": wq.FMT_F16}
+# the same weights with bfloat16 activations ("_bf16"), and plain bfloat16 weights as their baseline
+FMT_OF.update({k + "_bf16": v | wq.ACT_BF16 for k, v in list(FMT_OF.items()) if k != "f16"})
+FMT_OF["bf16"] = wq.FMT_BF16 | wq.ACT_BF16
+
+
+def is_bf16(code):
+    return bool(code & wq.ACT_BF16)
+
+
+def bf16_bits(a):
+    """float array -> bfloat16 bit patterns (torch's float32 -> bfloat16 rounding, nearest even)."""
+    import torch
+    f = torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.float32)))
+    return f.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 ROTATE_BYTES = 1 << 30
 
 
@@ -100,6 +114,9 @@ def metadata_bytes(fmt, n, k):
 
 def pack(fmt, w):
     """Quantize + pack fp32 W with libwq's host packers: (packed, scales or None, zeros or None)."""
+    fmt &= 0xFF
+    if fmt == wq.FMT_BF16:
+        return bf16_bits(w).view(np.uint8).reshape(-1), None, None
     if fmt == wq.FMT_W8:
         return wq.wq_pack_int8(w) + (None,)
     if fmt == wq.FMT_W4G32:
@@ -203,10 +220,13 @@ def gpu_state(torch):
     return state
 
 
-def cpu_baseline(fmt, linears_host, seconds):
+def cpu_baseline(code, linears_host, seconds):
     """The oracle (test infrastructure) timed on a bounded sample: per linear, a block of rows is
     unpacked, dequantized and multiplied in float64, repeated until `seconds` have passed."""
     import oracle  # the oracle is imported here only, for this reported baseline
+    fmt = code & 0xFF
+    act = oracle.ACT_BF16 if is_bf16(code) else oracle.ACT_F16
+    dequant = oracle.dequant_bf16 if is_bf16(code) else oracle.dequant_fp16
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
@@ -225,8 +245,8 @@ def cpu_baseline(fmt, linears_host, seconds):
     while True:
         for (pp, ss, zz, r, k, x, b) in work:
             codes = oracle.unpack_vectorized(fmt, pp, r, k)
-            wd = oracle.dequant_fp16(fmt, codes, ss, zz)
-            oracle.linear_ref(x, wd)
+            wd = dequant(fmt, codes, ss, zz)
+            oracle.linear_ref(x, wd, act=act)
             done_bytes += b
         reps += 1
         if time.perf_counter() - t0 >= seconds:
@@ -241,7 +261,7 @@ def cpu_baseline(fmt, linears_host, seconds):
             b1, t1, r1 = 0, time.perf_counter(), 0
             while time.perf_counter() - t1 < seconds / 4:
                 for (pp, ss, zz, r, k, x, b) in work:
-                    oracle.linear_ref(x, oracle.dequant_fp16(fmt, oracle.unpack_vectorized(fmt, pp, r, k), ss, zz))
+                    oracle.linear_ref(x, dequant(fmt, oracle.unpack_vectorized(fmt, pp, r, k), ss, zz), act=act)
                     b1 += b
                 r1 += 1
             out["single_thread"] = {"value": b1 / (time.perf_counter() - t1) / 1e9, "unit": "GB/s", "passes": r1}
@@ -354,6 +374,8 @@ def main():
     host = []
     for li, (n, k) in enumerate(shapes):
         w, x = inputs.weights_and_x(inputs.rng_for(stream_id, li), n, k, max(ms + [m]))
+        if is_bf16(fmt):   # the same draws, rounded to bfloat16
+            x = bf16_bits(x.view(np.float16).astype(np.float32))
         host.append((w, x[:m]))
     step_weight_bytes = sum(wq.wq_packed_bytes(fmt, n, k) + metadata_bytes(fmt, n, k) for n, k in shapes)
     rot = max(1, math.ceil(ROTATE_BYTES / step_weight_bytes))
@@ -419,13 +441,15 @@ def main():
     if not args.no_baselines:
         f16_bytes = sum(2 * n * k for n, k in shapes)
         rot16 = max(1, math.ceil(ROTATE_BYTES / f16_bytes))
-        f16 = [Linear(torch, wq.FMT_F16, w, x, rot16) for (w, x) in host]
+        base16 = wq.FMT_BF16 | wq.ACT_BF16 if is_bf16(fmt) else wq.FMT_F16   # 16-bit weights of the activation type
+        f16 = [Linear(torch, base16, w, x, rot16) for (w, x) in host]
         ms16g = time_steps(torch, grouped_step(f16, rot16), steps, args.warmup, rot16)
         ms16s = time_steps(torch, separate_step(f16, rot16), steps, args.warmup, rot16)
         # torch F.linear (hipBLASLt) on the same fp16 weights, same rotation
         import torch.nn.functional as F
-        tw = [[c[0].view(torch.float16).view(l.n, l.k) for c in l.copies] for l in f16]
-        tx = [l.x.view(torch.float16) for l in f16]
+        tdt = torch.bfloat16 if is_bf16(fmt) else torch.float16
+        tw = [[c[0].view(tdt).view(l.n, l.k) for c in l.copies] for l in f16]
+        tx = [l.x.view(tdt) for l in f16]
         def vendor_step(i):
             for j in range(len(f16)):
                 F.linear(tx[j], tw[j][i % rot16])
@@ -456,7 +480,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms_total / steps, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if is_bf16(fmt) else "f16", "data": "synthetic",
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "config": {"workload": args.workload, "weights": fmt_name, "M": m,
                    "shapes_NxK": ["%dx%d" % s for s in shapes], "weight_bytes_per_step": step_weight_bytes,

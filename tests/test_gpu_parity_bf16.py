@@ -181,17 +181,22 @@ def test_grouped_bf16_matches_separate_calls(fmt, m, set_name):
             assert np.array_equal(got, sep[i]), "item %d differs from its separate call (%s, %s)" % (i, own, grouped)
 
 
-def test_llama7b_w4_bf16_full_size_sampled():
-    _, shapes, _ = inputs.WORKLOADS["llama7b_w4g32_linears"]
+FULL = [("llama7b_w4g32_bf16_linears", wq.FMT_W4G32), ("llama70b_w6e3m2_bf16_linears", wq.FMT_W6E3M2)]
+
+
+@pytest.mark.parametrize("name,fmt", FULL, ids=[f[0] for f in FULL])
+def test_workload_bf16_full_size_sampled(name, fmt):
+    # the bench workloads at full size and every M they are timed at, on sampled output rows
+    _, shapes, ms = inputs.WORKLOADS[name]
     for li, (n, k) in enumerate(shapes):
-        w, x16 = inputs.weights_and_x(inputs.rng_for(inputs.WORKLOAD_STREAM["llama7b_w4g32_linears"], li), n, k, 16)
+        w, x16 = inputs.weights_and_x(inputs.rng_for(inputs.WORKLOAD_STREAM[name], li), n, k, max(ms))
         x = x_as_bf16(x16)
-        dw = DeviceWeights(wq.FMT_W4G32, w, BF)
+        dw = DeviceWeights(fmt, w, BF)
         rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(li).choice(n, 62, replace=False)]))
-        wd = oracle_rows(wq.FMT_W4G32, w[rows], BF)[0]
-        for m in (1, 4, 16):
+        wd = oracle_rows(fmt, w[rows], BF)[0]
+        for m in ms:
             y = dw.linear(x[:m])
-            check_linear(y[:, rows], x[:m], wd, "linear %d (%dx%d) m %d" % (li, n, k, m), act=BF)
+            check_linear(y[:, rows], x[:m], wd, "%s linear %d (%dx%d) m %d" % (name, li, n, k, m), act=BF)
         del dw
         torch_cuda().cuda.empty_cache()
 
