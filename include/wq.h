@@ -50,8 +50,8 @@
  *
  * Activations: by default x, y and dequantized weights are fp16. OR-ing WQ_ACT_BF16 into the
  * fmt argument of wq_dequant, wq_linear, wq_linear_grouped and the kernel-name calls makes them
- * bfloat16 (the other activation type the gpt-fast guide, www.jsqmd.com, section
- * "量化技术深度解析", offers). The packed weights and their fp16 metadata are the same for both;
+ * bfloat16 (named besides fp16 by the gpt-fast guide, www.jsqmd.com, section "混合精度训练与推理",
+ * and the speed-up strategies page, sharktoolz.top, section 4). The packed weights and their fp16 metadata are the same for both;
  * the product still accumulates in fp32, and the dequantized value of a weight is its exact
  * value rounded once to bfloat16. Valid codes with the flag: W8, W4G32, W6E3M2, W4E2M1 and BF16;
  * F16 weights take fp16 activations only and BF16 weights bfloat16 ones (else WQ_ERR_FMT).

@@ -15,8 +15,8 @@ width). These pages describe the method:
 * gpt-fast write-up (m.greenbasetech.com): decode is bound by memory bandwidth, and
   int8, then groupwise int4, weight quantization cut the bytes per parameter.
 * gpt-fast guide "终极PyTorch原生Transformer文本生成：gpt-fast极速体验指南"
-  (www.jsqmd.com), section "量化技术深度解析": int4 with group size 32, and bfloat16
-  as an alternative to fp16.
+  (www.jsqmd.com), section "量化技术深度解析": int4 with group size 32; section
+  "混合精度训练与推理": bfloat16 as an alternative to fp16.
 * FP6-LLM news "单卡跑Llama 70B快过双卡，微软硬生生把FP6搞到了A100里"
   (m.zhengruan.com), section "重新设计内核方案": FP6 weights dequantized to FP16
   inside one fused kernel, with the weights bit-level pre-packed offline into aligned

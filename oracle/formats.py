@@ -12,9 +12,10 @@ names none. FP4 is taken here as e2m1: 1 sign bit, 2 exponent bits with bias 1, 
 mantissa bit, subnormals when the exponent field is 0, no infinities or NaNs, largest
 magnitude 6 (the eight magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
 
-bfloat16 is the activation type the gpt-fast guide (www.jsqmd.com, section
-"量化技术深度解析") offers besides fp16: the 8-bit exponent of binary32 with 8
-significant bits (7 stored), rounded to nearest with ties to even.
+bfloat16 is the activation type named besides fp16 by the gpt-fast guide (www.jsqmd.com,
+section "混合精度训练与推理") and the speed-up strategies page (sharktoolz.top, section 4
+"Reduce model weight"): the 8-bit exponent of binary32 with 8 significant bits (7 stored),
+rounded to nearest with ties to even.
 """
 
 import numpy as np

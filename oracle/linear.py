@@ -10,9 +10,10 @@ reference below is therefore the exact sum, computed in float64, of the fp16 inp
 times the fp16 dequantised weights. A device result is accepted when it lies within the
 bound given by ``error_bound``.
 
-With bfloat16 activations (the dtype the gpt-fast guide, www.jsqmd.com, section
-"量化技术深度解析", offers besides fp16) the same statement holds with bfloat16 in
-place of fp16: x, the dequantised weights and y are bfloat16, the sum is fp32.
+With bfloat16 activations (named besides fp16 by the gpt-fast guide, www.jsqmd.com,
+section "混合精度训练与推理", and by the speed-up strategies page, sharktoolz.top,
+section 4 "Reduce model weight") the same statement holds with bfloat16 in place of
+fp16: x, the dequantised weights and y are bfloat16, the sum is fp32.
 """
 
 import numpy as np
