@@ -273,6 +273,11 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_grouped_kernel_name(3, 20, [(1024, 8192), (8192, 8192)]) == "lm_grouped_kernel<3, 2, 2>"
     assert wq.wq_linear_grouped_kernel_name(3, 65, [(1024, 8192), (8192, 8192)]) == "lm_kernel<3, 2, 4>"
     assert wq.wq_linear_grouped_kernel_name(1, 20, [(1024, 8192), (8192, 8192)]) == "mfma_kernel<1, 2>"
+    # the LDS-staged group takes two row blocks per wave when any item has 8192 rows or more,
+    # whatever the order of equal-size items
+    assert wq.wq_linear_grouped_kernel_name(2, 16, [(4096, 11008), (11008, 4096)]) == "lm_grouped_kernel<2, 2, 1>"
+    assert wq.wq_linear_grouped_kernel_name(2, 16, [(11008, 4096), (4096, 11008)]) == "lm_grouped_kernel<2, 2, 1>"
+    assert wq.wq_linear_grouped_kernel_name(3, 16, [(3584, 8192), (8192, 3584), (1280, 8192)]) == "lm_grouped_kernel<3, 2, 1>"
     # FP4: the GEMV up to M = 3 (and M = 4 below N*K = 2^24), the LDS-staged kernel above, for any K
     assert wq.wq_linear_kernel_name(4, 1, 4096, 4096) == "gemv_kernel<4, 1, 4>"
     assert wq.wq_linear_kernel_name(4, 4, 2048, 4096) == "gemv_kernel<4, 4, 4>"

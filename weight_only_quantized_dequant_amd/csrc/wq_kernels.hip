@@ -1263,19 +1263,22 @@ bool use_lm(int fmt, int64_t M, int64_t N, int64_t K) {
   return M > GEMV_MAX_M || (M == GEMV_MAX_M && N * K >= (int64_t(1) << 24));
 }
 
-// Two row blocks per wave from 8192 rows; WK doubled until ~1024 waves.
+// Two row blocks per wave from 8192 rows. WK doubled until ~1024 waves for W6 (one wave per
+// SIMD at two row blocks) and ~2048 for W4 and FP4 (two waves per SIMD fit): on the Llama-70B
+// gate/up pair at M = 8, W4 ran 88.5 us at 1024 and 83.5 us at 2048, W6 gained nothing.
 int lm_rows(int64_t N) { return N >= 8192 ? 2 : 1; }
 
-int lm_waves_for(int64_t N, int64_t K, int RB) {
+int lm_waves_for(int fmt, int64_t N, int64_t K, int RB) {
   const int64_t H = (K / 32 + 31) / 32;
   const int64_t groups = (N + 16 * RB - 1) / (16 * RB);
+  const int64_t target = fmt == WQ_FMT_W6E3M2 ? 1024 : 2048;
   int WK = 1;
-  while (WK < LM_WAVES && WK < H && groups * WK < 1024) WK *= 2;
+  while (WK < LM_WAVES && WK < H && groups * WK < target) WK *= 2;
   return WK;
 }
 
-LmPlan plan_lm(int64_t N, int64_t K) {
-  const int RB = lm_rows(N), WK = lm_waves_for(N, K, RB);
+LmPlan plan_lm(int fmt, int64_t N, int64_t K) {
+  const int RB = lm_rows(N), WK = lm_waves_for(fmt, N, K, RB);
   const int64_t groups = (N + 16 * RB - 1) / (16 * RB);
   const int R = LM_WAVES / WK;
   return {RB, WK, static_cast<int>((groups + R - 1) / R)};
@@ -1337,7 +1340,7 @@ template <int FMT>
 hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
                              uint16_t* y, int M, int N, int K) {
   if (use_lm(wfmt(FMT), M, N, K)) {
-    const LmPlan p = plan_lm(N, K);
+    const LmPlan p = plan_lm(wfmt(FMT), N, K);
     return launch_lm<FMT>(p.RB, M, dim3(p.grid), s, x, w, sc, z, y, N, K, p.WK, nullptr);
   }
   if (!use_mfma(wfmt(FMT), M, N)) {
@@ -1416,10 +1419,18 @@ Family group_family(int fmt, int64_t M, const int64_t* N, const int64_t* K, int 
   return f;
 }
 
-// rows per wave (GEMV) or 16-row blocks per wave (matrix cores) of a grouped launch
+// rows per wave (GEMV) or 16-row blocks per wave (matrix cores) of a grouped launch. The
+// LDS-staged kernel takes two row blocks if any item has the rows for them: picking the largest
+// item's made equal-size items (11008x4096 and 4096x11008) decide by their order, and one row
+// block cost up to a third (the Llama-70B TP8 shard group at M = 16: 43 us against 33 us).
 int group_rows(Family f, int fmt, const int64_t* N, const int64_t* K, int count) {
+  if (f == FAM_LM) {
+    int rb = 1;
+    for (int i = 0; i < count; ++i) rb = std::max(rb, lm_rows(N[i]));
+    return rb;
+  }
   const int big = largest_item(N, K, count);
-  return f == FAM_GEMV ? gemv_rows_per_wave(fmt, N[big], K[big]) : f == FAM_LM ? lm_rows(N[big]) : mfma_rows(fmt, N[big]);
+  return f == FAM_GEMV ? gemv_rows_per_wave(fmt, N[big], K[big]) : mfma_rows(fmt, N[big]);
 }
 
 // rows of x one grouped launch of this family takes for every item
@@ -1540,7 +1551,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
   int block_waves = fam == FAM_GEMV ? GEMV_WAVES : fam == FAM_LM ? LM_WAVES : 1;
   for (int i = 0; i < count; ++i) {
     const int64_t n = items[order[i]].N, k = items[order[i]].K;
-    g.WK[i] = fam == FAM_GEMV ? gemv_waves_for(pf, n, k, B) : fam == FAM_LM ? lm_waves_for(n, k, B) : mfma_waves_for(n, k, B);
+    g.WK[i] = fam == FAM_GEMV ? gemv_waves_for(pf, n, k, B) : fam == FAM_LM ? lm_waves_for(pf, n, k, B) : mfma_waves_for(n, k, B);
     if (fam == FAM_MFMA) block_waves = std::max(block_waves, g.WK[i]);   // powers of two up to MFMA_MAX_WAVES
   }
   const int rows_per_block = fam == FAM_GEMV ? B : 16 * B;
@@ -1585,7 +1596,7 @@ const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   const int pf = wfmt(fmt);
   const int64_t mm = M < slab_rows(pf, K) ? M : slab_rows(pf, K);   // the first launch's rows
   if (use_lm(pf, mm, N, K)) {
-    snprintf(buf, sizeof(buf), "lm_kernel<%d, %d, %d>", fmt, plan_lm(N, K).RB, lm_tiles(mm));
+    snprintf(buf, sizeof(buf), "lm_kernel<%d, %d, %d>", fmt, plan_lm(pf, N, K).RB, lm_tiles(mm));
   } else if (!use_mfma(pf, mm, N)) {
     const GemvPlan p = plan_gemv(pf, N, K);
     snprintf(buf, sizeof(buf), "gemv_kernel<%d, %d, %d>", fmt, static_cast<int>(mm), p.B);
