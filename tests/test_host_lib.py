@@ -265,6 +265,12 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_kernel_name(2, 64, 4096, 4128) == "mfma_kernel<2, 1>"
     assert wq.wq_linear_kernel_name(1, 40, 4096, 4096) == "mfma_kernel<1, 1>"
     assert wq.wq_linear_kernel_name(3, 100, 4096, 4096) == "lm_kernel<3, 1, 4>"
+    # from 512 rows of x on: the tiled prefill kernel, one launch for all rows
+    assert wq.wq_linear_kernel_name(3, 511, 4096, 4096) == "lm_kernel<3, 1, 4>"
+    assert wq.wq_linear_kernel_name(3, 512, 4096, 4096) == "pf_kernel<3>"
+    assert wq.wq_linear_kernel_name(2, 600, 4096, 4128) == "pf_kernel<2>"
+    assert wq.wq_linear_kernel_name(2 | wq.ACT_BF16, 512, 11008, 4096) == "pf_kernel<258>"
+    assert wq.wq_linear_kernel_name(0, 4096, 4096, 4096) == "pf_kernel<0>"
     # rows of 2^25 + 256 and more: 16-row slabs (32-bit x offsets stay in range)
     assert wq.wq_linear_kernel_name(3, 64, 64, (1 << 25) + 256) == "lm_kernel<3, 1, 1>"
     assert wq.wq_linear_kernel_name(3, 64, 64, 1 << 25) == "lm_kernel<3, 1, 4>"
@@ -272,6 +278,7 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_grouped_kernel_name(3, 16, [(64, 4096), (64, (1 << 25) + 256)]) == "lm_grouped_kernel<3, 1, 1>"
     assert wq.wq_linear_grouped_kernel_name(3, 20, [(1024, 8192), (8192, 8192)]) == "lm_grouped_kernel<3, 2, 2>"
     assert wq.wq_linear_grouped_kernel_name(3, 65, [(1024, 8192), (8192, 8192)]) == "lm_kernel<3, 2, 4>"
+    assert wq.wq_linear_grouped_kernel_name(3, 512, [(1024, 8192), (8192, 8192)]) == "pf_kernel<3>"
     assert wq.wq_linear_grouped_kernel_name(1, 20, [(1024, 8192), (8192, 8192)]) == "mfma_kernel<1, 2>"
     # the LDS-staged group takes two row blocks per wave when any item has 8192 rows or more,
     # whatever the order of equal-size items

@@ -1107,6 +1107,148 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lm_grouped_kernel(const GemvGro
                        blockIdx.x - g.first_block[j], g.WK[j]);
 }
 
+// ---------------------------------------------------------------- prefill: M > 64 on the matrix cores
+// Past 64 rows of x the weight stream stops being the only cost: the product itself, 2 M N K
+// flops, grows with M. Here a workgroup computes a 128 (x rows) x 128 (weight rows) tile of y.
+// Per K step of 64 (two 32-code units of each weight row) it parks the x tile and the weight
+// tile in LDS, the weights decoded once into 16-bit values of the activation type (the exact
+// decode of the other kernels; W4 as fp16((q - z) s), the other formats as exact code values
+// with their row scale applied to the result), and its four waves (2 x 2, 64 x 64 each) run 32
+// MFMAs from there, so each decoded weight serves 128 rows of x and each x value 128 weight
+// rows. Double-buffered LDS with one barrier per step: the global loads of step s+1 are in
+// flight while step s is multiplied, and are decoded and parked after it. LDS rows are padded
+// to 144 B, so the 16 rows of a fragment read start 36 banks apart. Each step reads two units
+// (32 B for W4) of each of 128 weight rows, a pattern HBM serves well below its contiguous rate,
+// which holds this kernel to 100-230 TFLOP/s; wq_linear takes it from 512 rows of x on, where
+// it beats launches of 64 rows that reread the weights.
+constexpr int PF_MIN_M = 512;   // M from which wq_linear takes this kernel (below, 64-row launches win)
+constexpr int PF_BM = 128, PF_BN = 128;       // tile of y
+constexpr int PF_ROW = 2 * 64 + 16;           // bytes per LDS row: 64 K of 16-bit values and padding
+constexpr int PF_TILE = 128 * PF_ROW;         // one operand tile (18 KB)
+constexpr int PF_LDS = 4 * PF_TILE;           // x and weights, two buffers each (72 KB)
+
+template <int FMT>
+struct PfStage {
+  uint4 x[4];               // 64 B: one unit's 32 values of one x row
+  Raw<wfmt(FMT)> w;         // one unit of one weight row
+  uint16_t s, z;            // W4: that unit's group scale and zero
+};
+
+// Thread t of the workgroup stages row t/2 of both tiles, unit (2 step + t%2) of the row.
+template <int FMT>
+__device__ __forceinline__ void pf_load(PfStage<FMT>& st, const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                        const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int m0,
+                                        int n0, int M, int N, int K, int step, int r, int h) {
+  const int U = K >> 5;
+  const int u = min(2 * step + h, U - 1);   // past the row end: a valid unit, zeroed when parked
+  const int mr = min(m0 + r, M - 1), nr = min(n0 + r, N - 1);
+  const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) + (size_t)mr * K * 2 + 64u * u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.x[i] = xp[i];
+  load_unit<FMT>(w, nr, u, U, st.w);
+  if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+    st.s = scales[(size_t)nr * U + u];
+    st.z = zeros[(size_t)nr * U + u];
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void pf_park(const PfStage<FMT>& st, uint8_t* xs, uint8_t* ws, bool unit_ok, int r, int h) {
+  h2 wv[16];
+  if constexpr (bf16_act(FMT)) {
+    decode_bf16<FMT>(st.w, st.s, st.z, wv);
+  } else {
+    h2 zc1 = {}, zc2 = {};
+    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) w4_consts(st.z, zc1, zc2);
+    decode<FMT>(st.w, zc1, zc2, wv);
+    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+      const _Float16 sv = __builtin_bit_cast(_Float16, st.s);
+      const h2 s2 = {sv, sv};
+#pragma unroll
+      for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
+    }
+  }
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  uint8_t* xrow = xs + r * PF_ROW + 64 * h;
+  uint8_t* wrow = ws + r * PF_ROW + 64 * h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    *reinterpret_cast<uint4*>(xrow + 16 * i) = unit_ok ? st.x[i] : zero;
+    *reinterpret_cast<uint4*>(wrow + 16 * i) =
+        unit_ok ? make_uint4(as_u32(wv[4 * i]), as_u32(wv[4 * i + 1]), as_u32(wv[4 * i + 2]), as_u32(wv[4 * i + 3])) : zero;
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void pf_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                                 const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
+                                                 uint16_t* __restrict__ y, int M, int N, int K) {
+  extern __shared__ uint4 pf_lds[];
+  uint8_t* lds = reinterpret_cast<uint8_t*>(pf_lds);
+  // Tiles in chunks of 8 weight-row tiles: every x-row tile of one weight tile gets the same
+  // block id modulo 8, i.e. the same XCD, so the weight tile's bytes are shared through its L2.
+  const int tiles_m = (M + PF_BM - 1) / PF_BM, tiles_n = (N + PF_BN - 1) / PF_BN;
+  const int b = blockIdx.x, chunk = b / (8 * tiles_m), rem = b - chunk * 8 * tiles_m;
+  const int nx = min(8, tiles_n - 8 * chunk);
+  const int mt = rem / nx, nt = 8 * chunk + rem % nx;
+  const int m0 = mt * PF_BM, n0 = nt * PF_BN;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave >> 1, wn = wave & 1;
+  const int r = t >> 1, h = t & 1;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int U = K >> 5, steps = (U + 1) >> 1;
+  f4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  PfStage<FMT> st;
+  pf_load<FMT>(st, x, w, scales, zeros, m0, n0, M, N, K, 0, r, h);
+  pf_park<FMT>(st, lds, lds + PF_TILE, h < U, r, h);
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < steps) pf_load<FMT>(st, x, w, scales, zeros, m0, n0, M, N, K, s + 1, r, h);
+    __builtin_amdgcn_sched_barrier(0);   // keep the next step's loads ahead of the products
+    const uint8_t* xs = lds + buf * 2 * PF_TILE;
+    const uint8_t* ws = xs + PF_TILE;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {   // the two units of the step; lane quad q takes K 8q .. 8q+7 of each
+      h8 a[4], bf[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        a[mi] = *reinterpret_cast<const h8*>(xs + (64 * wm + 16 * mi + i16) * PF_ROW + 64 * kh + 16 * q);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        bf[ni] = *reinterpret_cast<const h8*>(ws + (64 * wn + 16 * ni + i16) * PF_ROW + 64 * kh + 16 * q);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma16<FMT>(a[mi], bf[ni], acc[mi][ni]);
+    }
+    if (s + 1 < steps) {
+      uint8_t* nxs = lds + (buf ^ 1) * 2 * PF_TILE;
+      pf_park<FMT>(st, nxs, nxs + PF_TILE, 2 * (s + 1) + h < U, r, h);
+    }
+    __syncthreads();
+  }
+  // D[m][n] of a 16 x 16 tile sits in lane (n + 16 (m / 4)), register m % 4
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int n = n0 + 64 * wn + 16 * ni + i16;
+    if (n >= N) continue;
+    const float sc = row_scaled<FMT>() ? f16_to_f32(scales[n]) : 1.0f;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int m = m0 + 64 * wm + 16 * mi + 4 * q + k;
+        if (m < M) y[(size_t)m * N + n] = out16<FMT>(acc[mi][ni][k] * sc);
+      }
+  }
+}
+
 // ---------------------------------------------------------------- dequant
 // One thread per unit: decode exactly, multiply by the scale in fp32 (exact), round once.
 template <int FMT>
@@ -1290,9 +1432,25 @@ int lm_tiles(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 // Rows of x per launch: 64 where the LDS-staged kernel serves the shape (W6, FP4; W4 with K
 // a multiple of 256), else 16. The kernels address x with 32-bit lane offsets (row * 2K + 64 u),
 // which hold 64 rows only while K <= 2^25; longer rows take 16-row slabs.
+// The tiled prefill kernel from PF_MIN_M rows of x on, while its grid (128 x 128 tiles) fits
+// one launch and M fits an int.
+bool use_pf(int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  const int64_t tiles = ((M + PF_BM - 1) / PF_BM) * ((N + PF_BN - 1) / PF_BN);
+  return M >= PF_MIN_M && M <= INT32_MAX && tiles <= INT32_MAX;
+}
+
 int64_t slab_rows(int fmt, int64_t K) {
   const bool lm = fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W4E2M1 || (fmt == WQ_FMT_W4G32 && K % 256 == 0);
   return lm && K <= (int64_t(1) << 25) ? 16 * LM_MAX_MT : MFMA_M;
+}
+
+template <int FMT>
+hipError_t launch_pf(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
+                     uint16_t* y, int M, int N, int K) {
+  const int64_t tiles = (int64_t)((M + PF_BM - 1) / PF_BM) * ((N + PF_BN - 1) / PF_BN);
+  hipLaunchKernelGGL((pf_kernel<FMT>), dim3((unsigned)tiles), dim3(256), PF_LDS, s, x, w, sc, z, y, M, N, K);
+  return hipGetLastError();
 }
 
 template <int FMT, int M>
@@ -1478,6 +1636,16 @@ int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, c
   if (st != WQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* w = static_cast<const uint8_t*>(packed_w);
+  if (use_pf(M, N, K)) {   // prefill-sized M: one tiled launch for all rows
+    hipError_t e = hipSuccess;
+    switch (fmt) {
+#define WQ_CASE(C) case C: e = launch_pf<C>(s, x, w, scales, zeros, y, (int)M, (int)N, (int)K); break;
+      WQ_KERNEL_CODES(WQ_CASE)
+#undef WQ_CASE
+      default: return WQ_ERR_FMT;
+    }
+    return e == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
+  }
   const int64_t slab = slab_rows(wfmt(fmt), K);
   for (int64_t m0 = 0; m0 < M; m0 += slab) {
     const int mm = static_cast<int>(M - m0 < slab ? M - m0 : slab);
@@ -1594,6 +1762,10 @@ const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   static thread_local char buf[96];
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 32 || K % 32) return "";
   const int pf = wfmt(fmt);
+  if (use_pf(M, N, K)) {
+    snprintf(buf, sizeof(buf), "pf_kernel<%d>", fmt);
+    return buf;
+  }
   const int64_t mm = M < slab_rows(pf, K) ? M : slab_rows(pf, K);   // the first launch's rows
   if (use_lm(pf, mm, N, K)) {
     snprintf(buf, sizeof(buf), "lm_kernel<%d, %d, %d>", fmt, plan_lm(pf, N, K).RB, lm_tiles(mm));
