@@ -265,9 +265,9 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_kernel_name(2, 64, 4096, 4128) == "mfma_kernel<2, 1>"
     assert wq.wq_linear_kernel_name(1, 40, 4096, 4096) == "mfma_kernel<1, 1>"
     assert wq.wq_linear_kernel_name(3, 100, 4096, 4096) == "lm_kernel<3, 1, 4>"
-    # from 512 rows of x on: the tiled prefill kernel, one launch for all rows
-    assert wq.wq_linear_kernel_name(3, 511, 4096, 4096) == "lm_kernel<3, 1, 4>"
-    assert wq.wq_linear_kernel_name(3, 512, 4096, 4096) == "pf_kernel<3>"
+    # from 193 rows of x on: the tiled prefill kernel, one launch for all rows
+    assert wq.wq_linear_kernel_name(3, 192, 4096, 4096) == "lm_kernel<3, 1, 4>"
+    assert wq.wq_linear_kernel_name(3, 193, 4096, 4096) == "pf_kernel<3>"
     assert wq.wq_linear_kernel_name(2, 600, 4096, 4128) == "pf_kernel<2>"
     assert wq.wq_linear_kernel_name(2 | wq.ACT_BF16, 512, 11008, 4096) == "pf_kernel<258>"
     assert wq.wq_linear_kernel_name(0, 4096, 4096, 4096) == "pf_kernel<0>"

@@ -1115,13 +1115,12 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lm_grouped_kernel(const GemvGro
 // decode of the other kernels; W4 as fp16((q - z) s), the other formats as exact code values
 // with their row scale applied to the result), and its four waves (2 x 2, 64 x 64 each) run 32
 // MFMAs from there, so each decoded weight serves 128 rows of x and each x value 128 weight
-// rows. Double-buffered LDS with one barrier per step: the global loads of step s+1 are in
-// flight while step s is multiplied, and are decoded and parked after it. LDS rows are padded
-// to 144 B, so the 16 rows of a fragment read start 36 banks apart. Each step reads two units
-// (32 B for W4) of each of 128 weight rows, a pattern HBM serves well below its contiguous rate,
-// which holds this kernel to 100-230 TFLOP/s; wq_linear takes it from 512 rows of x on, where
-// it beats launches of 64 rows that reread the weights.
-constexpr int PF_MIN_M = 512;   // M from which wq_linear takes this kernel (below, 64-row launches win)
+// rows. Double-buffered LDS with one barrier per step; the global loads of the next two steps
+// are in flight while a step is multiplied. A step is short (32 MFMAs per wave), so the time of
+// a tile is the chain of its K steps, about 1 us each: wq_linear takes this kernel from 193
+// rows of x on, where it beats launches of 64 rows that reread the weights. LDS rows are padded
+// to 144 B, so the 16 rows of a fragment read start 36 banks apart.
+constexpr int PF_MIN_M = 193;   // M from which wq_linear takes this kernel (below, 64-row launches win)
 constexpr int PF_BM = 128, PF_BN = 128;       // tile of y
 constexpr int PF_ROW = 2 * 64 + 16;           // bytes per LDS row: 64 K of 16-bit values and padding
 constexpr int PF_TILE = 128 * PF_ROW;         // one operand tile (18 KB)
@@ -1129,31 +1128,44 @@ constexpr int PF_LDS = 4 * PF_TILE;           // x and weights, two buffers each
 
 template <int FMT>
 struct PfStage {
-  uint4 x[4];               // 64 B: one unit's 32 values of one x row
+  uint4 x[4];               // 16 B of each of 4 x rows
   Raw<wfmt(FMT)> w;         // one unit of one weight row
   uint16_t s, z;            // W4: that unit's group scale and zero
 };
 
-// Thread t of the workgroup stages row t/2 of both tiles, unit (2 step + t%2) of the row.
+// x: load i of wave v covers x rows 32 v + 8 i .. +7 of the tile, 8 lanes per row, so every
+// load reads whole 128-B lines (the step's 64 values of 8 rows). Weights: thread t stages row
+// t/2 of the weight tile, unit (2 step + t%2) of the row.
+__device__ __forceinline__ int pf_xrow(int t, int i) { return 32 * (t >> 6) + 8 * i + ((t & 63) >> 3); }
+__device__ __forceinline__ int pf_xunit(int t, int step) { return 2 * step + ((t & 7) >> 2); }
+
 template <int FMT>
 __device__ __forceinline__ void pf_load(PfStage<FMT>& st, const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                         const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int m0,
                                         int n0, int M, int N, int K, int step, int r, int h) {
-  const int U = K >> 5;
+  const int U = K >> 5, t = threadIdx.x;
   const int u = min(2 * step + h, U - 1);   // past the row end: a valid unit, zeroed when parked
-  const int mr = min(m0 + r, M - 1), nr = min(n0 + r, N - 1);
-  const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) + (size_t)mr * K * 2 + 64u * u);
+  const int nr = min(n0 + r, N - 1);
+  const uint32_t xo = 64u * (uint32_t)min(pf_xunit(t, step), U - 1) + 16u * (t & 3);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) st.x[i] = xp[i];
+  for (int i = 0; i < 4; ++i) {
+    const int mr = min(m0 + pf_xrow(t, i), M - 1);
+    st.x[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) + (size_t)mr * K * 2 + xo);
+  }
   load_unit<FMT>(w, nr, u, U, st.w);
-  if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
-    st.s = scales[(size_t)nr * U + u];
-    st.z = zeros[(size_t)nr * U + u];
+  if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {   // the aligned 32-bit word holding each (no 16-bit loads,
+    const size_t gi = (size_t)nr * U + u;       // whose partial register writes make the compiler wait for
+    const int sh = 16 * (int)(gi & 1);          // every load in flight)
+    st.s = (uint16_t)(reinterpret_cast<const uint32_t*>(scales)[gi >> 1] >> sh);
+    st.z = (uint16_t)(reinterpret_cast<const uint32_t*>(zeros)[gi >> 1] >> sh);
   }
 }
 
 template <int FMT>
-__device__ __forceinline__ void pf_park(const PfStage<FMT>& st, uint8_t* xs, uint8_t* ws, bool unit_ok, int r, int h) {
+__device__ __forceinline__ void pf_park(const PfStage<FMT>& st, uint8_t* xs, uint8_t* ws, int step, int U, int r, int h) {
+  const bool unit_ok = 2 * step + h < U;   // this thread's weight unit
+  const int t = threadIdx.x;
+  const bool xunit_ok = pf_xunit(t, step) < U;
   h2 wv[16];
   if constexpr (bf16_act(FMT)) {
     decode_bf16<FMT>(st.w, st.s, st.z, wv);
@@ -1168,14 +1180,17 @@ __device__ __forceinline__ void pf_park(const PfStage<FMT>& st, uint8_t* xs, uin
       for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
     }
   }
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  uint8_t* xrow = xs + r * PF_ROW + 64 * h;
+  // zeroing by masks, not selects: the stores stay unconditional and branch-free, so the wait
+  // before them covers only this stage's loads
+  const uint32_t xm = xunit_ok ? ~0u : 0u, wm = unit_ok ? ~0u : 0u;
   uint8_t* wrow = ws + r * PF_ROW + 64 * h;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<uint4*>(xrow + 16 * i) = unit_ok ? st.x[i] : zero;
-    *reinterpret_cast<uint4*>(wrow + 16 * i) =
-        unit_ok ? make_uint4(as_u32(wv[4 * i]), as_u32(wv[4 * i + 1]), as_u32(wv[4 * i + 2]), as_u32(wv[4 * i + 3])) : zero;
+    const uint4 xv = st.x[i];
+    *reinterpret_cast<uint4*>(xs + pf_xrow(t, i) * PF_ROW + 16 * (t & 7)) =
+        make_uint4(xv.x & xm, xv.y & xm, xv.z & xm, xv.w & xm);
+    *reinterpret_cast<uint4*>(wrow + 16 * i) = make_uint4(as_u32(wv[4 * i]) & wm, as_u32(wv[4 * i + 1]) & wm,
+                                                          as_u32(wv[4 * i + 2]) & wm, as_u32(wv[4 * i + 3]) & wm);
   }
 }
 
@@ -1203,15 +1218,17 @@ __global__ __launch_bounds__(256) void pf_kernel(const uint16_t* __restrict__ x,
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[a][c] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  PfStage<FMT> st;
-  pf_load<FMT>(st, x, w, scales, zeros, m0, n0, M, N, K, 0, r, h);
-  pf_park<FMT>(st, lds, lds + PF_TILE, h < U, r, h);
+  // Two register stages, no branches around loads or parks (past the last step they reread
+  // the last unit and park into the idle buffer), so the wait before each park covers only the
+  // older stage: while step s is multiplied, steps s+1 and s+2 are in flight.
+  PfStage<FMT> R0, R1;
+  pf_load<FMT>(R0, x, w, scales, zeros, m0, n0, M, N, K, 0, r, h);
+  pf_load<FMT>(R1, x, w, scales, zeros, m0, n0, M, N, K, 1, r, h);
+  pf_park<FMT>(R0, lds, lds + PF_TILE, 0, U, r, h);
+  pf_load<FMT>(R0, x, w, scales, zeros, m0, n0, M, N, K, 2, r, h);
   __syncthreads();
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < steps) pf_load<FMT>(st, x, w, scales, zeros, m0, n0, M, N, K, s + 1, r, h);
-    __builtin_amdgcn_sched_barrier(0);   // keep the next step's loads ahead of the products
-    const uint8_t* xs = lds + buf * 2 * PF_TILE;
+  auto mul = [&](int s) {
+    const uint8_t* xs = lds + (s & 1) * 2 * PF_TILE;
     const uint8_t* ws = xs + PF_TILE;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {   // the two units of the step; lane quad q takes K 8q .. 8q+7 of each
@@ -1227,10 +1244,16 @@ __global__ __launch_bounds__(256) void pf_kernel(const uint16_t* __restrict__ x,
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma16<FMT>(a[mi], bf[ni], acc[mi][ni]);
     }
-    if (s + 1 < steps) {
-      uint8_t* nxs = lds + (buf ^ 1) * 2 * PF_TILE;
-      pf_park<FMT>(st, nxs, nxs + PF_TILE, 2 * (s + 1) + h < U, r, h);
-    }
+  };
+  for (int s = 0; s < steps; s += 2) {   // R1 holds step s+1, R0 step s+2
+    mul(s);
+    pf_park<FMT>(R1, lds + ((s + 1) & 1) * 2 * PF_TILE, lds + ((s + 1) & 1) * 2 * PF_TILE + PF_TILE, s + 1, U, r, h);
+    pf_load<FMT>(R1, x, w, scales, zeros, m0, n0, M, N, K, s + 3, r, h);
+    __syncthreads();
+    if (s + 1 >= steps) break;
+    mul(s + 1);
+    pf_park<FMT>(R0, lds + (s & 1) * 2 * PF_TILE, lds + (s & 1) * 2 * PF_TILE + PF_TILE, s + 2, U, r, h);
+    pf_load<FMT>(R0, x, w, scales, zeros, m0, n0, M, N, K, s + 4, r, h);
     __syncthreads();
   }
   // D[m][n] of a 16 x 16 tile sits in lane (n + 16 (m / 4)), register m % 4
