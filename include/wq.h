@@ -133,9 +133,10 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
 /* On the device: y[M,N] = x[M,K] . dequant(packed_w)[N,K]^T with fp16 x and y (bfloat16 with
  * WQ_ACT_BF16 in fmt; row-major, row strides K and N) and fp32 accumulation; the one fused kernel reads every packed
  * byte once and never writes dequantized weights to memory. All pointers are device
- * pointers, 16-byte aligned; zeros only for W4 (else may be NULL). M of any size; one launch
- * takes up to 64 rows of x for W6 and for W4 with K a multiple of 256, up to 16 otherwise,
- * and larger M runs as several launches. y must not overlap the inputs.
+ * pointers, 16-byte aligned; zeros only for W4 (else may be NULL). M of any size: one launch
+ * takes up to 64 rows of x for W6, FP4 and W4 with K a multiple of 256, up to 16 otherwise,
+ * and M up to 192 runs as several such launches; from 193 rows on, one tiled launch takes
+ * all rows (prefill). y must not overlap the inputs.
  * Asynchronous on stream. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT, WQ_ERR_ALIGN,
  * WQ_ERR_DEVICE. */
 int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros, uint16_t* y,
