@@ -2,15 +2,17 @@
 
 The kernel stages 128 x 128 tiles of x and of the decoded weights in LDS; these cases cover
 ragged tiles in M and N, K with an odd number of 32-code units (a half-empty last K step),
-every weight format with fp16 and with bfloat16 activations, one-hot x (bit-exact), and the
-Llama-7B shapes at M = 512 on sampled output rows.
+every weight format with fp16 and with bfloat16 activations, one-hot x (bit-exact), grouped
+launches (bit-identical to separate calls), and the Llama-7B shapes at M = 512 on sampled
+output rows.
 """
 
 import numpy as np
 import pytest
 
 from weight_only_quantized_dequant_amd import inputs, wq
-from tests.gpu_util import DeviceWeights, bf16_bits_torch, check_linear, oracle_rows, torch_cuda, x_as_bf16
+from tests.gpu_util import (DeviceWeights, bf16_bits_torch, check_linear, dev, host_bits, oracle_rows, torch_cuda,
+                            x_as_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +86,29 @@ def test_prefill_repeatable_and_rows_independent(fmt, act):
     assert np.array_equal(y700, dw.linear(x))
     y512 = dw.linear(x[100:612])
     assert np.array_equal(y700[100:612], y512)
+
+
+@pytest.mark.parametrize("fmt,act", CODES, ids=IDS)
+@pytest.mark.parametrize("m", [193, 520])
+def test_prefill_grouped_matches_separate_calls(fmt, act, m):
+    # one launch over the tiles of every item (mixed K, ragged N, an odd number of K units):
+    # each item's y bit-identical to its own call, and within tolerance of the oracle
+    torch = torch_cuda()
+    shapes = [(130, 2080), (300, 4096), (64, 6144), (17, 96), (257, 4256)]
+    ws = [_weights(n, k, 60 + i) for i, (n, k) in enumerate(shapes)]
+    dws = [DeviceWeights(fmt, w, act) for w in ws]
+    xs = [_x(70 + i, k, m, act) for i, (_, k) in enumerate(shapes)]
+    sep = [dw.linear(x) for dw, x in zip(dws, xs)]
+    xd = [dev(x) for x in xs]
+    ys = [torch.empty((m, dw.n), dtype=torch.int16, device="cuda:0") for dw in dws]
+    items = [(xd[i], dw.packed, dw.scales, dw.zeros, ys[i], dw.n, dw.k) for i, dw in enumerate(dws)]
+    assert wq.wq_linear_grouped_kernel_name(fmt | act, m, shapes) == "pf_grouped_kernel<%d>" % (fmt | act)
+    wq.wq_linear_grouped(items, m, fmt | act)
+    torch.cuda.synchronize()
+    for i, (w, x) in enumerate(zip(ws, xs)):
+        got = host_bits(ys[i])
+        assert np.array_equal(got, sep[i]), "item %d differs from its separate call" % i
+        check_linear(got, x, _ref(fmt, act, w), "grouped item %d m %d" % (i, m), act=act)
 
 
 @pytest.mark.parametrize("fmt,act", [(wq.FMT_W4G32, 0), (wq.FMT_W6E3M2, 0), (wq.FMT_W4G32, BF)],

@@ -278,7 +278,11 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_grouped_kernel_name(3, 16, [(64, 4096), (64, (1 << 25) + 256)]) == "lm_grouped_kernel<3, 1, 1>"
     assert wq.wq_linear_grouped_kernel_name(3, 20, [(1024, 8192), (8192, 8192)]) == "lm_grouped_kernel<3, 2, 2>"
     assert wq.wq_linear_grouped_kernel_name(3, 65, [(1024, 8192), (8192, 8192)]) == "lm_kernel<3, 2, 4>"
-    assert wq.wq_linear_grouped_kernel_name(3, 512, [(1024, 8192), (8192, 8192)]) == "pf_kernel<3>"
+    # prefill-sized M: the tiles of every item in one launch (one item: the plain tiled kernel)
+    assert wq.wq_linear_grouped_kernel_name(3, 512, [(1024, 8192), (8192, 8192)]) == "pf_grouped_kernel<3>"
+    assert wq.wq_linear_grouped_kernel_name(2 | wq.ACT_BF16, 193, [(4096, 4096)] * 3) == "pf_grouped_kernel<258>"
+    assert wq.wq_linear_grouped_kernel_name(3, 512, [(8192, 28672)]) == "pf_kernel<3>"
+    assert wq.wq_linear_grouped_kernel_name(3, 192, [(1024, 8192), (8192, 8192)]) == "lm_kernel<3, 2, 4>"
     assert wq.wq_linear_grouped_kernel_name(1, 20, [(1024, 8192), (8192, 8192)]) == "mfma_kernel<1, 2>"
     # the LDS-staged group takes two row blocks per wave when any item has 8192 rows or more,
     # whatever the order of equal-size items

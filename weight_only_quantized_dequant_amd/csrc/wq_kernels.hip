@@ -42,270 +42,15 @@
 #include <cstdint>
 #include <cstdio>
 
+#include "wq_device.h"
 #include "wq_internal.h"
 
 namespace {
-
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h32 __attribute__((ext_vector_type(32)));
-typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-typedef __bf16 b8 __attribute__((ext_vector_type(8)));
-typedef __bf16 b32 __attribute__((ext_vector_type(32)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x6 __attribute__((ext_vector_type(6)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int GEMV_MAX_M = 4;   // largest M served by the VALU GEMV; above it the MFMA kernel runs
 constexpr int MFMA_M = 16;      // rows of x per MFMA launch
 constexpr int GEMV_WAVES = 4;   // waves per workgroup of the GEMV (row blocks x split of K)
 constexpr int MFMA_MAX_WAVES = 8;   // waves per workgroup of the MFMA kernel
-
-__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
-__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
-
-// A kernel's format code: the weight format in the low byte, WQ_ACT_BF16 for bfloat16
-// activations. Registers hold 16-bit pairs as h2 whatever their type; only the dot products,
-// the matrix instructions and the output conversion look at the type. wfmt() is the weight
-// layout (BF16 weights are laid out and loaded as F16 ones).
-constexpr int wfmt(int c) { return (c & 0xFF) == WQ_FMT_BF16 ? WQ_FMT_F16 : (c & 0xFF); }
-constexpr bool bf16_act(int c) { return (c & WQ_ACT_BF16) != 0; }
-
-__device__ __forceinline__ float dot2_bf16(h2 a, h2 b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
-}
-// Pairs 4k .. 4k+3 of a decoded unit as one 8-element MFMA fragment (32-bit moves only).
-__device__ __forceinline__ h8 frag_of(const h2 (&wv)[16], int k) {
-  return __builtin_bit_cast(h8, make_uint4(as_u32(wv[4 * k]), as_u32(wv[4 * k + 1]), as_u32(wv[4 * k + 2]),
-                                           as_u32(wv[4 * k + 3])));
-}
-
-__device__ __forceinline__ h2 pack_bf16(float lo, float hi) {   // two values rounded to nearest even
-  const b2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(h2, v);
-}
-
-template <int FMT>
-__device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {   // 16x16x32 product of the activation type
-  if constexpr (bf16_act(FMT))
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-template <int FMT>
-__device__ __forceinline__ uint16_t out16(float v) {   // y: rounded once to the activation type
-  if constexpr (bf16_act(FMT)) return __builtin_bit_cast(uint16_t, (__bf16)v);
-  else return __builtin_bit_cast(uint16_t, (_Float16)v);
-}
-
-// ---------------------------------------------------------------- raw units and loads
-// A 32-code unit in registers. W6 keeps its two plane slices (16 + 8 bytes), which read in
-// order are the unit's 192-bit little-endian stream.
-template <int FMT> struct Raw;
-template <> struct Raw<WQ_FMT_W8> { uint4 a, b; };
-template <> struct Raw<WQ_FMT_W4G32> { uint4 a; };
-template <> struct Raw<WQ_FMT_W6E3M2> { uint4 a; uint2 b; };
-template <> struct Raw<WQ_FMT_W4E2M1> { uint4 a; };
-template <> struct Raw<WQ_FMT_F16> { uint4 a, b, c, d; };
-
-template <int FMT> constexpr int unit_bytes() {
-  return wfmt(FMT) == WQ_FMT_W8 ? 32 : wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W4E2M1 ? 16 : wfmt(FMT) == WQ_FMT_W6E3M2 ? 24 : 64;
-}
-
-// Formats with one fp16 scale per output row, applied to the finished fp32 sum.
-template <int FMT> constexpr bool row_scaled() {
-  return wfmt(FMT) == WQ_FMT_W8 || wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1;
-}
-
-// Byte offsets, from the start of row n, of the two plane slices of W6 unit u (U units per row).
-__device__ __forceinline__ void w6_homes(int u, int U, uint32_t& lo, uint32_t& hi) {
-  const int c = u >> 6, j = u & 63, uc = min(64, U - 64 * c);
-  lo = (uint32_t)(64 * c * 24 + 16 * j);
-  hi = (uint32_t)(64 * c * 24 + 16 * uc + 8 * j);
-}
-
-// Unit u of row n (used by the MFMA and dequant kernels, where a lane owns a whole unit).
-template <int FMT>
-__device__ __forceinline__ void load_unit(const uint8_t* __restrict__ w, int n, int u, int U, Raw<wfmt(FMT)>& r) {
-  constexpr int UB = unit_bytes<FMT>();
-  const uint8_t* row = w + (size_t)n * U * UB;
-  if constexpr (wfmt(FMT) == WQ_FMT_W8) {
-    const uint4* q = reinterpret_cast<const uint4*>(row + (size_t)u * UB);
-    r.a = q[0]; r.b = q[1];
-  } else if constexpr (wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W4E2M1) {
-    r.a = *reinterpret_cast<const uint4*>(row + (size_t)u * UB);
-  } else if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2) {
-    uint32_t lo, hi;
-    w6_homes(u, U, lo, hi);
-    r.a = *reinterpret_cast<const uint4*>(row + lo);
-    r.b = *reinterpret_cast<const uint2*>(row + hi);
-  } else {
-    const uint4* q = reinterpret_cast<const uint4*>(row + (size_t)u * UB);
-    r.a = q[0]; r.b = q[1]; r.c = q[2]; r.d = q[3];
-  }
-}
-
-// ---------------------------------------------------------------- exact decode to fp16 pairs
-// out[p] holds the values of codes 2p and 2p+1 of the unit:
-//   W8: q      W4: q - z      W6: e3m2(code)      FP4: e2m1(code)      F16: the weights
-// zc1 = -(1024 + z), zc2 = -(64 + z) as fp16 pairs (W4 only; exact small integers).
-__device__ __forceinline__ void decode_w8_word(uint32_t d, h2& lo, h2& hi) {
-  const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  lo = as_h2(__builtin_amdgcn_perm(0x64646464u, d, 0x04010400u)) + bias;
-  hi = as_h2(__builtin_amdgcn_perm(0x64646464u, d, 0x04030402u)) + bias;
-}
-
-__device__ __forceinline__ void decode_w4_word(uint32_t d, h2 zc1, h2 zc2, h2& o0, h2& o1, h2& o2, h2& o3) {
-  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const uint32_t d8 = d >> 8;
-  o0 = as_h2((d & 0x000F000Fu) | 0x64006400u) + zc1;                       // codes 0,1: 1024+q
-  o1 = __builtin_elementwise_fma(as_h2((d & 0x00F000F0u) | 0x64006400u), sixteenth, zc2);   // 1024+16q
-  o2 = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + zc1;
-  o3 = __builtin_elementwise_fma(as_h2((d8 & 0x00F000F0u) | 0x64006400u), sixteenth, zc2);
-}
-
-// Byte b of d holds codes 2b (low nibble) and 2b+1 (high nibble); the convert takes the
-// byte index as an immediate and returns them in that order.
-__device__ __forceinline__ void decode_fp4_word(uint32_t d, h2& o0, h2& o1, h2& o2, h2& o3) {
-  o0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0);
-  o1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1);
-  o2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2);
-  o3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3);
-}
-
-template <int FMT>
-__device__ __forceinline__ void decode(const Raw<wfmt(FMT)>& r, h2 zc1, h2 zc2, h2 (&out)[16]) {
-  if constexpr (wfmt(FMT) == WQ_FMT_W8) {
-    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) decode_w8_word(w[i], out[2 * i], out[2 * i + 1]);
-  } else if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
-    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) decode_w4_word(w[i], zc1, zc2, out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-  } else if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2) {
-    u32x6 v;
-    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w; v[4] = r.b.x; v[5] = r.b.y;
-    const h32 h = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(v, 1.0f);
-#pragma unroll
-    for (int p = 0; p < 16; ++p) { out[p][0] = h[2 * p]; out[p][1] = h[2 * p + 1]; }
-  } else if constexpr (wfmt(FMT) == WQ_FMT_W4E2M1) {
-    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) decode_fp4_word(w[i], out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-  } else {
-    const uint32_t w[16] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w,
-                            r.c.x, r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w};
-#pragma unroll
-    for (int p = 0; p < 16; ++p) out[p] = as_h2(w[p]);
-  }
-}
-
-__device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
-
-// The weights of a unit as bfloat16 pairs for bfloat16 activations (same pair order as
-// decode): W8 q, W6 e3m2(code), FP4 e2m1(code), BF16 the weights, all exact, with the row
-// scale applied after the sum; W4 (q - z) s rounded once to bfloat16, since its scale changes
-// along K. For W4, the nibble placed at bit 16 of 128.0f gives (128 + q) in fp32, and one fma
-// with s and c = -(128 + z) s gives (q - z) s exactly (every product is exact in fp32).
-template <int FMT>
-__device__ __forceinline__ void decode_bf16(const Raw<wfmt(FMT)>& r, uint16_t sbits, uint16_t zbits, h2 (&out)[16]) {
-  constexpr int F = wfmt(FMT);
-  if constexpr (F == WQ_FMT_W8) {
-    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      out[2 * i] = pack_bf16((float)(w[i] & 0xFFu) - 128.0f, (float)((w[i] >> 8) & 0xFFu) - 128.0f);
-      out[2 * i + 1] = pack_bf16((float)((w[i] >> 16) & 0xFFu) - 128.0f, (float)(w[i] >> 24) - 128.0f);
-    }
-  } else if constexpr (F == WQ_FMT_W4G32) {
-    const float s = f16_to_f32(sbits);
-    const float c = -(128.0f + f16_to_f32(zbits)) * s;
-    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {   // codes 8i+2t (nibble t) and 8i+2t+1 (nibble t+4)
-        const float lo = __builtin_bit_cast(float, ((w[i] << (16 - 4 * t)) & 0x000F0000u) | 0x43000000u);
-        const float hi = __builtin_bit_cast(float, ((w[i] >> (4 * t)) & 0x000F0000u) | 0x43000000u);
-        out[4 * i + t] = pack_bf16(__builtin_fmaf(lo, s, c), __builtin_fmaf(hi, s, c));
-      }
-    }
-  } else if constexpr (F == WQ_FMT_W6E3M2) {
-    u32x6 v;
-    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w; v[4] = r.b.x; v[5] = r.b.y;
-    const u32x16 h = __builtin_bit_cast(u32x16, __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(v, 1.0f));
-#pragma unroll
-    for (int p = 0; p < 16; ++p) out[p] = as_h2(h[p]);
-  } else if constexpr (F == WQ_FMT_W4E2M1) {
-    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[4 * i] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 0));
-      out[4 * i + 1] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 1));
-      out[4 * i + 2] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 2));
-      out[4 * i + 3] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 3));
-    }
-  } else {
-    const uint32_t w[16] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w,
-                            r.c.x, r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w};
-#pragma unroll
-    for (int p = 0; p < 16; ++p) out[p] = as_h2(w[p]);
-  }
-}
-
-// zero-point constants of one W4 group
-__device__ __forceinline__ void w4_consts(uint16_t zbits, h2& zc1, h2& zc2) {
-  const _Float16 z = __builtin_bit_cast(_Float16, zbits);
-  const _Float16 c1 = (_Float16)-1024.0f - z, c2 = (_Float16)-64.0f - z;   // exact integers
-  zc1 = h2{c1, c1};
-  zc2 = h2{c2, c2};
-}
-
-// ---------------------------------------------------------------- wave reduction
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
-}
-
-// Sum over the 64 lanes with DPP only (no LDS): the total lands in lane 63.
-__device__ __forceinline__ float wave_sum_to_lane63(float v) {
-  v += dpp<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]: lane ^ 1
-  v += dpp<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]: lane ^ 2
-  v += dpp<0x141, 0xF>(v);   // row_half_mirror: adds the other quad of each 8 lanes
-  v += dpp<0x140, 0xF>(v);   // row_mirror: adds the other half of each 16-lane row
-  v += dpp<0x142, 0xA>(v);   // row_bcast15: rows 1 and 3 add the last lane of rows 0 and 2
-  v += dpp<0x143, 0xC>(v);   // row_bcast31: rows 2 and 3 add lane 31
-  return v;
-}
-
-// A constant kept in a VGPR. gfx950 VALU ops take at most one SGPR or literal and VOP3
-// ops take no literal, so masks used by v_and_or_b32 / v_perm_b32 must sit in VGPRs.
-__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
-  asm volatile("" : "+v"(c));
-  return c;
-}
-
-// A wave-uniform byte offset held in SGPRs. Adding it to a kernel-argument pointer keeps
-// the global address space and lets loads take the SGPR-base + 32-bit VGPR offset form
-// instead of a per-lane 64-bit address computed on the VALU.
-__device__ __forceinline__ size_t uniform(size_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return (static_cast<size_t>(hi) << 32) | lo;
-}
-
-__device__ __forceinline__ uint4 ld_nt16(const uint8_t* p) {
-  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(t[0], t[1], t[2], t[3]);
-}
-__device__ __forceinline__ uint2 ld_nt8(const uint8_t* p) {
-  const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-  return make_uint2(t[0], t[1]);
-}
 
 // ---------------------------------------------------------------- GEMV (M <= GEMV_MAX_M)
 // Lanes run along K. Lane l of a wave owns one "segment" of SEG consecutive K of a row
@@ -1107,171 +852,6 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lm_grouped_kernel(const GemvGro
                        blockIdx.x - g.first_block[j], g.WK[j]);
 }
 
-// ---------------------------------------------------------------- prefill: M > 64 on the matrix cores
-// Past 64 rows of x the weight stream stops being the only cost: the product itself, 2 M N K
-// flops, grows with M. Here a workgroup computes a 128 (x rows) x 128 (weight rows) tile of y.
-// Per K step of 64 (two 32-code units of each weight row) it parks the x tile and the weight
-// tile in LDS, the weights decoded once into 16-bit values of the activation type (the exact
-// decode of the other kernels; W4 as fp16((q - z) s), the other formats as exact code values
-// with their row scale applied to the result), and its four waves (2 x 2, 64 x 64 each) run 32
-// MFMAs from there, so each decoded weight serves 128 rows of x and each x value 128 weight
-// rows. Double-buffered LDS with one barrier per step; the global loads of the next two steps
-// are in flight while a step is multiplied. A step is short (32 MFMAs per wave), so the time of
-// a tile is the chain of its K steps, about 1 us each: wq_linear takes this kernel from 193
-// rows of x on, where it beats launches of 64 rows that reread the weights. LDS rows are padded
-// to 144 B, so the 16 rows of a fragment read start 36 banks apart.
-constexpr int PF_MIN_M = 193;   // M from which wq_linear takes this kernel (below, 64-row launches win)
-constexpr int PF_BM = 128, PF_BN = 128;       // tile of y
-constexpr int PF_ROW = 2 * 64 + 16;           // bytes per LDS row: 64 K of 16-bit values and padding
-constexpr int PF_TILE = 128 * PF_ROW;         // one operand tile (18 KB)
-constexpr int PF_LDS = 4 * PF_TILE;           // x and weights, two buffers each (72 KB)
-
-template <int FMT>
-struct PfStage {
-  uint4 x[4];               // 16 B of each of 4 x rows
-  Raw<wfmt(FMT)> w;         // one unit of one weight row
-  uint16_t s, z;            // W4: that unit's group scale and zero
-};
-
-// x: load i of wave v covers x rows 32 v + 8 i .. +7 of the tile, 8 lanes per row, so every
-// load reads whole 128-B lines (the step's 64 values of 8 rows). Weights: thread t stages row
-// t/2 of the weight tile, unit (2 step + t%2) of the row.
-__device__ __forceinline__ int pf_xrow(int t, int i) { return 32 * (t >> 6) + 8 * i + ((t & 63) >> 3); }
-__device__ __forceinline__ int pf_xunit(int t, int step) { return 2 * step + ((t & 7) >> 2); }
-
-template <int FMT>
-__device__ __forceinline__ void pf_load(PfStage<FMT>& st, const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
-                                        const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int m0,
-                                        int n0, int M, int N, int K, int step, int r, int h) {
-  const int U = K >> 5, t = threadIdx.x;
-  const int u = min(2 * step + h, U - 1);   // past the row end: a valid unit, zeroed when parked
-  const int nr = min(n0 + r, N - 1);
-  const uint32_t xo = 64u * (uint32_t)min(pf_xunit(t, step), U - 1) + 16u * (t & 3);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int mr = min(m0 + pf_xrow(t, i), M - 1);
-    st.x[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) + (size_t)mr * K * 2 + xo);
-  }
-  load_unit<FMT>(w, nr, u, U, st.w);
-  if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {   // the aligned 32-bit word holding each (no 16-bit loads,
-    const size_t gi = (size_t)nr * U + u;       // whose partial register writes make the compiler wait for
-    const int sh = 16 * (int)(gi & 1);          // every load in flight)
-    st.s = (uint16_t)(reinterpret_cast<const uint32_t*>(scales)[gi >> 1] >> sh);
-    st.z = (uint16_t)(reinterpret_cast<const uint32_t*>(zeros)[gi >> 1] >> sh);
-  }
-}
-
-template <int FMT>
-__device__ __forceinline__ void pf_park(const PfStage<FMT>& st, uint8_t* xs, uint8_t* ws, int step, int U, int r, int h) {
-  const bool unit_ok = 2 * step + h < U;   // this thread's weight unit
-  const int t = threadIdx.x;
-  const bool xunit_ok = pf_xunit(t, step) < U;
-  h2 wv[16];
-  if constexpr (bf16_act(FMT)) {
-    decode_bf16<FMT>(st.w, st.s, st.z, wv);
-  } else {
-    h2 zc1 = {}, zc2 = {};
-    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) w4_consts(st.z, zc1, zc2);
-    decode<FMT>(st.w, zc1, zc2, wv);
-    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
-      const _Float16 sv = __builtin_bit_cast(_Float16, st.s);
-      const h2 s2 = {sv, sv};
-#pragma unroll
-      for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
-    }
-  }
-  // zeroing by masks, not selects: the stores stay unconditional and branch-free, so the wait
-  // before them covers only this stage's loads
-  const uint32_t xm = xunit_ok ? ~0u : 0u, wm = unit_ok ? ~0u : 0u;
-  uint8_t* wrow = ws + r * PF_ROW + 64 * h;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 xv = st.x[i];
-    *reinterpret_cast<uint4*>(xs + pf_xrow(t, i) * PF_ROW + 16 * (t & 7)) =
-        make_uint4(xv.x & xm, xv.y & xm, xv.z & xm, xv.w & xm);
-    *reinterpret_cast<uint4*>(wrow + 16 * i) = make_uint4(as_u32(wv[4 * i]) & wm, as_u32(wv[4 * i + 1]) & wm,
-                                                          as_u32(wv[4 * i + 2]) & wm, as_u32(wv[4 * i + 3]) & wm);
-  }
-}
-
-template <int FMT>
-__global__ __launch_bounds__(256) void pf_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
-                                                 const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
-                                                 uint16_t* __restrict__ y, int M, int N, int K) {
-  extern __shared__ uint4 pf_lds[];
-  uint8_t* lds = reinterpret_cast<uint8_t*>(pf_lds);
-  // Tiles in chunks of 8 weight-row tiles: every x-row tile of one weight tile gets the same
-  // block id modulo 8, i.e. the same XCD, so the weight tile's bytes are shared through its L2.
-  const int tiles_m = (M + PF_BM - 1) / PF_BM, tiles_n = (N + PF_BN - 1) / PF_BN;
-  const int b = blockIdx.x, chunk = b / (8 * tiles_m), rem = b - chunk * 8 * tiles_m;
-  const int nx = min(8, tiles_n - 8 * chunk);
-  const int mt = rem / nx, nt = 8 * chunk + rem % nx;
-  const int m0 = mt * PF_BM, n0 = nt * PF_BN;
-  const int t = threadIdx.x, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), wm = wave >> 1, wn = wave & 1;
-  const int r = t >> 1, h = t & 1;
-  const int i16 = lane & 15, q = lane >> 4;
-  const int U = K >> 5, steps = (U + 1) >> 1;
-  f4 acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  // Two register stages, no branches around loads or parks (past the last step they reread
-  // the last unit and park into the idle buffer), so the wait before each park covers only the
-  // older stage: while step s is multiplied, steps s+1 and s+2 are in flight.
-  PfStage<FMT> R0, R1;
-  pf_load<FMT>(R0, x, w, scales, zeros, m0, n0, M, N, K, 0, r, h);
-  pf_load<FMT>(R1, x, w, scales, zeros, m0, n0, M, N, K, 1, r, h);
-  pf_park<FMT>(R0, lds, lds + PF_TILE, 0, U, r, h);
-  pf_load<FMT>(R0, x, w, scales, zeros, m0, n0, M, N, K, 2, r, h);
-  __syncthreads();
-  auto mul = [&](int s) {
-    const uint8_t* xs = lds + (s & 1) * 2 * PF_TILE;
-    const uint8_t* ws = xs + PF_TILE;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {   // the two units of the step; lane quad q takes K 8q .. 8q+7 of each
-      h8 a[4], bf[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        a[mi] = *reinterpret_cast<const h8*>(xs + (64 * wm + 16 * mi + i16) * PF_ROW + 64 * kh + 16 * q);
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        bf[ni] = *reinterpret_cast<const h8*>(ws + (64 * wn + 16 * ni + i16) * PF_ROW + 64 * kh + 16 * q);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma16<FMT>(a[mi], bf[ni], acc[mi][ni]);
-    }
-  };
-  for (int s = 0; s < steps; s += 2) {   // R1 holds step s+1, R0 step s+2
-    mul(s);
-    pf_park<FMT>(R1, lds + ((s + 1) & 1) * 2 * PF_TILE, lds + ((s + 1) & 1) * 2 * PF_TILE + PF_TILE, s + 1, U, r, h);
-    pf_load<FMT>(R1, x, w, scales, zeros, m0, n0, M, N, K, s + 3, r, h);
-    __syncthreads();
-    if (s + 1 >= steps) break;
-    mul(s + 1);
-    pf_park<FMT>(R0, lds + (s & 1) * 2 * PF_TILE, lds + (s & 1) * 2 * PF_TILE + PF_TILE, s + 2, U, r, h);
-    pf_load<FMT>(R0, x, w, scales, zeros, m0, n0, M, N, K, s + 4, r, h);
-    __syncthreads();
-  }
-  // D[m][n] of a 16 x 16 tile sits in lane (n + 16 (m / 4)), register m % 4
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int n = n0 + 64 * wn + 16 * ni + i16;
-    if (n >= N) continue;
-    const float sc = row_scaled<FMT>() ? f16_to_f32(scales[n]) : 1.0f;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int m = m0 + 64 * wm + 16 * mi + 4 * q + k;
-        if (m < M) y[(size_t)m * N + n] = out16<FMT>(acc[mi][ni][k] * sc);
-      }
-  }
-}
-
 // ---------------------------------------------------------------- dequant
 // One thread per unit: decode exactly, multiply by the scale in fp32 (exact), round once.
 template <int FMT>
@@ -1313,11 +893,6 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 
 // ---------------------------------------------------------------- host-side planning
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
-// Every kernel code: the weight formats with fp16 activations, and with bfloat16 ones.
-#define WQ_KERNEL_CODES(X)                                                                              \
-  X(WQ_FMT_F16) X(WQ_FMT_W8) X(WQ_FMT_W4G32) X(WQ_FMT_W6E3M2) X(WQ_FMT_W4E2M1)                          \
-  X(WQ_FMT_W8 | WQ_ACT_BF16) X(WQ_FMT_W4G32 | WQ_ACT_BF16) X(WQ_FMT_W6E3M2 | WQ_ACT_BF16)              \
-  X(WQ_FMT_W4E2M1 | WQ_ACT_BF16) X(WQ_FMT_BF16 | WQ_ACT_BF16)
 
 bool valid_fmt(int code) {
   switch (code) {
@@ -1455,25 +1030,9 @@ int lm_tiles(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 // Rows of x per launch: 64 where the LDS-staged kernel serves the shape (W6, FP4; W4 with K
 // a multiple of 256), else 16. The kernels address x with 32-bit lane offsets (row * 2K + 64 u),
 // which hold 64 rows only while K <= 2^25; longer rows take 16-row slabs.
-// The tiled prefill kernel from PF_MIN_M rows of x on, while its grid (128 x 128 tiles) fits
-// one launch and M fits an int.
-bool use_pf(int64_t M, int64_t N, int64_t K) {
-  (void)K;
-  const int64_t tiles = ((M + PF_BM - 1) / PF_BM) * ((N + PF_BN - 1) / PF_BN);
-  return M >= PF_MIN_M && M <= INT32_MAX && tiles <= INT32_MAX;
-}
-
 int64_t slab_rows(int fmt, int64_t K) {
   const bool lm = fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W4E2M1 || (fmt == WQ_FMT_W4G32 && K % 256 == 0);
   return lm && K <= (int64_t(1) << 25) ? 16 * LM_MAX_MT : MFMA_M;
-}
-
-template <int FMT>
-hipError_t launch_pf(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
-                     uint16_t* y, int M, int N, int K) {
-  const int64_t tiles = (int64_t)((M + PF_BM - 1) / PF_BM) * ((N + PF_BN - 1) / PF_BN);
-  hipLaunchKernelGGL((pf_kernel<FMT>), dim3((unsigned)tiles), dim3(256), PF_LDS, s, x, w, sc, z, y, M, N, K);
-  return hipGetLastError();
 }
 
 template <int FMT, int M>
@@ -1584,6 +1143,14 @@ Family family_of(int fmt, int64_t M, int64_t N, int64_t K) {
   return use_mfma(fmt, M, N) ? FAM_MFMA : FAM_GEMV;
 }
 
+// A grouped call at prefill-sized M runs as one tiled launch when the tiled kernel serves
+// every item.
+bool group_pf(int64_t M, const int64_t* N, const int64_t* K, int count) {
+  for (int i = 0; i < count; ++i)
+    if (!wq::pf_serves(M, N[i], K[i])) return false;
+  return true;
+}
+
 int largest_item(const int64_t* N, const int64_t* K, int count) {
   int big = 0;
   for (int i = 1; i < count; ++i)
@@ -1659,16 +1226,8 @@ int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, c
   if (st != WQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* w = static_cast<const uint8_t*>(packed_w);
-  if (use_pf(M, N, K)) {   // prefill-sized M: one tiled launch for all rows
-    hipError_t e = hipSuccess;
-    switch (fmt) {
-#define WQ_CASE(C) case C: e = launch_pf<C>(s, x, w, scales, zeros, y, (int)M, (int)N, (int)K); break;
-      WQ_KERNEL_CODES(WQ_CASE)
-#undef WQ_CASE
-      default: return WQ_ERR_FMT;
-    }
-    return e == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
-  }
+  if (wq::pf_serves(M, N, K))   // prefill-sized M: one tiled launch for all rows
+    return wq::pf_launch(fmt, x, w, scales, zeros, y, M, N, K, stream);
   const int64_t slab = slab_rows(wfmt(fmt), K);
   for (int64_t m0 = 0; m0 < M; m0 += slab) {
     const int mm = static_cast<int>(M - m0 < slab ? M - m0 : slab);
@@ -1724,6 +1283,8 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
   // one family and one rows-per-wave (B or RB) for the whole launch: the largest item's (the
   // small items alone would pick fewer rows per wave to get enough waves, which the launch
   // has anyway); each item keeps the K split its own plan gives for that B / RB
+  if (count > 1 && group_pf(M, Ns, Ks, count))   // prefill-sized M: the tiles of all items in one launch
+    return wq::pf_launch_grouped(fmt, items, count, M, stream);
   const int pf = wfmt(fmt);
   const Family fam = group_family(pf, M, Ns, Ks, count);
   if (M > group_launch_rows(fam, pf, Ks, count)) {   // several slabs: one wq_linear per item
@@ -1785,7 +1346,7 @@ const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   static thread_local char buf[96];
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 32 || K % 32) return "";
   const int pf = wfmt(fmt);
-  if (use_pf(M, N, K)) {
+  if (wq::pf_serves(M, N, K)) {
     snprintf(buf, sizeof(buf), "pf_kernel<%d>", fmt);
     return buf;
   }
@@ -1806,6 +1367,10 @@ const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, 
   if (!valid_fmt(fmt) || M < 1 || !N || !K || count < 1 || count > MAX_GROUP) return "";
   for (int i = 0; i < count; ++i)
     if (N[i] < 1 || K[i] < 32 || K[i] % 32) return "";
+  if (count > 1 && group_pf(M, N, K, count)) {
+    snprintf(buf, sizeof(buf), "pf_grouped_kernel<%d>", fmt);
+    return buf;
+  }
   const int big = largest_item(N, K, count);
   const int pf = wfmt(fmt);
   const Family fam = group_family(pf, M, N, K, count);
