@@ -83,14 +83,19 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SRC = os.path.join(ROOT, "weight_only_quantized_dequant_amd", "csrc", "wq_kernels.hip")
+CSRC = os.path.join(ROOT, "weight_only_quantized_dequant_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
 def kernel_source_hash():
+    """sha256[:16] over the device sources (csrc/*.hip and csrc/*.h, by name)."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):
