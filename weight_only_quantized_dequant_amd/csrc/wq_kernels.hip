@@ -609,9 +609,11 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_grouped_kernel(const
 //   W6: the lo slices as 2 rows x 512 B per instruction, the hi slices as 4 rows x 256 B.
 //   FP4: as W4 (16-byte units), with no metadata.
 // LDS image of one 16-row block (XOR swizzles put the 16 rows of a fragment read in
-// different banks):
-//   W4, FP4: unit u (0..31) of row r at 512 r + 16 (u ^ r)                         8 KB
-//   W6: lo slice of unit u at 512 r + 16 (u ^ r), hi slice at 8192 + 256 r + 8 (u ^ (2r & 31))   12 KB
+// different banks; gfx950 serves a 16-byte read in four groups of 16 lanes, and with the
+// swizzle u ^ r instead of u ^ (r & 7) every fragment read lost 4 cycles to conflicts):
+//   W4, FP4: unit u (0..31) of row r at 512 r + 16 (u ^ (r & 7))                         8 KB
+//   W6: lo slice of unit u at 512 r + 16 (u ^ (r & 7)),
+//       hi slice at 8192 + 256 r + 8 (u ^ (2r & 31))                                       12 KB
 // K tile j (0..7) of a stage is 4 units, one per lane quad q: unit 8q + j. Its x fragments
 // sit in a register ring of lm_xring slots and are loaded lm_xring - 1 tiles ahead (W4 keeps
 // the ring at 2 so that its two-block kernel fits 256 VGPRs: two waves per SIMD).
@@ -688,7 +690,7 @@ __device__ __forceinline__ void lm_store(const LmStage<FMT, RB>& st, uint8_t* ld
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int rr = 2 * i + (lane >> 5), u = lane & 31;
-      *reinterpret_cast<uint4*>(base + 512 * rr + 16 * (u ^ rr)) = st.v[r][i];
+      *reinterpret_cast<uint4*>(base + 512 * rr + 16 * (u ^ (rr & 7))) = st.v[r][i];
     }
     if constexpr (lm_w6<FMT>()) {
 #pragma unroll
@@ -772,7 +774,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
       for (int r = 0; r < RB; ++r) {
         const uint8_t* base = lds + r * lm_block<FMT>();
         Raw<wfmt(FMT)> raw;
-        raw.a = *reinterpret_cast<const uint4*>(base + 512 * nl + 16 * (u ^ nl));
+        raw.a = *reinterpret_cast<const uint4*>(base + 512 * nl + 16 * (u ^ (nl & 7)));
         if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2)
           raw.b = *reinterpret_cast<const uint2*>(base + 8192 + 256 * nl + 8 * (u ^ ((2 * nl) & 31)));
         h2 wv[16];
