@@ -1,4 +1,5 @@
-"""GPU parity of the tiled prefill kernel (wq_linear from 193 rows of x on) against the oracle.
+"""GPU parity of the tiled prefill kernel against the oracle (wq_linear from 193 rows of x on, and
+from 65 rows on for linears with enough tiles for their chain of K steps).
 
 The kernel stages 128 x 128 tiles of x and of the decoded weights in LDS; these cases cover
 ragged tiles in M and N, K with an odd number of 32-code units (a half-empty last K step),
@@ -50,7 +51,8 @@ def _x(seed, k, m, act):
 
 @pytest.mark.parametrize("fmt,act", CODES, ids=IDS)
 @pytest.mark.parametrize("n,k,m", [(1, 32, 193), (100, 96, 256), (130, 2080, 300), (257, 4256, 600), (64, 4096, 700),
-                                   (200, 256, 1030), (8200, 256, 512), (33, 11008, 512), (129, 2048, 200)])
+                                   (200, 256, 1030), (8200, 256, 512), (33, 11008, 512), (129, 2048, 200),
+                                   (4100, 256, 100), (1000, 512, 150), (300, 96, 65)])
 def test_prefill_shapes(fmt, act, n, k, m):
     w = _weights(n, k, 7 * n + k)
     x = _x(5000 + n + m, k, m, act)

@@ -264,9 +264,21 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_kernel_name(2, 64, 4096, 4096) == "lm_kernel<2, 1, 4>"
     assert wq.wq_linear_kernel_name(2, 64, 4096, 4128) == "mfma_kernel<2, 1>"
     assert wq.wq_linear_kernel_name(1, 40, 4096, 4096) == "mfma_kernel<1, 1>"
-    assert wq.wq_linear_kernel_name(3, 100, 4096, 4096) == "lm_kernel<3, 1, 4>"
-    # from 193 rows of x on: the tiled prefill kernel, one launch for all rows
-    assert wq.wq_linear_kernel_name(3, 192, 4096, 4096) == "lm_kernel<3, 1, 4>"
+    # 65..192 rows: the tiled prefill kernel when the linear has enough 128 x 128 tiles for its
+    # chain of K steps (K / 64 at most 2x the tiles for W4, 4x for W8/W6/FP4, any for fp16
+    # weights); else 64-row launches
+    assert wq.wq_linear_kernel_name(3, 100, 4096, 4096) == "pf_kernel<3>"      # 64 steps, 32 tiles
+    assert wq.wq_linear_kernel_name(2, 100, 4096, 4096) == "pf_kernel<2>"
+    assert wq.wq_linear_kernel_name(2, 100, 4096, 8192) == "lm_kernel<2, 1, 4>"   # 128 steps
+    assert wq.wq_linear_kernel_name(2, 129, 4096, 8192) == "pf_kernel<2>"      # 64 tiles
+    assert wq.wq_linear_kernel_name(3, 128, 4096, 11008) == "lm_kernel<3, 1, 4>"   # 172 steps, 32 tiles
+    assert wq.wq_linear_kernel_name(3, 160, 4096, 11008) == "pf_kernel<3>"     # 64 tiles
+    assert wq.wq_linear_kernel_name(2, 192, 8192, 28672) == "lm_kernel<2, 2, 4>"   # 448 steps, 128 tiles
+    assert wq.wq_linear_kernel_name(0, 65, 4096, 11008) == "pf_kernel<0>"
+    assert wq.wq_linear_kernel_name(3, 64, 4096, 4096) == "lm_kernel<3, 1, 4>"
+    # from 193 rows of x on: the tiled prefill kernel always, one launch for all rows
+    assert wq.wq_linear_kernel_name(2, 192, 4096, 11008) == "lm_kernel<2, 1, 4>"
+    assert wq.wq_linear_kernel_name(2, 193, 4096, 11008) == "pf_kernel<2>"
     assert wq.wq_linear_kernel_name(3, 193, 4096, 4096) == "pf_kernel<3>"
     assert wq.wq_linear_kernel_name(2, 600, 4096, 4128) == "pf_kernel<2>"
     assert wq.wq_linear_kernel_name(2 | wq.ACT_BF16, 512, 11008, 4096) == "pf_kernel<258>"
@@ -277,12 +289,18 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_grouped_kernel_name(3, 40, [(64, 4096), (64, (1 << 25) + 256)]) == "lm_kernel<3, 1, 1>"
     assert wq.wq_linear_grouped_kernel_name(3, 16, [(64, 4096), (64, (1 << 25) + 256)]) == "lm_grouped_kernel<3, 1, 1>"
     assert wq.wq_linear_grouped_kernel_name(3, 20, [(1024, 8192), (8192, 8192)]) == "lm_grouped_kernel<3, 2, 2>"
-    assert wq.wq_linear_grouped_kernel_name(3, 65, [(1024, 8192), (8192, 8192)]) == "lm_kernel<3, 2, 4>"
+    assert wq.wq_linear_grouped_kernel_name(3, 65, [(1024, 8192), (8192, 8192)]) == "pf_grouped_kernel<3>"
+    # a group whose longest chain is too long for its tiles: one call per item (the largest shown)
+    assert wq.wq_linear_grouped_kernel_name(3, 65, [(1024, 28672), (8192, 8192)]) == "pf_kernel<3>"
+    assert wq.wq_linear_grouped_kernel_name(3, 65, [(1024, 28672), (1024, 8192)]) == "lm_kernel<3, 1, 4>"
     # prefill-sized M: the tiles of every item in one launch (one item: the plain tiled kernel)
     assert wq.wq_linear_grouped_kernel_name(3, 512, [(1024, 8192), (8192, 8192)]) == "pf_grouped_kernel<3>"
     assert wq.wq_linear_grouped_kernel_name(2 | wq.ACT_BF16, 193, [(4096, 4096)] * 3) == "pf_grouped_kernel<258>"
     assert wq.wq_linear_grouped_kernel_name(3, 512, [(8192, 28672)]) == "pf_kernel<3>"
-    assert wq.wq_linear_grouped_kernel_name(3, 192, [(1024, 8192), (8192, 8192)]) == "lm_kernel<3, 2, 4>"
+    assert wq.wq_linear_grouped_kernel_name(3, 192, [(1024, 8192), (8192, 8192)]) == "pf_grouped_kernel<3>"
+    assert wq.wq_linear_grouped_kernel_name(2, 100, [(1024, 8192), (8192, 8192)]) == "pf_grouped_kernel<2>"
+    assert wq.wq_linear_grouped_kernel_name(2, 100, [(1024, 8192), (1024, 8192)]) == "lm_kernel<2, 1, 4>"
+    assert wq.wq_linear_grouped_kernel_name(2, 100, [(4096, 4096)] * 3) == "pf_grouped_kernel<2>"
     assert wq.wq_linear_grouped_kernel_name(1, 20, [(1024, 8192), (8192, 8192)]) == "mfma_kernel<1, 2>"
     # the LDS-staged group takes two row blocks per wave when any item has 8192 rows or more,
     # whatever the order of equal-size items
@@ -296,7 +314,8 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_kernel_name(4, 8, 4096, 4128) == "lm_kernel<4, 1, 1>"
     assert wq.wq_linear_kernel_name(4, 16, 8192, 4096) == "lm_kernel<4, 2, 1>"
     assert wq.wq_linear_kernel_name(4, 64, 4096, 4096) == "lm_kernel<4, 1, 4>"
-    assert wq.wq_linear_kernel_name(4, 100, 4096, 4096) == "lm_kernel<4, 1, 4>"
+    assert wq.wq_linear_kernel_name(4, 100, 4096, 4096) == "pf_kernel<4>"
+    assert wq.wq_linear_kernel_name(4, 100, 4096, 11008) == "lm_kernel<4, 1, 4>"
     assert wq.wq_linear_grouped_kernel_name(4, 1, [(4096, 4096), (11008, 4096)]) == "gemv_grouped_kernel<4, 1, 4>"
     assert wq.wq_linear_grouped_kernel_name(4, 8, [(1024, 8192), (8192, 8224)]) == "lm_grouped_kernel<4, 2, 1>"
     # bfloat16 activations: the same plan, named with the combined code (format | 0x100)

@@ -13,10 +13,10 @@ double f16_bits_to_f64(uint16_t h);
 uint8_t e3m2_encode(double t);        // finite t -> 6-bit e3m2 code (ties to even, saturating)
 uint8_t e2m1_encode(double t);        // finite t -> 4-bit e2m1 code (ties to even, saturating)
 
-// The tiled prefill kernel (wq_prefill.hip). pf_serves: whether it takes a linear of M rows
-// of x (from 193 rows on, while its grid fits one launch). The launches return a wq_status;
+// The tiled prefill kernel (wq_prefill.hip). pf_takes: whether it runs `count` linears (N[i] x
+// K[i]) of kernel code `code` at M rows of x, in one launch. The launches return a wq_status;
 // arguments are checked by the caller.
-bool pf_serves(int64_t M, int64_t N, int64_t K);
+bool pf_takes(int code, int64_t M, const int64_t* N, const int64_t* K, int count);
 int pf_launch(int code, const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros,
               uint16_t* y, int64_t M, int64_t N, int64_t K, void* stream);
 int pf_launch_grouped(int code, const wq_linear_item* items, int count, int64_t M, void* stream);

@@ -1145,14 +1145,6 @@ Family family_of(int fmt, int64_t M, int64_t N, int64_t K) {
   return use_mfma(fmt, M, N) ? FAM_MFMA : FAM_GEMV;
 }
 
-// A grouped call at prefill-sized M runs as one tiled launch when the tiled kernel serves
-// every item.
-bool group_pf(int64_t M, const int64_t* N, const int64_t* K, int count) {
-  for (int i = 0; i < count; ++i)
-    if (!wq::pf_serves(M, N[i], K[i])) return false;
-  return true;
-}
-
 int largest_item(const int64_t* N, const int64_t* K, int count) {
   int big = 0;
   for (int i = 1; i < count; ++i)
@@ -1228,7 +1220,7 @@ int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, c
   if (st != WQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* w = static_cast<const uint8_t*>(packed_w);
-  if (wq::pf_serves(M, N, K))   // prefill-sized M: one tiled launch for all rows
+  if (wq::pf_takes(fmt, M, &N, &K, 1))   // prefill-sized M: one tiled launch for all rows
     return wq::pf_launch(fmt, x, w, scales, zeros, y, M, N, K, stream);
   const int64_t slab = slab_rows(wfmt(fmt), K);
   for (int64_t m0 = 0; m0 < M; m0 += slab) {
@@ -1285,7 +1277,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
   // one family and one rows-per-wave (B or RB) for the whole launch: the largest item's (the
   // small items alone would pick fewer rows per wave to get enough waves, which the launch
   // has anyway); each item keeps the K split its own plan gives for that B / RB
-  if (count > 1 && group_pf(M, Ns, Ks, count))   // prefill-sized M: the tiles of all items in one launch
+  if (count > 1 && wq::pf_takes(fmt, M, Ns, Ks, count))   // prefill-sized M: all items' tiles in one launch
     return wq::pf_launch_grouped(fmt, items, count, M, stream);
   const int pf = wfmt(fmt);
   const Family fam = group_family(pf, M, Ns, Ks, count);
@@ -1348,7 +1340,7 @@ const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   static thread_local char buf[96];
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 32 || K % 32) return "";
   const int pf = wfmt(fmt);
-  if (wq::pf_serves(M, N, K)) {
+  if (wq::pf_takes(fmt, M, &N, &K, 1)) {
     snprintf(buf, sizeof(buf), "pf_kernel<%d>", fmt);
     return buf;
   }
@@ -1369,7 +1361,7 @@ const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, 
   if (!valid_fmt(fmt) || M < 1 || !N || !K || count < 1 || count > MAX_GROUP) return "";
   for (int i = 0; i < count; ++i)
     if (N[i] < 1 || K[i] < 32 || K[i] % 32) return "";
-  if (count > 1 && group_pf(M, N, K, count)) {
+  if (count > 1 && wq::pf_takes(fmt, M, N, K, count)) {
     snprintf(buf, sizeof(buf), "pf_grouped_kernel<%d>", fmt);
     return buf;
   }

@@ -36,7 +36,8 @@ namespace {
 // per lane let two workgroups share a CU. LDS rows are 128 B with the 16-byte chunks of each row
 // XOR-swizzled by the row (W4 with fp16 activations: 144-byte padded rows).
 
-constexpr int PF_MIN_M = 193;   // M from which wq_linear takes this kernel (below, 64-row launches win)
+constexpr int PF_MIN_M = 193;      // M from which the tiled kernel always runs
+constexpr int PF_MIN_M_ANY = 65;   // below: the decode kernels (up to 64 rows in one launch)
 constexpr int PF_BM = 128, PF_BN = 128;       // tile of y
 
 // The LDS layout of a tile row (64 K of 16-bit values, 16-byte chunks c = 0..7): by default 128
@@ -263,10 +264,22 @@ hipError_t launch_pf_grouped(hipStream_t s, const PfGroup& g, int M) {
 
 namespace wq {
 
-// From PF_MIN_M rows of x on, while the grid (128 x 128 tiles) fits one launch and M an int.
-bool pf_serves(int64_t M, int64_t N, int64_t K) {
-  (void)K;
-  return M >= PF_MIN_M && M <= INT32_MAX && pf_tiles(M, N) <= INT32_MAX;
+// The tiled kernel's time is about its longest chain of K steps (one per 64 K) while its tiles
+// fit the CUs; 64-row launches cost about one weight stream per 64 rows. So from 65 rows on it
+// runs when the linears have enough tiles for their chains: chain length (K / 64) at most 2x
+// (W4, the heaviest decode) or 4x (W8, W6, FP4) the tile count, any length for fp16 or bf16
+// weights; from 193 rows on always. Crossovers measured on the Llama-7B and 70B shapes at
+// M = 80..192: the down projections (K = 11008, 28672; 32 to 128 tiles) keep 64-row launches.
+bool pf_takes(int code, int64_t M, const int64_t* N, const int64_t* K, int count) {
+  if (M < PF_MIN_M_ANY || M > INT32_MAX) return false;
+  int64_t tiles = 0, kmax = 0;
+  for (int i = 0; i < count; ++i) {
+    tiles += pf_tiles(M, N[i]);
+    kmax = K[i] > kmax ? K[i] : kmax;
+  }
+  if (tiles > INT32_MAX) return false;
+  if (M >= PF_MIN_M || wfmt(code) == WQ_FMT_F16) return true;
+  return (kmax + 63) / 64 <= (wfmt(code) == WQ_FMT_W4G32 ? 2 : 4) * tiles;
 }
 
 int pf_launch(int code, const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros,
