@@ -61,6 +61,20 @@ def test_prefill_shapes(fmt, act, n, k, m):
     check_linear(dw.linear(x), x, _ref(fmt, act, w), "fmt %d act %d n %d k %d m %d" % (fmt, act, n, k, m), act=act)
 
 
+W8_F16 = [(f, a) for f, a in CODES if f in (wq.FMT_F16, wq.FMT_W8, wq.FMT_BF16)]
+
+
+@pytest.mark.parametrize("fmt,act", W8_F16, ids=["%s%s" % (NAMES[f], "_bf16" if a else "") for f, a in W8_F16])
+@pytest.mark.parametrize("n,k,m", [(300, 256, 40), (1100, 2080, 57), (130, 96, 64)])
+def test_prefill_small_m_w8_and_16bit_weights(fmt, act, n, k, m):
+    # W8 from 40 rows of x, fp16/bf16 weights from 17: the tiled kernel below 65 rows
+    w = _weights(n, k, 3 * n + k)
+    x = _x(6000 + n + m, k, m, act)
+    dw = DeviceWeights(fmt, w, act)
+    assert wq.wq_linear_kernel_name(fmt | act, m, n, k).startswith("pf_kernel")
+    check_linear(dw.linear(x), x, _ref(fmt, act, w), "fmt %d act %d n %d k %d m %d" % (fmt, act, n, k, m), act=act)
+
+
 @pytest.mark.parametrize("fmt,act", CODES, ids=IDS)
 def test_prefill_one_hot_is_bit_exact(fmt, act):
     n, k, m = 150, 2080, 520

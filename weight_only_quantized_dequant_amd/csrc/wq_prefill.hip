@@ -265,21 +265,24 @@ hipError_t launch_pf_grouped(hipStream_t s, const PfGroup& g, int M) {
 namespace wq {
 
 // The tiled kernel's time is about its longest chain of K steps (one per 64 K) while its tiles
-// fit the CUs; 64-row launches cost about one weight stream per 64 rows. So from 65 rows on it
-// runs when the linears have enough tiles for their chains: chain length (K / 64) at most 2x
-// (W4, the heaviest decode) or 4x (W8, W6, FP4) the tile count, any length for fp16 or bf16
-// weights; from 193 rows on always. Crossovers measured on the Llama-7B and 70B shapes at
-// M = 80..192: the down projections (K = 11008, 28672; 32 to 128 tiles) keep 64-row launches.
+// fit the CUs; the decode kernels cost about one weight stream per 64 rows (W4, W6, FP4) or per
+// 16 rows (W8, fp16 and bf16 weights). So the tiled kernel runs when the linears have enough
+// tiles for their chains: chain length (K / 64) at most 2x (W4, the heaviest decode) or 4x the
+// tile count, from 65 rows of x on (W8: 40, fp16/bf16 weights: 17, with any chain length from
+// 65 rows on); from 193 rows on always. Crossovers measured on the Llama-7B and 70B shapes at
+// M = 20..192: the down projections (K = 11008, 28672; 32 to 128 tiles) keep the decode kernels.
 bool pf_takes(int code, int64_t M, const int64_t* N, const int64_t* K, int count) {
-  if (M < PF_MIN_M_ANY || M > INT32_MAX) return false;
+  const int w = wfmt(code);
+  const int64_t m_min = w == WQ_FMT_F16 ? 17 : w == WQ_FMT_W8 ? 40 : PF_MIN_M_ANY;
+  if (M < m_min || M > INT32_MAX) return false;
   int64_t tiles = 0, kmax = 0;
   for (int i = 0; i < count; ++i) {
     tiles += pf_tiles(M, N[i]);
     kmax = K[i] > kmax ? K[i] : kmax;
   }
   if (tiles > INT32_MAX) return false;
-  if (M >= PF_MIN_M || wfmt(code) == WQ_FMT_F16) return true;
-  return (kmax + 63) / 64 <= (wfmt(code) == WQ_FMT_W4G32 ? 2 : 4) * tiles;
+  if (M >= PF_MIN_M || (w == WQ_FMT_F16 && M >= PF_MIN_M_ANY)) return true;
+  return (kmax + 63) / 64 <= (w == WQ_FMT_W4G32 ? 2 : 4) * tiles;
 }
 
 int pf_launch(int code, const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros,
