@@ -52,7 +52,7 @@ def _x(seed, k, m, act):
 @pytest.mark.parametrize("fmt,act", CODES, ids=IDS)
 @pytest.mark.parametrize("n,k,m", [(1, 32, 193), (100, 96, 256), (130, 2080, 300), (257, 4256, 600), (64, 4096, 700),
                                    (200, 256, 1030), (8200, 256, 512), (33, 11008, 512), (129, 2048, 200),
-                                   (4100, 256, 100), (1000, 512, 150), (300, 96, 65)])
+                                   (4100, 256, 100), (3000, 512, 150), (9000, 96, 65)])
 def test_prefill_shapes(fmt, act, n, k, m):
     w = _weights(n, k, 7 * n + k)
     x = _x(5000 + n + m, k, m, act)
@@ -65,9 +65,9 @@ W8_F16 = [(f, a) for f, a in CODES if f in (wq.FMT_F16, wq.FMT_W8, wq.FMT_BF16)]
 
 
 @pytest.mark.parametrize("fmt,act", W8_F16, ids=["%s%s" % (NAMES[f], "_bf16" if a else "") for f, a in W8_F16])
-@pytest.mark.parametrize("n,k,m", [(300, 256, 40), (1100, 2080, 57), (130, 96, 64)])
+@pytest.mark.parametrize("n,k,m", [(16600, 256, 48), (16500, 128, 24), (12000, 1024, 57)])
 def test_prefill_small_m_w8_and_16bit_weights(fmt, act, n, k, m):
-    # W8 from 40 rows of x, fp16/bf16 weights from 17: the tiled kernel below 65 rows
+    # W8 and fp16/bf16 weights below 65 rows of x: the tiled kernel where its K chain is short
     w = _weights(n, k, 3 * n + k)
     x = _x(6000 + n + m, k, m, act)
     dw = DeviceWeights(fmt, w, act)

@@ -263,11 +263,15 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_kernel_name(3, 20, 8192, 8192) == "lm_kernel<3, 2, 2>"
     assert wq.wq_linear_kernel_name(2, 64, 4096, 4096) == "lm_kernel<2, 1, 4>"
     assert wq.wq_linear_kernel_name(2, 64, 4096, 4128) == "mfma_kernel<2, 1>"
-    assert wq.wq_linear_kernel_name(1, 39, 4096, 4096) == "mfma_kernel<1, 1>"
-    # W8 from 40 rows, fp16 weights from 17 rows (their decode kernels take 16 rows per launch)
-    assert wq.wq_linear_kernel_name(1, 40, 4096, 4096) == "pf_kernel<1>"
-    assert wq.wq_linear_kernel_name(0, 17, 4096, 4096) == "pf_kernel<0>"
-    assert wq.wq_linear_kernel_name(0, 16, 4096, 4096) == "mfma_kernel<0, 1>"
+    assert wq.wq_linear_kernel_name(1, 40, 4096, 4096) == "mfma_kernel<1, 1>"
+    # W8 and fp16 weights (decode launches of 16 rows each) from 17 rows: the tiled kernel when
+    # its chain of K steps costs less than the 16-row launches' weight streams
+    assert wq.wq_linear_kernel_name(1, 17, 11008, 4096) == "mfma_kernel<1, 2>"
+    assert wq.wq_linear_kernel_name(1, 33, 11008, 4096) == "pf_kernel<1>"
+    assert wq.wq_linear_kernel_name(0, 17, 11008, 4096) == "pf_kernel<0>"
+    assert wq.wq_linear_kernel_name(0, 16, 11008, 4096) == "mfma_kernel<0, 2>"
+    assert wq.wq_linear_kernel_name(0, 17, 4096, 4096) == "mfma_kernel<0, 1>"
+    assert wq.wq_linear_kernel_name(0, 65, 4096, 4096) == "pf_kernel<0>"
     assert wq.wq_linear_kernel_name(0, 40, 4096, 11008) == "mfma_kernel<0, 1>"   # 172 steps, 32 tiles
     # 65..192 rows: the tiled prefill kernel when the linear has enough 128 x 128 tiles for its
     # chain of K steps (K / 64 at most 2x the tiles for W4, 4x for W8/W6/FP4, any for fp16

@@ -265,24 +265,37 @@ hipError_t launch_pf_grouped(hipStream_t s, const PfGroup& g, int M) {
 namespace wq {
 
 // The tiled kernel's time is about its longest chain of K steps (one per 64 K) while its tiles
-// fit the CUs; the decode kernels cost about one weight stream per 64 rows (W4, W6, FP4) or per
-// 16 rows (W8, fp16 and bf16 weights). So the tiled kernel runs when the linears have enough
-// tiles for their chains: chain length (K / 64) at most 2x (W4, the heaviest decode) or 4x the
-// tile count, from 65 rows of x on (W8: 40, fp16/bf16 weights: 17, with any chain length from
-// 65 rows on); from 193 rows on always. Crossovers measured on the Llama-7B and 70B shapes at
-// M = 20..192: the down projections (K = 11008, 28672; 32 to 128 tiles) keep the decode kernels.
+// fit the CUs, else its tile-steps over the CUs; the decode kernels cost about one weight
+// stream per 64 rows of x (W4, W6, FP4) or per 16 rows (W8, fp16 and bf16 weights). Which one
+// runs below 193 rows (from 193 always the tiled kernel) was fitted to crossovers measured on
+// the Llama-7B and 70B shapes at M = 20..192:
+//  * W8, fp16/bf16 weights, from 17 rows: the tiled kernel when max(chain, tile-steps / 256)
+//    times 1.58 (W8) or 2.1 (16-bit) us is at most the 16-row launches' weight megabytes;
+//  * W4, W6, FP4, from 65 rows: when the chain is at most 2x (W4, the heaviest decode) or 4x
+//    the tile count. (Past 64 rows a group that the tiled kernel does not take runs one call
+//    per linear, so the tiles of all its linears count.)
+// So the down projections (K = 11008, 28672; 32 to 128 tiles) keep the decode kernels.
 bool pf_takes(int code, int64_t M, const int64_t* N, const int64_t* K, int count) {
   const int w = wfmt(code);
-  const int64_t m_min = w == WQ_FMT_F16 ? 17 : w == WQ_FMT_W8 ? 40 : PF_MIN_M_ANY;
-  if (M < m_min || M > INT32_MAX) return false;
-  int64_t tiles = 0, kmax = 0;
+  const bool rows16 = w == WQ_FMT_F16 || w == WQ_FMT_W8;
+  if (M < (rows16 ? 17 : PF_MIN_M_ANY) || M > INT32_MAX) return false;
+  int64_t tiles = 0, kmax = 0, tile_steps = 0;
+  double mbytes = 0.0;
   for (int i = 0; i < count; ++i) {
-    tiles += pf_tiles(M, N[i]);
+    const int64_t t = pf_tiles(M, N[i]);
+    tiles += t;
+    tile_steps += t * ((K[i] + 63) / 64);
+    mbytes += (double)N[i] * (double)K[i] * (w == WQ_FMT_F16 ? 2.0 : 1.0) * 1e-6;
     kmax = K[i] > kmax ? K[i] : kmax;
   }
   if (tiles > INT32_MAX) return false;
-  if (M >= PF_MIN_M || (w == WQ_FMT_F16 && M >= PF_MIN_M_ANY)) return true;
-  return (kmax + 63) / 64 <= (w == WQ_FMT_W4G32 ? 2 : 4) * tiles;
+  if (M >= PF_MIN_M) return true;
+  const int64_t chain = (kmax + 63) / 64;
+  if (rows16) {
+    const double steps = chain > tile_steps / 256.0 ? (double)chain : tile_steps / 256.0;
+    return steps * (w == WQ_FMT_F16 ? 2.1 : 1.58) <= (double)((M + 15) / 16) * mbytes;
+  }
+  return chain <= (w == WQ_FMT_W4G32 ? 2 : 4) * tiles;
 }
 
 int pf_launch(int code, const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros,
