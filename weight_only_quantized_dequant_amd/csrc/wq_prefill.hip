@@ -34,22 +34,23 @@ namespace {
 // a tile is the chain of its K steps: wq_linear takes this kernel from 193 rows of x on, where
 // it beats launches of 64 rows that reread the weights. 64 or 72 KB of LDS and under 256 registers
 // per lane let two workgroups share a CU. LDS rows are 128 B with the 16-byte chunks of each row
-// XOR-swizzled by the row (W4 with fp16 activations: 144-byte padded rows).
+// XOR-swizzled by the row (the weight tile of W4 with fp16 activations: 144-byte padded rows).
 
 constexpr int PF_MIN_M = 193;      // M from which the tiled kernel always runs
 constexpr int PF_MIN_M_ANY = 65;   // below: the decode kernels (up to 64 rows in one launch)
 constexpr int PF_BM = 128, PF_BN = 128;       // tile of y
 
-// The LDS layout of a tile row (64 K of 16-bit values, 16-byte chunks c = 0..7): by default 128
-// bytes with chunk c at 16 (c ^ (row & 7)), see below. W4 with fp16 activations keeps 144-byte
-// rows with chunks in order: its decode needs more registers, and the swizzled addresses took
-// it past the 256 that two workgroups per CU allow (spills).
-template <int FMT> constexpr bool pf_xor() { return FMT != WQ_FMT_W4G32; }
-template <int FMT> constexpr int pf_row() { return pf_xor<FMT>() ? 128 : 144; }      // bytes per LDS row
-template <int FMT> constexpr int pf_tile_bytes() { return 128 * pf_row<FMT>(); }     // one operand tile
-template <int FMT> constexpr int pf_lds_bytes() { return 4 * pf_tile_bytes<FMT>(); }   // 2 buffers of x and w
-template <int FMT> __device__ __forceinline__ int pf_off(int row, int c) {   // byte offset of chunk c of a row
-  return row * pf_row<FMT>() + ((pf_xor<FMT>() ? c ^ (row & 7) : c) << 4);
+// The LDS layout of a tile row (64 K of 16-bit values, 16-byte chunks c = 0..7): 128 bytes with
+// chunk c at 16 (c ^ (row & 7)), see below; the weight tile of W4 with fp16 activations keeps
+// 144-byte rows with chunks in order: its decode needs more registers, and the swizzled weight
+// addresses took it past the 256 that two workgroups per CU allow (spills in the loop).
+template <int FMT, bool W> constexpr bool pf_xor() { return !W || FMT != WQ_FMT_W4G32; }   // W: weight tile
+template <int FMT, bool W> constexpr int pf_row() { return pf_xor<FMT, W>() ? 128 : 144; }   // bytes per row
+template <int FMT> constexpr int pf_x_bytes() { return 128 * pf_row<FMT, false>(); }      // the x tile
+template <int FMT> constexpr int pf_buf_bytes() { return pf_x_bytes<FMT>() + 128 * pf_row<FMT, true>(); }
+template <int FMT> constexpr int pf_lds_bytes() { return 2 * pf_buf_bytes<FMT>(); }     // two buffers
+template <int FMT, bool W> __device__ __forceinline__ int pf_off(int row, int c) {   // chunk c of a tile row
+  return row * pf_row<FMT, W>() + ((pf_xor<FMT, W>() ? c ^ (row & 7) : c) << 4);
 }
 
 // Swizzled rows: chunk c (K 8c .. 8c+7) of LDS row `row` sits at 128 row + 16 (c ^ (row & 7)).
@@ -127,9 +128,9 @@ __device__ __forceinline__ void pf_park(const PfStage<FMT>& st, uint8_t* xs, uin
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint4 xv = st.x[i];
-    *reinterpret_cast<uint4*>(xs + pf_off<FMT>(pf_xrow(t, i), t & 7)) =
+    *reinterpret_cast<uint4*>(xs + pf_off<FMT, false>(pf_xrow(t, i), t & 7)) =
         make_uint4(xv.x & xm, xv.y & xm, xv.z & xm, xv.w & xm);
-    *reinterpret_cast<uint4*>(ws + pf_off<FMT>(r, 4 * h + i)) =
+    *reinterpret_cast<uint4*>(ws + pf_off<FMT, true>(r, 4 * h + i)) =
         make_uint4(as_u32(wv[4 * i]) & wm, as_u32(wv[4 * i + 1]) & wm, as_u32(wv[4 * i + 2]) & wm,
                    as_u32(wv[4 * i + 3]) & wm);
   }
@@ -166,22 +167,22 @@ __device__ __forceinline__ void pf_tile(const uint16_t* __restrict__ x, const ui
   PfStage<FMT> R0, R1;
   pf_load<FMT>(R0, x, w, scales, zeros, m0, n0, M, N, K, 0, r, h);
   pf_load<FMT>(R1, x, w, scales, zeros, m0, n0, M, N, K, 1, r, h);
-  constexpr int TILE = pf_tile_bytes<FMT>();
-  pf_park<FMT>(R0, lds, lds + TILE, n0, N, 0, U, r, h);
+  constexpr int BUF = pf_buf_bytes<FMT>(), XT = pf_x_bytes<FMT>();
+  pf_park<FMT>(R0, lds, lds + XT, n0, N, 0, U, r, h);
   pf_load<FMT>(R0, x, w, scales, zeros, m0, n0, M, N, K, 2, r, h);
   __syncthreads();
   auto mul = [&](int s) {
-    const uint8_t* xs = lds + (s & 1) * 2 * TILE;
-    const uint8_t* ws = xs + TILE;
+    const uint8_t* xs = lds + (s & 1) * BUF;
+    const uint8_t* ws = xs + XT;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {   // the two units of the step; lane quad q takes K 8q .. 8q+7 of each
       h8 a[4], bf[4];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
-        a[mi] = *reinterpret_cast<const h8*>(xs + pf_off<FMT>(64 * wm + 16 * mi + i16, 4 * kh + q));
+        a[mi] = *reinterpret_cast<const h8*>(xs + pf_off<FMT, false>(64 * wm + 16 * mi + i16, 4 * kh + q));
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
-        bf[ni] = *reinterpret_cast<const h8*>(ws + pf_off<FMT>(64 * wn + 16 * ni + i16, 4 * kh + q));
+        bf[ni] = *reinterpret_cast<const h8*>(ws + pf_off<FMT, true>(64 * wn + 16 * ni + i16, 4 * kh + q));
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -190,11 +191,11 @@ __device__ __forceinline__ void pf_tile(const uint16_t* __restrict__ x, const ui
   };
   for (int s = 0; s < steps; s += 2) {   // R1 holds step s+1, R0 step s+2
     mul(s);
-    pf_park<FMT>(R1, lds + ((s + 1) & 1) * 2 * TILE, lds + ((s + 1) & 1) * 2 * TILE + TILE, n0, N, s + 1, U, r, h);
+    pf_park<FMT>(R1, lds + ((s + 1) & 1) * BUF, lds + ((s + 1) & 1) * BUF + XT, n0, N, s + 1, U, r, h);
     pf_load<FMT>(R1, x, w, scales, zeros, m0, n0, M, N, K, s + 3, r, h);
     __syncthreads();
     mul(s + 1);
-    pf_park<FMT>(R0, lds + (s & 1) * 2 * TILE, lds + (s & 1) * 2 * TILE + TILE, n0, N, s + 2, U, r, h);
+    pf_park<FMT>(R0, lds + (s & 1) * BUF, lds + (s & 1) * BUF + XT, n0, N, s + 2, U, r, h);
     pf_load<FMT>(R0, x, w, scales, zeros, m0, n0, M, N, K, s + 4, r, h);
     __syncthreads();
   }
