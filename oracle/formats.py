@@ -1,4 +1,4 @@
-"""Number formats: fp16 and bfloat16 rounding, the FP6 e3m2 code and the FP4 e2m1 code.
+"""Number formats: fp16 and bfloat16 rounding, the FP6 e3m2 code, and the FP4 e2m1 and FP5 e2m2 codes.
 
 Test infrastructure only (see the package docstring for who may import it).
 
@@ -10,7 +10,10 @@ exponent field is 0, no infinities or NaNs, largest magnitude 28.
 The same page says the kernel design serves weights of other bit widths as well, and
 names none. FP4 is taken here as e2m1: 1 sign bit, 2 exponent bits with bias 1, 1
 mantissa bit, subnormals when the exponent field is 0, no infinities or NaNs, largest
-magnitude 6 (the eight magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+magnitude 6 (the eight magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6). FP5 is taken as e2m2 in the
+same family: 1 sign bit, 2 exponent bits with bias 1, 2 mantissa bits, subnormals when the
+exponent field is 0, no infinities or NaNs, largest magnitude 7 (the sixteen magnitudes
+0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6, 7).
 
 bfloat16 is the activation type named besides fp16 by the gpt-fast guide (www.jsqmd.com,
 section "混合精度训练与推理") and the speed-up strategies page (sharktoolz.top, section 4
@@ -24,6 +27,8 @@ E3M2_BIAS = 3
 E3M2_MAX = 28.0
 E2M1_BIAS = 1
 E2M1_MAX = 6.0
+E2M2_BIAS = 1
+E2M2_MAX = 7.0
 
 
 def fp16_bits(values):
@@ -169,4 +174,51 @@ def e2m1_encode(t):
         mag_code = np.where(n_min > 1, np.argmax(is_min & even, axis=1), np.argmax(is_min, axis=1))
         sign = np.signbit(flat[i:i + step]).astype(np.uint8)
         out[i:i + step] = mag_code.astype(np.uint8) | (sign << 3)
+    return out.reshape(t.shape)
+
+
+def e2m2_value(code):
+    """Value of one 5-bit e2m2 code ``s e1 e0 m1 m0`` (closed form, exact in float64)."""
+    code = int(code)
+    if not 0 <= code < 32:
+        raise ValueError("e2m2 code out of range: %r" % code)
+    sign = -1.0 if (code >> 4) & 1 else 1.0
+    e = (code >> 2) & 3
+    m = code & 3
+    if e == 0:
+        mag = (m / 4.0) * 2.0 ** (1 - E2M2_BIAS)        # subnormal: 0.m x 2^(1-bias)
+    else:
+        mag = (1.0 + m / 4.0) * 2.0 ** (e - E2M2_BIAS)  # normal: 1.m x 2^(e-bias)
+    return sign * mag
+
+
+def e2m2_table():
+    """All 32 code values as float64 (code 16 is -0.0)."""
+    return np.array([e2m2_value(c) for c in range(32)], dtype=np.float64)
+
+
+def e2m2_encode(t):
+    """Encode float64 values as e2m2 codes: nearest magnitude, ties to the even code, saturating.
+
+    As for e2m1: the sign bit is the sign bit of ``t`` (a negative value that rounds to
+    zero gives code 16, i.e. -0), the magnitude is the nearest of the 16 non-negative
+    values, a tie goes to the even code, and magnitudes above 7 saturate at 7. Written as
+    a brute-force search over the 16 magnitudes.
+    """
+    t = np.asarray(t, dtype=np.float64)
+    if not np.all(np.isfinite(t)):
+        raise ValueError("e2m2_encode: non-finite input")
+    mags = e2m2_table()[:16].reshape(1, -1)       # increasing: 0, 0.25, ..., 6, 7
+    even = (np.arange(16) % 2 == 0).reshape(1, -1)
+    flat = t.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 1 << 15
+    for i in range(0, flat.size, step):
+        a = np.minimum(np.abs(flat[i:i + step]), E2M2_MAX).reshape(-1, 1)
+        dist = np.abs(a - mags)
+        is_min = dist == dist.min(axis=1, keepdims=True)
+        n_min = is_min.sum(axis=1)
+        mag_code = np.where(n_min > 1, np.argmax(is_min & even, axis=1), np.argmax(is_min, axis=1))
+        sign = np.signbit(flat[i:i + step]).astype(np.uint8)
+        out[i:i + step] = mag_code.astype(np.uint8) | (sign << 4)
     return out.reshape(t.shape)

@@ -21,20 +21,26 @@ kernel consumes them. It gives no concrete layout. The layout used here is:
     - FP4 (16 bytes): one 128-bit little-endian number; code j sits in bits 4j .. 4j+3,
       so byte p holds code 2p in its low nibble and code 2p+1 in its high nibble (the
       order in which gfx950's packed FP4 convert takes a byte).
+    - FP5 (20 bytes): one 160-bit little-endian number. Bits 0..127 hold the low four
+      bits of every code (e1 e0 m1 m0), placed as the W4 codes are: word d holds codes
+      8d .. 8d+7, code 8d+2t in nibble t and code 8d+2t+1 in nibble t+4. Bits 128..159
+      hold the signs: the sign of code 2p in bit 128+p and of code 2p+1 in bit 144+p
+      (p = 0..15), so that one shift puts the signs of a pair at bits 15 and 31.
     - F16 (64 bytes, the unquantized baseline): bytes 2j, 2j+1 hold the fp16 bits of
       weight j, little-endian.
     - BF16 (64 bytes, the unquantized baseline for bfloat16 activations): the same with
       bfloat16 bits.
-* W6 only, split by planes: the units of a row are taken 64 at a time ("chunks"; the
-  last chunk of a row may hold fewer, Uc units). In a chunk, bytes 0..15 of its units
-  come first, unit after unit (16*Uc bytes), then bytes 16..23 of its units (8*Uc
-  bytes). A chunk with one unit is therefore stored exactly as that unit. (A device
-  lane reads one unit, so each of the two loads of a wave reads one contiguous block.)
-* Metadata stays in logical order: W8/W6/FP4 scales [N]; W4 scales and zeros [N][K/32],
+* W6 and FP5 only, split by planes: the units of a row are taken 64 at a time ("chunks";
+  the last chunk of a row may hold fewer, Uc units). In a chunk, bytes 0..15 of its units
+  come first, unit after unit (16*Uc bytes), then bytes 16.. of its units (8*Uc bytes for
+  W6, 4*Uc for FP5). A chunk with one unit is therefore stored exactly as that unit. (A
+  device lane reads one unit, so each of the two loads of a wave reads one contiguous block.)
+* Metadata stays in logical order: W8/W6/FP4/FP5 scales [N]; W4 scales and zeros [N][K/32],
   row-major (group g of row n covers the same 32 K as unit g).
 
 Codes given to and returned by these functions are the logical codes: int8 q for W8,
-0..15 for W4 and FP4, 0..63 for W6, uint16 fp16 bits for F16, uint16 bfloat16 bits for BF16.
+0..15 for W4 and FP4, 0..63 for W6, 0..31 for FP5, uint16 fp16 bits for F16, uint16 bfloat16
+bits for BF16.
 """
 
 import numpy as np
@@ -45,10 +51,12 @@ FMT_W4G32 = 2
 FMT_W6E3M2 = 3
 FMT_W4E2M1 = 4
 FMT_BF16 = 5
+FMT_W5E2M2 = 6
 
-_BITS = {FMT_F16: 16, FMT_W8: 8, FMT_W4G32: 4, FMT_W6E3M2: 6, FMT_W4E2M1: 4, FMT_BF16: 16}
+_BITS = {FMT_F16: 16, FMT_W8: 8, FMT_W4G32: 4, FMT_W6E3M2: 6, FMT_W4E2M1: 4, FMT_BF16: 16, FMT_W5E2M2: 5}
 UNIT = 32
-CHUNK = 64          # units per W6 plane chunk
+CHUNK = 64          # units per W6 / FP5 plane chunk
+_PLANED = (FMT_W6E3M2, FMT_W5E2M2)
 
 
 def _bits(fmt):
@@ -79,8 +87,20 @@ def zeros_count(fmt, n, k):
     return n * (k // 32) if fmt == FMT_W4G32 else 0
 
 
+def code_fields(fmt, j):
+    """[(first bit, width, shift)] of code j inside its unit, counting bits little-endian from the
+    unit's first byte: bits shift .. shift+width-1 of the code's stored value go to bits
+    first .. first+width-1 (one field for every format but FP5, whose sign sits apart)."""
+    if fmt == FMT_W5E2M2:
+        nib_first, _ = code_field(FMT_W4G32, j)
+        p, odd = divmod(j, 2)
+        return [(nib_first, 4, 0), (128 + 16 * odd + p, 1, 4)]
+    first, width = code_field(fmt, j)
+    return [(first, width, 0)]
+
+
 def code_field(fmt, j):
-    """(first bit, width) of code j inside its unit, counting bits little-endian from the unit's first byte."""
+    """(first bit, width) of code j inside its unit, for the formats stored as one field per code."""
     if fmt == FMT_W8:
         return 8 * j, 8
     if fmt == FMT_W4G32:
@@ -104,7 +124,7 @@ def _stored(fmt, code):
         if not -127 <= code <= 127:
             raise ValueError("int8 code out of range")
         return code + 128
-    limit = {FMT_W4G32: 16, FMT_W6E3M2: 64, FMT_W4E2M1: 16, FMT_F16: 65536, FMT_BF16: 65536}[fmt]
+    limit = {FMT_W4G32: 16, FMT_W6E3M2: 64, FMT_W4E2M1: 16, FMT_W5E2M2: 32, FMT_F16: 65536, FMT_BF16: 65536}[fmt]
     if not 0 <= code < limit:
         raise ValueError("code out of range")
     return code
@@ -131,11 +151,11 @@ def pack_scalar(fmt, codes):
         for u in range(k // UNIT):
             acc = 0
             for j in range(UNIT):
-                first, width = code_field(fmt, j)
                 v = _stored(fmt, codes[r, UNIT * u + j])
-                for b in range(width):
-                    if (v >> b) & 1:
-                        acc |= 1 << (first + b)
+                for first, width, shift in code_fields(fmt, j):
+                    for b in range(width):
+                        if (v >> (shift + b)) & 1:
+                            acc |= 1 << (first + b)
             unit = acc.to_bytes(ub, "little")
             for i in range(ub):
                 out[_byte_home(fmt, r, u, i, k)] = unit[i]
@@ -146,12 +166,12 @@ def _byte_home(fmt, r, u, i, k):
     """Offset in the packed array of byte i of unit u of row r."""
     ub = unit_bytes(fmt)
     units = k // UNIT
-    if fmt != FMT_W6E3M2:
+    if fmt not in _PLANED:
         return (r * units + u) * ub + i
     c, j = divmod(u, CHUNK)
     uc = min(CHUNK, units - c * CHUNK)
     base = (r * units + c * CHUNK) * ub
-    return base + 16 * j + i if i < 16 else base + 16 * uc + 8 * j + (i - 16)
+    return base + 16 * j + i if i < 16 else base + 16 * uc + (ub - 16) * j + (i - 16)
 
 
 def unpack_scalar(fmt, packed, n, k):
@@ -161,15 +181,17 @@ def unpack_scalar(fmt, packed, n, k):
         raise ValueError("packed size mismatch")
     ub = unit_bytes(fmt)
     dtype = {FMT_W8: np.int8, FMT_W4G32: np.uint8, FMT_W6E3M2: np.uint8, FMT_W4E2M1: np.uint8, FMT_F16: np.uint16,
-             FMT_BF16: np.uint16}[fmt]
+             FMT_BF16: np.uint16, FMT_W5E2M2: np.uint8}[fmt]
     codes = np.zeros((n, k), dtype=dtype)
     for r in range(n):
         for u in range(k // UNIT):
             unit = bytes(int(packed[_byte_home(fmt, r, u, i, k)]) for i in range(ub))
             acc = int.from_bytes(unit, "little")
             for j in range(UNIT):
-                first, width = code_field(fmt, j)
-                codes[r, UNIT * u + j] = _logical(fmt, (acc >> first) & ((1 << width) - 1))
+                v = 0
+                for first, width, shift in code_fields(fmt, j):
+                    v |= ((acc >> first) & ((1 << width) - 1)) << shift
+                codes[r, UNIT * u + j] = _logical(fmt, v)
     return codes
 
 
@@ -203,13 +225,27 @@ def pack_vectorized(fmt, codes):
         c = c.reshape(n, k // 4, 4)
         v = c[:, :, 0] | (c[:, :, 1] << 6) | (c[:, :, 2] << 12) | (c[:, :, 3] << 18)
         b = np.stack([v & 0xFF, (v >> 8) & 0xFF, (v >> 16) & 0xFF], axis=-1).astype(np.uint8)
-        return _w6_to_planes(b.reshape(n, k // UNIT, 24)).reshape(-1)
+        return _to_planes(b.reshape(n, k // UNIT, 24)).reshape(-1)
     if fmt == FMT_W4E2M1:
         c = codes.astype(np.uint8)
         if c.max(initial=0) > 15:
             raise ValueError("fp4 code out of range")
         c = c.reshape(n, k // 2, 2)
         return (c[:, :, 0] | (c[:, :, 1] << 4)).astype(np.uint8).reshape(-1)
+    if fmt == FMT_W5E2M2:
+        c = codes.astype(np.uint32)
+        if c.max(initial=0) > 31:
+            raise ValueError("fp5 code out of range")
+        mag = (c & 0xF).reshape(n, k // 8, 8)[:, :, _W4_ORDER]
+        words = np.zeros((n, k // 8), dtype=np.uint32)
+        for p in range(8):
+            words |= mag[:, :, p] << np.uint32(4 * p)
+        sgn = (c >> 4).reshape(n, k // UNIT, 16, 2)            # [.., p, odd]
+        sw = np.zeros((n, k // UNIT), dtype=np.uint32)
+        for p in range(16):
+            sw |= (sgn[:, :, p, 0] << np.uint32(p)) | (sgn[:, :, p, 1] << np.uint32(16 + p))
+        units = np.concatenate([words.reshape(n, k // UNIT, 4), sw.reshape(n, k // UNIT, 1)], axis=2)
+        return _to_planes(units.astype("<u4").view(np.uint8).reshape(n, k // UNIT, 20)).reshape(-1)
     if fmt in (FMT_F16, FMT_BF16):
         return codes.astype(np.uint16).astype("<u2").view(np.uint8).reshape(-1)
     raise ValueError("unknown format %r" % fmt)
@@ -228,20 +264,33 @@ def unpack_vectorized(fmt, packed, n, k):
             out[:, :, _W4_ORDER[p]] = (words >> np.uint32(4 * p)) & 0xF
         return out.reshape(n, k)
     if fmt == FMT_W6E3M2:
-        b = _w6_from_planes(packed.reshape(n, -1), k // UNIT).reshape(n, k // 4, 3).astype(np.uint32)
+        b = _from_planes(packed.reshape(n, -1), k // UNIT, 24).reshape(n, k // 4, 3).astype(np.uint32)
         v = b[:, :, 0] | (b[:, :, 1] << 8) | (b[:, :, 2] << 16)
         out = np.stack([(v >> s) & 0x3F for s in (0, 6, 12, 18)], axis=-1).astype(np.uint8)
         return out.reshape(n, k)
     if fmt == FMT_W4E2M1:
         b = packed.reshape(n, k // 2)
         return np.stack([b & 0xF, b >> 4], axis=-1).astype(np.uint8).reshape(n, k)
+    if fmt == FMT_W5E2M2:
+        units = _from_planes(packed.reshape(n, -1), k // UNIT, 20).copy().view("<u4").reshape(n, k // UNIT, 5)
+        words = units[:, :, :4].reshape(n, k // 8)
+        mag = np.zeros((n, k // 8, 8), dtype=np.uint8)
+        for p in range(8):
+            mag[:, :, _W4_ORDER[p]] = (words >> np.uint32(4 * p)) & 0xF
+        sw = units[:, :, 4]
+        sgn = np.zeros((n, k // UNIT, 16, 2), dtype=np.uint8)
+        for p in range(16):
+            sgn[:, :, p, 0] = (sw >> np.uint32(p)) & 1
+            sgn[:, :, p, 1] = (sw >> np.uint32(16 + p)) & 1
+        return (mag.reshape(n, k) | (sgn.reshape(n, k) << 4)).astype(np.uint8)
     if fmt in (FMT_F16, FMT_BF16):
         return packed.view("<u2").reshape(n, k).astype(np.uint16)
     raise ValueError("unknown format %r" % fmt)
 
 
-def _w6_to_planes(units):
-    """[N, U, 24] unit-contiguous bytes -> [N, U*24] with every chunk of 64 units split into planes."""
+def _to_planes(units):
+    """[N, U, B] unit-contiguous bytes -> [N, U*B] with every chunk of 64 units split into planes
+    (bytes 0..15 of its units, then bytes 16..B-1)."""
     n, u, _ = units.shape
     parts = []
     for c0 in range(0, u, CHUNK):
@@ -251,15 +300,15 @@ def _w6_to_planes(units):
     return np.concatenate(parts, axis=1)
 
 
-def _w6_from_planes(rows, u):
-    """Inverse of _w6_to_planes: [N, U*24] -> [N, U, 24]."""
+def _from_planes(rows, u, ub):
+    """Inverse of _to_planes: [N, U*ub] -> [N, U, ub]."""
     n = rows.shape[0]
-    out = np.empty((n, u, 24), dtype=np.uint8)
+    out = np.empty((n, u, ub), dtype=np.uint8)
     pos = 0
     for c0 in range(0, u, CHUNK):
         uc = min(CHUNK, u - c0)
         out[:, c0:c0 + uc, :16] = rows[:, pos:pos + 16 * uc].reshape(n, uc, 16)
         pos += 16 * uc
-        out[:, c0:c0 + uc, 16:] = rows[:, pos:pos + 8 * uc].reshape(n, uc, 8)
-        pos += 8 * uc
+        out[:, c0:c0 + uc, 16:] = rows[:, pos:pos + (ub - 16) * uc].reshape(n, uc, ub - 16)
+        pos += (ub - 16) * uc
     return out

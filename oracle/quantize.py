@@ -19,6 +19,8 @@ The pages give no formulas. The readings are:
   ``w / s`` (nearest, ties to even code, saturating at 28).
 * FP4 (a further bit width through the same design; the page names none): e2m1 with one
   fp16 scale per output row, ``s = fp16(max|w| / 6)``, code = e2m1 encoding of ``w / s``.
+* FP5 (the same): e2m2 with one fp16 scale per output row, ``s = fp16(max|w| / 7)``, code =
+  e2m2 encoding of ``w / s``.
 * In all of them a scale that rounds to 0 makes every code of its row (or group) 0, and
   z = 0. A scale that overflows fp16 is an error.
 
@@ -28,7 +30,7 @@ weights and of the fp16 scale, then one rounding (``rint`` ties to even, or fp16
 
 import numpy as np
 
-from .formats import fp16_bits, fp16_from_bits, e3m2_encode, e2m1_encode, E2M1_MAX
+from .formats import fp16_bits, fp16_from_bits, e3m2_encode, e2m1_encode, e2m2_encode, E2M1_MAX, E2M2_MAX
 
 
 class OracleRangeError(ValueError):
@@ -106,4 +108,17 @@ def quantize_fp4(w):
     nz = s > 0
     if np.any(nz):
         codes[nz] = e2m1_encode(w[nz] / s[nz, None])
+    return codes, s_bits
+
+
+def quantize_fp5(w):
+    """FP5 e2m2 per output row. Returns (codes uint8 [N,K] in 0..31, scale bits uint16 [N])."""
+    w = _check_w(w)
+    amax = np.max(np.abs(w), axis=1)
+    s_bits = _scale16(amax / E2M2_MAX)
+    s = fp16_from_bits(s_bits)
+    codes = np.zeros(w.shape, dtype=np.uint8)
+    nz = s > 0
+    if np.any(nz):
+        codes[nz] = e2m2_encode(w[nz] / s[nz, None])
     return codes, s_bits

@@ -187,6 +187,30 @@ def check_e2m1_table(value_fn):
     return True
 
 
+def golden_e2m2():
+    """32 e2m2 magnitudes as Fractions with the sign of each code: (value, negative?)."""
+    rows = []
+    with open(os.path.join(GOLDEN, "e2m2_table.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([Fraction(t) for t in line.split()])
+    assert len(rows) == 4 and all(len(r) == 4 for r in rows)
+    mags = [rows[c >> 2][c & 3] for c in range(16)]
+    return [(mags[c & 15], bool(c & 16)) for c in range(32)]
+
+
+def check_e2m2_table(value_fn):
+    """value_fn(code) must equal the hand-typed e2m2 table, with -0 for code 16."""
+    for c, (mag, neg) in enumerate(golden_e2m2()):
+        v = value_fn(c)
+        if Fraction(v) != (-mag if neg else mag):
+            return False
+        if math.copysign(1.0, v) != (-1.0 if neg else 1.0):
+            return False
+    return True
+
+
 # ---------------------------------------------------------------- brute-force quantizers
 def brute_fp4_code(t):
     """Nearest e2m1 code to a float t: sign from t's sign bit, nearest magnitude, ties to even code."""
@@ -217,6 +241,38 @@ def brute_fp4_row(w_row):
             if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
                 best = (d, c)
         codes.append(best[1] | (8 if math.copysign(1.0, float(v)) < 0 else 0))
+    return codes, fraction_to_f16_bits(s)
+
+
+def brute_fp5_code(t):
+    """Nearest e2m2 code to a float t: sign from t's sign bit, nearest magnitude, ties to even code."""
+    tab = golden_e2m2()
+    neg = math.copysign(1.0, t) < 0
+    ft = abs(Fraction(t))
+    best = None
+    for c in range(16):
+        d = abs(ft - tab[c][0])
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1] | (16 if neg else 0)
+
+
+def brute_fp5_row(w_row):
+    """(codes, scale bits) for one fp32 row: exact quotient w/s, nearest e2m2 magnitude, ties to even code."""
+    amax = max(abs(Fraction(float(v))) for v in w_row)
+    s = fp16_round(amax / 7)
+    if s == 0:
+        return [0] * len(w_row), 0
+    tab = golden_e2m2()
+    codes = []
+    for v in w_row:
+        a = abs(Fraction(float(v))) / s
+        best = None
+        for c in range(16):
+            d = abs(a - tab[c][0])
+            if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+                best = (d, c)
+        codes.append(best[1] | (16 if math.copysign(1.0, float(v)) < 0 else 0))
     return codes, fraction_to_f16_bits(s)
 
 
@@ -320,9 +376,9 @@ def check_quantizer(fmt_name, quant_fn, w):
                 if [int(v) for v in q[r, 32 * g:32 * g + 32]] != bq:
                     return False
         return True
-    if fmt_name in ("w6", "fp4"):
+    if fmt_name in ("w6", "fp4", "fp5"):
         q, s = out
-        brute = brute_fp6_row if fmt_name == "w6" else brute_fp4_row
+        brute = {"w6": brute_fp6_row, "fp4": brute_fp4_row, "fp5": brute_fp5_row}[fmt_name]
         for r in range(n):
             bq, bs = brute(w[r])
             if int(s[r]) != bs or [int(v) for v in q[r]] != bq:
@@ -357,8 +413,8 @@ def exact_dequant(fmt_name, code, scale_bits, zero_bits=0, act="f16"):
         v = code * s
     elif fmt_name == "w4":
         v = (code - f16_bits_to_fraction(zero_bits)) * s
-    elif fmt_name in ("w6", "fp4"):
-        mag, neg = (golden_e3m2() if fmt_name == "w6" else golden_e2m1())[code]
+    elif fmt_name in ("w6", "fp4", "fp5"):
+        mag, neg = {"w6": golden_e3m2, "fp4": golden_e2m1, "fp5": golden_e2m2}[fmt_name]()[code]
         v = (-mag if neg else mag) * s
         if v == 0:
             return 0x8000 if (neg and s > 0) or (not neg and s < 0) else 0

@@ -22,6 +22,49 @@ def test_pins_accept_the_oracle():
     assert pins.check_quantizer("w6", oracle.quantize_fp6, w)
     assert pins.check_e2m1_table(oracle.e2m1_value)
     assert pins.check_quantizer("fp4", oracle.quantize_fp4, w)
+    assert pins.check_e2m2_table(oracle.e2m2_value)
+    assert pins.check_quantizer("fp5", oracle.quantize_fp5, w)
+
+
+def test_e2m2_wrong_bias_is_caught():
+    assert not pins.check_e2m2_table(lambda c: oracle.e2m2_value(c) * 2)
+
+
+def test_e2m2_subnormal_as_normal_is_caught():
+    def bad(c):
+        e, m = (c >> 2) & 3, c & 3
+        v = (1 + m / 4) * 2.0 ** (e - 1)          # forgets that exponent field 0 is subnormal
+        return -v if c & 16 else v
+    assert not pins.check_e2m2_table(bad)
+
+
+def test_e2m2_mantissa_bits_swapped_is_caught():
+    def bad(c):
+        return oracle.e2m2_value((c & 0x1C) | ((c & 1) << 1) | ((c >> 1) & 1))
+    assert not pins.check_e2m2_table(bad)
+
+
+def test_fp5_scale_from_fp4_range_is_caught():
+    def bad_quant(w):
+        w64 = w.astype(np.float64)
+        s_bits = oracle.fp16_bits(np.abs(w64).max(axis=1) / 6.0)     # the FP4 maximum, not 7
+        s = oracle.fp16_from_bits(s_bits)
+        return oracle.e2m2_encode(w64 / s[:, None]), s_bits
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((2, 64)) * 0.1).astype(np.float32)
+    assert not pins.check_quantizer("fp5", bad_quant, w)
+
+
+def test_fp5_sign_plane_order_is_caught():
+    for name, codes, expected in pins.golden_pack_examples():
+        if name != "FP5":
+            continue
+        c = np.array(codes, dtype=np.uint32)
+        sw = 0
+        for j in range(32):                       # signs in code order instead of (even codes, odd codes)
+            sw |= int(c[j] >> 4) << j
+        assert expected[16:] != sw.to_bytes(4, "little")
+        assert expected[16:] == bytes([0x00, 0xFF, 0x00, 0xFF])
 
 
 def test_e2m1_wrong_bias_is_caught():

@@ -7,10 +7,11 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, FMT_BF16
+from oracle import FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, FMT_BF16, FMT_W5E2M2
 from tests import pins
 
-FMTS = {"w8": FMT_W8, "w4": FMT_W4G32, "w6": FMT_W6E3M2, "f16": FMT_F16, "fp4": FMT_W4E2M1, "bf16": FMT_BF16}
+FMTS = {"w8": FMT_W8, "w4": FMT_W4G32, "w6": FMT_W6E3M2, "f16": FMT_F16, "fp4": FMT_W4E2M1, "bf16": FMT_BF16,
+        "fp5": FMT_W5E2M2}
 
 
 # ------------------------------------------------------------------ e3m2
@@ -114,6 +115,57 @@ def test_e2m1_encode_vs_exact_brute_force():
         assert int(g) == pins.brute_fp4_code(float(v)), v
 
 
+# ------------------------------------------------------------------ e2m2 (FP5)
+def test_e2m2_table_matches_hand_typed_table():
+    assert pins.check_e2m2_table(oracle.e2m2_value)
+
+
+def test_e2m2_special_values():
+    t = oracle.e2m2_table()
+    assert t[15] == 7.0 and t[31] == -7.0                   # largest magnitude, no inf/NaN
+    assert list(t[1:4]) == [0.25, 0.5, 0.75]                # the subnormals, 2^(1-1) m / 4
+    assert t[4] == 1.0                                      # smallest normal
+    assert t[0] == 0.0 and not math.copysign(1, t[0]) < 0
+    assert t[16] == 0.0 and math.copysign(1, t[16]) < 0     # -0
+    assert np.all(np.diff(t[:16]) > 0)
+    assert np.array_equal(t[16:], -t[:16])
+    # the FP4 values are the even-mantissa FP5 values: e2m1 code s.ee.m is e2m2 code s.ee.m0
+    assert all(oracle.e2m2_value(((c & 8) << 1) | ((c & 7) << 1)) == oracle.e2m1_value(c) for c in range(16))
+
+
+def test_e2m2_fp16_bit_placement_identity():
+    # code bits s.ee.mm placed at fp16 bits 15 and 11..8 give e2m2(c) * 2^-14 exactly,
+    # the subnormals and -0 included (fp16 exponent bias 15 = e2m2 bias 1 + 14)
+    for c in range(32):
+        bits = ((c & 0x10) << 11) | ((c & 0xF) << 8)
+        v = float(np.uint16(bits).view(np.float16))
+        assert v * 16384.0 == oracle.e2m2_value(c)
+        assert math.copysign(1, v) == math.copysign(1, oracle.e2m2_value(c))
+
+
+@pytest.mark.parametrize("t,code", [
+    (0.125, 0), (-0.125, 16),         # tie between 0 and 0.25: code 0, sign kept
+    (0.375, 2), (0.625, 2), (1.125, 4), (1.375, 6), (1.875, 8),   # ties go to the even code
+    (2.25, 8), (2.75, 10), (3.75, 12), (4.5, 12), (5.5, 14), (6.5, 14),
+    (6.51, 15), (7.0, 15), (1e6, 15), (-1e6, 31),
+    (-1e-9, 16), (-0.0, 16), (0.0, 0), (0.374, 1), (0.376, 2),
+])
+def test_e2m2_encode_examples(t, code):
+    assert int(oracle.e2m2_encode(np.array([t]))[0]) == code
+
+
+def test_e2m2_encode_vs_exact_brute_force():
+    rng = np.random.default_rng(19)
+    tab = oracle.e2m2_table()
+    mids = [(tab[c] + tab[c + 1]) / 2 for c in range(15)]
+    vals = list(rng.standard_normal(1000) * 3) + mids + [-m for m in mids]
+    vals += [m + d for m in mids for d in (1e-12, -1e-12)]
+    vals += [tab[c] for c in range(32)] + [8.0, -7.5, 7.01, 1e-30, -1e-30]
+    got = oracle.e2m2_encode(np.array(vals))
+    for v, g in zip(vals, got):
+        assert int(g) == pins.brute_fp5_code(float(v)), v
+
+
 # ------------------------------------------------------------------ fp16 rounding
 def test_fp16_rounding_vs_exact():
     rng = np.random.default_rng(3)
@@ -176,12 +228,12 @@ def _adversarial(n, k, rng):
     return w
 
 
-@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4"])
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4", "fp5"])
 def test_quantizer_vs_brute_force(name):
     rng = np.random.default_rng(11)
     w = _adversarial(8, 64, rng)
     fn = {"w8": oracle.quantize_int8, "w4": oracle.quantize_int4_g32, "w6": oracle.quantize_fp6,
-          "fp4": oracle.quantize_fp4}[name]
+          "fp4": oracle.quantize_fp4, "fp5": oracle.quantize_fp5}[name]
     assert pins.check_quantizer(name, fn, w)
 
 
@@ -233,6 +285,19 @@ def test_fp4_saturation_and_negative_zero():
     assert codes[0, :5].tolist() == [7, 15, 8, 4, 0]
 
 
+def test_fp5_saturation_and_negative_zero():
+    w = np.zeros((1, 32), dtype=np.float32)
+    w[0, 0] = 7.0           # scale 1
+    w[0, 1] = -7.0
+    w[0, 2] = -0.001        # rounds to -0
+    w[0, 3] = 4.5           # tie between 4 (code 12) and 5 (code 13) -> 12
+    w[0, 4] = 0.125         # tie between 0 and 0.25 -> 0
+    w[0, 5] = 0.625         # tie between 0.5 (code 2) and 0.75 (code 3) -> 2
+    codes, s = oracle.quantize_fp5(w)
+    assert int(s[0]) == 0x3C00
+    assert codes[0, :6].tolist() == [15, 31, 16, 12, 0, 2]
+
+
 def test_quantizer_errors():
     with pytest.raises(oracle.OracleRangeError):
         oracle.quantize_int8(np.array([[np.nan] * 32], dtype=np.float32))
@@ -249,7 +314,7 @@ def test_pack_matches_hand_derived_bytes():
         assert bytes(oracle.pack_vectorized(fmt, c)) == expected, name
 
 
-@pytest.mark.parametrize("name", ["w8", "w4", "w6", "f16", "fp4", "bf16"])
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "f16", "fp4", "bf16", "fp5"])
 @pytest.mark.parametrize("n,k", [(3, 96), (2, 32 * 130)])       # 130 units: two full chunks of 64 and one of 2
 def test_pack_scalar_equals_vectorized_and_round_trips(name, n, k):
     fmt = FMTS[name]
@@ -260,12 +325,14 @@ def test_pack_scalar_equals_vectorized_and_round_trips(name, n, k):
         codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
     elif name == "w6":
         codes = rng.integers(0, 64, (n, k)).astype(np.uint8)
+    elif name == "fp5":
+        codes = rng.integers(0, 32, (n, k)).astype(np.uint8)
     else:
         codes = rng.integers(0, 65536, (n, k)).astype(np.uint16)
     a = oracle.pack_scalar(fmt, codes)
     b = oracle.pack_vectorized(fmt, codes)
     assert a.size == oracle.packed_bytes(fmt, n, k) == n * k * {"w8": 8, "w4": 4, "w6": 6, "f16": 16, "fp4": 4,
-                                                                "bf16": 16}[name] // 8
+                                                                "bf16": 16, "fp5": 5}[name] // 8
     assert np.array_equal(a, b)
     assert np.array_equal(oracle.unpack_scalar(fmt, a, n, k), codes)
     assert np.array_equal(oracle.unpack_vectorized(fmt, b, n, k), codes)
@@ -278,10 +345,11 @@ def test_metadata_counts():
     assert oracle.scales_count(FMT_F16, 7, 64) == 0
     assert oracle.scales_count(FMT_W4E2M1, 7, 64) == 7 and oracle.zeros_count(FMT_W4E2M1, 7, 64) == 0
     assert oracle.scales_count(FMT_BF16, 7, 64) == 0 and oracle.zeros_count(FMT_BF16, 7, 64) == 0
+    assert oracle.scales_count(FMT_W5E2M2, 7, 64) == 7 and oracle.zeros_count(FMT_W5E2M2, 7, 64) == 0
 
 
 # ------------------------------------------------------------------ dequant
-@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4"])
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4", "fp5"])
 def test_dequant_exact_vs_fraction_and_fp32(name):
     fmt = FMTS[name]
     rng = np.random.default_rng(9)
@@ -297,7 +365,7 @@ def test_dequant_exact_vs_fraction_and_fp32(name):
             g = c // 32 if name == "w4" else 0
             want = pins.exact_dequant(name, int(codes[r, c]), int(sv[r, g]), int(zv[r, g]) if zv is not None else 0)
             got = int(d[r, c])
-            assert got == want or (want in (0, 0x8000) and got in (0, 0x8000) and name not in ("w6", "fp4")), (r, c)
+            assert got == want or (want in (0, 0x8000) and got in (0, 0x8000) and name not in ("w6", "fp4", "fp5")), (r, c)
     # the product is exact in fp32 as well, so an fp32 multiply then one rounding agrees bit for bit
     s32 = oracle.fp16_from_bits(sv).astype(np.float32)
     if name == "w8":
@@ -307,12 +375,14 @@ def test_dequant_exact_vs_fraction_and_fp32(name):
         v32 = (codes.astype(np.float32) - np.repeat(zz, 32, axis=1)) * np.repeat(s32, 32, axis=1)
     elif name == "w6":
         v32 = oracle.e3m2_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
+    elif name == "fp5":
+        v32 = oracle.e2m2_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
     else:
         v32 = oracle.e2m1_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
     assert np.array_equal(v32.astype(np.float16).view(np.uint16), d)
 
 
-@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4"])
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4", "fp5"])
 def test_dequant_bf16_exact_vs_fraction_and_fp32(name):
     import torch
     fmt = FMTS[name]
@@ -330,7 +400,7 @@ def test_dequant_bf16_exact_vs_fraction_and_fp32(name):
             want = pins.exact_dequant(name, int(codes[r, c]), int(sv[r, g]), int(zv[r, g]) if zv is not None else 0,
                                       act="bf16")
             got = int(d[r, c])
-            assert got == want or (want in (0, 0x8000) and got in (0, 0x8000) and name not in ("w6", "fp4")), (r, c)
+            assert got == want or (want in (0, 0x8000) and got in (0, 0x8000) and name not in ("w6", "fp4", "fp5")), (r, c)
     # exact in fp32 too: an fp32 product rounded once by torch gives the same bits
     s32 = oracle.fp16_from_bits(sv).astype(np.float32)
     if name == "w8":
@@ -340,6 +410,8 @@ def test_dequant_bf16_exact_vs_fraction_and_fp32(name):
         v32 = (codes.astype(np.float32) - np.repeat(zz, 32, axis=1)) * np.repeat(s32, 32, axis=1)
     elif name == "w6":
         v32 = oracle.e3m2_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
+    elif name == "fp5":
+        v32 = oracle.e2m2_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
     else:
         v32 = oracle.e2m1_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
     t = torch.from_numpy(np.ascontiguousarray(v32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
