@@ -25,6 +25,11 @@
  *                  no inf/NaN, max 6), one fp16 scale per row: s = fp16(max|w|/6), code =
  *                  nearest e2m1 to w/s (ties to even code, saturating); w^ = e2m1(code)*s.
  *                  A further bit width through the same kernels; the pages name none.
+ *   WQ_FMT_W5E2M2  FP5 e2m2 (sign, 2 exponent bits with bias 1, 2 mantissa bits, subnormals,
+ *                  no inf/NaN, max 7), one fp16 scale per row: s = fp16(max|w|/7), code =
+ *                  nearest e2m2 to w/s (ties to even code, saturating); w^ = e2m2(code)*s.
+ *                  Another further bit width (the FP6-LLM news page, section "重新设计内核方案",
+ *                  describes one kernel design for several bit widths and names none besides 6).
  *   WQ_FMT_F16     plain fp16 weights W[N,K] (the unquantized baseline); no metadata.
  *   WQ_FMT_BF16    plain bfloat16 weights W[N,K], the unquantized baseline for bfloat16
  *                  activations (WQ_ACT_BF16 below); no metadata.
@@ -42,9 +47,13 @@
  *       come first, unit after unit, then bytes 16..23 of the same units.
  *   FP4 16 B: code j in bits 4j..4j+3 of the unit read as a little-endian number (byte p:
  *       code 2p in the low nibble, code 2p+1 in the high nibble).
+ *   FP5 20 B: bytes 0..15 hold the low four bits of the codes placed as W4 codes; bytes 16..19
+ *       a little-endian u32 of signs, the sign of code 2p in bit p and of code 2p+1 in bit
+ *       16+p. Stored split by planes in chunks of 64 units as W6 (bytes 0..15 of the chunk's
+ *       units, then bytes 16..19 of the same units).
  *   F16 64 B: fp16 weight j at bytes 2j..2j+1 (so F16 is the plain row-major matrix); BF16 the same
  *       with bfloat16 bits.
- * So packed_w is exactly N*K*bits/8 bytes. scales: W8/W6/FP4 [N]; W4 [N][K/32] row-major.
+ * So packed_w is exactly N*K*bits/8 bytes. scales: W8/W6/FP4/FP5 [N]; W4 [N][K/32] row-major.
  * zeros: W4 [N][K/32] row-major; otherwise unused (may be NULL). fp16 values are passed
  * as uint16_t bit patterns.
  *
@@ -53,7 +62,7 @@
  * bfloat16 (named besides fp16 by the gpt-fast guide, www.jsqmd.com, section "混合精度训练与推理",
  * and the speed-up strategies page, sharktoolz.top, section 4). The packed weights and their fp16 metadata are the same for both;
  * the product still accumulates in fp32, and the dequantized value of a weight is its exact
- * value rounded once to bfloat16. Valid codes with the flag: W8, W4G32, W6E3M2, W4E2M1 and BF16;
+ * value rounded once to bfloat16. Valid codes with the flag: W8, W4G32, W6E3M2, W4E2M1, W5E2M2, BF16;
  * F16 weights take fp16 activations only and BF16 weights bfloat16 ones (else WQ_ERR_FMT).
  * The size calls ignore the flag.
  *
@@ -76,7 +85,10 @@
 extern "C" {
 #endif
 
-typedef enum { WQ_FMT_F16 = 0, WQ_FMT_W8 = 1, WQ_FMT_W4G32 = 2, WQ_FMT_W6E3M2 = 3, WQ_FMT_W4E2M1 = 4, WQ_FMT_BF16 = 5 } wq_fmt;
+typedef enum {
+  WQ_FMT_F16 = 0, WQ_FMT_W8 = 1, WQ_FMT_W4G32 = 2, WQ_FMT_W6E3M2 = 3, WQ_FMT_W4E2M1 = 4, WQ_FMT_BF16 = 5,
+  WQ_FMT_W5E2M2 = 6
+} wq_fmt;
 
 /* Activation-type flag, OR-ed into a format code: bfloat16 x and y instead of fp16. */
 typedef enum { WQ_ACT_F16 = 0, WQ_ACT_BF16 = 0x100 } wq_act;
@@ -114,9 +126,10 @@ int wq_pack_int8(const float* w, int64_t N, int64_t K, void* packed, uint16_t* s
 int wq_pack_int4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales, uint16_t* zeros);
 int wq_pack_fp6(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
 int wq_pack_fp4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
+int wq_pack_fp5(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
 
 /* Inverse of the packers' layout step, on the host: packed -> logical codes [N,K]
- * (int8 for W8; 0..15 for W4 and FP4; 0..63 for W6, one byte each; uint16 fp16 bits for F16) and
+ * (int8 for W8; 0..15 for W4 and FP4; 0..63 for W6; 0..31 for FP5, one byte each; uint16 fp16 bits for F16) and
  * a copy of the metadata in logical order (scales_out/zeros_out may be NULL to skip).
  * BF16: uint16 bfloat16 bits. A test hook. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT. */
 int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,

@@ -36,7 +36,8 @@ def test_version_and_status_strings():
         assert wq.wq_status_string(s) and wq.wq_status_string(s) != "unknown status"
 
 
-@pytest.mark.parametrize("fmt", [wq.FMT_F16, wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_BF16])
+@pytest.mark.parametrize("fmt", [wq.FMT_F16, wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_BF16,
+                                 wq.FMT_W5E2M2])
 @pytest.mark.parametrize("n,k", [(1, 32), (7, 64), (33, 96), (4096, 11008)])
 def test_sizes_match_oracle(fmt, n, k):
     assert wq.wq_packed_bytes(fmt, n, k) == oracle.packed_bytes(fmt, n, k)
@@ -50,7 +51,7 @@ def test_sizes_match_oracle(fmt, n, k):
 
 def test_sizes_reject_bad_shapes():
     assert wq.wq_packed_bytes(wq.FMT_W8 | 0x200, 4, 64) == 0
-    for fmt in range(6):
+    for fmt in range(7):
         assert wq.wq_packed_bytes(fmt, 4, 48) == 0
         assert wq.wq_packed_bytes(fmt, 0, 64) == 0
         assert wq.wq_packed_bytes(fmt, 4, 0) == 0
@@ -87,14 +88,20 @@ def _exact_ties(fmt):
         r = np.zeros(64, dtype=np.float32); r[0] = 6.0
         r[1:14] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -1.75, -5.0, -0.0, 0.2499, 5.0001]
         rows.append(r)
+    if fmt == wq.FMT_W5E2M2:
+        # s = 1: midpoints between neighbouring e2m2 values, both signs, and past-max values
+        r = np.zeros(64, dtype=np.float32); r[0] = 7.0
+        r[1:17] = [0.125, 0.375, 0.625, 1.125, 1.875, 2.25, 3.75, 4.5, 6.5, -0.125, -1.375, -6.5, -0.0, 0.1249, 6.5001,
+                   -7.25]
+        rows.append(r)
     if fmt == wq.FMT_W4G32:
         r = np.zeros(64, dtype=np.float32); r[0] = -7.5; r[1] = 7.5; r[2:6] = [0.5, 1.5, -0.5, 2.5]   # s = 1, z = 8 (7.5 -> even)
         rows.append(r)
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1])
-@pytest.mark.parametrize("n,k,seed", [(8, 64, 0), (9, 96, 1), (33, 128, 2), (300, 4096, 3)])
+@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_W5E2M2])
+@pytest.mark.parametrize("n,k,seed", [(8, 64, 0), (9, 96, 1), (33, 128, 2), (300, 4096, 3), (5, 32 * 130, 4)])
 def test_pack_bit_identical_to_oracle(fmt, n, k, seed):
     w = _adversarial(n, k, seed)
     packed_o, s_o, z_o, codes_o = oracle.quantize_and_pack(fmt, w)
@@ -105,6 +112,9 @@ def test_pack_bit_identical_to_oracle(fmt, n, k, seed):
         packed, s, z = wq.wq_pack_int4(w)
     elif fmt == wq.FMT_W6E3M2:
         packed, s = wq.wq_pack_fp6(w)
+        z = None
+    elif fmt == wq.FMT_W5E2M2:
+        packed, s = wq.wq_pack_fp5(w)
         z = None
     else:
         packed, s = wq.wq_pack_fp4(w)
@@ -118,12 +128,12 @@ def test_pack_bit_identical_to_oracle(fmt, n, k, seed):
     assert np.array_equal(s2, s)
 
 
-@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1])
+@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_W5E2M2])
 def test_pack_exact_ties_identical_to_oracle(fmt):
     w = _exact_ties(fmt)
     packed_o, s_o, z_o, _ = oracle.quantize_and_pack(fmt, w)
     fn = {wq.FMT_W8: wq.wq_pack_int8, wq.FMT_W4G32: wq.wq_pack_int4, wq.FMT_W6E3M2: wq.wq_pack_fp6,
-          wq.FMT_W4E2M1: wq.wq_pack_fp4}[fmt]
+          wq.FMT_W4E2M1: wq.wq_pack_fp4, wq.FMT_W5E2M2: wq.wq_pack_fp5}[fmt]
     out = fn(w)
     assert np.array_equal(out[0], packed_o)
     assert np.array_equal(out[1], s_o.reshape(-1))
@@ -153,6 +163,7 @@ def test_unpack_f16_and_round_trip_of_oracle_packing():
                        (wq.FMT_W4G32, rng.integers(0, 16, (3, 96)).astype(np.uint8)),
                        (wq.FMT_W6E3M2, rng.integers(0, 64, (3, 96)).astype(np.uint8)),
                        (wq.FMT_W4E2M1, rng.integers(0, 16, (3, 96)).astype(np.uint8)),
+                       (wq.FMT_W5E2M2, rng.integers(0, 32, (3, 96)).astype(np.uint8)),
                        (wq.FMT_F16, rng.integers(0, 65536, (3, 96)).astype(np.uint16))):
         packed = oracle.pack_scalar(fmt, codes)
         got, _, _ = wq.wq_unpack(fmt, packed, np.zeros(9, np.uint16), np.zeros(9, np.uint16), 3, 96)
@@ -201,6 +212,15 @@ def test_pack_errors():
         wq.wq_pack_int8(big)      # 1e7/127 > 65504
     assert e.value.status == -7
     assert L.wq_unpack(7, p(buf), p(sc), p(sc), 2, 64, p(buf), None, None) == -3
+    assert L.wq_pack_fp5(None, 2, 64, p(buf), p(sc)) == -1
+    assert L.wq_pack_fp5(p(w), 2, 40, p(buf), p(sc)) == -2
+    bad[1, 5] = -np.inf
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_pack_fp5(bad)
+    assert e.value.status == -4
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_pack_fp5(np.full((1, 32), 1e6, dtype=np.float32))      # 1e6/7 > 65504
+    assert e.value.status == -7
 
 
 def test_device_entry_points_reject_bad_arguments_before_launch():

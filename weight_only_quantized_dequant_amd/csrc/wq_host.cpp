@@ -11,6 +11,7 @@
 //                        q = clamp(rint(w/s) + z, 0, 15), lo/hi widened to include 0
 //   fp6   per row:       s = fp16(max|w| / 28),       code = e3m2 nearest to w/s
 //   fp4   per row:       s = fp16(max|w| / 6),        code = e2m1 nearest to w/s
+//   fp5   per row:       s = fp16(max|w| / 7),        code = e2m2 nearest to w/s
 // Every quotient is one IEEE float64 operation; every rounding is to nearest even.
 
 #include "wq_internal.h"
@@ -93,6 +94,23 @@ uint8_t e2m1_encode(double t) {
   return sign | static_cast<uint8_t>(code);
 }
 
+// e2m2 code of a finite float64 t, by the same rules (sign kept, ties to the even code,
+// saturating at 7). Below 1 the values are multiples of 1/4 (codes 0..4, code 4 being 1); from
+// 1 up, exponent E in [0, 2] and two mantissa bits.
+uint8_t e2m2_encode(double t) {
+  const uint8_t sign = std::signbit(t) ? 0x10 : 0;
+  const double a = std::fabs(t);
+  if (a >= 7.0) return sign | 15;
+  if (a < 1.0) return sign | static_cast<uint8_t>(std::nearbyint(a * 4.0));   // exact product; 0..4
+  int e2 = 0;
+  (void)std::frexp(a, &e2);
+  const int E = e2 - 1;                                                 // 0 .. 2
+  const double m = std::nearbyint((std::ldexp(a, -E) - 1.0) * 4.0);     // 0..4, ties to even
+  int code = 4 * (E + 1) + static_cast<int>(m);                         // m == 4 carries into the next binade
+  if (code > 15) code = 15;
+  return sign | static_cast<uint8_t>(code);
+}
+
 namespace {
 
 bool shape_ok(int64_t N, int64_t K) { return N >= 1 && K >= 32 && K % 32 == 0; }
@@ -105,6 +123,7 @@ int fmt_bits(int fmt) {
     case WQ_FMT_W6E3M2: return 6;
     case WQ_FMT_W4E2M1: return 4;
     case WQ_FMT_BF16: return 16;
+    case WQ_FMT_W5E2M2: return 5;
     default: return 0;
   }
 }
@@ -169,6 +188,23 @@ void w6_unit_homes(P base, int64_t r, int64_t u, int64_t U, P& lo, P& hi) {
   P chunk = base + (r * U + 64 * c) * 24;
   lo = chunk + 16 * j;
   hi = chunk + 16 * uc + 8 * j;
+}
+
+// FP5: the same chunks of 64 units; 16 bytes of magnitude nibbles per unit, then 4 bytes of signs.
+template <class P>
+void w5_unit_homes(P base, int64_t r, int64_t u, int64_t U, P& lo, P& hi) {
+  const int64_t c = u / 64, j = u % 64, uc = std::min<int64_t>(64, U - 64 * c);
+  P chunk = base + (r * U + 64 * c) * 20;
+  lo = chunk + 16 * j;
+  hi = chunk + 16 * uc + 4 * j;
+}
+
+// The sign word of an FP5 unit: the sign of code 2p in bit p, of code 2p+1 in bit 16+p.
+uint32_t w5_sign_word(const uint8_t* c) {
+  uint32_t s = 0;
+  for (int p = 0; p < 16; ++p) s |= static_cast<uint32_t>((c[2 * p] >> 4) & 1) << p |
+                                   static_cast<uint32_t>((c[2 * p + 1] >> 4) & 1) << (16 + p);
+  return s;
 }
 
 int check_weights(const float* w, int64_t K, int64_t r) {
@@ -338,6 +374,36 @@ int wq_pack_fp4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* sc
   });
 }
 
+int wq_pack_fp5(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales) {
+  if (!w || !packed || !scales || N < 0 || K < 0) return WQ_ERR_ARG;
+  if (!shape_ok(N, K)) return WQ_ERR_SHAPE;
+  uint8_t* out = static_cast<uint8_t*>(packed);
+  const int64_t U = K / 32;
+  return parallel_rows(N, K, [&](int64_t r0, int64_t r1) {
+    std::vector<uint8_t> c(K);
+    for (int64_t r = r0; r < r1; ++r) {
+      if (check_weights(w, K, r)) return static_cast<int>(WQ_ERR_NONFINITE);
+      const float* row = w + r * K;
+      float amax = 0.0f;
+      for (int64_t k = 0; k < K; ++k) amax = std::max(amax, std::fabs(row[k]));
+      const uint16_t sb = f64_to_f16_bits(static_cast<double>(amax) / 7.0);
+      if ((sb & 0x7FFF) == 0x7C00) return static_cast<int>(WQ_ERR_RANGE);
+      const double s = f16_bits_to_f64(sb);
+      scales[r] = sb;
+      for (int64_t k = 0; k < K; ++k) c[k] = s > 0 ? e2m2_encode(static_cast<double>(row[k]) / s) : 0;
+      for (int64_t u = 0; u < U; ++u) {
+        uint8_t* lo;
+        uint8_t* hi;
+        w5_unit_homes(out, r, u, U, lo, hi);
+        put_unit_w4(lo, c.data() + 32 * u);   // the low four bits, placed as W4 codes
+        const uint32_t sw = w5_sign_word(c.data() + 32 * u);
+        for (int b = 0; b < 4; ++b) hi[b] = static_cast<uint8_t>(sw >> (8 * b));
+      }
+    }
+    return static_cast<int>(WQ_OK);
+  });
+}
+
 int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,
               void* codes, uint16_t* scales_out, uint16_t* zeros_out) {
   if (!fmt_bits(fmt)) return WQ_ERR_FMT;
@@ -385,6 +451,28 @@ int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_
       o[2 * i] = in[i] & 15;
       o[2 * i + 1] = in[i] >> 4;
     }
+  } else if (fmt == WQ_FMT_W5E2M2) {
+    uint8_t* o = static_cast<uint8_t*>(codes);
+    for (int64_t r = 0; r < N; ++r)
+      for (int64_t u = 0; u < U; ++u) {
+        const uint8_t* lo;
+        const uint8_t* hi;
+        w5_unit_homes(in, r, u, U, lo, hi);
+        uint8_t* cu = o + r * K + 32 * u;
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t word = lo[4 * d] | (lo[4 * d + 1] << 8) | (lo[4 * d + 2] << 16) |
+                                (static_cast<uint32_t>(lo[4 * d + 3]) << 24);
+          for (int t = 0; t < 4; ++t) {
+            cu[8 * d + 2 * t] = (word >> (4 * t)) & 15;
+            cu[8 * d + 2 * t + 1] = (word >> (4 * (t + 4))) & 15;
+          }
+        }
+        const uint32_t sw = hi[0] | (hi[1] << 8) | (hi[2] << 16) | (static_cast<uint32_t>(hi[3]) << 24);
+        for (int p = 0; p < 16; ++p) {
+          cu[2 * p] |= static_cast<uint8_t>(((sw >> p) & 1) << 4);
+          cu[2 * p + 1] |= static_cast<uint8_t>(((sw >> (16 + p)) & 1) << 4);
+        }
+      }
   } else {
     std::memcpy(codes, packed, static_cast<size_t>(N) * K * 2);
   }

@@ -12,6 +12,7 @@ uint16_t f64_to_f16_bits(double v);   // round to nearest even; +-inf past 65504
 double f16_bits_to_f64(uint16_t h);
 uint8_t e3m2_encode(double t);        // finite t -> 6-bit e3m2 code (ties to even, saturating)
 uint8_t e2m1_encode(double t);        // finite t -> 4-bit e2m1 code (ties to even, saturating)
+uint8_t e2m2_encode(double t);        // finite t -> 5-bit e2m2 code (ties to even, saturating)
 
 // The tiled prefill kernel (wq_prefill.hip). pf_takes: whether it runs `count` linears (N[i] x
 // K[i]) of kernel code `code` at M rows of x, in one launch. The launches return a wq_status;

@@ -11,9 +11,9 @@ import os
 
 import numpy as np
 
-FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, FMT_BF16 = 0, 1, 2, 3, 4, 5
+FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, FMT_BF16, FMT_W5E2M2 = 0, 1, 2, 3, 4, 5, 6
 FMT_NAMES = {"f16": FMT_F16, "w8": FMT_W8, "w4g32": FMT_W4G32, "w6e3m2": FMT_W6E3M2, "w4e2m1": FMT_W4E2M1,
-             "bf16": FMT_BF16}
+             "bf16": FMT_BF16, "w5e2m2": FMT_W5E2M2}
 # OR-ed into a format code: bfloat16 activations (x, y and dequantized weights) instead of fp16
 ACT_F16, ACT_BF16 = 0, 0x100
 
@@ -55,6 +55,7 @@ def lib():
         L.wq_pack_int4.argtypes = [_p, _i64, _i64, _p, _p, _p]
         L.wq_pack_fp6.argtypes = [_p, _i64, _i64, _p, _p]
         L.wq_pack_fp4.argtypes = [_p, _i64, _i64, _p, _p]
+        L.wq_pack_fp5.argtypes = [_p, _i64, _i64, _p, _p]
         L.wq_unpack.argtypes = [ctypes.c_int, _p, _p, _p, _i64, _i64, _p, _p, _p]
         L.wq_dequant.argtypes = [ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _p]
         L.wq_linear.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, ctypes.c_int, _p]
@@ -64,7 +65,8 @@ def lib():
         L.wq_linear_kernel_name.argtypes = [ctypes.c_int, _i64, _i64, _i64]
         L.wq_linear_grouped_kernel_name.restype = ctypes.c_char_p
         L.wq_linear_grouped_kernel_name.argtypes = [ctypes.c_int, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.c_int]
-        for name in ("wq_pack_int8", "wq_pack_int4", "wq_pack_fp6", "wq_pack_fp4", "wq_unpack", "wq_dequant", "wq_linear"):
+        for name in ("wq_pack_int8", "wq_pack_int4", "wq_pack_fp6", "wq_pack_fp4", "wq_pack_fp5", "wq_unpack",
+                     "wq_dequant", "wq_linear"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -169,6 +171,15 @@ def wq_pack_fp4(w):
     n, k = w.shape
     packed, scales, _ = _alloc(FMT_W4E2M1, n, k)
     _check(lib().wq_pack_fp4(_host_ptr(w), n, k, _host_ptr(packed), _host_ptr(scales)), "wq_pack_fp4")
+    return packed, scales
+
+
+def wq_pack_fp5(w):
+    """fp32 W [N,K] -> (packed uint8, scales uint16 [N])."""
+    w = _w_host(w)
+    n, k = w.shape
+    packed, scales, _ = _alloc(FMT_W5E2M2, n, k)
+    _check(lib().wq_pack_fp5(_host_ptr(w), n, k, _host_ptr(packed), _host_ptr(scales)), "wq_pack_fp5")
     return packed, scales
 
 
