@@ -44,7 +44,8 @@ from weight_only_quantized_dequant_amd import inputs, wq  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "weight-stream HBM GB/s (% of peak) for W8/W6/W4-A16 linear, M=1..16"
-FMT_OF = {"w8": wq.FMT_W8, "w4g32": wq.FMT_W4G32, "w6e3m2": wq.FMT_W6E3M2, "w4e2m1": wq.FMT_W4E2M1, "f16": wq.FMT_F16}
+FMT_OF = {"w8": wq.FMT_W8, "w4g32": wq.FMT_W4G32, "w6e3m2": wq.FMT_W6E3M2, "w4e2m1": wq.FMT_W4E2M1,
+          "w5e2m2": wq.FMT_W5E2M2, "f16": wq.FMT_F16}
 # the same weights with bfloat16 activations ("_bf16"), and plain bfloat16 weights as their baseline
 FMT_OF.update({k + "_bf16": v | wq.ACT_BF16 for k, v in list(FMT_OF.items()) if k != "f16"})
 FMT_OF["bf16"] = wq.FMT_BF16 | wq.ACT_BF16
@@ -130,6 +131,8 @@ def pack(fmt, w):
         return wq.wq_pack_fp6(w) + (None,)
     if fmt == wq.FMT_W4E2M1:
         return wq.wq_pack_fp4(w) + (None,)
+    if fmt == wq.FMT_W5E2M2:
+        return wq.wq_pack_fp5(w) + (None,)
     return w.astype(np.float16).view(np.uint8).reshape(-1), None, None
 
 
@@ -277,7 +280,7 @@ def cpu_baseline(code, linears_host, seconds):
 
 SWEEPS = {
     # name: (layer shapes, layers, formats, Ms)
-    "llama2_7b": (inputs.LLAMA2_7B_LINEARS, 32, ["f16", "w8", "w4g32", "w6e3m2", "w4e2m1"], [1]),
+    "llama2_7b": (inputs.LLAMA2_7B_LINEARS, 32, ["f16", "w8", "w4g32", "w6e3m2", "w4e2m1", "w5e2m2"], [1]),
     "llama70b_w6": (inputs.LLAMA_70B_LINEARS, 80, ["w6e3m2", "f16"], [1, 2, 4, 8, 16]),
 }
 

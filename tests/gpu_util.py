@@ -53,6 +53,9 @@ def pack_with_library(fmt, w):
     if fmt == wq.FMT_W4E2M1:
         p, s = wq.wq_pack_fp4(w)
         return p, s, None
+    if fmt == wq.FMT_W5E2M2:
+        p, s = wq.wq_pack_fp5(w)
+        return p, s, None
     if fmt == wq.FMT_F16:
         return np.asarray(w, dtype=np.float32).astype(np.float16).view(np.uint8).reshape(-1), None, None
     if fmt == wq.FMT_BF16:

@@ -17,8 +17,9 @@ from tests.gpu_util import DeviceWeights, check_linear, dev, host_bits, oracle_r
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_F16]
-FMT_ID = {wq.FMT_W8: "w8", wq.FMT_W4G32: "w4", wq.FMT_W6E3M2: "w6", wq.FMT_W4E2M1: "fp4", wq.FMT_F16: "f16"}
+FMTS = [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_F16, wq.FMT_W5E2M2]
+FMT_ID = {wq.FMT_W8: "w8", wq.FMT_W4G32: "w4", wq.FMT_W6E3M2: "w6", wq.FMT_W4E2M1: "fp4", wq.FMT_F16: "f16",
+          wq.FMT_W5E2M2: "fp5"}
 
 
 def _weights(n, k, seed, adversarial=True):
@@ -48,7 +49,8 @@ def test_dequant_bit_exact(fmt, n, k):
     assert np.array_equal(got, want), "%d of %d differ" % (int((got != want).sum()), got.size)
 
 
-@pytest.mark.parametrize("fmt,ncodes", [(wq.FMT_W6E3M2, 64), (wq.FMT_W4E2M1, 16)], ids=["w6", "fp4"])
+@pytest.mark.parametrize("fmt,ncodes", [(wq.FMT_W6E3M2, 64), (wq.FMT_W4E2M1, 16), (wq.FMT_W5E2M2, 32)],
+                         ids=["w6", "fp4", "fp5"])
 def test_dequant_all_codes(fmt, ncodes):
     # every code in every position of a unit (codes run 0, 1, ..., shifted by one per row), at
     # scale 1, at a non-power-of-two scale and at a subnormal scale

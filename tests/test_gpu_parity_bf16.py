@@ -22,8 +22,9 @@ from tests.gpu_util import (DeviceWeights, bf16_bits_torch, check_linear, dev, h
 pytestmark = pytest.mark.gpu
 
 BF = wq.ACT_BF16
-FMTS = [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_BF16]
-FMT_ID = {wq.FMT_W8: "w8", wq.FMT_W4G32: "w4", wq.FMT_W6E3M2: "w6", wq.FMT_W4E2M1: "fp4", wq.FMT_BF16: "bf16"}
+FMTS = [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_BF16, wq.FMT_W5E2M2]
+FMT_ID = {wq.FMT_W8: "w8", wq.FMT_W4G32: "w4", wq.FMT_W6E3M2: "w6", wq.FMT_W4E2M1: "fp4", wq.FMT_BF16: "bf16",
+          wq.FMT_W5E2M2: "fp5"}
 
 
 def _weights(n, k, seed, adversarial=True):
@@ -61,7 +62,8 @@ def test_dequant_bf16_bit_exact(fmt, n, k):
     assert np.array_equal(got, want), "%d of %d differ" % (int((got != want).sum()), got.size)
 
 
-@pytest.mark.parametrize("fmt,ncodes", [(wq.FMT_W6E3M2, 64), (wq.FMT_W4E2M1, 16)], ids=["w6", "fp4"])
+@pytest.mark.parametrize("fmt,ncodes", [(wq.FMT_W6E3M2, 64), (wq.FMT_W4E2M1, 16), (wq.FMT_W5E2M2, 32)],
+                         ids=["w6", "fp4", "fp5"])
 def test_dequant_bf16_all_codes(fmt, ncodes):
     torch = torch_cuda()
     rows = ncodes

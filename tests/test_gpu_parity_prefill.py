@@ -19,9 +19,10 @@ pytestmark = pytest.mark.gpu
 
 BF = wq.ACT_BF16
 CODES = [(wq.FMT_F16, 0), (wq.FMT_W8, 0), (wq.FMT_W4G32, 0), (wq.FMT_W6E3M2, 0), (wq.FMT_W4E2M1, 0),
-         (wq.FMT_W8, BF), (wq.FMT_W4G32, BF), (wq.FMT_W6E3M2, BF), (wq.FMT_W4E2M1, BF), (wq.FMT_BF16, BF)]
+         (wq.FMT_W8, BF), (wq.FMT_W4G32, BF), (wq.FMT_W6E3M2, BF), (wq.FMT_W4E2M1, BF), (wq.FMT_BF16, BF),
+         (wq.FMT_W5E2M2, 0), (wq.FMT_W5E2M2, BF)]
 NAMES = {wq.FMT_F16: "f16", wq.FMT_W8: "w8", wq.FMT_W4G32: "w4", wq.FMT_W6E3M2: "w6", wq.FMT_W4E2M1: "fp4",
-         wq.FMT_BF16: "bf16w"}
+         wq.FMT_BF16: "bf16w", wq.FMT_W5E2M2: "fp5"}
 IDS = ["%s%s" % (NAMES[f], "_bf16" if a else "") for f, a in CODES]
 
 
@@ -57,7 +58,10 @@ def test_prefill_shapes(fmt, act, n, k, m):
     w = _weights(n, k, 7 * n + k)
     x = _x(5000 + n + m, k, m, act)
     dw = DeviceWeights(fmt, w, act)
-    assert wq.wq_linear_kernel_name(fmt | act, m, n, k).startswith("pf_kernel")
+    name = wq.wq_linear_kernel_name(fmt | act, m, n, k)
+    # from 193 rows always the tiled kernel; below, the planner may keep a decode kernel (FP5's
+    # smaller weight stream favours its 16-row launches on the shortest K): parity either way
+    assert name.startswith("pf_kernel") or (m < 193 and fmt == wq.FMT_W5E2M2), name
     check_linear(dw.linear(x), x, _ref(fmt, act, w), "fmt %d act %d n %d k %d m %d" % (fmt, act, n, k, m), act=act)
 
 

@@ -71,22 +71,36 @@ template <> struct Raw<WQ_FMT_W8> { uint4 a, b; };
 template <> struct Raw<WQ_FMT_W4G32> { uint4 a; };
 template <> struct Raw<WQ_FMT_W6E3M2> { uint4 a; uint2 b; };
 template <> struct Raw<WQ_FMT_W4E2M1> { uint4 a; };
+template <> struct Raw<WQ_FMT_W5E2M2> { uint4 a; uint32_t b; };   // magnitude nibbles, sign word
 template <> struct Raw<WQ_FMT_F16> { uint4 a, b, c, d; };
 
 template <int FMT> constexpr int unit_bytes() {
-  return wfmt(FMT) == WQ_FMT_W8 ? 32 : wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W4E2M1 ? 16 : wfmt(FMT) == WQ_FMT_W6E3M2 ? 24 : 64;
+  return wfmt(FMT) == WQ_FMT_W8 ? 32 : wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W4E2M1 ? 16
+       : wfmt(FMT) == WQ_FMT_W6E3M2 ? 24 : wfmt(FMT) == WQ_FMT_W5E2M2 ? 20 : 64;
 }
 
 // Formats with one fp16 scale per output row, applied to the finished fp32 sum.
 template <int FMT> constexpr bool row_scaled() {
-  return wfmt(FMT) == WQ_FMT_W8 || wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1;
+  return wfmt(FMT) == WQ_FMT_W8 || wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1 ||
+         wfmt(FMT) == WQ_FMT_W5E2M2;
 }
+
+// The decoders hand FP5 values over as e2m2(code) * 2^-14 (exact fp16 bit placement); the row
+// scale that multiplies the finished sum carries the 2^14 (exact in fp32).
+template <int FMT> constexpr float code_scale() { return wfmt(FMT) == WQ_FMT_W5E2M2 ? 16384.0f : 1.0f; }
 
 // Byte offsets, from the start of row n, of the two plane slices of W6 unit u (U units per row).
 __device__ __forceinline__ void w6_homes(int u, int U, uint32_t& lo, uint32_t& hi) {
   const int c = u >> 6, j = u & 63, uc = min(64, U - 64 * c);
   lo = (uint32_t)(64 * c * 24 + 16 * j);
   hi = (uint32_t)(64 * c * 24 + 16 * uc + 8 * j);
+}
+
+// FP5: the same chunks of 64 units, 16 bytes of magnitude nibbles and then a 4-byte sign word per unit.
+__device__ __forceinline__ void w5_homes(int u, int U, uint32_t& lo, uint32_t& hi) {
+  const int c = u >> 6, j = u & 63, uc = min(64, U - 64 * c);
+  lo = (uint32_t)(64 * c * 20 + 16 * j);
+  hi = (uint32_t)(64 * c * 20 + 16 * uc + 4 * j);
 }
 
 // Unit u of row n (used by the MFMA and dequant kernels, where a lane owns a whole unit).
@@ -104,6 +118,11 @@ __device__ __forceinline__ void load_unit(const uint8_t* __restrict__ w, int n, 
     w6_homes(u, U, lo, hi);
     r.a = *reinterpret_cast<const uint4*>(row + lo);
     r.b = *reinterpret_cast<const uint2*>(row + hi);
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W5E2M2) {
+    uint32_t lo, hi;
+    w5_homes(u, U, lo, hi);
+    r.a = *reinterpret_cast<const uint4*>(row + lo);
+    r.b = *reinterpret_cast<const uint32_t*>(row + hi);
   } else {
     const uint4* q = reinterpret_cast<const uint4*>(row + (size_t)u * UB);
     r.a = q[0]; r.b = q[1]; r.c = q[2]; r.d = q[3];
@@ -127,6 +146,22 @@ __device__ __forceinline__ void decode_w4_word(uint32_t d, h2 zc1, h2 zc2, h2& o
   o1 = __builtin_elementwise_fma(as_h2((d & 0x00F000F0u) | 0x64006400u), sixteenth, zc2);   // 1024+16q
   o2 = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + zc1;
   o3 = __builtin_elementwise_fma(as_h2((d8 & 0x00F000F0u) | 0x64006400u), sixteenth, zc2);
+}
+
+// FP5 e2m2: the pair of codes 2p, 2p+1 (p = 4d + t: nibbles t and t+4 of magnitude word d, sign
+// bits p and 16+p of the sign word) as fp16 bits s.ee.mm at 15 and 11..8, i.e. e2m2(code) * 2^-14
+// exactly (fp16's exponent bias 15 is e2m2's bias 1 + 14; the subnormal codes land on fp16
+// subnormals). A shift and an AND for the magnitudes, a shift and an AND for the signs, an OR.
+__device__ __forceinline__ void decode_fp5(const uint4& mag, uint32_t sgn, h2 (&out)[16]) {
+  const uint32_t w[4] = {mag.x, mag.y, mag.z, mag.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int p = 4 * d + t;
+      const uint32_t m = (t < 2 ? w[d] << (8 - 4 * t) : w[d] >> (4 * t - 8)) & 0x0F000F00u;
+      out[p] = as_h2(m | ((sgn << (15 - p)) & 0x80008000u));
+    }
 }
 
 // Byte b of d holds codes 2b (low nibble) and 2b+1 (high nibble); the convert takes the
@@ -158,6 +193,8 @@ __device__ __forceinline__ void decode(const Raw<wfmt(FMT)>& r, h2 zc1, h2 zc2, 
     const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) decode_fp4_word(w[i], out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W5E2M2) {
+    decode_fp5(r.a, r.b, out);
   } else {
     const uint32_t w[16] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w,
                             r.c.x, r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w};
@@ -202,6 +239,11 @@ __device__ __forceinline__ void decode_bf16(const Raw<wfmt(FMT)>& r, uint16_t sb
     const u32x16 h = __builtin_bit_cast(u32x16, __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(v, 1.0f));
 #pragma unroll
     for (int p = 0; p < 16; ++p) out[p] = as_h2(h[p]);
+  } else if constexpr (F == WQ_FMT_W5E2M2) {
+    h2 h[16];   // e2m2(code) * 2^-14 as fp16, then as bfloat16 (exact: at most 3 significant bits)
+    decode_fp5(r.a, r.b, h);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) out[p] = pack_bf16((float)h[p][0], (float)h[p][1]);
   } else if constexpr (F == WQ_FMT_W4E2M1) {
     const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
@@ -264,6 +306,9 @@ __device__ __forceinline__ uint4 ld_nt16(const uint8_t* p) {
   const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(t[0], t[1], t[2], t[3]);
 }
+__device__ __forceinline__ uint32_t ld_nt4(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
 __device__ __forceinline__ uint2 ld_nt8(const uint8_t* p) {
   const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
   return make_uint2(t[0], t[1]);
@@ -275,6 +320,6 @@ __device__ __forceinline__ uint2 ld_nt8(const uint8_t* p) {
 #define WQ_KERNEL_CODES(X)                                                                              \
   X(WQ_FMT_F16) X(WQ_FMT_W8) X(WQ_FMT_W4G32) X(WQ_FMT_W6E3M2) X(WQ_FMT_W4E2M1)                          \
   X(WQ_FMT_W8 | WQ_ACT_BF16) X(WQ_FMT_W4G32 | WQ_ACT_BF16) X(WQ_FMT_W6E3M2 | WQ_ACT_BF16)              \
-  X(WQ_FMT_W4E2M1 | WQ_ACT_BF16) X(WQ_FMT_BF16 | WQ_ACT_BF16)
+  X(WQ_FMT_W4E2M1 | WQ_ACT_BF16) X(WQ_FMT_BF16 | WQ_ACT_BF16) X(WQ_FMT_W5E2M2) X(WQ_FMT_W5E2M2 | WQ_ACT_BF16)
 
 #endif  // WQ_DEVICE_H_

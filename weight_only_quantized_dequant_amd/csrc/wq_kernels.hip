@@ -76,6 +76,7 @@ template <int FMT> constexpr int seg_codes() { return wfmt(FMT) == WQ_FMT_W8 ? 1
 
 template <int FMT> struct Seg { uint4 a; };
 template <> struct Seg<WQ_FMT_W6E3M2> { uint4 a; uint2 b; };
+template <> struct Seg<WQ_FMT_W5E2M2> { uint4 a; uint32_t b; };
 
 template <int FMT, int M, int B>
 struct GemvStage {
@@ -114,6 +115,11 @@ __device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16
       w6_homes(sg, S, lo, hi);
       st.w[b].a = ld_nt16(row + lo);
       st.w[b].b = ld_nt8(row + hi);
+    } else if constexpr (wfmt(FMT) == WQ_FMT_W5E2M2) {
+      uint32_t lo, hi;
+      w5_homes(sg, S, lo, hi);
+      st.w[b].a = ld_nt16(row + lo);
+      st.w[b].b = ld_nt4(row + hi);
     } else {
       st.w[b].a = ld_nt16(row + 16u * sg);
     }
@@ -182,6 +188,11 @@ __device__ __forceinline__ void gemv_compute_bf16(const GemvStage<FMT, M, B>& st
       const u32x16 h = __builtin_bit_cast(u32x16, __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(u, 1.0f));
 #pragma unroll
       for (int p = 0; p < 16; ++p) v[p] = as_h2(h[p]);
+    } else if constexpr (F == WQ_FMT_W5E2M2) {
+      h2 h[16];   // e2m2(code) * 2^-14 as fp16, then as bfloat16 (exact)
+      decode_fp5(st.w[b].a, st.w[b].b, h);
+#pragma unroll
+      for (int p = 0; p < 16; ++p) v[p] = pack_bf16((float)h[p][0], (float)h[p][1]);
     } else if constexpr (F == WQ_FMT_W4E2M1) {
       const uint32_t wd[4] = {st.w[b].a.x, st.w[b].a.y, st.w[b].a.z, st.w[b].a.w};
 #pragma unroll
@@ -304,6 +315,8 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
         const uint32_t wd[4] = {st.w[b].a.x, st.w[b].a.y, st.w[b].a.z, st.w[b].a.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) decode_fp4_word(wd[i], v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+      } else if constexpr (wfmt(FMT) == WQ_FMT_W5E2M2) {
+        decode_fp5(st.w[b].a, st.w[b].b, v);
       } else {
         v[0] = as_h2(st.w[b].a.x); v[1] = as_h2(st.w[b].a.y); v[2] = as_h2(st.w[b].a.z); v[3] = as_h2(st.w[b].a.w);
       }
@@ -371,7 +384,7 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const 
         float t = wave_sum_to_lane63(acc[b][m]);
         const int n = row0 + b;
         if (lane == 63 && n < N) {
-          if constexpr (row_scaled<FMT>()) t *= f16_to_f32(scales[n]);
+          if constexpr (row_scaled<FMT>()) t *= f16_to_f32(scales[n]) * code_scale<FMT>();
           y[(size_t)m * N + n] = out16<FMT>(t);
         }
       }
@@ -391,7 +404,7 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const 
     float t = 0.0f;
     for (int i = 0; i < WK; ++i) t += red[sub * WK + i][lane];   // fixed order: deterministic
     if (n < N) {
-      if constexpr (row_scaled<FMT>()) t *= f16_to_f32(scales[n]);
+      if constexpr (row_scaled<FMT>()) t *= f16_to_f32(scales[n]) * code_scale<FMT>();
       y[(size_t)m * N + n] = out16<FMT>(t);
     }
   }
@@ -463,6 +476,13 @@ __device__ __forceinline__ void mfma_load(MfmaStage<FMT, RB>& st, const uint16_t
     const uint32_t nn = (uint32_t)(min(n0 + 16 * r + nl, N - 1) - nb);   // 0..15
     const uint8_t* rowb = w + uniform((size_t)nb * row_bytes);
     static_assert(wfmt(FMT) != WQ_FMT_W6E3M2 && wfmt(FMT) != WQ_FMT_W4E2M1, "W6 and FP4 on the matrix cores take lm_kernel");
+    if constexpr (wfmt(FMT) == WQ_FMT_W5E2M2) {   // the unit's two plane slices
+      uint32_t lo, hi;
+      w5_homes((int)u, U, lo, hi);
+      st.w[r].a = ld_nt16(rowb + nn * row_bytes + lo);
+      st.w[r].b = ld_nt4(rowb + nn * row_bytes + hi);
+      continue;
+    }
     const uint8_t* p = rowb + nn * row_bytes + UB * u;
     st.w[r].a = ld_nt16(p);
     if constexpr (wfmt(FMT) == WQ_FMT_W8 || wfmt(FMT) == WQ_FMT_F16) st.w[r].b = ld_nt16(p + 16);
@@ -551,7 +571,7 @@ __device__ __forceinline__ void mfma_body(const uint16_t* __restrict__ x, const 
     const int n = n0 + 16 * r + nl;
     if (n >= N) return;
     float sc = 1.0f;
-    if constexpr (row_scaled<FMT>()) sc = f16_to_f32(scales[n]);
+    if constexpr (row_scaled<FMT>()) sc = f16_to_f32(scales[n]) * code_scale<FMT>();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * q + i;
@@ -819,7 +839,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
   for (int r = 0; r < RB; ++r) {
     if (r % WK != kw) continue;
     const int n = n0 + 16 * r + nl;
-    const float sc = row_scaled<FMT>() && n < N ? f16_to_f32(scales[n]) : 1.0f;
+    const float sc = row_scaled<FMT>() && n < N ? f16_to_f32(scales[n]) * code_scale<FMT>() : 1.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f4 t = red[(((sub * WK) * RB + r) * MT + mt) * 64 + lane];
@@ -872,7 +892,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
     w4_consts(zeros[gid], zc1, zc2);
     s = f16_to_f32(scales[gid]);
   } else if constexpr (row_scaled<FMT>()) {
-    s = f16_to_f32(scales[n]);
+    s = f16_to_f32(scales[n]) * code_scale<FMT>();
   }
   h2 wv[16];
   decode<FMT>(raw, zc1, zc2, wv);

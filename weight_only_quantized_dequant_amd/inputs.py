@@ -34,6 +34,8 @@ WORKLOADS = {
                                   [1, 4, 8, 16]),
     # the Llama-7B linears again with FP4 e2m1 weights (a further bit width)
     "llama7b_w4e2m1_linears": ("w4e2m1", [(4096, 4096), (11008, 4096), (4096, 11008)], [1, 4, 8, 16]),
+    # and with FP5 e2m2 weights
+    "llama7b_w5e2m2_linears": ("w5e2m2", [(4096, 4096), (11008, 4096), (4096, 11008)], [1, 4, 8, 16]),
     # bfloat16 activations: the Llama-7B W4 and Llama-70B W6 linears (x from the same kind of
     # draws, rounded to bfloat16 by the caller)
     "llama7b_w4g32_bf16_linears": ("w4g32_bf16", [(4096, 4096), (11008, 4096), (4096, 11008)], [1, 4, 8, 16]),
@@ -43,7 +45,7 @@ WORKLOADS = {
 # stream index of each workload, so that every workload draws from its own stream
 WORKLOAD_STREAM = {"w8_single_1024x1024": 0, "llama7b_w4g32_linears": 1, "llama70b_w6e3m2_linears": 2,
                    "llama70b_w6e3m2_tp8_shard": 3, "llama7b_w4e2m1_linears": 4, "llama7b_w4g32_bf16_linears": 5,
-                   "llama70b_w6e3m2_bf16_linears": 6}
+                   "llama70b_w6e3m2_bf16_linears": 6, "llama7b_w5e2m2_linears": 7}
 
 
 def rng_for(stream, linear):
