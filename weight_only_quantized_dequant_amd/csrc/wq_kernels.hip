@@ -628,17 +628,23 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_grouped_kernel(const
 //       row n, which are exactly the groups its fragments need.
 //   W6: the lo slices as 2 rows x 512 B per instruction, the hi slices as 4 rows x 256 B.
 //   FP4: as W4 (16-byte units), with no metadata.
+//   FP5: the 16-byte magnitude slices as W4, and one 4-byte sign word per unit and row.
 // LDS image of one 16-row block (XOR swizzles put the 16 rows of a fragment read in
 // different banks; gfx950 serves a 16-byte read in four groups of 16 lanes, and with the
 // swizzle u ^ r instead of u ^ (r & 7) every fragment read lost 4 cycles to conflicts):
 //   W4, FP4: unit u (0..31) of row r at 512 r + 16 (u ^ (r & 7))                         8 KB
 //   W6: lo slice of unit u at 512 r + 16 (u ^ (r & 7)),
 //       hi slice at 8192 + 256 r + 8 (u ^ (2r & 31))                                       12 KB
+//   FP5: magnitude slice of unit u as W4, sign word at 8192 + 128 r + 4 (u ^ ((r >> 1) & 7))
+//       (a 4-byte read serves 64 lanes over 64 banks: rows 2p and 2p+1 take either half)   10 KB
 // K tile j (0..7) of a stage is 4 units, one per lane quad q: unit 8q + j. Its x fragments
 // sit in a register ring of lm_xring slots and are loaded lm_xring - 1 tiles ahead (W4 keeps
 // the ring at 2 so that its two-block kernel fits 256 VGPRs: two waves per SIMD).
 template <int FMT> constexpr bool lm_w6() { return wfmt(FMT) == WQ_FMT_W6E3M2; }   // two plane slices per unit
-template <int FMT> constexpr int lm_block() { return lm_w6<FMT>() ? 16 * 512 + 16 * 256 : 16 * 512; }
+template <int FMT> constexpr bool lm_w5() { return wfmt(FMT) == WQ_FMT_W5E2M2; }   // 16-byte slice + sign word
+template <int FMT> constexpr int lm_block() {
+  return lm_w6<FMT>() ? 16 * 512 + 16 * 256 : lm_w5<FMT>() ? 16 * 512 + 16 * 128 : 16 * 512;
+}
 template <int FMT> constexpr int lm_loads() { return lm_w6<FMT>() ? 12 : 8; }
 template <int FMT, int MT> constexpr int lm_xring() { return wfmt(FMT) == WQ_FMT_W4G32 || MT > 1 ? 2 : 4; }
 constexpr int LM_MAX_MT = 4;   // 16-row tiles of x per launch (M up to 64 reads the weights once)
@@ -648,6 +654,7 @@ template <int FMT, int RB>
 struct LmStage {
   uint4 v[RB][lm_loads<FMT>()];
   uint4 s[wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1], z[wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1];   // W4: 8 groups' fp16 scales / zeros
+  uint32_t sg[lm_w5<FMT>() ? RB : 1][lm_w5<FMT>() ? 8 : 1];   // FP5: the sign words
 };
 
 // Global loads of stage h (units 32h .. 32h+31 of each row) of RB row blocks.
@@ -661,7 +668,18 @@ __device__ __forceinline__ void lm_load(LmStage<FMT, RB>& st, const uint8_t* __r
   for (int r = 0; r < RB; ++r) {
     const int nb = min(n0 + 16 * r, N - 1);
     const uint8_t* rowb = w + uniform((size_t)nb * row_bytes);
-    if constexpr (!lm_w6<FMT>()) {
+    if constexpr (lm_w5<FMT>()) {
+      const int c = h >> 1, half = h & 1;                  // 64-unit chunk and which half of it
+      const int uc = min(64, U - 64 * c);                   // units in the chunk
+      const uint32_t cbase = 64u * 20 * c;
+      const int j = min(32 * half + (lane & 31), uc - 1);  // past the chunk end: a valid unit, masked later
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {   // lane l -> row 2i + l/32, unit l%32: its 16-byte slice and sign word
+        const uint32_t nn = (uint32_t)(min(n0 + 16 * r + 2 * i + (lane >> 5), N - 1) - nb);
+        st.v[r][i] = ld_nt16(rowb + nn * row_bytes + cbase + 16u * j);
+        st.sg[r][i] = ld_nt4(rowb + nn * row_bytes + cbase + 16u * uc + 4u * j);
+      }
+    } else if constexpr (!lm_w6<FMT>()) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {   // lane l -> row 2i + l/32, unit l%32
         const uint32_t nn = (uint32_t)(min(n0 + 16 * r + 2 * i + (lane >> 5), N - 1) - nb);
@@ -711,6 +729,13 @@ __device__ __forceinline__ void lm_store(const LmStage<FMT, RB>& st, uint8_t* ld
     for (int i = 0; i < 8; ++i) {
       const int rr = 2 * i + (lane >> 5), u = lane & 31;
       *reinterpret_cast<uint4*>(base + 512 * rr + 16 * (u ^ (rr & 7))) = st.v[r][i];
+    }
+    if constexpr (lm_w5<FMT>()) {   // sign word of unit u of row rr at 8192 + 128 rr + 4 (u ^ ((rr >> 1) & 7))
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rr = 2 * i + (lane >> 5), u = lane & 31;
+        *reinterpret_cast<uint32_t*>(base + 8192 + 128 * rr + 4 * (u ^ ((rr >> 1) & 7))) = st.sg[r][i];
+      }
     }
     if constexpr (lm_w6<FMT>()) {
 #pragma unroll
@@ -797,6 +822,8 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
         raw.a = *reinterpret_cast<const uint4*>(base + 512 * nl + 16 * (u ^ (nl & 7)));
         if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2)
           raw.b = *reinterpret_cast<const uint2*>(base + 8192 + 256 * nl + 8 * (u ^ ((2 * nl) & 31)));
+        if constexpr (lm_w5<FMT>())
+          raw.b = *reinterpret_cast<const uint32_t*>(base + 8192 + 128 * nl + 4 * (u ^ ((nl >> 1) & 7)));
         h2 wv[16];
         if constexpr (bf16_act(FMT)) {
           if constexpr (wfmt(FMT) == WQ_FMT_W4G32) decode_bf16<FMT>(raw, half_of(cs[r], j), half_of(cz[r], j), wv);
@@ -1015,13 +1042,13 @@ struct LmPlan {
   int grid;   // workgroups
 };
 
-// The LDS-staged kernel serves W6, FP4 and W4 wherever the matrix cores run for them (W4 only
-// when K is a multiple of 256, so that a lane's 8 groups of metadata are one aligned 16-byte
-// load), and W4 and FP4 at M = 4 from N*K = 2^24 on, where it beats the VALU GEMV.
+// The LDS-staged kernel serves W6 wherever the matrix cores run for it, and W4, FP4 and FP5
+// from M = 5 on and at M = 4 from N*K = 2^24 on, where it beats the VALU GEMV (W4 only when K
+// is a multiple of 256, so that a lane's 8 groups of metadata are one aligned 16-byte load).
 bool use_lm(int fmt, int64_t M, int64_t N, int64_t K) {
   if (fmt == WQ_FMT_W6E3M2) return use_mfma(fmt, M, N);
   if (fmt == WQ_FMT_W4G32 && K % 256) return false;
-  if (fmt != WQ_FMT_W4G32 && fmt != WQ_FMT_W4E2M1) return false;
+  if (fmt != WQ_FMT_W4G32 && fmt != WQ_FMT_W4E2M1 && fmt != WQ_FMT_W5E2M2) return false;
   return M > GEMV_MAX_M || (M == GEMV_MAX_M && N * K >= (int64_t(1) << 24));
 }
 
@@ -1053,7 +1080,8 @@ int lm_tiles(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 // a multiple of 256), else 16. The kernels address x with 32-bit lane offsets (row * 2K + 64 u),
 // which hold 64 rows only while K <= 2^25; longer rows take 16-row slabs.
 int64_t slab_rows(int fmt, int64_t K) {
-  const bool lm = fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W4E2M1 || (fmt == WQ_FMT_W4G32 && K % 256 == 0);
+  const bool lm = fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W4E2M1 || fmt == WQ_FMT_W5E2M2 ||
+                  (fmt == WQ_FMT_W4G32 && K % 256 == 0);
   return lm && K <= (int64_t(1) << 25) ? 16 * LM_MAX_MT : MFMA_M;
 }
 
@@ -1081,7 +1109,8 @@ void lm_launch(dim3 grid, size_t shm, hipStream_t s, const uint16_t* x, const ui
 template <int FMT>
 hipError_t launch_lm(int RB, int M, dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
                      const uint16_t* z, uint16_t* y, int N, int K, int WK, const GemvGroup* g) {
-  if constexpr (wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1) {
+  if constexpr (wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1 ||
+                wfmt(FMT) == WQ_FMT_W5E2M2) {
     const size_t shm = (size_t)LM_WAVES * RB * lm_block<FMT>();
     const int MT = lm_tiles(M);
     if (RB == 2) {

@@ -267,19 +267,18 @@ namespace wq {
 
 // The tiled kernel's time is about its longest chain of K steps (one per 64 K) while its tiles
 // fit the CUs, else its tile-steps over the CUs; the decode kernels cost about one weight
-// stream per 64 rows of x (W4, W6, FP4) or per 16 rows (W8, fp16 and bf16 weights). Which one
+// stream per 64 rows of x (W4, W6, FP4, FP5) or per 16 rows (W8, fp16 and bf16 weights). Which one
 // runs below 193 rows (from 193 always the tiled kernel) was fitted to crossovers measured on
 // the Llama-7B and 70B shapes at M = 20..192:
 //  * W8, fp16/bf16 weights, from 17 rows: the tiled kernel when max(chain, tile-steps / 256)
-//    times 1.58 (W8) or 2.1 (16-bit) us is at most the 16-row launches' weight megabytes (FP5,
-//    whose matrix-core decode kernel also takes 16 rows per launch, uses W8's factor: not fitted);
-//  * W4, W6, FP4, from 65 rows: when the chain is at most 2x (W4, the heaviest decode) or 4x
+//    times 1.58 (W8) or 2.1 (16-bit) us is at most the 16-row launches' weight megabytes;
+//  * W4, W6, FP4, FP5, from 65 rows: when the chain is at most 2x (W4, the heaviest decode) or 4x
 //    the tile count. (Past 64 rows a group that the tiled kernel does not take runs one call
 //    per linear, so the tiles of all its linears count.)
 // So the down projections (K = 11008, 28672; 32 to 128 tiles) keep the decode kernels.
 bool pf_takes(int code, int64_t M, const int64_t* N, const int64_t* K, int count) {
   const int w = wfmt(code);
-  const bool rows16 = w == WQ_FMT_F16 || w == WQ_FMT_W8 || w == WQ_FMT_W5E2M2;
+  const bool rows16 = w == WQ_FMT_F16 || w == WQ_FMT_W8;
   if (M < (rows16 ? 17 : PF_MIN_M_ANY) || M > INT32_MAX) return false;
   int64_t tiles = 0, kmax = 0, tile_steps = 0;
   double mbytes = 0.0;
@@ -287,7 +286,7 @@ bool pf_takes(int code, int64_t M, const int64_t* N, const int64_t* K, int count
     const int64_t t = pf_tiles(M, N[i]);
     tiles += t;
     tile_steps += t * ((K[i] + 63) / 64);
-    mbytes += (double)N[i] * (double)K[i] * (w == WQ_FMT_F16 ? 2.0 : w == WQ_FMT_W5E2M2 ? 0.625 : 1.0) * 1e-6;
+    mbytes += (double)N[i] * (double)K[i] * (w == WQ_FMT_F16 ? 2.0 : 1.0) * 1e-6;
     kmax = K[i] > kmax ? K[i] : kmax;
   }
   if (tiles > INT32_MAX) return false;
@@ -295,7 +294,7 @@ bool pf_takes(int code, int64_t M, const int64_t* N, const int64_t* K, int count
   const int64_t chain = (kmax + 63) / 64;
   if (rows16) {
     const double steps = chain > tile_steps / 256.0 ? (double)chain : tile_steps / 256.0;
-    return steps * (w == WQ_FMT_F16 ? 2.1 : 1.58) <= (double)((M + 15) / 16) * mbytes;   // FP5: W8's fit
+    return steps * (w == WQ_FMT_F16 ? 2.1 : 1.58) <= (double)((M + 15) / 16) * mbytes;
   }
   return chain <= (w == WQ_FMT_W4G32 ? 2 : 4) * tiles;
 }
