@@ -103,12 +103,19 @@ typedef enum {
   WQ_ERR_DEVICE = -6,     /* the HIP runtime refused the launch                      */
   WQ_ERR_RANGE = -7       /* a scale would overflow fp16 (max|w| too large)          */
 } wq_status;
+/* WQ_ERR_DEVICE reflects only the call's own launches: after its argument checks, each
+ * launching entry point reads away (hipGetLastError) any error that an earlier HIP runtime
+ * call on the calling thread left pending, from this library or any other. */
 
 /* Library version, (major << 16) | minor. */
 int wq_version(void);
 
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* wq_status_string(int status);
+
+/* The name of the HIP runtime error (hipGetErrorName) behind the calling thread's most recent
+ * WQ_ERR_DEVICE, or "none" if it has had none. Static storage; never NULL; no device call. */
+const char* wq_last_device_error(void);
 
 /* Sizes in bytes of packed_w, scales and zeros for (fmt, N, K); 0 for an invalid
  * combination (unknown fmt, N < 1, K not a positive multiple of 32) or, for zeros, a

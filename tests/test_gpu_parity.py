@@ -162,6 +162,7 @@ FULL = [
     ("llama70b_w6e3m2_linears", wq.FMT_W6E3M2),
     ("llama70b_w6e3m2_tp8_shard", wq.FMT_W6E3M2),
     ("llama7b_w4e2m1_linears", wq.FMT_W4E2M1),
+    ("llama7b_w5e2m2_linears", wq.FMT_W5E2M2),
 ]
 
 
@@ -250,3 +251,26 @@ def test_grouped_argument_errors():
     assert L.wq_linear_grouped(arr, 17, 1, 1, None) == -1
     assert L.wq_linear_grouped(arr, 0, 1, 1, None) == 0
     assert L.wq_linear_grouped(arr, 1, 1, 9, None) == -3
+
+
+def test_library_loaded_before_torch_in_a_fresh_process():
+    # a process whose first use of the binding is a host packer (which loads libwq.so) and
+    # which imports torch only afterwards must still run its launches on torch's device memory
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import numpy as np\n"
+        "from weight_only_quantized_dequant_amd import wq, inputs\n"
+        "w, x = inputs.small_case(3, 64, 1024, 1)\n"
+        "p, s = wq.wq_pack_int8(w)\n"
+        "import torch\n"
+        "d = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).to('cuda:0')\n"
+        "y = torch.empty((1, 64), dtype=torch.int16, device='cuda:0')\n"
+        "wq.wq_linear(d(x), d(p), d(s), None, y, 1, 64, 1024, wq.FMT_W8, None)\n"
+        "torch.cuda.synchronize()\n"
+        "print('ok', int((y != 0).sum()))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=100)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.split()[0] == "ok" and int(r.stdout.split()[1]) > 0, r.stdout

@@ -59,8 +59,8 @@ def test_prefill_shapes(fmt, act, n, k, m):
     x = _x(5000 + n + m, k, m, act)
     dw = DeviceWeights(fmt, w, act)
     name = wq.wq_linear_kernel_name(fmt | act, m, n, k)
-    # from 193 rows always the tiled kernel; below, the planner may keep a decode kernel (FP5's
-    # smaller weight stream favours its 16-row launches on the shortest K): parity either way
+    # from 193 rows always the tiled kernel; below, the planner may keep a decode kernel (FP5
+    # leaves the decode kernels only from 81 rows, and then not on every shape): parity either way
     assert name.startswith("pf_kernel") or (m < 193 and fmt == wq.FMT_W5E2M2), name
     check_linear(dw.linear(x), x, _ref(fmt, act, w), "fmt %d act %d n %d k %d m %d" % (fmt, act, n, k, m), act=act)
 

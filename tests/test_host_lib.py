@@ -34,6 +34,8 @@ def test_version_and_status_strings():
     assert wq.wq_version() >> 16 == 1
     for s in range(-7, 1):
         assert wq.wq_status_string(s) and wq.wq_status_string(s) != "unknown status"
+    # no launch has failed on this thread (none ran): no device error to name
+    assert wq.wq_last_device_error() == "none"
 
 
 @pytest.mark.parametrize("fmt", [wq.FMT_F16, wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_BF16,

@@ -22,6 +22,10 @@ int pf_launch(int code, const uint16_t* x, const void* packed_w, const uint16_t*
               uint16_t* y, int64_t M, int64_t N, int64_t K, void* stream);
 int pf_launch_grouped(int code, const wq_linear_item* items, int count, int64_t M, void* stream);
 
+// A hipError_t from a launch -> WQ_OK, or WQ_ERR_DEVICE after keeping the error for
+// wq_last_device_error (per thread).
+int device_status(int hip_error);
+
 }  // namespace wq
 
 #endif  // WQ_INTERNAL_H_

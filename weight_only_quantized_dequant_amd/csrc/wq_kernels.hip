@@ -1259,14 +1259,35 @@ hipError_t launch_grouped_mc(Family f, const GemvGroup& g, int M, int RB, int bl
   }
 }
 
+// The HIP runtime keeps the last error of any runtime call on a thread until it is read, also
+// errors that another library in the process (torch's allocator, say) met and ignored. Each
+// entry point reads it away before its first launch, so that the checks after its launches
+// report only what its own launches met.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+thread_local int last_device_error = hipSuccess;
+
 }  // namespace
 
+namespace wq {
+int device_status(int hip_error) {
+  if (hip_error == hipSuccess) return WQ_OK;
+  last_device_error = hip_error;
+  return WQ_ERR_DEVICE;
+}
+}  // namespace wq
+
 extern "C" {
+
+const char* wq_last_device_error(void) {
+  return last_device_error == hipSuccess ? "none" : hipGetErrorName(static_cast<hipError_t>(last_device_error));
+}
 
 int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros, uint16_t* y,
               int64_t M, int64_t N, int64_t K, int fmt, void* stream) {
   const int st = check_linear_args(x, packed_w, scales, zeros, y, M, N, K, fmt);
   if (st != WQ_OK) return st;
+  clear_stale_error();
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* w = static_cast<const uint8_t*>(packed_w);
   if (wq::pf_takes(fmt, M, &N, &K, 1))   // prefill-sized M: one tiled launch for all rows
@@ -1283,7 +1304,7 @@ int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, c
 #undef WQ_CASE
       default: return WQ_ERR_FMT;
     }
-    if (e != hipSuccess) return WQ_ERR_DEVICE;
+    if (e != hipSuccess) return wq::device_status(e);
   }
   return WQ_OK;
 }
@@ -1298,6 +1319,7 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
   if (N * (K / 32) > INT32_MAX) return WQ_ERR_SHAPE;
   if (!aligned16(packed) || !aligned16(w_out) || (scales && !aligned16(scales)) || (zeros && !aligned16(zeros)))
     return WQ_ERR_ALIGN;
+  clear_stale_error();
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* w = static_cast<const uint8_t*>(packed);
   const int64_t units = N * (K / 32);
@@ -1309,7 +1331,7 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
 #undef WQ_CASE
     default: return WQ_ERR_FMT;
   }
-  return hipGetLastError() == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
+  return wq::device_status(hipGetLastError());
 }
 
 int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt, void* stream) {
@@ -1321,6 +1343,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
     const int st = check_linear_args(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt);
     if (st != WQ_OK) return st;
   }
+  clear_stale_error();
   int64_t Ns[MAX_GROUP], Ks[MAX_GROUP];
   for (int i = 0; i < count; ++i) { Ns[i] = items[i].N; Ks[i] = items[i].K; }
   // one family and one rows-per-wave (B or RB) for the whole launch: the largest item's (the
@@ -1382,7 +1405,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
       default: return WQ_ERR_FMT;
     }
   }
-  return e == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
+  return wq::device_status(e);
 }
 
 const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {

@@ -272,14 +272,16 @@ namespace wq {
 // the Llama-7B and 70B shapes at M = 20..192:
 //  * W8, fp16/bf16 weights, from 17 rows: the tiled kernel when max(chain, tile-steps / 256)
 //    times 1.58 (W8) or 2.1 (16-bit) us is at most the 16-row launches' weight megabytes;
-//  * W4, W6, FP4, FP5, from 65 rows: when the chain is at most 2x (W4, the heaviest decode) or 4x
-//    the tile count. (Past 64 rows a group that the tiled kernel does not take runs one call
-//    per linear, so the tiles of all its linears count.)
+//  * W4, W6, FP4, from 65 rows, and FP5 from 81 (its tiled kernel is the slowest of the 4- to
+//    6-bit ones; on the 7B linears it took 154 / 156 / 158 us at 65 / 96 / 128 rows, the
+//    decode kernels' 64-row slabs 130 / 174 / 216 us): when the chain is at most 2x (W4, the
+//    heaviest decode) or 4x the tile count. (Past 64 rows a group that the tiled kernel does
+//    not take runs one call per linear, so the tiles of all its linears count.)
 // So the down projections (K = 11008, 28672; 32 to 128 tiles) keep the decode kernels.
 bool pf_takes(int code, int64_t M, const int64_t* N, const int64_t* K, int count) {
   const int w = wfmt(code);
   const bool rows16 = w == WQ_FMT_F16 || w == WQ_FMT_W8;
-  if (M < (rows16 ? 17 : PF_MIN_M_ANY) || M > INT32_MAX) return false;
+  if (M < (rows16 ? 17 : w == WQ_FMT_W5E2M2 ? PF_MIN_M_ANY + 16 : PF_MIN_M_ANY) || M > INT32_MAX) return false;
   int64_t tiles = 0, kmax = 0, tile_steps = 0;
   double mbytes = 0.0;
   for (int i = 0; i < count; ++i) {
@@ -310,7 +312,7 @@ int pf_launch(int code, const uint16_t* x, const void* packed_w, const uint16_t*
 #undef WQ_CASE
     default: return WQ_ERR_FMT;
   }
-  return e == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
+  return device_status(e);
 }
 
 int pf_launch_grouped(int code, const wq_linear_item* items, int count, int64_t M, void* stream) {
@@ -344,7 +346,7 @@ int pf_launch_grouped(int code, const wq_linear_item* items, int count, int64_t 
 #undef WQ_CASE
     default: return WQ_ERR_FMT;
   }
-  return e == hipSuccess ? WQ_OK : WQ_ERR_DEVICE;
+  return device_status(e);
 }
 
 }  // namespace wq

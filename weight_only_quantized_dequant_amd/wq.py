@@ -34,7 +34,10 @@ class LinearItem(ctypes.Structure):
 class WqError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
-        super().__init__("%s: %s (status %d)" % (where, lib().wq_status_string(status).decode(), status))
+        text = lib().wq_status_string(status).decode()
+        if status == -6:
+            text += " [%s]" % lib().wq_last_device_error().decode()
+        super().__init__("%s: %s (status %d)" % (where, text, status))
 
 
 def lib():
@@ -43,10 +46,21 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libwq.so is not built (%s); run `python -m weight_only_quantized_dequant_amd.build`" % LIB_PATH)
+        # torch ships its own HIP runtime (file libamdhip64.so, soname libamdhip64.so.7). Loaded
+        # first, it also serves libwq.so, whose dependency is that soname; loaded after libwq.so,
+        # torch's copy would come in as a second HIP runtime beside the system one, and the
+        # launches of one would not run on the device state (memory, current device) of the
+        # other. So torch, when present, is loaded before the library.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         L.wq_version.restype = ctypes.c_int
         L.wq_status_string.restype = ctypes.c_char_p
         L.wq_status_string.argtypes = [ctypes.c_int]
+        L.wq_last_device_error.restype = ctypes.c_char_p
+        L.wq_last_device_error.argtypes = []
         for name in ("wq_packed_bytes", "wq_scales_bytes", "wq_zeros_bytes"):
             f = getattr(L, name)
             f.restype = ctypes.c_size_t
@@ -99,6 +113,11 @@ def wq_version():
 
 def wq_status_string(status):
     return lib().wq_status_string(status).decode()
+
+
+def wq_last_device_error():
+    """Name of the HIP error behind this thread's latest WQ_ERR_DEVICE, or "none"."""
+    return lib().wq_last_device_error().decode()
 
 
 def wq_packed_bytes(fmt, n, k):
