@@ -16,9 +16,11 @@ Method:
   that holds R steps (no host gaps), bracketed by synchronize + events on the launch
   stream. The other launch style and each linear alone are timed the same way and
   reported beside it.
-* Warm-up: W untimed steps first (default 10000, about 0.15 s). A step lasts microseconds,
-  and the GPU's clocks need that long under load to settle: with a few dozen warm-up steps
-  the same run varied by +-5%.
+* Warm-up: exactly W untimed steps first (default 10000), then an untimed clock-settle phase
+  of graph replays for at least 200 ms of wall time before every timed region, reported as
+  "clock_settle". A step lasts microseconds, and the GPU's clocks need about a tenth of a
+  second under load to rise: with a few warm-up steps alone the clocks were found at their
+  low level (sclk 1096 MHz) and the same run was 9% slower.
 * Roofline: the step holds only the dominant kernel's launches, back to back, so its
   average launch duration is the timed-region time per step over its launches.
 * fp16 baselines: libwq's own fp16 kernel (grouped and separate) and torch's F.linear
@@ -68,7 +70,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=4000)
     ap.add_argument("--warmup", type=int, default=10000,
-                    help="untimed steps first; steps are microseconds long, and the GPU clocks need ~0.1 s of load to settle")
+                    help="untimed steps before each timed region (a clock-settle phase of >= 200 ms follows them)")
     ap.add_argument("--workload", default="llama7b_w4g32_linears", choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--m", type=int, default=None, help="rows of x (default: the workload's first M)")
     ap.add_argument("--separate", action="store_true",
@@ -81,7 +83,40 @@ def parse():
                          "llama2_7b (32 layers, fp16/W8/W4/W6, M=1) or llama70b_w6 (80 layers, W6, M=1..16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 512 MiB (a known-size kernel for counter calibration)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV", default=None,
+                    help="no GPU work: print the per-kernel means of rocprofv3 --pmc counter_collection.csv files "
+                         "as a markdown table (optionally only kernels containing --kernel-filter)")
+    ap.add_argument("--kernel-filter", default=None)
     return ap.parse_args()
+
+
+def summarize_counters(paths, kfilter=None):
+    """Per kernel name: dispatches, resources (VGPRs, AGPRs, LDS, scratch, grid and workgroup size)
+    and the mean value per dispatch of every counter in rocprofv3 counter-collection CSV files."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    res = {}
+    for path in paths:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                k = row.get("Kernel_Name", "?")
+                if kfilter and kfilter not in k:
+                    continue
+                vals[k][row["Counter_Name"]].append(float(row["Counter_Value"]))
+                res.setdefault(k, {c: row.get(c) for c in ("VGPR_Count", "Accum_VGPR_Count", "SGPR_Count",
+                                                          "LDS_Block_Size", "Scratch_Size", "Grid_Size",
+                                                          "Workgroup_Size")})
+    counters = sorted({c for k in vals for c in vals[k]})
+    print("| kernel | dispatches | VGPR | AGPR | SGPR | LDS B | scratch | grid | wg | " + " | ".join(counters) + " |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|" + "---:|" * len(counters))
+    for k in sorted(vals):
+        n = max(len(v) for v in vals[k].values())
+        r = res[k]
+        cells = ["%.1f" % (sum(vals[k][c]) / len(vals[k][c])) if vals[k].get(c) else "" for c in counters]
+        print("| %s | %d | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            k[:90], n, r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"], r["LDS_Block_Size"],
+            r["Scratch_Size"], r["Grid_Size"], r["Workgroup_Size"], " | ".join(cells)))
 
 
 CSRC = os.path.join(ROOT, "weight_only_quantized_dequant_amd", "csrc")
@@ -174,16 +209,36 @@ def graph_of_steps(torch, run_step, first, count):
     return g
 
 
+SETTLE_MS = 200.0    # untimed load before every timed region, so that the GPU clocks have settled
+SETTLE_LOG = []      # (ms, steps) of each settle phase, reported in the line
+
+
 def time_steps(torch, run_step, steps, warmup, rot, spread=None):
     """Run `steps` steps as replays of graphs of `rot` steps; returns elapsed ms for exactly `steps` steps.
+    Before the timed region: exactly `warmup` untimed steps, then an untimed clock-settle phase of
+    replays until SETTLE_MS of wall time have passed (a step lasts microseconds; the GPU clocks need
+    about a tenth of a second of load to rise, and a few warm-up steps alone left them low).
     With a list as `spread`, an event after every full replay also gives each replay's time per
     step in microseconds (appended to the list); the timed work is the same."""
     full = graph_of_steps(torch, run_step, 0, rot)
     rem = steps % rot
     tail = graph_of_steps(torch, run_step, 0, rem) if rem else None
-    for _ in range(max(1, math.ceil(warmup / rot))):
+    wfull, wrem = divmod(warmup, rot)
+    for _ in range(wfull):
         full.replay()
+    if wrem:
+        graph_of_steps(torch, run_step, 0, wrem).replay()
     torch.cuda.synchronize()
+    t0, settled = time.perf_counter(), 0
+    while 1e3 * (time.perf_counter() - t0) < SETTLE_MS:
+        for _ in range(4):
+            full.replay()
+        settled += 4 * rot
+        torch.cuda.synchronize()
+    for _ in range(2):   # queued ahead of the timed region, so that the GPU does not idle before it
+        full.replay()
+    settled += 2 * rot
+    SETTLE_LOG.append((1e3 * (time.perf_counter() - t0), settled))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     marks = []
     e0.record()
@@ -228,6 +283,32 @@ def gpu_state(torch):
     return state
 
 
+def host_cpu():
+    """Cores this process may run on and the CPU model, as the host reports them."""
+    cores = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return cores, model
+
+
+def blas_on_host_cores():
+    """Limit numpy's BLAS to the cores this process may use (its default may count more), so that
+    the threads the oracle's product runs on are the host cores reported. Returns (context, threads)."""
+    cores, _ = host_cpu()
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=cores, user_api="blas"), cores
+    except Exception:
+        import contextlib
+        return contextlib.nullcontext(), None
+
+
 def cpu_baseline(code, linears_host, seconds):
     """The oracle (test infrastructure) timed on a bounded sample: per linear, a block of rows is
     unpacked, dequantized and multiplied in float64, repeated until `seconds` have passed."""
@@ -235,11 +316,8 @@ def cpu_baseline(code, linears_host, seconds):
     fmt = code & 0xFF
     act = oracle.ACT_BF16 if is_bf16(code) else oracle.ACT_F16
     dequant = oracle.dequant_bf16 if is_bf16(code) else oracle.dequant_fp16
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
+    cores, cpu_model = host_cpu()
+    limit, blas_threads = blas_on_host_cores()
     rows = 256
     work = []
     for (p, s, z, n, k, x) in linears_host:
@@ -250,19 +328,22 @@ def cpu_baseline(code, linears_host, seconds):
         work.append((p[:rows * rb], sl_s, sl_z, rows, k, x, rows * rb + 2 * (0 if s is None else sl_s.size)
                      + 2 * (0 if z is None else sl_z.size)))
     done_bytes, t0, reps = 0, time.perf_counter(), 0
-    while True:
-        for (pp, ss, zz, r, k, x, b) in work:
-            codes = oracle.unpack_vectorized(fmt, pp, r, k)
-            wd = dequant(fmt, codes, ss, zz)
-            oracle.linear_ref(x, wd, act=act)
-            done_bytes += b
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
+    with limit:
+        while True:
+            for (pp, ss, zz, r, k, x, b) in work:
+                codes = oracle.unpack_vectorized(fmt, pp, r, k)
+                wd = dequant(fmt, codes, ss, zz)
+                oracle.linear_ref(x, wd, act=act)
+                done_bytes += b
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
     dt = time.perf_counter() - t0
-    out = {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+    out = {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "cpu_model": cpu_model, "blas_threads": blas_threads,
            "sample": "%d rows of each linear (unpack + dequant + float64 product), %d passes in %.1f s; "
-                     "elementwise steps single-threaded, the product on %d BLAS threads" % (rows, reps, dt, blas_threads)}
+                     "elementwise steps single-threaded, the product on the BLAS threads (%s) over the %d host "
+                     "cores this process may use" % (rows, reps, dt, blas_threads, cores)}
     try:  # the same sample with the product on one thread, for a quarter of the time
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
@@ -279,84 +360,170 @@ def cpu_baseline(code, linears_host, seconds):
 
 
 SWEEPS = {
-    # name: (layer shapes, layers, formats, Ms)
-    "llama2_7b": (inputs.LLAMA2_7B_LINEARS, 32, ["f16", "w8", "w4g32", "w6e3m2", "w4e2m1", "w5e2m2"], [1]),
-    "llama70b_w6": (inputs.LLAMA_70B_LINEARS, 80, ["w6e3m2", "f16"], [1, 2, 4, 8, 16]),
+    # model (inputs.SWEEP_MODELS): formats, Ms, and the headline format
+    "llama2_7b": (["f16", "w8", "w4g32", "w6e3m2", "w4e2m1", "w5e2m2"], [1], "w4g32"),
+    "llama70b_w6": (["w6e3m2", "f16"], [1, 2, 4, 8, 16], "w6e3m2"),
 }
+# the launches of one decode-step layer, in order: q/k/v grouped, o, gate/up grouped, down
+STEP_LAUNCHES = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+
+
+def host_bits16(t):
+    return t.detach().cpu().contiguous().numpy().view(np.uint16)
 
 
 def run_sweep(args, torch):
     """A decode step's linears of a random-init model: per layer q/k/v in one grouped call, o,
     gate/up in one grouped call, down. Every layer has its own weight memory (device copies
-    of one seeded draw per shape: time depends only on shapes and bytes), so the step streams
-    the whole model from HBM. Timed as replays of a graph that holds one step."""
-    shapes, layers, fmts, ms_list = SWEEPS[args.sweep]
+    of one seeded draw per shape: time depends only on shapes and bytes) and its own outputs, so
+    the step streams the whole model from HBM. Timed as replays of a graph that holds one step.
+    Unless --no-cpu, the outputs of the first and the last layer are then checked against the
+    oracle and the oracle is timed on those two layers (sweep_oracle_leg)."""
+    shapes, layers, _ = inputs.SWEEP_MODELS[args.sweep]
+    fmts, ms_list, head_fmt = SWEEPS[args.sweep]
     if args.m is not None:
         ms_list = [args.m]
     name = {"llama2_7b": "llama2_7b_decode_sweep", "llama70b_w6": "llama70b_w6e3m2_decode_sweep"}[args.sweep]
-    distinct = sorted({(n, k) for _, n, k in shapes})
-    draws = {}
-    for i, (n, k) in enumerate(distinct):
-        draws[(n, k)] = inputs.weights_and_x(inputs.rng_for(10 + list(SWEEPS).index(args.sweep), i), n, k, max(ms_list))
     mmax = max(ms_list)
-    xs = {k: torch.from_numpy(draws[next(s for s in distinct if s[1] == k)][1].view(np.int16).copy()).to("cuda")
-          for k in {k for _, k in distinct}}
-    ys = {n: torch.empty((mmax, n), dtype=torch.int16, device="cuda") for n in {n for n, _ in distinct}}
-    results, steps = {}, max(1, args.steps // 100)
+    draws = inputs.sweep_draws(args.sweep, mmax)
+    xs = {k: torch.from_numpy(x.view(np.int16).copy()).to("cuda") for k, x in inputs.sweep_x(draws).items()}
+    results, outs, steps = {}, {}, max(1, args.steps // 100)
+    warm = max(2, args.warmup // 100)
+    dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).to("cuda")
     for fname in fmts:
         fmt = FMT_OF[fname]
         proto = {}
         for (n, k), (w, _) in draws.items():
-            p, sc, z = pack(fmt, w)
-            dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).to("cuda")
-            proto[(n, k)] = (dev(p), dev(sc), dev(z))
-        # one copy of every linear of every layer
-        model = [{nm: tuple(None if t is None else t.clone() for t in proto[(n, k)]) + (n, k) for nm, n, k in shapes}
+            proto[(n, k)] = tuple(dev(a) for a in pack(fmt, w))
+        # one copy of every linear of every layer, each with its own output rows
+        model = [{nm: tuple(None if t is None else t.clone() for t in proto[(n, k)]) +
+                  (n, k, torch.empty((mmax, n), dtype=torch.int16, device="cuda")) for nm, n, k in shapes}
                  for _ in range(layers)]
         del proto
         step_bytes = layers * sum(wq.wq_packed_bytes(fmt, n, k) + metadata_bytes(fmt, n, k) for _, n, k in shapes)
         for m in (ms_list if fname != "f16" else ms_list[:1]):
             def item(lin):
-                p, sc, z, n, k = lin
-                return (xs[k][:m], p, sc, z, ys[n][:m], n, k)
+                p, sc, z, n, k, y = lin
+                return (xs[k][:m], p, sc, z, y[:m], n, k)
 
             def step(_i):
                 for L in model:
-                    wq.wq_linear_grouped([item(L["q"]), item(L["k"]), item(L["v"])], m, fmt)
-                    wq.wq_linear_grouped([item(L["o"])], m, fmt)
-                    wq.wq_linear_grouped([item(L["gate"]), item(L["up"])], m, fmt)
-                    wq.wq_linear_grouped([item(L["down"])], m, fmt)
-            ms_total = time_steps(torch, step, steps, max(2, args.warmup // 100), 1)
+                    for names in STEP_LAUNCHES:
+                        wq.wq_linear_grouped([item(L[nm]) for nm in names], m, fmt)
+            ms_total = time_steps(torch, step, steps, warm, 1)
             t = ms_total / steps
             results["%s_m%d" % (fname, m)] = {"ms_per_step": round(t, 4), "GB/s": round(step_bytes / (t * 1e-3) / 1e9, 1),
                                              "pct_of_peak": round(100 * step_bytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                                              "tok_per_s": round(m / (t * 1e-3), 1), "weight_GB": round(step_bytes / 1e9, 3),
-                                             "launches_per_step": 4 * layers}
+                                             "launches_per_step": len(STEP_LAUNCHES) * layers}
+            torch.cuda.synchronize()
+            outs[(fname, m)] = {li: {nm: host_bits16(model[li][nm][5][:m]) for nm, _, _ in shapes}
+                                for li in (0, layers - 1)}
         del model
         torch.cuda.empty_cache()
     for key, r in results.items():
         f16 = results.get("f16_m" + key.split("_m")[1])
         if f16 and not key.startswith("f16"):
             r["speedup_vs_f16"] = round(f16["ms_per_step"] / r["ms_per_step"], 3)
-    head = "w4g32_m1" if args.sweep == "llama2_7b" else "w6e3m2_m%d" % ms_list[0]
+    head = "%s_m%d" % (head_fmt, ms_list[0])
     h = results[head]
-    out = {"metric": METRIC, "value": h["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": max(2, args.warmup // 100),
+    cpu, check = (None, None) if args.no_cpu else sweep_oracle_leg(args.sweep, draws, outs, head_fmt, ms_list[0])
+    out = {"metric": METRIC, "value": h["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
            "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "f16", "data": "synthetic", "pct_of_peak": h["pct_of_peak"],
-           "config": {"workload": name, "weights": head.split("_m")[0], "M": int(head.split("_m")[1]), "layers": layers,
+           "config": {"workload": name, "weights": head_fmt, "M": ms_list[0], "layers": layers,
                       "linears_per_layer": [nm for nm, _, _ in shapes],
                       "launch": "per layer: grouped q/k/v, o, grouped gate/up, down",
                       "timing": "HIP graph of one decode step's linears, replayed; events on the launch stream"},
            "roofline": {"bound": "hbm", "achieved": h["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(h["GB/s"] / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "decode step (mixed)",
                         "launches_per_step": h["launches_per_step"]},
-           "cpu_baseline": None, "sweep": results}
+           "cpu_baseline": cpu, "oracle_check": check, "sweep": results,
+           "clock_settle": {"ms_min": round(min(t for t, _ in SETTLE_LOG), 1), "timed_regions": len(SETTLE_LOG)}}
     print(json.dumps(out))
-    return 0
+    return 0 if check is None or check["ok"] else 1
+
+
+def sweep_oracle_leg(model, draws, outs, head_fmt, head_m):
+    """The oracle beside a decode sweep (test infrastructure, imported here only).
+
+    Check: for every format and M, the outputs of the first and the last layer on 64 sampled rows
+    of each linear (plus its first and last row) against the oracle's own quantization of those
+    rows of the fp32 draw (dequant, float64 product, closed-form bound and rtol = atol = 1e-2).
+    cpu_baseline: the oracle as it stands (unpack + dequant + float64 product of every row of every
+    linear, from the library's packed bytes) timed on the first and the last layer of the headline
+    format and M; its results are compared with those two layers in full, and the time of a whole
+    step is extrapolated from the two layers (labelled so)."""
+    import oracle
+    shapes, layers, _ = inputs.SWEEP_MODELS[model]
+    xk = inputs.sweep_x(draws)
+    check = {"layers": [0, layers - 1], "rows_per_linear": 66, "ok": True, "worst_err_over_bound": 0.0,
+             "worst_err_over_tol": 0.0, "cases": 0}
+    for (fname, m), per_layer in sorted(outs.items()):
+        fmt = FMT_OF[fname] & 0xFF
+        for li_shape, (nm, n, k) in enumerate(shapes):
+            w, _ = draws[(n, k)]
+            rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng([7, li_shape]).choice(n, 64, replace=False)]))
+            _, s, z, codes = oracle.quantize_and_pack(fmt, w[rows])
+            wd = oracle.dequant_fp16(fmt, codes, s, z)
+            x = xk[k][:m]
+            yref = oracle.linear_ref(x, wd)
+            bound = oracle.error_bound(x, wd, yref)
+            for li, ys in per_layer.items():
+                err = np.abs(oracle.fp16_from_bits(ys[nm][:, rows]) - yref)
+                rb = float((err / bound).max())
+                rt = float((err / (1e-2 + 1e-2 * np.abs(yref))).max())
+                check["worst_err_over_bound"] = max(check["worst_err_over_bound"], rb)
+                check["worst_err_over_tol"] = max(check["worst_err_over_tol"], rt)
+                check["cases"] += 1
+                if not (rb <= 1.0 and rt <= 1.0 and np.all(np.isfinite(err))):
+                    check["ok"] = False
+                    check.setdefault("failed", []).append("%s m%d layer %d %s" % (fname, m, li, nm))
+    # the headline format and M: the oracle on every row of the first and the last layer, timed
+    fmt = FMT_OF[head_fmt] & 0xFF
+    cores, cpu_model = host_cpu()
+    limit, blas_threads = blas_on_host_cores()
+    packs = {(n, k): pack(fmt, draws[(n, k)][0]) for (n, k) in draws}
+    elapsed, wbytes, full_ok, worst = 0.0, 0, True, 0.0
+    block = 2048
+    with limit:
+        for li in (0, layers - 1):
+            ys = outs[(head_fmt, head_m)][li]
+            for nm, n, k in shapes:
+                p, s, z = packs[(n, k)]
+                rb_bytes, g = wq.wq_packed_bytes(fmt, n, k) // n, k // 32
+                x = xk[k][:head_m]
+                for r0 in range(0, n, block):
+                    r1 = min(n, r0 + block)
+                    ss = None if s is None else (s[r0 * g:r1 * g] if fmt == wq.FMT_W4G32 else s[r0:r1])
+                    zz = None if z is None else z[r0 * g:r1 * g]
+                    t0 = time.perf_counter()
+                    codes = oracle.unpack_vectorized(fmt, p[r0 * rb_bytes:r1 * rb_bytes], r1 - r0, k)
+                    wd = oracle.dequant_fp16(fmt, codes, ss, zz)
+                    yref = oracle.linear_ref(x, wd)
+                    elapsed += time.perf_counter() - t0
+                    bound = oracle.error_bound(x, wd, yref)
+                    err = np.abs(oracle.fp16_from_bits(ys[nm][:, r0:r1]) - yref)
+                    worst = max(worst, float((err / bound).max()))
+                    full_ok &= bool(np.all(err <= bound))
+                wbytes += wq.wq_packed_bytes(fmt, n, k) + metadata_bytes(fmt, n, k)
+    check["full_layers"] = {"format": head_fmt, "M": head_m, "ok": full_ok, "worst_err_over_bound": worst}
+    check["ok"] &= full_ok
+    step_s = elapsed * layers / 2
+    cpu = {"value": wbytes / elapsed / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model,
+           "blas_threads": blas_threads,
+           "ms_per_step_extrapolated": round(1e3 * step_s, 1), "tok_per_s_extrapolated": head_m / step_s,
+           "sample": "layers 0 and %d in full (%s, M=%d: unpack + dequant + float64 product of all %d linears, "
+                     "%.1f s); the time of a %d-layer decode step is extrapolated x%d from these two layers"
+                     % (layers - 1, head_fmt, head_m, len(shapes), elapsed, layers, layers // 2)}
+    return cpu, check
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.kernel_filter)
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: libwq runs the linear on a single MI355X "
               "(no collectives); --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -503,6 +670,10 @@ def main():
         q = np.percentile(per_replay, [10, 50, 90])
         out["step_us_spread"] = {"p10": round(float(q[0]), 3), "p50": round(float(q[1]), 3), "p90": round(float(q[2]), 3),
                                  "replays": len(per_replay), "steps_per_replay": rot}
+    out["clock_settle"] = {"ms_min": round(min(t for t, _ in SETTLE_LOG), 1), "timed_regions": len(SETTLE_LOG),
+                           "steps_first_region": SETTLE_LOG[0][1],
+                           "what": "untimed graph replays for >= %d ms of wall time after the warm-up steps, "
+                                   "before every timed region" % SETTLE_MS}
     out["gpu"] = state
     out.update(extras)
     print(json.dumps(out))

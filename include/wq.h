@@ -71,8 +71,9 @@
  *     in an int32. Otherwise WQ_ERR_SHAPE.
  *   - Every error is returned synchronously, before anything is launched. The device
  *     calls never synchronize; a fault in a kernel shows up at the caller's next sync.
- *   - Memory is owned by the caller. The library allocates no device memory, keeps no
- *     state between calls and may be called from several host threads at once.
+ *   - Memory is owned by the caller. The library allocates no device memory and may be called
+ *     from several host threads at once. The only state it keeps between calls is, per host
+ *     thread, the HIP error behind that thread's latest WQ_ERR_DEVICE (wq_last_device_error).
  *   - stream is a hipStream_t (NULL = the legacy default stream).
  */
 #ifndef WQ_H_
@@ -103,9 +104,10 @@ typedef enum {
   WQ_ERR_DEVICE = -6,     /* the HIP runtime refused the launch                      */
   WQ_ERR_RANGE = -7       /* a scale would overflow fp16 (max|w| too large)          */
 } wq_status;
-/* WQ_ERR_DEVICE reflects only the call's own launches: after its argument checks, each
- * launching entry point reads away (hipGetLastError) any error that an earlier HIP runtime
- * call on the calling thread left pending, from this library or any other. */
+/* WQ_ERR_DEVICE reflects only the call's own launches: the status of each launch is the value
+ * that the launch call itself returns (hipLaunchKernel). An error that an earlier HIP runtime
+ * call on the calling thread left pending, from this library or any other, is neither read
+ * nor cleared by this library. */
 
 /* Library version, (major << 16) | minor. */
 int wq_version(void);
@@ -142,7 +144,11 @@ int wq_pack_fp5(const float* w, int64_t N, int64_t K, void* packed, uint16_t* sc
 int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,
               void* codes, uint16_t* scales_out, uint16_t* zeros_out);
 
-/* On the device: dequantize packed weights to fp16 W^[N,K] row-major, w_out[n*K+k] =
+/* On the device: the dequantization step on its own. The FP6-LLM news page (m.zhengruan.com),
+ * section "重新设计内核方案", describes turning the low-bit weights back into fp16 values, which the
+ * fused kernels below do in registers; this call writes them out, as the separate dequant kernel of
+ * the two-kernel approach that page contrasts with does (a test hook, and for callers that want the
+ * dense weights). Dequantize packed weights to fp16 W^[N,K] row-major, w_out[n*K+k] =
  * fp16(w^[n,k]) rounded once to nearest even (bit-exact by construction: each product
  * is exact in fp32); with WQ_ACT_BF16 in fmt, bfloat16 rounded once to nearest even. All
  * pointers are device pointers, 16-byte aligned; zeros only for W4. Asynchronous on
@@ -150,13 +156,21 @@ int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_
 int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16_t* zeros, uint16_t* w_out,
                int64_t N, int64_t K, void* stream);
 
-/* On the device: y[M,N] = x[M,K] . dequant(packed_w)[N,K]^T with fp16 x and y (bfloat16 with
- * WQ_ACT_BF16 in fmt; row-major, row strides K and N) and fp32 accumulation; the one fused kernel reads every packed
- * byte once and never writes dequantized weights to memory. All pointers are device
- * pointers, 16-byte aligned; zeros only for W4 (else may be NULL). M of any size: one launch
- * takes up to 64 rows of x for W6, FP4 and W4 with K a multiple of 256, up to 16 otherwise,
- * and M up to 192 runs as several such launches; from 193 rows on, one tiled launch takes
- * all rows (prefill). y must not overlap the inputs.
+/* On the device: the fused weight-only-quantized linear layer. The FP6-LLM news page
+ * (m.zhengruan.com), section "重新设计内核方案", fuses the dequantization and the matrix product
+ * into one kernel that turns the packed weights into fp16 values on chip and feeds them to the
+ * product; the gpt-fast write-up (m.greenbasetech.com, part on GPU quantization) explains why:
+ * decode is bound by memory bandwidth, so the bytes per weight set its speed.
+ * y[M,N] = x[M,K] . dequant(packed_w)[N,K]^T with fp16 x and y (bfloat16 with WQ_ACT_BF16 in
+ * fmt; row-major, row strides K and N) and fp32 accumulation; the kernel reads every packed byte
+ * once and never writes dequantized weights to memory. All pointers are device pointers, 16-byte
+ * aligned; zeros only for W4 (else may be NULL). y must not overlap the inputs.
+ * M of any size. The decode kernels take up to 64 rows of x per launch for W6, FP4, FP5 and W4
+ * with K a multiple of 256, up to 16 for W8, fp16/bf16 weights and other W4 shapes, and more rows
+ * run as several such launches. The tiled prefill kernel takes all rows in one launch from 193
+ * rows on, and from fewer rows where its chain of K steps is short against its tile count: W8
+ * and fp16/bf16 weights from 17 rows, W4, W6 and FP4 from 65, FP5 from 81.
+ * wq_linear_kernel_name names the kernel that runs for a shape.
  * Asynchronous on stream. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT, WQ_ERR_ALIGN,
  * WQ_ERR_DEVICE. */
 int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros, uint16_t* y,
@@ -172,7 +186,10 @@ typedef struct {
   int64_t N, K;
 } wq_linear_item;
 
-/* On the device: count (0..16) independent linears of one format and one M in a single
+/* On the device: several linears in one launch. The gpt-fast write-up (m.greenbasetech.com,
+ * part on torch.compile) finds decode held back because the CPU cannot issue work fast enough,
+ * and hands the GPU bigger pieces of work at a time; a grouped call is that at the level of one
+ * launch. count (0..16) independent linears of one format and one M in a single
  * launch, each computing exactly what wq_linear computes for it (same decode; the fp32
  * sum may run in another order when the items' sizes differ a lot). One launch
  * instead of count means the GPU ramps up and drains once; in a decode step this fits

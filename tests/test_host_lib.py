@@ -362,3 +362,99 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert wq.wq_linear_kernel_name(0 | bf, 1, 4096, 4096) == ""
     assert wq.wq_linear_kernel_name(5, 1, 4096, 4096) == ""
     assert wq.wq_linear_grouped_kernel_name(2 | bf, 1, [(4096, 4096), (11008, 4096)]) == "gemv_grouped_kernel<258, 1, 4>"
+
+
+def test_kernel_name_thresholds_stated_in_the_header():
+    # include/wq.h: the decode kernels take up to 64 rows of x per launch for W6, FP4, FP5 and W4
+    # with K a multiple of 256 (16 otherwise); the tiled kernel takes all rows from 193 on, and from
+    # 17 (W8, fp16 weights), 65 (W4, W6, FP4) or 81 (FP5) rows where its chain is short enough
+    big = (4096, 4096)                                  # 64 K steps, 32 tiles of 128 weight rows
+    for fmt in (wq.FMT_W8, wq.FMT_F16):
+        assert wq.wq_linear_kernel_name(fmt, 16, *big).startswith("mfma_kernel")
+        assert not wq.wq_linear_kernel_name(fmt, 16, 11008, 4096).startswith("pf_kernel")
+        assert wq.wq_linear_kernel_name(fmt, 40, 11008, 4096) == "pf_kernel<%d>" % fmt
+    for fmt in (wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1):
+        assert wq.wq_linear_kernel_name(fmt, 64, *big) == "lm_kernel<%d, 1, 4>" % fmt
+        assert wq.wq_linear_kernel_name(fmt, 65, *big) == "pf_kernel<%d>" % fmt
+    for fmt in (wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_W5E2M2, wq.FMT_W8, wq.FMT_F16):
+        assert wq.wq_linear_kernel_name(fmt, 193, 4096, 28672) == "pf_kernel<%d>" % fmt
+    for fmt in (wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_W5E2M2):   # 448 K steps, 64 tiles
+        assert wq.wq_linear_kernel_name(fmt, 192, 4096, 28672) == "lm_kernel<%d, 1, 4>" % fmt
+
+
+def test_fp5_kernel_choice():
+    # FP5 e2m2: the VALU GEMV up to M = 3 and at M = 4 below N*K = 2^24, the LDS-staged kernel from
+    # there (1 to 4 tiles of 16 rows), the tiled kernel from 81 rows when its chain is short enough
+    f = wq.FMT_W5E2M2
+    assert wq.wq_linear_kernel_name(f, 1, 4096, 4096) == "gemv_kernel<6, 1, 4>"
+    assert wq.wq_linear_kernel_name(f, 3, 4096, 4096) == "gemv_kernel<6, 3, 4>"
+    assert wq.wq_linear_kernel_name(f, 4, 2048, 4096) == "gemv_kernel<6, 4, 4>"
+    assert wq.wq_linear_kernel_name(f, 4, 4096, 4096) == "lm_kernel<6, 1, 1>"
+    assert wq.wq_linear_kernel_name(f, 5, 2048, 4096) == "lm_kernel<6, 1, 1>"
+    assert wq.wq_linear_kernel_name(f, 5, 8192, 8192) == "lm_kernel<6, 2, 1>"
+    assert wq.wq_linear_kernel_name(f, 17, 4096, 4096) == "lm_kernel<6, 1, 2>"
+    assert wq.wq_linear_kernel_name(f, 64, 4096, 4096) == "lm_kernel<6, 1, 4>"
+    assert wq.wq_linear_kernel_name(f, 65, 4096, 4096) == "lm_kernel<6, 1, 4>"
+    assert wq.wq_linear_kernel_name(f, 80, 4096, 4096) == "lm_kernel<6, 1, 4>"
+    assert wq.wq_linear_kernel_name(f, 81, 4096, 4096) == "pf_kernel<6>"
+    assert wq.wq_linear_kernel_name(f | wq.ACT_BF16, 81, 4096, 4096) == "pf_kernel<262>"
+    assert wq.wq_linear_grouped_kernel_name(f, 8, [(4096, 4096), (11008, 4096)]) == "lm_grouped_kernel<6, 2, 1>"
+    assert wq.wq_linear_grouped_kernel_name(f, 1, [(4096, 4096), (11008, 4096)]) == "gemv_grouped_kernel<6, 1, 4>"
+
+
+class _FakeDeviceTensor:
+    """Looks like a contiguous GPU tensor of `nbytes` bytes to the binding's checks; never launched."""
+
+    is_cuda = True
+
+    def __init__(self, nbytes, contiguous=True):
+        self.nbytes, self.contiguous = nbytes, contiguous
+
+    def get_device(self):
+        return 0
+
+    def is_contiguous(self):
+        return self.contiguous
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+    def data_ptr(self):
+        return 1 << 20
+
+
+def test_binding_rejects_cpu_strided_and_short_buffers_before_any_launch(monkeypatch):
+    import torch
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    m, n, k, fmt = 2, 64, 256, wq.FMT_W4G32
+    good = dict(x=_FakeDeviceTensor(2 * m * k), w=_FakeDeviceTensor(wq.wq_packed_bytes(fmt, n, k)),
+                s=_FakeDeviceTensor(wq.wq_scales_bytes(fmt, n, k)), z=_FakeDeviceTensor(wq.wq_zeros_bytes(fmt, n, k)),
+                y=_FakeDeviceTensor(2 * m * n))
+
+    def call(**over):
+        a = dict(good, **over)
+        wq.wq_linear(a["x"], a["w"], a["s"], a["z"], a["y"], m, n, k, fmt)
+
+    cpu = torch.zeros(4096, dtype=torch.int16)
+    for name in ("x", "w", "s", "z", "y"):
+        with pytest.raises(ValueError, match="GPU tensor"):
+            call(**{name: cpu})
+        with pytest.raises(ValueError, match="bytes"):
+            call(**{name: _FakeDeviceTensor(good[name].nbytes - 1)})
+        with pytest.raises(ValueError, match="contiguous"):
+            call(**{name: _FakeDeviceTensor(good[name].nbytes, contiguous=False)})
+    with pytest.raises(ValueError, match="item 1"):
+        wq.wq_linear_grouped([(good["x"], good["w"], good["s"], good["z"], good["y"], n, k),
+                              (good["x"], good["w"], good["s"], good["z"], _FakeDeviceTensor(2 * m * n - 2), n, k)],
+                             m, fmt)
+    with pytest.raises(ValueError, match="w_out"):
+        wq.wq_dequant(fmt, good["w"], good["s"], good["z"], _FakeDeviceTensor(2 * n * k - 1), n, k)
+    with pytest.raises(ValueError, match="packed"):
+        wq.wq_dequant(fmt, cpu, good["s"], good["z"], _FakeDeviceTensor(2 * n * k), n, k)
+    # the bf16 flag changes no size: a short y is short for either activation type
+    with pytest.raises(ValueError, match="y holds"):
+        wq.wq_linear(good["x"], good["w"], good["s"], good["z"], _FakeDeviceTensor(2 * m * n - 1), m, n, k,
+                     fmt | wq.ACT_BF16)

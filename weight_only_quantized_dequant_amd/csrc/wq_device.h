@@ -7,10 +7,28 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <tuple>
+#include <utility>
 
 #include "wq_internal.h"
 
 namespace {
+
+// Launch kernel k and return the launch's own status. hipLaunchKernel reports what this launch
+// met; the thread's last-error slot, which may hold an error another library left pending, is
+// neither read nor cleared. The arguments are converted to the kernel's parameter types first.
+template <typename... P, size_t... I>
+hipError_t launch_tuple(void (*k)(P...), dim3 grid, dim3 block, size_t shm, hipStream_t s, std::tuple<P...>& t,
+                        std::index_sequence<I...>) {
+  void* args[] = {static_cast<void*>(&std::get<I>(t))..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, shm, s);
+}
+template <typename... P, typename... A>
+hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, size_t shm, hipStream_t s, A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> t(a...);
+  return launch_tuple(k, grid, block, shm, s, t, std::index_sequence_for<P...>{});
+}
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));

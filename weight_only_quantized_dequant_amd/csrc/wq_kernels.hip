@@ -475,14 +475,8 @@ __device__ __forceinline__ void mfma_load(MfmaStage<FMT, RB>& st, const uint16_t
     const int nb = min(n0 + 16 * r, N - 1);                        // wave-uniform
     const uint32_t nn = (uint32_t)(min(n0 + 16 * r + nl, N - 1) - nb);   // 0..15
     const uint8_t* rowb = w + uniform((size_t)nb * row_bytes);
-    static_assert(wfmt(FMT) != WQ_FMT_W6E3M2 && wfmt(FMT) != WQ_FMT_W4E2M1, "W6 and FP4 on the matrix cores take lm_kernel");
-    if constexpr (wfmt(FMT) == WQ_FMT_W5E2M2) {   // the unit's two plane slices
-      uint32_t lo, hi;
-      w5_homes((int)u, U, lo, hi);
-      st.w[r].a = ld_nt16(rowb + nn * row_bytes + lo);
-      st.w[r].b = ld_nt4(rowb + nn * row_bytes + hi);
-      continue;
-    }
+    static_assert(wfmt(FMT) != WQ_FMT_W6E3M2 && wfmt(FMT) != WQ_FMT_W4E2M1 && wfmt(FMT) != WQ_FMT_W5E2M2,
+                  "W6, FP4 and FP5 on the matrix cores take lm_kernel");
     const uint8_t* p = rowb + nn * row_bytes + UB * u;
     st.w[r].a = ld_nt16(p);
     if constexpr (wfmt(FMT) == WQ_FMT_W8 || wfmt(FMT) == WQ_FMT_F16) st.w[r].b = ld_nt16(p + 16);
@@ -1090,20 +1084,19 @@ hipError_t launch_gemv_m(const GemvPlan& p, hipStream_t s, const uint16_t* x, co
                          const uint16_t* z, uint16_t* y, int N, int K) {
   const dim3 grid(p.grid), block(64 * p.WK * p.R);
   switch (p.B) {
-    case 4: hipLaunchKernelGGL((gemv_kernel<FMT, M, 4>), grid, block, 0, s, x, w, sc, z, y, N, K, p.WK); break;
-    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, M, 2>), grid, block, 0, s, x, w, sc, z, y, N, K, p.WK); break;
-    default: hipLaunchKernelGGL((gemv_kernel<FMT, M, 1>), grid, block, 0, s, x, w, sc, z, y, N, K, p.WK); break;
+    case 4: return launch(gemv_kernel<FMT, M, 4>, grid, block, 0, s, x, w, sc, z, y, N, K, p.WK);
+    case 2: return launch(gemv_kernel<FMT, M, 2>, grid, block, 0, s, x, w, sc, z, y, N, K, p.WK);
+    default: return launch(gemv_kernel<FMT, M, 1>, grid, block, 0, s, x, w, sc, z, y, N, K, p.WK);
   }
-  return hipGetLastError();
 }
 
 // The LDS-staged kernel for (RB, MT) as template arguments: one launch, or (GemvGroup) a
 // grouped one.
 template <int FMT, int RB, int MT>
-void lm_launch(dim3 grid, size_t shm, hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
-               const uint16_t* z, uint16_t* y, int M, int N, int K, int WK, const GemvGroup* g) {
-  if (g) hipLaunchKernelGGL((lm_grouped_kernel<FMT, RB, MT>), grid, dim3(64 * LM_WAVES), shm, s, *g, M);
-  else hipLaunchKernelGGL((lm_kernel<FMT, RB, MT>), grid, dim3(64 * LM_WAVES), shm, s, x, w, sc, z, y, M, N, K, WK);
+hipError_t lm_launch(dim3 grid, size_t shm, hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
+                     const uint16_t* z, uint16_t* y, int M, int N, int K, int WK, const GemvGroup* g) {
+  if (g) return launch(lm_grouped_kernel<FMT, RB, MT>, grid, dim3(64 * LM_WAVES), shm, s, *g, M);
+  return launch(lm_kernel<FMT, RB, MT>, grid, dim3(64 * LM_WAVES), shm, s, x, w, sc, z, y, M, N, K, WK);
 }
 
 template <int FMT>
@@ -1114,15 +1107,13 @@ hipError_t launch_lm(int RB, int M, dim3 grid, hipStream_t s, const uint16_t* x,
     const size_t shm = (size_t)LM_WAVES * RB * lm_block<FMT>();
     const int MT = lm_tiles(M);
     if (RB == 2) {
-      if (MT == 1) lm_launch<FMT, 2, 1>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
-      else if (MT == 2) lm_launch<FMT, 2, 2>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
-      else lm_launch<FMT, 2, 4>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
-    } else {
-      if (MT == 1) lm_launch<FMT, 1, 1>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
-      else if (MT == 2) lm_launch<FMT, 1, 2>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
-      else lm_launch<FMT, 1, 4>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
+      if (MT == 1) return lm_launch<FMT, 2, 1>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
+      if (MT == 2) return lm_launch<FMT, 2, 2>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
+      return lm_launch<FMT, 2, 4>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
     }
-    return hipGetLastError();
+    if (MT == 1) return lm_launch<FMT, 1, 1>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
+    if (MT == 2) return lm_launch<FMT, 1, 2>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
+    return lm_launch<FMT, 1, 4>(grid, shm, s, x, w, sc, z, y, M, N, K, WK, g);
   }
   return hipErrorInvalidValue;
 }
@@ -1143,28 +1134,26 @@ hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w,
       default: return launch_gemv_m<FMT, 4>(p, s, x, w, sc, z, y, N, K);
     }
   }
-  if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1) {
-    return hipErrorInvalidValue;   // W6 and FP4 on the matrix cores always take lm_kernel (use_lm)
+  if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1 || wfmt(FMT) == WQ_FMT_W5E2M2) {
+    return hipErrorInvalidValue;   // W6, FP4 and FP5 on the matrix cores always take lm_kernel (use_lm)
   } else {
     const MfmaPlan p = plan_mfma(wfmt(FMT), N, K);
     const dim3 grid(p.grid), block(64 * p.WK);
     switch (p.RB) {
-      case 4: hipLaunchKernelGGL((mfma_kernel<FMT, 4>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
-      case 2: hipLaunchKernelGGL((mfma_kernel<FMT, 2>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
-      default: hipLaunchKernelGGL((mfma_kernel<FMT, 1>), grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK); break;
+      case 4: return launch(mfma_kernel<FMT, 4>, grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK);
+      case 2: return launch(mfma_kernel<FMT, 2>, grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK);
+      default: return launch(mfma_kernel<FMT, 1>, grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK);
     }
-    return hipGetLastError();
   }
 }
 
 template <int FMT, int M>
 hipError_t launch_grouped_m(const GemvGroup& g, int B, int block_waves, int grid, hipStream_t s) {
   switch (B) {
-    case 4: hipLaunchKernelGGL((gemv_grouped_kernel<FMT, M, 4>), dim3(grid), dim3(64 * block_waves), 0, s, g); break;
-    case 2: hipLaunchKernelGGL((gemv_grouped_kernel<FMT, M, 2>), dim3(grid), dim3(64 * block_waves), 0, s, g); break;
-    default: hipLaunchKernelGGL((gemv_grouped_kernel<FMT, M, 1>), dim3(grid), dim3(64 * block_waves), 0, s, g); break;
+    case 4: return launch(gemv_grouped_kernel<FMT, M, 4>, dim3(grid), dim3(64 * block_waves), 0, s, g);
+    case 2: return launch(gemv_grouped_kernel<FMT, M, 2>, dim3(grid), dim3(64 * block_waves), 0, s, g);
+    default: return launch(gemv_grouped_kernel<FMT, M, 1>, dim3(grid), dim3(64 * block_waves), 0, s, g);
   }
-  return hipGetLastError();
 }
 
 template <int FMT>
@@ -1247,23 +1236,16 @@ int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, cons
 template <int FMT>
 hipError_t launch_grouped_mc(Family f, const GemvGroup& g, int M, int RB, int block_waves, int grid, hipStream_t s) {
   if (f == FAM_LM) return launch_lm<FMT>(RB, M, dim3(grid), s, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, &g);
-  if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1) {
-    return hipErrorInvalidValue;   // W6 and FP4 groups on the matrix cores are always FAM_LM
+  if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1 || wfmt(FMT) == WQ_FMT_W5E2M2) {
+    return hipErrorInvalidValue;   // W6, FP4 and FP5 groups on the matrix cores are always FAM_LM
   } else {
     switch (RB) {
-      case 4: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 4>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
-      case 2: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 2>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
-      default: hipLaunchKernelGGL((mfma_grouped_kernel<FMT, 1>), dim3(grid), dim3(64 * block_waves), 0, s, g, M); break;
+      case 4: return launch(mfma_grouped_kernel<FMT, 4>, dim3(grid), dim3(64 * block_waves), 0, s, g, M);
+      case 2: return launch(mfma_grouped_kernel<FMT, 2>, dim3(grid), dim3(64 * block_waves), 0, s, g, M);
+      default: return launch(mfma_grouped_kernel<FMT, 1>, dim3(grid), dim3(64 * block_waves), 0, s, g, M);
     }
-    return hipGetLastError();
   }
 }
-
-// The HIP runtime keeps the last error of any runtime call on a thread until it is read, also
-// errors that another library in the process (torch's allocator, say) met and ignored. Each
-// entry point reads it away before its first launch, so that the checks after its launches
-// report only what its own launches met.
-void clear_stale_error() { (void)hipGetLastError(); }
 
 thread_local int last_device_error = hipSuccess;
 
@@ -1287,7 +1269,6 @@ int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, c
               int64_t M, int64_t N, int64_t K, int fmt, void* stream) {
   const int st = check_linear_args(x, packed_w, scales, zeros, y, M, N, K, fmt);
   if (st != WQ_OK) return st;
-  clear_stale_error();
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* w = static_cast<const uint8_t*>(packed_w);
   if (wq::pf_takes(fmt, M, &N, &K, 1))   // prefill-sized M: one tiled launch for all rows
@@ -1319,19 +1300,19 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
   if (N * (K / 32) > INT32_MAX) return WQ_ERR_SHAPE;
   if (!aligned16(packed) || !aligned16(w_out) || (scales && !aligned16(scales)) || (zeros && !aligned16(zeros)))
     return WQ_ERR_ALIGN;
-  clear_stale_error();
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* w = static_cast<const uint8_t*>(packed);
   const int64_t units = N * (K / 32);
   const dim3 grid(static_cast<unsigned>((units + 255) / 256)), block(256);
+  hipError_t e = hipSuccess;
   switch (fmt) {
 #define WQ_CASE(C) \
-  case C: hipLaunchKernelGGL(dequant_kernel<C>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
+  case C: e = launch(dequant_kernel<C>, grid, block, 0, s, w, scales, zeros, w_out, (int)N, (int)K); break;
     WQ_KERNEL_CODES(WQ_CASE)
 #undef WQ_CASE
     default: return WQ_ERR_FMT;
   }
-  return wq::device_status(hipGetLastError());
+  return wq::device_status(e);
 }
 
 int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt, void* stream) {
@@ -1343,7 +1324,6 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
     const int st = check_linear_args(it.x, it.packed_w, it.scales, it.zeros, it.y, M, it.N, it.K, fmt);
     if (st != WQ_OK) return st;
   }
-  clear_stale_error();
   int64_t Ns[MAX_GROUP], Ks[MAX_GROUP];
   for (int i = 0; i < count; ++i) { Ns[i] = items[i].N; Ks[i] = items[i].K; }
   // one family and one rows-per-wave (B or RB) for the whole launch: the largest item's (the

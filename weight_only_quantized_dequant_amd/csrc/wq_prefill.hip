@@ -3,8 +3,8 @@
 // The FP6-LLM news page (m.zhengruan.com), section "重新设计内核方案", describes the fused
 // kernel: weights re-packed offline, turned into fp16 values on chip and fed to the matrix
 // units in the same kernel. Its batch range (the same page, on FP6-LLM's throughput across
-// batch sizes) and gpt-fast's prefill compile option (the gpt-fast guide on
-// m.greenbasetech.com) are the workloads where M reaches hundreds of rows. There the product
+// batch sizes) and gpt-fast's prefill compile option (the gpt-fast guide, www.jsqmd.com, section
+// 高级优化技巧 -> 编译优化技巧) are the workloads where M reaches hundreds of rows. There the product
 // (2 M N K flops) costs more than the weight stream, so this kernel tiles y and reuses each
 // decoded weight for 128 rows of x.
 //
@@ -249,16 +249,13 @@ int64_t pf_tiles(int64_t M, int64_t N) { return ((M + PF_BM - 1) / PF_BM) * ((N 
 template <int FMT>
 hipError_t launch_pf(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
                      uint16_t* y, int M, int N, int K) {
-  hipLaunchKernelGGL((pf_kernel<FMT>), dim3((unsigned)pf_tiles(M, N)), dim3(256), pf_lds_bytes<FMT>(), s, x, w, sc, z, y,
-                     M, N, K);
-  return hipGetLastError();
+  return launch(pf_kernel<FMT>, dim3((unsigned)pf_tiles(M, N)), dim3(256), pf_lds_bytes<FMT>(), s, x, w, sc, z, y, M, N,
+                K);
 }
 
 template <int FMT>
 hipError_t launch_pf_grouped(hipStream_t s, const PfGroup& g, int M) {
-  hipLaunchKernelGGL((pf_grouped_kernel<FMT>), dim3((unsigned)g.first_tile[g.count]), dim3(256), pf_lds_bytes<FMT>(), s,
-                     g, M);
-  return hipGetLastError();
+  return launch(pf_grouped_kernel<FMT>, dim3((unsigned)g.first_tile[g.count]), dim3(256), pf_lds_bytes<FMT>(), s, g, M);
 }
 
 }  // namespace

@@ -32,6 +32,9 @@ WORKLOADS = {
     # split by output rows (column-parallel), o and down split along K (row-parallel)
     "llama70b_w6e3m2_tp8_shard": ("w6e3m2", [(1280, 8192), (8192, 1024), (3584, 8192), (3584, 8192), (8192, 3584)],
                                   [1, 4, 8, 16]),
+    # the same Llama-7B linears with int8 and FP6 weights (the other two formats of the 7B decode sweep)
+    "llama7b_w8_linears": ("w8", [(4096, 4096), (11008, 4096), (4096, 11008)], [1, 4, 8, 16]),
+    "llama7b_w6e3m2_linears": ("w6e3m2", [(4096, 4096), (11008, 4096), (4096, 11008)], [1, 4, 8, 16]),
     # the Llama-7B linears again with FP4 e2m1 weights (a further bit width)
     "llama7b_w4e2m1_linears": ("w4e2m1", [(4096, 4096), (11008, 4096), (4096, 11008)], [1, 4, 8, 16]),
     # and with FP5 e2m2 weights
@@ -45,7 +48,33 @@ WORKLOADS = {
 # stream index of each workload, so that every workload draws from its own stream
 WORKLOAD_STREAM = {"w8_single_1024x1024": 0, "llama7b_w4g32_linears": 1, "llama70b_w6e3m2_linears": 2,
                    "llama70b_w6e3m2_tp8_shard": 3, "llama7b_w4e2m1_linears": 4, "llama7b_w4g32_bf16_linears": 5,
-                   "llama70b_w6e3m2_bf16_linears": 6, "llama7b_w5e2m2_linears": 7}
+                   "llama70b_w6e3m2_bf16_linears": 6, "llama7b_w5e2m2_linears": 7, "llama7b_w8_linears": 8,
+                   "llama7b_w6e3m2_linears": 9}
+
+
+# Decode sweeps over a whole random-init model: the linears of one layer, the layer count, and
+# the stream its seeded draws come from. Every layer holds a copy of one draw per distinct shape
+# (time depends only on shapes and bytes).
+SWEEP_MODELS = {
+    "llama2_7b": (LLAMA2_7B_LINEARS, 32, 10),
+    "llama70b_w6": (LLAMA_70B_LINEARS, 80, 11),
+}
+
+
+def sweep_draws(model, m):
+    """{(N, K): (W fp32, x fp16 bits [m, K])} for the distinct linear shapes of a sweep model, the
+    i-th shape in sorted order drawn from rng_for(stream, i)."""
+    shapes, _, stream = SWEEP_MODELS[model]
+    distinct = sorted({(n, k) for _, n, k in shapes})
+    return {(n, k): weights_and_x(rng_for(stream, i), n, k, m) for i, (n, k) in enumerate(distinct)}
+
+
+def sweep_x(draws):
+    """The activation rows of each K in a sweep (the x of the first distinct shape with that K)."""
+    out = {}
+    for (n, k) in sorted(draws):
+        out.setdefault(k, draws[(n, k)][1])
+    return out
 
 
 def rng_for(stream, linear):

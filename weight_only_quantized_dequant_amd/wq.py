@@ -218,14 +218,54 @@ def wq_unpack(fmt, packed, scales, zeros, n, k):
 
 
 # ------------------------------------------------------------------ device
+# The C ABI sees raw pointers and can check only their alignment. Before a device call the
+# binding checks every buffer the kernels will touch: a GPU tensor on the current device,
+# contiguous, and at least as many bytes as (fmt, M, N, K) imply. A CPU tensor, a strided view
+# or a short buffer would otherwise become out-of-bounds device accesses.
+def _valid_shape(m, n, k):
+    return m >= 1 and n >= 1 and k >= 32 and k % 32 == 0
+
+
+def _need(t, nbytes, name, where):
+    if t is None:
+        return          # a missing required buffer is the library's WQ_ERR_ARG
+    if not getattr(t, "is_cuda", False):
+        raise ValueError("%s: %s must be a GPU tensor" % (where, name))
+    import torch
+    if t.get_device() != torch.cuda.current_device():
+        raise ValueError("%s: %s is on device %d, not the current device %d" % (where, name, t.get_device(),
+                                                                                  torch.cuda.current_device()))
+    if not t.is_contiguous():
+        raise ValueError("%s: %s must be contiguous" % (where, name))
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError("%s: %s holds %d bytes; the call reads or writes %d" % (where, name, have, nbytes))
+
+
+def _check_linear_buffers(x, packed_w, scales, zeros, y, m, n, k, fmt, where):
+    sized = _valid_shape(m, n, k) and wq_packed_bytes(fmt, n, k) > 0
+    size = (lambda v: v) if sized else (lambda v: 0)
+    _need(x, size(2 * m * k), "x", where)
+    _need(y, size(2 * m * n), "y", where)
+    _need(packed_w, size(wq_packed_bytes(fmt, n, k)), "packed_w", where)
+    _need(scales, size(wq_scales_bytes(fmt, n, k)), "scales", where)
+    _need(zeros, size(wq_zeros_bytes(fmt, n, k)), "zeros", where)
+
+
 def wq_dequant(fmt, packed, scales, zeros, w_out, n, k, stream=None):
     """Device: packed (torch uint8 on the GPU) -> w_out (torch int16/uint16-sized [N,K] on the GPU), async."""
+    sized = _valid_shape(1, n, k) and wq_packed_bytes(fmt, n, k) > 0
+    _need(packed, wq_packed_bytes(fmt, n, k) if sized else 0, "packed", "wq_dequant")
+    _need(scales, wq_scales_bytes(fmt, n, k) if sized else 0, "scales", "wq_dequant")
+    _need(zeros, wq_zeros_bytes(fmt, n, k) if sized else 0, "zeros", "wq_dequant")
+    _need(w_out, 2 * n * k if sized else 0, "w_out", "wq_dequant")
     _check(lib().wq_dequant(fmt, _dev_ptr(packed), _dev_ptr(scales), _dev_ptr(zeros), _dev_ptr(w_out), n, k,
                             _stream_ptr(stream)), "wq_dequant")
 
 
 def wq_linear(x, packed_w, scales, zeros, y, m, n, k, fmt, stream=None):
     """Device: y[M,N] = x[M,K] . dequant(W)[N,K]^T on torch device buffers, async on stream."""
+    _check_linear_buffers(x, packed_w, scales, zeros, y, m, n, k, fmt, "wq_linear")
     _check(lib().wq_linear(_dev_ptr(x), _dev_ptr(packed_w), _dev_ptr(scales), _dev_ptr(zeros), _dev_ptr(y), m, n, k,
                            fmt, _stream_ptr(stream)), "wq_linear")
 
@@ -235,6 +275,7 @@ def wq_linear_grouped(items, m, fmt, stream=None):
     (x, packed_w, scales, zeros, y, n, k) with torch device buffers; async on stream."""
     arr = (LinearItem * max(1, len(items)))()
     for i, (x, pw, sc, z, y, n, k) in enumerate(items):
+        _check_linear_buffers(x, pw, sc, z, y, m, n, k, fmt, "wq_linear_grouped item %d" % i)
         arr[i] = LinearItem(x.data_ptr(), pw.data_ptr(), sc.data_ptr() if sc is not None else None,
                             z.data_ptr() if z is not None else None, y.data_ptr(), n, k)
     _check(lib().wq_linear_grouped(arr, len(items), m, fmt, _stream_ptr(stream)), "wq_linear_grouped")
