@@ -83,6 +83,10 @@ def parse():
                          "llama2_7b (32 layers, fp16/W8/W4/W6, M=1) or llama70b_w6 (80 layers, W6, M=1..16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 512 MiB (a known-size kernel for counter calibration)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="length of the untimed clock-settle phase before each timed region (0 under a counter profiler)")
+    ap.add_argument("--main-only", action="store_true",
+                    help="time only the workload's step (no per-linear and no other-launch-style timings)")
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV", default=None,
                     help="no GPU work: print the per-kernel means of rocprofv3 --pmc counter_collection.csv files "
                          "as a markdown table (optionally only kernels containing --kernel-filter)")
@@ -209,7 +213,7 @@ def graph_of_steps(torch, run_step, first, count):
     return g
 
 
-SETTLE_MS = 200.0    # untimed load before every timed region, so that the GPU clocks have settled
+SETTLE_MS = [200.0]  # untimed load before every timed region, so that the GPU clocks have settled (--settle-ms)
 SETTLE_LOG = []      # (ms, steps) of each settle phase, reported in the line
 
 
@@ -230,7 +234,7 @@ def time_steps(torch, run_step, steps, warmup, rot, spread=None):
         graph_of_steps(torch, run_step, 0, wrem).replay()
     torch.cuda.synchronize()
     t0, settled = time.perf_counter(), 0
-    while 1e3 * (time.perf_counter() - t0) < SETTLE_MS:
+    while 1e3 * (time.perf_counter() - t0) < SETTLE_MS[0]:
         for _ in range(4):
             full.replay()
         settled += 4 * rot
@@ -533,6 +537,7 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 1
     wq.lib()
+    SETTLE_MS[0] = args.settle_ms
     if args.sweep:
         return run_sweep(args, torch)
     if args.copy_calibration:
@@ -603,15 +608,16 @@ def main():
     extras = {}
     # each linear alone (one launch per step, its own graph): per-shape durations and rates
     per_shape = {}
-    for l in lins:
+    for l in ([] if args.main_only else lins):
         ms_l = time_steps(torch, separate_step([l], rot), steps, args.warmup, rot)
         per_shape["%dx%d" % (l.n, l.k)] = {"us": round(1e3 * ms_l / steps, 3),
                                            "GB/s": round(l.weight_bytes * steps / (ms_l * 1e-3) / 1e9, 1)}
     extras["per_linear"] = per_shape
-    other = separate_step(lins, rot) if grouped else grouped_step(lins, rot)
-    ms_other = time_steps(torch, other, steps, args.warmup, rot)
-    extras["separate_calls" if grouped else "grouped_call"] = {
-        "GB/s": round(step_weight_bytes * steps / (ms_other * 1e-3) / 1e9, 1), "ms_per_step": round(ms_other / steps, 5)}
+    if not args.main_only:
+        other = separate_step(lins, rot) if grouped else grouped_step(lins, rot)
+        ms_other = time_steps(torch, other, steps, args.warmup, rot)
+        extras["separate_calls" if grouped else "grouped_call"] = {
+            "GB/s": round(step_weight_bytes * steps / (ms_other * 1e-3) / 1e9, 1), "ms_per_step": round(ms_other / steps, 5)}
 
     if not args.no_baselines:
         f16_bytes = sum(2 * n * k for n, k in shapes)
@@ -673,7 +679,7 @@ def main():
     out["clock_settle"] = {"ms_min": round(min(t for t, _ in SETTLE_LOG), 1), "timed_regions": len(SETTLE_LOG),
                            "steps_first_region": SETTLE_LOG[0][1],
                            "what": "untimed graph replays for >= %d ms of wall time after the warm-up steps, "
-                                   "before every timed region" % SETTLE_MS}
+                                   "before every timed region" % SETTLE_MS[0]}
     out["gpu"] = state
     out.update(extras)
     print(json.dumps(out))

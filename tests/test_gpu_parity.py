@@ -163,6 +163,8 @@ FULL = [
     ("llama70b_w6e3m2_tp8_shard", wq.FMT_W6E3M2),
     ("llama7b_w4e2m1_linears", wq.FMT_W4E2M1),
     ("llama7b_w5e2m2_linears", wq.FMT_W5E2M2),
+    ("llama7b_w8_linears", wq.FMT_W8),
+    ("llama7b_w6e3m2_linears", wq.FMT_W6E3M2),
 ]
 
 

@@ -320,6 +320,27 @@ __device__ __forceinline__ size_t uniform(size_t v) {
   return (static_cast<size_t>(hi) << 32) | lo;
 }
 
+// The W4 decode of the matrix-core kernels with its masks in VGPRs, so that each pair takes one
+// v_and_or_b32 (with literal masks the compiler emits an AND and an OR). The masks are made once,
+// outside the loops. Nibbles 0 and 2 of a byte pair, placed in the mantissa of 1024.0 (step 1),
+// give 1024 + q; nibbles 1 and 3, placed in that of 64.0 (step 1/16, where the nibble weighs 16),
+// give 64 + q; adding zc1 = -(1024 + z) or zc2 = -(64 + z) gives q - z exactly.
+struct W4Masks { uint32_t lo, hi, mag_lo, mag_hi; };
+__device__ __forceinline__ W4Masks w4_masks() {
+  return {in_vgpr(0x000F000Fu), in_vgpr(0x00F000F0u), in_vgpr(0x64006400u), in_vgpr(0x54005400u)};
+}
+__device__ __forceinline__ void decode_w4_unit(const uint4& r, h2 zc1, h2 zc2, const W4Masks& k, h2 (&out)[16]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {   // word i: codes 8i..8i+7, pair t = codes 8i+2t (nibble t), 8i+2t+1 (nibble t+4)
+    const uint32_t d = w[i], e = d >> 8;
+    out[4 * i] = as_h2((d & k.lo) | k.mag_lo) + zc1;
+    out[4 * i + 1] = as_h2((d & k.hi) | k.mag_hi) + zc2;
+    out[4 * i + 2] = as_h2((e & k.lo) | k.mag_lo) + zc1;
+    out[4 * i + 3] = as_h2((e & k.hi) | k.mag_hi) + zc2;
+  }
+}
+
 __device__ __forceinline__ uint4 ld_nt16(const uint8_t* p) {
   const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(t[0], t[1], t[2], t[3]);

@@ -78,11 +78,16 @@ template <int FMT> struct Seg { uint4 a; };
 template <> struct Seg<WQ_FMT_W6E3M2> { uint4 a; uint2 b; };
 template <> struct Seg<WQ_FMT_W5E2M2> { uint4 a; uint32_t b; };
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 template <int FMT, int M, int B>
 struct GemvStage {
   h2 x[M][seg_codes<FMT>() / 2];
   Seg<wfmt(FMT)> w[B];
-  uint16_t s[wfmt(FMT) == WQ_FMT_W4G32 ? B : 1], z[wfmt(FMT) == WQ_FMT_W4G32 ? B : 1];   // W4 group scale / zero
+  // W4: the group's fp16 scale (.x) and zero point (.y) in one register: the zero lands in the
+  // high half straight from its load (a d16_hi load), so a stage in flight holds one register per
+  // row for its metadata
+  u16x2 sz[wfmt(FMT) == WQ_FMT_W4G32 ? B : 1];
 };
 
 // Base pointers are a kernel argument plus a wave-uniform offset (uniform() keeps it in
@@ -123,9 +128,10 @@ __device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16
     } else {
       st.w[b].a = ld_nt16(row + 16u * sg);
     }
-    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
-      st.s[b] = (scales + uniform((size_t)n * S))[sg];
-      st.z[b] = (zeros + uniform((size_t)n * S))[sg];
+    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {   // 32-bit lane offsets from a wave-uniform base
+      const size_t mb = uniform((size_t)n * S * 2);
+      st.sz[b].x = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(scales) + mb + 2u * sg);
+      st.sz[b].y = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(zeros) + mb + 2u * sg);
     }
   }
 }
@@ -165,7 +171,7 @@ __device__ __forceinline__ void gemv_compute_bf16(const GemvStage<FMT, M, B>& st
         v[4 * i + 2] = as_h2(((wd[i] >> 8) & m0) | mag);
         v[4 * i + 3] = as_h2(((wd[i] >> 12) & m0) | mag);
       }
-      const float s = f16_to_f32(st.s[b]), z = f16_to_f32(st.z[b]);
+      const float s = f16_to_f32(st.sz[b].x), z = f16_to_f32(st.sz[b].y);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float t = -(128.0f + z) * sx[m];
@@ -258,7 +264,7 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
         v[4 * i + 2] = as_h2((e & m0) | mag_lo);   // codes 8i+4, 8i+5
         v[4 * i + 3] = as_h2((e & m1) | mag_hi);   // codes 8i+6, 8i+7
       }
-      const float s = f16_to_f32(st.s[b]), z = f16_to_f32(st.z[b]);
+      const float s = f16_to_f32(st.sz[b].x), z = f16_to_f32(st.sz[b].y);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float t = -__builtin_fmaf(z, sx[m], cx[m]);
@@ -714,6 +720,44 @@ __device__ __forceinline__ void lm_load(LmStage<FMT, RB>& st, const uint8_t* __r
   }
 }
 
+// The ragged last stage of a row (nv < 32 valid units): units nv..31 were loaded from clamped
+// addresses and must contribute nothing. W4 zeroes their group scales ((q - z) * 0 = 0); the other
+// formats zero their bytes, whose code 0 is the value +0.
+template <int FMT, int RB>
+__device__ __forceinline__ void lm_zero_past_row(LmStage<FMT, RB>& st, int nv, int lane) {
+  auto keep = [](uint4 v, bool ok) { return ok ? v : make_uint4(0u, 0u, 0u, 0u); };
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+      // lane (n, q) holds the scales of units 8q .. 8q+7 of the stage, two per dword
+      const int v = nv - 8 * (lane >> 4);
+      const uint32_t m[4] = {(v > 0 ? 0xFFFFu : 0u) | (v > 1 ? 0xFFFF0000u : 0u),
+                             (v > 2 ? 0xFFFFu : 0u) | (v > 3 ? 0xFFFF0000u : 0u),
+                             (v > 4 ? 0xFFFFu : 0u) | (v > 5 ? 0xFFFF0000u : 0u),
+                             (v > 6 ? 0xFFFFu : 0u) | (v > 7 ? 0xFFFF0000u : 0u)};
+      st.s[r] = make_uint4(st.s[r].x & m[0], st.s[r].y & m[1], st.s[r].z & m[2], st.s[r].w & m[3]);
+    } else {
+      // lo slices (and FP4 units, FP5 magnitudes): lane l holds unit l % 32 of its rows
+      const bool ok = (lane & 31) < nv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.v[r][i] = keep(st.v[r][i], ok);
+      if constexpr (lm_w5<FMT>()) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.sg[r][i] = ok ? st.sg[r][i] : 0u;
+      }
+      if constexpr (lm_w6<FMT>()) {   // hi slices: lane l holds units 2(l % 16) and 2(l % 16) + 1
+        const int u0 = 2 * (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = st.v[r][8 + i];
+          st.v[r][8 + i] = make_uint4(u0 < nv ? v.x : 0u, u0 < nv ? v.y : 0u, u0 + 1 < nv ? v.z : 0u,
+                                      u0 + 1 < nv ? v.w : 0u);
+        }
+      }
+    }
+  }
+}
+
 template <int FMT, int RB>
 __device__ __forceinline__ void lm_store(const LmStage<FMT, RB>& st, uint8_t* lds, int lane) {
 #pragma unroll
@@ -773,6 +817,11 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
   constexpr int MS = wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1;
   uint4 cs[MS], cz[MS];   // W4: the metadata of the stage in LDS
   constexpr int XR = lm_xring<FMT, MT>();
+  [[maybe_unused]] const W4Masks w4m = wfmt(FMT) == WQ_FMT_W4G32 && !bf16_act(FMT) ? w4_masks() : W4Masks{};
+  // x fragments. Row m of the product depends only on row m of x, so the lanes of rows past M load
+  // row M - 1 again and their outputs are not stored (loading nothing there, under an exec mask,
+  // was slower). Units past the row end (the ragged last stage) contribute nothing because their
+  // weights are zeroed when the stage is parked.
   h8 xr[XR][MT][4];
   auto xload = [&](int t) {   // x[m = 16 mt + nl][unit 32h + 8q + j] of K tile t = 8i + j
     const int h = kw + (t >> 3) * WK, j = t & 7;
@@ -785,7 +834,8 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
       for (int k = 0; k < 4; ++k) xr[t % XR][mt][k] = __builtin_bit_cast(h8, xp[k]);
     }
   };
-  auto park = [&]() {   // the loaded stage -> LDS (and W4 metadata -> cs, cz)
+  auto park = [&](int h) {   // the loaded stage h -> LDS (and W4 metadata -> cs, cz)
+    if (32 * h + 32 > U) lm_zero_past_row<FMT, RB>(st, U - 32 * h, lane);   // wave-uniform: the ragged last stage
     lm_store<FMT, RB>(st, lds, lane);
     if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
 #pragma unroll
@@ -796,7 +846,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
 #pragma unroll
     for (int t = 0; t + 1 < XR; ++t) xload(t);
     lm_load<FMT, RB>(st, w, scales, zeros, n0, N, K, kw, lane);
-    park();
+    park(kw);
   }
   for (int i = 0; i < NI; ++i) {
     const int h = kw + i * WK;
@@ -807,8 +857,6 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
       const int t = 8 * i + j;
       if (j + XR - 1 < 8 || i + 1 < NI) xload(t + XR - 1);
       const int u = 8 * q + j;   // unit within the stage
-      const bool uok = 32 * h + u < U;
-      const h8 zero8 = {};
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const uint8_t* base = lds + r * lm_block<FMT>();
@@ -823,28 +871,27 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
           if constexpr (wfmt(FMT) == WQ_FMT_W4G32) decode_bf16<FMT>(raw, half_of(cs[r], j), half_of(cz[r], j), wv);
           else decode_bf16<FMT>(raw, 0, 0, wv);
         } else {
-          h2 zc1 = {}, zc2 = {};
-          if constexpr (wfmt(FMT) == WQ_FMT_W4G32) w4_consts(half_of(cz[r], j), zc1, zc2);
-          decode<FMT>(raw, zc1, zc2, wv);
           if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+            h2 zc1, zc2;
+            w4_consts(half_of(cz[r], j), zc1, zc2);
+            decode_w4_unit(raw.a, zc1, zc2, w4m, wv);
             const _Float16 sv = __builtin_bit_cast(_Float16, half_of(cs[r], j));
             const h2 s2 = {sv, sv};
 #pragma unroll
             for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
+          } else {
+            decode<FMT>(raw, h2{}, h2{}, wv);
           }
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const h8 b = frag_of(wv, k);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const bool ok = uok && 16 * mt + nl < M;
-            acc[r][mt] = mfma16<FMT>(ok ? xr[t % XR][mt][k] : zero8, b, acc[r][mt]);
-          }
+          for (int mt = 0; mt < MT; ++mt) acc[r][mt] = mfma16<FMT>(xr[t % XR][mt][k], b, acc[r][mt]);
         }
       }
     }
-    if (i + 1 < NI) park();
+    if (i + 1 < NI) park(h + WK);
   }
 
   // WK partials through LDS (every wave is done with its region after the barrier), fixed
