@@ -30,6 +30,8 @@ Modules:
   quantize  int8 / int4-g32 / fp6 / fp4 / fp5 quantizers (fp64 arithmetic)
   layout    the packed byte layout: a scalar bit-writer/reader and a vectorised packer
   linear    dequantisation to fp16 or bfloat16 and the fp64 reference linear, plus its error bound
+  decode    the decode step around the linears (RMSNorm, rotary embedding, attention over a key/value
+            cache, silu(gate)*up, residual stream, output layer, next token), imported as oracle.decode
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``. No
 function is "parity unpinned".

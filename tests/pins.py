@@ -453,3 +453,99 @@ def check_linear(linear_fn, x_bits, w_bits, value=f16_bits_to_fraction):
             if abs(Fraction(float(y[i, j])) - ye[i][j]) > mag * Fraction(k + 1, 2 ** 52):
                 return False
     return True
+
+
+# ---------------------------------------------------------------- decode-step components
+def golden_decode_examples():
+    """Parsed tests/golden/decode_examples.txt: {name: (inputs dict of strings, expected floats)}."""
+    out = {}
+    with open(os.path.join(GOLDEN, "decode_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, ins, exp = [p.strip() for p in line.split("|")]
+            kv = dict(item.split("=", 1) for item in ins.split())
+            out[name] = (kv, [float(v) for v in exp.split()])
+    return out
+
+
+def _vec(s):
+    return np.array([float(v) for v in s.split(",")])
+
+
+def check_rmsnorm(fn):
+    """fn(x [M,d], g [d], eps) against the hand-derived examples."""
+    ex = golden_decode_examples()
+    for name in ("rmsnorm", "rmsnorm_eps"):
+        kv, want = ex[name]
+        got = fn(_vec(kv["x"])[None, :], _vec(kv["g"]), float(kv["eps"]))[0]
+        if not np.allclose(got, want, rtol=2e-3, atol=0):    # the function rounds to fp16
+            return False
+    return True
+
+
+def check_rope(fn):
+    """fn(x [M, heads*hd], pos, hd, theta) against the hand-derived examples, plus two exact facts:
+    position 0 is the identity and every pair keeps its length."""
+    ex = golden_decode_examples()
+    for name in ("rope", "rope_pos2"):
+        kv, want = ex[name]
+        got = fn(_vec(kv["x"])[None, :], int(kv["pos"]), int(kv["hd"]), float(kv["theta"]))[0]
+        if not np.allclose(got, want, rtol=1e-11, atol=1e-12):
+            return False
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 3 * 8))
+    if not np.array_equal(fn(x, 0, 8, 10000.0), x):
+        return False
+    y = fn(x, 37, 8, 10000.0)
+    n0 = x.reshape(2, 3, 4, 2) ** 2
+    n1 = y.reshape(2, 3, 4, 2) ** 2
+    return bool(np.allclose(n0.sum(-1), n1.sum(-1), rtol=1e-12))
+
+
+def check_attention(fn):
+    """fn(q, cache_k, cache_v, pos, n_heads, n_kv_heads, hd) against the hand-derived example, the
+    one-position case (the output is that position's value), a library softmax (scipy) on random
+    data with grouped heads, and equal scores (the mean of the values)."""
+    from scipy.special import softmax
+    kv, want = golden_decode_examples()["attention"]
+    q = _vec(kv["q"])[None, :]
+    k = np.array([_vec(r) for r in kv["k"].split(";")])[None]
+    v = np.array([_vec(r) for r in kv["v"].split(";")])[None]
+    if not np.allclose(fn(q, k, v, 1, 1, 1, 2)[0], want, rtol=1e-8):
+        return False
+    rng = np.random.default_rng(9)
+    H, Hkv, hd, S, pos = 4, 2, 8, 6, 4
+    q = rng.standard_normal((2, H * hd))
+    ck, cv = rng.standard_normal((2, S, Hkv * hd)), rng.standard_normal((2, S, Hkv * hd))
+    if not np.allclose(fn(q, ck, cv, 0, H, Hkv, hd)[:, :hd], cv[:, 0, :hd], rtol=1e-13):
+        return False
+    got = fn(q, ck, cv, pos, H, Hkv, hd)
+    for b in range(2):
+        for h in range(H):
+            kvh = h // (H // Hkv)
+            s = ck[b, :pos + 1, kvh * hd:(kvh + 1) * hd] @ q[b, h * hd:(h + 1) * hd] / np.sqrt(hd)
+            ref = softmax(s) @ cv[b, :pos + 1, kvh * hd:(kvh + 1) * hd]
+            if not np.allclose(got[b, h * hd:(h + 1) * hd], ref, rtol=1e-12, atol=1e-14):
+                return False
+    z = fn(np.zeros((1, hd)), ck[:1, :, :hd], cv[:1, :, :hd], pos, 1, 1, hd)
+    return bool(np.allclose(z[0], cv[0, :pos + 1, :hd].mean(axis=0), rtol=1e-12))
+
+
+def check_silu_mul(fn):
+    """fn(g, u) against the hand-derived example and scipy's logistic function."""
+    from scipy.special import expit
+    kv, want = golden_decode_examples()["silu_mul"]
+    if not np.allclose(fn(np.array([float(kv["g"])]), np.array([float(kv["u"])])), want, rtol=1e-3):
+        return False
+    g = np.linspace(-12, 12, 97)
+    u = np.cos(g)
+    ref = g * expit(g) * u
+    return bool(np.allclose(fn(g, u), ref, rtol=2 ** -10, atol=2 ** -24))
+
+
+def check_argmax(fn):
+    """fn(logits [M, V]) -> the lowest index of the largest value per row."""
+    x = np.array([[1.0, 3.0, 3.0, 2.0], [-1.0, -1.0, -2.0, -1.0], [0.0, 0.0, 0.0, 5.0]])
+    return bool(np.array_equal(fn(x), [1, 0, 3]))
