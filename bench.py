@@ -81,6 +81,13 @@ def parse():
     ap.add_argument("--sweep", choices=["llama2_7b", "llama70b_w6"], default=None,
                     help="time a whole decode step's linears of a random-init model instead of --workload: "
                          "llama2_7b (32 layers, fp16/W8/W4/W6, M=1) or llama70b_w6 (80 layers, W6, M=1..16)")
+    ap.add_argument("--decode", choices=["llama2_7b"], default=None,
+                    help="time whole captured decode steps (embedding, every layer's norms, linears, rotary "
+                         "embedding, attention over the key/value cache, the output layer and the next token) of a "
+                         "random-init model, in tokens/s")
+    ap.add_argument("--weights", default="w4g32", help="weight format of --decode")
+    ap.add_argument("--context", type=int, default=512, help="cached positions when --decode starts timing")
+    ap.add_argument("--max-seq", type=int, default=2048, help="key/value cache length of --decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 512 MiB (a known-size kernel for counter calibration)")
     ap.add_argument("--settle-ms", type=float, default=200.0,
@@ -523,6 +530,108 @@ def sweep_oracle_leg(model, draws, outs, head_fmt, head_m):
     return cpu, check
 
 
+def run_decode(args, torch):
+    """Whole decode steps of a random-init model (weights of every layer in their own memory), one
+    step captured as a HIP graph and replayed; each replay generates the next token of M sequences."""
+    from weight_only_quantized_dequant_amd import decode
+    cfg = dict(decode.LLAMA2_7B)
+    fmt = FMT_OF[args.weights]
+    m = args.m or 1
+    S = args.max_seq
+    steps = max(1, args.steps // 100)
+    warm = max(1, min(args.warmup // 100, 100))
+    host, _ = decode.random_model(cfg, fmt, 20, distinct_layers=1)
+    dec = decode.Decoder(torch, cfg, fmt, m, S, *host)
+    dec.tokens.fill_(1)
+    graph = dec.capture()
+    dec.pos.fill_(args.context)
+    for _ in range(warm):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0, settled = time.perf_counter(), 0
+    while 1e3 * (time.perf_counter() - t0) < SETTLE_MS[0] and args.context + settled + 1 < S - steps:
+        graph.replay()
+        settled += 1
+        if settled % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    SETTLE_LOG.append((1e3 * (time.perf_counter() - t0), settled))
+    dec.pos.fill_(args.context)       # the timed steps run at positions context .. context + steps - 1
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    logits = dec.logits.view(torch.float16).float()
+    finite = bool(torch.isfinite(logits).all().item())
+    wbytes = dec.weight_bytes()
+    kv_bytes = 2 * cfg["layers"] * m * (args.context + steps // 2) * cfg["n_kv_heads"] * cfg["hd"] * 2
+    out = {"metric": "decode tokens/s, whole captured decode step (Llama-2-7B shapes, random-init)",
+           "value": round(m / (ms * 1e-3), 1), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f16", "data": "synthetic",
+           "config": {"workload": "llama2_7b_decode_step", "weights": args.weights, "M": m, "context": args.context,
+                      "max_seq": S, "layers": cfg["layers"], "vocab": cfg["vocab"],
+                      "launches_per_step": 3 + 8 * cfg["layers"],
+                      "timing": "HIP graph of one decode step, replayed; events on the launch stream"},
+           "weight_GB_per_step": round(wbytes / 1e9, 3), "kv_cache_GB_read_per_step": round(kv_bytes / 1e9, 3),
+           "weight_GB/s": round(wbytes / (ms * 1e-3) / 1e9, 1),
+           "pct_of_peak_weights_and_cache": round(100 * (wbytes + kv_bytes) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+           "logits_finite": finite,
+           "clock_settle": {"ms": round(SETTLE_LOG[-1][0], 1), "steps": SETTLE_LOG[-1][1]}}
+    if not args.no_cpu:
+        out["cpu_baseline"] = decode_cpu_baseline(cfg, fmt, host, args.context)
+    print(json.dumps(out))
+    return 0 if finite else 1
+
+
+def decode_cpu_baseline(cfg, fmt, host, context):
+    """The oracle (test infrastructure, imported here only) on one layer of the same model: unpack +
+    dequant + float64 products of its seven linears, the norms, rotary embedding and attention over
+    `context` cached positions, and the output layer; a whole step extrapolated from that layer."""
+    import oracle
+    from oracle import decode as D
+    from weight_only_quantized_dequant_amd import decode
+    cores, cpu_model = host_cpu()
+    limit, blas_threads = blas_on_host_cores()
+    layers, final_norm, lm_head, embed = host
+    f = fmt & 0xFF
+    L = layers[0]
+    rng = np.random.default_rng(3)
+    hd, H, Hkv, d = cfg["hd"], cfg["n_heads"], cfg["n_kv_heads"], cfg["d"]
+    ck = D.f16(rng.standard_normal((1, context + 1, Hkv * hd)))
+    cv = D.f16(rng.standard_normal((1, context + 1, Hkv * hd)))
+    x = D.f16(rng.standard_normal((1, d)))
+
+    def dq(pk, n, k):
+        p, s, z = pk
+        return oracle.dequant_fp16(f, oracle.unpack_vectorized(f, p, n, k), s, z)
+    with limit:
+        t0 = time.perf_counter()
+        shapes = {nm: (n, k) for nm, n, k in decode.linear_shapes(cfg)}
+        W = {nm: dq(L[nm], *shapes[nm]) for nm in shapes}
+        h = D.rmsnorm(x, oracle.fp16_from_bits(L["attn_norm"]), cfg["eps"])
+        q, k, v = D.lin(h, W["q"]), D.lin(h, W["k"]), D.lin(h, W["v"])
+        ck[:, context] = D.f16(D.rope(k, context, hd, cfg["theta"]))
+        cv[:, context] = v
+        a = D.f16(D.attention(D.rope(q, context, hd, cfg["theta"]), ck, cv, context, H, Hkv, hd))
+        x = x + D.lin(a, W["o"])
+        h2 = D.rmsnorm(x, oracle.fp16_from_bits(L["ffn_norm"]), cfg["eps"])
+        x = x + D.lin(D.silu_mul(D.lin(h2, W["gate"]), D.lin(h2, W["up"])), W["down"])
+        t_layer = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        D.lin(D.rmsnorm(x, oracle.fp16_from_bits(final_norm), cfg["eps"]), dq(lm_head, cfg["vocab"], d))
+        t_out = time.perf_counter() - t1
+    step_s = t_layer * cfg["layers"] + t_out
+    return {"value": 1.0 / step_s, "unit": "tok/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model,
+            "blas_threads": blas_threads, "extrapolated": True,
+            "sample": "one decode layer (unpack + dequant + float64 products of its 7 linears, norms, rotary "
+                      "embedding, attention over %d positions) in %.2f s and the output layer in %.2f s; a "
+                      "%d-layer step extrapolated: %.1f s" % (context, t_layer, t_out, cfg["layers"], step_s)}
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -538,6 +647,8 @@ def main():
         return 1
     wq.lib()
     SETTLE_MS[0] = args.settle_ms
+    if args.decode:
+        return run_decode(args, torch)
     if args.sweep:
         return run_sweep(args, torch)
     if args.copy_calibration:

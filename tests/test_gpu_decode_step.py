@@ -1,0 +1,274 @@
+"""GPU parity of the decode-step kernels (include/wq_decode.h) and of a whole captured decode step.
+
+Each kernel is compared with the oracle (oracle/decode.py) on seeded inputs: RMSNorm with the
+residual add, the embedding gather, silu(gate)*up, argmax with ties, and the rotary embedding +
+key/value cache append + attention at head sizes 64 and 128, grouped heads, single-chunk and
+several-chunk contexts (the chunks meet through the workspace), the chunk boundaries and the last
+cache position. Then a small random-init model runs whole decode steps (eagerly, and as replays of
+one captured HIP graph, which must agree bit for bit) against the oracle's decode step.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import decode as D
+from weight_only_quantized_dequant_amd import decode, inputs, wq
+from tests.gpu_util import dev, host_bits, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def f16_bits(a):
+    return np.asarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_vals(bits):
+    return oracle.fp16_from_bits(bits)
+
+
+def ulp_close(got_bits, want_vals, ulps=1):
+    """fp16 results within `ulps` units in the last place of the reference value (the reference is
+    the float64 value rounded once; the device rounds its float32 value once)."""
+    got = f16_vals(got_bits)
+    want = f16_vals(oracle.fp16_bits(want_vals))
+    spacing = np.maximum(np.abs(np.spacing(want.astype(np.float16))).astype(np.float64), 2.0 ** -24)
+    return np.abs(got - want) <= ulps * spacing
+
+
+@pytest.mark.parametrize("m,d", [(1, 4096), (3, 8192), (16, 4096), (2, 72), (1, 8200), (2, 16384)])
+@pytest.mark.parametrize("with_delta", [False, True])
+def test_add_rmsnorm(m, d, with_delta):
+    torch = torch_cuda()
+    rng = np.random.default_rng([m, d, int(with_delta)])
+    x = (3.0 * rng.standard_normal((m, d))).astype(np.float32)
+    delta = f16_bits(rng.standard_normal((m, d)))
+    g = f16_bits(1 + 0.1 * rng.standard_normal(d))
+    xd = torch.from_numpy(x.copy()).to("cuda:0")
+    out = torch.empty(m * d, dtype=torch.int16, device="cuda:0")
+    wq.wq_add_rmsnorm(xd, dev(delta) if with_delta else None, dev(g), 1e-5, out, m, d)
+    torch.cuda.synchronize()
+    x_new = x + f16_vals(delta).astype(np.float32) if with_delta else x   # float32 add, rounded once
+    assert np.array_equal(xd.cpu().numpy(), x_new)
+    want = D.rmsnorm(x_new.astype(np.float64), f16_vals(g), 1e-5)
+    ok = ulp_close(host_bits(out).reshape(m, d), want)
+    assert ok.all(), int((~ok).sum())
+
+
+def test_embed_and_token_clamp():
+    torch = torch_cuda()
+    V, d = 300, 4096
+    rng = np.random.default_rng(4)
+    table = f16_bits(rng.standard_normal((V, d)))
+    tokens = np.array([0, 299, 17, -5, 1000], dtype=np.int32)
+    x = torch.zeros(5 * d, dtype=torch.float32, device="cuda:0")
+    wq.wq_embed(dev(table), torch.from_numpy(tokens).to("cuda:0"), x, 5, d, V)
+    torch.cuda.synchronize()
+    want = f16_vals(table)[np.clip(tokens, 0, V - 1)]
+    assert np.array_equal(x.cpu().numpy().reshape(5, d), want.astype(np.float32))
+
+
+@pytest.mark.parametrize("n", [8, 11008, 16 * 28672])
+def test_silu_mul(n):
+    torch = torch_cuda()
+    rng = np.random.default_rng(n)
+    g = f16_bits(4 * rng.standard_normal(n))
+    u = f16_bits(rng.standard_normal(n))
+    g[:4] = f16_bits([0.0, -30.0, 30.0, 1.5])
+    out = torch.empty(n, dtype=torch.int16, device="cuda:0")
+    wq.wq_silu_mul(dev(g), dev(u), out, n)
+    torch.cuda.synchronize()
+    ok = ulp_close(host_bits(out), D.silu_mul(f16_vals(g), f16_vals(u)))
+    assert ok.all(), int((~ok).sum())
+
+
+@pytest.mark.parametrize("m,vocab", [(1, 32000), (4, 512), (16, 32000)])
+def test_argmax_next_ties_and_position(m, vocab):
+    torch = torch_cuda()
+    rng = np.random.default_rng(vocab + m)
+    logits = f16_bits(rng.standard_normal((m, vocab)))
+    logits[0, 100] = logits[0, 7] = f16_bits([9.0])[0]          # a tie: the lower index wins
+    if m > 1:
+        logits[1, :] = f16_bits([-1.0])[0]                      # all equal: index 0
+        logits[1, vocab - 1] = 0x7E00                            # NaN never wins
+    tokens = torch.zeros(m, dtype=torch.int32, device="cuda:0")
+    pos = torch.tensor([41], dtype=torch.int32, device="cuda:0")
+    wq.wq_argmax_next(dev(logits), m, vocab, tokens, pos)
+    torch.cuda.synchronize()
+    vals = f16_vals(logits)
+    vals[np.isnan(vals)] = -np.inf
+    assert np.array_equal(tokens.cpu().numpy(), D.argmax_lowest(vals))
+    assert tokens.cpu().numpy()[0] == 7
+    assert int(pos.cpu().numpy()[0]) == 42
+
+
+def _attention_case(m, H, Hkv, hd, S, p, seed):
+    rng = np.random.default_rng([seed, m, H, Hkv, hd, S, p])
+    q = f16_bits(rng.standard_normal((m, H * hd)))
+    k = f16_bits(rng.standard_normal((m, Hkv * hd)))
+    v = f16_bits(rng.standard_normal((m, Hkv * hd)))
+    ck = f16_bits(rng.standard_normal((m, S, Hkv * hd)))
+    cv = f16_bits(rng.standard_normal((m, S, Hkv * hd)))
+    return q, k, v, ck, cv
+
+
+def _run_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, p, theta=10000.0, calls=1):
+    torch = torch_cuda()
+    cos, sin = wq.wq_rope_table(theta, hd, S)
+    ckd, cvd = dev(ck.reshape(-1)), dev(cv.reshape(-1))
+    out = torch.empty(m * H * hd, dtype=torch.int16, device="cuda:0")
+    ws_bytes = wq.wq_attention_workspace_bytes(m, H, hd, S)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda:0") if ws_bytes else None
+    pos = torch.tensor([p], dtype=torch.int32, device="cuda:0")
+    outs = []
+    for _ in range(calls):
+        wq.wq_rope_attention(dev(q), dev(k), dev(v), ckd, cvd, torch.from_numpy(cos.reshape(-1)).to("cuda:0"),
+                             torch.from_numpy(sin.reshape(-1)).to("cuda:0"), pos, out, m, H, Hkv, hd, S, ws)
+        torch.cuda.synchronize()
+        outs.append(host_bits(out).reshape(m, H * hd))
+    return outs, host_bits(ckd).reshape(m, S, Hkv * hd), host_bits(cvd).reshape(m, S, Hkv * hd)
+
+
+def _check_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, p, theta=10000.0, calls=1):
+    outs, ck_dev, cv_dev = _run_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, p, theta, calls)
+    pc = min(max(p, 0), S - 1)
+    # the cache: position pc holds the rotated new key (within one fp16 unit) and the new value;
+    # every other position is untouched
+    k_rot = D.rope(f16_vals(k), pc, hd, theta)
+    assert ulp_close(ck_dev[:, pc], k_rot).all()
+    assert np.array_equal(cv_dev[:, pc], v)
+    others = np.arange(S) != pc
+    assert np.array_equal(ck_dev[:, others], ck[:, others]) and np.array_equal(cv_dev[:, others], cv[:, others])
+    # the output, against the oracle on the device's cache contents at positions < pc and the
+    # oracle's own rotated key at pc
+    ck_ref = f16_vals(ck).copy()
+    ck_ref[:, pc] = D.f16(k_rot)
+    cv_ref = f16_vals(cv).copy()
+    cv_ref[:, pc] = f16_vals(v)
+    qr = D.rope(f16_vals(q), pc, hd, theta)
+    ref = D.attention(qr, ck_ref, cv_ref, pc, H, Hkv, hd)
+    # bound: the fp16 output rounding, plus float32 scores and weights (relative 1e-4 of the
+    # weighted sum of |v|, far above their rounding at these sizes)
+    absv = D.attention(qr, ck_ref, np.abs(cv_ref), pc, H, Hkv, hd)
+    bound = 2.0 ** -11 * np.abs(ref) + 1e-4 * absv + 2.0 ** -24
+    for out in outs:
+        err = np.abs(f16_vals(out) - ref)
+        assert np.all(err <= bound), float((err / bound).max())
+    for out in outs[1:]:   # repeat calls are bit-identical
+        assert np.array_equal(out, outs[0])
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 2)])
+@pytest.mark.parametrize("p", [0, 1, 64, 127, 128, 129, 300, 511])
+def test_rope_attention(hd, H, Hkv, p):
+    m, S = 2, 512
+    q, k, v, ck, cv = _attention_case(m, H, Hkv, hd, S, p, 1)
+    _check_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, p, calls=2)
+
+
+def test_rope_attention_short_cache_needs_no_workspace():
+    m, H, Hkv, hd, S = 3, 4, 1, 128, 128
+    assert wq.wq_attention_workspace_bytes(m, H, hd, S) == 0
+    q, k, v, ck, cv = _attention_case(m, H, Hkv, hd, S, 40, 2)
+    _check_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, 40)
+
+
+def test_rope_attention_position_past_the_cache_is_clamped():
+    m, H, Hkv, hd, S = 1, 4, 2, 64, 128
+    q, k, v, ck, cv = _attention_case(m, H, Hkv, hd, S, 7, 3)
+    _check_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, S + 9)
+
+
+def test_rope_attention_llama7b_shape_long_context():
+    # Llama-2-7B heads (32 x 128) with 2048 cached positions at position 1500: 24 chunks
+    m, H, Hkv, hd, S, p = 1, 32, 32, 128, 2048, 1500
+    q, k, v, ck, cv = _attention_case(m, H, Hkv, hd, S, p, 4)
+    _check_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, p, calls=2)
+
+
+def test_rope_attention_rejects_bad_arguments():
+    torch = torch_cuda()
+    L = wq.lib()
+    a = torch.zeros(1 << 16, dtype=torch.int16, device="cuda:0")
+    pa = a.data_ptr()
+    assert L.wq_rope_attention(pa, pa, pa, pa, pa, pa, pa, pa, pa, 1, 4, 3, 64, 16, None, 0, None) == -2   # 4 % 3
+    assert L.wq_rope_attention(pa, pa, pa, pa, pa, pa, pa, pa, pa, 1, 4, 4, 96, 16, None, 0, None) == -2   # head size
+    assert L.wq_rope_attention(pa, pa, pa, pa, pa, pa, pa, pa, pa, 1, 4, 4, 64, 129, None, 0, None) == -1   # workspace
+    assert L.wq_rope_attention(pa + 2, pa, pa, pa, pa, pa, pa, pa, pa, 1, 4, 4, 64, 16, None, 0, None) == -5
+    assert L.wq_add_rmsnorm(pa, None, pa, 1e-5, pa, 1, 20, None) == -2
+    assert L.wq_silu_mul(pa, pa, pa, 12, None) == -2
+    assert L.wq_argmax_next(pa, 1, 10, pa, pa, None) == -2
+
+
+# ------------------------------------------------------------------ whole decode steps
+TINY = dict(d=256, n_heads=4, n_kv_heads=2, hd=64, ffn=512, layers=2, vocab=512, eps=1e-5, theta=10000.0)
+
+
+def _oracle_model(cfg, fmt, draws):
+    layers = []
+    for l in range(cfg["layers"]):
+        L = {nm: D.dequantized(fmt, draws[(l, nm)]) if fmt != wq.FMT_F16 else oracle.fp16_bits(draws[(l, nm)])
+             for nm in decode.LINEARS}
+        L["attn_norm"] = f16_vals(draws[(l, "attn_norm")])
+        L["ffn_norm"] = f16_vals(draws[(l, "ffn_norm")])
+        layers.append(L)
+    lm = D.dequantized(fmt, draws["lm_head"]) if fmt != wq.FMT_F16 else oracle.fp16_bits(draws["lm_head"])
+    return D.Model(cfg, layers, f16_vals(draws["final_norm"]), lm, f16_vals(draws["embed"]))
+
+
+def _fill(dec, torch, tokens, p0, caches):
+    dec.tokens.copy_(torch.from_numpy(tokens))
+    dec.pos.fill_(p0)
+    dec.x.zero_()
+    for l in range(len(dec.cache_k)):
+        dec.cache_k[l].copy_(torch.from_numpy(caches[0][l].reshape(-1).view(np.int16)))
+        dec.cache_v[l].copy_(torch.from_numpy(caches[1][l].reshape(-1).view(np.int16)))
+
+
+@pytest.mark.parametrize("fmt", [wq.FMT_W4G32, wq.FMT_W8, wq.FMT_W6E3M2], ids=["w4", "w8", "w6"])
+def test_decode_steps_match_the_oracle_eager_and_graph(fmt):
+    torch = torch_cuda()
+    cfg, m, S, p0, steps = TINY, 2, 128, 70, 3
+    host, draws = decode.random_model(cfg, fmt, 500 + fmt)
+    rng = np.random.default_rng([77, fmt])
+    kvw = cfg["n_kv_heads"] * cfg["hd"]
+    caches = ([f16_bits(rng.standard_normal((m, S, kvw))) for _ in range(cfg["layers"])],
+              [f16_bits(rng.standard_normal((m, S, kvw))) for _ in range(cfg["layers"])])
+    tokens0 = np.array([5, 300], dtype=np.int32)
+    eager = decode.Decoder(torch, cfg, fmt, m, S, *host)
+    graphed = decode.Decoder(torch, cfg, fmt, m, S, *host)
+    _fill(eager, torch, tokens0, p0, caches)
+    _fill(graphed, torch, tokens0, p0, caches)
+    graph = graphed.capture()
+    _fill(graphed, torch, tokens0, p0, caches)   # capture does not run the step; start from the same state
+    model = _oracle_model(cfg, fmt, draws)
+    ock = [f16_vals(c).copy() for c in caches[0]]
+    ocv = [f16_vals(c).copy() for c in caches[1]]
+    tokens = tokens0.copy()
+    for s in range(steps):
+        eager.step()
+        graph.replay()
+        torch.cuda.synchronize()
+        le = host_bits(eager.logits).reshape(m, cfg["vocab"])
+        lg = host_bits(graphed.logits).reshape(m, cfg["vocab"])
+        assert np.array_equal(le, lg), "step %d: graph replay differs from the eager step" % s
+        assert np.array_equal(eager.tokens.cpu().numpy(), graphed.tokens.cpu().numpy())
+        assert int(eager.pos.cpu().numpy()[0]) == p0 + s + 1 == int(graphed.pos.cpu().numpy()[0])
+        ref, nxt, x_ref = D.decode_step(model, tokens, p0 + s, ock, ocv)
+        got = f16_vals(le)
+        tol = 1e-2 + 1e-2 * np.abs(ref)
+        assert np.all(np.abs(got - ref) <= tol), (s, float((np.abs(got - ref) / tol).max()))
+        x_dev = eager.x.cpu().numpy().reshape(m, cfg["d"])
+        assert np.allclose(x_dev, x_ref, rtol=1e-2, atol=1e-2)
+        for l in (0, cfg["layers"] - 1):   # this step's cache row
+            kd = f16_vals(host_bits(eager.cache_k[l]).reshape(m, S, kvw)[:, p0 + s])
+            assert np.allclose(kd, ock[l][:, p0 + s], rtol=1e-2, atol=1e-2)
+        # next tokens agree wherever the oracle's two largest logits are apart by more than the tolerance
+        dev_next = eager.tokens.cpu().numpy()
+        top2 = np.sort(ref, axis=1)[:, -2:]
+        clear = (top2[:, 1] - top2[:, 0]) > 2 * tol.max()
+        assert np.array_equal(dev_next[clear], nxt[clear])
+        if not np.array_equal(dev_next, nxt):
+            break   # a near tie chose another token: later steps are no longer comparable
+        tokens = nxt

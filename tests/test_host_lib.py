@@ -17,7 +17,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(wq.LIB_PATH), reason="libwq.s
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    import glob
+    src = "".join(open(h).read() for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", src)))
 
@@ -458,3 +459,54 @@ def test_binding_rejects_cpu_strided_and_short_buffers_before_any_launch(monkeyp
     with pytest.raises(ValueError, match="y holds"):
         wq.wq_linear(good["x"], good["w"], good["s"], good["z"], _FakeDeviceTensor(2 * m * n - 1), m, n, k,
                      fmt | wq.ACT_BF16)
+
+
+def test_rope_table_matches_the_oracle_angles():
+    from oracle import decode as D
+    cos, sin = wq.wq_rope_table(10000.0, 128, 300)
+    for p in (0, 1, 17, 299):
+        a = D.rope_angles(p, 128, 10000.0)
+        assert np.allclose(cos[p], np.cos(a), rtol=0, atol=6e-8)   # float32 rounding of the float64 value
+        assert np.allclose(sin[p], np.sin(a), rtol=0, atol=6e-8)
+    assert np.array_equal(cos[0], np.ones(64, dtype=np.float32)) and not np.any(sin[0])
+    L = wq.lib()
+    buf = np.zeros(64, dtype=np.float32)
+    assert L.wq_rope_table(10000.0, 3, 4, wq._host_ptr(buf), wq._host_ptr(buf)) == -2
+    assert L.wq_rope_table(-1.0, 4, 4, wq._host_ptr(buf), wq._host_ptr(buf)) == -1
+
+
+def test_decode_entry_points_reject_bad_arguments_before_launch():
+    L = wq.lib()
+    a = 1 << 20
+    assert L.wq_embed(a, a, a, 1, 12, 10, None) == -2                 # d not a multiple of 8
+    assert L.wq_embed(None, a, a, 1, 16, 10, None) == -1
+    assert L.wq_add_rmsnorm(a, None, a, -1.0, a, 1, 16, None) == -1   # eps < 0
+    assert L.wq_add_rmsnorm(a + 4, None, a, 1e-5, a, 1, 16, None) == -5
+    assert L.wq_silu_mul(a, a, a, 0, None) == -2
+    assert L.wq_argmax_next(a, 0, 16, a, a, None) == -2
+    assert L.wq_rope_attention(a, a, a, a, a, a, a, a, a, 1, 6, 4, 128, 16, None, 0, None) == -2   # 6 % 4
+    assert L.wq_rope_attention(a, a, a, a, a, a, a, a, a, 1, 4, 4, 128, 200, None, 0, None) == -1  # no workspace
+    need = wq.wq_attention_workspace_bytes(1, 4, 128, 200)
+    assert need > 0 and wq.wq_attention_workspace_bytes(1, 4, 128, 128) == 0
+    assert L.wq_rope_attention(a, a, a, a, a, a, a, a, a, 1, 4, 4, 128, 200, a, need - 1, None) == -1
+
+
+def test_decode_binding_rejects_cpu_and_short_buffers(monkeypatch):
+    import torch
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    F = _FakeDeviceTensor
+    with pytest.raises(ValueError, match="x holds"):
+        wq.wq_add_rmsnorm(F(4 * 2 * 64 - 4), None, F(128), 1e-5, F(256), 2, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        wq.wq_silu_mul(torch.zeros(64, dtype=torch.int16), F(128), F(128), 64)
+    with pytest.raises(ValueError, match="cache_v"):
+        m, H, Hkv, hd, S = 1, 4, 2, 64, 16
+        wq.wq_rope_attention(F(2 * H * hd), F(2 * Hkv * hd), F(2 * Hkv * hd), F(2 * S * Hkv * hd),
+                             F(2 * S * Hkv * hd - 2), F(4 * S * hd // 2), F(4 * S * hd // 2), F(4), F(2 * H * hd),
+                             m, H, Hkv, hd, S, None)
+    with pytest.raises(ValueError, match="workspace"):
+        m, H, Hkv, hd, S = 1, 4, 2, 64, 256
+        need = wq.wq_attention_workspace_bytes(m, H, hd, S)
+        wq.wq_rope_attention(F(2 * H * hd), F(2 * Hkv * hd), F(2 * Hkv * hd), F(2 * S * Hkv * hd),
+                             F(2 * S * Hkv * hd), F(4 * S * hd // 2), F(4 * S * hd // 2), F(4), F(2 * H * hd),
+                             m, H, Hkv, hd, S, F(need - 1))

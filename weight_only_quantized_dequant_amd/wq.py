@@ -82,6 +82,18 @@ def lib():
         for name in ("wq_pack_int8", "wq_pack_int4", "wq_pack_fp6", "wq_pack_fp4", "wq_pack_fp5", "wq_unpack",
                      "wq_dequant", "wq_linear"):
             getattr(L, name).restype = ctypes.c_int
+        # decode-step calls (include/wq_decode.h)
+        L.wq_rope_table.argtypes = [ctypes.c_double, _i64, _i64, _p, _p]
+        L.wq_embed.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p]
+        L.wq_add_rmsnorm.argtypes = [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _p]
+        L.wq_attention_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+        L.wq_attention_workspace_bytes.restype = ctypes.c_size_t
+        L.wq_rope_attention.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p,
+                                        ctypes.c_size_t, _p]
+        L.wq_silu_mul.argtypes = [_p, _p, _p, _i64, _p]
+        L.wq_argmax_next.argtypes = [_p, _i64, _i64, _p, _p, _p]
+        for name in ("wq_rope_table", "wq_embed", "wq_add_rmsnorm", "wq_rope_attention", "wq_silu_mul", "wq_argmax_next"):
+            getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -279,3 +291,77 @@ def wq_linear_grouped(items, m, fmt, stream=None):
         arr[i] = LinearItem(x.data_ptr(), pw.data_ptr(), sc.data_ptr() if sc is not None else None,
                             z.data_ptr() if z is not None else None, y.data_ptr(), n, k)
     _check(lib().wq_linear_grouped(arr, len(items), m, fmt, _stream_ptr(stream)), "wq_linear_grouped")
+
+
+# ------------------------------------------------------------------ decode-step calls (include/wq_decode.h)
+def wq_rope_table(theta, head_dim, positions):
+    """Host: (cos, sin) float32 [positions, head_dim/2] of the rotary embedding."""
+    cos = np.empty((max(positions, 1), max(head_dim // 2, 1)), dtype=np.float32)
+    sin = np.empty_like(cos)
+    _check(lib().wq_rope_table(theta, head_dim, positions, _host_ptr(cos), _host_ptr(sin)), "wq_rope_table")
+    return cos, sin
+
+
+def wq_embed(table, tokens, x, m, d, vocab, stream=None):
+    """Device: x[m] = table[tokens[m]] (fp16 table [vocab, d] -> float32 x [M, d])."""
+    sized = m >= 1 and d >= 1 and vocab >= 1
+    _need(table, 2 * vocab * d if sized else 0, "table", "wq_embed")
+    _need(tokens, 4 * m if sized else 0, "tokens", "wq_embed")
+    _need(x, 4 * m * d if sized else 0, "x", "wq_embed")
+    _check(lib().wq_embed(_dev_ptr(table), _dev_ptr(tokens), _dev_ptr(x), m, d, vocab, _stream_ptr(stream)), "wq_embed")
+
+
+def wq_add_rmsnorm(x, delta, g, eps, out, m, d, stream=None):
+    """Device: x += delta (if given); out = fp16(rmsnorm(x) * g)."""
+    sized = m >= 1 and d >= 1
+    _need(x, 4 * m * d if sized else 0, "x", "wq_add_rmsnorm")
+    _need(delta, 2 * m * d if sized else 0, "delta", "wq_add_rmsnorm")
+    _need(g, 2 * d if sized else 0, "g", "wq_add_rmsnorm")
+    _need(out, 2 * m * d if sized else 0, "out", "wq_add_rmsnorm")
+    _check(lib().wq_add_rmsnorm(_dev_ptr(x), _dev_ptr(delta), _dev_ptr(g), eps, _dev_ptr(out), m, d, _stream_ptr(stream)),
+           "wq_add_rmsnorm")
+
+
+def wq_attention_workspace_bytes(m, n_heads, head_dim, max_seq):
+    return lib().wq_attention_workspace_bytes(m, n_heads, head_dim, max_seq)
+
+
+def wq_rope_attention(q, k, v, cache_k, cache_v, rope_cos, rope_sin, pos, out, m, n_heads, n_kv_heads, head_dim, max_seq,
+                      workspace, stream=None):
+    """Device: rotary embedding, key/value cache append and attention of one new token per sequence."""
+    where = "wq_rope_attention"
+    sized = min(m, n_heads, n_kv_heads, head_dim, max_seq) >= 1
+    z = (lambda b: b) if sized else (lambda b: 0)
+    _need(q, z(2 * m * n_heads * head_dim), "q", where)
+    _need(out, z(2 * m * n_heads * head_dim), "out", where)
+    _need(k, z(2 * m * n_kv_heads * head_dim), "k", where)
+    _need(v, z(2 * m * n_kv_heads * head_dim), "v", where)
+    _need(cache_k, z(2 * m * max_seq * n_kv_heads * head_dim), "cache_k", where)
+    _need(cache_v, z(2 * m * max_seq * n_kv_heads * head_dim), "cache_v", where)
+    _need(rope_cos, z(4 * max_seq * (head_dim // 2)), "rope_cos", where)
+    _need(rope_sin, z(4 * max_seq * (head_dim // 2)), "rope_sin", where)
+    _need(pos, z(4), "pos", where)
+    ws = wq_attention_workspace_bytes(m, n_heads, head_dim, max_seq) if sized else 0
+    _need(workspace, ws, "workspace", where)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().wq_rope_attention(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(cache_k), _dev_ptr(cache_v),
+                                   _dev_ptr(rope_cos), _dev_ptr(rope_sin), _dev_ptr(pos), _dev_ptr(out), m, n_heads,
+                                   n_kv_heads, head_dim, max_seq, _dev_ptr(workspace), have, _stream_ptr(stream)), where)
+
+
+def wq_silu_mul(gate, up, out, n, stream=None):
+    """Device: out = fp16(silu(gate) * up), n elements."""
+    _need(gate, 2 * max(n, 0), "gate", "wq_silu_mul")
+    _need(up, 2 * max(n, 0), "up", "wq_silu_mul")
+    _need(out, 2 * max(n, 0), "out", "wq_silu_mul")
+    _check(lib().wq_silu_mul(_dev_ptr(gate), _dev_ptr(up), _dev_ptr(out), n, _stream_ptr(stream)), "wq_silu_mul")
+
+
+def wq_argmax_next(logits, m, vocab, tokens, pos, stream=None):
+    """Device: tokens[m] = argmax(logits[m]) (lowest index of the largest); pos += 1."""
+    sized = m >= 1 and vocab >= 1
+    _need(logits, 2 * m * vocab if sized else 0, "logits", "wq_argmax_next")
+    _need(tokens, 4 * m if sized else 0, "tokens", "wq_argmax_next")
+    _need(pos, 4 if sized else 0, "pos", "wq_argmax_next")
+    _check(lib().wq_argmax_next(_dev_ptr(logits), m, vocab, _dev_ptr(tokens), _dev_ptr(pos), _stream_ptr(stream)),
+           "wq_argmax_next")
