@@ -102,7 +102,8 @@ typedef enum {
   WQ_ERR_NONFINITE = -4,  /* a weight given to a packer is NaN or infinite           */
   WQ_ERR_ALIGN = -5,      /* a device pointer is not 16-byte aligned                 */
   WQ_ERR_DEVICE = -6,     /* the HIP runtime refused the launch                      */
-  WQ_ERR_RANGE = -7       /* a scale would overflow fp16 (max|w| too large)          */
+  WQ_ERR_RANGE = -7,      /* a scale would overflow fp16 (max|w| too large)          */
+  WQ_ERR_SCRATCH = -8     /* the sizes need more than a no-allocation call's scratch */
 } wq_status;
 /* WQ_ERR_DEVICE reflects only the call's own launches: the status of each launch is the value
  * that the launch call itself returns (hipLaunchKernel). An error that an earlier HIP runtime

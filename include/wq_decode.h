@@ -79,6 +79,21 @@ int wq_rope_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
                       int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t max_seq, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture that may not
+ * call hipMalloc, tight serving loops, harnesses that forbid allocation): wq_rope_attention with
+ * its workspace taken from a buffer the library holds in device memory, WQ_NOALLOC_SCRATCH_BYTES
+ * per GPU, kept until the process ends. It allocates nothing and computes exactly what
+ * wq_rope_attention computes. Sizes whose workspace (wq_attention_workspace_bytes) exceeds the
+ * buffer return WQ_ERR_SCRATCH before any launch; other errors as wq_rope_attention, and
+ * WQ_ERR_DEVICE if the buffer's address cannot be found on the current device. Every call on a
+ * GPU shares that GPU's buffer (no contents need clearing: each call writes the partial results it
+ * reads), so calls that overlap in time on one GPU race. */
+#define WQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+int wq_rope_attention_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* cache_k,
+                              uint16_t* cache_v, const float* rope_cos, const float* rope_sin, const int32_t* pos,
+                              uint16_t* out, int64_t M, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                              int64_t max_seq, void* stream);
+
 /* Device: out[i] = fp16(gate[i] / (1 + exp(-gate[i])) * up[i]) in float32, i < n. n a multiple of 8. */
 int wq_silu_mul(const uint16_t* gate, const uint16_t* up, uint16_t* out, int64_t n, void* stream);
 

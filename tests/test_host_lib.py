@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert wq.wq_version() >> 16 == 1
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert wq.wq_status_string(s) and wq.wq_status_string(s) != "unknown status"
     # no launch has failed on this thread (none ran): no device error to name
     assert wq.wq_last_device_error() == "none"

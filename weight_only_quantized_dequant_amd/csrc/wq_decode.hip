@@ -25,6 +25,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "wq_device.h"
 #include "wq_internal.h"
@@ -377,6 +378,33 @@ __global__ __launch_bounds__(HD) void attention_combine_kernel(const int32_t* __
   out[head * HD + tid] = (uint16_t)to_f16(A / L);
 }
 
+// The workspace of wq_rope_attention_noalloc: device memory the library holds, one copy per GPU,
+// for callers that cannot allocate. In host code `scratch` names a host-side stand-in: its device
+// address, found per device, is what kernels receive.
+static __device__ __align__(256) unsigned char scratch[WQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device, looked up on the first call there.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return wq::device_status(e);
+  if (dev < 0 || dev >= MAX_DEVICES) return wq::device_status(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return wq::device_status(e);
+    if (!p) return wq::device_status(hipErrorInvalidSymbol);
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return WQ_OK;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int64_t att_splits(int64_t max_seq) { return (max_seq + ATT_CHUNK - 1) / ATT_CHUNK; }
@@ -428,21 +456,35 @@ size_t wq_attention_workspace_bytes(int64_t M, int64_t n_heads, int64_t head_dim
   return att_part_bytes(M, n_heads, head_dim, max_seq);
 }
 
-int wq_rope_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* cache_k, uint16_t* cache_v,
-                      const float* rope_cos, const float* rope_sin, const int32_t* pos, uint16_t* out, int64_t M,
-                      int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t max_seq, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+namespace {
+// The argument checks of wq_rope_attention that do not concern its workspace.
+int check_attention_args(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* cache_k,
+                         const uint16_t* cache_v, const float* rope_cos, const float* rope_sin, const int32_t* pos,
+                         const uint16_t* out, int64_t M, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                         int64_t max_seq) {
   if (!q || !k || !v || !cache_k || !cache_v || !rope_cos || !rope_sin || !pos || !out) return WQ_ERR_ARG;
   if (M < 0 || n_heads < 0 || n_kv_heads < 0 || head_dim < 0 || max_seq < 0) return WQ_ERR_ARG;
   if (M < 1 || M > 65535 || n_heads < 1 || n_heads > 65535 || n_kv_heads < 1 || n_heads % n_kv_heads ||
       (head_dim != 64 && head_dim != 128) || max_seq < 1 || max_seq > (1 << 24) ||
       (double)M * max_seq * n_kv_heads * head_dim > 9.0e15)
     return WQ_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(cache_k) || !aligned16(cache_v) ||
+      !aligned16(out) || !aligned16(rope_cos) || !aligned16(rope_sin))
+    return WQ_ERR_ALIGN;
+  return WQ_OK;
+}
+}  // namespace
+
+int wq_rope_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* cache_k, uint16_t* cache_v,
+                      const float* rope_cos, const float* rope_sin, const int32_t* pos, uint16_t* out, int64_t M,
+                      int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t max_seq, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  const int st = check_attention_args(q, k, v, cache_k, cache_v, rope_cos, rope_sin, pos, out, M, n_heads, n_kv_heads,
+                                      head_dim, max_seq);
+  if (st != WQ_OK) return st;
   const size_t need = wq_attention_workspace_bytes(M, n_heads, head_dim, max_seq);
   if (need && (!workspace || workspace_bytes < need)) return WQ_ERR_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(cache_k) || !aligned16(cache_v) ||
-      !aligned16(out) || !aligned16(rope_cos) || !aligned16(rope_sin) || (need && !aligned16(workspace)))
-    return WQ_ERR_ALIGN;
+  if (need && !aligned16(workspace)) return WQ_ERR_ALIGN;
   const int splits = (int)att_splits(max_seq);
   float* part = need ? static_cast<float*>(workspace) : nullptr;
   const dim3 grid((unsigned)splits, (unsigned)n_heads, (unsigned)M);
@@ -462,6 +504,24 @@ int wq_rope_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
                      (int)max_seq, splits);
   }
   return wq::device_status(e);
+}
+
+int wq_rope_attention_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* cache_k,
+                              uint16_t* cache_v, const float* rope_cos, const float* rope_sin, const int32_t* pos,
+                              uint16_t* out, int64_t M, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                              int64_t max_seq, void* stream) {
+  const int st = check_attention_args(q, k, v, cache_k, cache_v, rope_cos, rope_sin, pos, out, M, n_heads, n_kv_heads,
+                                      head_dim, max_seq);
+  if (st != WQ_OK) return st;
+  const size_t need = wq_attention_workspace_bytes(M, n_heads, head_dim, max_seq);
+  if (need > WQ_NOALLOC_SCRATCH_BYTES) return WQ_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need) {
+    const int s2 = scratch_on_current_device(&ws);
+    if (s2 != WQ_OK) return s2;
+  }
+  return wq_rope_attention(q, k, v, cache_k, cache_v, rope_cos, rope_sin, pos, out, M, n_heads, n_kv_heads, head_dim,
+                           max_seq, ws, need ? (size_t)WQ_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int wq_silu_mul(const uint16_t* gate, const uint16_t* up, uint16_t* out, int64_t n, void* stream) {

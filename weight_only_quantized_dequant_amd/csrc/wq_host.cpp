@@ -232,6 +232,7 @@ const char* wq_status_string(int s) {
     case WQ_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case WQ_ERR_DEVICE: return "HIP runtime error at launch";
     case WQ_ERR_RANGE: return "scale overflows fp16";
+    case WQ_ERR_SCRATCH: return "sizes exceed the scratch buffer of a no-allocation call";
     default: return "unknown status";
   }
 }

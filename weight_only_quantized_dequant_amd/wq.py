@@ -90,6 +90,8 @@ def lib():
         L.wq_attention_workspace_bytes.restype = ctypes.c_size_t
         L.wq_rope_attention.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p,
                                         ctypes.c_size_t, _p]
+        L.wq_rope_attention_noalloc.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p]
+        L.wq_rope_attention_noalloc.restype = ctypes.c_int
         L.wq_silu_mul.argtypes = [_p, _p, _p, _i64, _p]
         L.wq_argmax_next.argtypes = [_p, _i64, _i64, _p, _p, _p]
         for name in ("wq_rope_table", "wq_embed", "wq_add_rmsnorm", "wq_rope_attention", "wq_silu_mul", "wq_argmax_next"):
@@ -365,3 +367,26 @@ def wq_argmax_next(logits, m, vocab, tokens, pos, stream=None):
     _need(pos, 4 if sized else 0, "pos", "wq_argmax_next")
     _check(lib().wq_argmax_next(_dev_ptr(logits), m, vocab, _dev_ptr(tokens), _dev_ptr(pos), _stream_ptr(stream)),
            "wq_argmax_next")
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # WQ_NOALLOC_SCRATCH_BYTES of include/wq_decode.h
+
+
+def wq_rope_attention_noalloc(q, k, v, cache_k, cache_v, rope_cos, rope_sin, pos, out, m, n_heads, n_kv_heads, head_dim,
+                              max_seq, stream=None):
+    """Device: wq_rope_attention with its workspace in the library's own per-GPU buffer (no allocation)."""
+    where = "wq_rope_attention_noalloc"
+    sized = min(m, n_heads, n_kv_heads, head_dim, max_seq) >= 1
+    z = (lambda b: b) if sized else (lambda b: 0)
+    _need(q, z(2 * m * n_heads * head_dim), "q", where)
+    _need(out, z(2 * m * n_heads * head_dim), "out", where)
+    _need(k, z(2 * m * n_kv_heads * head_dim), "k", where)
+    _need(v, z(2 * m * n_kv_heads * head_dim), "v", where)
+    _need(cache_k, z(2 * m * max_seq * n_kv_heads * head_dim), "cache_k", where)
+    _need(cache_v, z(2 * m * max_seq * n_kv_heads * head_dim), "cache_v", where)
+    _need(rope_cos, z(4 * max_seq * (head_dim // 2)), "rope_cos", where)
+    _need(rope_sin, z(4 * max_seq * (head_dim // 2)), "rope_sin", where)
+    _need(pos, z(4), "pos", where)
+    _check(lib().wq_rope_attention_noalloc(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(cache_k), _dev_ptr(cache_v),
+                                           _dev_ptr(rope_cos), _dev_ptr(rope_sin), _dev_ptr(pos), _dev_ptr(out), m,
+                                           n_heads, n_kv_heads, head_dim, max_seq, _stream_ptr(stream)), where)
