@@ -8,9 +8,10 @@ it. The product path (the C-ABI library and its Python binding) never imports,
 links or calls anything here, and this package imports nothing from the product.
 
 What it computes: ``y[M,N] = x[M,K] . dequant(Wq)[N,K]^T`` with fp16 (or bfloat16)
-activations and five weight formats (int8 per output row, int4 asymmetric in groups of
-32 along K, FP6 e3m2 per output row, and FP4 e2m1 and FP5 e2m2 per output row as further
-bit widths). These pages describe the method:
+activations and these weight formats: int8 per output row, int4 asymmetric in groups of
+32 along K, FP6 e3m2 per output row (in two layouts: one for gfx950's bf6 convert and
+one split 2+4 into power-of-two-wide parts), and, as further bit widths, FP4 e2m1 and FP5
+e2m2 per output row and int3 asymmetric in groups of 32. These pages describe the method:
 
 * gpt-fast write-up (m.greenbasetech.com): decode is bound by memory bandwidth, and
   int8, then groupwise int4, weight quantization cut the bytes per parameter.
@@ -27,7 +28,7 @@ made here is a reading, and each is listed in the design notes of this repositor
 
 Modules:
   formats   fp16 and bfloat16 rounding, the e3m2, e2m1 and e2m2 code tables and encodings
-  quantize  int8 / int4-g32 / fp6 / fp4 / fp5 quantizers (fp64 arithmetic)
+  quantize  int8 / int4-g32 / int3-g32 / fp6 / fp4 / fp5 quantizers (fp64 arithmetic)
   layout    the packed byte layout: a scalar bit-writer/reader and a vectorised packer
   linear    dequantisation to fp16 or bfloat16 and the fp64 reference linear, plus its error bound
   decode    the decode step around the linears (RMSNorm, rotary embedding, attention over a key/value
@@ -52,7 +53,8 @@ from .formats import (
     e2m2_table,
     e2m2_encode,
 )
-from .quantize import quantize_int8, quantize_int4_g32, quantize_fp6, quantize_fp4, quantize_fp5, OracleRangeError
+from .quantize import (quantize_int8, quantize_int4_g32, quantize_int3_g32, quantize_fp6, quantize_fp4, quantize_fp5,
+                       OracleRangeError)
 from .layout import (
     FMT_F16,
     FMT_W8,
@@ -61,6 +63,8 @@ from .layout import (
     FMT_W4E2M1,
     FMT_BF16,
     FMT_W5E2M2,
+    FMT_W3G32,
+    FMT_W6E3M2_P24,
     packed_bytes,
     scales_count,
     zeros_count,
@@ -83,8 +87,9 @@ from .linear import (
 __all__ = [
     "fp16_bits", "fp16_from_bits", "bf16_bits", "bf16_from_bits", "e3m2_value", "e3m2_table", "e3m2_encode",
     "e2m1_value", "e2m1_table", "e2m1_encode", "e2m2_value", "e2m2_table", "e2m2_encode",
-    "quantize_int8", "quantize_int4_g32", "quantize_fp6", "quantize_fp4", "quantize_fp5", "OracleRangeError",
+    "quantize_int8", "quantize_int4_g32", "quantize_int3_g32", "quantize_fp6", "quantize_fp4", "quantize_fp5", "OracleRangeError",
     "FMT_F16", "FMT_W8", "FMT_W4G32", "FMT_W6E3M2", "FMT_W4E2M1", "FMT_BF16", "FMT_W5E2M2",
+    "FMT_W3G32", "FMT_W6E3M2_P24",
     "packed_bytes", "scales_count", "zeros_count",
     "pack_scalar", "unpack_scalar", "pack_vectorized", "unpack_vectorized",
     "ACT_F16", "ACT_BF16", "dequant_values", "dequant_fp16", "dequant_bf16", "linear_ref", "error_bound",

@@ -26,21 +26,31 @@ kernel consumes them. It gives no concrete layout. The layout used here is:
       8d .. 8d+7, code 8d+2t in nibble t and code 8d+2t+1 in nibble t+4. Bits 128..159
       hold the signs: the sign of code 2p in bit 128+p and of code 2p+1 in bit 144+p
       (p = 0..15), so that one shift puts the signs of a pair at bits 15 and 31.
+    - W3 (12 bytes): three little-endian 32-bit words. Codes 2p and 2p+1 form pair p
+      (p = 0..15); the even code sits in the low 16 bits of a word and the odd code in the
+      high 16 bits at the same offset, so that one mask takes both. Pairs 0..14: pair p sits
+      in word p // 5 at offset o = (0, 3, 6, 10, 13)[p % 5], code 2p in bits o .. o+2 and
+      code 2p+1 in bits 16+o .. 18+o. Pair 15 fills the two bits left in each word: bit b of
+      code 30 in bit 9 of word b and bit b of code 31 in bit 25 of word b (b = 0, 1, 2).
+    - W6 split 2+4 ("P24", 24 bytes; the same e3m2 codes as W6, the two-plus-four split of
+      the FP6-LLM news page): bytes 0..15 hold the low four bits of every code, placed as
+      the W4 codes; bytes 16..19 a little-endian word holding bit 4 of code 2p in bit p and
+      bit 4 of code 2p+1 in bit 16+p (p = 0..15); bytes 20..23 the same for bit 5, the sign.
     - F16 (64 bytes, the unquantized baseline): bytes 2j, 2j+1 hold the fp16 bits of
       weight j, little-endian.
     - BF16 (64 bytes, the unquantized baseline for bfloat16 activations): the same with
       bfloat16 bits.
-* W6 and FP5 only, split by planes: the units of a row are taken 64 at a time ("chunks";
+* W6, P24 and FP5 only, split by planes: the units of a row are taken 64 at a time ("chunks";
   the last chunk of a row may hold fewer, Uc units). In a chunk, bytes 0..15 of its units
   come first, unit after unit (16*Uc bytes), then bytes 16.. of its units (8*Uc bytes for
-  W6, 4*Uc for FP5). A chunk with one unit is therefore stored exactly as that unit. (A
+  W6 and P24, 4*Uc for FP5). A chunk with one unit is therefore stored exactly as that unit. (A
   device lane reads one unit, so each of the two loads of a wave reads one contiguous block.)
-* Metadata stays in logical order: W8/W6/FP4/FP5 scales [N]; W4 scales and zeros [N][K/32],
-  row-major (group g of row n covers the same 32 K as unit g).
+* Metadata stays in logical order: W8/W6/P24/FP4/FP5 scales [N]; W4 and W3 scales and zeros
+  [N][K/32], row-major (group g of row n covers the same 32 K as unit g).
 
 Codes given to and returned by these functions are the logical codes: int8 q for W8,
-0..15 for W4 and FP4, 0..63 for W6, 0..31 for FP5, uint16 fp16 bits for F16, uint16 bfloat16
-bits for BF16.
+0..15 for W4 and FP4, 0..63 for W6 and P24, 0..31 for FP5, 0..7 for W3, uint16 fp16 bits
+for F16, uint16 bfloat16 bits for BF16.
 """
 
 import numpy as np
@@ -52,11 +62,16 @@ FMT_W6E3M2 = 3
 FMT_W4E2M1 = 4
 FMT_BF16 = 5
 FMT_W5E2M2 = 6
+FMT_W3G32 = 7
+FMT_W6E3M2_P24 = 8
 
-_BITS = {FMT_F16: 16, FMT_W8: 8, FMT_W4G32: 4, FMT_W6E3M2: 6, FMT_W4E2M1: 4, FMT_BF16: 16, FMT_W5E2M2: 5}
+_BITS = {FMT_F16: 16, FMT_W8: 8, FMT_W4G32: 4, FMT_W6E3M2: 6, FMT_W4E2M1: 4, FMT_BF16: 16, FMT_W5E2M2: 5,
+         FMT_W3G32: 3, FMT_W6E3M2_P24: 6}
 UNIT = 32
-CHUNK = 64          # units per W6 / FP5 plane chunk
-_PLANED = (FMT_W6E3M2, FMT_W5E2M2)
+CHUNK = 64          # units per W6 / P24 / FP5 plane chunk
+_PLANED = (FMT_W6E3M2, FMT_W5E2M2, FMT_W6E3M2_P24)
+_GROUPED = (FMT_W4G32, FMT_W3G32)   # a scale and a zero point per group of 32 K
+_W3_OFFSETS = (0, 3, 6, 10, 13)     # W3: bit offset of pair p (p < 15) inside word p // 5
 
 
 def _bits(fmt):
@@ -78,23 +93,34 @@ def scales_count(fmt, n, k):
     _bits(fmt)
     if fmt in (FMT_F16, FMT_BF16):
         return 0
-    return n * (k // 32) if fmt == FMT_W4G32 else n
+    return n * (k // 32) if fmt in _GROUPED else n
 
 
 def zeros_count(fmt, n, k):
     """Number of fp16 zero points."""
     _bits(fmt)
-    return n * (k // 32) if fmt == FMT_W4G32 else 0
+    return n * (k // 32) if fmt in _GROUPED else 0
 
 
 def code_fields(fmt, j):
     """[(first bit, width, shift)] of code j inside its unit, counting bits little-endian from the
     unit's first byte: bits shift .. shift+width-1 of the code's stored value go to bits
-    first .. first+width-1 (one field for every format but FP5, whose sign sits apart)."""
+    first .. first+width-1 (one field for every format but FP5 and P24, whose high bits sit
+    apart, and the last pair of W3, whose bits are spread over the three words)."""
     if fmt == FMT_W5E2M2:
         nib_first, _ = code_field(FMT_W4G32, j)
         p, odd = divmod(j, 2)
         return [(nib_first, 4, 0), (128 + 16 * odd + p, 1, 4)]
+    if fmt == FMT_W6E3M2_P24:
+        nib_first, _ = code_field(FMT_W4G32, j)
+        p, odd = divmod(j, 2)
+        return [(nib_first, 4, 0), (128 + 16 * odd + p, 1, 4), (160 + 16 * odd + p, 1, 5)]
+    if fmt == FMT_W3G32:
+        p, odd = divmod(j, 2)
+        if p < 15:
+            word, f = divmod(p, 5)
+            return [(32 * word + 16 * odd + _W3_OFFSETS[f], 3, 0)]
+        return [(32 * b + 16 * odd + 9, 1, b) for b in range(3)]
     first, width = code_field(fmt, j)
     return [(first, width, 0)]
 
@@ -124,7 +150,8 @@ def _stored(fmt, code):
         if not -127 <= code <= 127:
             raise ValueError("int8 code out of range")
         return code + 128
-    limit = {FMT_W4G32: 16, FMT_W6E3M2: 64, FMT_W4E2M1: 16, FMT_W5E2M2: 32, FMT_F16: 65536, FMT_BF16: 65536}[fmt]
+    limit = {FMT_W4G32: 16, FMT_W6E3M2: 64, FMT_W4E2M1: 16, FMT_W5E2M2: 32, FMT_F16: 65536, FMT_BF16: 65536,
+             FMT_W3G32: 8, FMT_W6E3M2_P24: 64}[fmt]
     if not 0 <= code < limit:
         raise ValueError("code out of range")
     return code
@@ -180,8 +207,7 @@ def unpack_scalar(fmt, packed, n, k):
     if packed.size != packed_bytes(fmt, n, k):
         raise ValueError("packed size mismatch")
     ub = unit_bytes(fmt)
-    dtype = {FMT_W8: np.int8, FMT_W4G32: np.uint8, FMT_W6E3M2: np.uint8, FMT_W4E2M1: np.uint8, FMT_F16: np.uint16,
-             FMT_BF16: np.uint16, FMT_W5E2M2: np.uint8}[fmt]
+    dtype = {FMT_W8: np.int8, FMT_F16: np.uint16, FMT_BF16: np.uint16}.get(fmt, np.uint8)
     codes = np.zeros((n, k), dtype=dtype)
     for r in range(n):
         for u in range(k // UNIT):
@@ -246,6 +272,37 @@ def pack_vectorized(fmt, codes):
             sw |= (sgn[:, :, p, 0] << np.uint32(p)) | (sgn[:, :, p, 1] << np.uint32(16 + p))
         units = np.concatenate([words.reshape(n, k // UNIT, 4), sw.reshape(n, k // UNIT, 1)], axis=2)
         return _to_planes(units.astype("<u4").view(np.uint8).reshape(n, k // UNIT, 20)).reshape(-1)
+    if fmt == FMT_W6E3M2_P24:
+        c = codes.astype(np.uint32)
+        if c.max(initial=0) > 63:
+            raise ValueError("fp6 code out of range")
+        mag = (c & 0xF).reshape(n, k // 8, 8)[:, :, _W4_ORDER]
+        words = np.zeros((n, k // 8), dtype=np.uint32)
+        for p in range(8):
+            words |= mag[:, :, p] << np.uint32(4 * p)
+        planes = []
+        for bit in (4, 5):                                     # bit 4 (e2), then bit 5 (sign)
+            b = ((c >> np.uint32(bit)) & 1).reshape(n, k // UNIT, 16, 2)   # [.., p, odd]
+            pw = np.zeros((n, k // UNIT), dtype=np.uint32)
+            for p in range(16):
+                pw |= (b[:, :, p, 0] << np.uint32(p)) | (b[:, :, p, 1] << np.uint32(16 + p))
+            planes.append(pw.reshape(n, k // UNIT, 1))
+        units = np.concatenate([words.reshape(n, k // UNIT, 4)] + planes, axis=2)
+        return _to_planes(units.astype("<u4").view(np.uint8).reshape(n, k // UNIT, 24)).reshape(-1)
+    if fmt == FMT_W3G32:
+        c = codes.astype(np.uint32)
+        if c.max(initial=0) > 7:
+            raise ValueError("int3 code out of range")
+        c = c.reshape(n, k // UNIT, 16, 2)                    # [.., pair, odd]
+        words = np.zeros((n, k // UNIT, 3), dtype=np.uint32)
+        for p in range(15):
+            word, f = divmod(p, 5)
+            o = _W3_OFFSETS[f]
+            words[:, :, word] |= (c[:, :, p, 0] << np.uint32(o)) | (c[:, :, p, 1] << np.uint32(16 + o))
+        for b in range(3):
+            words[:, :, b] |= (((c[:, :, 15, 0] >> np.uint32(b)) & 1) << np.uint32(9)) | \
+                              (((c[:, :, 15, 1] >> np.uint32(b)) & 1) << np.uint32(25))
+        return words.astype("<u4").view(np.uint8).reshape(-1)
     if fmt in (FMT_F16, FMT_BF16):
         return codes.astype(np.uint16).astype("<u2").view(np.uint8).reshape(-1)
     raise ValueError("unknown format %r" % fmt)
@@ -283,6 +340,31 @@ def unpack_vectorized(fmt, packed, n, k):
             sgn[:, :, p, 0] = (sw >> np.uint32(p)) & 1
             sgn[:, :, p, 1] = (sw >> np.uint32(16 + p)) & 1
         return (mag.reshape(n, k) | (sgn.reshape(n, k) << 4)).astype(np.uint8)
+    if fmt == FMT_W6E3M2_P24:
+        units = _from_planes(packed.reshape(n, -1), k // UNIT, 24).copy().view("<u4").reshape(n, k // UNIT, 6)
+        words = units[:, :, :4].reshape(n, k // 8)
+        out = np.zeros((n, k // 8, 8), dtype=np.uint8)
+        for p in range(8):
+            out[:, :, _W4_ORDER[p]] = (words >> np.uint32(4 * p)) & 0xF
+        out = out.reshape(n, k // UNIT, 16, 2)
+        for bit, plane in ((4, 4), (5, 5)):
+            pw = units[:, :, plane]
+            for p in range(16):
+                out[:, :, p, 0] |= (((pw >> np.uint32(p)) & 1) << bit).astype(np.uint8)
+                out[:, :, p, 1] |= (((pw >> np.uint32(16 + p)) & 1) << bit).astype(np.uint8)
+        return out.reshape(n, k)
+    if fmt == FMT_W3G32:
+        words = packed.view("<u4").reshape(n, k // UNIT, 3)
+        out = np.zeros((n, k // UNIT, 16, 2), dtype=np.uint8)
+        for p in range(15):
+            word, f = divmod(p, 5)
+            o = _W3_OFFSETS[f]
+            out[:, :, p, 0] = (words[:, :, word] >> np.uint32(o)) & 7
+            out[:, :, p, 1] = (words[:, :, word] >> np.uint32(16 + o)) & 7
+        for b in range(3):
+            out[:, :, 15, 0] |= (((words[:, :, b] >> np.uint32(9)) & 1) << b).astype(np.uint8)
+            out[:, :, 15, 1] |= (((words[:, :, b] >> np.uint32(25)) & 1) << b).astype(np.uint8)
+        return out.reshape(n, k)
     if fmt in (FMT_F16, FMT_BF16):
         return packed.view("<u2").reshape(n, k).astype(np.uint16)
     raise ValueError("unknown format %r" % fmt)

@@ -19,7 +19,8 @@ fp16: x, the dequantised weights and y are bfloat16, the sum is fp32.
 import numpy as np
 
 from .formats import fp16_bits, fp16_from_bits, bf16_bits, bf16_from_bits, e3m2_table, e2m1_table, e2m2_table
-from .layout import FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, FMT_BF16, FMT_W5E2M2, pack_vectorized
+from .layout import (FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, FMT_BF16, FMT_W5E2M2, FMT_W3G32,
+                     FMT_W6E3M2_P24, pack_vectorized)
 
 # activation types: how x, the dequantised weights and y are stored
 ACT_F16 = "f16"
@@ -27,14 +28,14 @@ ACT_BF16 = "bf16"
 _ROUND = {ACT_F16: fp16_bits, ACT_BF16: bf16_bits}
 _VALUE = {ACT_F16: fp16_from_bits, ACT_BF16: bf16_from_bits}
 _UNIT_ROUNDOFF = {ACT_F16: 2.0 ** -11, ACT_BF16: 2.0 ** -8}
-from .quantize import quantize_int8, quantize_int4_g32, quantize_fp6, quantize_fp4, quantize_fp5
+from .quantize import quantize_int8, quantize_int4_g32, quantize_fp6, quantize_fp4, quantize_fp5, quantize_int3_g32
 
 
 def dequant_values(fmt, codes, scales=None, zeros=None):
     """Logical codes + fp16 metadata bits -> the exact dequantised values as float64 [N,K].
 
-    W8: q * s. W4: (q - z) * s with s, z of the weight's group. W6: e3m2(c) * s.
-    FP4: e2m1(c) * s. FP5: e2m2(c) * s. Each product is exact in float64 (the factors have at
+    W8: q * s. W4 and W3: (q - z) * s with s, z of the weight's group. W6 and P24 (the same
+    codes in another layout): e3m2(c) * s. FP4: e2m1(c) * s. FP5: e2m2(c) * s. Each product is exact in float64 (the factors have at
     most 11 and 8 significant bits). Not defined for the unquantized formats.
     """
     codes = np.asarray(codes)
@@ -42,11 +43,11 @@ def dequant_values(fmt, codes, scales=None, zeros=None):
     s = fp16_from_bits(scales)
     if fmt == FMT_W8:
         v = codes.astype(np.float64) * s.reshape(n, 1)
-    elif fmt == FMT_W4G32:
+    elif fmt in (FMT_W4G32, FMT_W3G32):
         z = fp16_from_bits(zeros).reshape(n, k // 32, 1)
         q = codes.astype(np.float64).reshape(n, k // 32, 32)
         v = ((q - z) * s.reshape(n, k // 32, 1)).reshape(n, k)
-    elif fmt == FMT_W6E3M2:
+    elif fmt in (FMT_W6E3M2, FMT_W6E3M2_P24):
         v = e3m2_table()[codes.astype(np.int64)] * s.reshape(n, 1)
     elif fmt == FMT_W4E2M1:
         v = e2m1_table()[codes.astype(np.int64)] * s.reshape(n, 1)
@@ -108,7 +109,9 @@ def quantize_and_pack(fmt, w):
         z = np.zeros(0, dtype=np.uint16)
     elif fmt == FMT_W4G32:
         codes, s, z = quantize_int4_g32(w)
-    elif fmt == FMT_W6E3M2:
+    elif fmt == FMT_W3G32:
+        codes, s, z = quantize_int3_g32(w)
+    elif fmt in (FMT_W6E3M2, FMT_W6E3M2_P24):
         codes, s = quantize_fp6(w)
         z = np.zeros(0, dtype=np.uint16)
     elif fmt == FMT_W4E2M1:

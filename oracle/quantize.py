@@ -15,6 +15,10 @@ The pages give no formulas. The readings are:
   ``hi = max(max w, 0)``, ``s = fp16((hi - lo) / 15)``, ``z = clamp(rint(-lo / s), 0, 15)``,
   ``q = clamp(rint(w / s) + z, 0, 15)``. The zero point z is an integer stored as fp16,
   and the dequantised weight is ``(q - z) * s``.
+* int3 (a further bit width through the same design, as the FP6-LLM news page
+  (m.zhengruan.com), section "重新设计内核方案", has one kernel design serve several bit
+  widths; the page names no 3-bit format): int4's rule with 7 in place of 15, i.e.
+  ``s = fp16((hi - lo) / 7)``, ``z = clamp(rint(-lo / s), 0, 7)``, ``q = clamp(rint(w / s) + z, 0, 7)``.
 * FP6: one fp16 scale per output row, ``s = fp16(max|w| / 28)``, code = e3m2 encoding of
   ``w / s`` (nearest, ties to even code, saturating at 28).
 * FP4 (a further bit width through the same design; the page names none): e2m1 with one
@@ -67,6 +71,16 @@ def quantize_int8(w):
 
 def quantize_int4_g32(w):
     """int4 asymmetric, group 32 along K. Returns (q uint8 [N,K] in 0..15, scale bits [N,K/32], zero bits [N,K/32])."""
+    return _asymmetric_g32(w, 15)
+
+
+def quantize_int3_g32(w):
+    """int3 asymmetric, group 32 along K. Returns (q uint8 [N,K] in 0..7, scale bits [N,K/32], zero bits [N,K/32])."""
+    return _asymmetric_g32(w, 7)
+
+
+def _asymmetric_g32(w, top):
+    """Codes 0..top with an fp16 scale and an integer zero point per group of 32 consecutive K."""
     w = _check_w(w)
     n, k = w.shape
     if k % 32:
@@ -74,14 +88,14 @@ def quantize_int4_g32(w):
     g = w.reshape(n, k // 32, 32)
     lo = np.minimum(g.min(axis=2), 0.0)
     hi = np.maximum(g.max(axis=2), 0.0)
-    s_bits = _scale16((hi - lo) / 15.0)
+    s_bits = _scale16((hi - lo) / float(top))
     s = fp16_from_bits(s_bits)
     q = np.zeros(g.shape, dtype=np.uint8)
     z = np.zeros(s.shape, dtype=np.float64)
     nz = s > 0
     # + 0.0 turns the -0 that rint(-0/s) yields for a group with lo = 0 into the integer 0
-    z[nz] = np.clip(np.rint(-lo[nz] / s[nz]), 0, 15) + 0.0
-    q[nz] = np.clip(np.rint(g[nz] / s[nz][:, None]) + z[nz][:, None], 0, 15).astype(np.uint8)
+    z[nz] = np.clip(np.rint(-lo[nz] / s[nz]), 0, top) + 0.0
+    q[nz] = np.clip(np.rint(g[nz] / s[nz][:, None]) + z[nz][:, None], 0, top).astype(np.uint8)
     return q.reshape(n, k), s_bits, fp16_bits(z)
 
 

@@ -307,17 +307,18 @@ def brute_int8_row(w_row):
     return codes, fraction_to_f16_bits(s)
 
 
-def brute_int4_group(w_grp):
-    """(codes, scale bits, zero bits) for one group of 32 fp32 weights."""
+def brute_int4_group(w_grp, top=15):
+    """(codes, scale bits, zero bits) for one group of 32 fp32 weights; codes 0..top (15 for int4,
+    7 for int3)."""
     fw = [Fraction(float(v)) for v in w_grp]
     lo = min(min(fw), Fraction(0))
     hi = max(max(fw), Fraction(0))
-    s = fp16_round((hi - lo) / 15)
+    s = fp16_round((hi - lo) / top)
     if s == 0:
         return [0] * len(w_grp), 0, 0
-    # zero point: the integer 0..15 nearest to -lo/s, ties to even
+    # zero point: the integer 0..top nearest to -lo/s, ties to even
     best = None
-    for z in range(16):
+    for z in range(top + 1):
         d = abs(-lo / s - z)
         if best is None or d < best[0] or (d == best[0] and z % 2 == 0):
             best = (d, z)
@@ -325,7 +326,7 @@ def brute_int4_group(w_grp):
     codes = []
     for fv in fw:
         best = None
-        for q in range(16):
+        for q in range(top + 1):
             d = abs(fv / s - (q - z))
             if best is None or d < best[0] or (d == best[0] and (q - z) % 2 == 0):
                 best = (d, q)
@@ -364,13 +365,13 @@ def check_quantizer(fmt_name, quant_fn, w):
             if int(s[r]) != bs or [int(v) for v in q[r]] != bq:
                 return False
         return True
-    if fmt_name == "w4":
+    if fmt_name in ("w4", "w3"):
         q, s, z = out
         s = np.asarray(s).reshape(n, k // 32)
         z = np.asarray(z).reshape(n, k // 32)
         for r in range(n):
             for g in range(k // 32):
-                bq, bs, bz = brute_int4_group(w[r, 32 * g:32 * g + 32])
+                bq, bs, bz = brute_int4_group(w[r, 32 * g:32 * g + 32], 15 if fmt_name == "w4" else 7)
                 if int(s[r, g]) != bs or int(z[r, g]) != bz:
                     return False
                 if [int(v) for v in q[r, 32 * g:32 * g + 32]] != bq:
@@ -411,10 +412,10 @@ def exact_dequant(fmt_name, code, scale_bits, zero_bits=0, act="f16"):
     s = f16_bits_to_fraction(scale_bits)
     if fmt_name == "w8":
         v = code * s
-    elif fmt_name == "w4":
+    elif fmt_name in ("w4", "w3"):
         v = (code - f16_bits_to_fraction(zero_bits)) * s
-    elif fmt_name in ("w6", "fp4", "fp5"):
-        mag, neg = {"w6": golden_e3m2, "fp4": golden_e2m1, "fp5": golden_e2m2}[fmt_name]()[code]
+    elif fmt_name in ("w6", "p24", "fp4", "fp5"):
+        mag, neg = {"w6": golden_e3m2, "p24": golden_e3m2, "fp4": golden_e2m1, "fp5": golden_e2m2}[fmt_name]()[code]
         v = (-mag if neg else mag) * s
         if v == 0:
             return 0x8000 if (neg and s > 0) or (not neg and s < 0) else 0

@@ -8,7 +8,7 @@ rule or a transposed operand, rather than agreeing with whatever the oracle comp
 import numpy as np
 
 import oracle
-from oracle import FMT_W4G32, FMT_W6E3M2
+from oracle import FMT_W4G32, FMT_W6E3M2, FMT_W3G32, FMT_W6E3M2_P24
 from tests import pins
 from tests.test_oracle_pins import _adversarial, _bf16_probe_values
 
@@ -24,6 +24,28 @@ def test_pins_accept_the_oracle():
     assert pins.check_quantizer("fp4", oracle.quantize_fp4, w)
     assert pins.check_e2m2_table(oracle.e2m2_value)
     assert pins.check_quantizer("fp5", oracle.quantize_fp5, w)
+    assert pins.check_quantizer("w3", oracle.quantize_int3_g32, w)
+
+
+def test_int3_with_the_int4_divisor_is_caught():
+    def bad_quant(w):   # the int4 rule (15 steps) clamped to 0..7
+        q, s, z = oracle.quantize_int4_g32(w)
+        return np.minimum(q, 7), s, np.minimum(oracle.fp16_from_bits(z), 7).astype(np.float16).view(np.uint16)
+    rng = np.random.default_rng(11)
+    assert not pins.check_quantizer("w3", bad_quant, _adversarial(8, 64, rng))
+
+
+def test_int3_codes_truncated_is_caught():
+    def bad_quant(w):   # codes rounded toward zero instead of to nearest
+        q, s, z = oracle.quantize_int3_g32(w)
+        n, k = w.shape
+        sv = oracle.fp16_from_bits(s).reshape(n, k // 32, 1)
+        zv = oracle.fp16_from_bits(z).reshape(n, k // 32, 1)
+        g = w.astype(np.float64).reshape(n, k // 32, 32)
+        q2 = np.clip(np.trunc(g / np.where(sv > 0, sv, 1)) + zv, 0, 7).astype(np.uint8)
+        return q2.reshape(n, k), s, z
+    rng = np.random.default_rng(11)
+    assert not pins.check_quantizer("w3", bad_quant, _adversarial(8, 64, rng))
 
 
 def test_e2m2_wrong_bias_is_caught():
@@ -257,3 +279,49 @@ def test_bf16_linear_reading_fp16_bits_is_caught():
     bad = lambda a, b: oracle.linear_ref(a, b)                         # the bits taken as fp16
     assert pins.check_linear(good, x, w, value=pins.bf16_bits_to_fraction)
     assert not pins.check_linear(bad, x, w, value=pins.bf16_bits_to_fraction)
+
+
+def test_w3_offsets_in_order_are_caught():
+    # pairs at offsets 0, 3, 6, 9, 12 (packed tight, the spread pair elsewhere) must not match the fixture
+    for name, codes, expected in pins.golden_pack_examples():
+        if name != "W3":
+            continue
+        c = np.array(codes, dtype=np.uint32).reshape(16, 2)
+        words = [0, 0, 0]
+        for p in range(15):
+            word, f = divmod(p, 5)
+            words[word] |= int(c[p, 0]) << (3 * f) | int(c[p, 1]) << (16 + 3 * f)
+        for b in range(3):
+            words[b] |= ((int(c[15, 0]) >> b) & 1) << 15 | ((int(c[15, 1]) >> b) & 1) << 31
+        assert b"".join(w.to_bytes(4, "little") for w in words) != expected
+
+
+def test_w3_spread_pair_bit_order_is_caught():
+    # bit b of the last pair in word 2 - b instead of word b
+    for name, codes, expected in pins.golden_pack_examples():
+        if name != "W3x1":
+            continue
+        words = [0, 0, 0]
+        for b in range(3):
+            words[2 - b] |= ((codes[30] >> b) & 1) << 9 | ((codes[31] >> b) & 1) << 25
+        assert b"".join(w.to_bytes(4, "little") for w in words) != expected
+        assert expected == bytes(oracle.pack_scalar(FMT_W3G32, np.array([codes])))
+
+
+def test_p24_planes_swapped_are_caught():
+    # the sign word before the bit-4 word must not match the fixture
+    for name, codes, expected in pins.golden_pack_examples():
+        if name != "P24":
+            continue
+        good = bytes(oracle.pack_scalar(FMT_W6E3M2_P24, np.array([codes])))
+        bad = good[:16] + good[20:24] + good[16:20]
+        assert good == expected and bad != expected
+
+
+def test_p24_units_stored_whole_is_caught():
+    for name, codes, expected in pins.golden_pack_examples():
+        if name != "P24x2":
+            continue
+        whole = b"".join(oracle.pack_scalar(FMT_W6E3M2_P24, np.array([codes[32 * i:32 * i + 32]])).tobytes()
+                         for i in range(2))
+        assert whole != expected and len(whole) == len(expected)

@@ -7,11 +7,12 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, FMT_BF16, FMT_W5E2M2
+from oracle import (FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, FMT_BF16, FMT_W5E2M2, FMT_W3G32,
+                    FMT_W6E3M2_P24)
 from tests import pins
 
 FMTS = {"w8": FMT_W8, "w4": FMT_W4G32, "w6": FMT_W6E3M2, "f16": FMT_F16, "fp4": FMT_W4E2M1, "bf16": FMT_BF16,
-        "fp5": FMT_W5E2M2}
+        "fp5": FMT_W5E2M2, "w3": FMT_W3G32, "p24": FMT_W6E3M2_P24}
 
 
 # ------------------------------------------------------------------ e3m2
@@ -228,12 +229,12 @@ def _adversarial(n, k, rng):
     return w
 
 
-@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4", "fp5"])
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4", "fp5", "w3"])
 def test_quantizer_vs_brute_force(name):
     rng = np.random.default_rng(11)
     w = _adversarial(8, 64, rng)
     fn = {"w8": oracle.quantize_int8, "w4": oracle.quantize_int4_g32, "w6": oracle.quantize_fp6,
-          "fp4": oracle.quantize_fp4, "fp5": oracle.quantize_fp5}[name]
+          "fp4": oracle.quantize_fp4, "fp5": oracle.quantize_fp5, "w3": oracle.quantize_int3_g32}[name]
     assert pins.check_quantizer(name, fn, w)
 
 
@@ -260,6 +261,21 @@ def test_int4_zero_point_and_range():
     assert sv == float(np.float16(0.2))
     assert float(np.uint16(z[0, 0]).view(np.float16)) == 5.0
     assert q[0, 0] == 0 and q[0, 1] == 15 and q[0, 2] == 5    # 0 maps to the zero point
+
+
+def test_int3_zero_point_and_range():
+    # group spanning [-1, 2.5]: s = fp16(3.5/7) = 0.5 exactly, z = rint(1/0.5) = 2;
+    # 0.25 / 0.5 = 0.5 is a tie: rint -> 0, code 2; 0.75 / 0.5 = 1.5 -> 2, code 4
+    w = np.zeros((1, 32), dtype=np.float32)
+    w[0, 0], w[0, 1], w[0, 3], w[0, 4] = -1.0, 2.5, 0.25, 0.75
+    q, s, z = oracle.quantize_int3_g32(w)
+    assert int(s[0, 0]) == 0x3800                             # fp16 0.5
+    assert float(np.uint16(z[0, 0]).view(np.float16)) == 2.0
+    assert q[0, :5].tolist() == [0, 7, 2, 2, 4]
+    # all-positive group: lo = 0, z = 0, the largest weight takes code 7
+    w = np.linspace(0.0, 7.0, 32, dtype=np.float32).reshape(1, 32)
+    q, s, z = oracle.quantize_int3_g32(w)
+    assert int(z[0, 0]) == 0 and q[0, 0] == 0 and q[0, 31] == 7
 
 
 def test_fp6_saturation_and_negative_zero():
@@ -314,7 +330,7 @@ def test_pack_matches_hand_derived_bytes():
         assert bytes(oracle.pack_vectorized(fmt, c)) == expected, name
 
 
-@pytest.mark.parametrize("name", ["w8", "w4", "w6", "f16", "fp4", "bf16", "fp5"])
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "f16", "fp4", "bf16", "fp5", "w3", "p24"])
 @pytest.mark.parametrize("n,k", [(3, 96), (2, 32 * 130)])       # 130 units: two full chunks of 64 and one of 2
 def test_pack_scalar_equals_vectorized_and_round_trips(name, n, k):
     fmt = FMTS[name]
@@ -323,16 +339,18 @@ def test_pack_scalar_equals_vectorized_and_round_trips(name, n, k):
         codes = rng.integers(-127, 128, (n, k)).astype(np.int8)
     elif name in ("w4", "fp4"):
         codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
-    elif name == "w6":
+    elif name in ("w6", "p24"):
         codes = rng.integers(0, 64, (n, k)).astype(np.uint8)
     elif name == "fp5":
         codes = rng.integers(0, 32, (n, k)).astype(np.uint8)
+    elif name == "w3":
+        codes = rng.integers(0, 8, (n, k)).astype(np.uint8)
     else:
         codes = rng.integers(0, 65536, (n, k)).astype(np.uint16)
     a = oracle.pack_scalar(fmt, codes)
     b = oracle.pack_vectorized(fmt, codes)
     assert a.size == oracle.packed_bytes(fmt, n, k) == n * k * {"w8": 8, "w4": 4, "w6": 6, "f16": 16, "fp4": 4,
-                                                                "bf16": 16, "fp5": 5}[name] // 8
+                                                                "bf16": 16, "fp5": 5, "w3": 3, "p24": 6}[name] // 8
     assert np.array_equal(a, b)
     assert np.array_equal(oracle.unpack_scalar(fmt, a, n, k), codes)
     assert np.array_equal(oracle.unpack_vectorized(fmt, b, n, k), codes)
@@ -346,10 +364,23 @@ def test_metadata_counts():
     assert oracle.scales_count(FMT_W4E2M1, 7, 64) == 7 and oracle.zeros_count(FMT_W4E2M1, 7, 64) == 0
     assert oracle.scales_count(FMT_BF16, 7, 64) == 0 and oracle.zeros_count(FMT_BF16, 7, 64) == 0
     assert oracle.scales_count(FMT_W5E2M2, 7, 64) == 7 and oracle.zeros_count(FMT_W5E2M2, 7, 64) == 0
+    assert oracle.scales_count(FMT_W3G32, 7, 64) == 14 and oracle.zeros_count(FMT_W3G32, 7, 64) == 14
+    assert oracle.scales_count(FMT_W6E3M2_P24, 7, 64) == 7 and oracle.zeros_count(FMT_W6E3M2_P24, 7, 64) == 0
+
+
+def test_p24_holds_the_w6_codes():
+    # the 2+4 split stores the same e3m2 codes and scales as W6; only the bytes differ
+    rng = np.random.default_rng(23)
+    w = rng.standard_normal((5, 32 * 67)).astype(np.float32)
+    pa, sa, za, ca = oracle.quantize_and_pack(FMT_W6E3M2, w)
+    pb, sb, zb, cb = oracle.quantize_and_pack(FMT_W6E3M2_P24, w)
+    assert np.array_equal(ca, cb) and np.array_equal(sa, sb) and pa.size == pb.size
+    assert not np.array_equal(pa, pb)
+    assert np.array_equal(oracle.unpack_vectorized(FMT_W6E3M2_P24, pb, 5, 32 * 67), ca)
 
 
 # ------------------------------------------------------------------ dequant
-@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4", "fp5"])
+@pytest.mark.parametrize("name", ["w8", "w4", "w6", "fp4", "fp5", "w3", "p24"])
 def test_dequant_exact_vs_fraction_and_fp32(name):
     fmt = FMTS[name]
     rng = np.random.default_rng(9)
@@ -359,21 +390,23 @@ def test_dequant_exact_vs_fraction_and_fp32(name):
     d = oracle.dequant_fp16(fmt, codes, s, z)
     n, k = codes.shape
     sv = np.asarray(s).reshape(n, -1)
-    zv = np.asarray(z).reshape(n, -1) if name == "w4" else None
+    grouped = name in ("w4", "w3")
+    zv = np.asarray(z).reshape(n, -1) if grouped else None
     for r in range(n):
         for c in range(k):
-            g = c // 32 if name == "w4" else 0
+            g = c // 32 if grouped else 0
             want = pins.exact_dequant(name, int(codes[r, c]), int(sv[r, g]), int(zv[r, g]) if zv is not None else 0)
             got = int(d[r, c])
-            assert got == want or (want in (0, 0x8000) and got in (0, 0x8000) and name not in ("w6", "fp4", "fp5")), (r, c)
+            assert got == want or (want in (0, 0x8000) and got in (0, 0x8000) and
+                                   name not in ("w6", "p24", "fp4", "fp5")), (r, c)
     # the product is exact in fp32 as well, so an fp32 multiply then one rounding agrees bit for bit
     s32 = oracle.fp16_from_bits(sv).astype(np.float32)
     if name == "w8":
         v32 = codes.astype(np.float32) * np.repeat(s32, k, axis=1)
-    elif name == "w4":
+    elif grouped:
         zz = oracle.fp16_from_bits(zv).astype(np.float32)
         v32 = (codes.astype(np.float32) - np.repeat(zz, 32, axis=1)) * np.repeat(s32, 32, axis=1)
-    elif name == "w6":
+    elif name in ("w6", "p24"):
         v32 = oracle.e3m2_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
     elif name == "fp5":
         v32 = oracle.e2m2_table().astype(np.float32)[codes] * np.repeat(s32, k, axis=1)
