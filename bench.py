@@ -42,7 +42,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from weight_only_quantized_dequant_amd import inputs, wq  # noqa: E402
+from weight_only_quantized_dequant_amd import decode, inputs, wq  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "weight-stream HBM GB/s (% of peak) for W8/W6/W4-A16 linear, M=1..16"
@@ -50,6 +50,8 @@ FMT_OF = {"w8": wq.FMT_W8, "w4g32": wq.FMT_W4G32, "w6e3m2": wq.FMT_W6E3M2, "w4e2
           "w5e2m2": wq.FMT_W5E2M2, "f16": wq.FMT_F16}
 # the same weights with bfloat16 activations ("_bf16"), and plain bfloat16 weights as their baseline
 FMT_OF.update({k + "_bf16": v | wq.ACT_BF16 for k, v in list(FMT_OF.items()) if k != "f16"})
+# int3 and the 2+4 split FP6 layout (fp16 activations only)
+FMT_OF.update({"w3g32": wq.FMT_W3G32, "w6e3m2_p24": wq.FMT_W6E3M2_P24})
 FMT_OF["bf16"] = wq.FMT_BF16 | wq.ACT_BF16
 
 
@@ -169,17 +171,7 @@ def pack(fmt, w):
     fmt &= 0xFF
     if fmt == wq.FMT_BF16:
         return bf16_bits(w).view(np.uint8).reshape(-1), None, None
-    if fmt == wq.FMT_W8:
-        return wq.wq_pack_int8(w) + (None,)
-    if fmt == wq.FMT_W4G32:
-        return wq.wq_pack_int4(w)
-    if fmt == wq.FMT_W6E3M2:
-        return wq.wq_pack_fp6(w) + (None,)
-    if fmt == wq.FMT_W4E2M1:
-        return wq.wq_pack_fp4(w) + (None,)
-    if fmt == wq.FMT_W5E2M2:
-        return wq.wq_pack_fp5(w) + (None,)
-    return w.astype(np.float16).view(np.uint8).reshape(-1), None, None
+    return decode.pack_host(fmt, w)
 
 
 class Linear:

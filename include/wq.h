@@ -30,6 +30,13 @@
  *                  nearest e2m2 to w/s (ties to even code, saturating); w^ = e2m2(code)*s.
  *                  Another further bit width (the FP6-LLM news page, section "重新设计内核方案",
  *                  describes one kernel design for several bit widths and names none besides 6).
+ *   WQ_FMT_W3G32   int3, asymmetric, groups of 32 consecutive K: int4's rule with 7 in place of
+ *                  15 (s = fp16((hi-lo)/7), z = clamp(rint(-lo/s), 0, 7), q = clamp(rint(w/s)+z,
+ *                  0, 7)); w^ = (q-z)*s. A further bit width, as for FP4 and FP5.
+ *   WQ_FMT_W6E3M2_P24  the FP6 e3m2 codes and scales of WQ_FMT_W6E3M2 in a second layout, each
+ *                  code split into a 4-bit and a 2-bit part (the "6 = 2 + 4" split of the
+ *                  FP6-LLM news page, section "重新设计内核方案"), stitched back together with
+ *                  bit operations instead of gfx950's bf6 convert: the two FP6 layouts side by side.
  *   WQ_FMT_F16     plain fp16 weights W[N,K] (the unquantized baseline); no metadata.
  *   WQ_FMT_BF16    plain bfloat16 weights W[N,K], the unquantized baseline for bfloat16
  *                  activations (WQ_ACT_BF16 below); no metadata.
@@ -51,10 +58,18 @@
  *       a little-endian u32 of signs, the sign of code 2p in bit p and of code 2p+1 in bit
  *       16+p. Stored split by planes in chunks of 64 units as W6 (bytes 0..15 of the chunk's
  *       units, then bytes 16..19 of the same units).
+ *   W3  12 B: three little-endian u32. Codes 2p, 2p+1 form pair p; the even code sits in the low
+ *       half of a word and the odd one in the high half at the same offset. Pair p < 15 is in
+ *       word p / 5 at offset o = 0, 3, 6, 10, 13 for p % 5 = 0..4 (code 2p in bits o..o+2,
+ *       code 2p+1 in bits 16+o..18+o); bit b of code 30 is bit 9 and bit b of code 31 bit 25
+ *       of word b. Units stored whole.
+ *   P24 24 B: bytes 0..15 hold the low four bits of the codes placed as W4 codes; bytes 16..19 a
+ *       little-endian u32 with bit 4 of code 2p in bit p and of code 2p+1 in bit 16+p; bytes
+ *       20..23 the same for bit 5 (the sign). Stored split by planes as W6.
  *   F16 64 B: fp16 weight j at bytes 2j..2j+1 (so F16 is the plain row-major matrix); BF16 the same
  *       with bfloat16 bits.
- * So packed_w is exactly N*K*bits/8 bytes. scales: W8/W6/FP4/FP5 [N]; W4 [N][K/32] row-major.
- * zeros: W4 [N][K/32] row-major; otherwise unused (may be NULL). fp16 values are passed
+ * So packed_w is exactly N*K*bits/8 bytes. scales: W8/W6/P24/FP4/FP5 [N]; W4 and W3 [N][K/32]
+ * row-major. zeros: W4 and W3 [N][K/32] row-major; otherwise unused (may be NULL). fp16 values are passed
  * as uint16_t bit patterns.
  *
  * Activations: by default x, y and dequantized weights are fp16. OR-ing WQ_ACT_BF16 into the
@@ -63,7 +78,8 @@
  * and the speed-up strategies page, sharktoolz.top, section 4). The packed weights and their fp16 metadata are the same for both;
  * the product still accumulates in fp32, and the dequantized value of a weight is its exact
  * value rounded once to bfloat16. Valid codes with the flag: W8, W4G32, W6E3M2, W4E2M1, W5E2M2, BF16;
- * F16 weights take fp16 activations only and BF16 weights bfloat16 ones (else WQ_ERR_FMT).
+ * F16, W3G32 and W6E3M2_P24 weights take fp16 activations only and BF16 weights bfloat16 ones
+ * (else WQ_ERR_FMT).
  * The size calls ignore the flag.
  *
  * Conventions for every call:
@@ -88,7 +104,7 @@ extern "C" {
 
 typedef enum {
   WQ_FMT_F16 = 0, WQ_FMT_W8 = 1, WQ_FMT_W4G32 = 2, WQ_FMT_W6E3M2 = 3, WQ_FMT_W4E2M1 = 4, WQ_FMT_BF16 = 5,
-  WQ_FMT_W5E2M2 = 6
+  WQ_FMT_W5E2M2 = 6, WQ_FMT_W3G32 = 7, WQ_FMT_W6E3M2_P24 = 8
 } wq_fmt;
 
 /* Activation-type flag, OR-ed into a format code: bfloat16 x and y instead of fp16. */
@@ -137,6 +153,8 @@ int wq_pack_int4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* s
 int wq_pack_fp6(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
 int wq_pack_fp4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
 int wq_pack_fp5(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
+int wq_pack_int3(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales, uint16_t* zeros);
+int wq_pack_fp6_p24(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales);
 
 /* Inverse of the packers' layout step, on the host: packed -> logical codes [N,K]
  * (int8 for W8; 0..15 for W4 and FP4; 0..63 for W6; 0..31 for FP5, one byte each; uint16 fp16 bits for F16) and

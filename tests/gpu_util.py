@@ -56,6 +56,11 @@ def pack_with_library(fmt, w):
     if fmt == wq.FMT_W5E2M2:
         p, s = wq.wq_pack_fp5(w)
         return p, s, None
+    if fmt == wq.FMT_W3G32:
+        return wq.wq_pack_int3(w)
+    if fmt == wq.FMT_W6E3M2_P24:
+        p, s = wq.wq_pack_fp6_p24(w)
+        return p, s, None
     if fmt == wq.FMT_F16:
         return np.asarray(w, dtype=np.float32).astype(np.float16).view(np.uint8).reshape(-1), None, None
     if fmt == wq.FMT_BF16:

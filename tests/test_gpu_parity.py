@@ -17,9 +17,10 @@ from tests.gpu_util import DeviceWeights, check_linear, dev, host_bits, oracle_r
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_F16, wq.FMT_W5E2M2]
+FMTS = [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_F16, wq.FMT_W5E2M2, wq.FMT_W3G32,
+        wq.FMT_W6E3M2_P24]
 FMT_ID = {wq.FMT_W8: "w8", wq.FMT_W4G32: "w4", wq.FMT_W6E3M2: "w6", wq.FMT_W4E2M1: "fp4", wq.FMT_F16: "f16",
-          wq.FMT_W5E2M2: "fp5"}
+          wq.FMT_W5E2M2: "fp5", wq.FMT_W3G32: "w3", wq.FMT_W6E3M2_P24: "p24"}
 
 
 def _weights(n, k, seed, adversarial=True):
@@ -49,8 +50,8 @@ def test_dequant_bit_exact(fmt, n, k):
     assert np.array_equal(got, want), "%d of %d differ" % (int((got != want).sum()), got.size)
 
 
-@pytest.mark.parametrize("fmt,ncodes", [(wq.FMT_W6E3M2, 64), (wq.FMT_W4E2M1, 16), (wq.FMT_W5E2M2, 32)],
-                         ids=["w6", "fp4", "fp5"])
+@pytest.mark.parametrize("fmt,ncodes", [(wq.FMT_W6E3M2, 64), (wq.FMT_W4E2M1, 16), (wq.FMT_W5E2M2, 32),
+                                        (wq.FMT_W6E3M2_P24, 64)], ids=["w6", "fp4", "fp5", "p24"])
 def test_dequant_all_codes(fmt, ncodes):
     # every code in every position of a unit (codes run 0, 1, ..., shifted by one per row), at
     # scale 1, at a non-power-of-two scale and at a subnormal scale
@@ -64,6 +65,25 @@ def test_dequant_all_codes(fmt, ncodes):
         wq.wq_dequant(fmt, dev(packed), dev(sc), None, out, rows, 64)
         torch.cuda.synchronize()
         want = oracle.dequant_fp16(fmt, codes, sc)
+        assert np.array_equal(host_bits(out), want), hex(s)
+
+
+@pytest.mark.parametrize("fmt,ncodes", [(wq.FMT_W4G32, 16), (wq.FMT_W3G32, 8)], ids=["w4", "w3"])
+def test_dequant_all_codes_and_zero_points(fmt, ncodes):
+    # every code in every position of a unit with every zero point, at scale 1, at a
+    # non-power-of-two scale and at a subnormal scale (group g of row r: zero point (r + g) mod ncodes)
+    torch = torch_cuda()
+    rows, k = ncodes, 64 * ncodes
+    codes = ((np.arange(k)[None, :] + np.arange(rows)[:, None]) % ncodes).astype(np.uint8)
+    packed = oracle.pack_vectorized(fmt, codes)
+    g = k // 32
+    zeros = ((np.arange(g)[None, :] + np.arange(rows)[:, None]) % ncodes).astype(np.float16).view(np.uint16)
+    for s in (0x3C00, 0x2E66, 0x0003):
+        sc = np.full((rows, g), s, dtype=np.uint16)
+        out = torch.empty((rows, k), dtype=torch.int16, device="cuda:0")
+        wq.wq_dequant(fmt, dev(packed), dev(sc), dev(zeros), out, rows, k)
+        torch.cuda.synchronize()
+        want = oracle.dequant_fp16(fmt, codes, sc, zeros)
         assert np.array_equal(host_bits(out), want), hex(s)
 
 
@@ -165,6 +185,9 @@ FULL = [
     ("llama7b_w5e2m2_linears", wq.FMT_W5E2M2),
     ("llama7b_w8_linears", wq.FMT_W8),
     ("llama7b_w6e3m2_linears", wq.FMT_W6E3M2),
+    ("llama7b_w3g32_linears", wq.FMT_W3G32),
+    ("llama70b_w6e3m2_p24_linears", wq.FMT_W6E3M2_P24),
+    ("llama7b_w6e3m2_p24_linears", wq.FMT_W6E3M2_P24),
 ]
 
 
@@ -276,3 +299,19 @@ def test_library_loaded_before_torch_in_a_fresh_process():
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=100)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.split()[0] == "ok" and int(r.stdout.split()[1]) > 0, r.stdout
+
+
+@pytest.mark.parametrize("n,k", [(37, 4256), (8200, 2304), (1024, 8192)])
+@pytest.mark.parametrize("m", [1, 3, 4, 8, 16, 33, 70])
+def test_p24_layout_gives_the_w6_outputs_bit_for_bit(n, k, m):
+    # the same weights in the two FP6 layouts: the 2+4 split decodes e3m2(code) * 2^-12 and folds
+    # the 2^12 into the row scale, so every fp32 sum is the W6 one scaled by a power of two and
+    # the rounded outputs agree bit for bit (each kernel family against itself)
+    w = _weights(n, k, 5 * n + k)
+    _, x = inputs.small_case(3000 + n + m, 1, k, m)
+    a, b = DeviceWeights(wq.FMT_W6E3M2, w), DeviceWeights(wq.FMT_W6E3M2_P24, w)
+    assert np.array_equal(wq.wq_unpack(wq.FMT_W6E3M2, a.packed_host, a.scales_host, None, n, k)[0],
+                          wq.wq_unpack(wq.FMT_W6E3M2_P24, b.packed_host, b.scales_host, None, n, k)[0])
+    ya, yb = a.linear(x), b.linear(x)
+    assert np.array_equal(ya, yb), "%d of %d differ (%s)" % (int((ya != yb).sum()), ya.size,
+                                                            wq.wq_linear_kernel_name(wq.FMT_W6E3M2_P24, m, n, k))

@@ -20,9 +20,9 @@ pytestmark = pytest.mark.gpu
 BF = wq.ACT_BF16
 CODES = [(wq.FMT_F16, 0), (wq.FMT_W8, 0), (wq.FMT_W4G32, 0), (wq.FMT_W6E3M2, 0), (wq.FMT_W4E2M1, 0),
          (wq.FMT_W8, BF), (wq.FMT_W4G32, BF), (wq.FMT_W6E3M2, BF), (wq.FMT_W4E2M1, BF), (wq.FMT_BF16, BF),
-         (wq.FMT_W5E2M2, 0), (wq.FMT_W5E2M2, BF)]
+         (wq.FMT_W5E2M2, 0), (wq.FMT_W5E2M2, BF), (wq.FMT_W3G32, 0), (wq.FMT_W6E3M2_P24, 0)]
 NAMES = {wq.FMT_F16: "f16", wq.FMT_W8: "w8", wq.FMT_W4G32: "w4", wq.FMT_W6E3M2: "w6", wq.FMT_W4E2M1: "fp4",
-         wq.FMT_BF16: "bf16w", wq.FMT_W5E2M2: "fp5"}
+         wq.FMT_BF16: "bf16w", wq.FMT_W5E2M2: "fp5", wq.FMT_W3G32: "w3", wq.FMT_W6E3M2_P24: "p24"}
 IDS = ["%s%s" % (NAMES[f], "_bf16" if a else "") for f, a in CODES]
 
 

@@ -40,7 +40,7 @@ def test_version_and_status_strings():
 
 
 @pytest.mark.parametrize("fmt", [wq.FMT_F16, wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_BF16,
-                                 wq.FMT_W5E2M2])
+                                 wq.FMT_W5E2M2, wq.FMT_W3G32, wq.FMT_W6E3M2_P24])
 @pytest.mark.parametrize("n,k", [(1, 32), (7, 64), (33, 96), (4096, 11008)])
 def test_sizes_match_oracle(fmt, n, k):
     assert wq.wq_packed_bytes(fmt, n, k) == oracle.packed_bytes(fmt, n, k)
@@ -54,7 +54,7 @@ def test_sizes_match_oracle(fmt, n, k):
 
 def test_sizes_reject_bad_shapes():
     assert wq.wq_packed_bytes(wq.FMT_W8 | 0x200, 4, 64) == 0
-    for fmt in range(7):
+    for fmt in range(9):
         assert wq.wq_packed_bytes(fmt, 4, 48) == 0
         assert wq.wq_packed_bytes(fmt, 0, 64) == 0
         assert wq.wq_packed_bytes(fmt, 4, 0) == 0
@@ -82,7 +82,7 @@ def _exact_ties(fmt):
     if fmt == wq.FMT_W8:
         r = np.zeros(64, dtype=np.float32); r[0] = 127.0; r[1:9] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, -126.5]
         rows.append(r)
-    if fmt == wq.FMT_W6E3M2:
+    if fmt in (wq.FMT_W6E3M2, wq.FMT_W6E3M2_P24):
         r = np.zeros(64, dtype=np.float32); r[0] = 28.0
         r[1:12] = [1.875, 0.03125, 0.09375, 26.0, -26.0, 5.5, -0.0, -0.01, 3.25, 0.40625, 14.999]
         rows.append(r)
@@ -100,10 +100,15 @@ def _exact_ties(fmt):
     if fmt == wq.FMT_W4G32:
         r = np.zeros(64, dtype=np.float32); r[0] = -7.5; r[1] = 7.5; r[2:6] = [0.5, 1.5, -0.5, 2.5]   # s = 1, z = 8 (7.5 -> even)
         rows.append(r)
+    if fmt == wq.FMT_W3G32:
+        r = np.zeros(64, dtype=np.float32); r[0] = -3.5; r[1] = 3.5; r[2:6] = [0.5, 1.5, -0.5, 2.5]   # s = 1, z = 4 (3.5 -> even)
+        r[32] = -2.5; r[33] = 4.5; r[34:37] = [0.5, -1.5, 3.5]                                        # s = 1, z = 2 (2.5 -> even)
+        rows.append(r)
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_W5E2M2])
+@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_W5E2M2, wq.FMT_W3G32,
+                                 wq.FMT_W6E3M2_P24])
 @pytest.mark.parametrize("n,k,seed", [(8, 64, 0), (9, 96, 1), (33, 128, 2), (300, 4096, 3), (5, 32 * 130, 4)])
 def test_pack_bit_identical_to_oracle(fmt, n, k, seed):
     w = _adversarial(n, k, seed)
@@ -119,27 +124,36 @@ def test_pack_bit_identical_to_oracle(fmt, n, k, seed):
     elif fmt == wq.FMT_W5E2M2:
         packed, s = wq.wq_pack_fp5(w)
         z = None
+    elif fmt == wq.FMT_W3G32:
+        packed, s, z = wq.wq_pack_int3(w)
+    elif fmt == wq.FMT_W6E3M2_P24:
+        packed, s = wq.wq_pack_fp6_p24(w)
+        z = None
     else:
         packed, s = wq.wq_pack_fp4(w)
         z = None
     assert np.array_equal(packed, packed_o)
     assert np.array_equal(s, s_o.reshape(-1))
-    if fmt == wq.FMT_W4G32:
+    if fmt in (wq.FMT_W4G32, wq.FMT_W3G32):
         assert np.array_equal(z, z_o.reshape(-1))
     codes, s2, z2 = wq.wq_unpack(fmt, packed, s, z, n, k)
     assert np.array_equal(codes, codes_o)
     assert np.array_equal(s2, s)
 
 
-@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_W5E2M2])
+@pytest.mark.parametrize("fmt", [wq.FMT_W8, wq.FMT_W4G32, wq.FMT_W6E3M2, wq.FMT_W4E2M1, wq.FMT_W5E2M2, wq.FMT_W3G32,
+                                 wq.FMT_W6E3M2_P24])
 def test_pack_exact_ties_identical_to_oracle(fmt):
     w = _exact_ties(fmt)
     packed_o, s_o, z_o, _ = oracle.quantize_and_pack(fmt, w)
     fn = {wq.FMT_W8: wq.wq_pack_int8, wq.FMT_W4G32: wq.wq_pack_int4, wq.FMT_W6E3M2: wq.wq_pack_fp6,
-          wq.FMT_W4E2M1: wq.wq_pack_fp4, wq.FMT_W5E2M2: wq.wq_pack_fp5}[fmt]
+          wq.FMT_W4E2M1: wq.wq_pack_fp4, wq.FMT_W5E2M2: wq.wq_pack_fp5, wq.FMT_W3G32: wq.wq_pack_int3,
+          wq.FMT_W6E3M2_P24: wq.wq_pack_fp6_p24}[fmt]
     out = fn(w)
     assert np.array_equal(out[0], packed_o)
     assert np.array_equal(out[1], s_o.reshape(-1))
+    if fmt in (wq.FMT_W4G32, wq.FMT_W3G32):
+        assert np.array_equal(out[2], z_o.reshape(-1))
 
 
 def test_pack_multithreaded_large_matches_oracle():
@@ -214,7 +228,17 @@ def test_pack_errors():
     with pytest.raises(wq.WqError) as e:
         wq.wq_pack_int8(big)      # 1e7/127 > 65504
     assert e.value.status == -7
-    assert L.wq_unpack(7, p(buf), p(sc), p(sc), 2, 64, p(buf), None, None) == -3
+    assert L.wq_unpack(9, p(buf), p(sc), p(sc), 2, 64, p(buf), None, None) == -3
+    assert L.wq_pack_int3(p(w), 2, 64, p(buf), p(sc), None) == -1
+    assert L.wq_pack_int3(p(w), 2, 48, p(buf), p(sc), p(sc)) == -2
+    assert L.wq_pack_fp6_p24(p(w), 2, 64, None, p(sc)) == -1
+    assert L.wq_pack_fp6_p24(p(w), 0, 64, p(buf), p(sc)) == -2
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_pack_int3(np.full((1, 32), np.nan, dtype=np.float32))
+    assert e.value.status == -4
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_pack_fp6_p24(np.full((1, 32), 1e7, dtype=np.float32))   # 1e7/28 > 65504
+    assert e.value.status == -7
     assert L.wq_pack_fp5(None, 2, 64, p(buf), p(sc)) == -1
     assert L.wq_pack_fp5(p(w), 2, 40, p(buf), p(sc)) == -2
     bad[1, 5] = -np.inf
@@ -401,6 +425,29 @@ def test_fp5_kernel_choice():
     assert wq.wq_linear_kernel_name(f | wq.ACT_BF16, 81, 4096, 4096) == "pf_kernel<262>"
     assert wq.wq_linear_grouped_kernel_name(f, 8, [(4096, 4096), (11008, 4096)]) == "lm_grouped_kernel<6, 2, 1>"
     assert wq.wq_linear_grouped_kernel_name(f, 1, [(4096, 4096), (11008, 4096)]) == "gemv_grouped_kernel<6, 1, 4>"
+
+
+def test_int3_and_split_fp6_kernel_choice():
+    # int3 follows W4's plan (groups of 32: the LDS-staged kernel needs K a multiple of 256, else
+    # the fragment-load kernel), the 2+4 FP6 layout follows W6's (same slices, other decode);
+    # neither takes bfloat16 activations
+    f3, f6 = wq.FMT_W3G32, wq.FMT_W6E3M2_P24
+    assert wq.wq_linear_kernel_name(f3, 1, 4096, 4096) == "gemv_kernel<7, 1, 4>"
+    assert wq.wq_linear_kernel_name(f3, 4, 2048, 4096) == "gemv_kernel<7, 4, 4>"
+    assert wq.wq_linear_kernel_name(f3, 4, 4096, 4096) == "lm_kernel<7, 1, 1>"
+    assert wq.wq_linear_kernel_name(f3, 8, 8192, 8192) == "lm_kernel<7, 2, 1>"
+    assert wq.wq_linear_kernel_name(f3, 8, 4096, 4096 + 32) == "mfma_kernel<7, 1>"
+    assert wq.wq_linear_kernel_name(f3, 64, 4096, 4096) == "lm_kernel<7, 1, 4>"
+    assert wq.wq_linear_kernel_name(f3, 65, 4096, 4096) == "pf_kernel<7>"
+    for m, n, k in ((1, 4096, 4096), (4, 2048, 4096), (4, 4096, 4096), (8, 28672, 8192), (16, 8192, 8192),
+                    (64, 4096, 4096), (65, 4096, 4096), (193, 4096, 28672)):
+        want = wq.wq_linear_kernel_name(wq.FMT_W6E3M2, m, n, k).replace("<3", "<8")
+        assert wq.wq_linear_kernel_name(f6, m, n, k) == want, (m, n, k)
+    assert wq.wq_linear_grouped_kernel_name(f3, 8, [(4096, 4096), (11008, 4096)]) == "lm_grouped_kernel<7, 2, 1>"
+    assert wq.wq_linear_grouped_kernel_name(f3, 8, [(4096, 4096), (4096, 4128)]) == "mfma_grouped_kernel<7, 1>"
+    assert wq.wq_linear_grouped_kernel_name(f6, 1, [(10240, 8192), (8192, 8192)]) == "gemv_grouped_kernel<8, 1, 4>"
+    for f in (f3, f6):
+        assert wq.wq_linear_kernel_name(f | wq.ACT_BF16, 1, 4096, 4096) == ""
 
 
 class _FakeDeviceTensor:

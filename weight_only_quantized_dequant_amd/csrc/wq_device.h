@@ -43,6 +43,13 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x16 __attribute__((ext_vector_type(16)));
 
 
+// A constant kept in a VGPR. gfx950 VALU ops take at most one SGPR or literal and VOP3
+// ops take no literal, so masks used by v_and_or_b32 / v_perm_b32 must sit in VGPRs.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
+  asm volatile("" : "+v"(c));
+  return c;
+}
+
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
@@ -52,6 +59,13 @@ __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uin
 // layout (BF16 weights are laid out and loaded as F16 ones).
 constexpr int wfmt(int c) { return (c & 0xFF) == WQ_FMT_BF16 ? WQ_FMT_F16 : (c & 0xFF); }
 constexpr bool bf16_act(int c) { return (c & WQ_ACT_BF16) != 0; }
+// The two FP6 layouts share W6's geometry (a 16-byte and an 8-byte slice per unit, in planes);
+// int4 and int3 carry a scale and a zero point per group of 32 K.
+constexpr bool w6_geom(int c) { return wfmt(c) == WQ_FMT_W6E3M2 || wfmt(c) == WQ_FMT_W6E3M2_P24; }
+constexpr bool group_meta(int c) { return wfmt(c) == WQ_FMT_W4G32 || wfmt(c) == WQ_FMT_W3G32; }
+// The layout the launch planner sizes work by: the 2+4 FP6 layout moves the same bytes in the
+// same slices as W6 and is planned as W6.
+constexpr int pfmt(int c) { return w6_geom(c) ? WQ_FMT_W6E3M2 : wfmt(c); }
 
 __device__ __forceinline__ float dot2_bf16(h2 a, h2 b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
@@ -90,22 +104,39 @@ template <> struct Raw<WQ_FMT_W4G32> { uint4 a; };
 template <> struct Raw<WQ_FMT_W6E3M2> { uint4 a; uint2 b; };
 template <> struct Raw<WQ_FMT_W4E2M1> { uint4 a; };
 template <> struct Raw<WQ_FMT_W5E2M2> { uint4 a; uint32_t b; };   // magnitude nibbles, sign word
+template <> struct Raw<WQ_FMT_W3G32> { uint4 a; };                  // the 12 bytes in .x .y .z (.w unused)
+template <> struct Raw<WQ_FMT_W6E3M2_P24> { uint4 a; uint2 b; };    // low nibbles; bit-4 word, sign word
 template <> struct Raw<WQ_FMT_F16> { uint4 a, b, c, d; };
 
 template <int FMT> constexpr int unit_bytes() {
-  return wfmt(FMT) == WQ_FMT_W8 ? 32 : wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W4E2M1 ? 16
-       : wfmt(FMT) == WQ_FMT_W6E3M2 ? 24 : wfmt(FMT) == WQ_FMT_W5E2M2 ? 20 : 64;
+  constexpr int f = wfmt(FMT);
+  return f == WQ_FMT_W8 ? 32 : f == WQ_FMT_W4G32 || f == WQ_FMT_W4E2M1 ? 16 : f == WQ_FMT_W3G32 ? 12
+       : w6_geom(f) ? 24 : f == WQ_FMT_W5E2M2 ? 20 : 64;
 }
 
 // Formats with one fp16 scale per output row, applied to the finished fp32 sum.
 template <int FMT> constexpr bool row_scaled() {
-  return wfmt(FMT) == WQ_FMT_W8 || wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1 ||
-         wfmt(FMT) == WQ_FMT_W5E2M2;
+  return wfmt(FMT) == WQ_FMT_W8 || w6_geom(FMT) || wfmt(FMT) == WQ_FMT_W4E2M1 || wfmt(FMT) == WQ_FMT_W5E2M2;
 }
 
-// The decoders hand FP5 values over as e2m2(code) * 2^-14 (exact fp16 bit placement); the row
-// scale that multiplies the finished sum carries the 2^14 (exact in fp32).
-template <int FMT> constexpr float code_scale() { return wfmt(FMT) == WQ_FMT_W5E2M2 ? 16384.0f : 1.0f; }
+// The decoders hand FP5 values over as e2m2(code) * 2^-14 and the 2+4 FP6 values as
+// e3m2(code) * 2^-12 (exact fp16 bit placements); the row scale that multiplies the finished
+// sum carries the power of two (exact in fp32).
+template <int FMT> constexpr float code_scale() {
+  return wfmt(FMT) == WQ_FMT_W5E2M2 ? 16384.0f : wfmt(FMT) == WQ_FMT_W6E3M2_P24 ? 4096.0f : 1.0f;
+}
+
+// 12 bytes at a 4-byte aligned address, as one dwordx3 load (the type's alignment is lowered to
+// 4 so that the load is never widened past the 12 bytes).
+typedef unsigned int u32x3a __attribute__((ext_vector_type(3), aligned(4)));
+__device__ __forceinline__ uint4 ld12(const uint8_t* p) {
+  const u32x3a t = *reinterpret_cast<const u32x3a*>(p);
+  return make_uint4(t[0], t[1], t[2], 0u);
+}
+__device__ __forceinline__ uint4 ld_nt12(const uint8_t* p) {
+  const u32x3a t = __builtin_nontemporal_load(reinterpret_cast<const u32x3a*>(p));
+  return make_uint4(t[0], t[1], t[2], 0u);
+}
 
 // Byte offsets, from the start of row n, of the two plane slices of W6 unit u (U units per row).
 __device__ __forceinline__ void w6_homes(int u, int U, uint32_t& lo, uint32_t& hi) {
@@ -131,7 +162,9 @@ __device__ __forceinline__ void load_unit(const uint8_t* __restrict__ w, int n, 
     r.a = q[0]; r.b = q[1];
   } else if constexpr (wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W4E2M1) {
     r.a = *reinterpret_cast<const uint4*>(row + (size_t)u * UB);
-  } else if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2) {
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W3G32) {
+    r.a = ld12(row + (size_t)u * UB);
+  } else if constexpr (w6_geom(FMT)) {
     uint32_t lo, hi;
     w6_homes(u, U, lo, hi);
     r.a = *reinterpret_cast<const uint4*>(row + lo);
@@ -182,6 +215,70 @@ __device__ __forceinline__ void decode_fp5(const uint4& mag, uint32_t sgn, h2 (&
     }
 }
 
+// FP6 e3m2 in the 2+4 split layout: pair p = 4d + t takes its two low nibbles from word d as FP5
+// does (to fp16 bits 11..8 and 27..24), bit 4 from bits p and 16+p of the bit-4 word (to fp16
+// bits 12 and 28) and the signs from the sign word (to bits 15 and 31): fp16 bits s.eee.mm at
+// 15 and 12..8, i.e. e3m2(code) * 2^-12 exactly (fp16's exponent bias 15 is e3m2's bias 3 + 12;
+// the subnormal codes land on fp16 subnormals). Three shifts, an AND and two AND-ORs per pair,
+// with the masks in VGPRs.
+struct P24Masks { uint32_t nib, e2, sg; };
+__device__ __forceinline__ P24Masks p24_masks() {
+  return {in_vgpr(0x0F000F00u), in_vgpr(0x10001000u), in_vgpr(0x80008000u)};
+}
+__device__ __forceinline__ void decode_p24(const uint4& mag, const uint2& hi, const P24Masks& k, h2 (&out)[16]) {
+  const uint32_t w[4] = {mag.x, mag.y, mag.z, mag.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int p = 4 * d + t;
+      const uint32_t m = t < 2 ? w[d] << (8 - 4 * t) : w[d] >> (4 * t - 8);
+      const uint32_t e = p <= 12 ? hi.x << (12 - p) : hi.x >> (p - 12);
+      const uint32_t sg = (hi.y << (15 - p)) & k.sg;
+      out[p] = as_h2((m & k.nib) | ((e & k.e2) | sg));
+    }
+}
+
+// int3 (W3 layout): in each word, the pairs at offsets 0, 3 and 6 of both halves are placed in
+// the mantissas of 1024.0 (step 1), 128.0 (step 1/8) and 16.0 (step 1/64), so the masked field
+// reads 1024 + q, 128 + q or 16 + q; the word shifted right by 10 brings offsets 10 and 13 to 0
+// and 3. The last pair is gathered from bits 9 and 25 of the three words. One AND-OR per pair
+// (the last takes three), with the masks in VGPRs. w3_class(p) names the bias of pair p:
+// 0 -> 1024, 1 -> 128, 2 -> 16.
+constexpr int w3_class(int p) { return p == 15 ? 0 : (p % 5 == 2 ? 2 : (p % 5 == 1 || p % 5 == 4) ? 1 : 0); }
+struct W3Masks { uint32_t f0, f1, f2, mag0, mag1, mag2, b0, b1, b2; };
+__device__ __forceinline__ W3Masks w3_masks() {
+  return {in_vgpr(0x00070007u), in_vgpr(0x00380038u), in_vgpr(0x01C001C0u), in_vgpr(0x64006400u),
+          in_vgpr(0x58005800u), in_vgpr(0x4C004C00u), in_vgpr(0x00010001u), in_vgpr(0x00020002u),
+          in_vgpr(0x00040004u)};
+}
+__device__ __forceinline__ void decode_w3_biased(const uint4& r, const W3Masks& k, h2 (&out)[16]) {
+  const uint32_t w[3] = {r.x, r.y, r.z};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const uint32_t d = w[i], e = d >> 10;
+    out[5 * i] = as_h2((d & k.f0) | k.mag0);
+    out[5 * i + 1] = as_h2((d & k.f1) | k.mag1);
+    out[5 * i + 2] = as_h2((d & k.f2) | k.mag2);
+    out[5 * i + 3] = as_h2((e & k.f0) | k.mag0);
+    out[5 * i + 4] = as_h2((e & k.f1) | k.mag1);
+  }
+  out[15] = as_h2(((r.x >> 9) & k.b0) | (((r.y >> 8) & k.b1) | (((r.z >> 7) & k.b2) | k.mag0)));
+}
+// q - z exactly: the biased values plus zc[class] = -(1024 + z), -(128 + z), -(16 + z).
+__device__ __forceinline__ void decode_w3_unit(const uint4& r, const h2 (&zc)[3], const W3Masks& k, h2 (&out)[16]) {
+  decode_w3_biased(r, k, out);
+#pragma unroll
+  for (int p = 0; p < 16; ++p) out[p] += zc[w3_class(p)];
+}
+__device__ __forceinline__ void w3_consts(uint16_t zbits, h2 (&zc)[3]) {
+  const _Float16 z = __builtin_bit_cast(_Float16, zbits);
+  const _Float16 c0 = (_Float16)-1024.0f - z, c1 = (_Float16)-128.0f - z, c2 = (_Float16)-16.0f - z;   // exact
+  zc[0] = h2{c0, c0};
+  zc[1] = h2{c1, c1};
+  zc[2] = h2{c2, c2};
+}
+
 // Byte b of d holds codes 2b (low nibble) and 2b+1 (high nibble); the convert takes the
 // byte index as an immediate and returns them in that order.
 __device__ __forceinline__ void decode_fp4_word(uint32_t d, h2& o0, h2& o1, h2& o2, h2& o3) {
@@ -213,11 +310,34 @@ __device__ __forceinline__ void decode(const Raw<wfmt(FMT)>& r, h2 zc1, h2 zc2, 
     for (int i = 0; i < 4; ++i) decode_fp4_word(w[i], out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
   } else if constexpr (wfmt(FMT) == WQ_FMT_W5E2M2) {
     decode_fp5(r.a, r.b, out);
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2_P24) {
+    decode_p24(r.a, r.b, P24Masks{0x0F000F00u, 0x10001000u, 0x80008000u}, out);
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W3G32) {
+    // zc1 = -(1024 + z), zc2 = -(128 + z) (w3_consts); -(16 + z) = zc2 + 112 exactly
+    const h2 zc[3] = {zc1, zc2, zc2 + h2{(_Float16)112.0f, (_Float16)112.0f}};
+    decode_w3_unit(r.a, zc, W3Masks{0x00070007u, 0x00380038u, 0x01C001C0u, 0x64006400u, 0x58005800u, 0x4C004C00u,
+                                    0x00010001u, 0x00020002u, 0x00040004u}, out);
   } else {
     const uint32_t w[16] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w,
                             r.c.x, r.c.y, r.c.z, r.c.w, r.d.x, r.d.y, r.d.z, r.d.w};
 #pragma unroll
     for (int p = 0; p < 16; ++p) out[p] = as_h2(w[p]);
+  }
+}
+
+// The zero-point constants decode<FMT> takes for a group's zero point z: W4 -(1024 + z) and
+// -(64 + z), W3 -(1024 + z) and -(128 + z); zero for the other formats.
+template <int FMT>
+__device__ __forceinline__ void group_consts(uint16_t zbits, h2& zc1, h2& zc2) {
+  if constexpr (wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W3G32) {
+    const _Float16 z = __builtin_bit_cast(_Float16, zbits);
+    const _Float16 c1 = (_Float16)-1024.0f - z;
+    const _Float16 c2 = (wfmt(FMT) == WQ_FMT_W4G32 ? (_Float16)-64.0f : (_Float16)-128.0f) - z;   // exact integers
+    zc1 = h2{c1, c1};
+    zc2 = h2{c2, c2};
+  } else {
+    zc1 = h2{};
+    zc2 = h2{};
   }
 }
 
@@ -304,12 +424,6 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v) {
   return v;
 }
 
-// A constant kept in a VGPR. gfx950 VALU ops take at most one SGPR or literal and VOP3
-// ops take no literal, so masks used by v_and_or_b32 / v_perm_b32 must sit in VGPRs.
-__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
-  asm volatile("" : "+v"(c));
-  return c;
-}
 
 // A wave-uniform byte offset held in SGPRs. Adding it to a kernel-argument pointer keeps
 // the global address space and lets loads take the SGPR-base + 32-bit VGPR offset form
@@ -355,10 +469,12 @@ __device__ __forceinline__ uint2 ld_nt8(const uint8_t* p) {
 
 }  // namespace
 
-// Every kernel code: the weight formats with fp16 activations, and with bfloat16 ones.
+// Every kernel code: the weight formats with fp16 activations, and (all but F16, W3G32 and
+// W6E3M2_P24) with bfloat16 ones.
 #define WQ_KERNEL_CODES(X)                                                                              \
   X(WQ_FMT_F16) X(WQ_FMT_W8) X(WQ_FMT_W4G32) X(WQ_FMT_W6E3M2) X(WQ_FMT_W4E2M1)                          \
   X(WQ_FMT_W8 | WQ_ACT_BF16) X(WQ_FMT_W4G32 | WQ_ACT_BF16) X(WQ_FMT_W6E3M2 | WQ_ACT_BF16)              \
-  X(WQ_FMT_W4E2M1 | WQ_ACT_BF16) X(WQ_FMT_BF16 | WQ_ACT_BF16) X(WQ_FMT_W5E2M2) X(WQ_FMT_W5E2M2 | WQ_ACT_BF16)
+  X(WQ_FMT_W4E2M1 | WQ_ACT_BF16) X(WQ_FMT_BF16 | WQ_ACT_BF16) X(WQ_FMT_W5E2M2) X(WQ_FMT_W5E2M2 | WQ_ACT_BF16) \
+  X(WQ_FMT_W3G32) X(WQ_FMT_W6E3M2_P24)
 
 #endif  // WQ_DEVICE_H_

@@ -9,7 +9,8 @@
 //   int8  per row:       s = fp16(max|w| / 127),      q = clamp(rint(w/s), -127, 127)
 //   int4  per 32 along K: s = fp16((hi - lo) / 15), z = clamp(rint(-lo/s), 0, 15),
 //                        q = clamp(rint(w/s) + z, 0, 15), lo/hi widened to include 0
-//   fp6   per row:       s = fp16(max|w| / 28),       code = e3m2 nearest to w/s
+//   int3  per 32 along K: the same with 7 in place of 15
+//   fp6   per row:       s = fp16(max|w| / 28),       code = e3m2 nearest to w/s (two layouts)
 //   fp4   per row:       s = fp16(max|w| / 6),        code = e2m1 nearest to w/s
 //   fp5   per row:       s = fp16(max|w| / 7),        code = e2m2 nearest to w/s
 // Every quotient is one IEEE float64 operation; every rounding is to nearest even.
@@ -124,6 +125,8 @@ int fmt_bits(int fmt) {
     case WQ_FMT_W4E2M1: return 4;
     case WQ_FMT_BF16: return 16;
     case WQ_FMT_W5E2M2: return 5;
+    case WQ_FMT_W3G32: return 3;
+    case WQ_FMT_W6E3M2_P24: return 6;
     default: return 0;
   }
 }
@@ -199,12 +202,44 @@ void w5_unit_homes(P base, int64_t r, int64_t u, int64_t U, P& lo, P& hi) {
   hi = chunk + 16 * uc + 4 * j;
 }
 
-// The sign word of an FP5 unit: the sign of code 2p in bit p, of code 2p+1 in bit 16+p.
-uint32_t w5_sign_word(const uint8_t* c) {
+// A word of one bit of every code of a unit: bit `bit` of code 2p in bit p, of code 2p+1 in bit
+// 16+p (the FP5 sign word: bit 4; the P24 bit-4 and sign words: bits 4 and 5).
+uint32_t bit_word(const uint8_t* c, int bit) {
   uint32_t s = 0;
-  for (int p = 0; p < 16; ++p) s |= static_cast<uint32_t>((c[2 * p] >> 4) & 1) << p |
-                                   static_cast<uint32_t>((c[2 * p + 1] >> 4) & 1) << (16 + p);
+  for (int p = 0; p < 16; ++p) s |= static_cast<uint32_t>((c[2 * p] >> bit) & 1) << p |
+                                   static_cast<uint32_t>((c[2 * p + 1] >> bit) & 1) << (16 + p);
   return s;
+}
+
+// W3: pair p = codes (2p, 2p+1); pairs 0..14 in word p / 5 at these offsets (even code in the
+// low half, odd code 16 bits up); bit b of the last pair in bits 9 and 25 of word b.
+constexpr int kW3Offset[5] = {0, 3, 6, 10, 13};
+
+void put_unit_w3(uint8_t* dst, const uint8_t* q) {
+  uint32_t w[3] = {0, 0, 0};
+  for (int p = 0; p < 15; ++p) {
+    const int o = kW3Offset[p % 5];
+    w[p / 5] |= static_cast<uint32_t>(q[2 * p] & 7) << o | static_cast<uint32_t>(q[2 * p + 1] & 7) << (16 + o);
+  }
+  for (int b = 0; b < 3; ++b)
+    w[b] |= static_cast<uint32_t>((q[30] >> b) & 1) << 9 | static_cast<uint32_t>((q[31] >> b) & 1) << 25;
+  for (int i = 0; i < 12; ++i) dst[i] = static_cast<uint8_t>(w[i >> 2] >> (8 * (i & 3)));
+}
+
+void get_unit_w3(const uint8_t* src, uint8_t* q) {
+  uint32_t w[3];
+  for (int i = 0; i < 3; ++i)
+    w[i] = src[4 * i] | (src[4 * i + 1] << 8) | (src[4 * i + 2] << 16) | (static_cast<uint32_t>(src[4 * i + 3]) << 24);
+  for (int p = 0; p < 15; ++p) {
+    const int o = kW3Offset[p % 5];
+    q[2 * p] = (w[p / 5] >> o) & 7;
+    q[2 * p + 1] = (w[p / 5] >> (16 + o)) & 7;
+  }
+  q[30] = q[31] = 0;
+  for (int b = 0; b < 3; ++b) {
+    q[30] |= static_cast<uint8_t>(((w[b] >> 9) & 1) << b);
+    q[31] |= static_cast<uint8_t>(((w[b] >> 25) & 1) << b);
+  }
 }
 
 int check_weights(const float* w, int64_t K, int64_t r) {
@@ -247,12 +282,13 @@ size_t wq_packed_bytes(int fmt, int64_t N, int64_t K) {
 size_t wq_scales_bytes(int fmt, int64_t N, int64_t K) {
   fmt = weight_fmt(fmt);
   if (!fmt_bits(fmt) || !shape_ok(N, K) || fmt == WQ_FMT_F16 || fmt == WQ_FMT_BF16) return 0;
-  return fmt == WQ_FMT_W4G32 ? static_cast<size_t>(N) * (K / 32) * 2 : static_cast<size_t>(N) * 2;
+  const bool grouped = fmt == WQ_FMT_W4G32 || fmt == WQ_FMT_W3G32;
+  return grouped ? static_cast<size_t>(N) * (K / 32) * 2 : static_cast<size_t>(N) * 2;
 }
 
 size_t wq_zeros_bytes(int fmt, int64_t N, int64_t K) {
   fmt = weight_fmt(fmt);
-  if (fmt != WQ_FMT_W4G32 || !shape_ok(N, K)) return 0;
+  if ((fmt != WQ_FMT_W4G32 && fmt != WQ_FMT_W3G32) || !shape_ok(N, K)) return 0;
   return static_cast<size_t>(N) * (K / 32) * 2;
 }
 
@@ -281,7 +317,15 @@ int wq_pack_int8(const float* w, int64_t N, int64_t K, void* packed, uint16_t* s
   });
 }
 
-int wq_pack_int4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales, uint16_t* zeros) {
+}  // extern "C"
+
+namespace {
+
+// int4 / int3: codes 0..top with an fp16 scale and an integer zero point per group of 32 K;
+// put writes one unit of UB bytes.
+template <int UB, class Put>
+int pack_asymmetric_g32(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales, uint16_t* zeros,
+                        double top, Put put) {
   if (!w || !packed || !scales || !zeros || N < 0 || K < 0) return WQ_ERR_ARG;
   if (!shape_ok(N, K)) return WQ_ERR_SHAPE;
   uint8_t* out = static_cast<uint8_t*>(packed);
@@ -297,29 +341,47 @@ int wq_pack_int4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* s
           lo = std::min(lo, static_cast<double>(grp[j]));
           hi = std::max(hi, static_cast<double>(grp[j]));
         }
-        const uint16_t sb = f64_to_f16_bits((hi - lo) / 15.0);
+        const uint16_t sb = f64_to_f16_bits((hi - lo) / top);
         if ((sb & 0x7FFF) == 0x7C00) return static_cast<int>(WQ_ERR_RANGE);
         const double s = f16_bits_to_f64(sb);
         double z = 0.0;
         if (s > 0) {
-          z = std::min(15.0, std::max(0.0, std::nearbyint(-lo / s)));
+          z = std::min(top, std::max(0.0, std::nearbyint(-lo / s)));
           for (int j = 0; j < 32; ++j) {
             double v = std::nearbyint(static_cast<double>(grp[j]) / s) + z;
-            q[j] = static_cast<uint8_t>(std::min(15.0, std::max(0.0, v)));
+            q[j] = static_cast<uint8_t>(std::min(top, std::max(0.0, v)));
           }
         } else {
           std::memset(q, 0, sizeof(q));
         }
         scales[r * G + g] = sb;
         zeros[r * G + g] = static_cast<uint16_t>(f64_to_f16_bits(z) & 0x7FFF);  // integer zero point: +0 never -0
-        put_unit_w4(out + (r * G + g) * 16, q);
+        put(out + (r * G + g) * UB, q);
       }
     }
     return static_cast<int>(WQ_OK);
   });
 }
 
-int wq_pack_fp6(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales) {
+}  // namespace
+
+extern "C" {
+
+int wq_pack_int4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales, uint16_t* zeros) {
+  return pack_asymmetric_g32<16>(w, N, K, packed, scales, zeros, 15.0, put_unit_w4);
+}
+
+int wq_pack_int3(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales, uint16_t* zeros) {
+  return pack_asymmetric_g32<12>(w, N, K, packed, scales, zeros, 7.0, put_unit_w3);
+}
+
+}  // extern "C"
+
+namespace {
+
+// FP6 e3m2 per row, in the bf6-convert layout (p24 false) or the 2+4 split (p24 true); both
+// store a unit as a 16-byte and an 8-byte slice in W6's planes.
+int pack_fp6_rows(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales, bool p24) {
   if (!w || !packed || !scales || N < 0 || K < 0) return WQ_ERR_ARG;
   if (!shape_ok(N, K)) return WQ_ERR_SHAPE;
   uint8_t* out = static_cast<uint8_t*>(packed);
@@ -337,8 +399,18 @@ int wq_pack_fp6(const float* w, int64_t N, int64_t K, void* packed, uint16_t* sc
       scales[r] = sb;
       for (int64_t k = 0; k < K; ++k) c[k] = s > 0 ? e3m2_encode(static_cast<double>(row[k]) / s) : 0;
       for (int64_t u = 0; u < U; ++u) {
+        const uint8_t* cu = c.data() + 32 * u;
         uint8_t unit[24];
-        put_unit_w6(unit, c.data() + 32 * u);
+        if (p24) {
+          put_unit_w4(unit, cu);   // the low four bits, placed as W4 codes
+          const uint32_t e2 = bit_word(cu, 4), sg = bit_word(cu, 5);
+          for (int b = 0; b < 4; ++b) {
+            unit[16 + b] = static_cast<uint8_t>(e2 >> (8 * b));
+            unit[20 + b] = static_cast<uint8_t>(sg >> (8 * b));
+          }
+        } else {
+          put_unit_w6(unit, cu);
+        }
         uint8_t* lo;
         uint8_t* hi;
         w6_unit_homes(out, r, u, U, lo, hi);
@@ -348,6 +420,18 @@ int wq_pack_fp6(const float* w, int64_t N, int64_t K, void* packed, uint16_t* sc
     }
     return static_cast<int>(WQ_OK);
   });
+}
+
+}  // namespace
+
+extern "C" {
+
+int wq_pack_fp6(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales) {
+  return pack_fp6_rows(w, N, K, packed, scales, false);
+}
+
+int wq_pack_fp6_p24(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales) {
+  return pack_fp6_rows(w, N, K, packed, scales, true);
 }
 
 int wq_pack_fp4(const float* w, int64_t N, int64_t K, void* packed, uint16_t* scales) {
@@ -397,7 +481,7 @@ int wq_pack_fp5(const float* w, int64_t N, int64_t K, void* packed, uint16_t* sc
         uint8_t* hi;
         w5_unit_homes(out, r, u, U, lo, hi);
         put_unit_w4(lo, c.data() + 32 * u);   // the low four bits, placed as W4 codes
-        const uint32_t sw = w5_sign_word(c.data() + 32 * u);
+        const uint32_t sw = bit_word(c.data() + 32 * u, 4);
         for (int b = 0; b < 4; ++b) hi[b] = static_cast<uint8_t>(sw >> (8 * b));
       }
     }
@@ -444,6 +528,34 @@ int wq_unpack(int fmt, const void* packed, const uint16_t* scales, const uint16_
             v |= ((p[bit >> 3] >> (bit & 7)) & 1) << b;
           }
           o[r * K + 32 * u + j] = static_cast<uint8_t>(v);
+        }
+      }
+  } else if (fmt == WQ_FMT_W3G32) {
+    uint8_t* o = static_cast<uint8_t*>(codes);
+    for (int64_t i = 0; i < N * U; ++i) get_unit_w3(in + 12 * i, o + 32 * i);
+  } else if (fmt == WQ_FMT_W6E3M2_P24) {
+    uint8_t* o = static_cast<uint8_t*>(codes);
+    for (int64_t r = 0; r < N; ++r)
+      for (int64_t u = 0; u < U; ++u) {
+        const uint8_t* lo;
+        const uint8_t* hi;
+        w6_unit_homes(in, r, u, U, lo, hi);
+        uint8_t* cu = o + r * K + 32 * u;
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t word = lo[4 * d] | (lo[4 * d + 1] << 8) | (lo[4 * d + 2] << 16) |
+                                (static_cast<uint32_t>(lo[4 * d + 3]) << 24);
+          for (int t = 0; t < 4; ++t) {
+            cu[8 * d + 2 * t] = (word >> (4 * t)) & 15;
+            cu[8 * d + 2 * t + 1] = (word >> (4 * (t + 4))) & 15;
+          }
+        }
+        for (int b = 0; b < 2; ++b) {
+          const uint8_t* h = hi + 4 * b;
+          const uint32_t bw = h[0] | (h[1] << 8) | (h[2] << 16) | (static_cast<uint32_t>(h[3]) << 24);
+          for (int p = 0; p < 16; ++p) {
+            cu[2 * p] |= static_cast<uint8_t>(((bw >> p) & 1) << (4 + b));
+            cu[2 * p + 1] |= static_cast<uint8_t>(((bw >> (16 + p)) & 1) << (4 + b));
+          }
         }
       }
   } else if (fmt == WQ_FMT_W4E2M1) {

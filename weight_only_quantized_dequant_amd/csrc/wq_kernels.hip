@@ -76,7 +76,8 @@ template <int FMT> constexpr int seg_codes() { return wfmt(FMT) == WQ_FMT_W8 ? 1
 
 template <int FMT> struct Seg { uint4 a; };
 template <> struct Seg<WQ_FMT_W6E3M2> { uint4 a; uint2 b; };
-template <> struct Seg<WQ_FMT_W5E2M2> { uint4 a; uint32_t b; };
+template <> struct Seg<WQ_FMT_W6E3M2_P24> { uint4 a; uint2 b; };
+template <> struct Seg<WQ_FMT_W5E2M2> { uint4 a; uint32_t b; };   // W3: Seg's .x .y .z hold its 12 bytes
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -84,10 +85,10 @@ template <int FMT, int M, int B>
 struct GemvStage {
   h2 x[M][seg_codes<FMT>() / 2];
   Seg<wfmt(FMT)> w[B];
-  // W4: the group's fp16 scale (.x) and zero point (.y) in one register: the zero lands in the
-  // high half straight from its load (a d16_hi load), so a stage in flight holds one register per
-  // row for its metadata
-  u16x2 sz[wfmt(FMT) == WQ_FMT_W4G32 ? B : 1];
+  // W4, W3: the group's fp16 scale (.x) and zero point (.y) in one register: the zero lands in
+  // the high half straight from its load (a d16_hi load), so a stage in flight holds one register
+  // per row for its metadata
+  u16x2 sz[group_meta(FMT) ? B : 1];
 };
 
 // Base pointers are a kernel argument plus a wave-uniform offset (uniform() keeps it in
@@ -115,11 +116,13 @@ __device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16
   for (int b = 0; b < B; ++b) {
     const int n = min(row0 + b, N - 1);
     const uint8_t* row = w + uniform((size_t)n * row_bytes);
-    if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2) {
+    if constexpr (w6_geom(FMT)) {
       uint32_t lo, hi;
       w6_homes(sg, S, lo, hi);
       st.w[b].a = ld_nt16(row + lo);
       st.w[b].b = ld_nt8(row + hi);
+    } else if constexpr (wfmt(FMT) == WQ_FMT_W3G32) {
+      st.w[b].a = ld_nt12(row + 12u * sg);
     } else if constexpr (wfmt(FMT) == WQ_FMT_W5E2M2) {
       uint32_t lo, hi;
       w5_homes(sg, S, lo, hi);
@@ -128,7 +131,7 @@ __device__ __forceinline__ void gemv_load(GemvStage<FMT, M, B>& st, const uint16
     } else {
       st.w[b].a = ld_nt16(row + 16u * sg);
     }
-    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {   // 32-bit lane offsets from a wave-uniform base
+    if constexpr (group_meta(FMT)) {   // 32-bit lane offsets from a wave-uniform base
       const size_t mb = uniform((size_t)n * S * 2);
       st.sz[b].x = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(scales) + mb + 2u * sg);
       st.sz[b].y = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(zeros) + mb + 2u * sg);
@@ -273,6 +276,32 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
         acc[b][m] = __builtin_fmaf(s, t, acc[b][m]);
       }
     }
+  } else if constexpr (wfmt(FMT) == WQ_FMT_W3G32) {
+    // biased pairs 1024 + q, 128 + q, 16 + q by class (w3_class); the chain starts at
+    // -(1024 X0 + 128 X1 + 16 X2 + z X) with Xc the sum of x over the pairs of class c
+    const W3Masks w3m = w3_masks();
+    float cx[M], sx[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float xc[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < 16; ++p) xc[w3_class(p)] = __builtin_amdgcn_fdot2(xp[m][p], ones, xc[w3_class(p)], false);
+      cx[m] = __builtin_fmaf(1024.0f, xc[0], __builtin_fmaf(128.0f, xc[1], 16.0f * xc[2]));
+      sx[m] = xc[0] + xc[1] + xc[2];
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      h2 v[16];
+      decode_w3_biased(st.w[b].a, w3m, v);
+      const float s = f16_to_f32(st.sz[b].x), z = f16_to_f32(st.sz[b].y);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float t = -__builtin_fmaf(z, sx[m], cx[m]);
+#pragma unroll
+        for (int p = 0; p < 16; ++p) t = __builtin_amdgcn_fdot2(v[p], xp[m][p], t, false);
+        acc[b][m] = __builtin_fmaf(s, t, acc[b][m]);
+      }
+    }
   } else if constexpr (wfmt(FMT) == WQ_FMT_W8) {
     const uint32_t mag = in_vgpr(0x64646464u);
     float sx[M];
@@ -307,6 +336,7 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
       }
     }
   } else {
+    [[maybe_unused]] const P24Masks p24m = wfmt(FMT) == WQ_FMT_W6E3M2_P24 ? p24_masks() : P24Masks{};
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       h2 v[P];
@@ -323,6 +353,8 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
         for (int i = 0; i < 4; ++i) decode_fp4_word(wd[i], v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
       } else if constexpr (wfmt(FMT) == WQ_FMT_W5E2M2) {
         decode_fp5(st.w[b].a, st.w[b].b, v);
+      } else if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2_P24) {
+        decode_p24(st.w[b].a, st.w[b].b, p24m, v);
       } else {
         v[0] = as_h2(st.w[b].a.x); v[1] = as_h2(st.w[b].a.y); v[2] = as_h2(st.w[b].a.z); v[3] = as_h2(st.w[b].a.w);
       }
@@ -460,7 +492,7 @@ template <int FMT, int RB>
 struct MfmaStage {
   h8 xa[4];
   Raw<wfmt(FMT)> w[RB];
-  uint16_t s[wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1], z[wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1];
+  uint16_t s[group_meta(FMT) ? RB : 1], z[group_meta(FMT) ? RB : 1];
 };
 
 template <int FMT, int RB>
@@ -481,13 +513,14 @@ __device__ __forceinline__ void mfma_load(MfmaStage<FMT, RB>& st, const uint16_t
     const int nb = min(n0 + 16 * r, N - 1);                        // wave-uniform
     const uint32_t nn = (uint32_t)(min(n0 + 16 * r + nl, N - 1) - nb);   // 0..15
     const uint8_t* rowb = w + uniform((size_t)nb * row_bytes);
-    static_assert(wfmt(FMT) != WQ_FMT_W6E3M2 && wfmt(FMT) != WQ_FMT_W4E2M1 && wfmt(FMT) != WQ_FMT_W5E2M2,
-                  "W6, FP4 and FP5 on the matrix cores take lm_kernel");
+    static_assert(!w6_geom(FMT) && wfmt(FMT) != WQ_FMT_W4E2M1 && wfmt(FMT) != WQ_FMT_W5E2M2,
+                  "W6 (both layouts), FP4 and FP5 on the matrix cores take lm_kernel");
     const uint8_t* p = rowb + nn * row_bytes + UB * u;
-    st.w[r].a = ld_nt16(p);
+    if constexpr (wfmt(FMT) == WQ_FMT_W3G32) st.w[r].a = ld_nt12(p);
+    else st.w[r].a = ld_nt16(p);
     if constexpr (wfmt(FMT) == WQ_FMT_W8 || wfmt(FMT) == WQ_FMT_F16) st.w[r].b = ld_nt16(p + 16);
     if constexpr (wfmt(FMT) == WQ_FMT_F16) { st.w[r].c = ld_nt16(p + 32); st.w[r].d = ld_nt16(p + 48); }
-    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+    if constexpr (group_meta(FMT)) {
       const size_t mb = uniform((size_t)nb * U);
       st.s[r] = (scales + mb)[nn * U + u];
       st.z[r] = (zeros + mb)[nn * U + u];
@@ -509,9 +542,9 @@ __device__ __forceinline__ void mfma_compute(const MfmaStage<FMT, RB>& st, f4 (&
       else decode_bf16<FMT>(st.w[r], 0, 0, wv);
     } else {
       h2 zc1 = {}, zc2 = {};
-      if constexpr (wfmt(FMT) == WQ_FMT_W4G32) w4_consts(st.z[r], zc1, zc2);
+      if constexpr (group_meta(FMT)) group_consts<FMT>(st.z[r], zc1, zc2);
       decode<FMT>(st.w[r], zc1, zc2, wv);
-      if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+      if constexpr (group_meta(FMT)) {
         const _Float16 sv = __builtin_bit_cast(_Float16, st.s[r]);
         const h2 s2 = {sv, sv};
 #pragma unroll
@@ -640,20 +673,20 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_grouped_kernel(const
 // K tile j (0..7) of a stage is 4 units, one per lane quad q: unit 8q + j. Its x fragments
 // sit in a register ring of lm_xring slots and are loaded lm_xring - 1 tiles ahead (W4 keeps
 // the ring at 2 so that its two-block kernel fits 256 VGPRs: two waves per SIMD).
-template <int FMT> constexpr bool lm_w6() { return wfmt(FMT) == WQ_FMT_W6E3M2; }   // two plane slices per unit
+template <int FMT> constexpr bool lm_w6() { return w6_geom(FMT); }   // two plane slices per unit (both FP6 layouts)
 template <int FMT> constexpr bool lm_w5() { return wfmt(FMT) == WQ_FMT_W5E2M2; }   // 16-byte slice + sign word
 template <int FMT> constexpr int lm_block() {
   return lm_w6<FMT>() ? 16 * 512 + 16 * 256 : lm_w5<FMT>() ? 16 * 512 + 16 * 128 : 16 * 512;
 }
 template <int FMT> constexpr int lm_loads() { return lm_w6<FMT>() ? 12 : 8; }
-template <int FMT, int MT> constexpr int lm_xring() { return wfmt(FMT) == WQ_FMT_W4G32 || MT > 1 ? 2 : 4; }
+template <int FMT, int MT> constexpr int lm_xring() { return group_meta(FMT) || MT > 1 ? 2 : 4; }
 constexpr int LM_MAX_MT = 4;   // 16-row tiles of x per launch (M up to 64 reads the weights once)
 constexpr int LM_WAVES = 4;   // waves per workgroup
 
 template <int FMT, int RB>
 struct LmStage {
   uint4 v[RB][lm_loads<FMT>()];
-  uint4 s[wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1], z[wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1];   // W4: 8 groups' fp16 scales / zeros
+  uint4 s[group_meta(FMT) ? RB : 1], z[group_meta(FMT) ? RB : 1];   // W4, W3: 8 groups' fp16 scales / zeros
   uint32_t sg[lm_w5<FMT>() ? RB : 1][lm_w5<FMT>() ? 8 : 1];   // FP5: the sign words
 };
 
@@ -684,10 +717,11 @@ __device__ __forceinline__ void lm_load(LmStage<FMT, RB>& st, const uint8_t* __r
       for (int i = 0; i < 8; ++i) {   // lane l -> row 2i + l/32, unit l%32
         const uint32_t nn = (uint32_t)(min(n0 + 16 * r + 2 * i + (lane >> 5), N - 1) - nb);
         const uint32_t j = (uint32_t)min(32 * h + (lane & 31), U - 1);   // past the row end: a valid unit, masked later
-        st.v[r][i] = ld_nt16(rowb + nn * row_bytes + 16u * j);
+        if constexpr (wfmt(FMT) == WQ_FMT_W3G32) st.v[r][i] = ld_nt12(rowb + nn * row_bytes + 12u * j);
+        else st.v[r][i] = ld_nt16(rowb + nn * row_bytes + 16u * j);
       }
     }
-    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+    if constexpr (group_meta(FMT)) {
       // lane (n, q): groups 32h + 8q .. +7 of row n (U is a multiple of 8, so a group of 8 lies
       // wholly inside the row or wholly past its end; one past the end reads the row's last 8)
       const uint32_t nn = (uint32_t)(min(n0 + 16 * r + (lane & 15), N - 1) - nb);
@@ -721,14 +755,14 @@ __device__ __forceinline__ void lm_load(LmStage<FMT, RB>& st, const uint8_t* __r
 }
 
 // The ragged last stage of a row (nv < 32 valid units): units nv..31 were loaded from clamped
-// addresses and must contribute nothing. W4 zeroes their group scales ((q - z) * 0 = 0); the other
-// formats zero their bytes, whose code 0 is the value +0.
+// addresses and must contribute nothing. W4 and W3 zero their group scales ((q - z) * 0 = 0); the
+// other formats zero their bytes, whose code 0 is the value +0.
 template <int FMT, int RB>
 __device__ __forceinline__ void lm_zero_past_row(LmStage<FMT, RB>& st, int nv, int lane) {
   auto keep = [](uint4 v, bool ok) { return ok ? v : make_uint4(0u, 0u, 0u, 0u); };
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
-    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+    if constexpr (group_meta(FMT)) {
       // lane (n, q) holds the scales of units 8q .. 8q+7 of the stage, two per dword
       const int v = nv - 8 * (lane >> 4);
       const uint32_t m[4] = {(v > 0 ? 0xFFFFu : 0u) | (v > 1 ? 0xFFFF0000u : 0u),
@@ -814,10 +848,12 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
     for (int mt = 0; mt < MT; ++mt) acc[r][mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   LmStage<FMT, RB> st;
-  constexpr int MS = wfmt(FMT) == WQ_FMT_W4G32 ? RB : 1;
-  uint4 cs[MS], cz[MS];   // W4: the metadata of the stage in LDS
+  constexpr int MS = group_meta(FMT) ? RB : 1;
+  uint4 cs[MS], cz[MS];   // W4, W3: the metadata of the stage in LDS
   constexpr int XR = lm_xring<FMT, MT>();
   [[maybe_unused]] const W4Masks w4m = wfmt(FMT) == WQ_FMT_W4G32 && !bf16_act(FMT) ? w4_masks() : W4Masks{};
+  [[maybe_unused]] const W3Masks w3m = wfmt(FMT) == WQ_FMT_W3G32 ? w3_masks() : W3Masks{};
+  [[maybe_unused]] const P24Masks p24m = wfmt(FMT) == WQ_FMT_W6E3M2_P24 ? p24_masks() : P24Masks{};
   // x fragments. Row m of the product depends only on row m of x, so the lanes of rows past M load
   // row M - 1 again and their outputs are not stored (loading nothing there, under an exec mask,
   // was slower). Units past the row end (the ragged last stage) contribute nothing because their
@@ -837,7 +873,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
   auto park = [&](int h) {   // the loaded stage h -> LDS (and W4 metadata -> cs, cz)
     if (32 * h + 32 > U) lm_zero_past_row<FMT, RB>(st, U - 32 * h, lane);   // wave-uniform: the ragged last stage
     lm_store<FMT, RB>(st, lds, lane);
-    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+    if constexpr (group_meta(FMT)) {
 #pragma unroll
       for (int r = 0; r < RB; ++r) { cs[r] = st.s[r]; cz[r] = st.z[r]; }
     }
@@ -862,7 +898,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
         const uint8_t* base = lds + r * lm_block<FMT>();
         Raw<wfmt(FMT)> raw;
         raw.a = *reinterpret_cast<const uint4*>(base + 512 * nl + 16 * (u ^ (nl & 7)));
-        if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2)
+        if constexpr (w6_geom(FMT))
           raw.b = *reinterpret_cast<const uint2*>(base + 8192 + 256 * nl + 8 * (u ^ ((2 * nl) & 31)));
         if constexpr (lm_w5<FMT>())
           raw.b = *reinterpret_cast<const uint32_t*>(base + 8192 + 128 * nl + 4 * (u ^ ((nl >> 1) & 7)));
@@ -879,6 +915,16 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
             const h2 s2 = {sv, sv};
 #pragma unroll
             for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
+          } else if constexpr (wfmt(FMT) == WQ_FMT_W3G32) {
+            h2 zc[3];
+            w3_consts(half_of(cz[r], j), zc);
+            decode_w3_unit(raw.a, zc, w3m, wv);
+            const _Float16 sv = __builtin_bit_cast(_Float16, half_of(cs[r], j));
+            const h2 s2 = {sv, sv};
+#pragma unroll
+            for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
+          } else if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2_P24) {
+            decode_p24(raw.a, raw.b, p24m, wv);
           } else {
             decode<FMT>(raw, h2{}, h2{}, wv);
           }
@@ -956,8 +1002,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   load_unit<FMT>(w, n, u, U, raw);
   h2 zc1 = {}, zc2 = {};
   float s = 1.0f;
-  if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
-    w4_consts(zeros[gid], zc1, zc2);
+  if constexpr (group_meta(FMT)) {
+    group_consts<FMT>(zeros[gid], zc1, zc2);
     s = f16_to_f32(scales[gid]);
   } else if constexpr (row_scaled<FMT>()) {
     s = f16_to_f32(scales[n]) * code_scale<FMT>();
@@ -1012,7 +1058,7 @@ struct GemvPlan {
 int gemv_waves_for(int fmt, int64_t N, int64_t K, int B) {
   const int64_t L = fmt == WQ_FMT_W8 ? 16 : fmt == WQ_FMT_F16 ? 8 : 32;
   const int64_t C = (K / L + 63) / 64, blocks = (N + B - 1) / B;
-  const int64_t target = fmt == WQ_FMT_W4G32 || fmt == WQ_FMT_W4E2M1 ? 1024 : 4096;
+  const int64_t target = fmt == WQ_FMT_W4G32 || fmt == WQ_FMT_W4E2M1 || fmt == WQ_FMT_W3G32 ? 1024 : 4096;
   static const int cand[] = {1, 2, 4};
   int WK = 1;
   for (int w : cand) {
@@ -1083,13 +1129,14 @@ struct LmPlan {
   int grid;   // workgroups
 };
 
-// The LDS-staged kernel serves W6 wherever the matrix cores run for it, and W4, FP4 and FP5
-// from M = 5 on and at M = 4 from N*K = 2^24 on, where it beats the VALU GEMV (W4 only when K
-// is a multiple of 256, so that a lane's 8 groups of metadata are one aligned 16-byte load).
+// The LDS-staged kernel serves W6 (both layouts: fmt is the planning layout, pfmt) wherever the
+// matrix cores run for it, and W4, W3, FP4 and FP5 from M = 5 on and at M = 4 from N*K = 2^24 on,
+// where it beats the VALU GEMV (W4 and W3 only when K is a multiple of 256, so that a lane's 8
+// groups of metadata are one aligned 16-byte load).
 bool use_lm(int fmt, int64_t M, int64_t N, int64_t K) {
   if (fmt == WQ_FMT_W6E3M2) return use_mfma(fmt, M, N);
-  if (fmt == WQ_FMT_W4G32 && K % 256) return false;
-  if (fmt != WQ_FMT_W4G32 && fmt != WQ_FMT_W4E2M1 && fmt != WQ_FMT_W5E2M2) return false;
+  if (group_meta(fmt) && K % 256) return false;
+  if (!group_meta(fmt) && fmt != WQ_FMT_W4E2M1 && fmt != WQ_FMT_W5E2M2) return false;
   return M > GEMV_MAX_M || (M == GEMV_MAX_M && N * K >= (int64_t(1) << 24));
 }
 
@@ -1122,7 +1169,7 @@ int lm_tiles(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 // which hold 64 rows only while K <= 2^25; longer rows take 16-row slabs.
 int64_t slab_rows(int fmt, int64_t K) {
   const bool lm = fmt == WQ_FMT_W6E3M2 || fmt == WQ_FMT_W4E2M1 || fmt == WQ_FMT_W5E2M2 ||
-                  (fmt == WQ_FMT_W4G32 && K % 256 == 0);
+                  (group_meta(fmt) && K % 256 == 0);
   return lm && K <= (int64_t(1) << 25) ? 16 * LM_MAX_MT : MFMA_M;
 }
 
@@ -1149,8 +1196,7 @@ hipError_t lm_launch(dim3 grid, size_t shm, hipStream_t s, const uint16_t* x, co
 template <int FMT>
 hipError_t launch_lm(int RB, int M, dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
                      const uint16_t* z, uint16_t* y, int N, int K, int WK, const GemvGroup* g) {
-  if constexpr (wfmt(FMT) == WQ_FMT_W4G32 || wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1 ||
-                wfmt(FMT) == WQ_FMT_W5E2M2) {
+  if constexpr (group_meta(FMT) || w6_geom(FMT) || wfmt(FMT) == WQ_FMT_W4E2M1 || wfmt(FMT) == WQ_FMT_W5E2M2) {
     const size_t shm = (size_t)LM_WAVES * RB * lm_block<FMT>();
     const int MT = lm_tiles(M);
     if (RB == 2) {
@@ -1168,12 +1214,12 @@ hipError_t launch_lm(int RB, int M, dim3 grid, hipStream_t s, const uint16_t* x,
 template <int FMT>
 hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
                              uint16_t* y, int M, int N, int K) {
-  if (use_lm(wfmt(FMT), M, N, K)) {
-    const LmPlan p = plan_lm(wfmt(FMT), N, K);
+  if (use_lm(pfmt(FMT), M, N, K)) {
+    const LmPlan p = plan_lm(pfmt(FMT), N, K);
     return launch_lm<FMT>(p.RB, M, dim3(p.grid), s, x, w, sc, z, y, N, K, p.WK, nullptr);
   }
-  if (!use_mfma(wfmt(FMT), M, N)) {
-    const GemvPlan p = plan_gemv(wfmt(FMT), N, K);
+  if (!use_mfma(pfmt(FMT), M, N)) {
+    const GemvPlan p = plan_gemv(pfmt(FMT), N, K);
     switch (M) {
       case 1: return launch_gemv_m<FMT, 1>(p, s, x, w, sc, z, y, N, K);
       case 2: return launch_gemv_m<FMT, 2>(p, s, x, w, sc, z, y, N, K);
@@ -1181,10 +1227,10 @@ hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w,
       default: return launch_gemv_m<FMT, 4>(p, s, x, w, sc, z, y, N, K);
     }
   }
-  if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1 || wfmt(FMT) == WQ_FMT_W5E2M2) {
+  if constexpr (w6_geom(FMT) || wfmt(FMT) == WQ_FMT_W4E2M1 || wfmt(FMT) == WQ_FMT_W5E2M2) {
     return hipErrorInvalidValue;   // W6, FP4 and FP5 on the matrix cores always take lm_kernel (use_lm)
   } else {
-    const MfmaPlan p = plan_mfma(wfmt(FMT), N, K);
+    const MfmaPlan p = plan_mfma(pfmt(FMT), N, K);
     const dim3 grid(p.grid), block(64 * p.WK);
     switch (p.RB) {
       case 4: return launch(mfma_kernel<FMT, 4>, grid, block, 0, s, x, w, sc, z, y, M, N, K, p.WK);
@@ -1240,7 +1286,7 @@ int largest_item(const int64_t* N, const int64_t* K, int count) {
 Family group_family(int fmt, int64_t M, const int64_t* N, const int64_t* K, int count) {
   const int big = largest_item(N, K, count);
   Family f = family_of(fmt, M, N[big], K[big]);
-  if (f == FAM_LM && fmt == WQ_FMT_W4G32)
+  if (f == FAM_LM && group_meta(fmt))
     for (int i = 0; i < count; ++i)
       if (K[i] % 256) f = FAM_MFMA;
   return f;
@@ -1273,7 +1319,7 @@ int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, cons
   if (!valid_fmt(fmt)) return WQ_ERR_FMT;
   if (!x || !w || !y || M < 0 || N < 0 || K < 0) return WQ_ERR_ARG;
   if (wfmt(fmt) != WQ_FMT_F16 && !sc) return WQ_ERR_ARG;
-  if (wfmt(fmt) == WQ_FMT_W4G32 && !z) return WQ_ERR_ARG;
+  if (group_meta(fmt) && !z) return WQ_ERR_ARG;
   if (M < 1 || N < 1 || K < 32 || K % 32) return WQ_ERR_SHAPE;
   if (N > INT32_MAX / 2 || K > (int64_t(1) << 26) || (N * (K / 32)) > INT32_MAX) return WQ_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (sc && !aligned16(sc)) || (z && !aligned16(z))) return WQ_ERR_ALIGN;
@@ -1283,7 +1329,7 @@ int check_linear_args(const uint16_t* x, const void* w, const uint16_t* sc, cons
 template <int FMT>
 hipError_t launch_grouped_mc(Family f, const GemvGroup& g, int M, int RB, int block_waves, int grid, hipStream_t s) {
   if (f == FAM_LM) return launch_lm<FMT>(RB, M, dim3(grid), s, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, &g);
-  if constexpr (wfmt(FMT) == WQ_FMT_W6E3M2 || wfmt(FMT) == WQ_FMT_W4E2M1 || wfmt(FMT) == WQ_FMT_W5E2M2) {
+  if constexpr (w6_geom(FMT) || wfmt(FMT) == WQ_FMT_W4E2M1 || wfmt(FMT) == WQ_FMT_W5E2M2) {
     return hipErrorInvalidValue;   // W6, FP4 and FP5 groups on the matrix cores are always FAM_LM
   } else {
     switch (RB) {
@@ -1320,7 +1366,7 @@ int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, c
   const uint8_t* w = static_cast<const uint8_t*>(packed_w);
   if (wq::pf_takes(fmt, M, &N, &K, 1))   // prefill-sized M: one tiled launch for all rows
     return wq::pf_launch(fmt, x, w, scales, zeros, y, M, N, K, stream);
-  const int64_t slab = slab_rows(wfmt(fmt), K);
+  const int64_t slab = slab_rows(pfmt(fmt), K);
   for (int64_t m0 = 0; m0 < M; m0 += slab) {
     const int mm = static_cast<int>(M - m0 < slab ? M - m0 : slab);
     const uint16_t* xs = x + m0 * K;
@@ -1342,7 +1388,7 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
   if (!valid_fmt(fmt)) return WQ_ERR_FMT;
   if (!packed || !w_out || N < 0 || K < 0) return WQ_ERR_ARG;
   if (wfmt(fmt) != WQ_FMT_F16 && !scales) return WQ_ERR_ARG;
-  if (wfmt(fmt) == WQ_FMT_W4G32 && !zeros) return WQ_ERR_ARG;
+  if (group_meta(fmt) && !zeros) return WQ_ERR_ARG;
   if (N < 1 || K < 32 || K % 32) return WQ_ERR_SHAPE;
   if (N * (K / 32) > INT32_MAX) return WQ_ERR_SHAPE;
   if (!aligned16(packed) || !aligned16(w_out) || (scales && !aligned16(scales)) || (zeros && !aligned16(zeros)))
@@ -1378,7 +1424,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
   // has anyway); each item keeps the K split its own plan gives for that B / RB
   if (count > 1 && wq::pf_takes(fmt, M, Ns, Ks, count))   // prefill-sized M: all items' tiles in one launch
     return wq::pf_launch_grouped(fmt, items, count, M, stream);
-  const int pf = wfmt(fmt);
+  const int pf = pfmt(fmt);
   const Family fam = group_family(pf, M, Ns, Ks, count);
   if (M > group_launch_rows(fam, pf, Ks, count)) {   // several slabs: one wq_linear per item
     for (int i = 0; i < count; ++i) {
@@ -1438,7 +1484,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
 const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
   static thread_local char buf[96];
   if (!valid_fmt(fmt) || M < 1 || N < 1 || K < 32 || K % 32) return "";
-  const int pf = wfmt(fmt);
+  const int pf = pfmt(fmt);
   if (wq::pf_takes(fmt, M, &N, &K, 1)) {
     snprintf(buf, sizeof(buf), "pf_kernel<%d>", fmt);
     return buf;
@@ -1465,7 +1511,7 @@ const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, 
     return buf;
   }
   const int big = largest_item(N, K, count);
-  const int pf = wfmt(fmt);
+  const int pf = pfmt(fmt);
   const Family fam = group_family(pf, M, N, K, count);
   if (M > group_launch_rows(fam, pf, K, count))
     return wq_linear_kernel_name(fmt, M, N[big], K[big]);   // separate launches: the largest item's

@@ -63,7 +63,7 @@ template <int FMT>
 struct PfStage {
   uint4 x[4];               // 16 B of each of 4 x rows
   Raw<wfmt(FMT)> w;         // one unit of one weight row
-  uint32_t sw, zw;          // W4: the aligned 32-bit words holding that unit's group scale and zero
+  uint32_t sw, zw;          // W4, W3: the aligned 32-bit words holding that unit's group scale and zero
 };
 
 // x: load i of wave v covers x rows 32 v + 8 i .. +7 of the tile, 8 lanes per row, so every
@@ -86,7 +86,7 @@ __device__ __forceinline__ void pf_load(PfStage<FMT>& st, const uint16_t* __rest
     st.x[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) + (size_t)mr * K * 2 + xo);
   }
   load_unit<FMT>(w, nr, u, U, st.w);
-  if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {   // the aligned 32-bit word holding each (no 16-bit loads,
+  if constexpr (group_meta(FMT)) {   // the aligned 32-bit word holding each (no 16-bit loads,
     const size_t gi = (size_t)nr * U + u;       // whose partial register writes make the compiler wait for
     st.sw = reinterpret_cast<const uint32_t*>(scales)[gi >> 1];   // every load in flight); the halves
     st.zw = reinterpret_cast<const uint32_t*>(zeros)[gi >> 1];    // are taken when the stage is parked
@@ -100,7 +100,7 @@ __device__ __forceinline__ void pf_park(const PfStage<FMT>& st, uint8_t* xs, uin
   const int t = threadIdx.x;
   const bool xunit_ok = pf_xunit(t, step) < U;
   uint16_t sb = 0, zb = 0;
-  if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {   // the unit's half of each metadata word
+  if constexpr (group_meta(FMT)) {   // the unit's half of each metadata word
     const int sh = 16 * (int)(((size_t)min(n0 + r, N - 1) * U + min(2 * step + h, U - 1)) & 1);
     sb = (uint16_t)(st.sw >> sh);
     zb = (uint16_t)(st.zw >> sh);
@@ -110,9 +110,9 @@ __device__ __forceinline__ void pf_park(const PfStage<FMT>& st, uint8_t* xs, uin
     decode_bf16<FMT>(st.w, sb, zb, wv);
   } else {
     h2 zc1 = {}, zc2 = {};
-    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) w4_consts(zb, zc1, zc2);
+    if constexpr (group_meta(FMT)) group_consts<FMT>(zb, zc1, zc2);
     decode<FMT>(st.w, zc1, zc2, wv);
-    if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
+    if constexpr (group_meta(FMT)) {
       const _Float16 sv = __builtin_bit_cast(_Float16, sb);
       const h2 s2 = {sv, sv};
 #pragma unroll
@@ -276,7 +276,7 @@ namespace wq {
 //    not take runs one call per linear, so the tiles of all its linears count.)
 // So the down projections (K = 11008, 28672; 32 to 128 tiles) keep the decode kernels.
 bool pf_takes(int code, int64_t M, const int64_t* N, const int64_t* K, int count) {
-  const int w = wfmt(code);
+  const int w = pfmt(code);
   const bool rows16 = w == WQ_FMT_F16 || w == WQ_FMT_W8;
   if (M < (rows16 ? 17 : w == WQ_FMT_W5E2M2 ? PF_MIN_M_ANY + 16 : PF_MIN_M_ANY) || M > INT32_MAX) return false;
   int64_t tiles = 0, kmax = 0, tile_steps = 0;
@@ -295,7 +295,7 @@ bool pf_takes(int code, int64_t M, const int64_t* N, const int64_t* K, int count
     const double steps = chain > tile_steps / 256.0 ? (double)chain : tile_steps / 256.0;
     return steps * (w == WQ_FMT_F16 ? 2.1 : 1.58) <= (double)((M + 15) / 16) * mbytes;
   }
-  return chain <= (w == WQ_FMT_W4G32 ? 2 : 4) * tiles;
+  return chain <= (group_meta(w) ? 2 : 4) * tiles;
 }
 
 int pf_launch(int code, const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros,

@@ -43,6 +43,10 @@ def pack_host(fmt, w):
         return wq.wq_pack_fp4(w) + (None,)
     if fmt == wq.FMT_W5E2M2:
         return wq.wq_pack_fp5(w) + (None,)
+    if fmt == wq.FMT_W3G32:
+        return wq.wq_pack_int3(w)
+    if fmt == wq.FMT_W6E3M2_P24:
+        return wq.wq_pack_fp6_p24(w) + (None,)
     if fmt == wq.FMT_F16:
         return np.asarray(w, dtype=np.float32).astype(np.float16).view(np.uint8).reshape(-1), None, None
     raise ValueError("format %r" % fmt)

@@ -44,12 +44,20 @@ WORKLOADS = {
     "llama7b_w4g32_bf16_linears": ("w4g32_bf16", [(4096, 4096), (11008, 4096), (4096, 11008)], [1, 4, 8, 16]),
     "llama70b_w6e3m2_bf16_linears": ("w6e3m2_bf16", [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)],
                                      [1, 4, 8, 16]),
+    # the Llama-7B linears with int3 weights (a further bit width)
+    "llama7b_w3g32_linears": ("w3g32", [(4096, 4096), (11008, 4096), (4096, 11008)], [1, 4, 8, 16]),
+    # FP6 in the 2+4 split layout: the same draws as the W6 workloads (same stream), so that the two
+    # layouts of one set of weights can be timed side by side
+    "llama70b_w6e3m2_p24_linears": ("w6e3m2_p24", [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)],
+                                    [1, 4, 8, 16]),
+    "llama7b_w6e3m2_p24_linears": ("w6e3m2_p24", [(4096, 4096), (11008, 4096), (4096, 11008)], [1, 4, 8, 16]),
 }
 # stream index of each workload, so that every workload draws from its own stream
 WORKLOAD_STREAM = {"w8_single_1024x1024": 0, "llama7b_w4g32_linears": 1, "llama70b_w6e3m2_linears": 2,
                    "llama70b_w6e3m2_tp8_shard": 3, "llama7b_w4e2m1_linears": 4, "llama7b_w4g32_bf16_linears": 5,
                    "llama70b_w6e3m2_bf16_linears": 6, "llama7b_w5e2m2_linears": 7, "llama7b_w8_linears": 8,
-                   "llama7b_w6e3m2_linears": 9}
+                   "llama7b_w6e3m2_linears": 9, "llama7b_w3g32_linears": 12, "llama70b_w6e3m2_p24_linears": 2,
+                   "llama7b_w6e3m2_p24_linears": 9}
 
 
 # Decode sweeps over a whole random-init model: the linears of one layer, the layer count, and

@@ -12,8 +12,9 @@ import os
 import numpy as np
 
 FMT_F16, FMT_W8, FMT_W4G32, FMT_W6E3M2, FMT_W4E2M1, FMT_BF16, FMT_W5E2M2 = 0, 1, 2, 3, 4, 5, 6
+FMT_W3G32, FMT_W6E3M2_P24 = 7, 8
 FMT_NAMES = {"f16": FMT_F16, "w8": FMT_W8, "w4g32": FMT_W4G32, "w6e3m2": FMT_W6E3M2, "w4e2m1": FMT_W4E2M1,
-             "bf16": FMT_BF16, "w5e2m2": FMT_W5E2M2}
+             "bf16": FMT_BF16, "w5e2m2": FMT_W5E2M2, "w3g32": FMT_W3G32, "w6e3m2_p24": FMT_W6E3M2_P24}
 # OR-ed into a format code: bfloat16 activations (x, y and dequantized weights) instead of fp16
 ACT_F16, ACT_BF16 = 0, 0x100
 
@@ -70,6 +71,8 @@ def lib():
         L.wq_pack_fp6.argtypes = [_p, _i64, _i64, _p, _p]
         L.wq_pack_fp4.argtypes = [_p, _i64, _i64, _p, _p]
         L.wq_pack_fp5.argtypes = [_p, _i64, _i64, _p, _p]
+        L.wq_pack_int3.argtypes = [_p, _i64, _i64, _p, _p, _p]
+        L.wq_pack_fp6_p24.argtypes = [_p, _i64, _i64, _p, _p]
         L.wq_unpack.argtypes = [ctypes.c_int, _p, _p, _p, _i64, _i64, _p, _p, _p]
         L.wq_dequant.argtypes = [ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _p]
         L.wq_linear.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, ctypes.c_int, _p]
@@ -79,7 +82,8 @@ def lib():
         L.wq_linear_kernel_name.argtypes = [ctypes.c_int, _i64, _i64, _i64]
         L.wq_linear_grouped_kernel_name.restype = ctypes.c_char_p
         L.wq_linear_grouped_kernel_name.argtypes = [ctypes.c_int, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.c_int]
-        for name in ("wq_pack_int8", "wq_pack_int4", "wq_pack_fp6", "wq_pack_fp4", "wq_pack_fp5", "wq_unpack",
+        for name in ("wq_pack_int8", "wq_pack_int4", "wq_pack_fp6", "wq_pack_fp4", "wq_pack_fp5", "wq_pack_int3",
+                     "wq_pack_fp6_p24", "wq_unpack",
                      "wq_dequant", "wq_linear"):
             getattr(L, name).restype = ctypes.c_int
         # decode-step calls (include/wq_decode.h)
@@ -213,6 +217,24 @@ def wq_pack_fp5(w):
     n, k = w.shape
     packed, scales, _ = _alloc(FMT_W5E2M2, n, k)
     _check(lib().wq_pack_fp5(_host_ptr(w), n, k, _host_ptr(packed), _host_ptr(scales)), "wq_pack_fp5")
+    return packed, scales
+
+
+def wq_pack_int3(w):
+    """fp32 W [N,K] -> (packed uint8, scales uint16 [N*K/32], zeros uint16 [N*K/32])."""
+    w = _w_host(w)
+    n, k = w.shape
+    packed, scales, zeros = _alloc(FMT_W3G32, n, k)
+    _check(lib().wq_pack_int3(_host_ptr(w), n, k, _host_ptr(packed), _host_ptr(scales), _host_ptr(zeros)), "wq_pack_int3")
+    return packed, scales, zeros
+
+
+def wq_pack_fp6_p24(w):
+    """fp32 W [N,K] -> (packed uint8 in the 2+4 split layout, scales uint16 [N])."""
+    w = _w_host(w)
+    n, k = w.shape
+    packed, scales, _ = _alloc(FMT_W6E3M2_P24, n, k)
+    _check(lib().wq_pack_fp6_p24(_host_ptr(w), n, k, _host_ptr(packed), _host_ptr(scales)), "wq_pack_fp6_p24")
     return packed, scales
 
 
