@@ -136,14 +136,19 @@ CSRC = os.path.join(ROOT, "weight_only_quantized_dequant_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
+# The sources that define the decode-sized linear kernels (GEMV, fragment-load and LDS-staged
+# matrix-core kernels) and the decoders they share; the prefill and decode-step kernels live in
+# files of their own and do not change these kernels.
+LINEAR_KERNEL_SOURCES = ("wq_device.h", "wq_internal.h", "wq_kernels.hip")
+
+
 def kernel_source_hash():
-    """sha256[:16] over the device sources (csrc/*.hip and csrc/*.h, by name)."""
+    """sha256[:16] over the linear-kernel sources (LINEAR_KERNEL_SOURCES, in that order)."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in LINEAR_KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -566,7 +571,7 @@ def run_decode(args, torch):
            "dtype": "f16", "data": "synthetic",
            "config": {"workload": "llama2_7b_decode_step", "weights": args.weights, "M": m, "context": args.context,
                       "max_seq": S, "layers": cfg["layers"], "vocab": cfg["vocab"],
-                      "launches_per_step": 3 + 8 * cfg["layers"],
+                      "launches_per_step": dec.launches_per_step(),
                       "timing": "HIP graph of one decode step, replayed; events on the launch stream"},
            "weight_GB_per_step": round(wbytes / 1e9, 3), "kv_cache_GB_read_per_step": round(kv_bytes / 1e9, 3),
            "weight_GB/s": round(wbytes / (ms * 1e-3) / 1e9, 1),
@@ -602,8 +607,9 @@ def decode_cpu_baseline(cfg, fmt, host, context):
         return oracle.dequant_fp16(f, oracle.unpack_vectorized(f, p, n, k), s, z)
     with limit:
         t0 = time.perf_counter()
-        shapes = {nm: (n, k) for nm, n, k in decode.linear_shapes(cfg)}
+        shapes = decode.device_shapes(cfg)
         W = {nm: dq(L[nm], *shapes[nm]) for nm in shapes}
+        W["gate"], W["up"] = W["gu"][0::2], W["gu"][1::2]   # gate/up are held as interleaved rows
         h = D.rmsnorm(x, oracle.fp16_from_bits(L["attn_norm"]), cfg["eps"])
         q, k, v = D.lin(h, W["q"]), D.lin(h, W["k"]), D.lin(h, W["v"])
         ck[:, context] = D.f16(D.rope(k, context, hd, cfg["theta"]))

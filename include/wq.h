@@ -183,7 +183,7 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
  * y[M,N] = x[M,K] . dequant(packed_w)[N,K]^T with fp16 x and y (bfloat16 with WQ_ACT_BF16 in
  * fmt; row-major, row strides K and N) and fp32 accumulation; the kernel reads every packed byte
  * once and never writes dequantized weights to memory. All pointers are device pointers, 16-byte
- * aligned; zeros only for W4 (else may be NULL). y must not overlap the inputs.
+ * aligned; zeros only for W4 and W3 (else may be NULL). y must not overlap the inputs.
  * M of any size. The decode kernels take up to 64 rows of x per launch for W6, FP4, FP5 and W4
  * with K a multiple of 256, up to 16 for W8, fp16/bf16 weights and other W4 shapes, and more rows
  * run as several such launches. The tiled prefill kernel takes all rows in one launch from 193
@@ -200,7 +200,7 @@ typedef struct {
   const uint16_t* x;       /* [M,K] fp16 */
   const void* packed_w;    /* packed weights of fmt */
   const uint16_t* scales;  /* as for wq_linear */
-  const uint16_t* zeros;   /* W4 only, else NULL */
+  const uint16_t* zeros;   /* W4 and W3 only, else NULL */
   uint16_t* y;             /* [M,N] fp16 output */
   int64_t N, K;
 } wq_linear_item;
@@ -218,6 +218,24 @@ typedef struct {
  * launch (see wq_linear), every item runs as its own wq_linear call instead. Errors: as wq_linear, per item, all checked before any launch; WQ_ERR_ARG
  * also for count outside 0..16 or items == NULL. */
 int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt, void* stream);
+
+/* On the device: the first half of a Llama feed-forward in one launch, act = silu(gate) * up
+ * (silu(g) = g / (1 + e^-g)), with the gate and up projections as one weight matrix of 2F rows:
+ * row 2i is the gate projection's row i and row 2i+1 the up projection's row i (quantize and
+ * pack the interleaved fp32 matrix [2F, K] with any wq_pack_*: every format's metadata is per row
+ * or per group within a row, so the codes are those of the two matrices packed apart). The
+ * speed-up strategies page (sharktoolz.top, section 6) and the gpt-fast write-up (part on
+ * torch.compile) motivate the decode step this serves: fewer, larger launches per token.
+ * act[m, i] = fp16(g / (1 + exp(-g)) * u) in float32, where g and u are rows 2i and 2i+1 of
+ * y = x . dequant(packed_w)^T as wq_linear computes them with its decode kernels (rounded to
+ * fp16 each); that is, the result equals wq_linear on the [2F, K] matrix followed by
+ * wq_silu_mul (wq_decode.h) on its even and odd columns, bit for bit, wherever wq_linear takes
+ * a decode kernel for the shape (wq_linear_kernel_name not "pf_kernel..."), without the 2F
+ * outputs ever reaching memory. Prefill-sized M runs as several decode-kernel launches (never
+ * the tiled prefill kernel). x [M, K] fp16; act [M, F] fp16; F >= 1; fp16 activations only
+ * (WQ_ACT_BF16 in fmt: WQ_ERR_FMT). Other arguments and errors as wq_linear with N = 2F. */
+int wq_linear_silu(const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros,
+                   uint16_t* act, int64_t M, int64_t F, int64_t K, int fmt, void* stream);
 
 /* Name of the kernel wq_linear launches for (fmt, M, N, K) (for profiles), or "" if the
  * arguments are invalid. Host only; static storage. */

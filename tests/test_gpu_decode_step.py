@@ -160,7 +160,7 @@ def _check_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, p, theta=10000.0, calls=
 
 @pytest.mark.parametrize("hd", [64, 128])
 @pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 2)])
-@pytest.mark.parametrize("p", [0, 1, 64, 127, 128, 129, 300, 511])
+@pytest.mark.parametrize("p", [0, 1, 63, 64, 65, 127, 128, 129, 300, 511])
 def test_rope_attention(hd, H, Hkv, p):
     m, S = 2, 512
     q, k, v, ck, cv = _attention_case(m, H, Hkv, hd, S, p, 1)
@@ -168,7 +168,7 @@ def test_rope_attention(hd, H, Hkv, p):
 
 
 def test_rope_attention_short_cache_needs_no_workspace():
-    m, H, Hkv, hd, S = 3, 4, 1, 128, 128
+    m, H, Hkv, hd, S = 3, 4, 1, 128, 64
     assert wq.wq_attention_workspace_bytes(m, H, hd, S) == 0
     q, k, v, ck, cv = _attention_case(m, H, Hkv, hd, S, 40, 2)
     _check_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, 40)
@@ -181,7 +181,7 @@ def test_rope_attention_position_past_the_cache_is_clamped():
 
 
 def test_rope_attention_llama7b_shape_long_context():
-    # Llama-2-7B heads (32 x 128) with 2048 cached positions at position 1500: 24 chunks
+    # Llama-2-7B heads (32 x 128) with 2048 cached positions at position 1500: 24 chunks of 64
     m, H, Hkv, hd, S, p = 1, 32, 32, 128, 2048, 1500
     q, k, v, ck, cv = _attention_case(m, H, Hkv, hd, S, p, 4)
     _check_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, p, calls=2)

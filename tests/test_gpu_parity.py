@@ -315,3 +315,76 @@ def test_p24_layout_gives_the_w6_outputs_bit_for_bit(n, k, m):
     ya, yb = a.linear(x), b.linear(x)
     assert np.array_equal(ya, yb), "%d of %d differ (%s)" % (int((ya != yb).sum()), ya.size,
                                                             wq.wq_linear_kernel_name(wq.FMT_W6E3M2_P24, m, n, k))
+
+
+# ------------------------------------------------------------------ gate/up with silu in one launch
+SILU_CASES = [(1, 64, 256), (3, 64, 256), (4, 5504, 4096), (1, 5504, 4096), (2, 700, 4256), (5, 300, 2304),
+              (8, 5504, 4096), (16, 4100, 2304), (33, 200, 4096), (13, 64, 4128), (70, 300, 512)]
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_ID[f])
+@pytest.mark.parametrize("m,f,k", SILU_CASES)
+def test_linear_silu_equals_linear_then_silu_mul(fmt, m, f, k):
+    # one [2F, K] matrix of interleaved gate/up rows: wq_linear_silu must give exactly what
+    # wq_linear on that matrix followed by wq_silu_mul on its even and odd columns gives, wherever
+    # wq_linear takes a decode kernel; and silu(gate) * up of the oracle's linear within the bound
+    torch = torch_cuda()
+    from oracle import decode as D
+    wg, wu = _weights(f, k, 11 * f + k), _weights(f, k, 13 * f + k + 1)
+    w = np.empty((2 * f, k), dtype=np.float32)
+    w[0::2], w[1::2] = wg, wu
+    _, x = inputs.small_case(4000 + m + f, 1, k, m)
+    dw = DeviceWeights(fmt, w)
+    act = torch.empty((m, f), dtype=torch.int16, device="cuda:0")
+    wq.wq_linear_silu(dev(x), dw.packed, dw.scales, dw.zeros, act, m, f, k, fmt)
+    torch.cuda.synchronize()
+    got = host_bits(act)
+    name = wq.wq_linear_kernel_name(fmt, m, 2 * f, k)
+    y = dw.linear(x)
+    if not name.startswith("pf_kernel"):
+        n8 = (m * f + 7) // 8 * 8   # wq_silu_mul takes a multiple of 8 values: pad with zeros
+        pad = lambda a: np.concatenate([np.ascontiguousarray(a).reshape(-1), np.zeros(n8 - m * f, dtype=np.uint16)])
+        g, u = dev(pad(y[:, 0::2])), dev(pad(y[:, 1::2]))
+        ref = torch.empty(n8, dtype=torch.int16, device="cuda:0")
+        wq.wq_silu_mul(g, u, ref, n8)
+        torch.cuda.synchronize()
+        want = host_bits(ref)[:m * f].reshape(m, f)
+        assert np.array_equal(got, want), "%d of %d differ (%s)" % (int((got != want).sum()), got.size, name)
+    # against the oracle: silu(g) * u of the oracle's fp16-rounded linear outputs; the device's g and u
+    # are each within the linear's bound of the oracle's, and silu * u moves that error by at most
+    # |d(silu(g) u)/dg| <= 1.1 |u| and |silu(g)| in u
+    wd = w.astype(np.float16).view(np.uint16) if fmt == wq.FMT_F16 else oracle_rows(fmt, w)[0]
+    yref = oracle.linear_ref(x, wd)
+    bound = oracle.error_bound(x, wd, yref)
+    gv, uv = oracle.fp16_from_bits(oracle.fp16_bits(yref[:, 0::2])), oracle.fp16_from_bits(oracle.fp16_bits(yref[:, 1::2]))
+    want = oracle.fp16_from_bits(oracle.fp16_bits(D.silu_mul(gv, uv)))
+    silu = np.abs(gv / (1 + np.exp(-gv)))
+    tol = (1.1 * np.abs(uv) * (bound[:, 0::2] + 2.0 ** -11 * np.abs(gv)) + (silu + 1e-3) * (bound[:, 1::2] + 2.0 ** -11 * np.abs(uv))
+           + 2.0 ** -10 * np.abs(want) + 2.0 ** -24)
+    err = np.abs(oracle.fp16_from_bits(got) - want)
+    assert np.all(err <= tol), float((err / tol).max())
+
+
+def test_linear_silu_graph_replays_match_eager():
+    torch = torch_cuda()
+    m, f, k = 1, 5504, 4096
+    w = _weights(2 * f, k, 99)
+    _, x = inputs.small_case(98, 1, k, m)
+    dw = DeviceWeights(wq.FMT_W4G32, w)
+    xd = dev(x)
+    eager = torch.empty((m, f), dtype=torch.int16, device="cuda:0")
+    wq.wq_linear_silu(xd, dw.packed, dw.scales, dw.zeros, eager, m, f, k, wq.FMT_W4G32)
+    torch.cuda.synchronize()
+    out = torch.zeros((m, f), dtype=torch.int16, device="cuda:0")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            wq.wq_linear_silu(xd, dw.packed, dw.scales, dw.zeros, out, m, f, k, wq.FMT_W4G32)
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out), host_bits(eager))

@@ -1,6 +1,7 @@
 """CPU tests of libwq's host half: exported symbols, sizes, quantize+pack bit-identical to the oracle,
 unpack round trips and every synchronous error path. No GPU calls."""
 
+import ctypes
 import os
 import re
 
@@ -427,6 +428,18 @@ def test_fp5_kernel_choice():
     assert wq.wq_linear_grouped_kernel_name(f, 1, [(4096, 4096), (11008, 4096)]) == "gemv_grouped_kernel<6, 1, 4>"
 
 
+def test_linear_silu_rejects_bad_arguments_before_launch():
+    L = wq.lib()
+    a = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails its checks first
+    assert L.wq_linear_silu(a, a, a, a, a, 1, 64, 256, wq.FMT_W8 | wq.ACT_BF16, None) == -3
+    assert L.wq_linear_silu(a, a, a, a, a, 1, 64, 256, 9, None) == -3
+    assert L.wq_linear_silu(a, a, a, a, a, 1, 0, 256, wq.FMT_W8, None) == -2
+    assert L.wq_linear_silu(a, a, a, a, a, 1, -1, 256, wq.FMT_W8, None) == -1
+    assert L.wq_linear_silu(a, a, a, a, a, 1, 64, 48, wq.FMT_W8, None) == -2
+    assert L.wq_linear_silu(a, a, a, None, a, 1, 64, 256, wq.FMT_W4G32, None) == -1   # W4 needs zeros
+    assert L.wq_linear_silu(a, a, a, a, ctypes.c_void_p((1 << 20) + 2), 1, 64, 256, wq.FMT_W8, None) == -5
+
+
 def test_int3_and_split_fp6_kernel_choice():
     # int3 follows W4's plan (groups of 32: the LDS-staged kernel needs K a multiple of 256, else
     # the fragment-load kernel), the 2+4 FP6 layout follows W6's (same slices, other decode);
@@ -534,7 +547,7 @@ def test_decode_entry_points_reject_bad_arguments_before_launch():
     assert L.wq_rope_attention(a, a, a, a, a, a, a, a, a, 1, 6, 4, 128, 16, None, 0, None) == -2   # 6 % 4
     assert L.wq_rope_attention(a, a, a, a, a, a, a, a, a, 1, 4, 4, 128, 200, None, 0, None) == -1  # no workspace
     need = wq.wq_attention_workspace_bytes(1, 4, 128, 200)
-    assert need > 0 and wq.wq_attention_workspace_bytes(1, 4, 128, 128) == 0
+    assert need > 0 and wq.wq_attention_workspace_bytes(1, 4, 128, 64) == 0 and wq.wq_attention_workspace_bytes(1, 4, 128, 65) > 0
     assert L.wq_rope_attention(a, a, a, a, a, a, a, a, a, 1, 4, 4, 128, 200, a, need - 1, None) == -1
 
 

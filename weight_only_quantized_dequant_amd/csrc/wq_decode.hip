@@ -10,8 +10,9 @@
 //  * Every kernel reads the decode position and the token ids from device memory, so a step is
 //    captured once as a HIP graph and replayed for step after step; wq_argmax_next advances them.
 //  * Attention of one new token (flash-decoding style): the positions 0..pos are cut into
-//    chunks of 128, one workgroup per (chunk, query head, sequence), so that even a short context
-//    spreads over many CUs. A workgroup first issues the loads of all its key and value rows (16
+//    chunks of 64, one workgroup per (chunk, query head, sequence), so that even a short context
+//    spreads over the CUs (Llama-2-7B at 512 positions: 256 workgroups; chunks of 128 left half
+//    the CUs idle). A workgroup first issues the loads of all its key and value rows (16
 //    lanes per position, a 16-byte slice each: 256-byte coalesced reads), then rotates its query
 //    (and, in the last chunk, the new key), scores its positions with a 16-lane shuffle sum, takes
 //    the softmax of its chunk in LDS and sums the weighted value slices. Chunks meet in a workspace:
@@ -34,7 +35,7 @@
 namespace {
 
 constexpr int DEC_THREADS = 256;
-constexpr int ATT_CHUNK = 128;   // positions per attention workgroup
+constexpr int ATT_CHUNK = 64;    // positions per attention workgroup (at 512 cached positions, 8 per head)
 
 __device__ __forceinline__ float f16v(uint32_t bits) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits); }
 __device__ __forceinline__ uint32_t to_f16(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
@@ -165,12 +166,14 @@ __global__ __launch_bounds__(DEC_THREADS) void silu_mul_kernel(const uint16_t* _
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= n8) return;
   const uint4 g = reinterpret_cast<const uint4*>(gate)[c], u = reinterpret_cast<const uint4*>(up)[c];
-  auto f = [](float gv, float uv) { return to_f16(gv / (1.0f + expf(-gv)) * uv); };
+  auto f = [](uint32_t gw, uint32_t uw) {   // both fp16 halves of a word
+    return (uint32_t)silu_mul_f16(gw & 0xFFFFu, uw & 0xFFFFu) | ((uint32_t)silu_mul_f16(gw >> 16, uw >> 16) << 16);
+  };
   uint4 o;
-  o.x = f(lo16(g.x), lo16(u.x)) | (f(hi16(g.x), hi16(u.x)) << 16);
-  o.y = f(lo16(g.y), lo16(u.y)) | (f(hi16(g.y), hi16(u.y)) << 16);
-  o.z = f(lo16(g.z), lo16(u.z)) | (f(hi16(g.z), hi16(u.z)) << 16);
-  o.w = f(lo16(g.w), lo16(u.w)) | (f(hi16(g.w), hi16(u.w)) << 16);
+  o.x = f(g.x, u.x);
+  o.y = f(g.y, u.y);
+  o.z = f(g.z, u.z);
+  o.w = f(g.w, u.w);
   reinterpret_cast<uint4*>(out)[c] = o;
 }
 

@@ -343,6 +343,14 @@ __device__ __forceinline__ void group_consts(uint16_t zbits, h2& zc1, h2& zc2) {
 
 __device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
+// The feed-forward's gate: silu(g) * u = g / (1 + e^-g) * u for fp16 g and u, in float32, rounded
+// once to fp16. One definition for the stand-alone kernel and the fused linear epilogue, so that
+// both give the same bits.
+__device__ __forceinline__ uint16_t silu_mul_f16(uint16_t g, uint16_t u) {
+  const float gv = f16_to_f32(g), uv = f16_to_f32(u);
+  return __builtin_bit_cast(uint16_t, (_Float16)(gv / (1.0f + expf(-gv)) * uv));
+}
+
 // The weights of a unit as bfloat16 pairs for bfloat16 activations (same pair order as
 // decode): W8 q, W6 e3m2(code), FP4 e2m1(code), BF16 the weights, all exact, with the row
 // scale applied after the sum; W4 (q - z) s rounded once to bfloat16, since its scale changes

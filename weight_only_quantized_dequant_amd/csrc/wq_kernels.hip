@@ -373,8 +373,10 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<FMT, M, B>& st, flo
 }
 
 // One workgroup's work: R = 4 / WK row blocks of B rows of one linear; the WK waves of
-// each block split K.
-template <int FMT, int M, int B>
+// each block split K. SILU (B even): rows 2i and 2i+1 are a gate row and an up row, and the
+// output is silu(gate) * up of each pair (act [M, N / 2]), formed from the two rows' fp16
+// results exactly as wq_silu_mul forms it.
+template <int FMT, int M, int B, bool SILU = false>
 __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                           const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
                                           uint16_t* __restrict__ y, int N, int K, int block, int WK) {
@@ -415,17 +417,30 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const 
   }
 
   if (WK == 1) {   // each wave is its own row block: no cross-wave step
+    [[maybe_unused]] uint16_t o16[B][M];
 #pragma unroll
     for (int b = 0; b < B; ++b)
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float t = wave_sum_to_lane63(acc[b][m]);
         const int n = row0 + b;
-        if (lane == 63 && n < N) {
+        if constexpr (SILU) {
+          if constexpr (row_scaled<FMT>()) t *= f16_to_f32(scales[min(n, N - 1)]) * code_scale<FMT>();
+          o16[b][m] = out16<FMT>(t);
+        } else if (lane == 63 && n < N) {
           if constexpr (row_scaled<FMT>()) t *= f16_to_f32(scales[n]) * code_scale<FMT>();
           y[(size_t)m * N + n] = out16<FMT>(t);
         }
       }
+    if constexpr (SILU) {
+      static_assert(B % 2 == 0, "gate/up pairs need an even row count per wave");
+      if (lane == 63)
+#pragma unroll
+        for (int b = 0; b < B; b += 2)
+          if (row0 + b < N)
+#pragma unroll
+            for (int m = 0; m < M; ++m) y[(size_t)m * (N / 2) + (row0 + b) / 2] = silu_mul_f16(o16[b][m], o16[b + 1][m]);
+    }
     return;
   }
   __shared__ float red[GEMV_WAVES][B * M];
@@ -437,6 +452,20 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const 
       if (lane == 63) red[wave_id][b * M + m] = t;
     }
   __syncthreads();
+  if constexpr (SILU) {
+    if (wave == 0) {   // lane b * M + m holds (b, m); its pair partner (b + 1, m) is M lanes up
+      const int b = lane / M, m = lane % M, n = row0 + b;
+      const bool mine = lane < B * M && n < N;
+      float t = 0.0f;
+      if (lane < B * M)
+        for (int i = 0; i < WK; ++i) t += red[sub * WK + i][lane];   // fixed order: deterministic
+      if constexpr (row_scaled<FMT>()) t *= mine ? f16_to_f32(scales[n]) * code_scale<FMT>() : 1.0f;
+      const uint16_t o = out16<FMT>(t);
+      const uint16_t ou = (uint16_t)__shfl_down((int)o, M, 64);
+      if (mine && (b & 1) == 0) y[(size_t)m * (N / 2) + n / 2] = silu_mul_f16(o, ou);
+    }
+    return;
+  }
   if (wave == 0 && lane < B * M) {
     const int b = lane / M, m = lane % M, n = row0 + b;
     float t = 0.0f;
@@ -455,6 +484,16 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_kernel(const uint16_t* _
                                                                    const uint16_t* __restrict__ zeros,
                                                                    uint16_t* __restrict__ y, int N, int K, int WK) {
   gemv_body<FMT, M, B>(x, w, scales, zeros, y, N, K, blockIdx.x, WK);
+}
+
+// gemv_kernel whose N rows are gate/up pairs: act [M, N / 2] = silu(gate) * up (see gemv_body).
+template <int FMT, int M, int B>
+__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_silu_kernel(const uint16_t* __restrict__ x,
+                                                                   const uint8_t* __restrict__ w,
+                                                                   const uint16_t* __restrict__ scales,
+                                                                   const uint16_t* __restrict__ zeros,
+                                                                   uint16_t* __restrict__ act, int N, int K, int WK) {
+  gemv_body<FMT, M, B, true>(x, w, scales, zeros, act, N, K, blockIdx.x, WK);
 }
 
 // Several independent linears of one format and one M in a single launch: the grid is the
@@ -556,7 +595,7 @@ __device__ __forceinline__ void mfma_compute(const MfmaStage<FMT, RB>& st, f4 (&
   }
 }
 
-template <int FMT, int RB>
+template <int FMT, int RB, bool SILU = false>
 __device__ __forceinline__ void mfma_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                            const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
                                            uint16_t* __restrict__ y, int M, int N, int K, int block, int WK) {
@@ -602,6 +641,18 @@ __device__ __forceinline__ void mfma_body(const uint16_t* __restrict__ x, const 
   // by the group's wave r % WK, which adds the WK partials in a fixed order.
   auto store = [&](int r, const f4& t) {
     const int n = n0 + 16 * r + nl;
+    if constexpr (SILU) {   // rows n, n ^ 1 (a gate/up pair) sit in lanes l, l ^ 1 (wave-uniform call)
+      float sc = 1.0f;
+      if constexpr (row_scaled<FMT>()) sc = f16_to_f32(scales[min(n, N - 1)]) * code_scale<FMT>();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * q + i;
+        const uint16_t o = out16<FMT>(t[i] * sc);
+        const uint16_t ou = (uint16_t)__builtin_amdgcn_update_dpp(0, (int)o, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+        if (m < M && n < N && (nl & 1) == 0) y[(size_t)m * (N / 2) + n / 2] = silu_mul_f16(o, ou);
+      }
+      return;
+    }
     if (n >= N) return;
     float sc = 1.0f;
     if constexpr (row_scaled<FMT>()) sc = f16_to_f32(scales[n]) * code_scale<FMT>();
@@ -637,6 +688,17 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_kernel(const uint16_
                                                                      uint16_t* __restrict__ y, int M, int N, int K,
                                                                      int WK) {
   mfma_body<FMT, RB>(x, w, scales, zeros, y, M, N, K, blockIdx.x, WK);
+}
+
+// mfma_kernel whose N rows are gate/up pairs: act [M, N / 2] = silu(gate) * up.
+template <int FMT, int RB>
+__global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_silu_kernel(const uint16_t* __restrict__ x,
+                                                                          const uint8_t* __restrict__ w,
+                                                                          const uint16_t* __restrict__ scales,
+                                                                          const uint16_t* __restrict__ zeros,
+                                                                          uint16_t* __restrict__ act, int M, int N, int K,
+                                                                          int WK) {
+  mfma_body<FMT, RB, true>(x, w, scales, zeros, act, M, N, K, blockIdx.x, WK);
 }
 
 // Several linears of one format and one M in a single launch (see GemvGroup); each item keeps
@@ -827,7 +889,7 @@ __device__ __forceinline__ uint16_t half_of(const uint4& v, int j) {   // 16-bit
 
 // A workgroup of LM_WAVES waves holds R = LM_WAVES / WK row groups of 16 RB rows; the WK
 // waves of a group take the stages h = kw, kw + WK, ...
-template <int FMT, int RB, int MT>
+template <int FMT, int RB, int MT, bool SILU = false>
 __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
                                         const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
                                         uint16_t* __restrict__ y, int M, int N, int K, int block, int WK) {
@@ -958,6 +1020,16 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
     for (int mt = 0; mt < MT; ++mt) {
       f4 t = red[(((sub * WK) * RB + r) * MT + mt) * 64 + lane];
       for (int k = 1; k < WK; ++k) t += red[(((sub * WK + k) * RB + r) * MT + mt) * 64 + lane];
+      if constexpr (SILU) {   // rows n, n ^ 1 (a gate/up pair) sit in lanes l, l ^ 1
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int m = 16 * mt + 4 * q + k;
+          const uint16_t o = out16<FMT>(t[k] * sc);
+          const uint16_t ou = (uint16_t)__builtin_amdgcn_update_dpp(0, (int)o, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+          if (m < M && n < N && (nl & 1) == 0) y[(size_t)m * (N / 2) + n / 2] = silu_mul_f16(o, ou);
+        }
+        continue;
+      }
       if (n < N) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -977,6 +1049,16 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lm_kernel(const uint16_t* __res
                                                           const uint16_t* __restrict__ zeros, uint16_t* __restrict__ y,
                                                           int M, int N, int K, int WK) {
   lm_body<FMT, RB, MT>(x, w, scales, zeros, y, M, N, K, blockIdx.x, WK);
+}
+
+// lm_kernel whose N rows are gate/up pairs: act [M, N / 2] = silu(gate) * up.
+template <int FMT, int RB, int MT>
+__global__ __launch_bounds__(64 * LM_WAVES) void lm_silu_kernel(const uint16_t* __restrict__ x,
+                                                               const uint8_t* __restrict__ w,
+                                                               const uint16_t* __restrict__ scales,
+                                                               const uint16_t* __restrict__ zeros,
+                                                               uint16_t* __restrict__ act, int M, int N, int K, int WK) {
+  lm_body<FMT, RB, MT, true>(x, w, scales, zeros, act, M, N, K, blockIdx.x, WK);
 }
 
 // Several linears in a single launch (see GemvGroup), each with its own K split.
@@ -1240,6 +1322,64 @@ hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w,
   }
 }
 
+// wq_linear_silu: the decode kernels of wq_linear's plan for the [N, K] matrix of gate/up row
+// pairs, with the pair epilogue; the GEMV takes at least 2 rows per wave (a row's sum does not
+// depend on the rows per wave, only on the K split, which stays the plan's). Never the tiled
+// prefill kernel: prefill-sized M runs as slabs of the decode kernels.
+template <int FMT>
+hipError_t launch_linear_silu_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc,
+                                  const uint16_t* z, uint16_t* act, int M, int N, int K) {
+  if constexpr (bf16_act(FMT)) {
+    return hipErrorInvalidValue;   // fp16 activations only (the entry point rejects the flag)
+  } else {
+    const int pf = pfmt(FMT);
+    if (use_lm(pf, M, N, K)) {
+      if constexpr (group_meta(FMT) || w6_geom(FMT) || wfmt(FMT) == WQ_FMT_W4E2M1 || wfmt(FMT) == WQ_FMT_W5E2M2) {
+        const LmPlan p = plan_lm(pf, N, K);
+        const size_t shm = (size_t)LM_WAVES * p.RB * lm_block<FMT>();
+        const dim3 grid(p.grid), block(64 * LM_WAVES);
+        const int MT = lm_tiles(M);
+        if (p.RB == 2) {
+          if (MT == 1) return launch(lm_silu_kernel<FMT, 2, 1>, grid, block, shm, s, x, w, sc, z, act, M, N, K, p.WK);
+          if (MT == 2) return launch(lm_silu_kernel<FMT, 2, 2>, grid, block, shm, s, x, w, sc, z, act, M, N, K, p.WK);
+          return launch(lm_silu_kernel<FMT, 2, 4>, grid, block, shm, s, x, w, sc, z, act, M, N, K, p.WK);
+        }
+        if (MT == 1) return launch(lm_silu_kernel<FMT, 1, 1>, grid, block, shm, s, x, w, sc, z, act, M, N, K, p.WK);
+        if (MT == 2) return launch(lm_silu_kernel<FMT, 1, 2>, grid, block, shm, s, x, w, sc, z, act, M, N, K, p.WK);
+        return launch(lm_silu_kernel<FMT, 1, 4>, grid, block, shm, s, x, w, sc, z, act, M, N, K, p.WK);
+      }
+      return hipErrorInvalidValue;
+    }
+    if (!use_mfma(pf, M, N)) {
+      const GemvPlan p = plan_gemv(pf, N, K);
+      const int B = p.B < 2 ? 2 : p.B;
+      const int64_t blocks = ((int64_t)N + B - 1) / B;
+      const dim3 grid((unsigned)((blocks + p.R - 1) / p.R)), block(64 * p.WK * p.R);
+      auto go = [&](auto kb2, auto kb4) {
+        return B == 4 ? launch(kb4, grid, block, 0, s, x, w, sc, z, act, N, K, p.WK)
+                      : launch(kb2, grid, block, 0, s, x, w, sc, z, act, N, K, p.WK);
+      };
+      switch (M) {
+        case 1: return go(gemv_silu_kernel<FMT, 1, 2>, gemv_silu_kernel<FMT, 1, 4>);
+        case 2: return go(gemv_silu_kernel<FMT, 2, 2>, gemv_silu_kernel<FMT, 2, 4>);
+        case 3: return go(gemv_silu_kernel<FMT, 3, 2>, gemv_silu_kernel<FMT, 3, 4>);
+        default: return go(gemv_silu_kernel<FMT, 4, 2>, gemv_silu_kernel<FMT, 4, 4>);
+      }
+    }
+    if constexpr (w6_geom(FMT) || wfmt(FMT) == WQ_FMT_W4E2M1 || wfmt(FMT) == WQ_FMT_W5E2M2) {
+      return hipErrorInvalidValue;   // these take lm_kernel wherever the matrix cores run (use_lm)
+    } else {
+      const MfmaPlan p = plan_mfma(pf, N, K);
+      const dim3 grid(p.grid), block(64 * p.WK);
+      switch (p.RB) {
+        case 4: return launch(mfma_silu_kernel<FMT, 4>, grid, block, 0, s, x, w, sc, z, act, M, N, K, p.WK);
+        case 2: return launch(mfma_silu_kernel<FMT, 2>, grid, block, 0, s, x, w, sc, z, act, M, N, K, p.WK);
+        default: return launch(mfma_silu_kernel<FMT, 1>, grid, block, 0, s, x, w, sc, z, act, M, N, K, p.WK);
+      }
+    }
+  }
+}
+
 template <int FMT, int M>
 hipError_t launch_grouped_m(const GemvGroup& g, int B, int block_waves, int grid, hipStream_t s) {
   switch (B) {
@@ -1374,6 +1514,33 @@ int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, c
     hipError_t e = hipSuccess;
     switch (fmt) {
 #define WQ_CASE(C) case C: e = launch_linear_fmt<C>(s, xs, w, scales, zeros, ys, mm, (int)N, (int)K); break;
+      WQ_KERNEL_CODES(WQ_CASE)
+#undef WQ_CASE
+      default: return WQ_ERR_FMT;
+    }
+    if (e != hipSuccess) return wq::device_status(e);
+  }
+  return WQ_OK;
+}
+
+int wq_linear_silu(const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros,
+                   uint16_t* act, int64_t M, int64_t F, int64_t K, int fmt, void* stream) {
+  if (!valid_fmt(fmt) || bf16_act(fmt)) return WQ_ERR_FMT;
+  if (F < 0) return WQ_ERR_ARG;
+  if (F < 1 || F > INT32_MAX / 4) return WQ_ERR_SHAPE;
+  const int64_t N = 2 * F;
+  const int st = check_linear_args(x, packed_w, scales, zeros, act, M, N, K, fmt);
+  if (st != WQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* w = static_cast<const uint8_t*>(packed_w);
+  const int64_t slab = slab_rows(pfmt(fmt), K);
+  for (int64_t m0 = 0; m0 < M; m0 += slab) {
+    const int mm = static_cast<int>(M - m0 < slab ? M - m0 : slab);
+    const uint16_t* xs = x + m0 * K;
+    uint16_t* as = act + m0 * F;
+    hipError_t e = hipSuccess;
+    switch (fmt) {
+#define WQ_CASE(C) case C: e = launch_linear_silu_fmt<C>(s, xs, w, scales, zeros, as, mm, (int)N, (int)K); break;
       WQ_KERNEL_CODES(WQ_CASE)
 #undef WQ_CASE
       default: return WQ_ERR_FMT;

@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the model runs in libwq's kernels (wq_embed,
 wq_add_rmsnorm, wq_linear_grouped / wq_linear on the packed weights, wq_rope_attention,
-wq_silu_mul, wq_argmax_next). torch provides device memory, the stream and the HIP graph that
+wq_linear_silu for gate/up and silu(gate)*up in one launch, wq_argmax_next). torch provides device memory, the stream and the HIP graph that
 records one step. The position and the token ids live in device memory and wq_argmax_next
 advances them, so replaying the graph generates token after token.
 
@@ -17,6 +17,9 @@ import numpy as np
 from . import inputs, wq
 
 LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
+# The linears as the device holds them: gate and up as one matrix of interleaved rows (row 2i
+# gate row i, row 2i+1 up row i) for wq_linear_silu.
+DEVICE_LINEARS = ("q", "k", "v", "o", "gu", "down")
 
 # Llama-2-7B decoder shapes (random-init weights of this architecture stand in for trained ones)
 LLAMA2_7B = dict(d=4096, n_heads=32, n_kv_heads=32, hd=128, ffn=11008, layers=32, vocab=32000, eps=1e-5,
@@ -28,6 +31,20 @@ def linear_shapes(cfg):
     d, hd, ffn = cfg["d"], cfg["hd"], cfg["ffn"]
     return [("q", cfg["n_heads"] * hd, d), ("k", cfg["n_kv_heads"] * hd, d), ("v", cfg["n_kv_heads"] * hd, d),
             ("o", d, cfg["n_heads"] * hd), ("gate", ffn, d), ("up", ffn, d), ("down", d, ffn)]
+
+
+def device_shapes(cfg):
+    """{name: (N, K)} of the linears as the device holds them (DEVICE_LINEARS)."""
+    s = {nm: (n, k) for nm, n, k in linear_shapes(cfg)}
+    s["gu"] = (2 * cfg["ffn"], cfg["d"])
+    return {nm: s[nm] for nm in DEVICE_LINEARS}
+
+
+def interleave_rows(a, b):
+    """[F, K] and [F, K] -> [2F, K] with row 2i = a[i], row 2i+1 = b[i]."""
+    out = np.empty((2 * a.shape[0], a.shape[1]), dtype=a.dtype)
+    out[0::2], out[1::2] = a, b
+    return out
 
 
 def pack_host(fmt, w):
@@ -55,8 +72,8 @@ def pack_host(fmt, w):
 class Decoder:
     """Device state of a model and one decode step of M sequences (all at the same position).
 
-    layers: list over layers of dicts: each linear name -> host packed tuple (packed, scales,
-    zeros), 'attn_norm' / 'ffn_norm' -> fp16 bits [d]. final_norm: fp16 bits [d]; lm_head: packed
+    layers: list over layers of dicts: each name of DEVICE_LINEARS -> host packed tuple (packed,
+    scales, zeros), 'attn_norm' / 'ffn_norm' -> fp16 bits [d]. final_norm: fp16 bits [d]; lm_head: packed
     tuple [vocab, d]; embed: fp16 bits [vocab, d]. Every layer gets its own device copy of its
     arrays (layers that share host arrays still stream their own bytes, as a real model would)."""
 
@@ -65,10 +82,10 @@ class Decoder:
         dev = lambda a: None if a is None else torch.from_numpy(
             np.ascontiguousarray(a).view(np.uint8).reshape(-1).copy()).to(device)
         d, hd, H, Hkv, ffn, V = cfg["d"], cfg["hd"], cfg["n_heads"], cfg["n_kv_heads"], cfg["ffn"], cfg["vocab"]
-        self.shapes = {nm: (n, k) for nm, n, k in linear_shapes(cfg)}
+        self.shapes = device_shapes(cfg)
         self.layers = []
         for L in layers:
-            self.layers.append({nm: tuple(dev(a) for a in L[nm]) for nm in LINEARS})
+            self.layers.append({nm: tuple(dev(a) for a in L[nm]) for nm in DEVICE_LINEARS})
             self.layers[-1]["attn_norm"] = dev(L["attn_norm"])
             self.layers[-1]["ffn_norm"] = dev(L["ffn_norm"])
         self.final_norm = dev(final_norm)
@@ -80,7 +97,7 @@ class Decoder:
         self.q, self.att = empty(m * H * hd), empty(m * H * hd)
         self.k, self.v = empty(m * Hkv * hd), empty(m * Hkv * hd)
         self.o, self.down = empty(m * d), empty(m * d)
-        self.gate, self.up, self.act = empty(m * ffn), empty(m * ffn), empty(m * ffn)
+        self.act = empty(m * ffn)
         self.logits = empty(m * V)
         self.tokens = empty(m, torch.int32)
         self.pos = empty(1, torch.int32)
@@ -90,6 +107,12 @@ class Decoder:
         self.rope_cos, self.rope_sin = torch.from_numpy(cos.reshape(-1)).to(device), torch.from_numpy(sin.reshape(-1)).to(device)
         ws = wq.wq_attention_workspace_bytes(m, H, hd, max_seq)
         self.workspace = empty(max(ws, 16), torch.uint8) if ws else None
+
+    def launches_per_step(self):
+        """Kernel launches of one step: embedding, final norm, output layer, next token, and per layer two
+        norms, q/k/v, attention (and its combine launch when the cache holds more than one chunk), o,
+        gate/up with silu, down."""
+        return 4 + len(self.layers) * (7 + (1 if self.workspace is not None else 0))
 
     def weight_bytes(self):
         """Bytes of packed weights and metadata one step reads (layers and output layer)."""
@@ -118,9 +141,8 @@ class Decoder:
                                  self.pos, self.att, m, H, Hkv, hd, self.S, self.workspace, stream)
             wq.wq_linear_grouped([self._item(L, "o", self.att, self.o)], m, f, stream)
             wq.wq_add_rmsnorm(self.x, self.o, L["ffn_norm"], c["eps"], self.h, m, d, stream)
-            wq.wq_linear_grouped([self._item(L, "gate", self.h, self.gate), self._item(L, "up", self.h, self.up)], m, f,
-                                 stream)
-            wq.wq_silu_mul(self.gate, self.up, self.act, m * ffn, stream)
+            p, s, z = L["gu"]
+            wq.wq_linear_silu(self.h, p, s, z, self.act, m, ffn, d, f, stream)
             wq.wq_linear_grouped([self._item(L, "down", self.act, self.down)], m, f, stream)
             delta = self.down
         wq.wq_add_rmsnorm(self.x, delta, self.final_norm, c["eps"], self.h, m, d, stream)
@@ -156,7 +178,9 @@ def random_model(cfg, fmt, stream_id, distinct_layers=None):
         for nm, n, kk in linear_shapes(cfg):
             w = (0.02 * rng.standard_normal((n, kk), dtype=np.float32)).astype(np.float32)
             draws[(l, nm)] = w
-            L[nm] = pack_host(fmt, w)
+            if nm not in ("gate", "up"):
+                L[nm] = pack_host(fmt, w)
+        L["gu"] = pack_host(fmt, interleave_rows(draws[(l, "gate")], draws[(l, "up")]))
         L["attn_norm"] = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float16).view(np.uint16)
         L["ffn_norm"] = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float16).view(np.uint16)
         draws[(l, "attn_norm")], draws[(l, "ffn_norm")] = L["attn_norm"], L["ffn_norm"]

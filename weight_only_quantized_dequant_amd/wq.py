@@ -77,6 +77,8 @@ def lib():
         L.wq_dequant.argtypes = [ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _p]
         L.wq_linear.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, ctypes.c_int, _p]
         L.wq_linear_grouped.argtypes = [ctypes.POINTER(LinearItem), ctypes.c_int, _i64, ctypes.c_int, _p]
+        L.wq_linear_silu.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, ctypes.c_int, _p]
+        L.wq_linear_silu.restype = ctypes.c_int
         L.wq_linear_grouped.restype = ctypes.c_int
         L.wq_linear_kernel_name.restype = ctypes.c_char_p
         L.wq_linear_kernel_name.argtypes = [ctypes.c_int, _i64, _i64, _i64]
@@ -278,11 +280,12 @@ def _need(t, nbytes, name, where):
         raise ValueError("%s: %s holds %d bytes; the call reads or writes %d" % (where, name, have, nbytes))
 
 
-def _check_linear_buffers(x, packed_w, scales, zeros, y, m, n, k, fmt, where):
+def _check_linear_buffers(x, packed_w, scales, zeros, y, m, n, k, fmt, where, y_rows=None):
+    """y_rows: the output's columns when they are not n (wq_linear_silu writes n / 2)."""
     sized = _valid_shape(m, n, k) and wq_packed_bytes(fmt, n, k) > 0
     size = (lambda v: v) if sized else (lambda v: 0)
     _need(x, size(2 * m * k), "x", where)
-    _need(y, size(2 * m * n), "y", where)
+    _need(y, size(2 * m * (n if y_rows is None else y_rows)), "y", where)
     _need(packed_w, size(wq_packed_bytes(fmt, n, k)), "packed_w", where)
     _need(scales, size(wq_scales_bytes(fmt, n, k)), "scales", where)
     _need(zeros, size(wq_zeros_bytes(fmt, n, k)), "zeros", where)
@@ -304,6 +307,13 @@ def wq_linear(x, packed_w, scales, zeros, y, m, n, k, fmt, stream=None):
     _check_linear_buffers(x, packed_w, scales, zeros, y, m, n, k, fmt, "wq_linear")
     _check(lib().wq_linear(_dev_ptr(x), _dev_ptr(packed_w), _dev_ptr(scales), _dev_ptr(zeros), _dev_ptr(y), m, n, k,
                            fmt, _stream_ptr(stream)), "wq_linear")
+
+
+def wq_linear_silu(x, packed_w, scales, zeros, act, m, f, k, fmt, stream=None):
+    """Device: act[M,F] = silu(gate) * up from one packed [2F, K] matrix of gate/up row pairs."""
+    _check_linear_buffers(x, packed_w, scales, zeros, act, m, 2 * f, k, fmt, "wq_linear_silu", y_rows=f)
+    _check(lib().wq_linear_silu(_dev_ptr(x), _dev_ptr(packed_w), _dev_ptr(scales), _dev_ptr(zeros), _dev_ptr(act), m,
+                                f, k, fmt, _stream_ptr(stream)), "wq_linear_silu")
 
 
 def wq_linear_grouped(items, m, fmt, stream=None):
