@@ -59,6 +59,11 @@ def is_bf16(code):
     return bool(code & wq.ACT_BF16)
 
 
+def group_scaled(code):
+    """Formats with a scale and a zero point per group of 32 K (int4, int3)."""
+    return (code & 0xFF) in (wq.FMT_W4G32, wq.FMT_W3G32)
+
+
 def bf16_bits(a):
     """float array -> bfloat16 bit patterns (torch's float32 -> bfloat16 rounding, nearest even)."""
     import torch
@@ -331,7 +336,7 @@ def cpu_baseline(code, linears_host, seconds):
     for (p, s, z, n, k, x) in linears_host:
         rb = wq.wq_packed_bytes(fmt, n, k) // n
         g = k // 32
-        sl_s = None if s is None else (s[:rows] if fmt != wq.FMT_W4G32 else s[:rows * g])
+        sl_s = None if s is None else (s[:rows * g] if group_scaled(fmt) else s[:rows])
         sl_z = None if z is None else z[:rows * g]
         work.append((p[:rows * rb], sl_s, sl_z, rows, k, x, rows * rb + 2 * (0 if s is None else sl_s.size)
                      + 2 * (0 if z is None else sl_z.size)))
@@ -503,7 +508,7 @@ def sweep_oracle_leg(model, draws, outs, head_fmt, head_m):
                 x = xk[k][:head_m]
                 for r0 in range(0, n, block):
                     r1 = min(n, r0 + block)
-                    ss = None if s is None else (s[r0 * g:r1 * g] if fmt == wq.FMT_W4G32 else s[r0:r1])
+                    ss = None if s is None else (s[r0 * g:r1 * g] if group_scaled(fmt) else s[r0:r1])
                     zz = None if z is None else z[r0 * g:r1 * g]
                     t0 = time.perf_counter()
                     codes = oracle.unpack_vectorized(fmt, p[r0 * rb_bytes:r1 * rb_bytes], r1 - r0, k)
