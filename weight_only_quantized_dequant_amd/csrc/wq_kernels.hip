@@ -732,16 +732,26 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_grouped_kernel(const
 //       hi slice at 8192 + 256 r + 8 (u ^ (2r & 31))                                       12 KB
 //   FP5: magnitude slice of unit u as W4, sign word at 8192 + 128 r + 4 (u ^ ((r >> 1) & 7))
 //       (a 4-byte read serves 64 lanes over 64 banks: rows 2p and 2p+1 take either half)   10 KB
-// K tile j (0..7) of a stage is 4 units, one per lane quad q: unit 8q + j. Its x fragments
+// K tile j (0..7) of a stage is 4 units, one per lane quad q: unit 4j + q, so that the 4 quads of a
+// row read adjacent units of x (a wave's x load touches half as many cache lines as with unit 8q + j,
+// which cost up to a fifth of the time at M = 16). W4 and W3 park the stage's group scales and zeros
+// (loaded as 8 groups per lane) in the wave's LDS region too, and read each unit's pair from there:
+//   W4, W3 metadata: scale of group g of row r at 8192 + 64 r + 2 (g ^ (((r >> 2) & 3) << 3)),
+//       zero 1024 bytes further (the XOR spreads the 16 rows of a read over the banks)      +2 KB
+// Its x fragments
 // sit in a register ring of lm_xring slots and are loaded lm_xring - 1 tiles ahead (W4 keeps
 // the ring at 2 so that its two-block kernel fits 256 VGPRs: two waves per SIMD).
 template <int FMT> constexpr bool lm_w6() { return w6_geom(FMT); }   // two plane slices per unit (both FP6 layouts)
 template <int FMT> constexpr bool lm_w5() { return wfmt(FMT) == WQ_FMT_W5E2M2; }   // 16-byte slice + sign word
 template <int FMT> constexpr int lm_block() {
-  return lm_w6<FMT>() ? 16 * 512 + 16 * 256 : lm_w5<FMT>() ? 16 * 512 + 16 * 128 : 16 * 512;
+  return lm_w6<FMT>() ? 16 * 512 + 16 * 256 : lm_w5<FMT>() ? 16 * 512 + 16 * 128 : group_meta(FMT) ? 16 * 512 + 2048
+                                                                                                 : 16 * 512;
 }
 template <int FMT> constexpr int lm_loads() { return lm_w6<FMT>() ? 12 : 8; }
 template <int FMT, int MT> constexpr int lm_xring() { return group_meta(FMT) || MT > 1 ? 2 : 4; }
+__device__ __forceinline__ int lm_unit(int q, int j) { return 4 * j + q; }
+// byte offset, within a row block's LDS image, of the scale of group g (0..31) of row r (W4, W3)
+__device__ __forceinline__ uint32_t lm_meta_off(int r, int g) { return 8192u + 64u * r + 2u * (g ^ (((r >> 2) & 3) << 3)); }
 constexpr int LM_MAX_MT = 4;   // 16-row tiles of x per launch (M up to 64 reads the weights once)
 constexpr int LM_WAVES = 4;   // waves per workgroup
 
@@ -864,6 +874,11 @@ __device__ __forceinline__ void lm_store(const LmStage<FMT, RB>& st, uint8_t* ld
       const int rr = 2 * i + (lane >> 5), u = lane & 31;
       *reinterpret_cast<uint4*>(base + 512 * rr + 16 * (u ^ (rr & 7))) = st.v[r][i];
     }
+    if constexpr (group_meta(FMT)) {   // lane (rr, qq) holds the scales and zeros of groups 8qq .. 8qq+7 of row rr
+      const int rr = lane & 15, qq = lane >> 4;
+      *reinterpret_cast<uint4*>(base + lm_meta_off(rr, 8 * qq)) = st.s[r];
+      *reinterpret_cast<uint4*>(base + 1024 + lm_meta_off(rr, 8 * qq)) = st.z[r];
+    }
     if constexpr (lm_w5<FMT>()) {   // sign word of unit u of row rr at 8192 + 128 rr + 4 (u ^ ((rr >> 1) & 7))
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -880,11 +895,6 @@ __device__ __forceinline__ void lm_store(const LmStage<FMT, RB>& st, uint8_t* ld
       }
     }
   }
-}
-
-__device__ __forceinline__ uint16_t half_of(const uint4& v, int j) {   // 16-bit element j (0..7) of v
-  const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
-  return static_cast<uint16_t>((j & 1) ? (w >> 16) : (w & 0xFFFFu));
 }
 
 // A workgroup of LM_WAVES waves holds R = LM_WAVES / WK row groups of 16 RB rows; the WK
@@ -910,8 +920,6 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
     for (int mt = 0; mt < MT; ++mt) acc[r][mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   LmStage<FMT, RB> st;
-  constexpr int MS = group_meta(FMT) ? RB : 1;
-  uint4 cs[MS], cz[MS];   // W4, W3: the metadata of the stage in LDS
   constexpr int XR = lm_xring<FMT, MT>();
   [[maybe_unused]] const W4Masks w4m = wfmt(FMT) == WQ_FMT_W4G32 && !bf16_act(FMT) ? w4_masks() : W4Masks{};
   [[maybe_unused]] const W3Masks w3m = wfmt(FMT) == WQ_FMT_W3G32 ? w3_masks() : W3Masks{};
@@ -921,9 +929,9 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
   // was slower). Units past the row end (the ragged last stage) contribute nothing because their
   // weights are zeroed when the stage is parked.
   h8 xr[XR][MT][4];
-  auto xload = [&](int t) {   // x[m = 16 mt + nl][unit 32h + 8q + j] of K tile t = 8i + j
+  auto xload = [&](int t) {   // x[m = 16 mt + nl][unit 32h + lm_unit(q, j)] of K tile t = 8i + j
     const int h = kw + (t >> 3) * WK, j = t & 7;
-    const uint32_t u = (uint32_t)min(32 * h + 8 * q + j, U - 1);
+    const uint32_t u = (uint32_t)min(32 * h + lm_unit(q, j), U - 1);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) +
@@ -932,13 +940,9 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
       for (int k = 0; k < 4; ++k) xr[t % XR][mt][k] = __builtin_bit_cast(h8, xp[k]);
     }
   };
-  auto park = [&](int h) {   // the loaded stage h -> LDS (and W4 metadata -> cs, cz)
+  auto park = [&](int h) {   // the loaded stage h -> LDS (W4 and W3: with its metadata)
     if (32 * h + 32 > U) lm_zero_past_row<FMT, RB>(st, U - 32 * h, lane);   // wave-uniform: the ragged last stage
     lm_store<FMT, RB>(st, lds, lane);
-    if constexpr (group_meta(FMT)) {
-#pragma unroll
-      for (int r = 0; r < RB; ++r) { cs[r] = st.s[r]; cz[r] = st.z[r]; }
-    }
   };
   if (NI > 0) {
 #pragma unroll
@@ -954,7 +958,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
     for (int j = 0; j < 8; ++j) {
       const int t = 8 * i + j;
       if (j + XR - 1 < 8 || i + 1 < NI) xload(t + XR - 1);
-      const int u = 8 * q + j;   // unit within the stage
+      const int u = lm_unit(q, j);   // unit within the stage
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const uint8_t* base = lds + r * lm_block<FMT>();
@@ -964,24 +968,29 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
           raw.b = *reinterpret_cast<const uint2*>(base + 8192 + 256 * nl + 8 * (u ^ ((2 * nl) & 31)));
         if constexpr (lm_w5<FMT>())
           raw.b = *reinterpret_cast<const uint32_t*>(base + 8192 + 128 * nl + 4 * (u ^ ((nl >> 1) & 7)));
+        [[maybe_unused]] uint16_t sb = 0, zb = 0;   // W4, W3: this unit's group scale and zero
+        if constexpr (group_meta(FMT)) {
+          sb = *reinterpret_cast<const uint16_t*>(base + lm_meta_off(nl, u));
+          zb = *reinterpret_cast<const uint16_t*>(base + 1024 + lm_meta_off(nl, u));
+        }
         h2 wv[16];
         if constexpr (bf16_act(FMT)) {
-          if constexpr (wfmt(FMT) == WQ_FMT_W4G32) decode_bf16<FMT>(raw, half_of(cs[r], j), half_of(cz[r], j), wv);
+          if constexpr (wfmt(FMT) == WQ_FMT_W4G32) decode_bf16<FMT>(raw, sb, zb, wv);
           else decode_bf16<FMT>(raw, 0, 0, wv);
         } else {
           if constexpr (wfmt(FMT) == WQ_FMT_W4G32) {
             h2 zc1, zc2;
-            w4_consts(half_of(cz[r], j), zc1, zc2);
+            w4_consts(zb, zc1, zc2);
             decode_w4_unit(raw.a, zc1, zc2, w4m, wv);
-            const _Float16 sv = __builtin_bit_cast(_Float16, half_of(cs[r], j));
+            const _Float16 sv = __builtin_bit_cast(_Float16, sb);
             const h2 s2 = {sv, sv};
 #pragma unroll
             for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
           } else if constexpr (wfmt(FMT) == WQ_FMT_W3G32) {
             h2 zc[3];
-            w3_consts(half_of(cz[r], j), zc);
+            w3_consts(zb, zc);
             decode_w3_unit(raw.a, zc, w3m, wv);
-            const _Float16 sv = __builtin_bit_cast(_Float16, half_of(cs[r], j));
+            const _Float16 sv = __builtin_bit_cast(_Float16, sb);
             const h2 s2 = {sv, sv};
 #pragma unroll
             for (int p = 0; p < 16; ++p) wv[p] = wv[p] * s2;   // fp16((q-z)*s): one rounding of an exact product
