@@ -105,12 +105,16 @@ def parse():
                     help="no GPU work: print the per-kernel means of rocprofv3 --pmc counter_collection.csv files "
                          "as a markdown table (optionally only kernels containing --kernel-filter)")
     ap.add_argument("--kernel-filter", default=None)
+    ap.add_argument("--counter-stat", choices=["mean", "max"], default="mean",
+                    help="--summarize-counters: the mean per dispatch, or the largest dispatch")
     return ap.parse_args()
 
 
-def summarize_counters(paths, kfilter=None):
+def summarize_counters(paths, kfilter=None, stat="mean"):
     """Per kernel name: dispatches, resources (VGPRs, AGPRs, LDS, scratch, grid and workgroup size)
-    and the mean value per dispatch of every counter in rocprofv3 counter-collection CSV files."""
+    and the mean (or, stat="max", the largest) value per dispatch of every counter in rocprofv3
+    counter-collection CSV files. The largest picks one dispatch out of many of the same kernel: the
+    512 MiB copy of --copy-calibration among the smaller copies that set up the rotated weights."""
     import csv
     from collections import defaultdict
     vals = defaultdict(lambda: defaultdict(list))
@@ -131,7 +135,8 @@ def summarize_counters(paths, kfilter=None):
     for k in sorted(vals):
         n = max(len(v) for v in vals[k].values())
         r = res[k]
-        cells = ["%.1f" % (sum(vals[k][c]) / len(vals[k][c])) if vals[k].get(c) else "" for c in counters]
+        agg = (lambda v: max(v)) if stat == "max" else (lambda v: sum(v) / len(v))
+        cells = ["%.1f" % agg(vals[k][c]) if vals[k].get(c) else "" for c in counters]
         print("| %s | %d | %s | %s | %s | %s | %s | %s | %s | %s |" % (
             k[:90], n, r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"], r["LDS_Block_Size"],
             r["Scratch_Size"], r["Grid_Size"], r["Workgroup_Size"], " | ".join(cells)))
@@ -638,7 +643,7 @@ def decode_cpu_baseline(cfg, fmt, host, context):
 def main():
     args = parse()
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.kernel_filter)
+        summarize_counters(args.summarize_counters, args.kernel_filter, args.counter_stat)
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: libwq runs the linear on a single MI355X "
