@@ -388,3 +388,56 @@ def test_linear_silu_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host_bits(out), host_bits(eager))
+
+
+# ------------------------------------------------------------------ the largest K the library takes
+@pytest.mark.parametrize("fmt", [wq.FMT_W4G32, wq.FMT_W8, wq.FMT_W6E3M2], ids=["w4", "w8", "w6"])
+def test_largest_k(fmt):
+    # K = 2^26 (the limit), N = 3: past K = 2^25 the decode kernels take 16-row slabs of x, so M = 17
+    # runs as two launches; M = 1 takes the GEMV.
+    #  * one-hot rows of x at positions spread over K (around 2^25 and at the last index): y must be
+    #    the dequantized weight at that position bit for bit, which any addressing error would break;
+    #  * random x: the oracle's closed-form bound, with the reference summed over K chunks in float64
+    #    (the oracle's plain product, chunk by chunk, so that its memory stays bounded). The fixed
+    #    rtol = atol = 1e-2 of the other tests is not applied: it suits K up to ~1e5, and a float32 sum
+    #    of 2^26 terms carries absolute errors of order 0.1 on outputs of order 100.
+    torch = torch_cuda()
+    n, k = 3, 1 << 26
+    rng = inputs.rng_for(95, fmt)
+    w = (0.02 * rng.standard_normal((n, k), dtype=np.float32)).astype(np.float32)
+    dw = DeviceWeights(fmt, w)
+    wd, codes, _, _ = oracle_rows(fmt, w)
+    lib_codes, _, _ = wq.wq_unpack(fmt, dw.packed_host, dw.scales_host, dw.zeros_host, n, k)
+    assert np.array_equal(lib_codes, codes)
+    assert np.array_equal(dw.dequant(), wd)
+    del lib_codes, codes, w
+    pos = [0, 31, 32, 1000, (1 << 25) - 1, 1 << 25, (1 << 25) + 1, (1 << 25) + 31, (1 << 25) + 32, 3 << 24,
+           k - 1025, k - 64, k - 33, k - 32, k - 31, k - 2, k - 1]
+    onehot = np.zeros((len(pos), k), dtype=np.uint16)
+    for i, kk in enumerate(pos):
+        onehot[i, kk] = 0x3C00                      # fp16 1.0
+    for rows in (onehot[:1], onehot):              # the GEMV, and two 16-row slabs
+        y = dw.linear(rows)
+        want = wd[:, [pos[i] for i in range(rows.shape[0])]].T
+        same = (y == want) | (((y & 0x7FFF) == 0) & ((want & 0x7FFF) == 0))
+        assert same.all(), (rows.shape[0], np.argwhere(~same)[:3].tolist())
+    del onehot
+    for m in (1, 17):
+        x = rng.standard_normal((m, k), dtype=np.float32).astype(np.float16).view(np.uint16)
+        y = dw.linear(x)
+        yref = np.zeros((m, n))
+        s_abs = np.zeros((m, n))
+        a_abs = np.zeros((m, 1))
+        step = 1 << 22
+        for c0 in range(0, k, step):
+            xc, wc = x[:, c0:c0 + step], wd[:, c0:c0 + step]
+            yref += oracle.linear_ref(xc, wc)
+            xa, wa = np.abs(oracle.fp16_from_bits(xc)), np.abs(oracle.fp16_from_bits(wc))
+            s_abs += xa @ wa.T
+            a_abs += xa.sum(axis=1, keepdims=True)
+        u = 2.0 ** -11
+        bound = u * np.abs(yref) + (u + k * 2.0 ** -23) * s_abs + 2.0 ** -25 * a_abs + 2.0 ** -24
+        err = np.abs(oracle.fp16_from_bits(y) - yref)
+        assert np.all(err <= bound), (m, wq.wq_linear_kernel_name(fmt, m, n, k), float((err / bound).max()))
+    del dw
+    torch.cuda.empty_cache()
