@@ -110,7 +110,9 @@ def test_linear_every_m(fmt, m):
                                    # 8192 rows, a single stage (K = 256)
                                    (37, 2304, 5), (37, 2304, 16), (8200, 2304, 8), (40, 11008, 13), (48, 256, 6),
                                    # 17..64 rows of x in one launch (2 or 4 tiles of 16), and slabs beyond
-                                   (130, 8192, 64), (37, 2304, 33), (8200, 256, 50), (40, 4352, 17), (33, 512, 130)])
+                                   (130, 8192, 64), (37, 2304, 33), (8200, 256, 50), (40, 4352, 17), (33, 512, 130),
+                                   # the plane layouts' last 64-unit chunk holding a single unit (65 units)
+                                   (37, 2080, 8), (37, 2080, 20)])
 def test_linear_shapes(fmt, n, k, m):
     w = _weights(n, k, 3 * n + k)
     _, x = inputs.small_case(2000 + n + m, 1, k, m)
