@@ -189,7 +189,10 @@ int wq_dequant(int fmt, const void* packed, const uint16_t* scales, const uint16
  * run as several such launches. The tiled prefill kernel takes all rows in one launch from 193
  * rows on, and from fewer rows where its chain of K steps is short against its tile count: W8
  * and fp16/bf16 weights from 17 rows, W4, W6 and FP4 from 65, FP5 from 81.
- * wq_linear_kernel_name names the kernel that runs for a shape.
+ * Up to 4 rows the VALU GEMV runs, except on large matrices (N*K >= 2^24) where the LDS-staged
+ * matrix-core kernel takes W4 and W3 (K a multiple of 256) and W6 from 3 rows, FP4 and FP5 from
+ * 2, and W6 at 4 rows from N = 2048; W8 takes the fragment-load matrix-core kernel at 4 rows from
+ * N = 4096. wq_linear_kernel_name names the kernel that runs for a shape.
  * Asynchronous on stream. Errors: WQ_ERR_ARG, WQ_ERR_SHAPE, WQ_ERR_FMT, WQ_ERR_ALIGN,
  * WQ_ERR_DEVICE. */
 int wq_linear(const uint16_t* x, const void* packed_w, const uint16_t* scales, const uint16_t* zeros, uint16_t* y,

@@ -288,7 +288,27 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     # W4 on the matrix cores: through LDS when K is a multiple of 256, else fragment loads
     assert wq.wq_linear_kernel_name(2, 8, 4096, 4096) == "lm_kernel<2, 1, 1>"
     assert wq.wq_linear_kernel_name(2, 8, 4096, 4128) == "mfma_kernel<2, 1>"
-    assert wq.wq_linear_kernel_name(3, 3, 4096, 4096).startswith("gemv_kernel")
+    # M = 2 and 3: the LDS-staged kernel on large matrices (N*K >= 2^24) from 3 rows, from 2 for FP4
+    # and FP5; the GEMV below that, for W8, and for W4 / int3 with K not a multiple of 256
+    assert wq.wq_linear_kernel_name(3, 3, 4096, 4096) == "lm_kernel<3, 1, 1>"
+    assert wq.wq_linear_kernel_name(3, 3, 2048, 4096).startswith("gemv_kernel")
+    assert wq.wq_linear_kernel_name(3, 2, 4096, 4096).startswith("gemv_kernel")
+    assert wq.wq_linear_kernel_name(2, 3, 4096, 4096) == "lm_kernel<2, 1, 1>"
+    assert wq.wq_linear_kernel_name(2, 2, 4096, 4096).startswith("gemv_kernel")
+    assert wq.wq_linear_kernel_name(2, 3, 4096, 4128).startswith("gemv_kernel")
+    assert wq.wq_linear_kernel_name(7, 3, 11008, 4096) == "lm_kernel<7, 2, 1>"
+    assert wq.wq_linear_kernel_name(4, 2, 4096, 4096) == "lm_kernel<4, 1, 1>"
+    assert wq.wq_linear_kernel_name(6, 2, 4096, 4096) == "lm_kernel<6, 1, 1>"
+    assert wq.wq_linear_kernel_name(4, 1, 4096, 4096).startswith("gemv_kernel")
+    assert wq.wq_linear_kernel_name(1, 3, 11008, 4096).startswith("gemv_kernel")
+    assert wq.wq_linear_grouped_kernel_name(2, 3, [(4096, 4096), (11008, 4096), (4096, 11008)]) == \
+        "lm_grouped_kernel<2, 2, 1>"
+    # bfloat16 x: W6 from 3 rows as with fp16 x, W4 on the GEMV up to 3 rows
+    assert wq.wq_linear_kernel_name(3 | wq.ACT_BF16, 3, 4096, 4096) == "lm_kernel<259, 1, 1>"
+    assert wq.wq_linear_kernel_name(2 | wq.ACT_BF16, 3, 4096, 4096).startswith("gemv_kernel<258, 3,")
+    assert wq.wq_linear_kernel_name(2 | wq.ACT_BF16, 4, 4096, 4096) == "lm_kernel<258, 1, 1>"
+    assert wq.wq_linear_grouped_kernel_name(2 | wq.ACT_BF16, 3, [(4096, 4096), (11008, 4096)]).startswith(
+        "gemv_grouped_kernel<258, 3,")
     # M = 4: the matrix cores for W6 with N >= 2048, W8 with N >= 4096 and W4 from N*K = 2^24, the GEMV otherwise
     assert wq.wq_linear_kernel_name(3, 4, 4096, 4096).startswith("lm_kernel")
     assert wq.wq_linear_kernel_name(3, 4, 2048, 4096).startswith("lm_kernel")
@@ -409,11 +429,13 @@ def test_kernel_name_thresholds_stated_in_the_header():
 
 
 def test_fp5_kernel_choice():
-    # FP5 e2m2: the VALU GEMV up to M = 3 and at M = 4 below N*K = 2^24, the LDS-staged kernel from
-    # there (1 to 4 tiles of 16 rows), the tiled kernel from 81 rows when its chain is short enough
+    # FP5 e2m2: the VALU GEMV at M = 1, and up to M = 4 below N*K = 2^24; the LDS-staged kernel from
+    # M = 2 above that and from M = 5 always (1 to 4 tiles of 16 rows), the tiled kernel from 81 rows
+    # when its chain is short enough
     f = wq.FMT_W5E2M2
     assert wq.wq_linear_kernel_name(f, 1, 4096, 4096) == "gemv_kernel<6, 1, 4>"
-    assert wq.wq_linear_kernel_name(f, 3, 4096, 4096) == "gemv_kernel<6, 3, 4>"
+    assert wq.wq_linear_kernel_name(f, 3, 4096, 4096) == "lm_kernel<6, 1, 1>"
+    assert wq.wq_linear_kernel_name(f, 3, 2048, 4096) == "gemv_kernel<6, 3, 4>"
     assert wq.wq_linear_kernel_name(f, 4, 2048, 4096) == "gemv_kernel<6, 4, 4>"
     assert wq.wq_linear_kernel_name(f, 4, 4096, 4096) == "lm_kernel<6, 1, 1>"
     assert wq.wq_linear_kernel_name(f, 5, 2048, 4096) == "lm_kernel<6, 1, 1>"

@@ -816,18 +816,14 @@ __device__ __forceinline__ void lm_load(LmStage<FMT, RB>& st, const uint8_t* __r
 #pragma unroll
       for (int i = 0; i < 4; ++i) {   // hi: lane l -> row 4i + l/16, units 2(l%16), 2(l%16)+1
         const uint32_t nn = (uint32_t)(min(n0 + 16 * r + 4 * i + (lane >> 4), N - 1) - nb);
-        // when j0 is the chunk's last unit (odd uc), read units j0-1, j0 and keep the second; a
-        // one-unit chunk (the last of a row of 64c + 1 units) has a single 8-byte slice
+        // when j0 is the chunk's last unit (odd uc), read the 16 bytes that end with its slice and
+        // keep the second half: units j0-1, j0, or for a one-unit chunk (the last of a row of
+        // 64c + 1 units) the end of the lo plane and the one slice. No branch: a branch between
+        // the loads of a stage would make the compiler wait for them at the join.
         const int j0 = min(32 * half + 2 * (lane & 15), uc - 1);
-        const uint8_t* hp = rowb + nn * row_bytes + cbase + 16u * uc;
-        if (uc == 1) {
-          const uint2 v = ld_nt8(hp);
-          st.v[r][8 + i] = make_uint4(v.x, v.y, v.x, v.y);
-        } else {
-          const int sh = (j0 + 1 >= uc) ? 1 : 0;
-          const uint4 v = ld_nt16(hp + 8u * (j0 - sh));
-          st.v[r][8 + i] = sh ? make_uint4(v.z, v.w, v.z, v.w) : v;
-        }
+        const uint32_t sh = (j0 + 1 >= uc) ? 8u : 0u;
+        const uint4 v = ld_nt16(rowb + (nn * row_bytes + cbase + 16u * uc + 8u * j0 - sh));
+        st.v[r][8 + i] = sh ? make_uint4(v.z, v.w, v.z, v.w) : v;
       }
     }
   }
@@ -1235,11 +1231,21 @@ struct LmPlan {
 // matrix cores run for it, and W4, W3, FP4 and FP5 from M = 5 on and at M = 4 from N*K = 2^24 on,
 // where it beats the VALU GEMV (W4 and W3 only when K is a multiple of 256, so that a lane's 8
 // groups of metadata are one aligned 16-byte load).
-bool use_lm(int fmt, int64_t M, int64_t N, int64_t K) {
-  if (fmt == WQ_FMT_W6E3M2) return use_mfma(fmt, M, N);
+// The LDS-staged kernel (code: a format code, with or without WQ_ACT_BF16): every M above
+// GEMV_MAX_M (W6 also at M = 4 from N = 2048), and on large matrices (N*K >= 2^24) from 3 rows of
+// x, 2 for FP4 and FP5: the GEMV's work grows with every row of x, this kernel's hardly (Llama-7B
+// linears at M = 3: W4 22.2 -> 20.6 us, W6 30.1 -> 24.9, FP4 19.6 -> 15.8, int3 22.4 -> 19.9, FP5
+// 26.4 -> 20.4; at M = 2 FP4 17.7 -> 15.2, while W4, int3 and W6 stay faster on the GEMV there).
+// With bfloat16 x only W6 moves to 3 rows (Llama-70B linears 102.4 -> 85.3 us); W4, which scales
+// every weight in fp32 there, stays on the GEMV up to 3 rows (22.2 us against 28.1).
+bool use_lm(int code, int64_t M, int64_t N, int64_t K) {
+  const int fmt = pfmt(code);
   if (group_meta(fmt) && K % 256) return false;
-  if (!group_meta(fmt) && fmt != WQ_FMT_W4E2M1 && fmt != WQ_FMT_W5E2M2) return false;
-  return M > GEMV_MAX_M || (M == GEMV_MAX_M && N * K >= (int64_t(1) << 24));
+  if (!group_meta(fmt) && fmt != WQ_FMT_W4E2M1 && fmt != WQ_FMT_W5E2M2 && fmt != WQ_FMT_W6E3M2) return false;
+  if (use_mfma(fmt, M, N)) return true;   // W6 takes no other matrix-core kernel
+  const int64_t from = bf16_act(code) ? (fmt == WQ_FMT_W6E3M2 ? 3 : 4)
+                                      : (fmt == WQ_FMT_W4E2M1 || fmt == WQ_FMT_W5E2M2 ? 2 : 3);
+  return M >= from && N * K >= (int64_t(1) << 24);
 }
 
 // Two row blocks per wave from 8192 rows. WK doubled until ~1024 waves for W6 (one wave per
@@ -1316,7 +1322,7 @@ hipError_t launch_lm(int RB, int M, dim3 grid, hipStream_t s, const uint16_t* x,
 template <int FMT>
 hipError_t launch_linear_fmt(hipStream_t s, const uint16_t* x, const uint8_t* w, const uint16_t* sc, const uint16_t* z,
                              uint16_t* y, int M, int N, int K) {
-  if (use_lm(pfmt(FMT), M, N, K)) {
+  if (use_lm(FMT, M, N, K)) {
     const LmPlan p = plan_lm(pfmt(FMT), N, K);
     return launch_lm<FMT>(p.RB, M, dim3(p.grid), s, x, w, sc, z, y, N, K, p.WK, nullptr);
   }
@@ -1431,9 +1437,9 @@ void grouped_order(const wq_linear_item* items, int count, int (&order)[MAX_GROU
 // and otherwise takes the fragment-load kernel. Every family computes any shape correctly.
 enum Family { FAM_GEMV, FAM_LM, FAM_MFMA };
 
-Family family_of(int fmt, int64_t M, int64_t N, int64_t K) {
-  if (use_lm(fmt, M, N, K)) return FAM_LM;
-  return use_mfma(fmt, M, N) ? FAM_MFMA : FAM_GEMV;
+Family family_of(int code, int64_t M, int64_t N, int64_t K) {
+  if (use_lm(code, M, N, K)) return FAM_LM;
+  return use_mfma(pfmt(code), M, N) ? FAM_MFMA : FAM_GEMV;
 }
 
 int largest_item(const int64_t* N, const int64_t* K, int count) {
@@ -1443,9 +1449,10 @@ int largest_item(const int64_t* N, const int64_t* K, int count) {
   return big;
 }
 
-Family group_family(int fmt, int64_t M, const int64_t* N, const int64_t* K, int count) {
+Family group_family(int code, int64_t M, const int64_t* N, const int64_t* K, int count) {
   const int big = largest_item(N, K, count);
-  Family f = family_of(fmt, M, N[big], K[big]);
+  const int fmt = pfmt(code);
+  Family f = family_of(code, M, N[big], K[big]);
   if (f == FAM_LM && group_meta(fmt))
     for (int i = 0; i < count; ++i)
       if (K[i] % 256) f = FAM_MFMA;
@@ -1612,7 +1619,7 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
   if (count > 1 && wq::pf_takes(fmt, M, Ns, Ks, count))   // prefill-sized M: all items' tiles in one launch
     return wq::pf_launch_grouped(fmt, items, count, M, stream);
   const int pf = pfmt(fmt);
-  const Family fam = group_family(pf, M, Ns, Ks, count);
+  const Family fam = group_family(fmt, M, Ns, Ks, count);
   if (M > group_launch_rows(fam, pf, Ks, count)) {   // several slabs: one wq_linear per item
     for (int i = 0; i < count; ++i) {
       const wq_linear_item& it = items[i];
@@ -1677,7 +1684,7 @@ const char* wq_linear_kernel_name(int fmt, int64_t M, int64_t N, int64_t K) {
     return buf;
   }
   const int64_t mm = M < slab_rows(pf, K) ? M : slab_rows(pf, K);   // the first launch's rows
-  if (use_lm(pf, mm, N, K)) {
+  if (use_lm(fmt, mm, N, K)) {
     snprintf(buf, sizeof(buf), "lm_kernel<%d, %d, %d>", fmt, plan_lm(pf, N, K).RB, lm_tiles(mm));
   } else if (!use_mfma(pf, mm, N)) {
     const GemvPlan p = plan_gemv(pf, N, K);
@@ -1699,7 +1706,7 @@ const char* wq_linear_grouped_kernel_name(int fmt, int64_t M, const int64_t* N, 
   }
   const int big = largest_item(N, K, count);
   const int pf = pfmt(fmt);
-  const Family fam = group_family(pf, M, N, K, count);
+  const Family fam = group_family(fmt, M, N, K, count);
   if (M > group_launch_rows(fam, pf, K, count))
     return wq_linear_kernel_name(fmt, M, N[big], K[big]);   // separate launches: the largest item's
   const int B = group_rows(fam, pf, N, K, count);
