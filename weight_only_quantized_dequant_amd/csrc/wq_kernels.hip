@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <numeric>
 #include <cstdint>
 #include <cstdio>
@@ -51,6 +52,10 @@ constexpr int GEMV_MAX_M = 4;   // largest M served by the VALU GEMV; above it t
 constexpr int MFMA_M = 16;      // rows of x per MFMA launch
 constexpr int GEMV_WAVES = 4;   // waves per workgroup of the GEMV (row blocks x split of K)
 constexpr int MFMA_MAX_WAVES = 8;   // waves per workgroup of the MFMA kernel
+
+// The waves that split K (WK) are a power of two (1, 2, 4 or 8; the planner picks no other),
+// so a wave's share of the work is found with shifts and masks on its wave-uniform index.
+__device__ __forceinline__ int wk_log2(int WK) { return __builtin_ctz((unsigned)WK); }
 
 // ---------------------------------------------------------------- GEMV (M <= GEMV_MAX_M)
 // Lanes run along K. Lane l of a wave owns one "segment" of SEG consecutive K of a row
@@ -382,11 +387,12 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, const 
                                           uint16_t* __restrict__ y, int N, int K, int block, int WK) {
   const int lane = threadIdx.x & 63;
   const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar arithmetic
-  const int R = (blockDim.x >> 6) / WK;
-  const int sub = wave_id / WK, wave = wave_id - sub * WK;
+  const int lwk = wk_log2(WK);
+  const int R = (blockDim.x >> 6) >> lwk;
+  const int sub = wave_id >> lwk, wave = wave_id & (WK - 1);
   const int S = K / seg_codes<FMT>(), C = (S + 63) >> 6;
   const int row0 = (block * R + sub) * B;
-  const int NI = wave < C ? (C - wave + WK - 1) / WK : 0;   // chunks of this wave (wave-uniform)
+  const int NI = wave < C ? (C - wave + WK - 1) >> lwk : 0;   // chunks of this wave (wave-uniform)
   float acc[B][M];
 #pragma unroll
   for (int b = 0; b < B; ++b)
@@ -498,24 +504,42 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_silu_kernel(const uint16
 
 // Several independent linears of one format and one M in a single launch: the grid is the
 // concatenation of their workgroups, so the machine ramps up and drains once for all of them.
+// A wave finds its item without a dependent chain of scalar loads: the item boundaries are
+// read at once and compared branch-free, and an item's fields sit in one 64-byte record that
+// a single round of scalar loads brings in (the first loads of a launch miss every cache, so
+// each dependent round before the first weight load adds to the launch's ramp-up).
 constexpr int MAX_GROUP = 16;
+struct GroupItem {
+  const uint16_t* x;
+  const uint8_t* w;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  uint16_t* y;
+  int N, K, WK, first_block;
+  int pad[2];
+};
+static_assert(sizeof(GroupItem) == 64, "one item is one 64-byte record");
 struct GemvGroup {
   int count;
-  int first_block[MAX_GROUP + 1];   // prefix sums of the per-linear workgroup counts
-  const uint16_t* x[MAX_GROUP];
-  const uint8_t* w[MAX_GROUP];
-  const uint16_t* scales[MAX_GROUP];
-  const uint16_t* zeros[MAX_GROUP];
-  uint16_t* y[MAX_GROUP];
-  int N[MAX_GROUP], K[MAX_GROUP], WK[MAX_GROUP];
+  int first_block[MAX_GROUP];   // first workgroup of each item (prefix sums); INT_MAX past count
+  GroupItem item[MAX_GROUP];
 };
+
+// The item of this workgroup: the number of later items whose first workgroup it has reached
+// (b >= first_block[i] exactly when first_block[i] - b - 1 is negative: no overflow for
+// 0 <= b, first_block[i] <= INT_MAX), counted in scalar arithmetic.
+__device__ __forceinline__ const GroupItem& group_item(const GemvGroup& g) {
+  const int b = blockIdx.x;
+  int j = 0;
+#pragma unroll
+  for (int i = 1; i < MAX_GROUP; ++i) j += (int)((unsigned)(g.first_block[i] - b - 1) >> 31);
+  return g.item[j];
+}
 
 template <int FMT, int M, int B>
 __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_grouped_kernel(const GemvGroup g) {
-  int j = 0;
-  while (j + 1 < g.count && (int)blockIdx.x >= g.first_block[j + 1]) ++j;   // workgroup-uniform
-  gemv_body<FMT, M, B>(g.x[j], g.w[j], g.scales[j], g.zeros[j], g.y[j], g.N[j], g.K[j], blockIdx.x - g.first_block[j],
-                       g.WK[j]);
+  const GroupItem& it = group_item(g);
+  gemv_body<FMT, M, B>(it.x, it.w, it.scales, it.zeros, it.y, it.N, it.K, blockIdx.x - it.first_block, it.WK);
 }
 
 // ---------------------------------------------------------------- MFMA, fragment loads (W8, F16, W4 with K % 256 != 0)
@@ -601,12 +625,13 @@ __device__ __forceinline__ void mfma_body(const uint16_t* __restrict__ x, const 
                                            uint16_t* __restrict__ y, int M, int N, int K, int block, int WK) {
   const int lane = threadIdx.x & 63;
   const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int R = (blockDim.x >> 6) / WK;
-  const int sub = wave_id / WK, kw = wave_id - sub * WK;
+  const int lwk = wk_log2(WK);
+  const int R = (blockDim.x >> 6) >> lwk;
+  const int sub = wave_id >> lwk, kw = wave_id & (WK - 1);
   const int nl = lane & 15, q = lane >> 4;
   const int U = K >> 5, T = (U + 3) >> 2;
   const int n0 = (block * R + sub) * 16 * RB;
-  const int NI = kw < T ? (T - kw + WK - 1) / WK : 0;
+  const int NI = kw < T ? (T - kw + WK - 1) >> lwk : 0;
   const bool xrow = nl < M;
   f4 acc[RB];
 #pragma unroll
@@ -673,7 +698,7 @@ __device__ __forceinline__ void mfma_body(const uint16_t* __restrict__ x, const 
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
-    if (r % WK != kw) continue;
+    if ((r & (WK - 1)) != kw) continue;
     f4 t = red[sub * WK][r][lane];
     for (int i = 1; i < WK; ++i) t += red[sub * WK + i][r][lane];   // fixed order: deterministic
     store(r, t);
@@ -705,10 +730,8 @@ __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_silu_kernel(const ui
 // its own K split, and a workgroup holds blockDim / 64 / WK of its row groups.
 template <int FMT, int RB>
 __global__ __launch_bounds__(64 * MFMA_MAX_WAVES) void mfma_grouped_kernel(const GemvGroup g, int M) {
-  int j = 0;
-  while (j + 1 < g.count && (int)blockIdx.x >= g.first_block[j + 1]) ++j;   // workgroup-uniform
-  mfma_body<FMT, RB>(g.x[j], g.w[j], g.scales[j], g.zeros[j], g.y[j], M, g.N[j], g.K[j], blockIdx.x - g.first_block[j],
-                     g.WK[j]);
+  const GroupItem& it = group_item(g);
+  mfma_body<FMT, RB>(it.x, it.w, it.scales, it.zeros, it.y, M, it.N, it.K, blockIdx.x - it.first_block, it.WK);
 }
 
 // ---------------------------------------------------------------- W4 / W6 / FP4 on the matrix cores through LDS
@@ -909,12 +932,13 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
   extern __shared__ uint4 lm_lds[];
   const int lane = threadIdx.x & 63;
   const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int R = LM_WAVES / WK;
-  const int sub = wave_id / WK, kw = wave_id - sub * WK;
+  const int lwk = wk_log2(WK);
+  const int R = LM_WAVES >> lwk;
+  const int sub = wave_id >> lwk, kw = wave_id & (WK - 1);
   const int nl = lane & 15, q = lane >> 4;
   const int U = K >> 5, H = (U + 31) >> 5;
   const int n0 = (block * R + sub) * 16 * RB;
-  const int NI = kw < H ? (H - kw + WK - 1) / WK : 0;
+  const int NI = kw < H ? (H - kw + WK - 1) >> lwk : 0;
   uint8_t* lds = reinterpret_cast<uint8_t*>(lm_lds) + wave_id * RB * lm_block<FMT>();
   f4 acc[RB][MT];
 #pragma unroll
@@ -1025,7 +1049,7 @@ __device__ __forceinline__ void lm_body(const uint16_t* __restrict__ x, const ui
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
-    if (r % WK != kw) continue;
+    if ((r & (WK - 1)) != kw) continue;
     const int n = n0 + 16 * r + nl;
     const float sc = row_scaled<FMT>() && n < N ? f16_to_f32(scales[n]) * code_scale<FMT>() : 1.0f;
 #pragma unroll
@@ -1076,10 +1100,8 @@ __global__ __launch_bounds__(64 * LM_WAVES) void lm_silu_kernel(const uint16_t* 
 // Several linears in a single launch (see GemvGroup), each with its own K split.
 template <int FMT, int RB, int MT>
 __global__ __launch_bounds__(64 * LM_WAVES) void lm_grouped_kernel(const GemvGroup g, int M) {
-  int j = 0;
-  while (j + 1 < g.count && (int)blockIdx.x >= g.first_block[j + 1]) ++j;   // workgroup-uniform
-  lm_body<FMT, RB, MT>(g.x[j], g.w[j], g.scales[j], g.zeros[j], g.y[j], M, g.N[j], g.K[j],
-                       blockIdx.x - g.first_block[j], g.WK[j]);
+  const GroupItem& it = group_item(g);
+  lm_body<FMT, RB, MT>(it.x, it.w, it.scales, it.zeros, it.y, M, it.N, it.K, blockIdx.x - it.first_block, it.WK);
 }
 
 // ---------------------------------------------------------------- dequant
@@ -1633,28 +1655,31 @@ int wq_linear_grouped(const wq_linear_item* items, int count, int64_t M, int fmt
   grouped_order(items, count, order);
   GemvGroup g = {};
   g.count = count;
+  int WKs[MAX_GROUP];
   int block_waves = fam == FAM_GEMV ? GEMV_WAVES : fam == FAM_LM ? LM_WAVES : 1;
   for (int i = 0; i < count; ++i) {
     const int64_t n = items[order[i]].N, k = items[order[i]].K;
-    g.WK[i] = fam == FAM_GEMV ? gemv_waves_for(pf, n, k, B) : fam == FAM_LM ? lm_waves_for(pf, n, k, B) : mfma_waves_for(n, k, B);
-    if (fam == FAM_MFMA) block_waves = std::max(block_waves, g.WK[i]);   // powers of two up to MFMA_MAX_WAVES
+    WKs[i] = fam == FAM_GEMV ? gemv_waves_for(pf, n, k, B) : fam == FAM_LM ? lm_waves_for(pf, n, k, B) : mfma_waves_for(n, k, B);
+    if (fam == FAM_MFMA) block_waves = std::max(block_waves, WKs[i]);   // powers of two up to MFMA_MAX_WAVES
   }
   const int rows_per_block = fam == FAM_GEMV ? B : 16 * B;
   int grid = 0;
+  for (int i = 0; i < MAX_GROUP; ++i) g.first_block[i] = INT_MAX;
   for (int i = 0; i < count; ++i) {
     const wq_linear_item& it = items[order[i]];
-    const int R = block_waves / g.WK[i];
-    g.first_block[i] = grid;
-    g.x[i] = it.x;
-    g.w[i] = static_cast<const uint8_t*>(it.packed_w);
-    g.scales[i] = it.scales;
-    g.zeros[i] = it.zeros;
-    g.y[i] = it.y;
-    g.N[i] = static_cast<int>(it.N);
-    g.K[i] = static_cast<int>(it.K);
+    const int R = block_waves / WKs[i];
+    GroupItem& gi = g.item[i];
+    g.first_block[i] = gi.first_block = grid;
+    gi.x = it.x;
+    gi.w = static_cast<const uint8_t*>(it.packed_w);
+    gi.scales = it.scales;
+    gi.zeros = it.zeros;
+    gi.y = it.y;
+    gi.N = static_cast<int>(it.N);
+    gi.K = static_cast<int>(it.K);
+    gi.WK = WKs[i];
     grid += static_cast<int>(((it.N + rows_per_block - 1) / rows_per_block + R - 1) / R);
   }
-  g.first_block[count] = grid;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (fam == FAM_GEMV) {
