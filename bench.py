@@ -276,6 +276,41 @@ def time_steps(torch, run_step, steps, warmup, rot, spread=None):
     return e0.elapsed_time(e1)
 
 
+def plain_read_floor(torch, nbytes, steps, warmup):
+    """How fast a kernel that only reads does it for the same byte count: libwq_probe.so streams
+    a buffer of nbytes with contiguous 1 KB wave loads, rotated over copies and timed exactly as
+    the step is (graph replays, events). The fastest of a few wave counts and load depths is
+    reported: the practical ceiling of a weight stream of this size on this GPU, against which
+    the 8 TB/s peak alone overstates what any kernel of this size can reach."""
+    import ctypes
+    path = os.path.join(ROOT, "weight_only_quantized_dequant_amd", "libwq_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libwq_probe.so is missing: build with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.wq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.wq_probe_read.restype = ctypes.c_int
+    nb = nbytes // 16 * 16
+    rot = max(1, math.ceil(ROTATE_BYTES / nb))
+    bufs = [torch.full((nb,), i + 1, dtype=torch.uint8, device="cuda") for i in range(rot)]
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    variants = {}
+    for waves, unroll in ((4096, 2), (16384, 4), (32768, 2)):
+        def run(i):
+            st = lib.wq_probe_read(bufs[i % rot].data_ptr(), nb, waves, unroll, sink.data_ptr(), sink.numel(),
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError("wq_probe_read failed: %d" % st)
+        ms = time_steps(torch, run, steps, warmup, rot)
+        variants["waves=%d,loads_in_flight=%d" % (waves, unroll)] = round(1e3 * ms / steps, 3)
+    best = min(variants.values())
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return {"bytes": nb, "us": best, "GB/s": round(nb / best / 1e3, 1), "pct_of_peak": round(100 * nb / best / 1e3 / PEAK_HBM_GBS, 2),
+            "us_by_variant": variants, "what": "the fastest plain read of the step's algorithmic bytes "
+            "(libwq_probe.so, one contiguous span per wave), timed like the step"}
+
+
 def gpu_state(torch):
     """The device and its current clock levels and power as the kernel driver's sysfs files show
     them (plain file reads, best effort: no helper program is started)."""
@@ -725,6 +760,10 @@ def main():
                 "algorithmic_bytes_per_launch": int(step_bytes / launches)}
 
     extras = {}
+    if not args.main_only:
+        floor = plain_read_floor(torch, step_bytes, steps, args.warmup)
+        floor["kernel_frac_of_floor"] = round(floor["us"] / (1e3 * avg_launch_ms * launches), 4)
+        extras["plain_read_floor"] = floor
     # each linear alone (one launch per step, its own graph): per-shape durations and rates
     per_shape = {}
     for l in ([] if args.main_only else lins):

@@ -15,6 +15,9 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libwq.so")
+# the plain-read probe that bench.py times beside the linears (measurement only, not libwq)
+PROBE_SRC = os.path.join(CSRC, "probe", "read_floor.hip")
+PROBE_LIB = os.path.join(HERE, "libwq_probe.so")
 ARCH = "gfx950"
 
 # Flags of one translation unit only. The prefill kernel keeps its MFMA accumulators in VGPRs:
@@ -37,7 +40,8 @@ def _run(cmd):
 
 
 def build(verbose=False):
-    """Compile csrc/*.hip and csrc/*.cpp into libwq.so. Returns the library path."""
+    """Compile csrc/*.hip and csrc/*.cpp into libwq.so, and csrc/probe/read_floor.hip into
+    libwq_probe.so. Returns the path of libwq.so."""
     names = [f for f in sorted(os.listdir(CSRC)) if f.endswith((".hip", ".cpp"))]
     common = [hipcc(), "--offload-arch=%s" % ARCH, "-O3", "-std=c++17", "-fPIC",
               # packed fp32 VALU ops stay off: the compiler must not form v_pk_{add,mul,fma}_f32
@@ -59,6 +63,11 @@ def build(verbose=False):
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    rc, m = _run(common + ["-shared", PROBE_SRC, "-o", tmp])
+    if rc != 0:
+        raise RuntimeError("libwq_probe build failed:\n" + "\n".join(m))
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
