@@ -32,6 +32,26 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def test_read_probe_library_rejects_bad_arguments_before_any_launch():
+    # the plain-read probe that bench.py times beside the linears: built with libwq, and every
+    # argument error returns -1 without touching the device
+    path = os.path.join(os.path.dirname(wq.LIB_PATH), "libwq_probe.so")
+    assert os.path.exists(path)
+    P = ctypes.CDLL(path)
+    f = P.wq_probe_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    a = 1 << 20   # an aligned address the checks stop before any use
+    assert f(None, 1024, 4096, 2, a, 1024, None) == -1                 # no buffer
+    assert f(a, 1024, 4096, 2, None, 1024, None) == -1                 # no sink
+    assert f(a, 1000, 4096, 2, a, 1024, None) == -1                    # not a multiple of 16 bytes
+    assert f(a, 1024, 4098, 2, a, 1024, None) == -1                    # waves not a multiple of 4
+    assert f(a, 1024, 8192, 2, a, 1024, None) == -1                    # sink smaller than waves / 4 words
+    assert f(a, 1024, 4096, 3, a, 1024, None) == -1                    # 2 or 4 loads in flight only
+    assert f(a + 8, 1024, 4096, 2, a, 1024, None) == -1                # buffer not 16-byte aligned
+
+
 def test_version_and_status_strings():
     assert wq.wq_version() >> 16 == 1
     for s in range(-8, 1):
