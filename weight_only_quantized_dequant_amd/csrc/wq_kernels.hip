@@ -1167,7 +1167,8 @@ struct GemvPlan {
 };
 
 // Waves splitting K: the fewest that give enough waves over the row blocks (W4, with the
-// most decode work per byte, runs best at ~4 waves per CU, the others at ~16), then,
+// most decode work per byte, runs best at ~4 waves per CU, W8 at ~32 (Llama-7B linears at
+// M = 1: 18.9 -> 18.6 us against ~16; ~4 and ~8 were slower), the others at ~16), then,
 // among the splits with the same chunks per wave, the smallest (even work). Only powers
 // of two, so that workgroups hold a multiple of 4 waves and spread evenly over a CU's
 // four SIMDs (a 6-wave workgroup puts two waves on two SIMDs and one on the others).
@@ -1176,7 +1177,8 @@ struct GemvPlan {
 int gemv_waves_for(int fmt, int64_t N, int64_t K, int B) {
   const int64_t L = fmt == WQ_FMT_W8 ? 16 : fmt == WQ_FMT_F16 ? 8 : 32;
   const int64_t C = (K / L + 63) / 64, blocks = (N + B - 1) / B;
-  const int64_t target = fmt == WQ_FMT_W4G32 || fmt == WQ_FMT_W4E2M1 || fmt == WQ_FMT_W3G32 ? 1024 : 4096;
+  const int64_t target = fmt == WQ_FMT_W4G32 || fmt == WQ_FMT_W4E2M1 || fmt == WQ_FMT_W3G32 ? 1024
+                         : fmt == WQ_FMT_W8 ? 8192 : 4096;
   static const int cand[] = {1, 2, 4};
   int WK = 1;
   for (int w : cand) {
