@@ -57,7 +57,7 @@ int wq_add_rmsnorm(float* x, const uint16_t* delta, const uint16_t* g, float eps
                    void* stream);
 
 /* Host: bytes of the workspace wq_rope_attention needs for these sizes (the partial results of the
- * position chunks); 0 when max_seq <= 64. */
+ * position chunks); 0 when max_seq <= 4096 (one workgroup per head, nothing leaves it). */
 size_t wq_attention_workspace_bytes(int64_t M, int64_t n_heads, int64_t head_dim, int64_t max_seq);
 
 /* Device: rotary embedding, key/value cache append and attention of one new token per sequence.
@@ -70,10 +70,12 @@ size_t wq_attention_workspace_bytes(int64_t M, int64_t n_heads, int64_t head_dim
  * in float32. q, out [M, n_heads*head_dim] fp16; k, v [M, n_kv_heads*head_dim] fp16; cache_k,
  * cache_v [M, max_seq, n_kv_heads*head_dim] fp16 (this layer's); rope_cos, rope_sin float32
  * [max_seq, head_dim/2] (wq_rope_table). head_dim 64 or 128; n_heads a multiple of n_kv_heads.
- * The positions are split over workgroups of 64; when max_seq exceeds 64 their partial results
- * meet in `workspace` (wq_attention_workspace_bytes; WQ_ERR_ARG if smaller; no initial contents
- * needed) and a second launch combines them. Calls that share a workspace must not overlap in
- * time. */
+ * Caches of up to 4096 positions (max_seq <= 4096): one launch, one workgroup per (query head,
+ * sequence), and `workspace` is not used (it may be NULL). Longer caches: the positions are split
+ * over workgroups of 64, whose partial results meet in `workspace` (wq_attention_workspace_bytes;
+ * WQ_ERR_ARG if smaller; no initial contents needed), and a second launch combines them; calls
+ * that share a workspace must not overlap in time. The two paths sum in different orders, so their
+ * results may differ in the last bits; each is deterministic. */
 int wq_rope_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* cache_k, uint16_t* cache_v,
                       const float* rope_cos, const float* rope_sin, const int32_t* pos, uint16_t* out, int64_t M,
                       int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t max_seq, void* workspace,

@@ -181,9 +181,29 @@ def test_rope_attention_position_past_the_cache_is_clamped():
 
 
 def test_rope_attention_llama7b_shape_long_context():
-    # Llama-2-7B heads (32 x 128) with 2048 cached positions at position 1500: 24 chunks of 64
+    # Llama-2-7B heads (32 x 128) with 2048 cached positions at position 1500: one workgroup of 16
+    # waves per head, 6 steps of 16 positions for most waves
     m, H, Hkv, hd, S, p = 1, 32, 32, 128, 2048, 1500
     q, k, v, ck, cv = _attention_case(m, H, Hkv, hd, S, p, 4)
+    _check_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, p, calls=2)
+
+
+@pytest.mark.parametrize("hd,p", [(128, 4095), (128, 255), (64, 4000), (64, 511)])
+def test_rope_attention_largest_single_workgroup_cache(hd, p):
+    # 4096 positions, the longest cache one workgroup per head serves (no workspace)
+    m, H, Hkv, S = 1, 4, 2, 4096
+    assert wq.wq_attention_workspace_bytes(m, H, hd, S) == 0
+    q, k, v, ck, cv = _attention_case(m, H, Hkv, hd, S, p, 5)
+    _check_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, p, calls=2)
+
+
+@pytest.mark.parametrize("hd,p", [(128, 4200), (128, 63), (128, 64), (64, 4159), (64, 1000)])
+def test_rope_attention_chunked_past_4096_positions(hd, p):
+    # a cache longer than 4096 positions: chunks of 64 positions whose partial results meet in the
+    # workspace, and the combine launch
+    m, H, Hkv, S = 2, 4, 2, 4160
+    assert wq.wq_attention_workspace_bytes(m, H, hd, S) > 0
+    q, k, v, ck, cv = _attention_case(m, H, Hkv, hd, S, p, 6)
     _check_attention(q, k, v, ck, cv, m, H, Hkv, hd, S, p, calls=2)
 
 
@@ -194,7 +214,7 @@ def test_rope_attention_rejects_bad_arguments():
     pa = a.data_ptr()
     assert L.wq_rope_attention(pa, pa, pa, pa, pa, pa, pa, pa, pa, 1, 4, 3, 64, 16, None, 0, None) == -2   # 4 % 3
     assert L.wq_rope_attention(pa, pa, pa, pa, pa, pa, pa, pa, pa, 1, 4, 4, 96, 16, None, 0, None) == -2   # head size
-    assert L.wq_rope_attention(pa, pa, pa, pa, pa, pa, pa, pa, pa, 1, 4, 4, 64, 129, None, 0, None) == -1   # workspace
+    assert L.wq_rope_attention(pa, pa, pa, pa, pa, pa, pa, pa, pa, 1, 4, 4, 64, 4097, None, 0, None) == -1  # workspace
     assert L.wq_rope_attention(pa + 2, pa, pa, pa, pa, pa, pa, pa, pa, 1, 4, 4, 64, 16, None, 0, None) == -5
     assert L.wq_add_rmsnorm(pa, None, pa, 1e-5, pa, 1, 20, None) == -2
     assert L.wq_silu_mul(pa, pa, pa, 12, None) == -2

@@ -587,10 +587,11 @@ def test_decode_entry_points_reject_bad_arguments_before_launch():
     assert L.wq_silu_mul(a, a, a, 0, None) == -2
     assert L.wq_argmax_next(a, 0, 16, a, a, None) == -2
     assert L.wq_rope_attention(a, a, a, a, a, a, a, a, a, 1, 6, 4, 128, 16, None, 0, None) == -2   # 6 % 4
-    assert L.wq_rope_attention(a, a, a, a, a, a, a, a, a, 1, 4, 4, 128, 200, None, 0, None) == -1  # no workspace
-    need = wq.wq_attention_workspace_bytes(1, 4, 128, 200)
-    assert need > 0 and wq.wq_attention_workspace_bytes(1, 4, 128, 64) == 0 and wq.wq_attention_workspace_bytes(1, 4, 128, 65) > 0
-    assert L.wq_rope_attention(a, a, a, a, a, a, a, a, a, 1, 4, 4, 128, 200, a, need - 1, None) == -1
+    assert L.wq_rope_attention(a, a, a, a, a, a, a, a, a, 1, 4, 4, 128, 5000, None, 0, None) == -1  # no workspace
+    need = wq.wq_attention_workspace_bytes(1, 4, 128, 5000)
+    # caches of up to 4096 positions take one workgroup per head and no workspace; longer ones the chunks
+    assert need > 0 and wq.wq_attention_workspace_bytes(1, 4, 128, 4096) == 0 and wq.wq_attention_workspace_bytes(1, 4, 128, 4097) > 0
+    assert L.wq_rope_attention(a, a, a, a, a, a, a, a, a, 1, 4, 4, 128, 5000, a, need - 1, None) == -1
 
 
 def test_decode_binding_rejects_cpu_and_short_buffers(monkeypatch):
@@ -607,7 +608,7 @@ def test_decode_binding_rejects_cpu_and_short_buffers(monkeypatch):
                              F(2 * S * Hkv * hd - 2), F(4 * S * hd // 2), F(4 * S * hd // 2), F(4), F(2 * H * hd),
                              m, H, Hkv, hd, S, None)
     with pytest.raises(ValueError, match="workspace"):
-        m, H, Hkv, hd, S = 1, 4, 2, 64, 256
+        m, H, Hkv, hd, S = 1, 4, 2, 64, 4160
         need = wq.wq_attention_workspace_bytes(m, H, hd, S)
         wq.wq_rope_attention(F(2 * H * hd), F(2 * Hkv * hd), F(2 * Hkv * hd), F(2 * S * Hkv * hd),
                              F(2 * S * Hkv * hd), F(4 * S * hd // 2), F(4 * S * hd // 2), F(4), F(2 * H * hd),

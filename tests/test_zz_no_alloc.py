@@ -41,8 +41,8 @@ def _call(noalloc, m, H, Hkv, hd, S, p, seed):
 
 
 def test_noalloc_matches_the_workspace_call_twice_in_a_row():
-    cases = [(4, 32, 8, 128, 2048, 1500, 1),   # 24 chunks: partial results through the scratch buffer
-             (2, 8, 2, 64, 512, 300, 2)]       # smaller, right after it on the same buffer
+    cases = [(2, 16, 4, 128, 8192, 6000, 1),   # 94 chunks: partial results through the scratch buffer
+             (1, 8, 2, 64, 4608, 4200, 2)]     # smaller, right after it on the same buffer
     got = [_call(True, *c) for c in cases]
     for c, g in zip(cases, got):
         want = _call(False, *c)

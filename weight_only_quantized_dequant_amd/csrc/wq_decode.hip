@@ -9,7 +9,10 @@
 // gfx950 design:
 //  * Every kernel reads the decode position and the token ids from device memory, so a step is
 //    captured once as a HIP graph and replayed for step after step; wq_argmax_next advances them.
-//  * Attention of one new token (flash-decoding style): the positions 0..pos are cut into
+//  * Attention of one new token, caches of up to 4096 positions: one workgroup of 16 waves per
+//    (query head, sequence) over all positions, a running softmax per wave and the waves combined
+//    in LDS: one launch and no workspace (rope_attention_wide_kernel). Longer caches, flash-decoding
+//    style: the positions 0..pos are cut into
 //    chunks of 64, one workgroup per (chunk, query head, sequence), so that even a short context
 //    spreads over the CUs (Llama-2-7B at 512 positions: 256 workgroups; chunks of 128 left half
 //    the CUs idle). A workgroup first issues the loads of all its key and value rows (16
@@ -35,7 +38,11 @@
 namespace {
 
 constexpr int DEC_THREADS = 256;
-constexpr int ATT_CHUNK = 64;    // positions per attention workgroup (at 512 cached positions, 8 per head)
+constexpr int ATT_CHUNK = 64;    // positions per attention workgroup of the chunked kernel
+constexpr int ATT_WIDE_THREADS = 1024;   // the single-workgroup kernel: 16 waves per (query head, sequence)
+constexpr int ATT_WIDE_MAX = 4096;       // longest cache (positions) it serves; longer ones take the chunks
+constexpr int ATT_WIDE_PPL = 32 * 16;    // positions x dimensions per 16-lane group and step (a register budget:
+                                         // 4 positions per lane group at head size 128, 8 at 64)
 
 __device__ __forceinline__ float f16v(uint32_t bits) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits); }
 __device__ __forceinline__ uint32_t to_f16(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
@@ -341,6 +348,164 @@ __global__ __launch_bounds__(DEC_THREADS) void rope_attention_kernel(
   if (tid == 0) { pr[0] = mx; pr[1] = l; }
 }
 
+// One workgroup of 16 waves per (query head h, sequence m) over all positions 0..p, for caches of
+// up to ATT_WIDE_MAX positions: no partial result leaves the workgroup, so there is no workspace
+// and no combine launch (a launch costs a few microseconds whatever it does, and the chunked
+// kernel's combine was one per layer). Wave w takes the steps of STEP positions (16 at head size
+// 128, 32 at 64) that start at STEP w, STEP (w + 16), ...; lane (lg = lane / 16, j = lane % 16)
+// holds dimensions j*HD/16.. of positions step + lg + 4 i (i < STEP / 4), as a 16-byte (8-byte)
+// slice of each key and value row. Each wave keeps
+// a running softmax over its steps (its maximum M_w, sum L_w and weighted values A_w, rescaled by
+// e^(old max - new max) when the maximum grows); the 16 waves then meet in LDS and thread d < HD
+// combines them in wave order: out = sum_w e^(M_w - M) A_w / sum_w e^(M_w - M) L_w (deterministic).
+// The query (float32, scaled by 1/sqrt(HD)) and the new key at p are rotated as in the chunked
+// kernel; one query head of each key/value group writes the cache row at p, and every head uses
+// the rotated key and the value from LDS at p rather than the cache row.
+template <int HD>
+__global__ __launch_bounds__(ATT_WIDE_THREADS) void rope_attention_wide_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ cache_k, uint16_t* __restrict__ cache_v, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, const int32_t* __restrict__ posp, uint16_t* __restrict__ out, int H, int Hkv,
+    int S) {
+  constexpr int P2 = HD / 2;               // rotated pairs of a head
+  constexpr int DPL = HD / 16;             // dimensions per lane
+  constexpr int WPL = DPL / 2;             // their 32-bit words
+  constexpr int NW = ATT_WIDE_THREADS / 64;
+  constexpr int PPL = ATT_WIDE_PPL / HD;   // positions of a lane group per step
+  constexpr int STEP = 4 * PPL;            // positions of one wave step
+  __shared__ float qs[HD], kn[HD], vn[HD], wm[NW], wl[NW], wacc[NW][HD];
+  const int h = blockIdx.x, m = blockIdx.y, tid = threadIdx.x;
+  const int wave = tid >> 6, lg = (tid >> 4) & 3, j = tid & 15;
+  int p = *posp;
+  p = p < 0 ? 0 : p >= S ? S - 1 : p;
+  const int group = H / Hkv, kh = h / group;
+  const size_t kvrow = (size_t)Hkv * HD;   // elements of one cache position
+  const uint16_t* ckm = cache_k + (size_t)m * S * kvrow + (size_t)kh * HD + j * DPL;
+  const uint16_t* cvm = cache_v + (size_t)m * S * kvrow + (size_t)kh * HD + j * DPL;
+
+  uint32_t kw[PPL][WPL], vw[PPL][WPL];
+  auto load = [&](int t0) {   // positions past p read position p (its row is not used: kn, vn replace it)
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const size_t t = (size_t)min(t0 + lg + 4 * i, p);
+      if constexpr (WPL == 4) {
+        const uint4 a = *reinterpret_cast<const uint4*>(ckm + t * kvrow);
+        const uint4 b = *reinterpret_cast<const uint4*>(cvm + t * kvrow);
+        kw[i][0] = a.x; kw[i][1] = a.y; kw[i][2] = a.z; kw[i][3] = a.w;
+        vw[i][0] = b.x; vw[i][1] = b.y; vw[i][2] = b.z; vw[i][3] = b.w;
+      } else {
+        const uint2 a = *reinterpret_cast<const uint2*>(ckm + t * kvrow);
+        const uint2 b = *reinterpret_cast<const uint2*>(cvm + t * kvrow);
+        kw[i][0] = a.x; kw[i][1] = a.y;
+        vw[i][0] = b.x; vw[i][1] = b.y;
+      }
+    }
+  };
+  const int first = wave * STEP;
+  if (first <= p) load(first);   // wave-uniform: the first step's loads before the rotation
+
+  if (tid < P2) {   // rotate pair tid of the query (kept in float32, scaled), and of the new key
+    const float co = rope_cos[(size_t)p * P2 + tid], si = rope_sin[(size_t)p * P2 + tid];
+    const float scale = 1.0f / sqrtf((float)HD);
+    const uint32_t qq = *reinterpret_cast<const uint32_t*>(q + ((size_t)m * H + h) * HD + 2 * tid);
+    qs[2 * tid] = (lo16(qq) * co - hi16(qq) * si) * scale;
+    qs[2 * tid + 1] = (lo16(qq) * si + hi16(qq) * co) * scale;
+    const uint32_t kk = *reinterpret_cast<const uint32_t*>(k + ((size_t)m * Hkv + kh) * HD + 2 * tid);
+    const uint32_t vv = *reinterpret_cast<const uint32_t*>(v + ((size_t)m * Hkv + kh) * HD + 2 * tid);
+    const uint32_t kr = to_f16(lo16(kk) * co - hi16(kk) * si) | (to_f16(lo16(kk) * si + hi16(kk) * co) << 16);
+    kn[2 * tid] = lo16(kr);
+    kn[2 * tid + 1] = hi16(kr);
+    vn[2 * tid] = lo16(vv);
+    vn[2 * tid + 1] = hi16(vv);
+    if (h % group == 0) {   // one query head of the group writes the cache; the others use kn, vn
+      *reinterpret_cast<uint32_t*>(cache_k + ((size_t)m * S + p) * kvrow + (size_t)kh * HD + 2 * tid) = kr;
+      *reinterpret_cast<uint32_t*>(cache_v + ((size_t)m * S + p) * kvrow + (size_t)kh * HD + 2 * tid) = vv;
+    }
+  }
+  __syncthreads();
+
+  float qv[DPL];
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) qv[d] = qs[j * DPL + d];
+  float mx = -INFINITY, l = 0.0f, acc[DPL];
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) acc[d] = 0.0f;
+  for (int t0 = first; t0 <= p; t0 += NW * STEP) {   // wave-uniform loop
+    if (t0 != first) load(t0);
+    float sc[PPL];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {   // scores: a 16-lane shuffle sum per position
+      const int t = t0 + lg + 4 * i;
+      float s = 0.0f;
+      if (t == p) {
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) s += qv[d] * kn[j * DPL + d];
+      } else {
+#pragma unroll
+        for (int w = 0; w < WPL; ++w) s += qv[2 * w] * lo16(kw[i][w]) + qv[2 * w + 1] * hi16(kw[i][w]);
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
+      sc[i] = t <= p ? s : -INFINITY;
+      bm = fmaxf(bm, sc[i]);
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));   // the step's maximum over the wave: finite (t0 <= p)
+    const float nm = fmaxf(mx, bm);
+    const float so = expf(mx - nm);       // 0 on the wave's first step
+    l *= so;
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) acc[d] *= so;
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {       // weighted values of this lane's positions
+      const int t = t0 + lg + 4 * i;
+      const float e = expf(sc[i] - nm);   // 0 past p
+      l += e;
+      if (t == p) {
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) acc[d] += e * vn[j * DPL + d];
+      } else {
+#pragma unroll
+        for (int w = 0; w < WPL; ++w) {
+          acc[2 * w] += e * lo16(vw[i][w]);
+          acc[2 * w + 1] += e * hi16(vw[i][w]);
+        }
+      }
+    }
+    mx = nm;
+  }
+  // the wave's 4 lane groups share its maximum: add their sums (a fixed xor tree), then the waves
+  // meet in LDS (a wave with no positions brings M = -inf, L = 0, A = 0)
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) {
+    acc[d] += __shfl_xor(acc[d], 16);
+    acc[d] += __shfl_xor(acc[d], 32);
+  }
+  if (lg == 0) {
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) wacc[wave][j * DPL + d] = acc[d];
+    if (j == 0) {
+      wm[wave] = mx;
+      wl[wave] = l;
+    }
+  }
+  __syncthreads();
+  if (tid < HD) {
+    float M = -INFINITY;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w]);   // finite: wave 0 holds position 0
+    float L = 0.0f, A = 0.0f;
+    for (int w = 0; w < NW; ++w) {   // waves in order: deterministic
+      const float c = expf(wm[w] - M);
+      L += c * wl[w];
+      A += c * wacc[w][tid];
+    }
+    out[((size_t)m * H + h) * HD + tid] = (uint16_t)to_f16(A / L);
+  }
+}
+
 // The chunks of one (query head, sequence) combined in chunk order (deterministic), as a running
 // softmax: M the largest maximum so far, L = sum_c e^(max_c - M) sum_c, A = sum_c e^(max_c - M)
 // acc_c; out = A / L. A separate launch, so that every chunk's partial result is visible to it
@@ -455,7 +620,7 @@ int wq_add_rmsnorm(float* x, const uint16_t* delta, const uint16_t* g, float eps
 
 size_t wq_attention_workspace_bytes(int64_t M, int64_t n_heads, int64_t head_dim, int64_t max_seq) {
   if (M < 1 || n_heads < 1 || head_dim < 1 || max_seq < 1) return 0;
-  if (att_splits(max_seq) == 1) return 0;   // a single chunk needs no workspace
+  if (max_seq <= ATT_WIDE_MAX) return 0;   // one workgroup per head: no partial results leave it
   return att_part_bytes(M, n_heads, head_dim, max_seq);
 }
 
@@ -488,10 +653,19 @@ int wq_rope_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
   const size_t need = wq_attention_workspace_bytes(M, n_heads, head_dim, max_seq);
   if (need && (!workspace || workspace_bytes < need)) return WQ_ERR_ARG;
   if (need && !aligned16(workspace)) return WQ_ERR_ALIGN;
-  const int splits = (int)att_splits(max_seq);
-  float* part = need ? static_cast<float*>(workspace) : nullptr;
-  const dim3 grid((unsigned)splits, (unsigned)n_heads, (unsigned)M);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_seq <= ATT_WIDE_MAX) {   // one workgroup per (query head, sequence), one launch
+    const dim3 gw((unsigned)n_heads, (unsigned)M);
+    return wq::device_status(
+        head_dim == 128
+            ? launch(rope_attention_wide_kernel<128>, gw, dim3(ATT_WIDE_THREADS), 0, s, q, k, v, cache_k, cache_v,
+                     rope_cos, rope_sin, pos, out, (int)n_heads, (int)n_kv_heads, (int)max_seq)
+            : launch(rope_attention_wide_kernel<64>, gw, dim3(ATT_WIDE_THREADS), 0, s, q, k, v, cache_k, cache_v,
+                     rope_cos, rope_sin, pos, out, (int)n_heads, (int)n_kv_heads, (int)max_seq));
+  }
+  const int splits = (int)att_splits(max_seq);
+  float* part = static_cast<float*>(workspace);
+  const dim3 grid((unsigned)splits, (unsigned)n_heads, (unsigned)M);
   hipError_t e =
       head_dim == 128
           ? launch(rope_attention_kernel<128>, grid, dim3(DEC_THREADS), 0, s, q, k, v, cache_k, cache_v, rope_cos, rope_sin,
