@@ -95,6 +95,9 @@ def parse():
     ap.add_argument("--weights", default="w4g32", help="weight format of --decode")
     ap.add_argument("--context", type=int, default=512, help="cached positions when --decode starts timing")
     ap.add_argument("--max-seq", type=int, default=2048, help="key/value cache length of --decode")
+    ap.add_argument("--read-floors", action="store_true",
+                    help="time only the plain-read probe (libwq_probe.so) at the byte counts of the linears and "
+                         "groups measured here, and an empty launch: the floors the design notes compare against")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 512 MiB (a known-size kernel for counter calibration)")
     ap.add_argument("--settle-ms", type=float, default=200.0,
@@ -309,6 +312,46 @@ def plain_read_floor(torch, nbytes, steps, warmup):
     return {"bytes": nb, "us": best, "GB/s": round(nb / best / 1e3, 1), "pct_of_peak": round(100 * nb / best / 1e3 / PEAK_HBM_GBS, 2),
             "us_by_variant": variants, "what": "the fastest plain read of the step's algorithmic bytes "
             "(libwq_probe.so, one contiguous span per wave), timed like the step"}
+
+
+def run_read_floors(args, torch):
+    """The plain-read floor (plain_read_floor) at the byte counts of single linears and grouped
+    launches of both headline models, and the time per launch of a kernel that does nothing
+    (1 and 1024 workgroups), all timed as the steps are (graph replays, events)."""
+    import ctypes
+    path = os.path.join(ROOT, "weight_only_quantized_dequant_amd", "libwq_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libwq_probe.so is missing: build with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.wq_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.wq_probe_empty.restype = ctypes.c_int
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    steps = args.steps
+    empty = {}
+    for wg in (1, 1024):
+        def run(i, wg=wg):
+            st = lib.wq_probe_empty(wg, sink.data_ptr(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError("wq_probe_empty failed: %d" % st)
+        # graphs of 100 launches: the launches run back to back, as the linears of a step do
+        empty["workgroups=%d" % wg] = round(1e3 * time_steps(torch, run, steps, args.warmup, 100) / steps, 3)
+    sizes = {}
+    for name, fmt_name, shapes in (("llama7b_w4g32 4096x4096", "w4g32", [(4096, 4096)]),
+                                   ("llama7b_w4g32 11008x4096", "w4g32", [(11008, 4096)]),
+                                   ("llama7b_w4g32 group of 3", "w4g32", [(4096, 4096), (11008, 4096), (4096, 11008)]),
+                                   ("llama7b_w8 group of 3", "w8", [(4096, 4096), (11008, 4096), (4096, 11008)]),
+                                   ("llama70b_w6e3m2 group of 4", "w6e3m2", [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)])):
+        fmt = FMT_OF[fmt_name]
+        nbytes = sum(wq.wq_packed_bytes(fmt, n, k) + metadata_bytes(fmt, n, k) + 2 * k + 2 * n for n, k in shapes)
+        f = plain_read_floor(torch, nbytes, steps, args.warmup)
+        sizes[name] = {"bytes": f["bytes"], "us": f["us"], "GB/s": f["GB/s"], "pct_of_peak": f["pct_of_peak"]}
+    print(json.dumps({"metric": "plain-read floor and empty-launch cost", "unit": "us", "steps": steps, "warmup": args.warmup,
+                      "empty_launch_us": empty, "plain_read_floor": sizes,
+                      "what": "libwq_probe.so kernels timed as graph replays with events on the launch stream; the floor "
+                              "of a byte count is the fastest of three wave counts (bench.py plain_read_floor), the bytes "
+                              "those of the linears' weights, metadata, x and y at M = 1",
+                      "gpu": gpu_state(torch), "clock_settle": {"ms_min": round(min(t for t, _ in SETTLE_LOG), 1)}}))
+    return 0
 
 
 def gpu_state(torch):
@@ -694,6 +737,8 @@ def main():
         return run_decode(args, torch)
     if args.sweep:
         return run_sweep(args, torch)
+    if args.read_floors:
+        return run_read_floors(args, torch)
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

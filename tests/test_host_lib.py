@@ -50,6 +50,10 @@ def test_read_probe_library_rejects_bad_arguments_before_any_launch():
     assert f(a, 1024, 8192, 2, a, 1024, None) == -1                    # sink smaller than waves / 4 words
     assert f(a, 1024, 4096, 3, a, 1024, None) == -1                    # 2 or 4 loads in flight only
     assert f(a + 8, 1024, 4096, 2, a, 1024, None) == -1                # buffer not 16-byte aligned
+    e = P.wq_probe_empty
+    e.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    e.restype = ctypes.c_int
+    assert e(1, None, None) == -1 and e(0, a, None) == -1              # no sink; no workgroups
 
 
 def test_version_and_status_strings():

@@ -39,9 +39,25 @@ __global__ __launch_bounds__(256) void read_span_kernel(const probe_u32x4* __res
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
+// A kernel that does nothing: launched back to back, what every launch costs whatever its work.
+__global__ __launch_bounds__(256) void empty_kernel(uint32_t* __restrict__ sink, uint32_t never) {
+  if (threadIdx.x == never) sink[0] = never;   // never == 0xFFFFFFFF: no thread stores
+}
+
 }  // namespace
 
 extern "C" {
+
+// Launch `workgroups` workgroups of 256 threads of a kernel that does nothing (sink: any device
+// buffer of 4 bytes or more, never written). Returns 0, -1 for bad arguments (nothing launched),
+// or the HIP error code of the launch.
+int wq_probe_empty(int workgroups, uint32_t* sink, void* stream) {
+  if (!sink || workgroups < 1) return -1;
+  uint32_t never = 0xFFFFFFFFu;
+  void* args[] = {&sink, &never};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(empty_kernel), dim3(workgroups), dim3(256), args, 0,
+                              static_cast<hipStream_t>(stream));
+}
 
 // Read `bytes` (a multiple of 16) of the device buffer `buf` (16-byte aligned) with `waves`
 // waves (a multiple of 4) and `unroll` (2 or 4) loads in flight per lane. `sink` is a device
