@@ -348,6 +348,17 @@ __global__ __launch_bounds__(DEC_THREADS) void rope_attention_kernel(
   if (tid == 0) { pr[0] = mx; pr[1] = l; }
 }
 
+// Sum over each row of 16 lanes, left in every lane of the row: four DPP adds (lane ^ 1, lane ^ 2,
+// the other half of each 8 lanes, the other half of the 16), no LDS traffic (a __shfl_xor tree
+// compiled to ds_bpermute, an LDS round trip per step).
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  v += dpp<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0x141, 0xF>(v);   // row_half_mirror
+  v += dpp<0x140, 0xF>(v);   // row_mirror
+  return v;
+}
+
 // One workgroup of 16 waves per (query head h, sequence m) over all positions 0..p, for caches of
 // up to ATT_WIDE_MAX positions: no partial result leaves the workgroup, so there is no workspace
 // and no combine launch (a launch costs a few microseconds whatever it does, and the chunked
@@ -359,8 +370,9 @@ __global__ __launch_bounds__(DEC_THREADS) void rope_attention_kernel(
 // e^(old max - new max) when the maximum grows); the 16 waves then meet in LDS and thread d < HD
 // combines them in wave order: out = sum_w e^(M_w - M) A_w / sum_w e^(M_w - M) L_w (deterministic).
 // The query (float32, scaled by 1/sqrt(HD)) and the new key at p are rotated as in the chunked
-// kernel; one query head of each key/value group writes the cache row at p, and every head uses
-// the rotated key and the value from LDS at p rather than the cache row.
+// kernel; one query head of each key/value group writes the cache row at p, and every head selects
+// the rotated key and the value at p (from LDS) in place of that cache row's words. Scores sum over
+// a position's 16 lanes with DPP; the exponentials are __expf (exp2 of x log2 e).
 template <int HD>
 __global__ __launch_bounds__(ATT_WIDE_THREADS) void rope_attention_wide_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -373,7 +385,8 @@ __global__ __launch_bounds__(ATT_WIDE_THREADS) void rope_attention_wide_kernel(
   constexpr int NW = ATT_WIDE_THREADS / 64;
   constexpr int PPL = ATT_WIDE_PPL / HD;   // positions of a lane group per step
   constexpr int STEP = 4 * PPL;            // positions of one wave step
-  __shared__ float qs[HD], kn[HD], vn[HD], wm[NW], wl[NW], wacc[NW][HD];
+  __shared__ float qs[HD], wm[NW], wl[NW], wacc[NW][HD];
+  __shared__ uint32_t knp[P2], vnp[P2];   // the rotated new key and the new value at p, fp16 pairs
   const int h = blockIdx.x, m = blockIdx.y, tid = threadIdx.x;
   const int wave = tid >> 6, lg = (tid >> 4) & 3, j = tid & 15;
   int p = *posp;
@@ -413,11 +426,9 @@ __global__ __launch_bounds__(ATT_WIDE_THREADS) void rope_attention_wide_kernel(
     const uint32_t kk = *reinterpret_cast<const uint32_t*>(k + ((size_t)m * Hkv + kh) * HD + 2 * tid);
     const uint32_t vv = *reinterpret_cast<const uint32_t*>(v + ((size_t)m * Hkv + kh) * HD + 2 * tid);
     const uint32_t kr = to_f16(lo16(kk) * co - hi16(kk) * si) | (to_f16(lo16(kk) * si + hi16(kk) * co) << 16);
-    kn[2 * tid] = lo16(kr);
-    kn[2 * tid + 1] = hi16(kr);
-    vn[2 * tid] = lo16(vv);
-    vn[2 * tid + 1] = hi16(vv);
-    if (h % group == 0) {   // one query head of the group writes the cache; the others use kn, vn
+    knp[tid] = kr;
+    vnp[tid] = vv;
+    if (h % group == 0) {   // one query head of the group writes the cache; the others use knp, vnp
       *reinterpret_cast<uint32_t*>(cache_k + ((size_t)m * S + p) * kvrow + (size_t)kh * HD + 2 * tid) = kr;
       *reinterpret_cast<uint32_t*>(cache_v + ((size_t)m * S + p) * kvrow + (size_t)kh * HD + 2 * tid) = vv;
     }
@@ -427,6 +438,12 @@ __global__ __launch_bounds__(ATT_WIDE_THREADS) void rope_attention_wide_kernel(
   float qv[DPL];
 #pragma unroll
   for (int d = 0; d < DPL; ++d) qv[d] = qs[j * DPL + d];
+  uint32_t knw[WPL], vnw[WPL];   // this lane's words of the key and value at p: selected, not branched to
+#pragma unroll
+  for (int w = 0; w < WPL; ++w) {
+    knw[w] = knp[j * WPL + w];
+    vnw[w] = vnp[j * WPL + w];
+  }
   float mx = -INFINITY, l = 0.0f, acc[DPL];
 #pragma unroll
   for (int d = 0; d < DPL; ++d) acc[d] = 0.0f;
@@ -435,42 +452,35 @@ __global__ __launch_bounds__(ATT_WIDE_THREADS) void rope_attention_wide_kernel(
     float sc[PPL];
     float bm = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < PPL; ++i) {   // scores: a 16-lane shuffle sum per position
+    for (int i = 0; i < PPL; ++i) {   // scores: a DPP sum over the 16 lanes of a position
       const int t = t0 + lg + 4 * i;
       float s = 0.0f;
-      if (t == p) {
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) s += qv[d] * kn[j * DPL + d];
-      } else {
-#pragma unroll
-        for (int w = 0; w < WPL; ++w) s += qv[2 * w] * lo16(kw[i][w]) + qv[2 * w + 1] * hi16(kw[i][w]);
+      for (int w = 0; w < WPL; ++w) {
+        const uint32_t kwd = t == p ? knw[w] : kw[i][w];
+        s += qv[2 * w] * lo16(kwd) + qv[2 * w + 1] * hi16(kwd);
       }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
+      s = row_sum16(s);
       sc[i] = t <= p ? s : -INFINITY;
       bm = fmaxf(bm, sc[i]);
     }
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));   // the step's maximum over the wave: finite (t0 <= p)
     const float nm = fmaxf(mx, bm);
-    const float so = expf(mx - nm);       // 0 on the wave's first step
+    const float so = __expf(mx - nm);     // 0 on the wave's first step
     l *= so;
 #pragma unroll
     for (int d = 0; d < DPL; ++d) acc[d] *= so;
 #pragma unroll
     for (int i = 0; i < PPL; ++i) {       // weighted values of this lane's positions
       const int t = t0 + lg + 4 * i;
-      const float e = expf(sc[i] - nm);   // 0 past p
+      const float e = __expf(sc[i] - nm); // 0 past p
       l += e;
-      if (t == p) {
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[d] += e * vn[j * DPL + d];
-      } else {
-#pragma unroll
-        for (int w = 0; w < WPL; ++w) {
-          acc[2 * w] += e * lo16(vw[i][w]);
-          acc[2 * w + 1] += e * hi16(vw[i][w]);
-        }
+      for (int w = 0; w < WPL; ++w) {
+        const uint32_t vwd = t == p ? vnw[w] : vw[i][w];
+        acc[2 * w] += e * lo16(vwd);
+        acc[2 * w + 1] += e * hi16(vwd);
       }
     }
     mx = nm;
@@ -498,7 +508,7 @@ __global__ __launch_bounds__(ATT_WIDE_THREADS) void rope_attention_wide_kernel(
     for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w]);   // finite: wave 0 holds position 0
     float L = 0.0f, A = 0.0f;
     for (int w = 0; w < NW; ++w) {   // waves in order: deterministic
-      const float c = expf(wm[w] - M);
+      const float c = __expf(wm[w] - M);
       L += c * wl[w];
       A += c * wacc[w][tid];
     }
