@@ -17,7 +17,7 @@
 //    spreads over the CUs (Llama-2-7B at 512 positions: 256 workgroups; chunks of 128 left half
 //    the CUs idle). A workgroup first issues the loads of all its key and value rows (16
 //    lanes per position, a 16-byte slice each: 256-byte coalesced reads), then rotates its query
-//    (and, in the last chunk, the new key), scores its positions with a 16-lane shuffle sum, takes
+//    (and, in the last chunk, the new key), scores its positions with a 16-lane DPP sum, takes
 //    the softmax of its chunk in LDS and sums the weighted value slices. Chunks meet in a workspace:
 //    each writes (max, sum, weighted values), and a second launch combines them in chunk order
 //    (deterministic). A single launch in which the last chunk to finish combines (an atomic counter
@@ -212,6 +212,17 @@ __global__ __launch_bounds__(DEC_THREADS) void argmax_kernel(const uint16_t* __r
   }
 }
 
+// Sum over each row of 16 lanes, left in every lane of the row: four DPP adds (lane ^ 1, lane ^ 2,
+// the other half of each 8 lanes, the other half of the 16), no LDS traffic (a __shfl_xor tree
+// compiled to ds_bpermute, an LDS round trip per step).
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  v += dpp<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0x141, 0xF>(v);   // row_half_mirror
+  v += dpp<0x140, 0xF>(v);   // row_mirror
+  return v;
+}
+
 // ---------------------------------------------------------------- rotary embedding + cache append + attention
 // Workgroup (chunk c, query head h, sequence m); HD = head size (64 or 128). Lane (lg = tid / 16,
 // j = tid % 16) owns dimensions j*HD/16 .. of the positions t0 + lg + 16 i (i < ATT_CHUNK / 16), and
@@ -297,8 +308,7 @@ __global__ __launch_bounds__(DEC_THREADS) void rope_attention_kernel(
 #pragma unroll
       for (int w = 0; w < WPL; ++w) s += qv[2 * w] * lo16(kw[i][w]) + qv[2 * w + 1] * hi16(kw[i][w]);
     }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
+    s = row_sum16(s);
     if (j == 0 && t < t1) sc[t - t0] = s;
   }
   __syncthreads();
@@ -346,17 +356,6 @@ __global__ __launch_bounds__(DEC_THREADS) void rope_attention_kernel(
   float* pr = part + (((size_t)m * H + h) * nsplit_max + c) * (HD + 2);
   if (tid < HD) pr[2 + tid] = a;
   if (tid == 0) { pr[0] = mx; pr[1] = l; }
-}
-
-// Sum over each row of 16 lanes, left in every lane of the row: four DPP adds (lane ^ 1, lane ^ 2,
-// the other half of each 8 lanes, the other half of the 16), no LDS traffic (a __shfl_xor tree
-// compiled to ds_bpermute, an LDS round trip per step).
-__device__ __forceinline__ float row_sum16(float v) {
-  v += dpp<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
-  v += dpp<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
-  v += dpp<0x141, 0xF>(v);   // row_half_mirror
-  v += dpp<0x140, 0xF>(v);   // row_mirror
-  return v;
 }
 
 // One workgroup of 16 waves per (query head h, sequence m) over all positions 0..p, for caches of
