@@ -24,7 +24,8 @@
 //    per head) needs device-scope fences, which write back and invalidate L2 on every XCD, and was
 //    an order of magnitude slower.
 //  * RMSNorm, embedding, silu*up and argmax stream 16 bytes per lane; reductions run in a fixed
-//    order (shuffle tree in a wave, then waves in order), so every result is deterministic.
+//    order (DPP within 16-lane rows, shuffles across the rows of a wave, then waves in order), so
+//    every result is deterministic.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -49,11 +50,33 @@ __device__ __forceinline__ uint32_t to_f16(float v) { return __builtin_bit_cast(
 __device__ __forceinline__ float lo16(uint32_t w) { return f16v(w & 0xFFFFu); }
 __device__ __forceinline__ float hi16(uint32_t w) { return f16v(w >> 16); }
 
-// Sum / max over the workgroup in a fixed order: a shuffle tree in each wave, then the waves in
-// order. Every thread gets the result. `red` holds one float per wave.
+// Sum over each row of 16 lanes, left in every lane of the row: four DPP adds (lane ^ 1, lane ^ 2,
+// the other half of each 8 lanes, the other half of the 16), no LDS traffic (a __shfl_xor tree
+// compiled to ds_bpermute, an LDS round trip per step).
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  v += dpp<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0x141, 0xF>(v);   // row_half_mirror
+  v += dpp<0x140, 0xF>(v);   // row_mirror
+  return v;
+}
+
+// The same for the maximum.
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<0xB1, 0xF>(v));
+  v = fmaxf(v, dpp<0x4E, 0xF>(v));
+  v = fmaxf(v, dpp<0x141, 0xF>(v));
+  v = fmaxf(v, dpp<0x140, 0xF>(v));
+  return v;
+}
+
+// Sum / max over the workgroup in a fixed order: DPP within each 16-lane row, the four rows of a
+// wave by two shuffles, then the waves in order. Every thread gets the result. `red` holds one
+// float per wave.
 __device__ __forceinline__ float block_sum(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  v = row_sum16(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -62,8 +85,9 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 __device__ __forceinline__ float block_max(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  v = row_max16(v);
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -210,17 +234,6 @@ __global__ __launch_bounds__(DEC_THREADS) void argmax_kernel(const uint16_t* __r
     tokens[m] = idx == 0x7FFFFFFF ? 0 : idx;
     if (m == 0) *pos += 1;
   }
-}
-
-// Sum over each row of 16 lanes, left in every lane of the row: four DPP adds (lane ^ 1, lane ^ 2,
-// the other half of each 8 lanes, the other half of the 16), no LDS traffic (a __shfl_xor tree
-// compiled to ds_bpermute, an LDS round trip per step).
-__device__ __forceinline__ float row_sum16(float v) {
-  v += dpp<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
-  v += dpp<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
-  v += dpp<0x141, 0xF>(v);   // row_half_mirror
-  v += dpp<0x140, 0xF>(v);   // row_mirror
-  return v;
 }
 
 // ---------------------------------------------------------------- rotary embedding + cache append + attention
